@@ -1,0 +1,23 @@
+"""AttnRes depth-routing hot path for AMD Instinct MI355X (gfx950).
+
+The compute lives in libattnres.so (hand-written HIP kernels behind a C ABI,
+declared in include/attnres.h).  This package is its thin Python binding.
+"""
+
+from .binding import (  # noqa: F401
+    BF16,
+    F32,
+    LIB_PATH,
+    AttnResError,
+    attnres_block_phase1,
+    attnres_block_phase2_merge,
+    attnres_bwd,
+    attnres_bwd_workspace_size,
+    attnres_full_fwd,
+    attnres_last_error,
+    attnres_set_kernel_policy,
+    attnres_version,
+    lib,
+    mhar_fwd,
+    mhar_fwd_workspace_size,
+)

@@ -1,0 +1,211 @@
+"""Thin ctypes binding of libattnres.so.
+
+Argument marshalling only: every function here fills in sizes and pointers
+from torch tensors (torch supplies device memory and the stream) and calls the
+C entry point of the same name.  All arithmetic runs in the library's HIP
+kernels; there is no fallback.  A missing library raises at first use.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattnres.so")
+
+F32 = 0
+BF16 = 1
+
+_lib = None
+
+
+class AttnResError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"attnres error {code}: {message}")
+        self.code = code
+        self.message = message
+
+
+def lib() -> ctypes.CDLL:
+    """Load libattnres.so (once) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with depth_wise_attention_amd/build.py")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    L.attnres_full_fwd.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, f32, i32, i32, vp, vp]
+    L.attnres_block_phase1.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, f32, i32, i32, vp, i32, vp, vp]
+    L.attnres_block_phase2_merge.argtypes = [vp, i32, vp, vp, i64, i64, vp, vp, f32, i32, i32, vp, vp]
+    L.mhar_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i32]
+    L.mhar_fwd.argtypes = [vp, i64, vp, i64, i64, i64, vp, vp, i64, f32, i32, i32, vp, vp, sz, vp]
+    L.attnres_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i32]
+    L.attnres_bwd.argtypes = [vp, i64, vp, i64, i64, i64, vp, vp, i64, f32, i32, i32, vp, vp, vp, vp,
+                              vp, i32, vp, sz, vp]
+    L.attnres_set_kernel_policy.argtypes = [i32]
+    for name in ("attnres_full_fwd", "attnres_block_phase1", "attnres_block_phase2_merge", "mhar_fwd",
+                 "attnres_bwd", "attnres_version", "attnres_set_kernel_policy"):
+        getattr(L, name).restype = ctypes.c_int
+    L.mhar_fwd_workspace_size.restype = sz
+    L.attnres_bwd_workspace_size.restype = sz
+    L.attnres_last_error.restype = ctypes.c_char_p
+    L.attnres_last_error.argtypes = []
+    L.attnres_version.argtypes = []
+    _lib = L
+    return L
+
+
+def attnres_last_error() -> str:
+    return lib().attnres_last_error().decode()
+
+
+def attnres_version() -> int:
+    return lib().attnres_version()
+
+
+def attnres_set_kernel_policy(policy: int) -> int:
+    rc = lib().attnres_set_kernel_policy(policy)
+    if rc < 0:
+        raise AttnResError(rc, attnres_last_error())
+    return rc
+
+
+def mhar_fwd_workspace_size(N: int, S: int, T: int, d: int, H: int) -> int:
+    return lib().mhar_fwd_workspace_size(N, S, T, d, H)
+
+
+def attnres_bwd_workspace_size(N: int, S: int, T: int, d: int, H: int) -> int:
+    return lib().attnres_bwd_workspace_size(N, S, T, d, H)
+
+
+# ----------------------------------------------------------------- marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def _code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _p(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _gain(gain, rows: int, d: int):
+    """(pointer, gain_ld) for a gain tensor: [rows, d] -> ld d, [d] -> ld 0, None -> NULL."""
+    if gain is None:
+        return None, 0
+    if gain.dim() == 1:
+        return _p(gain), 0
+    if tuple(gain.shape) != (rows, d):
+        raise ValueError(f"gain must be [{rows}, {d}] or [{d}]")
+    return _p(gain), d
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise AttnResError(rc, attnres_last_error())
+
+
+# ----------------------------------------------------------------- entry points
+def attnres_full_fwd(src, w, gain=None, eps: float = 1e-6, H: int = 1, out=None, stream=None):
+    """Full AttnRes forward.  src [n_src, T, d]; w [n_dst, d] -> out [n_dst, T, d]."""
+    n_src, T, d = src.shape
+    n_dst = w.shape[0]
+    if out is None:
+        out = _torch().empty((n_dst, T, d), dtype=src.dtype, device=src.device)
+    gp, gld = _gain(gain, n_dst, d)
+    _check(lib().attnres_full_fwd(_p(src), n_src, T, d, _p(w), n_dst, gp, gld, eps, H, _code(src),
+                                  _p(out), _stream(stream)))
+    return out
+
+
+def attnres_block_phase1(reps, w, gain=None, eps: float = 1e-6, H: int = 1, o=None, o_dtype=None,
+                         lse=None, stream=None):
+    """Block Phase 1.  reps [N, T, d]; w [S, d] -> (o [S, T, d], lse [S, H, T])."""
+    torch = _torch()
+    N, T, d = reps.shape
+    S = w.shape[0]
+    if o is None:
+        o = torch.empty((S, T, d), dtype=torch.float32 if o_dtype is None else o_dtype,
+                        device=reps.device)
+    if lse is None:
+        lse = torch.empty((S, H, T), dtype=torch.float32, device=reps.device)
+    gp, gld = _gain(gain, S, d)
+    _check(lib().attnres_block_phase1(_p(reps), N, T, d, _p(w), S, gp, gld, eps, H, _code(reps),
+                                      _p(o), _code(o), _p(lse), _stream(stream)))
+    return o, lse
+
+
+def attnres_block_phase2_merge(o_i, lse_i, partial, w_i, gain_i=None, eps: float = 1e-6, H: int = 1,
+                               h_i=None, stream=None):
+    """Block Phase 2 merge.  o_i [T, d]; lse_i [H, T]; partial [T, d] -> h_i [T, d]."""
+    T, d = partial.shape
+    if h_i is None:
+        h_i = _torch().empty((T, d), dtype=partial.dtype, device=partial.device)
+    _check(lib().attnres_block_phase2_merge(_p(o_i), _code(o_i), _p(lse_i), _p(partial), T, d, _p(w_i),
+                                            _p(gain_i), eps, H, _code(partial), _p(h_i),
+                                            _stream(stream)))
+    return h_i
+
+
+def mhar_fwd(reps, partials, w, gain=None, eps: float = 1e-6, H: int = 1, h=None, ws=None,
+             stream=None):
+    """One block of (multi-head) Block AttnRes: Phase 1 + S-1 merges -> h [S, T, d]."""
+    torch = _torch()
+    N, T, d = reps.shape
+    S = w.shape[0]
+    if h is None:
+        h = torch.empty((S, T, d), dtype=reps.dtype, device=reps.device)
+    need = mhar_fwd_workspace_size(N, S, T, d, H)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=reps.device)
+    gp, gld = _gain(gain, S, d)
+    _check(lib().mhar_fwd(_p(reps), N, _p(partials) if S > 1 else None, S, T, d, _p(w), gp, gld, eps, H,
+                          _code(reps), _p(h), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return h
+
+
+def attnres_bwd(reps, partials, w, dh, gain=None, eps: float = 1e-6, H: int = 1, d_reps=None,
+                d_partials=None, dw=None, dgain=None, accumulate: bool = False, ws=None, stream=None):
+    """Backward of mhar_fwd -> (d_reps, d_partials, dw, dgain)."""
+    torch = _torch()
+    N, T, d = reps.shape
+    S = w.shape[0]
+    dev = reps.device
+    if d_reps is None:
+        d_reps = torch.empty_like(reps)
+    if d_partials is None and S > 1:
+        d_partials = torch.empty((S - 1, T, d), dtype=reps.dtype, device=dev)
+    if dw is None:
+        dw = torch.empty((S, d), dtype=torch.float32, device=dev)
+    if dgain is None and gain is not None:
+        dgain = torch.empty(tuple(gain.shape), dtype=torch.float32, device=dev)
+    need = attnres_bwd_workspace_size(N, S, T, d, H)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    gp, gld = _gain(gain, S, d)
+    _check(lib().attnres_bwd(_p(reps), N, _p(partials) if S > 1 else None, S, T, d, _p(w), gp, gld, eps,
+                             H, _code(reps), _p(dh), _p(d_reps), _p(d_partials) if S > 1 else None,
+                             _p(dw), _p(dgain), int(bool(accumulate)), _p(ws),
+                             ws.numel() * ws.element_size(), _stream(stream)))
+    return d_reps, d_partials, dw, dgain

@@ -1,0 +1,395 @@
+// C ABI of libattnres.so: argument validation, error reporting and kernel
+// dispatch.  Every check runs before the first HIP call, so a rejected call
+// enqueues nothing.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/attnres.h"
+#include "launch.hpp"
+
+using namespace attnres;
+
+namespace {
+
+thread_local char g_err[1024] = "";
+std::atomic<int> g_policy{0};
+
+constexpr int kMaxSources = 64;
+constexpr int64_t kMaxD = int64_t(1) << 22;
+constexpr size_t kAlign = 256;
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(ATTNRES_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// a * b * c without int64 overflow; false on overflow or negative operands.
+bool mul3(int64_t a, int64_t b, int64_t c, int64_t* out) {
+  if (a < 0 || b < 0 || c < 0) return false;
+  int64_t ab;
+  if (__builtin_mul_overflow(a, b, &ab)) return false;
+  return !__builtin_mul_overflow(ab, c, out);
+}
+
+struct Range {
+  const void* p;
+  size_t bytes;
+  const char* name;
+};
+
+bool overlap(const Range& x, const Range& y) {
+  if (x.p == nullptr || y.p == nullptr || x.bytes == 0 || y.bytes == 0) return false;
+  const uintptr_t a0 = (uintptr_t)x.p, a1 = a0 + x.bytes;
+  const uintptr_t b0 = (uintptr_t)y.p, b1 = b0 + y.bytes;
+  return a0 < b1 && b0 < a1;
+}
+
+// Each output must not overlap any input or any other output.
+int check_aliasing(const Range* ins, int nin, const Range* outs, int nout) {
+  for (int o = 0; o < nout; ++o) {
+    for (int i = 0; i < nin; ++i)
+      if (overlap(outs[o], ins[i]))
+        return fail(ATTNRES_ERR_INVALID, "output %s overlaps input %s", outs[o].name, ins[i].name);
+    for (int p = o + 1; p < nout; ++p)
+      if (overlap(outs[o], outs[p]))
+        return fail(ATTNRES_ERR_INVALID, "outputs %s and %s overlap", outs[o].name, outs[p].name);
+  }
+  return ATTNRES_OK;
+}
+
+// Checks shared by every call.  elems = T*d (validated for overflow).
+int check_common(int64_t T, int64_t d, int32_t H, int32_t dtype, float eps, const float* gain,
+                 int64_t gain_ld, int64_t* td) {
+  if (dtype != ATTNRES_F32 && dtype != ATTNRES_BF16)
+    return fail(ATTNRES_ERR_INVALID, "dtype %d is not ATTNRES_F32 (0) or ATTNRES_BF16 (1)", dtype);
+  if (T < 0) return fail(ATTNRES_ERR_INVALID, "T = %lld is negative", (long long)T);
+  if (d < 1) return fail(ATTNRES_ERR_INVALID, "d = %lld must be >= 1", (long long)d);
+  if (d > kMaxD) return fail(ATTNRES_ERR_UNSUPPORTED, "d = %lld exceeds %lld", (long long)d, (long long)kMaxD);
+  if (H < 1) return fail(ATTNRES_ERR_INVALID, "H = %d must be >= 1", H);
+  if (d % H != 0) return fail(ATTNRES_ERR_INVALID, "d = %lld is not divisible by H = %d", (long long)d, H);
+  if (!(eps >= 0.0f) || !std::isfinite(eps))
+    return fail(ATTNRES_ERR_INVALID, "eps must be finite and >= 0");
+  if (gain != nullptr && gain_ld != 0 && gain_ld != d)
+    return fail(ATTNRES_ERR_INVALID, "gain_ld = %lld must be 0 (shared) or d = %lld", (long long)gain_ld,
+                (long long)d);
+  if (!mul3(T, d, 4, td)) return fail(ATTNRES_ERR_INVALID, "T * d overflows");
+  *td = T * d;
+  return ATTNRES_OK;
+}
+
+int check_count(int64_t n, int64_t td, int64_t es, const char* name, size_t* bytes) {
+  int64_t b;
+  if (!mul3(n, td, es, &b)) return fail(ATTNRES_ERR_INVALID, "%s size overflows", name);
+  *bytes = (size_t)b;
+  return ATTNRES_OK;
+}
+
+#define RETURN_IF(x)          \
+  do {                        \
+    const int rc_ = (x);      \
+    if (rc_ != ATTNRES_OK) return rc_; \
+  } while (0)
+
+#define REQUIRE_PTR(p, name) \
+  if ((p) == nullptr) return fail(ATTNRES_ERR_INVALID, "%s is NULL", name)
+
+bool use_fast() { return g_policy.load(std::memory_order_relaxed) == 0; }
+
+int run_phase1(const Phase1Args& a, hipStream_t st) {
+  const hipError_t e = (use_fast() && phase1_fast_ok(a)) ? launch_phase1_fast(a, st)
+                                                         : launch_phase1_generic(a, st);
+  return e == hipSuccess ? ATTNRES_OK : hip_fail(e, "phase 1 launch");
+}
+
+int run_phase2(const Phase2Args& a, hipStream_t st) {
+  const hipError_t e = (use_fast() && phase2_fast_ok(a)) ? launch_phase2_fast(a, st)
+                                                         : launch_phase2_generic(a, st);
+  return e == hipSuccess ? ATTNRES_OK : hip_fail(e, "phase 2 launch");
+}
+
+int64_t bwd_slots(int64_t T) {
+  const int64_t s = (T + 3) / 4 * 4;
+  return s < kMaxBwdSlots ? s : kMaxBwdSlots;
+}
+
+}  // namespace
+
+namespace attnres {
+int num_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+    v = 256;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+}  // namespace attnres
+
+extern "C" {
+
+const char* attnres_last_error(void) { return g_err; }
+
+int attnres_version(void) { return (1 << 16) | 0; }
+
+int attnres_set_kernel_policy(int32_t policy) {
+  if (policy != 0 && policy != 1) return fail(ATTNRES_ERR_INVALID, "unknown kernel policy %d", policy);
+  return g_policy.exchange(policy);
+}
+
+int attnres_full_fwd(const void* src, int64_t n_src, int64_t T, int64_t d, const float* w,
+                     int64_t n_dst, const float* gain, int64_t gain_ld, float eps, int32_t H,
+                     int32_t dtype, void* out, hipStream_t stream) {
+  clear_error();
+  int64_t td = 0;
+  RETURN_IF(check_common(T, d, H, dtype, eps, gain, gain_ld, &td));
+  if (n_src < 1 || n_src > kMaxSources)
+    return fail(ATTNRES_ERR_INVALID, "n_src = %lld must be in [1, %d]", (long long)n_src, kMaxSources);
+  if (n_dst < 1 || n_dst > n_src)
+    return fail(ATTNRES_ERR_INVALID, "n_dst = %lld must be in [1, n_src = %lld]", (long long)n_dst,
+                (long long)n_src);
+  if (T == 0) return ATTNRES_OK;
+  REQUIRE_PTR(src, "src");
+  REQUIRE_PTR(w, "w");
+  REQUIRE_PTR(out, "out");
+  const int64_t es = (int64_t)dt_size(dtype);
+  size_t b_src, b_out;
+  RETURN_IF(check_count(n_src, td, es, "src", &b_src));
+  RETURN_IF(check_count(n_dst, td, es, "out", &b_out));
+  const Range ins[] = {{src, b_src, "src"},
+                       {w, (size_t)(n_dst * d * 4), "w"},
+                       {gain, gain ? (size_t)((gain_ld ? n_dst : 1) * d * 4) : 0, "gain"}};
+  const Range outs[] = {{out, b_out, "out"}};
+  RETURN_IF(check_aliasing(ins, 3, outs, 1));
+
+  FullArgs a{src, n_src, T, d, w, n_dst, gain, gain ? gain_ld : 0, eps, H, dtype, out};
+  const hipError_t e = (use_fast() && full_fast_ok(a)) ? launch_full_fast(a, stream)
+                                                       : launch_full_generic(a, stream);
+  return e == hipSuccess ? ATTNRES_OK : hip_fail(e, "full forward launch");
+}
+
+int attnres_block_phase1(const void* reps, int64_t N, int64_t T, int64_t d, const float* w,
+                         int64_t S, const float* gain, int64_t gain_ld, float eps, int32_t H,
+                         int32_t dtype, void* o, int32_t o_dtype, float* lse, hipStream_t stream) {
+  clear_error();
+  int64_t td = 0;
+  RETURN_IF(check_common(T, d, H, dtype, eps, gain, gain_ld, &td));
+  if (N < 1 || N > kMaxSources - 1)
+    return fail(ATTNRES_ERR_INVALID, "N = %lld must be in [1, %d]", (long long)N, kMaxSources - 1);
+  if (S < 1) return fail(ATTNRES_ERR_INVALID, "S = %lld must be >= 1", (long long)S);
+  if (o_dtype != ATTNRES_F32 && o_dtype != dtype)
+    return fail(ATTNRES_ERR_INVALID, "o_dtype %d must be ATTNRES_F32 or the call's dtype", o_dtype);
+  if (T == 0) return ATTNRES_OK;
+  REQUIRE_PTR(reps, "reps");
+  REQUIRE_PTR(w, "w");
+  REQUIRE_PTR(o, "o");
+  REQUIRE_PTR(lse, "lse");
+  const int64_t es = (int64_t)dt_size(dtype), eo = (int64_t)dt_size(o_dtype);
+  size_t b_reps, b_o, b_lse;
+  RETURN_IF(check_count(N, td, es, "reps", &b_reps));
+  RETURN_IF(check_count(S, td, eo, "o", &b_o));
+  RETURN_IF(check_count(S * H, T, 4, "lse", &b_lse));
+  const Range ins[] = {{reps, b_reps, "reps"},
+                       {w, (size_t)(S * d * 4), "w"},
+                       {gain, gain ? (size_t)((gain_ld ? S : 1) * d * 4) : 0, "gain"}};
+  const Range outs[] = {{o, b_o, "o"}, {lse, b_lse, "lse"}};
+  RETURN_IF(check_aliasing(ins, 3, outs, 2));
+
+  Phase1Args a{reps, N, T, d, w, S, gain, gain ? gain_ld : 0, eps, H, dtype,
+               o, o_dtype, static_cast<char*>(o) + td * eo, o_dtype, lse};
+  return run_phase1(a, stream);
+}
+
+int attnres_block_phase2_merge(const void* o_i, int32_t o_dtype, const float* lse_i,
+                               const void* partial, int64_t T, int64_t d, const float* w_i,
+                               const float* gain_i, float eps, int32_t H, int32_t dtype, void* h_i,
+                               hipStream_t stream) {
+  clear_error();
+  int64_t td = 0;
+  RETURN_IF(check_common(T, d, H, dtype, eps, nullptr, 0, &td));
+  if (o_dtype != ATTNRES_F32 && o_dtype != dtype)
+    return fail(ATTNRES_ERR_INVALID, "o_dtype %d must be ATTNRES_F32 or the call's dtype", o_dtype);
+  if (T == 0) return ATTNRES_OK;
+  REQUIRE_PTR(o_i, "o_i");
+  REQUIRE_PTR(lse_i, "lse_i");
+  REQUIRE_PTR(partial, "partial");
+  REQUIRE_PTR(w_i, "w_i");
+  REQUIRE_PTR(h_i, "h_i");
+  const int64_t es = (int64_t)dt_size(dtype), eo = (int64_t)dt_size(o_dtype);
+  size_t b_p, b_o, b_lse;
+  RETURN_IF(check_count(1, td, es, "partial", &b_p));
+  RETURN_IF(check_count(1, td, eo, "o_i", &b_o));
+  RETURN_IF(check_count(H, T, 4, "lse_i", &b_lse));
+  const bool in_place = (h_i == o_i);
+  if (in_place && o_dtype != dtype)
+    return fail(ATTNRES_ERR_INVALID, "in-place merge needs o_dtype == dtype");
+  const Range ins[] = {{in_place ? nullptr : o_i, b_o, "o_i"},
+                       {lse_i, b_lse, "lse_i"},
+                       {partial, b_p, "partial"},
+                       {w_i, (size_t)(d * 4), "w_i"},
+                       {gain_i, gain_i ? (size_t)(d * 4) : 0, "gain_i"}};
+  const Range outs[] = {{h_i, b_p, "h_i"}};
+  RETURN_IF(check_aliasing(ins, 5, outs, 1));
+  Phase2Args a{o_i, o_dtype, lse_i, partial, T, d, w_i, gain_i, eps, H, dtype, h_i};
+  return run_phase2(a, stream);
+}
+
+size_t mhar_fwd_workspace_size(int64_t N, int64_t S, int64_t T, int64_t d, int32_t H) {
+  (void)N;
+  int64_t st, ls;
+  if (S < 1 || T < 0 || d < 1 || H < 1) return 0;
+  if (!mul3(S - 1, T, d, &st) || !mul3(st, 4, 1, &st)) return 0;
+  if (!mul3(S, H, T, &ls) || !mul3(ls, 4, 1, &ls)) return 0;
+  return align_up((size_t)st) + align_up((size_t)ls);
+}
+
+int mhar_fwd(const void* reps, int64_t N, const void* partials, int64_t S, int64_t T, int64_t d,
+             const float* w, const float* gain, int64_t gain_ld, float eps, int32_t H, int32_t dtype,
+             void* h, void* ws, size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  int64_t td = 0;
+  RETURN_IF(check_common(T, d, H, dtype, eps, gain, gain_ld, &td));
+  if (N < 1 || N > kMaxSources - 1)
+    return fail(ATTNRES_ERR_INVALID, "N = %lld must be in [1, %d]", (long long)N, kMaxSources - 1);
+  if (S < 1) return fail(ATTNRES_ERR_INVALID, "S = %lld must be >= 1", (long long)S);
+  if (T == 0) return ATTNRES_OK;
+  REQUIRE_PTR(reps, "reps");
+  REQUIRE_PTR(w, "w");
+  REQUIRE_PTR(h, "h");
+  if (S > 1) REQUIRE_PTR(partials, "partials");
+  const size_t need = mhar_fwd_workspace_size(N, S, T, d, H);
+  if (need == 0) return fail(ATTNRES_ERR_INVALID, "workspace size overflows");
+  if (ws == nullptr || ws_bytes < need)
+    return fail(ATTNRES_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? ws_bytes : 0,
+                need);
+  const int64_t es = (int64_t)dt_size(dtype);
+  size_t b_reps, b_parts, b_h;
+  RETURN_IF(check_count(N, td, es, "reps", &b_reps));
+  RETURN_IF(check_count(S - 1, td, es, "partials", &b_parts));
+  RETURN_IF(check_count(S, td, es, "h", &b_h));
+  const Range ins[] = {{reps, b_reps, "reps"},
+                       {partials, b_parts, "partials"},
+                       {w, (size_t)(S * d * 4), "w"},
+                       {gain, gain ? (size_t)((gain_ld ? S : 1) * d * 4) : 0, "gain"}};
+  const Range outs[] = {{h, b_h, "h"}, {ws, need, "ws"}};
+  RETURN_IF(check_aliasing(ins, 4, outs, 2));
+
+  float* state = static_cast<float*>(ws);                          // [S-1, T, d] fp32
+  float* lse = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                        align_up((size_t)((S - 1) * td * 4)));  // [S, H, T]
+  const float* g = gain;
+  const int64_t gld = gain ? gain_ld : 0;
+  Phase1Args p1{reps, N, T, d, w, S, g, gld, eps, H, dtype, h, dtype, state, ATTNRES_F32, lse};
+  RETURN_IF(run_phase1(p1, stream));
+  for (int64_t i = 2; i <= S; ++i) {
+    Phase2Args p2{state + (i - 2) * td,
+                  ATTNRES_F32,
+                  lse + (i - 1) * H * T,
+                  static_cast<const char*>(partials) + (i - 2) * td * es,
+                  T,
+                  d,
+                  w + (i - 1) * d,
+                  g ? g + (i - 1) * gld : nullptr,
+                  eps,
+                  H,
+                  dtype,
+                  static_cast<char*>(h) + (i - 1) * td * es};
+    RETURN_IF(run_phase2(p2, stream));
+  }
+  return ATTNRES_OK;
+}
+
+size_t attnres_bwd_workspace_size(int64_t N, int64_t S, int64_t T, int64_t d, int32_t H) {
+  (void)N;
+  (void)H;
+  int64_t b;
+  if (S < 1 || T < 0 || d < 1) return 0;
+  if (!mul3(bwd_slots(T), S, d, &b) || !mul3(b, 4, 1, &b)) return 0;
+  return (size_t)b;
+}
+
+int attnres_bwd(const void* reps, int64_t N, const void* partials, int64_t S, int64_t T, int64_t d,
+                const float* w, const float* gain, int64_t gain_ld, float eps, int32_t H,
+                int32_t dtype, const void* dh, void* d_reps, void* d_partials, float* dw,
+                float* dgain, int32_t accumulate, void* ws, size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  int64_t td = 0;
+  RETURN_IF(check_common(T, d, H, dtype, eps, gain, gain_ld, &td));
+  if (N < 1) return fail(ATTNRES_ERR_INVALID, "N = %lld must be >= 1", (long long)N);
+  if (S < 1) return fail(ATTNRES_ERR_INVALID, "S = %lld must be >= 1", (long long)S);
+  if (N + S - 1 > kMaxSources)
+    return fail(ATTNRES_ERR_UNSUPPORTED, "N + S - 1 = %lld exceeds %d sources", (long long)(N + S - 1),
+                kMaxSources);
+  if (accumulate != 0 && accumulate != 1)
+    return fail(ATTNRES_ERR_INVALID, "accumulate = %d must be 0 or 1", accumulate);
+  REQUIRE_PTR(w, "w");
+  REQUIRE_PTR(dw, "dw");
+  if (gain != nullptr) REQUIRE_PTR(dgain, "dgain");
+  const int64_t es = (int64_t)dt_size(dtype);
+  size_t b_reps, b_parts;
+  RETURN_IF(check_count(N, td, es, "reps", &b_reps));
+  RETURN_IF(check_count(S - 1, td, es, "partials", &b_parts));
+  const size_t b_dh = (size_t)(S * td * es);
+  const size_t b_dw = (size_t)(S * d * 4);
+  const size_t b_dg = gain ? (size_t)((gain_ld ? S : 1) * d * 4) : 0;
+  const size_t need = attnres_bwd_workspace_size(N, S, T, d, H);
+  if (T > 0) {
+    REQUIRE_PTR(reps, "reps");
+    REQUIRE_PTR(dh, "dh");
+    REQUIRE_PTR(d_reps, "d_reps");
+    if (S > 1) {
+      REQUIRE_PTR(partials, "partials");
+      REQUIRE_PTR(d_partials, "d_partials");
+    }
+    if (need == 0) return fail(ATTNRES_ERR_INVALID, "workspace size overflows");
+    if (ws == nullptr || ws_bytes < need)
+      return fail(ATTNRES_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
+                  ws ? ws_bytes : 0, need);
+  }
+  const Range ins[] = {{reps, T ? b_reps : 0, "reps"},
+                       {partials, T ? b_parts : 0, "partials"},
+                       {w, b_dw, "w"},
+                       {gain, b_dg, "gain"},
+                       {dh, T ? b_dh : 0, "dh"}};
+  const Range outs[] = {{d_reps, T ? b_reps : 0, "d_reps"},
+                        {d_partials, T ? b_parts : 0, "d_partials"},
+                        {dw, b_dw, "dw"},
+                        {dgain, b_dg, "dgain"},
+                        {ws, T ? need : 0, "ws"}};
+  RETURN_IF(check_aliasing(ins, 5, outs, 5));
+  BwdArgs a{reps,  N,    partials, S,         T,    d,        w,          gain,
+            gain ? gain_ld : 0, eps, H,  dtype,    dh,   d_reps, d_partials, dw,
+            dgain, accumulate, static_cast<float*>(ws), T ? bwd_slots(T) : 0};
+  const bool fast = use_fast() && bwd_fast_ok(a);
+  if (!fast && S * (int64_t)H * (N + 1) > 1024)
+    return fail(ATTNRES_ERR_UNSUPPORTED, "S * H * (N + 1) = %lld exceeds 1024 on the general path",
+                (long long)(S * H * (N + 1)));
+  int64_t used = 0;
+  if (T > 0) {
+    const hipError_t e = fast ? launch_bwd_fast(a, &used, stream) : launch_bwd_generic(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "backward launch");
+    if (!fast) used = a.slots;
+  }
+  const hipError_t e = launch_bwd_reduce(a, used, stream);
+  return e == hipSuccess ? ATTNRES_OK : hip_fail(e, "backward reduction launch");
+}
+
+}  // extern "C"

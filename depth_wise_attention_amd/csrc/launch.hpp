@@ -1,0 +1,108 @@
+// Internal launch interface between the C ABI (attnres_abi.cpp) and the
+// kernel files.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attnres {
+
+enum Dt : int { kF32 = 0, kBF16 = 1 };
+
+inline size_t dt_size(int dt) { return dt == kF32 ? 4 : 2; }
+
+struct FullArgs {
+  const void* src;
+  int64_t n_src, T, d;
+  const float* w;
+  int64_t n_dst;
+  const float* gain;
+  int64_t gain_ld;
+  float eps;
+  int H;
+  int dtype;
+  void* out;
+};
+
+// Phase 1: layer 0 is written to o0 (o0_dtype), layers 1..S-1 to
+// orest + (l-1)*T*d (orest_dtype).
+struct Phase1Args {
+  const void* reps;
+  int64_t N, T, d;
+  const float* w;
+  int64_t S;
+  const float* gain;
+  int64_t gain_ld;
+  float eps;
+  int H;
+  int dtype;
+  void* o0;
+  int o0_dtype;
+  void* orest;
+  int orest_dtype;
+  float* lse;  // [S, H, T]
+};
+
+struct Phase2Args {
+  const void* o;
+  int o_dtype;
+  const float* lse;  // [H, T]
+  const void* partial;
+  int64_t T, d;
+  const float* w;
+  const float* gain;  // [d] or null
+  float eps;
+  int H;
+  int dtype;
+  void* h;
+};
+
+struct BwdArgs {
+  const void* reps;
+  int64_t N;
+  const void* partials;
+  int64_t S, T, d;
+  const float* w;
+  const float* gain;
+  int64_t gain_ld;
+  float eps;
+  int H;
+  int dtype;
+  const void* dh;
+  void* d_reps;
+  void* d_partials;
+  float* dw;
+  float* dgain;
+  int accumulate;
+  float* zslots;  // [slots, S, d] fp32
+  int64_t slots;
+};
+
+// Maximum number of [S, d] partial-gradient slabs in the backward workspace.
+constexpr int64_t kMaxBwdSlots = 1024;
+
+// General kernels: any shape within the documented limits.
+hipError_t launch_full_generic(const FullArgs& a, hipStream_t st);
+hipError_t launch_phase1_generic(const Phase1Args& a, hipStream_t st);
+hipError_t launch_phase2_generic(const Phase2Args& a, hipStream_t st);
+hipError_t launch_bwd_generic(const BwdArgs& a, hipStream_t st);  // uses a.slots waves
+
+// Fixed-order reduction of the slot partials into dw / dgain.
+hipError_t launch_bwd_reduce(const BwdArgs& a, int64_t slots_used, hipStream_t st);
+
+// Specialised gfx950 kernels.  The *_ok predicates are pure functions of the
+// arguments (no HIP calls); a launcher may only be called when its predicate
+// holds.
+bool phase1_fast_ok(const Phase1Args& a);
+bool phase2_fast_ok(const Phase2Args& a);
+bool bwd_fast_ok(const BwdArgs& a);
+bool full_fast_ok(const FullArgs& a);
+hipError_t launch_phase1_fast(const Phase1Args& a, hipStream_t st);
+hipError_t launch_phase2_fast(const Phase2Args& a, hipStream_t st);
+hipError_t launch_bwd_fast(const BwdArgs& a, int64_t* slots_used, hipStream_t st);
+hipError_t launch_full_fast(const FullArgs& a, hipStream_t st);
+
+int num_cus();  // compute units of the current device (cached per device)
+
+}  // namespace attnres

@@ -1,0 +1,193 @@
+/*
+ * attnres.h -- C ABI of libattnres.so: the Attention Residuals (AttnRes)
+ * depth-routing hot path on AMD Instinct MI355X (gfx950).
+ *
+ * For every token t and every destination sublayer l, a learned pseudo-query
+ * w_l scores each stored depth source v_i as s = w_l . (g * RMSNorm(v_i)); a
+ * softmax over depth turns the scores into weights alpha_{i->l}; the output is
+ * h_l = sum_i alpha_{i->l} v_i over the UN-normalised sources.
+ *   Definitions: b-lab.team summary of "Attention Residuals", §1 (Full) and
+ *   §2 (Block); ai-systems-engineering.com "Attention Residuals" explainer,
+ *   learned-query section (RMSNorm only on the score side, gain, RMS = root
+ *   mean square); chatpaper.ai "Multi-Head Attention Residuals" abstract (H
+ *   heads, each with its own depth softmax; H = 1 is AttnRes).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  Memory     Every tensor argument is a DEVICE pointer owned by the caller.
+ *             The library never allocates, frees, copies between host and
+ *             device, or synchronises.  All work is enqueued on `stream`.
+ *  Layout     Row-major, contiguous, channel (d) fastest.  A stack of sources
+ *             [n, T, d] holds source s at base + s*T*d elements.
+ *  dtype      ATTNRES_F32 or ATTNRES_BF16, applied to every activation-shaped
+ *             tensor of the call (sources, partials, outputs, dh, source
+ *             gradients).  Arithmetic is fp32 throughout.
+ *  Parameters w (pseudo-queries), gain, lse, dw, dgain are always fp32.
+ *             gain: gain_ld == d -> one [d] vector per destination ([n_dst,d]);
+ *                   gain_ld == 0 -> one shared [d] vector;
+ *                   gain == NULL -> gain is all ones (gain_ld ignored).
+ *  Scalars    eps >= 0 and finite (RMSNorm: x / sqrt(mean(x^2) + eps)).
+ *             H >= 1, d % H == 0; head h owns channels [h*d/H, (h+1)*d/H).
+ *  Status     0 on success, negative on error (ATTNRES_ERR_*).  Every
+ *             argument is checked before any HIP call, so a call that fails
+ *             validation enqueues nothing.  attnres_last_error() returns a
+ *             thread-local message describing the last failure.
+ *  Empty      T == 0 is valid and enqueues nothing, except that attnres_bwd
+ *             with accumulate == 0 still writes zeros to dw and dgain.
+ *  Aliasing   Outputs must not overlap inputs, except where a call says so.
+ *  Determinism  Identical inputs, shapes and device give bit-identical
+ *             outputs (no floating-point atomics).
+ */
+#ifndef ATTNRES_H
+#define ATTNRES_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTNRES_F32 0
+#define ATTNRES_BF16 1
+
+#define ATTNRES_OK 0
+#define ATTNRES_ERR_INVALID (-1)     /* bad pointer, size, flag, or aliasing   */
+#define ATTNRES_ERR_UNSUPPORTED (-2) /* valid request outside built kernels    */
+#define ATTNRES_ERR_HIP (-3)         /* HIP launch or runtime error            */
+#define ATTNRES_ERR_WORKSPACE (-4)   /* workspace missing or too small         */
+
+/*
+ * Full AttnRes forward (b-lab.team summary §1: h_l = sum_{i=0}^{l-1}
+ * alpha_{i->l} v_i, v_0 the embedding, v_i the sublayer outputs).
+ *
+ *  src   [n_src, T, d] dtype   depth sources v_0 .. v_{n_src-1}
+ *  w     [n_dst, d] fp32       pseudo-queries of the destinations
+ *  gain  see conventions (per-destination rows of length d, shared, or NULL)
+ *  out   [n_dst, T, d] dtype   out[j] reads sources 0 .. n_src - n_dst + j
+ *
+ * With n_dst == n_src == L, destination l = j + 1 reads v_0 .. v_{l-1}; with
+ * n_dst == 1 it is the single call a model makes per sublayer.
+ * Requires 1 <= n_dst <= n_src <= 64.
+ */
+int attnres_full_fwd(const void* src, int64_t n_src, int64_t T, int64_t d,
+                     const float* w, int64_t n_dst, const float* gain, int64_t gain_ld,
+                     float eps, int32_t H, int32_t dtype, void* out, hipStream_t stream);
+
+/*
+ * Block AttnRes, Phase 1 of two-phase inference (b-lab.team summary §3,
+ * Inference; dimensionstp "Attention Residuals Review" §3-2 (4)): the S
+ * pseudo-queries of one block against the N cached block representations
+ * b_0 .. b_{N-1}, reading each representation once for all S queries.
+ *
+ *  reps  [N, T, d] dtype
+ *  w     [S, d] fp32;  gain as in the conventions (rows per sublayer)
+ *  o     [S, T, d] in o_dtype: o[l] = sum_i alpha_{l,i} v_i over the reps only,
+ *        normalised per head.  o[0] is already the input of the block's first
+ *        sublayer (its source set has no partial sum).
+ *  o_dtype  ATTNRES_F32 (recommended state for Phase 2: no extra rounding) or
+ *        the call's dtype.
+ *  lse   [S, H, T] fp32: log of the softmax denominator over the reps,
+ *        lse = max_i s_i + log sum_i exp(s_i - max_i s_i).
+ * Requires 1 <= N <= 63, S >= 1.
+ */
+int attnres_block_phase1(const void* reps, int64_t N, int64_t T, int64_t d,
+                         const float* w, int64_t S, const float* gain, int64_t gain_ld,
+                         float eps, int32_t H, int32_t dtype,
+                         void* o, int32_t o_dtype, float* lse, hipStream_t stream);
+
+/*
+ * Block AttnRes, Phase 2 for sublayer i >= 2 of a block (b-lab.team summary
+ * §2 value matrix, §3 Inference; Review §3-2 (4) exact online-softmax merge):
+ * score the intra-block partial sum p = b^{(n)}_{i-1} and merge it with
+ * Phase 1's state by online softmax, per head:
+ *   s_p = w_i . (g_i * RMSNorm(p)),  m = max(lse_i, s_p),
+ *   h_i = (exp(lse_i - m) o_i + exp(s_p - m) p) / (exp(lse_i - m) + exp(s_p - m)).
+ *
+ *  o_i      [T, d] in o_dtype (ATTNRES_F32 or dtype)   Phase 1 output row i
+ *  lse_i    [H, T] fp32                                 Phase 1 statistics row i
+ *  partial  [T, d] dtype
+ *  w_i      [d] fp32;  gain_i [d] fp32 or NULL (ones)
+ *  h_i      [T, d] dtype.  h_i may equal o_i when o_dtype == dtype (in place).
+ */
+int attnres_block_phase2_merge(const void* o_i, int32_t o_dtype, const float* lse_i,
+                               const void* partial, int64_t T, int64_t d,
+                               const float* w_i, const float* gain_i, float eps, int32_t H,
+                               int32_t dtype, void* h_i, hipStream_t stream);
+
+/*
+ * Bytes of device workspace mhar_fwd needs: the fp32 Phase-1 state of
+ * sublayers 2..S ([S-1, T, d]) and the statistics ([S, H, T]), each aligned
+ * to 256 bytes.  Returns 0 for invalid sizes.
+ */
+size_t mhar_fwd_workspace_size(int64_t N, int64_t S, int64_t T, int64_t d, int32_t H);
+
+/*
+ * One block of multi-head Block AttnRes routing (chatpaper.ai "Multi-Head
+ * Attention Residuals" abstract; H = 1 is Block AttnRes): Phase 1 for all S
+ * sublayers, then S-1 Phase-2 merges, one launch each, in order.
+ *
+ *  reps      [N, T, d] dtype            b_0 .. b_{N-1}
+ *  partials  [S-1, T, d] dtype          partials[k] = b^{(n)}_{k+1}, the sum
+ *            of the block's first k+1 sublayer outputs (NULL allowed if S == 1)
+ *  w         [S, d] fp32;  gain as in the conventions (rows per sublayer)
+ *  h         [S, T, d] dtype            h[i-1] is the input of sublayer i
+ *  ws        device workspace of at least mhar_fwd_workspace_size() bytes
+ * Requires 1 <= N <= 63.
+ */
+int mhar_fwd(const void* reps, int64_t N, const void* partials, int64_t S, int64_t T, int64_t d,
+             const float* w, const float* gain, int64_t gain_ld, float eps, int32_t H,
+             int32_t dtype, void* h, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Bytes of device workspace attnres_bwd needs (fp32 partial sums of the
+ * pseudo-query gradient, one [S, d] slab per slot, min(T, 1024) slots).
+ */
+size_t attnres_bwd_workspace_size(int64_t N, int64_t S, int64_t T, int64_t d, int32_t H);
+
+/*
+ * Backward of mhar_fwd: gradients of L = sum_j <dh_j, h_j> with respect to the
+ * reps, the partial sums, the pseudo-queries and the RMSNorm gain.  The pages
+ * give no backward; this is the analytic gradient of the forward definition:
+ * with x_i = RMSNorm(v_i), r_i = 1/sqrt(mean v_i^2 + eps), q_j = w_j * g_j,
+ *   a = dh_j . v_i (per head), c = alpha (a - sum alpha a),
+ *   dv_i = sum_j [alpha dh_j + r_i c q_j] - r_i x_i sum_{j,h} c s / d,
+ *   dw_j = g_j * Z_j, dg_j = w_j * Z_j, Z_j = sum_{t,i} c x_i.
+ *
+ *  dh          [S, T, d] dtype   upstream gradient of h
+ *  d_reps      [N, T, d] dtype   d_partials [S-1, T, d] dtype (NULL if S == 1)
+ *  dw          [S, d] fp32
+ *  dgain       [S, d] fp32 (gain_ld == d) or [d] (gain_ld == 0); ignored and
+ *              may be NULL when gain == NULL
+ *  accumulate  0: overwrite the four outputs; 1: add into them (reps are read
+ *              by later blocks too, so their gradients accumulate)
+ *  ws          device workspace of at least attnres_bwd_workspace_size() bytes
+ * Requires 1 <= N, N + S - 1 <= 64, S * H * (N + 1) <= 1024 on the general
+ * path.
+ */
+int attnres_bwd(const void* reps, int64_t N, const void* partials, int64_t S, int64_t T, int64_t d,
+                const float* w, const float* gain, int64_t gain_ld, float eps, int32_t H,
+                int32_t dtype, const void* dh, void* d_reps, void* d_partials, float* dw,
+                float* dgain, int32_t accumulate, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Thread-local message for the last failing call on this thread ("" if none). */
+const char* attnres_last_error(void);
+
+/* ABI version: (major << 16) | minor. */
+int attnres_version(void);
+
+/*
+ * Kernel selection, process-wide.  0 (default): the specialised gfx950 kernels
+ * wherever the shape allows, the general kernels elsewhere; 1: the general
+ * kernels only.  Both give results within the documented tolerance; the
+ * setting exists so tests can cross-check the two families on one shape.
+ * Returns the previous policy, or ATTNRES_ERR_INVALID for an unknown value.
+ */
+int attnres_set_kernel_policy(int32_t policy);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTNRES_H */

@@ -1,0 +1,220 @@
+"""The C ABI without a GPU: exports, versions, workspace sizes and argument
+validation.  Every call here fails validation, which the library performs
+before its first HIP call, so nothing is ever enqueued."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attnres.h")
+
+binding = pytest.importorskip("depth_wise_attention_amd.binding")
+
+OK, EINVAL, EUNSUP, EHIP, EWS = 0, -1, -2, -3, -4
+F32, BF16 = 0, 1
+FAKE = 0x7F0000000000  # never dereferenced: every call below is rejected first
+
+
+def _gpu_visible() -> bool:
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+fake_ptrs = pytest.mark.skipif(_gpu_visible(), reason="fake-pointer validation cases run on CPU-only hosts")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("attnres_full_fwd", "attnres_block_phase1", "attnres_block_phase2_merge", "mhar_fwd",
+                 "attnres_bwd", "mhar_fwd_workspace_size", "attnres_bwd_workspace_size",
+                 "attnres_last_error", "attnres_version", "attnres_set_kernel_policy"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_version_and_policy():
+    assert binding.attnres_version() >> 16 == 1
+    prev = binding.attnres_set_kernel_policy(1)
+    assert binding.attnres_set_kernel_policy(prev) == 1
+    with pytest.raises(binding.AttnResError):
+        binding.attnres_set_kernel_policy(7)
+
+
+def test_workspace_sizes():
+    N, S, T, d, H = 8, 4, 16384, 4096, 1
+    state = (S - 1) * T * d * 4
+    lse = S * H * T * 4
+    up = lambda x: (x + 255) // 256 * 256
+    assert binding.mhar_fwd_workspace_size(N, S, T, d, H) == up(state) + up(lse)
+    assert binding.mhar_fwd_workspace_size(N, 1, 5, 3, 1) == up(4 * 5)
+    assert binding.mhar_fwd_workspace_size(N, 0, T, d, H) == 0
+    assert binding.attnres_bwd_workspace_size(N, S, 8192, d, H) == 1024 * S * d * 4
+    assert binding.attnres_bwd_workspace_size(N, S, 5, d, H) == 8 * S * d * 4
+    assert binding.attnres_bwd_workspace_size(N, S, 0, d, H) == 0
+
+
+def _rc_full(**kw):
+    a = dict(src=FAKE, n_src=4, T=8, d=16, w=FAKE + (1 << 30), n_dst=4, gain=None, gain_ld=0, eps=1e-6,
+             H=1, dtype=BF16, out=FAKE + (2 << 30), stream=None)
+    a.update(kw)
+    L = binding.lib()
+    return L.attnres_full_fwd(a["src"], a["n_src"], a["T"], a["d"], a["w"], a["n_dst"], a["gain"],
+                              a["gain_ld"], a["eps"], a["H"], a["dtype"], a["out"], a["stream"])
+
+
+def test_full_rejects_bad_scalars():
+    cases = [dict(dtype=7), dict(T=-1), dict(d=0), dict(H=0), dict(H=3), dict(eps=-1.0),
+             dict(eps=float("nan")), dict(eps=float("inf")), dict(n_src=0), dict(n_src=65),
+             dict(n_dst=0), dict(n_dst=5), dict(gain=FAKE + (3 << 30), gain_ld=7)]
+    for c in cases:
+        assert _rc_full(**c) == EINVAL, c
+        assert binding.attnres_last_error() != ""
+
+
+def test_full_rejects_null_pointers():
+    assert _rc_full(src=None) == EINVAL
+    assert "src" in binding.attnres_last_error()
+    assert _rc_full(w=None) == EINVAL
+    assert _rc_full(out=None) == EINVAL
+
+
+@fake_ptrs
+def test_full_rejects_aliasing():
+    assert _rc_full(out=FAKE + 16) == EINVAL
+    assert "overlaps" in binding.attnres_last_error()
+
+
+def test_empty_token_count_is_a_no_op():
+    # T == 0 enqueues nothing, even with NULL tensors and no stream.
+    assert _rc_full(T=0, src=None, out=None, w=None) == OK
+    assert binding.attnres_last_error() == ""
+    L = binding.lib()
+    assert L.attnres_block_phase1(None, 8, 0, 64, None, 4, None, 0, 1e-6, 1, BF16, None, F32, None, None) == OK
+    assert L.attnres_block_phase2_merge(None, F32, None, None, 0, 64, None, None, 1e-6, 1, BF16, None,
+                                        None) == OK
+    assert L.mhar_fwd(None, 8, None, 4, 0, 64, None, None, 0, 1e-6, 1, BF16, None, None, 0, None) == OK
+
+
+def _rc_phase1(**kw):
+    a = dict(reps=FAKE, N=8, T=8, d=64, w=FAKE + (1 << 30), S=4, gain=None, gain_ld=0, eps=1e-6, H=1,
+             dtype=BF16, o=FAKE + (2 << 30), o_dtype=F32, lse=FAKE + (3 << 30))
+    a.update(kw)
+    return binding.lib().attnres_block_phase1(a["reps"], a["N"], a["T"], a["d"], a["w"], a["S"], a["gain"],
+                                              a["gain_ld"], a["eps"], a["H"], a["dtype"], a["o"],
+                                              a["o_dtype"], a["lse"], None)
+
+
+def test_phase1_rejects_bad_arguments():
+    for c in [dict(N=0), dict(N=64), dict(S=0), dict(o_dtype=5), dict(dtype=F32, o_dtype=BF16),
+              dict(lse=None), dict(o=None), dict(reps=None), dict(H=5), dict(d=63, H=2)]:
+        assert _rc_phase1(**c) == EINVAL, c
+
+
+@fake_ptrs
+def test_phase1_rejects_overlapping_outputs():
+    assert _rc_phase1(lse=FAKE + (2 << 30) + 64) == EINVAL
+    assert _rc_phase1(o=FAKE + 8) == EINVAL
+
+
+def _rc_phase2(**kw):
+    a = dict(o=FAKE, o_dtype=F32, lse=FAKE + (1 << 30), partial=FAKE + (2 << 30), T=8, d=64,
+             w=FAKE + (3 << 30), gain=None, eps=1e-6, H=1, dtype=BF16, h=FAKE + (4 << 30))
+    a.update(kw)
+    return binding.lib().attnres_block_phase2_merge(a["o"], a["o_dtype"], a["lse"], a["partial"], a["T"],
+                                                    a["d"], a["w"], a["gain"], a["eps"], a["H"],
+                                                    a["dtype"], a["h"], None)
+
+
+def test_phase2_rejects_bad_arguments():
+    for c in [dict(o_dtype=3), dict(partial=None), dict(lse=None), dict(w=None), dict(h=None),
+              dict(H=7)]:
+        assert _rc_phase2(**c) == EINVAL, c
+
+
+@fake_ptrs
+def test_phase2_in_place_needs_matching_dtype():
+    assert _rc_phase2(h=FAKE) == EINVAL          # o is fp32, h bf16: cannot share storage
+    assert "in-place" in binding.attnres_last_error()
+    assert _rc_phase2(h=FAKE + (2 << 30)) == EINVAL  # h over the partial
+
+
+def _rc_mhar(**kw):
+    a = dict(reps=FAKE, N=8, partials=FAKE + (1 << 30), S=4, T=8, d=64, w=FAKE + (2 << 30), gain=None,
+             gain_ld=0, eps=1e-6, H=1, dtype=BF16, h=FAKE + (3 << 30), ws=FAKE + (4 << 30), ws_bytes=1 << 20)
+    a.update(kw)
+    return binding.lib().mhar_fwd(a["reps"], a["N"], a["partials"], a["S"], a["T"], a["d"], a["w"],
+                                  a["gain"], a["gain_ld"], a["eps"], a["H"], a["dtype"], a["h"], a["ws"],
+                                  a["ws_bytes"], None)
+
+
+def test_mhar_rejects_bad_arguments():
+    assert _rc_mhar(partials=None) == EINVAL
+    assert _rc_mhar(N=0) == EINVAL
+    assert _rc_mhar(ws=None) == EWS
+    assert _rc_mhar(ws_bytes=16) == EWS
+    assert "workspace" in binding.attnres_last_error()
+
+
+@fake_ptrs
+def test_mhar_rejects_workspace_over_inputs():
+    assert _rc_mhar(ws=FAKE + 64) == EINVAL
+
+
+def _rc_bwd(**kw):
+    a = dict(reps=FAKE, N=8, partials=FAKE + (1 << 30), S=4, T=8, d=64, w=FAKE + (2 << 30), gain=None,
+             gain_ld=0, eps=1e-6, H=1, dtype=BF16, dh=FAKE + (3 << 30), d_reps=FAKE + (4 << 30),
+             d_partials=FAKE + (5 << 30), dw=FAKE + (6 << 30), dgain=None, accumulate=0,
+             ws=FAKE + (7 << 30), ws_bytes=1 << 24)
+    a.update(kw)
+    return binding.lib().attnres_bwd(a["reps"], a["N"], a["partials"], a["S"], a["T"], a["d"], a["w"],
+                                     a["gain"], a["gain_ld"], a["eps"], a["H"], a["dtype"], a["dh"],
+                                     a["d_reps"], a["d_partials"], a["dw"], a["dgain"], a["accumulate"],
+                                     a["ws"], a["ws_bytes"], None)
+
+
+def test_bwd_rejects_bad_arguments():
+    for c in [dict(N=0), dict(S=0), dict(accumulate=2), dict(dh=None), dict(d_reps=None),
+              dict(d_partials=None), dict(dw=None), dict(gain=FAKE + (8 << 30), dgain=None)]:
+        assert _rc_bwd(**c) == EINVAL, c
+    assert _rc_bwd(N=60, S=6) == EUNSUP
+    assert _rc_bwd(ws=None) == EWS
+    assert _rc_bwd(ws_bytes=100) == EWS
+
+
+@fake_ptrs
+def test_bwd_rejects_aliasing():
+    assert _rc_bwd(d_reps=FAKE + 2) == EINVAL
+    assert _rc_bwd(dw=FAKE + (6 << 30), ws=FAKE + (6 << 30) + 4) == EINVAL
+
+
+def test_error_message_is_thread_local():
+    import threading
+    assert _rc_full(dtype=9) == EINVAL
+    seen = {}
+
+    def other():
+        seen["msg"] = binding.attnres_last_error()
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == ""
+    assert "dtype" in binding.attnres_last_error()
