@@ -1,0 +1,332 @@
+"""Benchmark of the AttnRes Block two-phase routing on one MI355X.
+
+One step = one pass of the Block hot path over a batch of T tokens: Phase 1
+(all S pseudo-queries against the N cached reps, one launch) followed by the
+S-1 Phase-2 online-softmax merges (one launch each) -- exactly the launches of
+mhar_fwd, issued through the public C-ABI calls so HIP events can bracket each
+kernel inside the timed region.  Inputs are seeded synthetic tensors, resident
+in HBM before timing starts.
+
+Prints ONE JSON line on stdout.  Everything else goes to stderr.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                  [--no-extra] [--workload block|mhar|full|bwd] [--copy-calibration]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, AMD's published peak
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="block", choices=["block", "mhar", "full", "bwd"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device copy (counter calibration)")
+    return p.parse_args()
+
+
+# ------------------------------------------------------------------ byte accounting
+def block_bytes(T, d, N, S, H, es=2, state_es=4):
+    """Algorithmic bytes of one Phase-1 launch, one Phase-2 launch, and one step."""
+    p1 = T * (N * d * es + d * es + (S - 1) * d * state_es + S * H * 4)
+    p2 = T * (d * state_es + H * 4 + d * es + d * es)
+    return p1, p2, p1 + (S - 1) * p2
+
+
+def full_bytes(T, d, L, es=2):
+    return T * (L * d * es + L * d * es)
+
+
+def bwd_bytes(T, d, N, S, es=2):
+    # read reps, partials, dh; write d_reps, d_partials (the dw/dgain slabs are small)
+    return T * d * es * ((N + (S - 1) + S) + (N + (S - 1)))
+
+
+# ------------------------------------------------------------------ helpers
+def to_dev(x, dtype):
+    import numpy as np
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
+    return t.to(dtype)
+
+
+def time_loop(fn, steps, warmup):
+    """Run fn() warmup times, then time `steps` calls bracketed by synchronisation."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / 1e3, wall
+
+
+def kernel_source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "depth_wise_attention_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counters_for(kernel_key, src_hash):
+    """Per-launch HBM bytes measured by rocprofv3 (FETCH_SIZE + WRITE_SIZE, scaled
+    by the copy-kernel factor), if recorded for this exact kernel source."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel_key)
+    if not rec or rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ------------------------------------------------------------------ workloads
+def bench_block(args, H=1, T=16384, name=None, with_events=True):
+    import torch
+    import depth_wise_attention_amd as ar
+    from workloads import synth
+
+    wl = synth.config_block_two_phase(T=T) if H == 1 else synth.config_mhar(T=T, H=H)
+    N, S, d = wl.N, wl.S, wl.d
+    log(f"[bench] {wl.name}: generating done, uploading")
+    reps = to_dev(wl.reps, torch.bfloat16)
+    parts = to_dev(wl.partials, torch.bfloat16)
+    w = to_dev(wl.w, torch.float32)
+    g = to_dev(wl.gain, torch.float32)
+    del wl
+    h = torch.empty((S, T, d), dtype=torch.bfloat16, device="cuda")
+    state = torch.empty((S - 1, T, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((S, H, T), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(S + 1)] for _ in range(args.steps)]
+    k = {"i": -1}
+
+    def step(record=False):
+        e = ev[k["i"]] if record else None
+        if e:
+            e[0].record(stream)
+        ar.attnres_block_phase1(reps, w, g, 1e-6, H, h_first=h[0], o_state=state, lse=lse, stream=stream)
+        if e:
+            e[1].record(stream)
+        for i in range(2, S + 1):
+            ar.attnres_block_phase2_merge(state[i - 2], lse[i - 1], parts[i - 2], w[i - 1], g[i - 1], 1e-6,
+                                          H, h_i=h[i - 1], stream=stream)
+            if e:
+                e[i].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for s in range(args.steps):
+        k["i"] = s
+        step(record=with_events)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total = start.elapsed_time(end) / 1e3
+    p1_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in range(args.steps)]
+    p2_ms = [ev[s][i - 1].elapsed_time(ev[s][i]) for s in range(args.steps) for i in range(2, S + 1)]
+    p1_b, p2_b, step_b = block_bytes(T, d, N, S, H)
+    p1_avg = sum(p1_ms) / len(p1_ms) / 1e3
+    p2_avg = sum(p2_ms) / len(p2_ms) / 1e3
+    res = dict(
+        name=name or f"block_two_phase_bf16_T{T}_d{d}_N{N}_S{S}_H{H}",
+        T=T, d=d, N=N, S=S, H=H, seconds=total, wall=wall,
+        tokens_per_s=T * args.steps / total, ms_per_step=total / args.steps * 1e3,
+        step_bytes=step_b, step_gbs=step_b * args.steps / total / 1e9,
+        phase1=dict(bytes_per_launch=p1_b, avg_us=p1_avg * 1e6, gbs=p1_b / p1_avg / 1e9),
+        phase2=dict(bytes_per_launch=p2_b, avg_us=p2_avg * 1e6, gbs=p2_b / p2_avg / 1e9),
+    )
+    return res
+
+
+def bench_full(args, T=4096):
+    import torch
+    import depth_wise_attention_amd as ar
+    from workloads import synth
+
+    wl = synth.config_full_bf16(T=T)
+    src = to_dev(wl.src, torch.bfloat16)
+    w = to_dev(wl.w, torch.float32)
+    g = to_dev(wl.gain, torch.float32)
+    L, d = wl.src.shape[0], wl.d
+    del wl
+    out = torch.empty((L, T, d), dtype=torch.bfloat16, device="cuda")
+    sec, wall = time_loop(lambda: ar.attnres_full_fwd(src, w, g, 1e-6, 1, out=out), max(3, args.steps // 4),
+                          2)
+    n = max(3, args.steps // 4)
+    b = full_bytes(T, d, L)
+    return dict(name=f"full_bf16_T{T}_d{d}_L{L}", tokens_per_s=T * n / sec, ms_per_step=sec / n * 1e3,
+                step_bytes=b, step_gbs=b * n / sec / 1e9)
+
+
+def bench_bwd(args, T=8192):
+    import torch
+    import depth_wise_attention_amd as ar
+    from workloads import synth
+
+    wl = synth.config_block_fwd_bwd(T=T)
+    reps, parts, dh = (to_dev(x, torch.bfloat16) for x in (wl.reps, wl.partials, wl.dh))
+    w, g = to_dev(wl.w, torch.float32), to_dev(wl.gain, torch.float32)
+    N, S, d = wl.N, wl.S, wl.d
+    del wl
+    h = torch.empty((S, T, d), dtype=torch.bfloat16, device="cuda")
+    ws_f = torch.empty(ar.mhar_fwd_workspace_size(N, S, T, d, 1), dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(ar.attnres_bwd_workspace_size(N, S, T, d, 1), dtype=torch.uint8, device="cuda")
+    d_reps, d_parts = torch.empty_like(reps), torch.empty_like(parts)
+    dw, dg = torch.empty_like(w), torch.empty_like(g)
+
+    def step():
+        ar.mhar_fwd(reps, parts, w, g, 1e-6, 1, h=h, ws=ws_f)
+        ar.attnres_bwd(reps, parts, w, dh, g, 1e-6, 1, d_reps=d_reps, d_partials=d_parts, dw=dw, dgain=dg,
+                       ws=ws_b)
+
+    n = max(3, args.steps // 4)
+    sec, wall = time_loop(step, n, 2)
+    fwd_b = block_bytes(T, d, N, S, 1)[2]
+    b = fwd_b + bwd_bytes(T, d, N, S)
+    return dict(name=f"block_fwd_bwd_bf16_T{T}_d{d}_N{N}_S{S}", tokens_per_s=T * n / sec,
+                ms_per_step=sec / n * 1e3, step_bytes=b, step_gbs=b * n / sec / 1e9)
+
+
+def cpu_baseline(T=16384, chunk=2048):
+    """The float64 oracle (as it stands) over the headline batch, in token chunks.
+
+    Tokens are independent, so chunking changes nothing but peak memory.  About
+    10 s of single-thread numpy work on a server core."""
+    from oracle import attnres_oracle as orc
+    from workloads import synth
+
+    wl = synth.config_block_two_phase(T=T)
+    sec = 0.0
+    for lo in range(0, T, chunk):
+        sl = slice(lo, min(T, lo + chunk))
+        reps, parts = wl.reps[:, sl], wl.partials[:, sl]
+        t0 = time.perf_counter()
+        orc.block_direct(reps, parts, wl.w, wl.gain, wl.eps, 1)
+        sec += time.perf_counter() - t0
+    return dict(value=T / sec, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"all {T} tokens of the d=4096 N=8 S=4 H=1 block workload in chunks of {chunk}, "
+                       f"float64 numpy oracle (plain definition), single thread, {sec:.1f} s")
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"[bench] copied {n} bytes x5")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the routing shards along "
+              f"tokens with no exchange, so multi-GPU throughput is N times the one-GPU figure and is not "
+              f"measured here.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import depth_wise_attention_amd as ar
+
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        sys.exit(1)
+    ar.lib()  # fail loudly if the HIP library is missing
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    if args.workload != "block":
+        fn = {"mhar": lambda: bench_block(args, H=8, T=32768), "full": lambda: bench_full(args),
+              "bwd": lambda: bench_bwd(args)}[args.workload]
+        log(json.dumps(fn()))
+        return
+
+    head = bench_block(args)
+    log(f"[bench] headline: {json.dumps(head)}")
+    src_hash = kernel_source_hash("block_fast.hip", "xlane.hpp", "common.hpp")
+    traffic = counters_for("phase1_block_T16384_d4096_N8_S4_H1", src_hash)
+    p1 = head["phase1"]
+    extra = {}
+    if not args.no_extra:
+        torch.cuda.empty_cache()
+        for fn in (lambda: bench_block(args, H=8, T=32768, with_events=True), lambda: bench_full(args),
+                   lambda: bench_bwd(args)):
+            r = fn()
+            extra[r.pop("name")] = {k: v for k, v in r.items() if k not in ("T", "d", "N", "S", "H")}
+            torch.cuda.empty_cache()
+    line = {
+        "metric": "Block AttnRes routing tokens/s + achieved HBM GB/s (% peak), d=4096 N=8 S=4",
+        "value": head["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": head["name"], "T": head["T"], "d": head["d"], "N": head["N"], "S": head["S"],
+            "H": head["H"], "io_dtype": "bf16", "state_dtype": "f32",
+            "step": "phase1 + 3 phase2 merges (the launches of mhar_fwd)",
+            "step_bytes_per_token": head["step_bytes"] // head["T"],
+            "step_gbs": head["step_gbs"], "step_frac_of_peak": head["step_gbs"] / PEAK_HBM_GBS,
+            "phase2_gbs": head["phase2"]["gbs"], "phase2_avg_us": head["phase2"]["avg_us"],
+        },
+        "roofline": {
+            "kernel": "k_phase1_fast (Block Phase 1)",
+            "bound": "hbm",
+            "achieved": p1["gbs"],
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": p1["gbs"] / PEAK_HBM_GBS,
+            "traffic": traffic,
+            "avg_us": p1["avg_us"],
+            "algorithmic_bytes_per_launch": p1["bytes_per_launch"],
+        },
+        "extra_workloads": extra,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

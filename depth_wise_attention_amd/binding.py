@@ -38,7 +38,7 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
     L.attnres_full_fwd.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, f32, i32, i32, vp, vp]
-    L.attnres_block_phase1.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, f32, i32, i32, vp, i32, vp, vp]
+    L.attnres_block_phase1.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, f32, i32, i32, vp, vp, i32, vp, vp]
     L.attnres_block_phase2_merge.argtypes = [vp, i32, vp, vp, i64, i64, vp, vp, f32, i32, i32, vp, vp]
     L.mhar_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i32]
     L.mhar_fwd.argtypes = [vp, i64, vp, i64, i64, i64, vp, vp, i64, f32, i32, i32, vp, vp, sz, vp]
@@ -139,21 +139,27 @@ def attnres_full_fwd(src, w, gain=None, eps: float = 1e-6, H: int = 1, out=None,
     return out
 
 
-def attnres_block_phase1(reps, w, gain=None, eps: float = 1e-6, H: int = 1, o=None, o_dtype=None,
-                         lse=None, stream=None):
-    """Block Phase 1.  reps [N, T, d]; w [S, d] -> (o [S, T, d], lse [S, H, T])."""
+def attnres_block_phase1(reps, w, gain=None, eps: float = 1e-6, H: int = 1, h_first=None, o_state=None,
+                         o_dtype=None, lse=None, stream=None):
+    """Block Phase 1.  reps [N, T, d]; w [S, d] -> (h_first [T, d], o_state [S-1, T, d], lse [S, H, T]).
+
+    o_state defaults to float32 (the fp32 state); pass o_dtype=reps.dtype for
+    a state in the I/O dtype."""
     torch = _torch()
     N, T, d = reps.shape
     S = w.shape[0]
-    if o is None:
-        o = torch.empty((S, T, d), dtype=torch.float32 if o_dtype is None else o_dtype,
-                        device=reps.device)
+    if h_first is None:
+        h_first = torch.empty((T, d), dtype=reps.dtype, device=reps.device)
+    if o_state is None:
+        o_state = torch.empty((S - 1, T, d), dtype=torch.float32 if o_dtype is None else o_dtype,
+                              device=reps.device)
     if lse is None:
         lse = torch.empty((S, H, T), dtype=torch.float32, device=reps.device)
     gp, gld = _gain(gain, S, d)
     _check(lib().attnres_block_phase1(_p(reps), N, T, d, _p(w), S, gp, gld, eps, H, _code(reps),
-                                      _p(o), _code(o), _p(lse), _stream(stream)))
-    return o, lse
+                                      _p(h_first), _p(o_state) if S > 1 else None, _code(o_state),
+                                      _p(lse), _stream(stream)))
+    return h_first, o_state, lse
 
 
 def attnres_block_phase2_merge(o_i, lse_i, partial, w_i, gain_i=None, eps: float = 1e-6, H: int = 1,

@@ -188,7 +188,8 @@ int attnres_full_fwd(const void* src, int64_t n_src, int64_t T, int64_t d, const
 
 int attnres_block_phase1(const void* reps, int64_t N, int64_t T, int64_t d, const float* w,
                          int64_t S, const float* gain, int64_t gain_ld, float eps, int32_t H,
-                         int32_t dtype, void* o, int32_t o_dtype, float* lse, hipStream_t stream) {
+                         int32_t dtype, void* h_first, void* o_state, int32_t o_dtype, float* lse,
+                         hipStream_t stream) {
   clear_error();
   int64_t td = 0;
   RETURN_IF(check_common(T, d, H, dtype, eps, gain, gain_ld, &td));
@@ -200,21 +201,23 @@ int attnres_block_phase1(const void* reps, int64_t N, int64_t T, int64_t d, cons
   if (T == 0) return ATTNRES_OK;
   REQUIRE_PTR(reps, "reps");
   REQUIRE_PTR(w, "w");
-  REQUIRE_PTR(o, "o");
+  REQUIRE_PTR(h_first, "h_first");
+  if (S > 1) REQUIRE_PTR(o_state, "o_state");
   REQUIRE_PTR(lse, "lse");
   const int64_t es = (int64_t)dt_size(dtype), eo = (int64_t)dt_size(o_dtype);
-  size_t b_reps, b_o, b_lse;
+  size_t b_reps, b_h, b_o, b_lse;
   RETURN_IF(check_count(N, td, es, "reps", &b_reps));
-  RETURN_IF(check_count(S, td, eo, "o", &b_o));
+  RETURN_IF(check_count(1, td, es, "h_first", &b_h));
+  RETURN_IF(check_count(S - 1, td, eo, "o_state", &b_o));
   RETURN_IF(check_count(S * H, T, 4, "lse", &b_lse));
   const Range ins[] = {{reps, b_reps, "reps"},
                        {w, (size_t)(S * d * 4), "w"},
                        {gain, gain ? (size_t)((gain_ld ? S : 1) * d * 4) : 0, "gain"}};
-  const Range outs[] = {{o, b_o, "o"}, {lse, b_lse, "lse"}};
-  RETURN_IF(check_aliasing(ins, 3, outs, 2));
+  const Range outs[] = {{h_first, b_h, "h_first"}, {o_state, b_o, "o_state"}, {lse, b_lse, "lse"}};
+  RETURN_IF(check_aliasing(ins, 3, outs, 3));
 
   Phase1Args a{reps, N, T, d, w, S, gain, gain ? gain_ld : 0, eps, H, dtype,
-               o, o_dtype, static_cast<char*>(o) + td * eo, o_dtype, lse};
+               h_first, dtype, o_state, o_dtype, lse};
   return run_phase1(a, stream);
 }
 

@@ -62,10 +62,17 @@ __device__ void depth_read_wave(RowFn row, int n, float r_lane, int d, int H, co
     const float l = wave_sum(e);
     const float a_lane = e / l;
     if (lse != nullptr && lane == 0) lse[h * lse_stride] = m + logf(l);
-    for (int k = c0 + lane; k < c1; k += kWave) {
+    // Uniform loop bounds: the cross-lane reads below must run with every lane
+    // active, so the channel bound is a predicate on the loads and the store.
+    for (int kb = c0; kb < c1; kb += kWave) {
+      const int k = kb + lane;
+      const bool in = k < c1;
       float acc = 0.f;
-      for (int i = 0; i < n; ++i) acc = fmaf(read_lane(a_lane, i), ld(row(i) + k), acc);
-      st(out + k, acc);
+      for (int i = 0; i < n; ++i) {
+        const float ai = read_lane(a_lane, i);
+        acc = fmaf(ai, in ? ld(row(i) + k) : 0.f, acc);
+      }
+      if (in) st(out + k, acc);
     }
   }
 }
@@ -250,15 +257,17 @@ __global__ __launch_bounds__(256) void k_bwd_generic(BwdArgs a) {
 
     for (int j = 0; j < S; ++j) {
       const int nj = N + (j >= 1 ? 1 : 0);
-      for (int k = lane; k < d; k += kWave) {
-        const int hh = k / hd;
+      for (int kb = 0; kb < d; kb += kWave) {  // uniform bounds around read_lane
+        const int k = kb + lane;
+        const bool in = k < d;
+        const int hh = (in ? k : 0) / hd;
         float zz = 0.f;
         for (int u = 0; u < nj; ++u) {
           const int i = u < N ? u : N + j - 1;
-          const int idx = (j * H + hh) * NS + u;
-          zz = fmaf(t_c[idx] * read_lane(r_lane, i), ld(src(i) + k), zz);
+          const float ri = read_lane(r_lane, i);
+          if (in) zz = fmaf(t_c[(j * H + hh) * NS + u] * ri, ld(src(i) + k), zz);
         }
-        z[(int64_t)j * d + k] += zz;
+        if (in) z[(int64_t)j * d + k] += zz;
       }
     }
     wave_lds_sync();

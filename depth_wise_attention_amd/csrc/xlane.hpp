@@ -1,0 +1,99 @@
+// Cross-lane reductions for wave64 on gfx950, built from v_permlane32_swap,
+// v_permlane16_swap and DPP row/quad/bank controls (no LDS traffic).
+#pragma once
+
+#include "common.hpp"
+
+namespace attnres {
+
+namespace dpp {
+constexpr int kXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kRor4 = 0x124;  // row_ror:4  (lane L reads lane (L - 4) mod 16 of its row)
+constexpr int kRor8 = 0x128;  // row_ror:8  (lane L reads lane L ^ 8)
+constexpr int kRor12 = 0x12C; // row_ror:12 (lane L reads lane (L + 4) mod 16 of its row)
+}  // namespace dpp
+
+template <int Ctrl, int BankMask = 0xF>
+__device__ __forceinline__ float dpp_move(float old, float src) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), Ctrl, 0xF,
+                                                    BankMask, false));
+}
+
+// Value of lane (lane ^ 4).  row_ror:n gives lane L the value of lane (L - n)
+// mod 16 within its row.  Lanes whose bit 2 is set (DPP banks 1 and 3) need
+// lane L - 4 (row_ror:4); the others (banks 0 and 2) need L + 4 (row_ror:12).
+__device__ __forceinline__ float xor4(float v) {
+  const float t = dpp_move<dpp::kRor4, 0xA>(0.f, v);
+  return dpp_move<dpp::kRor12, 0x5>(t, v);
+}
+
+// {a + a[lane ^ 32] in lanes 0..31, b + b[lane ^ 32] in lanes 32..63}.
+__device__ __forceinline__ float swap32_add(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// {a + a[lane ^ 16] in rows 0 and 2, b + b[lane ^ 16] in rows 1 and 3} (rows of 16 lanes).
+__device__ __forceinline__ float swap16_add(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum over all 64 lanes, returned in every lane.
+__device__ __forceinline__ float wave_allsum(float v) {
+  v += dpp_move<dpp::kXor1>(0.f, v);
+  v += dpp_move<dpp::kXor2>(0.f, v);
+  v += xor4(v);
+  v += dpp_move<dpp::kRor8>(0.f, v);
+  v = swap16_add(v, v);
+  v = swap32_add(v, v);
+  return v;
+}
+
+// Transpose-reduce of 64 values per lane: on return, lane L holds the sum over
+// all 64 lanes of value index L.  Each halving stage keeps, per lane, the half
+// of the values selected by one lane bit and adds the partner lane's copy.
+__device__ __forceinline__ float transpose_reduce64(const float (&v)[64]) {
+  const int lane = lane_id();
+  float a[32];
+#pragma unroll
+  for (int m = 0; m < 32; ++m) a[m] = swap32_add(v[m], v[m + 32]);  // lane bit 5 -> index bit 5
+  float b[16];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) b[m] = swap16_add(a[m], a[m + 16]);  // lane bit 4 -> index bit 4
+  float c[8];
+  const bool hi8 = (lane & 8) != 0;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {                                      // lane bit 3 -> index bit 3
+    const float send = hi8 ? b[m] : b[m + 8];
+    const float keep = hi8 ? b[m + 8] : b[m];
+    c[m] = keep + dpp_move<dpp::kRor8>(0.f, send);
+  }
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {                                      // full sums over lane bits 0..2
+    c[m] += dpp_move<dpp::kXor1>(0.f, c[m]);
+    c[m] += dpp_move<dpp::kXor2>(0.f, c[m]);
+    c[m] += xor4(c[m]);
+  }
+  const int sel = lane & 7;
+  float r = c[0];
+#pragma unroll
+  for (int m = 1; m < 8; ++m) r = (sel == m) ? c[m] : r;
+  return r;
+}
+
+// Reduce P values per lane over the wave.  out[g] in lane L is the total of
+// value 64*g + L (zero for indices >= P).
+template <int P>
+__device__ __forceinline__ void wave_reduce_values(const float (&v)[P], float (&out)[(P + 63) / 64]) {
+#pragma unroll
+  for (int g = 0; g < (P + 63) / 64; ++g) {
+    float t[64];
+#pragma unroll
+    for (int m = 0; m < 64; ++m) t[m] = (64 * g + m < P) ? v[64 * g + m] : 0.f;
+    out[g] = transpose_reduce64(t);
+  }
+}
+
+}  // namespace attnres

@@ -79,23 +79,25 @@ int attnres_full_fwd(const void* src, int64_t n_src, int64_t T, int64_t d,
  * Block AttnRes, Phase 1 of two-phase inference (b-lab.team summary §3,
  * Inference; dimensionstp "Attention Residuals Review" §3-2 (4)): the S
  * pseudo-queries of one block against the N cached block representations
- * b_0 .. b_{N-1}, reading each representation once for all S queries.
+ * b_0 .. b_{N-1}, reading each representation once for all S queries.  For
+ * sublayer l, o_l = sum_i alpha_{l,i} b_i with alpha the softmax over the reps
+ * only (per head).
  *
- *  reps  [N, T, d] dtype
- *  w     [S, d] fp32;  gain as in the conventions (rows per sublayer)
- *  o     [S, T, d] in o_dtype: o[l] = sum_i alpha_{l,i} v_i over the reps only,
- *        normalised per head.  o[0] is already the input of the block's first
- *        sublayer (its source set has no partial sum).
- *  o_dtype  ATTNRES_F32 (recommended state for Phase 2: no extra rounding) or
- *        the call's dtype.
- *  lse   [S, H, T] fp32: log of the softmax denominator over the reps,
- *        lse = max_i s_i + log sum_i exp(s_i - max_i s_i).
+ *  reps     [N, T, d] dtype
+ *  w        [S, d] fp32;  gain as in the conventions (rows per sublayer)
+ *  h_first  [T, d] dtype: o_1, already the final input of the block's first
+ *           sublayer (its source set has no partial sum)
+ *  o_state  [S-1, T, d] in o_dtype: o_2 .. o_S, the state Phase 2 merges
+ *           (may be NULL when S == 1)
+ *  o_dtype  ATTNRES_F32 (recommended: the merge then rounds only once) or the
+ *           call's dtype
+ *  lse      [S, H, T] fp32: lse_l = max_i s_i + log sum_i exp(s_i - max_i s_i)
  * Requires 1 <= N <= 63, S >= 1.
  */
 int attnres_block_phase1(const void* reps, int64_t N, int64_t T, int64_t d,
                          const float* w, int64_t S, const float* gain, int64_t gain_ld,
-                         float eps, int32_t H, int32_t dtype,
-                         void* o, int32_t o_dtype, float* lse, hipStream_t stream);
+                         float eps, int32_t H, int32_t dtype, void* h_first,
+                         void* o_state, int32_t o_dtype, float* lse, hipStream_t stream);
 
 /*
  * Block AttnRes, Phase 2 for sublayer i >= 2 of a block (b-lab.team summary
@@ -125,8 +127,9 @@ size_t mhar_fwd_workspace_size(int64_t N, int64_t S, int64_t T, int64_t d, int32
 
 /*
  * One block of multi-head Block AttnRes routing (chatpaper.ai "Multi-Head
- * Attention Residuals" abstract; H = 1 is Block AttnRes): Phase 1 for all S
- * sublayers, then S-1 Phase-2 merges, one launch each, in order.
+ * Attention Residuals" abstract; H = 1 is Block AttnRes): exactly the launches
+ * of attnres_block_phase1 (h_first = h[0], fp32 state in ws) followed by the
+ * S-1 attnres_block_phase2_merge calls for sublayers 2..S, in order.
  *
  *  reps      [N, T, d] dtype            b_0 .. b_{N-1}
  *  partials  [S-1, T, d] dtype          partials[k] = b^{(n)}_{k+1}, the sum

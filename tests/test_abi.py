@@ -27,7 +27,7 @@ def _gpu_visible() -> bool:
         return False
 
 
-fake_ptrs = pytest.mark.skipif(_gpu_visible(), reason="fake-pointer validation cases run on CPU-only hosts")
+fake_ptrs = pytest.mark.skipif(_gpu_visible(), reason="calls with fake pointers run only on hosts without a GPU")
 
 
 def declared_functions():
@@ -80,6 +80,7 @@ def _rc_full(**kw):
                               a["gain_ld"], a["eps"], a["H"], a["dtype"], a["out"], a["stream"])
 
 
+@fake_ptrs
 def test_full_rejects_bad_scalars():
     cases = [dict(dtype=7), dict(T=-1), dict(d=0), dict(H=0), dict(H=3), dict(eps=-1.0),
              dict(eps=float("nan")), dict(eps=float("inf")), dict(n_src=0), dict(n_src=65),
@@ -89,6 +90,7 @@ def test_full_rejects_bad_scalars():
         assert binding.attnres_last_error() != ""
 
 
+@fake_ptrs
 def test_full_rejects_null_pointers():
     assert _rc_full(src=None) == EINVAL
     assert "src" in binding.attnres_last_error()
@@ -102,12 +104,14 @@ def test_full_rejects_aliasing():
     assert "overlaps" in binding.attnres_last_error()
 
 
+@fake_ptrs
 def test_empty_token_count_is_a_no_op():
     # T == 0 enqueues nothing, even with NULL tensors and no stream.
     assert _rc_full(T=0, src=None, out=None, w=None) == OK
     assert binding.attnres_last_error() == ""
     L = binding.lib()
-    assert L.attnres_block_phase1(None, 8, 0, 64, None, 4, None, 0, 1e-6, 1, BF16, None, F32, None, None) == OK
+    assert L.attnres_block_phase1(None, 8, 0, 64, None, 4, None, 0, 1e-6, 1, BF16, None, None, F32, None,
+                                  None) == OK
     assert L.attnres_block_phase2_merge(None, F32, None, None, 0, 64, None, None, 1e-6, 1, BF16, None,
                                         None) == OK
     assert L.mhar_fwd(None, 8, None, 4, 0, 64, None, None, 0, 1e-6, 1, BF16, None, None, 0, None) == OK
@@ -115,16 +119,17 @@ def test_empty_token_count_is_a_no_op():
 
 def _rc_phase1(**kw):
     a = dict(reps=FAKE, N=8, T=8, d=64, w=FAKE + (1 << 30), S=4, gain=None, gain_ld=0, eps=1e-6, H=1,
-             dtype=BF16, o=FAKE + (2 << 30), o_dtype=F32, lse=FAKE + (3 << 30))
+             dtype=BF16, h=FAKE + (4 << 30), o=FAKE + (2 << 30), o_dtype=F32, lse=FAKE + (3 << 30))
     a.update(kw)
     return binding.lib().attnres_block_phase1(a["reps"], a["N"], a["T"], a["d"], a["w"], a["S"], a["gain"],
-                                              a["gain_ld"], a["eps"], a["H"], a["dtype"], a["o"],
+                                              a["gain_ld"], a["eps"], a["H"], a["dtype"], a["h"], a["o"],
                                               a["o_dtype"], a["lse"], None)
 
 
+@fake_ptrs
 def test_phase1_rejects_bad_arguments():
     for c in [dict(N=0), dict(N=64), dict(S=0), dict(o_dtype=5), dict(dtype=F32, o_dtype=BF16),
-              dict(lse=None), dict(o=None), dict(reps=None), dict(H=5), dict(d=63, H=2)]:
+              dict(lse=None), dict(o=None), dict(h=None), dict(reps=None), dict(H=5), dict(d=63, H=2)]:
         assert _rc_phase1(**c) == EINVAL, c
 
 
@@ -132,6 +137,7 @@ def test_phase1_rejects_bad_arguments():
 def test_phase1_rejects_overlapping_outputs():
     assert _rc_phase1(lse=FAKE + (2 << 30) + 64) == EINVAL
     assert _rc_phase1(o=FAKE + 8) == EINVAL
+    assert _rc_phase1(h=FAKE + (2 << 30) + 16) == EINVAL
 
 
 def _rc_phase2(**kw):
@@ -143,6 +149,7 @@ def _rc_phase2(**kw):
                                                     a["dtype"], a["h"], None)
 
 
+@fake_ptrs
 def test_phase2_rejects_bad_arguments():
     for c in [dict(o_dtype=3), dict(partial=None), dict(lse=None), dict(w=None), dict(h=None),
               dict(H=7)]:
@@ -165,6 +172,7 @@ def _rc_mhar(**kw):
                                   a["ws_bytes"], None)
 
 
+@fake_ptrs
 def test_mhar_rejects_bad_arguments():
     assert _rc_mhar(partials=None) == EINVAL
     assert _rc_mhar(N=0) == EINVAL
@@ -190,6 +198,7 @@ def _rc_bwd(**kw):
                                      a["ws"], a["ws_bytes"], None)
 
 
+@fake_ptrs
 def test_bwd_rejects_bad_arguments():
     for c in [dict(N=0), dict(S=0), dict(accumulate=2), dict(dh=None), dict(d_reps=None),
               dict(d_partials=None), dict(dw=None), dict(gain=FAKE + (8 << 30), dgain=None)]:
@@ -205,6 +214,7 @@ def test_bwd_rejects_aliasing():
     assert _rc_bwd(dw=FAKE + (6 << 30), ws=FAKE + (6 << 30) + 4) == EINVAL
 
 
+@fake_ptrs
 def test_error_message_is_thread_local():
     import threading
     assert _rc_full(dtype=9) == EINVAL

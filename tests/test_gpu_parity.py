@@ -145,18 +145,17 @@ def test_block_shapes(T, d, N, S, H, dtype, gain, policy):
     reps, parts, w, gg = _block_on_gpu(wl, dtype, g)
     h = ar.mhar_fwd(reps, parts, w, gg, wl.eps, H)
     check(host(h), ref, dtype, "mhar_fwd")
-    # Public two-phase calls with the fp32 state reproduce mhar_fwd bit for bit.
-    o, lse = ar.attnres_block_phase1(reps, w, gg, wl.eps, H)
-    h2 = torch.empty_like(h)
-    h2[0].copy_(o[0].to(h.dtype))
+    # The public two-phase calls are exactly mhar_fwd's launches: bit-identical.
+    h_first, o_state, lse = ar.attnres_block_phase1(reps, w, gg, wl.eps, H)
+    assert torch.equal(h_first, h[0]), "phase 1 h_first differs from mhar_fwd"
     for i in range(2, S + 1):
-        ar.attnres_block_phase2_merge(o[i - 1], lse[i - 1], parts[i - 2], w[i - 1],
-                                      None if gg is None else (gg if gg.dim() == 1 else gg[i - 1]),
-                                      wl.eps, H, h_i=h2[i - 1])
-    assert torch.equal(h2[1:], h[1:]), "public phase calls differ from mhar_fwd"
-    # Phase 1 statistics against the oracle's two-phase check function.
+        hi = ar.attnres_block_phase2_merge(o_state[i - 2], lse[i - 1], parts[i - 2], w[i - 1],
+                                           None if gg is None else (gg if gg.dim() == 1 else gg[i - 1]),
+                                           wl.eps, H)
+        assert torch.equal(hi, h[i - 1]), f"phase 2 of sublayer {i} differs from mhar_fwd"
+    # Phase 1 state and statistics against the oracle's two-phase check function.
     o_ref, lse_ref = orc.block_phase1(wl.reps, wl.w, g, wl.eps, H)
-    check(host(o), o_ref, "f32" if dtype == "f32" else "f32_from_bf16", "phase1 o")
+    check(host(o_state), o_ref[1:], "f32" if dtype == "f32" else "f32_from_bf16", "phase1 state")
     np.testing.assert_allclose(host(lse), lse_ref, rtol=0, atol=1e-4 if dtype == "bf16" else 2e-5)
 
 
@@ -165,12 +164,12 @@ def test_phase2_in_place_and_bf16_state(policy):
     wl = synth.block_workload(T=300, d=4096, N=8, S=4, H=2, rep_std_step=0.3, dtype="bf16", seed=9)
     say(f"phase2 in place T={wl.T} policy={policy}")
     reps, parts, w, g = _block_on_gpu(wl, "bf16", wl.gain)
-    o, lse = ar.attnres_block_phase1(reps, w, g, wl.eps, 2, o_dtype=torch.bfloat16)
-    out_of_place = ar.attnres_block_phase2_merge(o[1], lse[1], parts[0], w[1], g[1], wl.eps, 2)
-    ar.attnres_block_phase2_merge(o[1], lse[1], parts[0], w[1], g[1], wl.eps, 2, h_i=o[1])
-    assert torch.equal(o[1], out_of_place)
+    _, o, lse = ar.attnres_block_phase1(reps, w, g, wl.eps, 2, o_dtype=torch.bfloat16)
+    out_of_place = ar.attnres_block_phase2_merge(o[0], lse[1], parts[0], w[1], g[1], wl.eps, 2)
+    ar.attnres_block_phase2_merge(o[0], lse[1], parts[0], w[1], g[1], wl.eps, 2, h_i=o[0])
+    assert torch.equal(o[0], out_of_place)
     ref = orc.block_direct(wl.reps, wl.partials, wl.w, wl.gain, wl.eps, 2)
-    err = bf16_excess_over_rms(host(o[1]), ref[1])
+    err = bf16_excess_over_rms(host(o[0]), ref[1])
     print(f"  bf16-state merge excess/RMS {err:.2e} (fp32 state is the default)")
 
 
