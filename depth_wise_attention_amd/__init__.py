@@ -6,6 +6,7 @@ declared in include/attnres.h).  This package is its thin Python binding.
 
 from .binding import (  # noqa: F401
     BF16,
+    F16,
     F32,
     LIB_PATH,
     AttnResError,

@@ -13,10 +13,12 @@ import os
 from typing import Optional
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libattnres.so")
+# ATTNRES_LIB selects another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("ATTNRES_LIB") or os.path.join(_PKG, "libattnres.so")
 
 F32 = 0
 BF16 = 1
+F16 = 2  # Phase-1 state only: fp16 scaled per token by a power of two
 
 _lib = None
 
@@ -38,8 +40,9 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
     L.attnres_full_fwd.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, f32, i32, i32, vp, vp]
-    L.attnres_block_phase1.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, f32, i32, i32, vp, vp, i32, vp, vp]
-    L.attnres_block_phase2_merge.argtypes = [vp, i32, vp, vp, i64, i64, vp, vp, f32, i32, i32, vp, vp]
+    L.attnres_block_phase1.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, f32, i32, i32, vp, vp, i32, vp, vp,
+                                       vp]
+    L.attnres_block_phase2_merge.argtypes = [vp, i32, vp, vp, vp, i64, i64, vp, vp, f32, i32, i32, vp, vp]
     L.mhar_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i32]
     L.mhar_fwd.argtypes = [vp, i64, vp, i64, i64, i64, vp, vp, i64, f32, i32, i32, vp, vp, sz, vp]
     L.attnres_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i32]
@@ -93,6 +96,8 @@ def _code(t) -> int:
         return F32
     if t.dtype == torch.bfloat16:
         return BF16
+    if t.dtype == torch.float16:
+        return F16
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -140,11 +145,12 @@ def attnres_full_fwd(src, w, gain=None, eps: float = 1e-6, H: int = 1, out=None,
 
 
 def attnres_block_phase1(reps, w, gain=None, eps: float = 1e-6, H: int = 1, h_first=None, o_state=None,
-                         o_dtype=None, lse=None, stream=None):
-    """Block Phase 1.  reps [N, T, d]; w [S, d] -> (h_first [T, d], o_state [S-1, T, d], lse [S, H, T]).
+                         o_dtype=None, lse=None, o_scale=None, stream=None):
+    """Block Phase 1.  reps [N, T, d]; w [S, d] ->
+    (h_first [T, d], o_state [S-1, T, d], lse [S, H, T], o_scale [T] or None).
 
-    o_state defaults to float32 (the fp32 state); pass o_dtype=reps.dtype for
-    a state in the I/O dtype."""
+    o_dtype: torch.float32 (default), reps.dtype, or torch.float16 (the scaled
+    fp16 state, bf16 reps only; o_scale then holds the per-token scales)."""
     torch = _torch()
     N, T, d = reps.shape
     S = w.shape[0]
@@ -155,21 +161,26 @@ def attnres_block_phase1(reps, w, gain=None, eps: float = 1e-6, H: int = 1, h_fi
                               device=reps.device)
     if lse is None:
         lse = torch.empty((S, H, T), dtype=torch.float32, device=reps.device)
+    scaled = o_state.dtype == torch.float16
+    if o_scale is None and scaled:
+        o_scale = torch.empty((T,), dtype=torch.float32, device=reps.device)
     gp, gld = _gain(gain, S, d)
     _check(lib().attnres_block_phase1(_p(reps), N, T, d, _p(w), S, gp, gld, eps, H, _code(reps),
                                       _p(h_first), _p(o_state) if S > 1 else None, _code(o_state),
-                                      _p(lse), _stream(stream)))
-    return h_first, o_state, lse
+                                      _p(lse), _p(o_scale) if scaled else None, _stream(stream)))
+    return h_first, o_state, lse, (o_scale if scaled else None)
 
 
 def attnres_block_phase2_merge(o_i, lse_i, partial, w_i, gain_i=None, eps: float = 1e-6, H: int = 1,
-                               h_i=None, stream=None):
-    """Block Phase 2 merge.  o_i [T, d]; lse_i [H, T]; partial [T, d] -> h_i [T, d]."""
+                               h_i=None, o_scale=None, stream=None):
+    """Block Phase 2 merge.  o_i [T, d]; lse_i [H, T]; partial [T, d] -> h_i [T, d].
+
+    o_scale [T] is required when o_i is the scaled fp16 state."""
     T, d = partial.shape
     if h_i is None:
         h_i = _torch().empty((T, d), dtype=partial.dtype, device=partial.device)
-    _check(lib().attnres_block_phase2_merge(_p(o_i), _code(o_i), _p(lse_i), _p(partial), T, d, _p(w_i),
-                                            _p(gain_i), eps, H, _code(partial), _p(h_i),
+    _check(lib().attnres_block_phase2_merge(_p(o_i), _code(o_i), _p(o_scale), _p(lse_i), _p(partial), T, d,
+                                            _p(w_i), _p(gain_i), eps, H, _code(partial), _p(h_i),
                                             _stream(stream)))
     return h_i
 

@@ -49,26 +49,30 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link the shared library; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile every source and link the shared library; returns its path.
+
+    `defines` (e.g. ["-DATTNRES_P1_PREFETCH=0"]) override the kernels'
+    compile-time tuning knobs; such builds go to their own object directory."""
+    bdir = BUILD if out == LIB else os.path.join(BUILD, os.path.basename(out) + ".d")
+    os.makedirs(bdir, exist_ok=True)
     cc = hipcc()
     srcs = sources()
 
     def compile_one(src):
-        obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+        obj = os.path.join(bdir, os.path.basename(src) + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        out = _run([cc, *COMMON, *lang, "-c", src, "-o", obj])
-        if verbose and out.strip():
-            print(out)
+        out_ = _run([cc, *COMMON, *defines, *lang, "-c", src, "-o", obj])
+        if verbose and out_.strip():
+            print(out_)
         return obj
 
     with ThreadPoolExecutor(min(8, len(srcs))) as ex:
         objs = list(ex.map(compile_one, srcs))
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

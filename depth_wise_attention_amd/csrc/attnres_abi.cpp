@@ -93,6 +93,14 @@ int check_common(int64_t T, int64_t d, int32_t H, int32_t dtype, float eps, cons
   return ATTNRES_OK;
 }
 
+// Phase-1 state: fp32, the I/O dtype, or (bf16 I/O only) the scaled fp16 state.
+int check_state_dtype(int32_t o_dtype, int32_t dtype) {
+  if (o_dtype == ATTNRES_F32 || o_dtype == dtype) return ATTNRES_OK;
+  if (o_dtype == ATTNRES_F16 && dtype == ATTNRES_BF16) return ATTNRES_OK;
+  return fail(ATTNRES_ERR_INVALID,
+              "o_dtype %d must be ATTNRES_F32, the call's dtype, or ATTNRES_F16 with bf16 I/O", o_dtype);
+}
+
 int check_count(int64_t n, int64_t td, int64_t es, const char* name, size_t* bytes) {
   int64_t b;
   if (!mul3(n, td, es, &b)) return fail(ATTNRES_ERR_INVALID, "%s size overflows", name);
@@ -189,21 +197,21 @@ int attnres_full_fwd(const void* src, int64_t n_src, int64_t T, int64_t d, const
 int attnres_block_phase1(const void* reps, int64_t N, int64_t T, int64_t d, const float* w,
                          int64_t S, const float* gain, int64_t gain_ld, float eps, int32_t H,
                          int32_t dtype, void* h_first, void* o_state, int32_t o_dtype, float* lse,
-                         hipStream_t stream) {
+                         float* o_scale, hipStream_t stream) {
   clear_error();
   int64_t td = 0;
   RETURN_IF(check_common(T, d, H, dtype, eps, gain, gain_ld, &td));
   if (N < 1 || N > kMaxSources - 1)
     return fail(ATTNRES_ERR_INVALID, "N = %lld must be in [1, %d]", (long long)N, kMaxSources - 1);
   if (S < 1) return fail(ATTNRES_ERR_INVALID, "S = %lld must be >= 1", (long long)S);
-  if (o_dtype != ATTNRES_F32 && o_dtype != dtype)
-    return fail(ATTNRES_ERR_INVALID, "o_dtype %d must be ATTNRES_F32 or the call's dtype", o_dtype);
+  RETURN_IF(check_state_dtype(o_dtype, dtype));
   if (T == 0) return ATTNRES_OK;
   REQUIRE_PTR(reps, "reps");
   REQUIRE_PTR(w, "w");
   REQUIRE_PTR(h_first, "h_first");
   if (S > 1) REQUIRE_PTR(o_state, "o_state");
   REQUIRE_PTR(lse, "lse");
+  if (o_dtype == ATTNRES_F16 && S > 1) REQUIRE_PTR(o_scale, "o_scale");
   const int64_t es = (int64_t)dt_size(dtype), eo = (int64_t)dt_size(o_dtype);
   size_t b_reps, b_h, b_o, b_lse;
   RETURN_IF(check_count(N, td, es, "reps", &b_reps));
@@ -213,25 +221,29 @@ int attnres_block_phase1(const void* reps, int64_t N, int64_t T, int64_t d, cons
   const Range ins[] = {{reps, b_reps, "reps"},
                        {w, (size_t)(S * d * 4), "w"},
                        {gain, gain ? (size_t)((gain_ld ? S : 1) * d * 4) : 0, "gain"}};
-  const Range outs[] = {{h_first, b_h, "h_first"}, {o_state, b_o, "o_state"}, {lse, b_lse, "lse"}};
-  RETURN_IF(check_aliasing(ins, 3, outs, 3));
+  const bool scaled = o_dtype == ATTNRES_F16 && S > 1;
+  const Range outs[] = {{h_first, b_h, "h_first"},
+                        {o_state, b_o, "o_state"},
+                        {lse, b_lse, "lse"},
+                        {scaled ? o_scale : nullptr, (size_t)T * 4, "o_scale"}};
+  RETURN_IF(check_aliasing(ins, 3, outs, 4));
 
   Phase1Args a{reps, N, T, d, w, S, gain, gain ? gain_ld : 0, eps, H, dtype,
-               h_first, dtype, o_state, o_dtype, lse};
+               h_first, dtype, o_state, o_dtype, lse, scaled ? o_scale : nullptr};
   return run_phase1(a, stream);
 }
 
-int attnres_block_phase2_merge(const void* o_i, int32_t o_dtype, const float* lse_i,
-                               const void* partial, int64_t T, int64_t d, const float* w_i,
-                               const float* gain_i, float eps, int32_t H, int32_t dtype, void* h_i,
-                               hipStream_t stream) {
+int attnres_block_phase2_merge(const void* o_i, int32_t o_dtype, const float* o_scale,
+                               const float* lse_i, const void* partial, int64_t T, int64_t d,
+                               const float* w_i, const float* gain_i, float eps, int32_t H,
+                               int32_t dtype, void* h_i, hipStream_t stream) {
   clear_error();
   int64_t td = 0;
   RETURN_IF(check_common(T, d, H, dtype, eps, nullptr, 0, &td));
-  if (o_dtype != ATTNRES_F32 && o_dtype != dtype)
-    return fail(ATTNRES_ERR_INVALID, "o_dtype %d must be ATTNRES_F32 or the call's dtype", o_dtype);
+  RETURN_IF(check_state_dtype(o_dtype, dtype));
   if (T == 0) return ATTNRES_OK;
   REQUIRE_PTR(o_i, "o_i");
+  if (o_dtype == ATTNRES_F16) REQUIRE_PTR(o_scale, "o_scale");
   REQUIRE_PTR(lse_i, "lse_i");
   REQUIRE_PTR(partial, "partial");
   REQUIRE_PTR(w_i, "w_i");
@@ -248,20 +260,23 @@ int attnres_block_phase2_merge(const void* o_i, int32_t o_dtype, const float* ls
                        {lse_i, b_lse, "lse_i"},
                        {partial, b_p, "partial"},
                        {w_i, (size_t)(d * 4), "w_i"},
-                       {gain_i, gain_i ? (size_t)(d * 4) : 0, "gain_i"}};
+                       {gain_i, gain_i ? (size_t)(d * 4) : 0, "gain_i"},
+                       {o_dtype == ATTNRES_F16 ? o_scale : nullptr, (size_t)T * 4, "o_scale"}};
   const Range outs[] = {{h_i, b_p, "h_i"}};
-  RETURN_IF(check_aliasing(ins, 5, outs, 1));
-  Phase2Args a{o_i, o_dtype, lse_i, partial, T, d, w_i, gain_i, eps, H, dtype, h_i};
+  RETURN_IF(check_aliasing(ins, 6, outs, 1));
+  Phase2Args a{o_i, o_dtype, o_dtype == ATTNRES_F16 ? o_scale : nullptr, lse_i, partial, T, d,
+               w_i, gain_i, eps, H, dtype, h_i};
   return run_phase2(a, stream);
 }
 
 size_t mhar_fwd_workspace_size(int64_t N, int64_t S, int64_t T, int64_t d, int32_t H) {
   (void)N;
-  int64_t st, ls;
+  int64_t st, ls, sc;
   if (S < 1 || T < 0 || d < 1 || H < 1) return 0;
-  if (!mul3(S - 1, T, d, &st) || !mul3(st, 4, 1, &st)) return 0;
+  if (!mul3(S - 1, T, d, &st) || !mul3(st, 4, 1, &st)) return 0;  // fp32 state (the largest)
   if (!mul3(S, H, T, &ls) || !mul3(ls, 4, 1, &ls)) return 0;
-  return align_up((size_t)st) + align_up((size_t)ls);
+  if (!mul3(T, 4, 1, &sc)) return 0;
+  return align_up((size_t)st) + align_up((size_t)ls) + align_up((size_t)sc);
 }
 
 int mhar_fwd(const void* reps, int64_t N, const void* partials, int64_t S, int64_t T, int64_t d,
@@ -295,16 +310,22 @@ int mhar_fwd(const void* reps, int64_t N, const void* partials, int64_t S, int64
   const Range outs[] = {{h, b_h, "h"}, {ws, need, "ws"}};
   RETURN_IF(check_aliasing(ins, 4, outs, 2));
 
-  float* state = static_cast<float*>(ws);                          // [S-1, T, d] fp32
-  float* lse = reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                        align_up((size_t)((S - 1) * td * 4)));  // [S, H, T]
+  // State between the phases: the scaled fp16 state for bf16 I/O, fp32 for fp32 I/O.
+  const int sdt = dtype == ATTNRES_BF16 ? ATTNRES_F16 : ATTNRES_F32;
+  const int64_t se = (int64_t)dt_size(sdt);
+  char* state = static_cast<char*>(ws);                                     // [S-1, T, d]
+  char* base = static_cast<char*>(ws) + align_up((size_t)((S - 1) * td * 4));
+  float* lse = reinterpret_cast<float*>(base);                              // [S, H, T]
+  float* oscale = reinterpret_cast<float*>(base + align_up((size_t)(S * H * T * 4)));  // [T]
   const float* g = gain;
   const int64_t gld = gain ? gain_ld : 0;
-  Phase1Args p1{reps, N, T, d, w, S, g, gld, eps, H, dtype, h, dtype, state, ATTNRES_F32, lse};
+  Phase1Args p1{reps, N, T, d, w, S, g, gld, eps, H, dtype, h, dtype, state, sdt, lse,
+                sdt == ATTNRES_F16 ? oscale : nullptr};
   RETURN_IF(run_phase1(p1, stream));
   for (int64_t i = 2; i <= S; ++i) {
-    Phase2Args p2{state + (i - 2) * td,
-                  ATTNRES_F32,
+    Phase2Args p2{state + (i - 2) * td * se,
+                  sdt,
+                  sdt == ATTNRES_F16 ? oscale : nullptr,
                   lse + (i - 1) * H * T,
                   static_cast<const char*>(partials) + (i - 2) * td * es,
                   T,

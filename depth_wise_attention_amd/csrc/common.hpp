@@ -7,6 +7,7 @@
 namespace attnres {
 
 typedef uint16_t bf16_t;
+typedef _Float16 f16_t;
 
 constexpr int kWave = 64;
 
@@ -30,10 +31,26 @@ __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 
 template <typename E> __device__ __forceinline__ float ld(const E* p);
 template <> __device__ __forceinline__ float ld<float>(const float* p) { return *p; }
 template <> __device__ __forceinline__ float ld<bf16_t>(const bf16_t* p) { return bf2f(*p); }
+template <> __device__ __forceinline__ float ld<f16_t>(const f16_t* p) { return (float)*p; }
 
 template <typename E> __device__ __forceinline__ void st(E* p, float v);
 template <> __device__ __forceinline__ void st<float>(float* p, float v) { *p = v; }
 template <> __device__ __forceinline__ void st<bf16_t>(bf16_t* p, float v) { *p = f2bf(v); }
+template <> __device__ __forceinline__ void st<f16_t>(f16_t* p, float v) { *p = (f16_t)v; }
+
+// Per-token power-of-two scale for an fp16 state whose values are bounded by
+// `bound` (>= max |value|): returns 2^e with bound / 32768 = m * 2^e, m in
+// [0.5, 1), so the stored values value * 2^-e satisfy |.| < 32768 (below the
+// fp16 limit 65504) and the bound itself lands in [16384, 32768): the top of
+// fp16's range, where its 11 significant bits apply.  Zero, NaN and infinite
+// bounds give 1.
+__device__ __forceinline__ float f16_state_scale(float bound) {
+  if (!(bound > 0.f) || !(bound <= 3.0e38f)) return 1.0f;
+  int e = 0;
+  frexpf(bound * (1.0f / 32768.0f), &e);
+  e = e < -120 ? -120 : (e > 120 ? 120 : e);
+  return ldexpf(1.0f, e);
+}
 
 // -------------------------------------------------------------- cross-lane ops
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }

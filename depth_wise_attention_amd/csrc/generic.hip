@@ -18,9 +18,9 @@ constexpr int kBwdTab = 1024;      // S*H*(N+1) table entries per wave (backward
 // Inverse RMS of sources row(0..n-1): lane i returns r_i = 1/sqrt(mean(v_i^2) + eps).
 // (ai-systems-engineering explainer, learned-query section: RMS = root mean square.)
 template <typename E, typename RowFn>
-__device__ float inv_rms_lanes(RowFn row, int n, int d, float eps) {
+__device__ float inv_rms_lanes(RowFn row, int n, int d, float eps, float* max_ss = nullptr) {
   const int lane = lane_id();
-  float r_lane = 0.f;
+  float r_lane = 0.f, mx = 0.f;
   for (int i = 0; i < n; ++i) {
     const E* v = row(i);
     float ss = 0.f;
@@ -29,8 +29,10 @@ __device__ float inv_rms_lanes(RowFn row, int n, int d, float eps) {
       ss = fmaf(x, x, ss);
     }
     ss = wave_sum(ss);
+    mx = fmaxf(mx, ss);
     if (lane == i) r_lane = 1.0f / sqrtf(ss / (float)d + eps);
   }
+  if (max_ss) *max_ss = mx;
   return r_lane;
 }
 
@@ -38,9 +40,12 @@ __device__ float inv_rms_lanes(RowFn row, int n, int d, float eps) {
 //   s_i = r_i * (w * g) . v_i per head, alpha = softmax over i, out = sum alpha_i v_i
 // (b-lab.team summary §1; chatpaper MHAR abstract for the per-head softmax).
 // When lse != nullptr, lse[h * lse_stride] = max s + log sum exp(s - max s).
+// Outputs are multiplied by out_mul before the store (a power of two for a
+// scaled fp16 state, else 1).
 template <typename E, typename O, typename RowFn>
 __device__ void depth_read_wave(RowFn row, int n, float r_lane, int d, int H, const float* w,
-                                const float* g, O* out, float* lse, int64_t lse_stride) {
+                                const float* g, O* out, float* lse, int64_t lse_stride,
+                                float out_mul = 1.0f) {
   const int lane = lane_id();
   const int hd = d / H;
   for (int h = 0; h < H; ++h) {
@@ -72,7 +77,7 @@ __device__ void depth_read_wave(RowFn row, int n, float r_lane, int d, int H, co
         const float ai = read_lane(a_lane, i);
         acc = fmaf(ai, in ? ld(row(i) + k) : 0.f, acc);
       }
-      if (in) st(out + k, acc);
+      if (in) st(out + k, acc * out_mul);
     }
   }
 }
@@ -106,7 +111,15 @@ __global__ __launch_bounds__(256) void k_phase1_generic(Phase1Args a) {
   const int64_t nw = (int64_t)gridDim.x * kGenWaves;
   for (int64_t t = wave; t < T; t += nw) {
     auto row = [&](int i) { return reps + i * td + t * d; };
-    const float r_lane = inv_rms_lanes<E>(row, (int)a.N, d, a.eps);
+    float max_ss = 0.f;
+    const float r_lane = inv_rms_lanes<E>(row, (int)a.N, d, a.eps, &max_ss);
+    // A scaled fp16 state: |o| <= max_i ||v_i||_2 = sqrt(max_i ss_i) bounds every value.
+    float inv_scale = 1.0f;
+    if (a.orest_dtype == kF16) {
+      const float scale = f16_state_scale(sqrtf(max_ss));
+      inv_scale = 1.0f / scale;
+      if (lane_id() == 0) a.oscale[t] = scale;
+    }
     for (int64_t l = 0; l < a.S; ++l) {
       const float* g = a.gain ? a.gain + l * a.gain_ld : nullptr;
       float* lse = a.lse + l * a.H * T + t;
@@ -115,7 +128,7 @@ __global__ __launch_bounds__(256) void k_phase1_generic(Phase1Args a) {
                                static_cast<O0*>(a.o0) + t * d, lse, T);
       else
         depth_read_wave<E, OR>(row, (int)a.N, r_lane, d, a.H, a.w + l * d, g,
-                               static_cast<OR*>(a.orest) + ((l - 1) * T + t) * d, lse, T);
+                               static_cast<OR*>(a.orest) + ((l - 1) * T + t) * d, lse, T, inv_scale);
     }
   }
 }
@@ -150,8 +163,9 @@ __global__ __launch_bounds__(256) void k_phase2_generic(Phase2Args a) {
       const float m = fmaxf(L, s_p);
       const float wa = expf(L - m), wb = expf(s_p - m);
       const float inv = 1.0f / (wa + wb);
+      const float ca = wa * inv * (a.o_dtype == kF16 ? a.oscale[t] : 1.0f), cb = wb * inv;
       for (int k = c0 + lane; k < c1; k += kWave)
-        st(hout + k, (wa * ld(o + k) + wb * ld(p + k)) * inv);
+        st(hout + k, ca * ld(o + k) + cb * ld(p + k));
     }
   }
 }
@@ -343,8 +357,8 @@ hipError_t launch_phase1_generic(const Phase1Args& a, hipStream_t st) {
     hipLaunchKernelGGL((k_phase1_generic<bf16_t, bf16_t, bf16_t>), grid, block, 0, st, a);
   } else if (a.o0_dtype == kBF16 && a.orest_dtype == kF32) {
     hipLaunchKernelGGL((k_phase1_generic<bf16_t, bf16_t, float>), grid, block, 0, st, a);
-  } else if (a.o0_dtype == kF32 && a.orest_dtype == kF32) {
-    hipLaunchKernelGGL((k_phase1_generic<bf16_t, float, float>), grid, block, 0, st, a);
+  } else if (a.o0_dtype == kBF16 && a.orest_dtype == kF16) {
+    hipLaunchKernelGGL((k_phase1_generic<bf16_t, bf16_t, f16_t>), grid, block, 0, st, a);
   } else {
     return hipErrorNotSupported;
   }
@@ -357,6 +371,8 @@ hipError_t launch_phase2_generic(const Phase2Args& a, hipStream_t st) {
     hipLaunchKernelGGL((k_phase2_generic<float, float>), grid, block, 0, st, a);
   else if (a.o_dtype == kF32)
     hipLaunchKernelGGL((k_phase2_generic<bf16_t, float>), grid, block, 0, st, a);
+  else if (a.o_dtype == kF16)
+    hipLaunchKernelGGL((k_phase2_generic<bf16_t, f16_t>), grid, block, 0, st, a);
   else
     hipLaunchKernelGGL((k_phase2_generic<bf16_t, bf16_t>), grid, block, 0, st, a);
   return hipGetLastError();

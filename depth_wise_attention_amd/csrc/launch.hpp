@@ -8,7 +8,9 @@
 
 namespace attnres {
 
-enum Dt : int { kF32 = 0, kBF16 = 1 };
+// kF16 is only a Phase-1 -> Phase-2 state format: fp16 values scaled per token
+// by a power of two (see Phase1Args::oscale).
+enum Dt : int { kF32 = 0, kBF16 = 1, kF16 = 2 };
 
 inline size_t dt_size(int dt) { return dt == kF32 ? 4 : 2; }
 
@@ -41,12 +43,14 @@ struct Phase1Args {
   int o0_dtype;
   void* orest;
   int orest_dtype;
-  float* lse;  // [S, H, T]
+  float* lse;     // [S, H, T]
+  float* oscale;  // [T], written when orest_dtype == kF16: orest = o * (1 / oscale[t])
 };
 
 struct Phase2Args {
   const void* o;
   int o_dtype;
+  const float* oscale;  // [T] when o_dtype == kF16 (o = stored * oscale[t])
   const float* lse;  // [H, T]
   const void* partial;
   int64_t T, d;

@@ -51,6 +51,13 @@ extern "C" {
 
 #define ATTNRES_F32 0
 #define ATTNRES_BF16 1
+/* Phase-1 state format only (o_dtype, with bf16 I/O): fp16 values scaled per
+ * token by a power of two, o = stored * o_scale[t].  o_scale[t] = 2^e is
+ * chosen from the bound |o| <= max_i ||b_i||_2 so that every stored value is
+ * below 32768 in magnitude and the bound sits in [16384, 32768): no fp16
+ * overflow for any finite input, and 11 significant bits for the state
+ * (bf16 keeps 8).  Requires each rep's sum of squares to be finite in fp32. */
+#define ATTNRES_F16 2
 
 #define ATTNRES_OK 0
 #define ATTNRES_ERR_INVALID (-1)     /* bad pointer, size, flag, or aliasing   */
@@ -89,15 +96,19 @@ int attnres_full_fwd(const void* src, int64_t n_src, int64_t T, int64_t d,
  *           sublayer (its source set has no partial sum)
  *  o_state  [S-1, T, d] in o_dtype: o_2 .. o_S, the state Phase 2 merges
  *           (may be NULL when S == 1)
- *  o_dtype  ATTNRES_F32 (recommended: the merge then rounds only once) or the
- *           call's dtype
+ *  o_dtype  ATTNRES_F32, the call's dtype, or ATTNRES_F16 (bf16 I/O only; see
+ *           its definition).  The merge rounds the state once more, so the
+ *           state's precision adds to the error: fp32 adds nothing, the scaled
+ *           fp16 state about 2^-12 of the value, a bf16 state about 2^-9.
  *  lse      [S, H, T] fp32: lse_l = max_i s_i + log sum_i exp(s_i - max_i s_i)
+ *  o_scale  [T] fp32, written when o_dtype == ATTNRES_F16 (else may be NULL)
  * Requires 1 <= N <= 63, S >= 1.
  */
 int attnres_block_phase1(const void* reps, int64_t N, int64_t T, int64_t d,
                          const float* w, int64_t S, const float* gain, int64_t gain_ld,
                          float eps, int32_t H, int32_t dtype, void* h_first,
-                         void* o_state, int32_t o_dtype, float* lse, hipStream_t stream);
+                         void* o_state, int32_t o_dtype, float* lse, float* o_scale,
+                         hipStream_t stream);
 
 /*
  * Block AttnRes, Phase 2 for sublayer i >= 2 of a block (b-lab.team summary
@@ -107,29 +118,31 @@ int attnres_block_phase1(const void* reps, int64_t N, int64_t T, int64_t d,
  *   s_p = w_i . (g_i * RMSNorm(p)),  m = max(lse_i, s_p),
  *   h_i = (exp(lse_i - m) o_i + exp(s_p - m) p) / (exp(lse_i - m) + exp(s_p - m)).
  *
- *  o_i      [T, d] in o_dtype (ATTNRES_F32 or dtype)   Phase 1 output row i
- *  lse_i    [H, T] fp32                                 Phase 1 statistics row i
+ *  o_i      [T, d] in o_dtype                 Phase 1 state row i
+ *  o_scale  [T] fp32 when o_dtype == ATTNRES_F16 (Phase 1's o_scale), else ignored
+ *  lse_i    [H, T] fp32                       Phase 1 statistics row i
  *  partial  [T, d] dtype
  *  w_i      [d] fp32;  gain_i [d] fp32 or NULL (ones)
  *  h_i      [T, d] dtype.  h_i may equal o_i when o_dtype == dtype (in place).
  */
-int attnres_block_phase2_merge(const void* o_i, int32_t o_dtype, const float* lse_i,
-                               const void* partial, int64_t T, int64_t d,
+int attnres_block_phase2_merge(const void* o_i, int32_t o_dtype, const float* o_scale,
+                               const float* lse_i, const void* partial, int64_t T, int64_t d,
                                const float* w_i, const float* gain_i, float eps, int32_t H,
                                int32_t dtype, void* h_i, hipStream_t stream);
 
 /*
- * Bytes of device workspace mhar_fwd needs: the fp32 Phase-1 state of
- * sublayers 2..S ([S-1, T, d]) and the statistics ([S, H, T]), each aligned
- * to 256 bytes.  Returns 0 for invalid sizes.
+ * Bytes of device workspace mhar_fwd needs: room for an fp32 Phase-1 state of
+ * sublayers 2..S ([S-1, T, d]), the statistics ([S, H, T]) and the per-token
+ * state scale ([T]), each aligned to 256 bytes.  Returns 0 for invalid sizes.
  */
 size_t mhar_fwd_workspace_size(int64_t N, int64_t S, int64_t T, int64_t d, int32_t H);
 
 /*
  * One block of multi-head Block AttnRes routing (chatpaper.ai "Multi-Head
  * Attention Residuals" abstract; H = 1 is Block AttnRes): exactly the launches
- * of attnres_block_phase1 (h_first = h[0], fp32 state in ws) followed by the
- * S-1 attnres_block_phase2_merge calls for sublayers 2..S, in order.
+ * of attnres_block_phase1 (h_first = h[0]; state in ws: the scaled fp16 state
+ * ATTNRES_F16 for bf16 I/O, fp32 for fp32 I/O) followed by the S-1
+ * attnres_block_phase2_merge calls for sublayers 2..S, in order.
  *
  *  reps      [N, T, d] dtype            b_0 .. b_{N-1}
  *  partials  [S-1, T, d] dtype          partials[k] = b^{(n)}_{k+1}, the sum

@@ -15,7 +15,7 @@ HEADER = os.path.join(ROOT, "include", "attnres.h")
 binding = pytest.importorskip("depth_wise_attention_amd.binding")
 
 OK, EINVAL, EUNSUP, EHIP, EWS = 0, -1, -2, -3, -4
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 FAKE = 0x7F0000000000  # never dereferenced: every call below is rejected first
 
 
@@ -63,8 +63,8 @@ def test_workspace_sizes():
     state = (S - 1) * T * d * 4
     lse = S * H * T * 4
     up = lambda x: (x + 255) // 256 * 256
-    assert binding.mhar_fwd_workspace_size(N, S, T, d, H) == up(state) + up(lse)
-    assert binding.mhar_fwd_workspace_size(N, 1, 5, 3, 1) == up(4 * 5)
+    assert binding.mhar_fwd_workspace_size(N, S, T, d, H) == up(state) + up(lse) + up(4 * T)
+    assert binding.mhar_fwd_workspace_size(N, 1, 5, 3, 1) == up(4 * 5) + up(4 * 5)
     assert binding.mhar_fwd_workspace_size(N, 0, T, d, H) == 0
     assert binding.attnres_bwd_workspace_size(N, S, 8192, d, H) == 1024 * S * d * 4
     assert binding.attnres_bwd_workspace_size(N, S, 5, d, H) == 8 * S * d * 4
@@ -111,25 +111,27 @@ def test_empty_token_count_is_a_no_op():
     assert binding.attnres_last_error() == ""
     L = binding.lib()
     assert L.attnres_block_phase1(None, 8, 0, 64, None, 4, None, 0, 1e-6, 1, BF16, None, None, F32, None,
-                                  None) == OK
-    assert L.attnres_block_phase2_merge(None, F32, None, None, 0, 64, None, None, 1e-6, 1, BF16, None,
+                                  None, None) == OK
+    assert L.attnres_block_phase2_merge(None, F32, None, None, None, 0, 64, None, None, 1e-6, 1, BF16, None,
                                         None) == OK
     assert L.mhar_fwd(None, 8, None, 4, 0, 64, None, None, 0, 1e-6, 1, BF16, None, None, 0, None) == OK
 
 
 def _rc_phase1(**kw):
     a = dict(reps=FAKE, N=8, T=8, d=64, w=FAKE + (1 << 30), S=4, gain=None, gain_ld=0, eps=1e-6, H=1,
-             dtype=BF16, h=FAKE + (4 << 30), o=FAKE + (2 << 30), o_dtype=F32, lse=FAKE + (3 << 30))
+             dtype=BF16, h=FAKE + (4 << 30), o=FAKE + (2 << 30), o_dtype=F32, lse=FAKE + (3 << 30),
+             scale=None)
     a.update(kw)
     return binding.lib().attnres_block_phase1(a["reps"], a["N"], a["T"], a["d"], a["w"], a["S"], a["gain"],
                                               a["gain_ld"], a["eps"], a["H"], a["dtype"], a["h"], a["o"],
-                                              a["o_dtype"], a["lse"], None)
+                                              a["o_dtype"], a["lse"], a["scale"], None)
 
 
 @fake_ptrs
 def test_phase1_rejects_bad_arguments():
     for c in [dict(N=0), dict(N=64), dict(S=0), dict(o_dtype=5), dict(dtype=F32, o_dtype=BF16),
-              dict(lse=None), dict(o=None), dict(h=None), dict(reps=None), dict(H=5), dict(d=63, H=2)]:
+              dict(lse=None), dict(o=None), dict(h=None), dict(reps=None), dict(H=5), dict(d=63, H=2),
+              dict(dtype=F32, o_dtype=F16, scale=FAKE + (5 << 30)), dict(o_dtype=F16, scale=None)]:
         assert _rc_phase1(**c) == EINVAL, c
 
 
@@ -138,21 +140,22 @@ def test_phase1_rejects_overlapping_outputs():
     assert _rc_phase1(lse=FAKE + (2 << 30) + 64) == EINVAL
     assert _rc_phase1(o=FAKE + 8) == EINVAL
     assert _rc_phase1(h=FAKE + (2 << 30) + 16) == EINVAL
+    assert _rc_phase1(o_dtype=F16, scale=FAKE + (3 << 30) + 32) == EINVAL  # scale over lse
 
 
 def _rc_phase2(**kw):
-    a = dict(o=FAKE, o_dtype=F32, lse=FAKE + (1 << 30), partial=FAKE + (2 << 30), T=8, d=64,
+    a = dict(o=FAKE, o_dtype=F32, scale=None, lse=FAKE + (1 << 30), partial=FAKE + (2 << 30), T=8, d=64,
              w=FAKE + (3 << 30), gain=None, eps=1e-6, H=1, dtype=BF16, h=FAKE + (4 << 30))
     a.update(kw)
-    return binding.lib().attnres_block_phase2_merge(a["o"], a["o_dtype"], a["lse"], a["partial"], a["T"],
-                                                    a["d"], a["w"], a["gain"], a["eps"], a["H"],
+    return binding.lib().attnres_block_phase2_merge(a["o"], a["o_dtype"], a["scale"], a["lse"], a["partial"],
+                                                    a["T"], a["d"], a["w"], a["gain"], a["eps"], a["H"],
                                                     a["dtype"], a["h"], None)
 
 
 @fake_ptrs
 def test_phase2_rejects_bad_arguments():
     for c in [dict(o_dtype=3), dict(partial=None), dict(lse=None), dict(w=None), dict(h=None),
-              dict(H=7)]:
+              dict(H=7), dict(o_dtype=F16, scale=None), dict(o_dtype=F16, dtype=F32, scale=FAKE + (5 << 30))]:
         assert _rc_phase2(**c) == EINVAL, c
 
 
