@@ -334,6 +334,7 @@ def main():
             "unit": "GB/s",
             "frac": p1["gbs"] / PEAK_HBM_GBS,
             "traffic": traffic,
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "avg_us": p1["avg_us"],
             "algorithmic_bytes_per_launch": p1["bytes_per_launch"],
         },
