@@ -189,8 +189,10 @@ def bench_full(args, T=4096):
     L, d = wl.src.shape[0], wl.d
     del wl
     out = torch.empty((L, T, d), dtype=torch.bfloat16, device="cuda")
-    sec, wall = time_loop(lambda: ar.attnres_full_fwd(src, w, g, 1e-6, 1, out=out), max(3, args.steps // 4),
-                          2)
+    ws = torch.empty(max(1, ar.attnres_full_fwd_workspace_size(L, L, d, 1, ar.BF16)), dtype=torch.uint8,
+                     device="cuda")
+    sec, wall = time_loop(lambda: ar.attnres_full_fwd(src, w, g, 1e-6, 1, out=out, ws=ws),
+                          max(3, args.steps // 4), 2)
     n = max(3, args.steps // 4)
     b = full_bytes(T, d, L)
     return dict(name=f"full_bf16_T{T}_d{d}_L{L}", tokens_per_s=T * n / sec, ms_per_step=sec / n * 1e3,

@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     attnres_bwd,
     attnres_bwd_workspace_size,
     attnres_full_fwd,
+    attnres_full_fwd_workspace_size,
     attnres_last_error,
     attnres_set_kernel_policy,
     attnres_version,

@@ -39,7 +39,8 @@ def lib() -> ctypes.CDLL:
         raise ImportError(f"{LIB_PATH} is missing: build it with depth_wise_attention_amd/build.py")
     L = ctypes.CDLL(LIB_PATH)
     vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
-    L.attnres_full_fwd.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, f32, i32, i32, vp, vp]
+    L.attnres_full_fwd_workspace_size.argtypes = [i64, i64, i64, i32, i32]
+    L.attnres_full_fwd.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, f32, i32, i32, vp, vp, sz, vp]
     L.attnres_block_phase1.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, f32, i32, i32, vp, vp, i32, vp, vp,
                                        vp]
     L.attnres_block_phase2_merge.argtypes = [vp, i32, vp, vp, vp, i64, i64, vp, vp, f32, i32, i32, vp, vp]
@@ -52,6 +53,7 @@ def lib() -> ctypes.CDLL:
     for name in ("attnres_full_fwd", "attnres_block_phase1", "attnres_block_phase2_merge", "mhar_fwd",
                  "attnres_bwd", "attnres_version", "attnres_set_kernel_policy"):
         getattr(L, name).restype = ctypes.c_int
+    L.attnres_full_fwd_workspace_size.restype = sz
     L.mhar_fwd_workspace_size.restype = sz
     L.attnres_bwd_workspace_size.restype = sz
     L.attnres_last_error.restype = ctypes.c_char_p
@@ -74,6 +76,10 @@ def attnres_set_kernel_policy(policy: int) -> int:
     if rc < 0:
         raise AttnResError(rc, attnres_last_error())
     return rc
+
+
+def attnres_full_fwd_workspace_size(n_src: int, n_dst: int, d: int, H: int, dtype: int) -> int:
+    return lib().attnres_full_fwd_workspace_size(n_src, n_dst, d, H, dtype)
 
 
 def mhar_fwd_workspace_size(N: int, S: int, T: int, d: int, H: int) -> int:
@@ -99,6 +105,10 @@ def _code(t) -> int:
     if t.dtype == torch.float16:
         return F16
     raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 def _p(t) -> Optional[int]:
@@ -132,15 +142,19 @@ def _check(rc: int) -> None:
 
 
 # ----------------------------------------------------------------- entry points
-def attnres_full_fwd(src, w, gain=None, eps: float = 1e-6, H: int = 1, out=None, stream=None):
+def attnres_full_fwd(src, w, gain=None, eps: float = 1e-6, H: int = 1, out=None, ws=None, stream=None):
     """Full AttnRes forward.  src [n_src, T, d]; w [n_dst, d] -> out [n_dst, T, d]."""
+    torch = _torch()
     n_src, T, d = src.shape
     n_dst = w.shape[0]
     if out is None:
-        out = _torch().empty((n_dst, T, d), dtype=src.dtype, device=src.device)
+        out = torch.empty((n_dst, T, d), dtype=src.dtype, device=src.device)
+    need = attnres_full_fwd_workspace_size(n_src, n_dst, d, H, _code(src))
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=src.device)
     gp, gld = _gain(gain, n_dst, d)
     _check(lib().attnres_full_fwd(_p(src), n_src, T, d, _p(w), n_dst, gp, gld, eps, H, _code(src),
-                                  _p(out), _stream(stream)))
+                                  _p(out), _p(ws), _nbytes(ws), _stream(stream)))
     return out
 
 

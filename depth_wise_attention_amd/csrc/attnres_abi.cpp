@@ -156,16 +156,22 @@ extern "C" {
 
 const char* attnres_last_error(void) { return g_err; }
 
-int attnres_version(void) { return (1 << 16) | 0; }
+int attnres_version(void) { return (2 << 16) | 0; }
 
 int attnres_set_kernel_policy(int32_t policy) {
   if (policy != 0 && policy != 1) return fail(ATTNRES_ERR_INVALID, "unknown kernel policy %d", policy);
   return g_policy.exchange(policy);
 }
 
+size_t attnres_full_fwd_workspace_size(int64_t n_src, int64_t n_dst, int64_t d, int32_t H,
+                                       int32_t dtype) {
+  if (n_src < 1 || n_dst < 1 || n_dst > n_src || d < 1 || d > kMaxD || H < 1) return 0;
+  return full_fast_workspace_bytes(n_src, n_dst, d, H, dtype);
+}
+
 int attnres_full_fwd(const void* src, int64_t n_src, int64_t T, int64_t d, const float* w,
                      int64_t n_dst, const float* gain, int64_t gain_ld, float eps, int32_t H,
-                     int32_t dtype, void* out, hipStream_t stream) {
+                     int32_t dtype, void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
   clear_error();
   int64_t td = 0;
   RETURN_IF(check_common(T, d, H, dtype, eps, gain, gain_ld, &td));
@@ -185,10 +191,15 @@ int attnres_full_fwd(const void* src, int64_t n_src, int64_t T, int64_t d, const
   const Range ins[] = {{src, b_src, "src"},
                        {w, (size_t)(n_dst * d * 4), "w"},
                        {gain, gain ? (size_t)((gain_ld ? n_dst : 1) * d * 4) : 0, "gain"}};
-  const Range outs[] = {{out, b_out, "out"}};
-  RETURN_IF(check_aliasing(ins, 3, outs, 1));
+  const size_t need = attnres_full_fwd_workspace_size(n_src, n_dst, d, H, dtype);
+  if (need > 0 && (ws == nullptr || ws_bytes < need))
+    return fail(ATTNRES_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? ws_bytes : 0,
+                need);
+  const Range outs[] = {{out, b_out, "out"}, {need > 0 ? ws : nullptr, need, "ws"}};
+  RETURN_IF(check_aliasing(ins, 3, outs, 2));
 
-  FullArgs a{src, n_src, T, d, w, n_dst, gain, gain ? gain_ld : 0, eps, H, dtype, out};
+  FullArgs a{src, n_src, T, d, w, n_dst, gain, gain ? gain_ld : 0, eps, H, dtype, out,
+             need > 0 ? ws : nullptr, need};
   const hipError_t e = (use_fast() && full_fast_ok(a)) ? launch_full_fast(a, stream)
                                                        : launch_full_generic(a, stream);
   return e == hipSuccess ? ATTNRES_OK : hip_fail(e, "full forward launch");

@@ -25,6 +25,8 @@ struct FullArgs {
   int H;
   int dtype;
   void* out;
+  void* ws;  // scratch for the specialised kernel (may be null)
+  size_t ws_bytes;
 };
 
 // Phase 1: layer 0 is written to o0 (o0_dtype), layers 1..S-1 to
@@ -102,6 +104,7 @@ bool phase1_fast_ok(const Phase1Args& a);
 bool phase2_fast_ok(const Phase2Args& a);
 bool bwd_fast_ok(const BwdArgs& a);
 bool full_fast_ok(const FullArgs& a);
+size_t full_fast_workspace_bytes(int64_t n_src, int64_t n_dst, int64_t d, int H, int dtype);
 hipError_t launch_phase1_fast(const Phase1Args& a, hipStream_t st);
 hipError_t launch_phase2_fast(const Phase2Args& a, hipStream_t st);
 hipError_t launch_bwd_fast(const BwdArgs& a, int64_t* slots_used, hipStream_t st);

@@ -74,13 +74,26 @@ extern "C" {
  *  gain  see conventions (per-destination rows of length d, shared, or NULL)
  *  out   [n_dst, T, d] dtype   out[j] reads sources 0 .. n_src - n_dst + j
  *
+ *  ws    device workspace of at least attnres_full_fwd_workspace_size() bytes
+ *        (may be NULL when that size is 0); its contents are scratch
+ *
  * With n_dst == n_src == L, destination l = j + 1 reads v_0 .. v_{l-1}; with
  * n_dst == 1 it is the single call a model makes per sublayer.
  * Requires 1 <= n_dst <= n_src <= 64.
  */
 int attnres_full_fwd(const void* src, int64_t n_src, int64_t T, int64_t d,
                      const float* w, int64_t n_dst, const float* gain, int64_t gain_ld,
-                     float eps, int32_t H, int32_t dtype, void* out, hipStream_t stream);
+                     float eps, int32_t H, int32_t dtype, void* out, void* ws,
+                     size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Bytes of device workspace attnres_full_fwd needs.  Single-head bf16 calls
+ * with n_src <= 32 may run the score contraction on the matrix cores, which
+ * takes q = w * gain as a bf16 high part plus a bf16 low part ([2, 32, d]
+ * bf16, 128 * d bytes); every other request needs none and gets 0.
+ */
+size_t attnres_full_fwd_workspace_size(int64_t n_src, int64_t n_dst, int64_t d, int32_t H,
+                                       int32_t dtype);
 
 /*
  * Block AttnRes, Phase 1 of two-phase inference (b-lab.team summary §3,
@@ -190,7 +203,7 @@ int attnres_bwd(const void* reps, int64_t N, const void* partials, int64_t S, in
 /* Thread-local message for the last failing call on this thread ("" if none). */
 const char* attnres_last_error(void);
 
-/* ABI version: (major << 16) | minor. */
+/* ABI version: (major << 16) | minor.  Major 2 added the Full-forward workspace. */
 int attnres_version(void);
 
 /*

@@ -39,7 +39,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("attnres_full_fwd", "attnres_block_phase1", "attnres_block_phase2_merge", "mhar_fwd",
-                 "attnres_bwd", "mhar_fwd_workspace_size", "attnres_bwd_workspace_size",
+                 "attnres_bwd", "attnres_full_fwd_workspace_size", "mhar_fwd_workspace_size", "attnres_bwd_workspace_size",
                  "attnres_last_error", "attnres_version", "attnres_set_kernel_policy"):
         assert want in names
 
@@ -51,7 +51,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_policy():
-    assert binding.attnres_version() >> 16 == 1
+    assert binding.attnres_version() >> 16 == 2
     prev = binding.attnres_set_kernel_policy(1)
     assert binding.attnres_set_kernel_policy(prev) == 1
     with pytest.raises(binding.AttnResError):
@@ -73,11 +73,34 @@ def test_workspace_sizes():
 
 def _rc_full(**kw):
     a = dict(src=FAKE, n_src=4, T=8, d=16, w=FAKE + (1 << 30), n_dst=4, gain=None, gain_ld=0, eps=1e-6,
-             H=1, dtype=BF16, out=FAKE + (2 << 30), stream=None)
+             H=1, dtype=BF16, out=FAKE + (2 << 30), ws=FAKE + (5 << 30), ws_bytes=1 << 20, stream=None)
     a.update(kw)
     L = binding.lib()
     return L.attnres_full_fwd(a["src"], a["n_src"], a["T"], a["d"], a["w"], a["n_dst"], a["gain"],
-                              a["gain_ld"], a["eps"], a["H"], a["dtype"], a["out"], a["stream"])
+                              a["gain_ld"], a["eps"], a["H"], a["dtype"], a["out"], a["ws"], a["ws_bytes"],
+                              a["stream"])
+
+
+def test_full_workspace_size():
+    # bf16, one head, at most 32 sources: q = w * gain as two bf16 parts, [2, 32, d].
+    assert binding.attnres_full_fwd_workspace_size(32, 32, 2048, 1, BF16) == 2 * 32 * 2048 * 2
+    assert binding.attnres_full_fwd_workspace_size(8, 1, 4096, 1, BF16) == 2 * 32 * 4096 * 2
+    for args in [(32, 32, 2048, 1, F32), (33, 1, 2048, 1, BF16), (8, 8, 2048, 2, BF16), (4, 5, 64, 1, BF16),
+                 (0, 0, 64, 1, BF16), (4, 4, 0, 1, BF16)]:
+        assert binding.attnres_full_fwd_workspace_size(*args) == 0, args
+
+
+@fake_ptrs
+def test_full_workspace_checks():
+    assert _rc_full(ws=None) == EWS
+    assert "workspace" in binding.attnres_last_error()
+    assert _rc_full(ws_bytes=2 * 32 * 16 * 2 - 1) == EWS
+    # The workspace is an output: it may not overlap the sources (checked before any launch).
+    assert _rc_full(ws=FAKE + 64) == EINVAL
+    assert "overlaps" in binding.attnres_last_error()
+    # fp32 needs none: a NULL workspace passes the workspace check (aliased output rejects the call).
+    assert _rc_full(dtype=F32, ws=None, out=FAKE + 16) == EINVAL
+    assert "overlaps" in binding.attnres_last_error()
 
 
 @fake_ptrs

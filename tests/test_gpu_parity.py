@@ -97,6 +97,13 @@ def test_full_fp32_config(policy):
     (9, 2048, 32, 32, 4, "bf16", "none"),
     (1, 16, 64, 2, 1, "f32", "none"),
     (33, 1000, 3, 3, 5, "bf16", "per"),
+    # single-head bf16 with n_src <= 32 and d % 256 == 0: the matrix-core kernel under "auto"
+    (67, 256, 32, 32, 1, "bf16", "per"),
+    (300, 512, 32, 1, 1, "bf16", "shared"),
+    (45, 4096, 17, 9, 1, "bf16", "none"),
+    (3, 768, 1, 1, 1, "bf16", "per"),
+    (513, 2304, 32, 32, 1, "bf16", "per"),
+    (20, 256, 33, 33, 1, "bf16", "per"),
 ])
 def test_full_shapes(T, d, L, n_dst, H, dtype, gain, policy):
     say(f"full T={T} d={d} L={L} n_dst={n_dst} H={H} {dtype} gain={gain} policy={policy}")
@@ -106,6 +113,20 @@ def test_full_shapes(T, d, L, n_dst, H, dtype, gain, policy):
     ref = orc.full_fwd(wl.src, wl.w, g, wl.eps, H)
     out = ar.attnres_full_fwd(dev(wl.src, dtype), dev(wl.w), dev(g), wl.eps, H)
     check(host(out), ref, dtype, "full")
+
+
+def test_full_workspace_reuse(policy):
+    """One caller-owned workspace across calls with different queries and destination counts."""
+    say(f"full workspace reuse T=96 d=1024 L=24 policy={policy}")
+    ws = torch.empty(ar.attnres_full_fwd_workspace_size(24, 24, 1024, 1, ar.BF16), dtype=torch.uint8,
+                     device=DEV)
+    assert ws.numel() == 2 * 32 * 1024 * 2
+    for seed, n_dst in ((5, 24), (6, 7)):
+        wl = synth.full_workload(T=96, d=1024, L=24, std_step=0.2, dtype="bf16", seed=seed,
+                                 gain_variance=0.02, n_dst=n_dst)
+        ref = orc.full_fwd(wl.src, wl.w, wl.gain, wl.eps, 1)
+        out = ar.attnres_full_fwd(dev(wl.src, "bf16"), dev(wl.w), dev(wl.gain), wl.eps, 1, ws=ws)
+        check(host(out), ref, "bf16", f"full ws reuse n_dst={n_dst}")
 
 
 def test_full_bf16_config_sampled():
