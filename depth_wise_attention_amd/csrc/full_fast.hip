@@ -1,20 +1,29 @@
 // Specialised Full AttnRes forward for gfx950 (bf16 I/O, H = 1, up to 32
 // sources and destinations).
 //
-// Per token the routing is a dense contraction: scores S[j][i] = q_j . v_i over
-// d channels for up to 32 x 32 (destination, source) pairs (b-lab.team summary
-// §1: O(L^2 d) per token).  That part runs on the matrix cores:
-// v_mfma_f32_32x32x16_bf16 with A = q (split into bf16 hi + lo parts, so the
-// product carries about 16 significant bits of q) and B = the token's sources,
-// read straight from HBM in the MFMA operand layout.  The same source registers
-// also give G = V V^T, whose diagonal is each source's sum of squares.
-//
+// Per token the routing is two dense contractions (b-lab.team summary §1:
+// O(L^2 d) per token), and both run on the matrix cores with
+// v_mfma_f32_32x32x16_bf16:
+//   stage 1  S = Q V^T (32 destinations x 32 sources over d channels), with
+//            q = w * g split into bf16 high + low parts so the product keeps
+//            about 16 significant bits of q; G = V V^T on the same operands
+//            gives each source's sum of squares on its diagonal;
+//   stage 2  H = alpha V, with alpha split the same way.
 // A workgroup of 4 waves owns one token at a time; wave w covers channels
-// [w d/4, (w+1) d/4).  The four partial S tiles and diag(G) are summed through
-// LDS, the causal softmax runs 8 threads per destination (4 sources each), and
-// alpha^T goes to LDS.  The weighted sums h_j = sum_i alpha_ji v_i then run on
-// the vector ALUs, one thread per 8 channels and 8 destinations at a time,
-// reading the sources a second time (from cache) channel-contiguously.
+// [w d/4, (w+1) d/4) in chunks of 64.
+//
+// Operand staging.  Each chunk of the token's sources (32 rows x 128 bytes)
+// is read with coalesced 16-byte loads (8 whole rows per wave instruction) and
+// written to a per-wave LDS tile whose 16-byte pieces are XOR-swizzled by row,
+// so the MFMA operand reads (one row per lane) hit distinct banks.  The query
+// parts are packed once per call in exact operand-register order, so each
+// lane's 16 bytes of a k-step are one contiguous 1 KiB block per wave.
+//
+// Stage 2 needs the sources with the source index inside a lane (the
+// contraction dimension); the staged operands have one source per lane.  An
+// MFMA against an identity matrix moves the channel index into the lanes
+// (exact: every output is one bf16 value times 1).  Outputs are staged through
+// a second LDS tile and written as whole rows with 16-byte stores.
 #include <math.h>
 
 #include "common.hpp"
@@ -25,91 +34,193 @@ namespace {
 
 typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
 typedef float f16acc __attribute__((ext_vector_type(16)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
-constexpr int kFW = 4;          // waves per workgroup
-constexpr int kFB = kFW * 64;   // threads per workgroup
-constexpr int kTile = 32;       // MFMA tile: 32 destinations x 32 sources
+constexpr int kFW = 4;            // waves per workgroup
+constexpr int kFB = kFW * 64;     // threads per workgroup
+constexpr int kTile = 32;         // MFMA tile: 32 destinations x 32 sources
+constexpr int kChunk = 64;        // channels per staged chunk
+constexpr int kVRow = 128;        // bytes per staged source row (64 bf16)
+constexpr int kORow = 160;        // bytes per staged output row (64 bf16 + pad)
+constexpr int kARow = 36;         // floats per alpha row (32 + pad, 16-byte aligned)
 
 __device__ __forceinline__ bf8v as_bf8(uint4 u) { return __builtin_bit_cast(bf8v, u); }
 
-// q = w * g split into bf16 hi + lo parts, rows padded to 32 with zeros:
-// qhi/qlo [32][d].
-__global__ __launch_bounds__(256) void k_full_qsplit(FullArgs a, bf16_t* qhi, bf16_t* qlo) {
-  const int64_t n = (int64_t)kTile * a.d;
-  for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < n; x += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t j = x / a.d, k = x % a.d;
-    float q = 0.f;
-    if (j < a.n_dst) {
-      q = a.w[j * a.d + k];
-      if (a.gain) q *= a.gain[j * a.gain_ld + k];
+__device__ __forceinline__ f16acc mfma(uint4 a, uint4 b, f16acc c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(a), as_bf8(b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint4 pack8(float a0, float a1, float a2, float a3, float a4, float a5, float a6,
+                                       float a7) {
+  return make_uint4(pack_bf2(a0, a1), pack_bf2(a2, a3), pack_bf2(a4, a5), pack_bf2(a6, a7));
+}
+
+// Packs q = w * g into MFMA A-operand order: for chunk g (64 channels), k-step
+// s (16 channels) and part (0 = bf16 high, 1 = low), lane l's 8 values are
+// q_part[l % 32][64 g + 16 s + 8 (l / 32) + e], stored at
+// qpk[((g * 4 + s) * 2 + part) * 512 + l * 8 + e].  Rows past n_dst are zero.
+__global__ __launch_bounds__(256) void k_full_qsplit(FullArgs a, bf16_t* qpk) {
+  const int64_t units = a.d / kChunk * 4 * 64;  // (g, s, lane) triples
+  for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < units;
+       x += (int64_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(x % 64);
+    const int64_t gs = x / 64;  // g * 4 + s
+    const int j = lane % 32;
+    const int64_t k0 = gs * 16 + 8 * (lane / 32);
+    float hi[8], lo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float q = 0.f;
+      if (j < a.n_dst) {
+        q = a.w[j * a.d + k0 + e];
+        if (a.gain) q *= a.gain[j * a.gain_ld + k0 + e];
+      }
+      hi[e] = bf2f(f2bf(q));
+      lo[e] = q - hi[e];
     }
-    const bf16_t h = f2bf(q);
-    qhi[x] = h;
-    qlo[x] = f2bf(q - bf2f(h));
+    uint4* dst = reinterpret_cast<uint4*>(qpk) + gs * 2 * 64 + lane;
+    dst[0] = pack8(hi[0], hi[1], hi[2], hi[3], hi[4], hi[5], hi[6], hi[7]);
+    dst[64] = pack8(lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]);
   }
 }
 
-__global__ __launch_bounds__(kFB, 2) void k_full_fast(FullArgs a, const bf16_t* qhi, const bf16_t* qlo) {
-  __shared__ float sred[kFW][kTile * kTile];          // per-wave partial S
-  __shared__ float gred[kFW][kTile];                   // per-wave partial diag(G)
-  __shared__ __align__(16) float alphaT[kTile][kTile];  // alpha^T[i][j]
+struct FullSmem {
+  float sred[kFW][kTile * kTile];                   // per-wave partial S[j][i]
+  float gred[kFW][kTile];                           // per-wave partial sum of squares
+  __attribute__((aligned(16))) float alpha[kTile][kARow];  // alpha[j][i]
+  __attribute__((aligned(16))) unsigned char vtile[kFW][kTile * kVRow];
+  __attribute__((aligned(16))) unsigned char otile[kFW][kTile * kORow];
+};
+
+// Coalesced load of one 64-channel chunk of the token's sources: instruction u
+// of lane l reads row 8u + l/8, 16-byte piece l%8.  The loads carry no branch
+// (rows >= n_src point at row 0 and are zeroed when staged), so the wait
+// counters stay exact and a chunk's loads overlap the work on earlier chunks.
+__device__ __forceinline__ void load_chunk(const bf16_t* const rowp[4], int ch, uint4 v[4]) {
+  const int piece = lane_id() & 7;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const uint4*>(rowp[u] + ch + 8 * piece);
+}
+
+// Swizzled position of (row, 16-byte piece) in a staged source tile.
+__device__ __forceinline__ int vpos(int row, int piece) { return row * kVRow + ((piece ^ (row & 7)) << 4); }
+
+// Rows 8u + l/8 share the swizzle of row l/8, so one per-lane base serves all
+// four writes (constant offsets u * 1 KiB).
+// rowmask[u] is all ones for a real source row and zero past n_src (a mask, not
+// a select, so no branch splits the wait for the loads).
+__device__ __forceinline__ void stage_chunk(unsigned char* tile, const uint4 v[4], const uint32_t rowmask[4]) {
+  const int lane = lane_id();
+  unsigned char* base = tile + vpos(lane >> 3, lane & 7);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint32_t m = rowmask[u];
+    *reinterpret_cast<uint4*>(base + u * 8 * kVRow) = make_uint4(v[u].x & m, v[u].y & m, v[u].z & m, v[u].w & m);
+  }
+}
+
+// Operand of k-step s (channels 16 s .. 16 s + 15 of the chunk): lane l holds
+// row l % 32, channels 16 s + 8 (l / 32) .. + 7.
+__device__ __forceinline__ uint4 tile_operand(const unsigned char* tile, int s) {
+  const int lane = lane_id();
+  return *reinterpret_cast<const uint4*>(tile + vpos(lane & 31, 2 * s + (lane >> 5)));
+}
+
+__global__ __launch_bounds__(kFB, 2) void k_full_fast(FullArgs a, const bf16_t* qpk) {
+  __shared__ FullSmem sm;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int d = (int)a.d, n_src = (int)a.n_src, n_dst = (int)a.n_dst;
-  const int64_t T = a.T, Td = a.T * a.d;
+  const int64_t T = a.T;
   const bf16_t* src = static_cast<const bf16_t*>(a.src);
   bf16_t* out = static_cast<bf16_t*>(a.out);
-  const int kw = d / kFW;             // channels per wave (multiple of 64)
-  const int row = lane % 32;          // MFMA row (destination j for A, source i for B)
-  const int kofs = 8 * (lane / 32);   // 8-channel half of each 16-channel step
-  const bool src_ok = row < n_src;
+  const int kw = d / kFW;                  // channels per wave
+  const int nch = kw / kChunk;             // chunks per wave
+  const int ch_base = wave * kw;
+  unsigned char* vt = sm.vtile[wave];
+  unsigned char* ot = sm.otile[wave];
+  const int h = lane >> 5;                 // MFMA half (k offset 8)
+  const int n = lane & 31;                 // MFMA column
+  const uint4* qv = reinterpret_cast<const uint4*>(qpk) + lane;
+
+  // Identity operands for the transpose: I_a[k][n] = 1 when 16 a + k == n,
+  // with k = 8 h + e held by lane (h, n).
+  uint4 ident[2];
+#pragma unroll
+  for (int a2 = 0; a2 < 2; ++a2) {
+    uint32_t wds[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e0 = 2 * q, e1 = 2 * q + 1;
+      const uint32_t lo16 = (16 * a2 + 8 * h + e0 == n) ? 0x3F80u : 0u;
+      const uint32_t hi16 = (16 * a2 + 8 * h + e1 == n) ? 0x3F80u : 0u;
+      wds[q] = lo16 | (hi16 << 16);
+    }
+    ident[a2] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+  }
 
   for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    const bf16_t* rowp[4];
+    uint32_t rowmask[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = 8 * u + (lane >> 3);
+      rowmask[u] = r < n_src ? 0xFFFFFFFFu : 0u;
+      rowp[u] = src + ((int64_t)(r < n_src ? r : 0) * T + t) * d + ch_base;
+    }
+
     // ---------------- stage 1: S = Q V^T and G = V V^T over this wave's channels
-    // Operands for step k0 + 64 are loaded while step k0 runs on the matrix cores.
+    // Two chunks of sources are in flight while one is consumed (ping-pong
+    // buffers, no register copies of loads in flight); the query operands of a
+    // chunk come from L2 and are loaded when its turn comes.
     f16acc S = {}, G = {};
-    const bf16_t* vrow = src + ((int64_t)(src_ok ? row : 0) * T + t) * d + wave * kw + kofs;
-    const bf16_t* qh = qhi + (int64_t)row * d + wave * kw + kofs;
-    const bf16_t* ql = qlo + (int64_t)row * d + wave * kw + kofs;
-    uint4 vb[4], ah[4], al[4];
-    auto load_step = [&](int k0, uint4* v, uint4* h, uint4* l) {
+    {
+      auto chunk1 = [&](int c, uint4 (&v)[4]) {
+        const uint4* qc = qv + (int64_t)(ch_base / kChunk + c) * 8 * 64;
+        uint4 q[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        v[u] = src_ok ? *reinterpret_cast<const uint4*>(vrow + k0 + 16 * u) : make_uint4(0, 0, 0, 0);
-        h[u] = *reinterpret_cast<const uint4*>(qh + k0 + 16 * u);
-        l[u] = *reinterpret_cast<const uint4*>(ql + k0 + 16 * u);
-      }
-    };
-    load_step(0, vb, ah, al);
-    for (int k0 = 0; k0 < kw; k0 += 64) {
-      uint4 vn[4], hn[4], ln[4];
-      if (k0 + 64 < kw) load_step(k0 + 64, vn, hn, ln);
+        for (int k = 0; k < 8; ++k) q[k] = qc[k * 64];
+        stage_chunk(vt, v, rowmask);
+        load_chunk(rowp, min(c + 2, nch - 1) * kChunk, v);  // unconditional: exact wait counts
+        wave_lds_sync();
+        uint4 b[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(ah[u]), as_bf8(vb[u]), S, 0, 0, 0);
-        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(al[u]), as_bf8(vb[u]), S, 0, 0, 0);
-        G = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(vb[u]), as_bf8(vb[u]), G, 0, 0, 0);
-      }
+        for (int s = 0; s < 4; ++s) b[s] = tile_operand(vt, s);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        vb[u] = vn[u];
-        ah[u] = hn[u];
-        al[u] = ln[u];
+        for (int s = 0; s < 4; ++s) {
+          S = mfma(q[2 * s], b[s], S);
+          S = mfma(q[2 * s + 1], b[s], S);
+          G = mfma(b[s], b[s], G);
+        }
+        wave_lds_sync();  // operand reads done before the tile is rewritten
+      };
+      uint4 va[4], vb[4];
+      load_chunk(rowp, 0, va);
+      __builtin_amdgcn_sched_barrier(0);  // keep the loop's load order (va, then vb)
+      load_chunk(rowp, kChunk, vb);
+      // nch is even and >= 2.  The first pair is peeled so that the loop head
+      // sees the same outstanding loads and stores on entry as on the back edge
+      // (the wait counts are then exact, not the minimum over both paths).
+      chunk1(0, va);
+      chunk1(1, vb);
+      for (int c = 2; c < nch; c += 2) {
+        chunk1(c, va);
+        chunk1(c + 1, vb);
       }
     }
-    // D layout: element r of lane l is D[8*(r/4) + 4*(l/32) + r%4][l%32].
+    // D layout: element r of lane l is D[8 (r/4) + 4 (l/32) + r%4][l%32].
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int m = 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
-      sred[wave][m * kTile + row] = S[r];
-      if (m == row) gred[wave][row] = G[r];
+      const int m = 8 * (r / 4) + 4 * h + (r % 4);
+      sm.sred[wave][m * kTile + n] = S[r];
+      if (m == n) sm.gred[wave][n] = G[r];
     }
     __syncthreads();
 
-    // ---------------- softmax: thread -> destination j = tid / 8, sources 4*(tid % 8) .. +4
+    // ---------------- softmax: thread -> destination j = tid / 8, sources 4 (tid % 8) .. + 3
     {
       const int j = tid / 8, i0 = 4 * (tid % 8);
       const int lim = n_src - n_dst + j;  // destination j reads sources 0..lim
-      float s[4];
+      float sc[4];
       float m = -INFINITY;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -117,83 +228,105 @@ __global__ __launch_bounds__(kFB, 2) void k_full_fast(FullArgs a, const bf16_t* 
         float sv = 0.f, gv = 0.f;
 #pragma unroll
         for (int w2 = 0; w2 < kFW; ++w2) {
-          sv += sred[w2][j * kTile + i];
-          gv += gred[w2][i];
+          sv += sm.sred[w2][j * kTile + i];
+          gv += sm.gred[w2][i];
         }
         const float r = 1.0f / sqrtf(gv / (float)d + a.eps);
-        s[q] = (j < n_dst && i <= lim) ? r * sv : -INFINITY;
-        m = fmaxf(m, s[q]);
+        sc[q] = (j < n_dst && i <= lim) ? r * sv : -INFINITY;
+        m = fmaxf(m, sc[q]);
       }
 #pragma unroll
       for (int off = 1; off < 8; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
       float e[4], l = 0.f;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        e[q] = (s[q] == -INFINITY) ? 0.f : expf(s[q] - m);
+        e[q] = (sc[q] == -INFINITY) ? 0.f : expf(sc[q] - m);
         l += e[q];
       }
 #pragma unroll
       for (int off = 1; off < 8; off <<= 1) l += __shfl_xor(l, off, kWave);
       const float inv = l > 0.f ? 1.0f / l : 0.f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) alphaT[i0 + q][j] = e[q] * inv;
+      *reinterpret_cast<float4*>(&sm.alpha[j][i0]) = make_float4(e[0] * inv, e[1] * inv, e[2] * inv, e[3] * inv);
     }
     __syncthreads();
 
-    // ---------------- stage 2: h_j = sum_i alpha_ji v_i, 4 channels per thread.
-    // All source rows of the thread's channels are loaded first (one pass over
-    // the sources), then destinations are produced 8 at a time from registers.
-    // Row bases are wave-uniform; the per-thread offset t*d + col fits 32 bits.
-    for (int col = tid * 4; col < d; col += kFB * 4) {
-      const uint32_t voff = (uint32_t)t * (uint32_t)d + (uint32_t)col;
-      uint2 vv[kTile];
-      int64_t step = Td;
-      asm volatile("" : "+s"(step));  // keeps 32 row offsets from being precomputed and held
-      const bf16_t* rp = src + voff;
+    // ---------------- stage 2: H = alpha V
+    // A operands: lane (h, j = l%32) holds alpha_part[j][src(b, h, e)] with
+    // src(b, h, e) = 16 b + 8 (e/4) + 4 h + e%4, the source order the
+    // transpose leaves in the B operand.
+    uint4 ahi[2], alo[2];
 #pragma unroll
-      for (int i = 0; i < kTile; ++i) {
-        vv[i] = i < n_src ? *reinterpret_cast<const uint2*>(rp) : make_uint2(0, 0);
-        rp += step;
+    for (int b2 = 0; b2 < 2; ++b2) {
+      const float4 x0 = *reinterpret_cast<const float4*>(&sm.alpha[n][16 * b2 + 4 * h]);
+      const float4 x1 = *reinterpret_cast<const float4*>(&sm.alpha[n][16 * b2 + 8 + 4 * h]);
+      const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      float hi[8], lo[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        hi[e] = bf2f(f2bf(x[e]));
+        lo[e] = x[e] - hi[e];
       }
-      for (int jb = 0; jb < n_dst; jb += 8) {
-        const int i_end = min(n_src, n_src - n_dst + jb + 8);  // sources any of j in [jb, jb+8) reads
-        // Keep the rows packed: without this the unpacked fp32 copies of all
-        // rows are hoisted out of the jb loop (twice the registers).
+      ahi[b2] = pack8(hi[0], hi[1], hi[2], hi[3], hi[4], hi[5], hi[6], hi[7]);
+      alo[b2] = pack8(lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]);
+    }
+    {
+      // Output tile addresses: row j = 8 (r/4) + 4 h + r%4 and channel 32 half + n
+      // are one per-lane base plus compile-time offsets.
+      unsigned char* obase = ot + 4 * h * kORow + 2 * n;
+      auto chunk2 = [&](int c, uint4 (&v)[4]) {
+        stage_chunk(vt, v, rowmask);
+        load_chunk(rowp, min(c + 2, nch - 1) * kChunk, v);
+        wave_lds_sync();
+        uint4 op[4];
 #pragma unroll
-        for (int i = 0; i < kTile; ++i) asm volatile("" : "+v"(vv[i].x), "+v"(vv[i].y));
-        float acc[8][4];
+        for (int s = 0; s < 4; ++s) op[s] = tile_operand(vt, s);
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
+        for (int half = 0; half < 2; ++half) {
+          // D1[i][n'] = V[i][32 half + n']: lane (h, n') element r holds source 8 (r/4) + 4 h + r%4.
+          f16acc D1 = {};
+          D1 = mfma(op[2 * half], ident[0], D1);
+          D1 = mfma(op[2 * half + 1], ident[1], D1);
+          const uint4 b0 = pack8(D1[0], D1[1], D1[2], D1[3], D1[4], D1[5], D1[6], D1[7]);
+          const uint4 b1 = pack8(D1[8], D1[9], D1[10], D1[11], D1[12], D1[13], D1[14], D1[15]);
+          f16acc D2 = {};
+          D2 = mfma(ahi[0], b0, D2);
+          D2 = mfma(alo[0], b0, D2);
+          D2 = mfma(ahi[1], b1, D2);
+          D2 = mfma(alo[1], b1, D2);
+          // D2[j][n'] -> output tile row j, channel 32 half + n'.
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[jj][e] = 0.f;
-#pragma unroll
-        for (int i = 0; i < kTile; ++i) {
-          if (i < i_end) {
-            const float x[4] = {bf_lo(vv[i].x), bf_hi(vv[i].x), bf_lo(vv[i].y), bf_hi(vv[i].y)};
-            const float4 a0 = *reinterpret_cast<const float4*>(&alphaT[i][jb]);
-            const float4 a1 = *reinterpret_cast<const float4*>(&alphaT[i][jb + 4]);
-            const float al[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) acc[jj][e] = fmaf(al[jj], x[e], acc[jj][e]);
-          }
+          for (int r = 0; r < 16; ++r)
+            *reinterpret_cast<bf16_t*>(obase + (8 * (r / 4) + (r % 4)) * kORow + 64 * half) = f2bf(D2[r]);
         }
+        wave_lds_sync();
+        const int ch = ch_base + c * kChunk + 8 * (lane & 7);
+        // Rows past n_dst store row n_dst - 1 again (identical bytes), so the
+        // stores need no branch.
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int j = jb + jj;
-          if (j < n_dst) {
-            uint2 o;
-            o.x = pack_bf2(acc[jj][0], acc[jj][1]);
-            o.y = pack_bf2(acc[jj][2], acc[jj][3]);
-            *reinterpret_cast<uint2*>(out + (int64_t)j * Td + voff) = o;
-          }
+        for (int u = 0; u < 4; ++u) {
+          const int j = min(8 * u + (lane >> 3), n_dst - 1);
+          const uint4 o = *reinterpret_cast<const uint4*>(ot + j * kORow + ((lane & 7) << 4));
+          __builtin_nontemporal_store(v4u{o.x, o.y, o.z, o.w}, reinterpret_cast<v4u*>(out + ((int64_t)j * T + t) * d + ch));
         }
+        wave_lds_sync();  // tiles are rewritten by the next chunk
+      };
+      uint4 va[4], vb[4];
+      load_chunk(rowp, 0, va);
+      __builtin_amdgcn_sched_barrier(0);  // keep the loop's load order (va, then vb)
+      load_chunk(rowp, kChunk, vb);
+      // nch is even and >= 2.  The first pair is peeled so that the loop head
+      // sees the same outstanding loads and stores on entry as on the back edge
+      // (the wait counts are then exact, not the minimum over both paths).
+      chunk2(0, va);
+      chunk2(1, vb);
+      for (int c = 2; c < nch; c += 2) {
+        chunk2(c, va);
+        chunk2(c + 1, vb);
       }
     }
     // No barrier needed here: the next token writes sred/gred only after every
     // thread passed this token's second barrier (all softmax reads done), and
-    // alphaT only after its own first barrier (all stage-2 reads done).
+    // alpha only after its own first barrier (all operand reads done).
   }
 }
 
@@ -209,27 +342,23 @@ size_t full_fast_workspace_bytes(int64_t n_src, int64_t n_dst, int64_t d, int H,
 bool full_fast_ok(const FullArgs& a) {
   if (a.dtype != kBF16 || a.H != 1 || a.T < 1) return false;
   if (a.n_src > kTile || a.n_dst > a.n_src) return false;
-  // Stage 1 steps 64 channels per wave; stage 2 moves 4 channels per thread
-  // and addresses a source row with a 32-bit offset.
-  if (a.d % (kFW * 64) != 0 || a.d > ((int64_t)1 << 16)) return false;
-  if (a.T > (((int64_t)1 << 31) - 1) / a.d) return false;
+  // Each wave streams an even number of whole 64-channel chunks.
+  if (a.d % (2 * kFW * kChunk) != 0 || a.d > ((int64_t)1 << 16)) return false;
   const size_t need = full_fast_workspace_bytes(a.n_src, a.n_dst, a.d, a.H, a.dtype);
   if (a.ws == nullptr || a.ws_bytes < need) return false;
   return al16(a.src) && al16(a.out) && al16(a.ws);
 }
 
 hipError_t launch_full_fast(const FullArgs& a, hipStream_t st) {
-  bf16_t* qhi = static_cast<bf16_t*>(a.ws);
-  bf16_t* qlo = qhi + (size_t)kTile * a.d;
-  hipLaunchKernelGGL(k_full_qsplit, dim3(64), dim3(256), 0, st, a, qhi, qlo);
+  bf16_t* qpk = static_cast<bf16_t*>(a.ws);
+  hipLaunchKernelGGL(k_full_qsplit, dim3(64), dim3(256), 0, st, a, qpk);
   int per_cu = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_full_fast, kFB, 0);
   if (e != hipSuccess) return e;
   if (per_cu < 1) per_cu = 1;
   int64_t grid = (int64_t)num_cus() * per_cu;
   if (grid > a.T) grid = a.T;
-  hipLaunchKernelGGL(k_full_fast, dim3((unsigned)grid), dim3(kFB), 0, st, a, (const bf16_t*)qhi,
-                     (const bf16_t*)qlo);
+  hipLaunchKernelGGL(k_full_fast, dim3((unsigned)grid), dim3(kFB), 0, st, a, (const bf16_t*)qpk);
   return hipGetLastError();
 }
 

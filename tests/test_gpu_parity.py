@@ -97,13 +97,14 @@ def test_full_fp32_config(policy):
     (9, 2048, 32, 32, 4, "bf16", "none"),
     (1, 16, 64, 2, 1, "f32", "none"),
     (33, 1000, 3, 3, 5, "bf16", "per"),
-    # single-head bf16 with n_src <= 32 and d % 256 == 0: the matrix-core kernel under "auto"
-    (67, 256, 32, 32, 1, "bf16", "per"),
-    (300, 512, 32, 1, 1, "bf16", "shared"),
+    # single-head bf16 with n_src <= 32 and d % 512 == 0: the matrix-core kernel under "auto"
+    (67, 512, 32, 32, 1, "bf16", "per"),
+    (300, 1024, 32, 1, 1, "bf16", "shared"),
     (45, 4096, 17, 9, 1, "bf16", "none"),
-    (3, 768, 1, 1, 1, "bf16", "per"),
-    (513, 2304, 32, 32, 1, "bf16", "per"),
-    (20, 256, 33, 33, 1, "bf16", "per"),
+    (3, 1536, 1, 1, 1, "bf16", "per"),
+    (513, 2560, 32, 32, 1, "bf16", "per"),
+    (20, 512, 33, 33, 1, "bf16", "per"),
+    (11, 768, 32, 32, 1, "bf16", "per"),
 ])
 def test_full_shapes(T, d, L, n_dst, H, dtype, gain, policy):
     say(f"full T={T} d={d} L={L} n_dst={n_dst} H={H} {dtype} gain={gain} policy={policy}")
