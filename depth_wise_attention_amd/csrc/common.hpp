@@ -73,6 +73,17 @@ __device__ __forceinline__ float read_lane(float v, int src) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
 }
 
+// Workgroup barrier that orders LDS only: the fences are restricted to the
+// local address space, so the wait before s_barrier is lgkmcnt(0) alone and
+// this wave's global loads and stores stay in flight across it.
+// (__syncthreads' workgroup fence also covers global memory and waits for
+// every outstanding load and store, which defeats loads issued ahead.)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Orders this wave's LDS writes before its later LDS reads by other lanes.
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

@@ -25,6 +25,7 @@
 // (exact: every output is one bf16 value times 1).  Outputs are staged through
 // a second LDS tile and written as whole rows with 16-byte stores.
 #include <math.h>
+#include <stdlib.h>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(kFB, 2) void k_full_fast(FullArgs a, const bf16_t* 
       sm.sred[wave][m * kTile + n] = S[r];
       if (m == n) sm.gred[wave][n] = G[r];
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---------------- softmax: thread -> destination j = tid / 8, sources 4 (tid % 8) .. + 3
     {
@@ -248,7 +249,7 @@ __global__ __launch_bounds__(kFB, 2) void k_full_fast(FullArgs a, const bf16_t* 
       const float inv = l > 0.f ? 1.0f / l : 0.f;
       *reinterpret_cast<float4*>(&sm.alpha[j][i0]) = make_float4(e[0] * inv, e[1] * inv, e[2] * inv, e[3] * inv);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---------------- stage 2: H = alpha V
     // A operands: lane (h, j = l%32) holds alpha_part[j][src(b, h, e)] with
@@ -330,7 +331,242 @@ __global__ __launch_bounds__(kFB, 2) void k_full_fast(FullArgs a, const bf16_t* 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Resident variant for d <= 2048: 8 waves, one workgroup per CU.  Wave w owns
+// channels [w d/8, (w+1) d/8) as NCH 64-channel chunks and keeps its whole
+// slice of the token's sources (NCH x 4 KiB) in its own LDS slots through
+// both contractions, so the sources are read from HBM exactly once.  The next
+// token's slice is loaded into registers while the current token's reductions
+// and weighted sums run, and each slot doubles as the output tile once its
+// operands have been read.
+constexpr int kRW = 8;            // waves per workgroup
+constexpr int kRB = kRW * 64;     // threads per workgroup
+constexpr int kRMaxCh = 4;        // chunks per wave at d = 2048
+
+struct ResidentSmem {
+  __attribute__((aligned(16))) unsigned char slots[kRW][kRMaxCh][kTile * kVRow];
+  float sred[kRW / 2][kTile * kTile];                      // pairwise-summed partial S
+  float gred[kRW][kTile];                                  // partial sums of squares
+  __attribute__((aligned(16))) float alpha[kTile][kARow];  // alpha[j][i]
+};
+
+template <int NCH>
+__global__ __launch_bounds__(kRB, 1) void k_full_resident(FullArgs a, const bf16_t* qpk) {
+  __shared__ ResidentSmem sm;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int d = (int)a.d, n_src = (int)a.n_src, n_dst = (int)a.n_dst;
+  const int64_t T = a.T;
+  const bf16_t* src = static_cast<const bf16_t*>(a.src);
+  bf16_t* out = static_cast<bf16_t*>(a.out);
+  const int ch_base = wave * NCH * kChunk;
+  const int h = lane >> 5, n = lane & 31;
+  const uint4* qv = reinterpret_cast<const uint4*>(qpk) + lane;
+
+  uint4 ident[2];
+#pragma unroll
+  for (int a2 = 0; a2 < 2; ++a2) {
+    uint32_t wds[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t lo16 = (16 * a2 + 8 * h + 2 * q == n) ? 0x3F80u : 0u;
+      const uint32_t hi16 = (16 * a2 + 8 * h + 2 * q + 1 == n) ? 0x3F80u : 0u;
+      wds[q] = lo16 | (hi16 << 16);
+    }
+    ident[a2] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+  }
+  uint32_t rowmask[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) rowmask[u] = 8 * u + (lane >> 3) < n_src ? 0xFFFFFFFFu : 0u;
+
+  // Loads of one token's slice: P[c][u] = row 8u + l/8, piece l%8 of chunk c.
+  // Rows >= n_src read row 0 (masked when staged); the token index is clamped,
+  // so every load is unconditional and the wait counts stay exact.
+  uint4 P[NCH][4];
+  auto load_slice = [&](int64_t tt) {
+    const int piece = lane & 7;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = 8 * u + (lane >> 3);
+      const bf16_t* rp = src + ((int64_t)(r < n_src ? r : 0) * T + tt) * d + ch_base + 8 * piece;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) P[c][u] = *reinterpret_cast<const uint4*>(rp + c * kChunk);
+    }
+  };
+  load_slice(blockIdx.x < T ? blockIdx.x : 0);
+
+  auto token = [&](int64_t t) {
+    // ---------------- stage the slice, then start loading the next token's
+    wave_lds_sync();  // previous token's reads of the slots are done
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) stage_chunk(sm.slots[wave][c], P[c], rowmask);
+    wave_lds_sync();
+
+    // ---------------- stage 1: S = Q V^T, G = V V^T over this wave's channels
+    f16acc S = {}, G = {};
+    // The query operands of chunk c + 1 are loaded while chunk c runs (the
+    // next-token registers are free during this stage).
+    {
+      uint4 q[2][8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) q[0][k] = qv[(int64_t)((ch_base / kChunk) * 8 + k) * 64];
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        if (c + 1 < NCH) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) q[(c + 1) & 1][k] = qv[(int64_t)((ch_base / kChunk + c + 1) * 8 + k) * 64];
+        }
+        __builtin_amdgcn_sched_barrier(0);  // issue them now, not next to their use
+        uint4 b[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) b[s] = tile_operand(sm.slots[wave][c], s);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          S = mfma(q[c & 1][2 * s], b[s], S);
+          S = mfma(q[c & 1][2 * s + 1], b[s], S);
+          G = mfma(b[s], b[s], G);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // bound the live ranges to one chunk
+      }
+    }
+    // The next token's slice is requested only now: the wait counter retires
+    // loads in order, so loads issued before the query loads above would have
+    // delayed stage 1.  From here on nothing loads from memory until the next
+    // token is staged, so these loads overlap the reductions and stage 2.
+    {
+      const int64_t tn = t + gridDim.x;
+      load_slice(tn < T ? tn : t);
+    }
+    // ---------------- cross-wave sums: waves 4..7 hand their partials to waves 0..3
+    if (wave >= kRW / 2) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sm.sred[wave - kRW / 2][(8 * (r / 4) + 4 * h + (r % 4)) * kTile + n] = S[r];
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (8 * (r / 4) + 4 * h + (r % 4) == n) sm.gred[wave][n] = G[r];
+    lds_barrier();
+    if (wave < kRW / 2) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float* p = &sm.sred[wave][(8 * (r / 4) + 4 * h + (r % 4)) * kTile + n];
+        *p = *p + S[r];
+      }
+    }
+    lds_barrier();
+
+    // ---------------- softmax (waves 0..3): destination j = tid / 8, sources 4 (tid % 8) .. + 3
+    if (wave < kRW / 2) {
+      const int j = tid / 8, i0 = 4 * (tid % 8);
+      const int lim = n_src - n_dst + j;
+      float sc[4];
+      float m = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = i0 + q;
+        float sv = 0.f, gv = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < kRW / 2; ++w2) sv += sm.sred[w2][j * kTile + i];
+#pragma unroll
+        for (int w2 = 0; w2 < kRW; ++w2) gv += sm.gred[w2][i];
+        const float r = 1.0f / sqrtf(gv / (float)d + a.eps);
+        sc[q] = (j < n_dst && i <= lim) ? r * sv : -INFINITY;
+        m = fmaxf(m, sc[q]);
+      }
+#pragma unroll
+      for (int off = 1; off < 8; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+      float e[4], l = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        e[q] = (sc[q] == -INFINITY) ? 0.f : expf(sc[q] - m);
+        l += e[q];
+      }
+#pragma unroll
+      for (int off = 1; off < 8; off <<= 1) l += __shfl_xor(l, off, kWave);
+      const float inv = l > 0.f ? 1.0f / l : 0.f;
+      *reinterpret_cast<float4*>(&sm.alpha[j][i0]) = make_float4(e[0] * inv, e[1] * inv, e[2] * inv, e[3] * inv);
+    }
+    lds_barrier();
+
+    // ---------------- stage 2: H = alpha V from the resident slots
+    uint4 ahi[2], alo[2];
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2) {
+      const float4 x0 = *reinterpret_cast<const float4*>(&sm.alpha[n][16 * b2 + 4 * h]);
+      const float4 x1 = *reinterpret_cast<const float4*>(&sm.alpha[n][16 * b2 + 8 + 4 * h]);
+      const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      float hi[8], lo[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        hi[e] = bf2f(f2bf(x[e]));
+        lo[e] = x[e] - hi[e];
+      }
+      ahi[b2] = pack8(hi[0], hi[1], hi[2], hi[3], hi[4], hi[5], hi[6], hi[7]);
+      alo[b2] = pack8(lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]);
+    }
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      unsigned char* slot = sm.slots[wave][c];
+      uint4 op[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) op[s] = tile_operand(slot, s);
+      wave_lds_sync();  // the slot becomes the output tile below
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        f16acc D1 = {};
+        D1 = mfma(op[2 * half], ident[0], D1);
+        D1 = mfma(op[2 * half + 1], ident[1], D1);
+        const uint4 b0 = pack8(D1[0], D1[1], D1[2], D1[3], D1[4], D1[5], D1[6], D1[7]);
+        const uint4 b1 = pack8(D1[8], D1[9], D1[10], D1[11], D1[12], D1[13], D1[14], D1[15]);
+        // H^T = V^T alpha^T: the transposed sources are the A operand and alpha
+        // the B operand, so D[c'][j] leaves lane (h, j) with channels
+        // 8q + 4h .. + 3 of destination j in elements 4q .. 4q + 3.
+        f16acc D2 = {};
+        D2 = mfma(b0, ahi[0], D2);
+        D2 = mfma(b0, alo[0], D2);
+        D2 = mfma(b1, ahi[1], D2);
+        D2 = mfma(b1, alo[1], D2);
+        // Tile row j = n, channels 32 half + 8q + 4h .. + 3: 8 bytes at offset 8h of
+        // 16-byte piece 4 half + q (same swizzle as the sources).
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<uint2*>(slot + vpos(n, 4 * half + q) + 8 * h) =
+              make_uint2(pack_bf2(D2[4 * q], D2[4 * q + 1]), pack_bf2(D2[4 * q + 2], D2[4 * q + 3]));
+      }
+      wave_lds_sync();
+      const int ch = ch_base + c * kChunk + 8 * (lane & 7);
+      uint4 o[4];
+      int jr[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        jr[u] = min(8 * u + (lane >> 3), n_dst - 1);  // rows past n_dst repeat row n_dst - 1
+        o[u] = *reinterpret_cast<const uint4*>(slot + vpos(jr[u], lane & 7));
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        __builtin_nontemporal_store(v4u{o[u].x, o[u].y, o[u].z, o[u].w},
+                                    reinterpret_cast<v4u*>(out + ((int64_t)jr[u] * T + t) * d + ch));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // The first token is peeled so that the loop head sees the same outstanding
+  // loads and stores on entry as on the back edge; the wait for the staged
+  // slice then leaves the previous token's stores in flight.
+  int64_t t = blockIdx.x;
+  if (t < T) token(t);
+  for (t += gridDim.x; t < T; t += gridDim.x) token(t);
+}
+
 bool al16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
+
+// The resident kernel can be switched off (ATTNRES_FULL_RESIDENT=0) to compare
+// it with the streaming kernel on the same build.
+bool full_resident_enabled() {
+  static const bool on = [] {
+    const char* e = getenv("ATTNRES_FULL_RESIDENT");
+    return e == nullptr || e[0] != '0';
+  }();
+  return on;
+}
 
 }  // namespace
 
@@ -349,9 +585,26 @@ bool full_fast_ok(const FullArgs& a) {
   return al16(a.src) && al16(a.out) && al16(a.ws);
 }
 
+template <int NCH>
+hipError_t launch_resident(const FullArgs& a, const bf16_t* qpk, hipStream_t st) {
+  int64_t grid = num_cus();
+  if (grid > a.T) grid = a.T;
+  hipLaunchKernelGGL(k_full_resident<NCH>, dim3((unsigned)grid), dim3(kRB), 0, st, a, qpk);
+  return hipGetLastError();
+}
+
 hipError_t launch_full_fast(const FullArgs& a, hipStream_t st) {
   bf16_t* qpk = static_cast<bf16_t*>(a.ws);
   hipLaunchKernelGGL(k_full_qsplit, dim3(64), dim3(256), 0, st, a, qpk);
+  if (a.d <= kRW * kRMaxCh * kChunk && full_resident_enabled()) {
+    switch (a.d / (kRW * kChunk)) {
+      case 1: return launch_resident<1>(a, qpk, st);
+      case 2: return launch_resident<2>(a, qpk, st);
+      case 3: return launch_resident<3>(a, qpk, st);
+      case 4: return launch_resident<4>(a, qpk, st);
+      default: break;
+    }
+  }
   int per_cu = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_full_fast, kFB, 0);
   if (e != hipSuccess) return e;
