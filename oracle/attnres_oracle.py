@@ -35,9 +35,10 @@ Readings where the pages are silent (each also listed in the design notes):
   * MHAR normalises over the full width d, then splits keys, query and values
     into H contiguous chunks of d/H channels.  Heads beyond H = 1 are pinned
     only by the per-head worked example and the zero-query invariant.
-  * Backward: the pages give no formula; block_bwd is the analytic gradient of
-    sum_j <dh_j, h_j> derived from the forward definition, pinned by central
-    finite differences (finite_difference_grads) and closed-form identities.
+  * Backward: the pages give no formula; block_bwd and full_bwd are the
+    analytic gradients of sum_j <dh_j, h_j> derived from the forward
+    definition, pinned by central finite differences (finite_difference_grads,
+    full_finite_difference_grads) and closed-form identities.
 """
 
 from __future__ import annotations
@@ -319,7 +320,94 @@ def finite_difference_grads(reps, partials, w, gain, eps: float, H: int, dh, ste
 
 
 def full_loss(src, w, gain, eps: float, H: int, dout) -> float:
+    """L = sum_j <dout_j, out_j> for out = full_fwd(...)."""
     return float(np.sum(_f64(dout) * full_fwd(src, w, gain, eps, H)))
+
+
+def full_bwd(src, w, gain=None, eps: float = 1e-6, H: int = 1, dout=None):
+    """Analytic gradients of L = sum_j <dout_j, out_j> for out = full_fwd(...).
+
+    The pages give no backward.  This is the chain rule through the forward
+    definition ([B-LAB] §1; [EXPL] learned-query section; [MHAR] heads), with
+    destination j reading the causal prefix of sources 0 .. n_src-n_dst+j.
+    With x_i = RMSNorm(v_i), r_i = 1/sqrt(mean v_i^2 + eps), q_j = w_j * g_j and
+    s_{j,i,h} = q_{j,h} . x_{i,h}:
+      a_{j,i,h} = dout_{j,h} . v_{i,h}
+      c_{j,i,h} = alpha_{j,i,h} (a_{j,i,h} - sum_m alpha_{j,m,h} a_{j,m,h})    (dL/ds)
+      dv_i[k]   = sum_j alpha_{j,i,h(k)} dout_j[k]
+                  + r_i sum_j c_{j,i,h(k)} q_j[k]
+                  - r_i x_i[k] sum_{j,h} c_{j,i,h} s_{j,i,h} / d
+      Z_j[k]    = sum_{t,i} c_{j,i,h(k)} x_i[k];  dw_j = g_j * Z_j;  dg_j = w_j * Z_j
+    where j runs over the destinations whose prefix contains source i.  A
+    shared gain gets dg = sum_j w_j * Z_j.  Returns (d_src, dw, dgain).
+    """
+    src = _f64(src)
+    w = _f64(w)
+    dout = _f64(dout)
+    n_src, T, d = src.shape
+    n_dst = w.shape[0]
+    assert 1 <= n_dst <= n_src and dout.shape == (n_dst, T, d)
+    hd = d // H
+    shared_gain = gain is not None and _f64(gain).ndim == 1
+
+    d_src = np.zeros_like(src)
+    Z = np.zeros((n_dst, d))
+    for j in range(n_dst):
+        n = n_src - n_dst + j + 1
+        V = src[:n]                                                # [n, T, d]
+        g = _gain_row(gain, j, d)
+        q = w[j] * g
+        r = 1.0 / np.sqrt(np.mean(V * V, axis=-1) + eps)           # [n, T]
+        X = V * r[..., None]
+        _, alpha, sc = depth_read(V, w[j], g, eps, H)             # [T, H, n]
+        a = np.einsum("thk,nthk->thn", dout[j].reshape(T, H, hd), V.reshape(n, T, H, hd))
+        c = alpha * (a - np.sum(alpha * a, axis=-1, keepdims=True))
+        cs = np.einsum("thn,thn->tn", c, sc)                      # sum_h c*s, [T, n]
+        alpha_full = np.repeat(alpha, hd, axis=1)                 # [T, d, n]
+        c_full = np.repeat(c, hd, axis=1)
+        d_src[:n] += (np.einsum("tkn,tk->ntk", alpha_full, dout[j])
+                      + r[..., None] * np.einsum("tkn,k->ntk", c_full, q)
+                      - X * r[..., None] * cs.T[..., None] / d)
+        Z[j] = np.einsum("tkn,ntk->k", c_full, X)
+    dw = np.empty((n_dst, d))
+    dg_rows = np.empty((n_dst, d))
+    for j in range(n_dst):
+        dw[j] = _gain_row(gain, j, d) * Z[j]
+        dg_rows[j] = w[j] * Z[j]
+    if gain is None:
+        dgain = None
+    elif shared_gain:
+        dgain = dg_rows.sum(axis=0)
+    else:
+        dgain = dg_rows
+    return d_src, dw, dgain
+
+
+def full_finite_difference_grads(src, w, gain, eps: float, H: int, dout, step: float = 1e-6):
+    """Central finite differences of full_loss w.r.t. every input element.
+
+    Independent of full_bwd: it calls only the forward definition.
+    Returns (d_src, dw, dgain) with dgain None when gain is None.
+    """
+    src = _f64(src).copy()
+    w = _f64(w).copy()
+    gain = None if gain is None else _f64(gain).copy()
+
+    def grad_of(arr: np.ndarray) -> np.ndarray:
+        out = np.empty_like(arr)
+        flat = arr.reshape(-1)
+        gflat = out.reshape(-1)
+        for k in range(flat.size):
+            old = flat[k]
+            flat[k] = old + step
+            lp = full_loss(src, w, gain, eps, H, dout)
+            flat[k] = old - step
+            lm = full_loss(src, w, gain, eps, H, dout)
+            flat[k] = old
+            gflat[k] = (lp - lm) / (2 * step)
+        return out
+
+    return grad_of(src), grad_of(w), None if gain is None else grad_of(gain)
 
 
 def tolerance_error(y, y_ref) -> float:
@@ -335,5 +423,5 @@ def tolerance_error(y, y_ref) -> float:
 __all__: Sequence[str] = (
     "rms_normalise", "depth_read", "full_fwd", "block_sources", "block_direct", "mhar_fwd",
     "block_phase1", "block_phase2_merge", "block_two_phase", "block_bwd", "block_loss",
-    "finite_difference_grads", "full_loss", "tolerance_error",
+    "finite_difference_grads", "full_loss", "full_bwd", "full_finite_difference_grads", "tolerance_error",
 )

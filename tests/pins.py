@@ -316,6 +316,59 @@ def pin_bwd_closed_forms():
     np.testing.assert_allclose(lhs_reps, rhs_reps, rtol=1e-11, atol=1e-11)
 
 
+def _full_bwd_case(seed, H, gain, n_src=5, n_dst=5, T=3, d=8):
+    rng = np.random.default_rng(seed)
+    src = rng.standard_normal((n_src, T, d)) * (1.0 + 0.3 * np.arange(n_src))[:, None, None]
+    w = rng.standard_normal((n_dst, d)) * 0.7
+    if gain == "per":
+        g = 1.0 + 0.1 * rng.standard_normal((n_dst, d))
+    elif gain == "shared":
+        g = 1.0 + 0.1 * rng.standard_normal(d)
+    else:
+        g = None
+    dout = rng.standard_normal((n_dst, T, d))
+    return src, w, g, dout
+
+
+def pin_full_bwd_finite_differences(H=1, gain="per", n_dst=5, eps=1e-6):
+    """full_bwd against central differences of full_loss (forward only)."""
+    src, w, g, dout = _full_bwd_case(50 + H + n_dst, H, gain, n_dst=n_dst)
+    an = orc.full_bwd(src, w, g, eps, H, dout)
+    fd = orc.full_finite_difference_grads(src, w, g, eps, H, dout, step=1e-6)
+    for name, a, f in zip(("d_src", "dw", "dgain"), an, fd):
+        if f is None:
+            assert a is None, name
+            continue
+        scale = max(1.0, float(np.max(np.abs(f))))
+        err = float(np.max(np.abs(a - f))) / scale
+        assert err < 1e-6, f"{name}: {err}"
+
+
+def pin_full_bwd_single_source():
+    """One source, one destination: alpha = 1 whatever the score, so the
+    gradient is dout itself and nothing reaches the query or the gain."""
+    src, w, g, dout = _full_bwd_case(61, 1, "per", n_src=1, n_dst=1, T=4, d=8)
+    d_src, dw, dg = orc.full_bwd(src, w, g, 1e-6, 1, dout)
+    np.testing.assert_array_equal(d_src, dout)
+    np.testing.assert_array_equal(dw, 0.0)
+    np.testing.assert_array_equal(dg, 0.0)
+
+
+def pin_full_bwd_block_s1_identity():
+    """A Block with S = 1 reads exactly its N reps, which is Full with one
+    destination over N sources ([REVIEW] §5 block-size sweep: S = 1 is Full),
+    so the two derived backwards agree; dw * w == dg * g per destination."""
+    src, w, g, dout = _full_bwd_case(62, 2, "per", n_src=6, n_dst=1, T=3, d=8)
+    d_src, dw, dg = orc.full_bwd(src, w, g, 1e-6, 2, dout)
+    d_reps, d_parts, dw_b, dg_b = orc.block_bwd(src, np.zeros((0, 3, 8)), w, g, 1e-6, 2, dout)
+    np.testing.assert_allclose(d_src, d_reps, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dw, dw_b, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dg, dg_b, rtol=1e-12, atol=1e-13)
+    src, w, g, dout = _full_bwd_case(63, 1, "per")
+    _, dw, dg = orc.full_bwd(src, w, g, 1e-3, 1, dout)
+    np.testing.assert_allclose(dw * w, dg * g, rtol=1e-12, atol=1e-14)
+
+
 def pin_tolerance_error():
     y_ref = np.array([3.0, -4.0, 0.0, 0.0])      # RMS = 2.5
     y = y_ref + np.array([0.0, 0.05, 0.0, -0.01])
@@ -334,4 +387,10 @@ ALL_BACKWARD_PINS = [
     lambda: pin_bwd_finite_differences(1, "per"),
     lambda: pin_bwd_finite_differences(2, "shared"),
     pin_bwd_closed_forms,
+]
+ALL_FULL_BACKWARD_PINS = [
+    lambda: pin_full_bwd_finite_differences(1, "per", 5),
+    lambda: pin_full_bwd_finite_differences(2, "shared", 3),
+    pin_full_bwd_single_source,
+    pin_full_bwd_block_s1_identity,
 ]

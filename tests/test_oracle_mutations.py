@@ -16,6 +16,7 @@ from oracle import attnres_oracle as orc
 
 FWD = pins.ALL_FORWARD_PINS
 BWD = pins.ALL_BACKWARD_PINS
+FBWD = pins.ALL_FULL_BACKWARD_PINS
 
 MUTATIONS = [
     ("rms_sum_not_mean", "rms_normalise",
@@ -48,6 +49,16 @@ MUTATIONS = [
      "d_partials[i_sub - 2] += grad[N]", "d_partials[i_sub - 2] += grad[0]", BWD),
     ("bwd_query_path_without_r", "block_bwd",
      "+ r[..., None] * np.einsum(\"tkn,k->ntk\", c_full, q)", "+ np.einsum(\"tkn,k->ntk\", c_full, q)", BWD),
+    ("full_bwd_prefix_one_too_long", "full_bwd",
+     "n = n_src - n_dst + j + 1", "n = min(n_src, n_src - n_dst + j + 2)", FBWD),
+    ("full_bwd_drops_norm_path", "full_bwd",
+     "- X * r[..., None] * cs.T[..., None] / d)", ")", FBWD),
+    ("full_bwd_c_without_centering", "full_bwd",
+     "c = alpha * (a - np.sum(alpha * a, axis=-1, keepdims=True))", "c = alpha * a", FBWD),
+    ("full_bwd_dgain_uses_gain", "full_bwd",
+     "dg_rows[j] = w[j] * Z[j]", "dg_rows[j] = _gain_row(gain, j, d) * Z[j]", FBWD),
+    ("full_bwd_value_path_from_wrong_destination", "full_bwd",
+     "np.einsum(\"tkn,tk->ntk\", alpha_full, dout[j])", "np.einsum(\"tkn,tk->ntk\", alpha_full, dout[0])", FBWD),
 ]
 
 
