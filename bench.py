@@ -37,7 +37,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="block", choices=["block", "mhar", "full", "bwd"])
+    p.add_argument("--workload", default="block", choices=["block", "mhar", "full", "bwd", "full_bwd"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     p.add_argument("--copy-calibration", action="store_true",
@@ -228,6 +228,38 @@ def bench_bwd(args, T=8192):
                 ms_per_step=sec / n * 1e3, step_bytes=b, step_gbs=b * n / sec / 1e9)
 
 
+def full_bwd_bytes(T, d, L, es=2):
+    # read src and dout, write d_src (the dw/dgain slabs are small)
+    return T * d * es * (L + L + L)
+
+
+def bench_full_bwd(args, T=4096):
+    import torch
+    import depth_wise_attention_amd as ar
+    from workloads import synth
+
+    wl = synth.config_full_fwd_bwd(T=T)
+    src, dout = to_dev(wl.src, torch.bfloat16), to_dev(wl.dh, torch.bfloat16)
+    w, g = to_dev(wl.w, torch.float32), to_dev(wl.gain, torch.float32)
+    L, d = wl.src.shape[0], wl.d
+    del wl
+    out = torch.empty((L, T, d), dtype=torch.bfloat16, device="cuda")
+    ws_f = torch.empty(max(1, ar.attnres_full_fwd_workspace_size(L, L, d, 1, ar.BF16)), dtype=torch.uint8,
+                       device="cuda")
+    ws_b = torch.empty(ar.attnres_full_bwd_workspace_size(L, L, T, d, 1), dtype=torch.uint8, device="cuda")
+    d_src, dw, dg = torch.empty_like(src), torch.empty_like(w), torch.empty_like(g)
+
+    def step():
+        ar.attnres_full_fwd(src, w, g, 1e-6, 1, out=out, ws=ws_f)
+        ar.attnres_full_bwd(src, w, dout, g, 1e-6, 1, d_src=d_src, dw=dw, dgain=dg, ws=ws_b)
+
+    n = max(3, args.steps // 4)
+    sec, wall = time_loop(step, n, 2)
+    b = full_bytes(T, d, L) + full_bwd_bytes(T, d, L)
+    return dict(name=f"full_fwd_bwd_bf16_T{T}_d{d}_L{L}", tokens_per_s=T * n / sec,
+                ms_per_step=sec / n * 1e3, step_bytes=b, step_gbs=b * n / sec / 1e9)
+
+
 def cpu_baseline(T=16384, chunk=2048):
     """The float64 oracle (as it stands) over the headline batch, in token chunks.
 
@@ -290,7 +322,7 @@ def main():
 
     if args.workload != "block":
         fn = {"mhar": lambda: bench_block(args, H=8, T=32768), "full": lambda: bench_full(args),
-              "bwd": lambda: bench_bwd(args)}[args.workload]
+              "bwd": lambda: bench_bwd(args), "full_bwd": lambda: bench_full_bwd(args)}[args.workload]
         log(json.dumps(fn()))
         return
 
@@ -303,7 +335,7 @@ def main():
     if not args.no_extra:
         torch.cuda.empty_cache()
         for fn in (lambda: bench_block(args, H=8, T=32768, with_events=True), lambda: bench_full(args),
-                   lambda: bench_bwd(args)):
+                   lambda: bench_bwd(args), lambda: bench_full_bwd(args)):
             r = fn()
             extra[r.pop("name")] = {k: v for k, v in r.items() if k not in ("T", "d", "N", "S", "H")}
             torch.cuda.empty_cache()

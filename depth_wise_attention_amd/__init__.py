@@ -14,6 +14,8 @@ from .binding import (  # noqa: F401
     attnres_block_phase2_merge,
     attnres_bwd,
     attnres_bwd_workspace_size,
+    attnres_full_bwd,
+    attnres_full_bwd_workspace_size,
     attnres_full_fwd,
     attnres_full_fwd_workspace_size,
     attnres_last_error,

@@ -49,13 +49,17 @@ def lib() -> ctypes.CDLL:
     L.attnres_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i32]
     L.attnres_bwd.argtypes = [vp, i64, vp, i64, i64, i64, vp, vp, i64, f32, i32, i32, vp, vp, vp, vp,
                               vp, i32, vp, sz, vp]
+    L.attnres_full_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i32]
+    L.attnres_full_bwd.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, f32, i32, i32, vp, vp, vp, vp, i32, vp,
+                                   sz, vp]
     L.attnres_set_kernel_policy.argtypes = [i32]
     for name in ("attnres_full_fwd", "attnres_block_phase1", "attnres_block_phase2_merge", "mhar_fwd",
-                 "attnres_bwd", "attnres_version", "attnres_set_kernel_policy"):
+                 "attnres_bwd", "attnres_full_bwd", "attnres_version", "attnres_set_kernel_policy"):
         getattr(L, name).restype = ctypes.c_int
     L.attnres_full_fwd_workspace_size.restype = sz
     L.mhar_fwd_workspace_size.restype = sz
     L.attnres_bwd_workspace_size.restype = sz
+    L.attnres_full_bwd_workspace_size.restype = sz
     L.attnres_last_error.restype = ctypes.c_char_p
     L.attnres_last_error.argtypes = []
     L.attnres_version.argtypes = []
@@ -84,6 +88,10 @@ def attnres_full_fwd_workspace_size(n_src: int, n_dst: int, d: int, H: int, dtyp
 
 def mhar_fwd_workspace_size(N: int, S: int, T: int, d: int, H: int) -> int:
     return lib().mhar_fwd_workspace_size(N, S, T, d, H)
+
+
+def attnres_full_bwd_workspace_size(n_src: int, n_dst: int, T: int, d: int, H: int) -> int:
+    return lib().attnres_full_bwd_workspace_size(n_src, n_dst, T, d, H)
 
 
 def attnres_bwd_workspace_size(N: int, S: int, T: int, d: int, H: int) -> int:
@@ -240,3 +248,26 @@ def attnres_bwd(reps, partials, w, dh, gain=None, eps: float = 1e-6, H: int = 1,
                              _p(dw), _p(dgain), int(bool(accumulate)), _p(ws),
                              ws.numel() * ws.element_size(), _stream(stream)))
     return d_reps, d_partials, dw, dgain
+
+
+def attnres_full_bwd(src, w, dout, gain=None, eps: float = 1e-6, H: int = 1, d_src=None, dw=None, dgain=None,
+                     accumulate: bool = False, ws=None, stream=None):
+    """Backward of attnres_full_fwd -> (d_src, dw, dgain)."""
+    torch = _torch()
+    n_src, T, d = src.shape
+    n_dst = w.shape[0]
+    dev = src.device
+    if d_src is None:
+        d_src = torch.empty_like(src)
+    if dw is None:
+        dw = torch.empty((n_dst, d), dtype=torch.float32, device=dev)
+    if dgain is None and gain is not None:
+        dgain = torch.empty(tuple(gain.shape), dtype=torch.float32, device=dev)
+    need = attnres_full_bwd_workspace_size(n_src, n_dst, T, d, H)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    gp, gld = _gain(gain, n_dst, d)
+    _check(lib().attnres_full_bwd(_p(src), n_src, T, d, _p(w), n_dst, gp, gld, eps, H, _code(src), _p(dout),
+                                  _p(d_src), _p(dw), _p(dgain), int(bool(accumulate)), _p(ws), _nbytes(ws),
+                                  _stream(stream)))
+    return d_src, dw, dgain

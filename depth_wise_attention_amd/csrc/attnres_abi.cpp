@@ -136,6 +136,11 @@ int64_t bwd_slots(int64_t T) {
   return s < kMaxBwdSlots ? s : kMaxBwdSlots;
 }
 
+int64_t full_bwd_slots(int64_t T) {
+  const int64_t s = (T + 3) / 4 * 4;
+  return s < kMaxFullBwdSlots ? s : kMaxFullBwdSlots;
+}
+
 }  // namespace
 
 namespace attnres {
@@ -156,7 +161,7 @@ extern "C" {
 
 const char* attnres_last_error(void) { return g_err; }
 
-int attnres_version(void) { return (2 << 16) | 0; }
+int attnres_version(void) { return (2 << 16) | 1; }
 
 int attnres_set_kernel_policy(int32_t policy) {
   if (policy != 0 && policy != 1) return fail(ATTNRES_ERR_INVALID, "unknown kernel policy %d", policy);
@@ -425,6 +430,70 @@ int attnres_bwd(const void* reps, int64_t N, const void* partials, int64_t S, in
   }
   const hipError_t e = launch_bwd_reduce(a, used, stream);
   return e == hipSuccess ? ATTNRES_OK : hip_fail(e, "backward reduction launch");
+}
+
+size_t attnres_full_bwd_workspace_size(int64_t n_src, int64_t n_dst, int64_t T, int64_t d, int32_t H) {
+  (void)n_src;
+  (void)H;
+  int64_t b;
+  if (n_dst < 1 || T < 0 || d < 1) return 0;
+  if (!mul3(full_bwd_slots(T), n_dst, d, &b) || !mul3(b, 4, 1, &b)) return 0;
+  return (size_t)b;
+}
+
+int attnres_full_bwd(const void* src, int64_t n_src, int64_t T, int64_t d, const float* w, int64_t n_dst,
+                     const float* gain, int64_t gain_ld, float eps, int32_t H, int32_t dtype, const void* dout,
+                     void* d_src, float* dw, float* dgain, int32_t accumulate, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  clear_error();
+  int64_t td = 0;
+  RETURN_IF(check_common(T, d, H, dtype, eps, gain, gain_ld, &td));
+  if (n_src < 1 || n_src > kMaxSources)
+    return fail(ATTNRES_ERR_INVALID, "n_src = %lld must be in [1, %d]", (long long)n_src, kMaxSources);
+  if (n_dst < 1 || n_dst > n_src)
+    return fail(ATTNRES_ERR_INVALID, "n_dst = %lld must be in [1, n_src = %lld]", (long long)n_dst,
+                (long long)n_src);
+  if (accumulate != 0 && accumulate != 1)
+    return fail(ATTNRES_ERR_INVALID, "accumulate = %d must be 0 or 1", accumulate);
+  if (n_dst * (int64_t)H * n_src > kBwdTable)
+    return fail(ATTNRES_ERR_UNSUPPORTED, "n_dst * H * n_src = %lld exceeds %d", (long long)(n_dst * H * n_src),
+                kBwdTable);
+  REQUIRE_PTR(w, "w");
+  REQUIRE_PTR(dw, "dw");
+  if (gain != nullptr) REQUIRE_PTR(dgain, "dgain");
+  const int64_t es = (int64_t)dt_size(dtype);
+  size_t b_src, b_dout;
+  RETURN_IF(check_count(n_src, td, es, "src", &b_src));
+  RETURN_IF(check_count(n_dst, td, es, "dout", &b_dout));
+  const size_t b_dw = (size_t)(n_dst * d * 4);
+  const size_t b_dg = gain ? (size_t)((gain_ld ? n_dst : 1) * d * 4) : 0;
+  const size_t need = attnres_full_bwd_workspace_size(n_src, n_dst, T, d, H);
+  if (T > 0) {
+    REQUIRE_PTR(src, "src");
+    REQUIRE_PTR(dout, "dout");
+    REQUIRE_PTR(d_src, "d_src");
+    if (need == 0) return fail(ATTNRES_ERR_INVALID, "workspace size overflows");
+    if (ws == nullptr || ws_bytes < need)
+      return fail(ATTNRES_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? ws_bytes : 0, need);
+  }
+  const Range ins[] = {{src, T ? b_src : 0, "src"},
+                       {w, b_dw, "w"},
+                       {gain, b_dg, "gain"},
+                       {dout, T ? b_dout : 0, "dout"}};
+  const Range outs[] = {{d_src, T ? b_src : 0, "d_src"},
+                        {dw, b_dw, "dw"},
+                        {dgain, b_dg, "dgain"},
+                        {ws, T ? need : 0, "ws"}};
+  RETURN_IF(check_aliasing(ins, 4, outs, 4));
+  FullBwdArgs a{src,   n_src, T,    d,     w,     n_dst,      gain,    gain ? gain_ld : 0, eps,
+                H,     dtype, dout, d_src, dw,    dgain,      accumulate, static_cast<float*>(ws),
+                T ? full_bwd_slots(T) : 0};
+  if (T > 0) {
+    const hipError_t e = launch_full_bwd_generic(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "full backward launch");
+  }
+  const hipError_t e = launch_full_bwd_reduce(a, a.slots, stream);
+  return e == hipSuccess ? ATTNRES_OK : hip_fail(e, "full backward reduction launch");
 }
 
 }  // extern "C"

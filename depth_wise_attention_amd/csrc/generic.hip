@@ -13,7 +13,7 @@ namespace attnres {
 namespace {
 
 constexpr int kGenWaves = 4;       // wavefronts per block
-constexpr int kBwdTab = 1024;      // S*H*(N+1) table entries per wave (backward)
+constexpr int kBwdTab = kBwdTable; // S*H*(N+1) table entries per wave (backward)
 
 // Inverse RMS of sources row(0..n-1): lane i returns r_i = 1/sqrt(mean(v_i^2) + eps).
 // (ai-systems-engineering explainer, learned-query section: RMS = root mean square.)
@@ -288,6 +288,124 @@ __global__ __launch_bounds__(256) void k_bwd_generic(BwdArgs a) {
   }
 }
 
+// Full AttnRes backward, one wavefront per token (any shape with
+// n_dst * H * n_src <= kBwdTab).  Destination j reads sources 0 .. lim_j,
+// lim_j = n_src - n_dst + j (b-lab.team summary §1).  With x_i = RMSNorm(v_i),
+// r_i its inverse RMS, q_j = w_j * g_j and s = r_i q_j . v_i per head:
+//   a_{j,i} = dout_j . v_i,  c_{j,i} = alpha_{j,i} (a_{j,i} - sum_m alpha_{j,m} a_{j,m})
+//   dv_i = sum_{j: lim_j >= i} (alpha_{j,i} dout_j + r_i c_{j,i} q_j) - r_i^2 v_i sum_{j,h} c s / d
+//   Z_j += sum_{i <= lim_j} c_{j,i} r_i v_i   (per head chunk; dw_j = g_j Z_j, dg_j = w_j Z_j)
+// The pages give no backward; this is the chain rule through the forward.
+template <typename E>
+__global__ __launch_bounds__(256) void k_full_bwd_generic(FullBwdArgs a) {
+  __shared__ float tab[kGenWaves][3][kBwdTab];
+  const int lane = lane_id();
+  const int wv = threadIdx.x >> 6;
+  float* t_alpha = tab[wv][0];
+  float* t_c = tab[wv][1];
+  float* t_s = tab[wv][2];
+  const int n_src = (int)a.n_src, n_dst = (int)a.n_dst, d = (int)a.d, H = a.H, hd = d / H;
+  const int off = n_src - n_dst;  // destination j reads sources 0 .. off + j
+  const int64_t T = a.T, td = a.T * a.d;
+  const int64_t wave = (int64_t)blockIdx.x * kGenWaves + wv;
+  const int64_t nw = (int64_t)gridDim.x * kGenWaves;
+  const E* src = static_cast<const E*>(a.src);
+  const E* dout = static_cast<const E*>(a.dout);
+  E* d_src = static_cast<E*>(a.d_src);
+  float* z = a.zslots + wave * (int64_t)n_dst * d;
+  for (int64_t k = lane; k < (int64_t)n_dst * d; k += kWave) z[k] = 0.f;
+
+  auto q = [&](int j, int k) {
+    const float wq = a.w[(int64_t)j * d + k];
+    return a.gain ? wq * a.gain[j * a.gain_ld + k] : wq;
+  };
+  for (int64_t t = wave; t < T; t += nw) {
+    auto row = [&](int i) { return src + i * td + t * d; };
+    const float r_lane = inv_rms_lanes<E>(row, n_src, d, a.eps);
+
+    // alpha, c and s for every (destination, head, source) pair of this token.
+    for (int j = 0; j < n_dst; ++j) {
+      const int nj = off + j + 1;
+      const E* dj = dout + j * td + t * d;
+      for (int h = 0; h < H; ++h) {
+        const int c0 = h * hd, c1 = c0 + hd;
+        float s_lane = -INFINITY, a_lane = 0.f;
+        for (int u = 0; u < nj; ++u) {
+          const E* v = row(u);
+          float aq = 0.f, ad = 0.f;
+          for (int k = c0 + lane; k < c1; k += kWave) {
+            const float x = ld(v + k);
+            aq = fmaf(q(j, k), x, aq);
+            ad = fmaf(ld(dj + k), x, ad);
+          }
+          aq = wave_sum(aq);
+          ad = wave_sum(ad);
+          const float ru = read_lane(r_lane, u);
+          if (lane == u) {
+            s_lane = ru * aq;
+            a_lane = ad;
+          }
+        }
+        const float m = wave_max(s_lane);
+        const float e = (lane < nj) ? expf(s_lane - m) : 0.f;
+        const float al = e / wave_sum(e);
+        const float sa = wave_sum(al * a_lane);
+        if (lane < nj) {
+          const int idx = (j * H + h) * n_src + lane;
+          t_alpha[idx] = al;
+          t_c[idx] = al * (a_lane - sa);
+          t_s[idx] = s_lane;
+        }
+      }
+    }
+    wave_lds_sync();
+
+    // Source gradients: every destination whose prefix contains source i.
+    for (int i = 0; i < n_src; ++i) {
+      const float ri = read_lane(r_lane, i);
+      const int j0 = i > off ? i - off : 0;
+      float cs = 0.f;
+      for (int j = j0; j < n_dst; ++j)
+        for (int h = 0; h < H; ++h) {
+          const int idx = (j * H + h) * n_src + i;
+          cs = fmaf(t_c[idx], t_s[idx], cs);
+        }
+      const float coef = ri * ri * cs / (float)d;
+      const E* v = row(i);
+      E* gout = d_src + i * td + t * d;
+      for (int k = lane; k < d; k += kWave) {
+        const int hh = k / hd;
+        float gk = 0.f;
+        for (int j = j0; j < n_dst; ++j) {
+          const int idx = (j * H + hh) * n_src + i;
+          gk = fmaf(t_alpha[idx], ld(dout + j * td + t * d + k), gk);
+          gk = fmaf(ri * t_c[idx], q(j, k), gk);
+        }
+        gk = fmaf(-coef, ld(v + k), gk);
+        if (a.accumulate) gk += ld(gout + k);
+        st(gout + k, gk);
+      }
+    }
+
+    // Z_j partials for dw / dgain.
+    for (int j = 0; j < n_dst; ++j) {
+      const int nj = off + j + 1;
+      for (int kb = 0; kb < d; kb += kWave) {  // uniform bounds around read_lane
+        const int k = kb + lane;
+        const bool in = k < d;
+        const int hh = (in ? k : 0) / hd;
+        float zz = 0.f;
+        for (int u = 0; u < nj; ++u) {
+          const float ru = read_lane(r_lane, u);
+          if (in) zz = fmaf(t_c[(j * H + hh) * n_src + u] * ru, ld(row(u) + k), zz);
+        }
+        if (in) z[(int64_t)j * d + k] += zz;
+      }
+    }
+    wave_lds_sync();
+  }
+}
+
 // dw_j = g_j * Z_j, dg_j = w_j * Z_j (summed over j for a shared gain), with
 // Z_j the fixed-order sum of the slot partials.  Block = 4 groups of 64 lanes
 // over 64 consecutive channels of one destination; group gi sums slots
@@ -388,16 +506,37 @@ hipError_t launch_bwd_generic(const BwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_reduce(const BwdArgs& a, int64_t slots_used, hipStream_t st) {
-  const int d = (int)a.d, S = (int)a.S;
-  const bool shared = a.gain != nullptr && a.gain_ld == 0;
-  hipLaunchKernelGGL(k_bwd_reduce, dim3((unsigned)((d + 63) / 64), (unsigned)S), dim3(256), 0, st,
-                     (const float*)a.zslots, slots_used, S, d, a.w, a.gain, a.gain_ld, a.dw,
-                     a.dgain, a.accumulate);
+// Z slots [slots_used, rows, d] -> dw [rows, d] and dgain (rows or shared).
+static hipError_t launch_z_reduce(const float* z, int64_t slots_used, int rows, int d, const float* w,
+                                  const float* gain, int64_t gain_ld, float* dw, float* dgain,
+                                  int accumulate, hipStream_t st) {
+  const bool shared = gain != nullptr && gain_ld == 0;
+  hipLaunchKernelGGL(k_bwd_reduce, dim3((unsigned)((d + 63) / 64), (unsigned)rows), dim3(256), 0, st, z,
+                     slots_used, rows, d, w, gain, gain_ld, dw, dgain, accumulate);
   if (shared)
-    hipLaunchKernelGGL(k_bwd_reduce_shared_gain, dim3((unsigned)((d + 255) / 256)), dim3(256), 0,
-                       st, (const float*)a.zslots, slots_used, S, d, a.w, a.dgain, a.accumulate);
+    hipLaunchKernelGGL(k_bwd_reduce_shared_gain, dim3((unsigned)((d + 255) / 256)), dim3(256), 0, st, z,
+                       slots_used, rows, d, w, dgain, accumulate);
   return hipGetLastError();
+}
+
+hipError_t launch_bwd_reduce(const BwdArgs& a, int64_t slots_used, hipStream_t st) {
+  return launch_z_reduce(a.zslots, slots_used, (int)a.S, (int)a.d, a.w, a.gain, a.gain_ld, a.dw, a.dgain,
+                         a.accumulate, st);
+}
+
+hipError_t launch_full_bwd_generic(const FullBwdArgs& a, hipStream_t st) {
+  if (a.slots % kGenWaves != 0 || a.slots < kGenWaves) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(a.slots / kGenWaves)), block(kGenWaves * kWave);
+  if (a.dtype == kF32)
+    hipLaunchKernelGGL(k_full_bwd_generic<float>, grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL(k_full_bwd_generic<bf16_t>, grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_full_bwd_reduce(const FullBwdArgs& a, int64_t slots_used, hipStream_t st) {
+  return launch_z_reduce(a.zslots, slots_used, (int)a.n_dst, (int)a.d, a.w, a.gain, a.gain_ld, a.dw, a.dgain,
+                         a.accumulate, st);
 }
 
 }  // namespace attnres

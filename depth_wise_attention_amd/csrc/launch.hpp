@@ -88,6 +88,32 @@ struct BwdArgs {
 // Maximum number of [S, d] partial-gradient slabs in the backward workspace.
 constexpr int64_t kMaxBwdSlots = 1024;
 
+// Full AttnRes backward: gradients of sum_j <dout_j, out_j> for the Full forward.
+struct FullBwdArgs {
+  const void* src;
+  int64_t n_src, T, d;
+  const float* w;
+  int64_t n_dst;
+  const float* gain;
+  int64_t gain_ld;
+  float eps;
+  int H;
+  int dtype;
+  const void* dout;
+  void* d_src;
+  float* dw;
+  float* dgain;
+  int accumulate;
+  float* zslots;  // [slots, n_dst, d] fp32
+  int64_t slots;
+};
+
+// Maximum number of [n_dst, d] slabs in the Full backward workspace (one per
+// wavefront of the general kernel).
+constexpr int64_t kMaxFullBwdSlots = 1024;
+// Per-wave table entries (alpha, c, s) of the general backward kernels.
+constexpr int kBwdTable = 1024;
+
 // General kernels: any shape within the documented limits.
 hipError_t launch_full_generic(const FullArgs& a, hipStream_t st);
 hipError_t launch_phase1_generic(const Phase1Args& a, hipStream_t st);
@@ -96,6 +122,8 @@ hipError_t launch_bwd_generic(const BwdArgs& a, hipStream_t st);  // uses a.slot
 
 // Fixed-order reduction of the slot partials into dw / dgain.
 hipError_t launch_bwd_reduce(const BwdArgs& a, int64_t slots_used, hipStream_t st);
+hipError_t launch_full_bwd_generic(const FullBwdArgs& a, hipStream_t st);  // uses a.slots waves
+hipError_t launch_full_bwd_reduce(const FullBwdArgs& a, int64_t slots_used, hipStream_t st);
 
 // Specialised gfx950 kernels.  The *_ok predicates are pure functions of the
 // arguments (no HIP calls); a launcher may only be called when its predicate

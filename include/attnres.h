@@ -32,8 +32,9 @@
  *             argument is checked before any HIP call, so a call that fails
  *             validation enqueues nothing.  attnres_last_error() returns a
  *             thread-local message describing the last failure.
- *  Empty      T == 0 is valid and enqueues nothing, except that attnres_bwd
- *             with accumulate == 0 still writes zeros to dw and dgain.
+ *  Empty      T == 0 is valid and enqueues nothing, except that the two
+ *             backward calls with accumulate == 0 still write zeros to dw and
+ *             dgain.
  *  Aliasing   Outputs must not overlap inputs, except where a call says so.
  *  Determinism  Identical inputs, shapes and device give bit-identical
  *             outputs (no floating-point atomics).
@@ -203,7 +204,44 @@ int attnres_bwd(const void* reps, int64_t N, const void* partials, int64_t S, in
 /* Thread-local message for the last failing call on this thread ("" if none). */
 const char* attnres_last_error(void);
 
-/* ABI version: (major << 16) | minor.  Major 2 added the Full-forward workspace. */
+/*
+ * Bytes of device workspace attnres_full_bwd needs (fp32 partial sums of the
+ * query and gain gradients, one [n_dst, d] slab per wavefront, at most 1024
+ * slabs).  0 on invalid sizes.
+ */
+size_t attnres_full_bwd_workspace_size(int64_t n_src, int64_t n_dst, int64_t T, int64_t d,
+                                       int32_t H);
+
+/*
+ * Full AttnRes backward: gradients of L = sum_j <dout_j, out_j> for out =
+ * attnres_full_fwd(src, w, gain, ...) with the same arguments.  The pages
+ * give no backward; this is the chain rule through the forward definition
+ * (b-lab.team summary §1; ai-systems-engineering.com explainer, learned-query
+ * section; chatpaper.ai MHAR abstract for heads), with destination j reading
+ * the causal prefix of sources 0 .. n_src - n_dst + j.  Per token, with
+ * x_i = RMSNorm(v_i), r_i its inverse RMS and q_j = w_j * g_j:
+ *   c_{j,i,h} = alpha (dout_j . v_i - sum_m alpha_m dout_j . v_m)    (per head h)
+ *   dv_i = sum_j (alpha_{j,i} dout_j + r_i c_{j,i} q_j) - r_i x_i sum_{j,h} c s / d
+ *   dw_j = g_j * Z_j,  dgain_j = w_j * Z_j,  Z_j = sum over tokens and sources of c x_i
+ *
+ *  src, w, gain, eps, H, dtype   as for attnres_full_fwd
+ *  dout        [n_dst, T, d] dtype     upstream gradient of out
+ *  d_src       [n_src, T, d] dtype
+ *  dw          [n_dst, d] fp32
+ *  dgain       [n_dst, d] fp32 (gain_ld == d) or [d] (gain_ld == 0); ignored
+ *              and may be NULL when gain == NULL
+ *  accumulate  0: overwrite d_src, dw and dgain; 1: add into them
+ *  ws          device workspace of at least attnres_full_bwd_workspace_size()
+ * Requires 1 <= n_dst <= n_src <= 64 and n_dst * H * n_src <= 1024.  dw and
+ * dgain are fixed-order sums over tokens (no atomics).
+ */
+int attnres_full_bwd(const void* src, int64_t n_src, int64_t T, int64_t d, const float* w,
+                     int64_t n_dst, const float* gain, int64_t gain_ld, float eps, int32_t H,
+                     int32_t dtype, const void* dout, void* d_src, float* dw, float* dgain,
+                     int32_t accumulate, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ABI version: (major << 16) | minor.  Major 2 added the Full-forward workspace;
+ * minor 1 added the Full backward. */
 int attnres_version(void);
 
 /*

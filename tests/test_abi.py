@@ -39,7 +39,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("attnres_full_fwd", "attnres_block_phase1", "attnres_block_phase2_merge", "mhar_fwd",
-                 "attnres_bwd", "attnres_full_fwd_workspace_size", "mhar_fwd_workspace_size", "attnres_bwd_workspace_size",
+                 "attnres_bwd", "attnres_full_bwd", "attnres_full_fwd_workspace_size", "mhar_fwd_workspace_size",
+                 "attnres_bwd_workspace_size", "attnres_full_bwd_workspace_size",
                  "attnres_last_error", "attnres_version", "attnres_set_kernel_policy"):
         assert want in names
 
@@ -52,6 +53,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_policy():
     assert binding.attnres_version() >> 16 == 2
+    assert binding.attnres_version() & 0xFFFF >= 1
     prev = binding.attnres_set_kernel_policy(1)
     assert binding.attnres_set_kernel_policy(prev) == 1
     with pytest.raises(binding.AttnResError):
@@ -254,3 +256,36 @@ def test_error_message_is_thread_local():
     t.join()
     assert seen["msg"] == ""
     assert "dtype" in binding.attnres_last_error()
+
+
+def test_full_bwd_workspace_size():
+    # one [n_dst, d] fp32 slab per wavefront, T rounded up to 4, at most 1024 slabs
+    assert binding.attnres_full_bwd_workspace_size(32, 32, 4096, 2048, 1) == 1024 * 32 * 2048 * 4
+    assert binding.attnres_full_bwd_workspace_size(8, 3, 5, 64, 1) == 8 * 3 * 64 * 4
+    assert binding.attnres_full_bwd_workspace_size(8, 3, 0, 64, 1) == 0
+    assert binding.attnres_full_bwd_workspace_size(8, 0, 16, 64, 1) == 0
+
+
+def _rc_full_bwd(**kw):
+    a = dict(src=FAKE, n_src=4, T=8, d=16, w=FAKE + (1 << 30), n_dst=4, gain=None, gain_ld=0, eps=1e-6, H=1,
+             dtype=BF16, dout=FAKE + (2 << 30), d_src=FAKE + (3 << 30), dw=FAKE + (4 << 30), dgain=None,
+             acc=0, ws=FAKE + (5 << 30), ws_bytes=1 << 20)
+    a.update(kw)
+    return binding.lib().attnres_full_bwd(a["src"], a["n_src"], a["T"], a["d"], a["w"], a["n_dst"], a["gain"],
+                                          a["gain_ld"], a["eps"], a["H"], a["dtype"], a["dout"], a["d_src"],
+                                          a["dw"], a["dgain"], a["acc"], a["ws"], a["ws_bytes"], None)
+
+
+@fake_ptrs
+def test_full_bwd_rejects_bad_arguments():
+    for c in [dict(n_src=0), dict(n_src=65), dict(n_dst=0), dict(n_dst=5), dict(acc=2), dict(dtype=7),
+              dict(H=3), dict(eps=-1.0), dict(w=None), dict(dw=None), dict(src=None), dict(dout=None),
+              dict(d_src=None), dict(gain=FAKE + (6 << 30), gain_ld=16, dgain=None),
+              dict(d_src=FAKE + 64), dict(ws=FAKE + (2 << 30) + 64)]:
+        assert _rc_full_bwd(**c) == EINVAL, c
+        assert binding.attnres_last_error() != ""
+    assert _rc_full_bwd(ws=None) == EWS
+    assert _rc_full_bwd(ws_bytes=16) == EWS
+    # n_dst * H * n_src beyond the general kernel's 1024-entry tables
+    assert _rc_full_bwd(n_src=64, n_dst=17, d=64) == EUNSUP
+    assert "1024" in binding.attnres_last_error()

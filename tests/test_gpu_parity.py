@@ -392,3 +392,88 @@ def test_bwd_config_sampled():
     # determinism
     again = ar.attnres_bwd(reps, parts, w, dh, g, wl.eps, 1)
     assert all(torch.equal(x, y) for x, y in zip(again, (d_reps, d_parts, dw, dg)))
+
+
+# ----------------------------------------------------------------- Full backward
+@pytest.mark.parametrize("T,d,L,n_dst,H,dtype,gain", [
+    (5, 16, 4, 4, 1, "f32", "per"),
+    (9, 64, 6, 3, 2, "bf16", "shared"),
+    (3, 24, 3, 1, 3, "f32", "none"),
+    (41, 256, 8, 8, 1, "bf16", "per"),
+    (6, 2048, 32, 32, 1, "bf16", "per"),
+    (2, 8, 64, 16, 1, "f32", "none"),      # 16 x 64 = 1024 table entries, the limit
+])
+def test_full_bwd_shapes(T, d, L, n_dst, H, dtype, gain):
+    say(f"full bwd T={T} d={d} L={L} n_dst={n_dst} H={H} {dtype} gain={gain}")
+    wl = synth.full_workload(T=T, d=d, L=L, std_step=0.2, dtype=dtype, seed=9, gain_variance=0.02,
+                             n_dst=n_dst, with_dout=True)
+    g = _gain_arg(wl.gain, gain, n_dst, d, np.random.default_rng(4))
+    ref = orc.full_bwd(wl.src, wl.w, g, wl.eps, H, wl.dh)
+    got = ar.attnres_full_bwd(dev(wl.src, dtype), dev(wl.w), dev(wl.dh, dtype), dev(g), wl.eps, H)
+    check(host(got[0]), ref[0], dtype, "d_src")
+    pdt = "f32" if dtype == "f32" else "f32_from_bf16"
+    check(host(got[1]), ref[1], pdt, "dw")
+    if g is not None:
+        check(host(got[2]), ref[2], pdt, "dgain")
+
+
+def test_full_bwd_accumulate():
+    wl = synth.full_workload(T=21, d=128, L=6, std_step=0.2, dtype="f32", seed=10, gain_variance=0.02,
+                             with_dout=True)
+    say("full bwd accumulate")
+    src, w, g, dout = dev(wl.src), dev(wl.w), dev(wl.gain), dev(wl.dh)
+    base = [torch.randn_like(x) for x in (src, w, g)]
+    outs = [b.clone() for b in base]
+    ar.attnres_full_bwd(src, w, dout, g, wl.eps, 1, d_src=outs[0], dw=outs[1], dgain=outs[2], accumulate=True)
+    fresh = ar.attnres_full_bwd(src, w, dout, g, wl.eps, 1)
+    for b, o, f in zip(base, outs, fresh):
+        np.testing.assert_allclose(host(o), host(b) + host(f), rtol=1e-6, atol=1e-6)
+
+
+def test_full_bwd_no_tokens_zeroes_parameter_grads():
+    say("full bwd T=0")
+    w = dev(np.ones((3, 64), np.float32))
+    g = dev(np.ones(64, np.float32))
+    src = torch.empty((4, 0, 64), dtype=torch.bfloat16, device=DEV)
+    dout = torch.empty((3, 0, 64), dtype=torch.bfloat16, device=DEV)
+    dw = torch.full((3, 64), 7.0, device=DEV)
+    dg = torch.full((64,), 7.0, device=DEV)
+    ar.attnres_full_bwd(src, w, dout, g, 1e-6, 1, dw=dw, dgain=dg)
+    assert torch.count_nonzero(dw).item() == 0 and torch.count_nonzero(dg).item() == 0
+
+
+def test_full_bwd_full_width_against_oracle():
+    """Full backward at the full width (d=2048, L=32) over every token of a
+    T=128 batch, so dw and dgain (sums over tokens) are compared exactly."""
+    wl = synth.config_full_fwd_bwd(T=128)
+    say(f"full bwd full-width T={wl.T}")
+    ref = orc.full_bwd(wl.src, wl.w, wl.gain, wl.eps, 1, wl.dh)
+    got = ar.attnres_full_bwd(dev(wl.src, "bf16"), dev(wl.w), dev(wl.dh, "bf16"), dev(wl.gain), wl.eps, 1)
+    for name, y, r, kind in zip(("d_src", "dw", "dgain"), got, ref, ("bf16", "f32_from_bf16", "f32_from_bf16")):
+        err = check(host(y), r, kind, name)
+        print(f"  {name}: {err:.2e}")
+
+
+def test_full_bwd_config_sampled():
+    """Full fwd+bwd bf16 at full size: T=4096, d=2048, L=32.
+
+    Per-token gradients on sampled tokens against the oracle; dw/dgain through
+    properties: dw_j * w_j == dg_j * g_j, additivity over two token halves,
+    and bit-identical repeats."""
+    wl = synth.config_full_fwd_bwd()
+    say(f"full bwd config T={wl.T} (sampled tokens + properties)")
+    src, w, g, dout = dev(wl.src, "bf16"), dev(wl.w), dev(wl.gain), dev(wl.dh, "bf16")
+    d_src, dw, dg = ar.attnres_full_bwd(src, w, dout, g, wl.eps, 1)
+    idx = synth.sample_tokens(wl.T, 24)
+    ref = orc.full_bwd(synth.take_tokens(wl.src, idx), wl.w, wl.gain, wl.eps, 1, synth.take_tokens(wl.dh, idx))
+    check(host(d_src[:, idx]), ref[0], "bf16", "d_src (sampled)")
+    lhs, rhs = host(dw) * wl.w, host(dg) * wl.gain
+    assert max_abs_over_rms(lhs, rhs) < 1e-5
+    half = wl.T // 2
+    a = ar.attnres_full_bwd(src[:, :half].contiguous(), w, dout[:, :half].contiguous(), g, wl.eps, 1)
+    b = ar.attnres_full_bwd(src[:, half:].contiguous(), w, dout[:, half:].contiguous(), g, wl.eps, 1)
+    assert max_abs_over_rms(host(a[1]) + host(b[1]), host(dw)) < 1e-4
+    assert max_abs_over_rms(host(a[2]) + host(b[2]), host(dg)) < 1e-4
+    again = ar.attnres_full_bwd(src, w, dout, g, wl.eps, 1)
+    for x, y in zip((d_src, dw, dg), again):
+        assert torch.equal(x, y)

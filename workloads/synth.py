@@ -119,6 +119,7 @@ class Workload:
              0 .. n_src - n_dst + j.
       block: reps [N, T, d], partials [S-1, T, d], w [S, d]; dh [S, T, d] if
              a backward is part of the workload.
+      (full workloads with a backward carry dout [n_dst, T, d] in dh.)
     gain: [n_dst, d] (one per destination), [d] (shared) or None (all ones).
     """
 
@@ -165,19 +166,21 @@ def _gain(n: int, d: int, seed: int, variance: float) -> np.ndarray:
 
 def full_workload(T: int, d: int, L: int, std_step: float, dtype: str, seed: int = 0,
                   gain_variance: Optional[float] = None, eps: float = 1e-6, H: int = 1,
-                  n_dst: Optional[int] = None, name: str = "full") -> Workload:
+                  n_dst: Optional[int] = None, name: str = "full", with_dout: bool = False) -> Workload:
     """Full AttnRes: L sources v_i ~ N(0, (1 + std_step*i)^2), i = 0..L-1.
 
     With n_dst = L (default) destination l = 1..L reads v_0..v_{l-1}.
-    gain_variance None means gain = 1 (passed as None).
+    gain_variance None means gain = 1 (passed as None).  With with_dout, the
+    upstream gradient dout [n_dst, T, d] ~ N(0, 1) is stored in dh.
     """
     n_dst = L if n_dst is None else n_dst
     src = normal_stack(L, (T, d), [1.0 + std_step * i for i in range(L)], seed, _TID_SOURCES)
     src = _maybe_round(src, dtype)
     w = _pseudo_queries(n_dst, d, seed)
     gain = None if gain_variance is None else _gain(n_dst, d, seed, gain_variance)
+    dout = _maybe_round(normal_stack(n_dst, (T, d), [1.0] * n_dst, seed, _TID_DH), dtype) if with_dout else None
     return Workload(name=name, kind="full", dtype=dtype, T=T, d=d, H=H, eps=eps, w=w,
-                    gain=gain, src=src, n_dst=n_dst,
+                    gain=gain, src=src, n_dst=n_dst, dh=dout,
                     meta=dict(L=L, std_step=std_step, seed=seed, gain_variance=gain_variance))
 
 
@@ -224,6 +227,12 @@ def config_full_bf16(seed: int = 0, T: int = 4096) -> Workload:
     """Full AttnRes, bf16: T=4096, d=2048, L=32, v_i ~ N(0,(1+0.1i)^2), gain 1+N(0,0.02)."""
     return full_workload(T=T, d=2048, L=32, std_step=0.1, dtype="bf16", seed=seed,
                          gain_variance=0.02, eps=1e-6, name=f"full_bf16_T{T}_d2048_L32")
+
+
+def config_full_fwd_bwd(seed: int = 0, T: int = 4096) -> Workload:
+    """Full AttnRes fwd+bwd, bf16: the Full bf16 workload (d=2048, L=32) with dout ~ N(0,1)."""
+    return full_workload(T=T, d=2048, L=32, std_step=0.1, dtype="bf16", seed=seed,
+                         gain_variance=0.02, eps=1e-6, name=f"full_bwd_bf16_T{T}_d2048_L32", with_dout=True)
 
 
 def config_block_two_phase(seed: int = 0, T: int = 16384) -> Workload:
