@@ -435,10 +435,12 @@ int attnres_bwd(const void* reps, int64_t N, const void* partials, int64_t S, in
 size_t attnres_full_bwd_workspace_size(int64_t n_src, int64_t n_dst, int64_t T, int64_t d, int32_t H) {
   (void)n_src;
   (void)H;
-  int64_t b;
-  if (n_dst < 1 || T < 0 || d < 1) return 0;
-  if (!mul3(full_bwd_slots(T), n_dst, d, &b) || !mul3(b, 4, 1, &b)) return 0;
-  return (size_t)b;
+  int64_t b, c;
+  if (n_dst < 1 || T < 1 || d < 1 || d > kMaxD) return 0;  // T == 0 needs none
+  if (!mul3(full_bwd_slots(T), n_dst, d, &b) || !mul3(b, 4, 1, &b)) return 0;  // general path
+  if (!mul3(T, 4096, 1, &c)) return 0;                                      // matrix-core path
+  const size_t fast = full_bwd_fast_workspace_bytes(n_dst, T, d);
+  return (size_t)b > fast ? (size_t)b : fast;
 }
 
 int attnres_full_bwd(const void* src, int64_t n_src, int64_t T, int64_t d, const float* w, int64_t n_dst,
@@ -487,12 +489,20 @@ int attnres_full_bwd(const void* src, int64_t n_src, int64_t T, int64_t d, const
   RETURN_IF(check_aliasing(ins, 4, outs, 4));
   FullBwdArgs a{src,   n_src, T,    d,     w,     n_dst,      gain,    gain ? gain_ld : 0, eps,
                 H,     dtype, dout, d_src, dw,    dgain,      accumulate, static_cast<float*>(ws),
-                T ? full_bwd_slots(T) : 0};
+                T ? full_bwd_slots(T) : 0, T ? ws_bytes : 0};
+  const float* slabs = static_cast<const float*>(ws);
+  int64_t n_slabs = 0;
   if (T > 0) {
-    const hipError_t e = launch_full_bwd_generic(a, stream);
+    hipError_t e;
+    if (use_fast() && full_bwd_fast_ok(a)) {
+      e = launch_full_bwd_fast(a, &slabs, &n_slabs, stream);
+    } else {
+      e = launch_full_bwd_generic(a, stream);
+      n_slabs = a.slots;
+    }
     if (e != hipSuccess) return hip_fail(e, "full backward launch");
   }
-  const hipError_t e = launch_full_bwd_reduce(a, a.slots, stream);
+  const hipError_t e = launch_full_bwd_reduce(a, slabs, n_slabs, stream);
   return e == hipSuccess ? ATTNRES_OK : hip_fail(e, "full backward reduction launch");
 }
 

@@ -534,8 +534,8 @@ hipError_t launch_full_bwd_generic(const FullBwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_full_bwd_reduce(const FullBwdArgs& a, int64_t slots_used, hipStream_t st) {
-  return launch_z_reduce(a.zslots, slots_used, (int)a.n_dst, (int)a.d, a.w, a.gain, a.gain_ld, a.dw, a.dgain,
+hipError_t launch_full_bwd_reduce(const FullBwdArgs& a, const float* slabs, int64_t n_slabs, hipStream_t st) {
+  return launch_z_reduce(slabs, n_slabs, (int)a.n_dst, (int)a.d, a.w, a.gain, a.gain_ld, a.dw, a.dgain,
                          a.accumulate, st);
 }
 

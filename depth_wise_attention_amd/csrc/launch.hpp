@@ -104,8 +104,9 @@ struct FullBwdArgs {
   float* dw;
   float* dgain;
   int accumulate;
-  float* zslots;  // [slots, n_dst, d] fp32
+  float* zslots;  // workspace: [slots, n_dst, d] fp32 on the general path
   int64_t slots;
+  size_t ws_bytes;
 };
 
 // Maximum number of [n_dst, d] slabs in the Full backward workspace (one per
@@ -123,7 +124,13 @@ hipError_t launch_bwd_generic(const BwdArgs& a, hipStream_t st);  // uses a.slot
 // Fixed-order reduction of the slot partials into dw / dgain.
 hipError_t launch_bwd_reduce(const BwdArgs& a, int64_t slots_used, hipStream_t st);
 hipError_t launch_full_bwd_generic(const FullBwdArgs& a, hipStream_t st);  // uses a.slots waves
-hipError_t launch_full_bwd_reduce(const FullBwdArgs& a, int64_t slots_used, hipStream_t st);
+// Fixed-order sum of n_slabs [n_dst, d] slabs at `slabs` into dw / dgain.
+hipError_t launch_full_bwd_reduce(const FullBwdArgs& a, const float* slabs, int64_t n_slabs, hipStream_t st);
+// Matrix-core Full backward (bf16, H = 1, n_src <= 32, d % 512 == 0); leaves
+// its Z slabs at *slabs (n_slabs of them) inside the workspace.
+bool full_bwd_fast_ok(const FullBwdArgs& a);
+size_t full_bwd_fast_workspace_bytes(int64_t n_dst, int64_t T, int64_t d);
+hipError_t launch_full_bwd_fast(const FullBwdArgs& a, const float** slabs, int64_t* n_slabs, hipStream_t st);
 
 // Specialised gfx950 kernels.  The *_ok predicates are pure functions of the
 // arguments (no HIP calls); a launcher may only be called when its predicate

@@ -207,7 +207,8 @@ const char* attnres_last_error(void);
 /*
  * Bytes of device workspace attnres_full_bwd needs (fp32 partial sums of the
  * query and gain gradients, one [n_dst, d] slab per wavefront, at most 1024
- * slabs).  0 on invalid sizes.
+ * slabs), or of the matrix-core path if larger; 0 when T == 0 or on invalid
+ * sizes.
  */
 size_t attnres_full_bwd_workspace_size(int64_t n_src, int64_t n_dst, int64_t T, int64_t d,
                                        int32_t H);

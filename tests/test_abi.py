@@ -259,9 +259,16 @@ def test_error_message_is_thread_local():
 
 
 def test_full_bwd_workspace_size():
-    # one [n_dst, d] fp32 slab per wavefront, T rounded up to 4, at most 1024 slabs
+    # the larger of the two paths' needs:
+    #   general: one [n_dst, d] fp32 slab per wavefront, T rounded up to 4, at most 1024 slabs;
+    #   matrix cores: split q and q^T (256 d bytes) + r*c per token (T x 32 x 32 fp32)
+    #                 + one [n_dst, d] fp32 slab per token group (min(T, 64) groups)
+    general = lambda n_dst, T, d: min((T + 3) // 4 * 4, 1024) * n_dst * d * 4
+    fast = lambda n_dst, T, d: 256 * d + T * 4096 + min(T, 64) * n_dst * d * 4
+    for n_src, n_dst, T, d in [(32, 32, 4096, 2048), (8, 3, 5, 64), (32, 32, 1, 512)]:
+        want = max(general(n_dst, T, d), fast(n_dst, T, d))
+        assert binding.attnres_full_bwd_workspace_size(n_src, n_dst, T, d, 1) == want
     assert binding.attnres_full_bwd_workspace_size(32, 32, 4096, 2048, 1) == 1024 * 32 * 2048 * 4
-    assert binding.attnres_full_bwd_workspace_size(8, 3, 5, 64, 1) == 8 * 3 * 64 * 4
     assert binding.attnres_full_bwd_workspace_size(8, 3, 0, 64, 1) == 0
     assert binding.attnres_full_bwd_workspace_size(8, 0, 16, 64, 1) == 0
 

@@ -402,9 +402,14 @@ def test_bwd_config_sampled():
     (41, 256, 8, 8, 1, "bf16", "per"),
     (6, 2048, 32, 32, 1, "bf16", "per"),
     (2, 8, 64, 16, 1, "f32", "none"),      # 16 x 64 = 1024 table entries, the limit
+    # bf16, one head, n_src <= 32, d % 512 == 0: the matrix-core kernels under "auto"
+    (37, 512, 32, 32, 1, "bf16", "per"),
+    (19, 1024, 7, 3, 1, "bf16", "shared"),
+    (70, 1536, 32, 1, 1, "bf16", "none"),
+    (3, 4096, 17, 17, 1, "bf16", "per"),
 ])
-def test_full_bwd_shapes(T, d, L, n_dst, H, dtype, gain):
-    say(f"full bwd T={T} d={d} L={L} n_dst={n_dst} H={H} {dtype} gain={gain}")
+def test_full_bwd_shapes(T, d, L, n_dst, H, dtype, gain, policy):
+    say(f"full bwd T={T} d={d} L={L} n_dst={n_dst} H={H} {dtype} gain={gain} policy={policy}")
     wl = synth.full_workload(T=T, d=d, L=L, std_step=0.2, dtype=dtype, seed=9, gain_variance=0.02,
                              n_dst=n_dst, with_dout=True)
     g = _gain_arg(wl.gain, gain, n_dst, d, np.random.default_rng(4))
@@ -428,6 +433,23 @@ def test_full_bwd_accumulate():
     fresh = ar.attnres_full_bwd(src, w, dout, g, wl.eps, 1)
     for b, o, f in zip(base, outs, fresh):
         np.testing.assert_allclose(host(o), host(b) + host(f), rtol=1e-6, atol=1e-6)
+
+
+def test_full_bwd_accumulate_bf16(policy):
+    """accumulate = 1 adds the gradient in fp32 to the bf16 d_src before one rounding."""
+    wl = synth.full_workload(T=45, d=512, L=12, std_step=0.2, dtype="bf16", seed=11, gain_variance=0.02,
+                             with_dout=True)
+    say(f"full bwd accumulate bf16 policy={policy}")
+    ref = orc.full_bwd(wl.src, wl.w, wl.gain, wl.eps, 1, wl.dh)
+    src, w, g, dout = dev(wl.src, "bf16"), dev(wl.w), dev(wl.gain), dev(wl.dh, "bf16")
+    rng = np.random.default_rng(12)
+    base = [rng.standard_normal(x.shape).astype(np.float32) for x in (wl.src, wl.w, wl.gain)]
+    base[0] = synth.bf16_round(base[0])
+    outs = [dev(base[0], "bf16"), dev(base[1]), dev(base[2])]
+    ar.attnres_full_bwd(src, w, dout, g, wl.eps, 1, d_src=outs[0], dw=outs[1], dgain=outs[2], accumulate=True)
+    check(host(outs[0]), base[0] + ref[0], "bf16", "d_src accumulated")
+    check(host(outs[1]), base[1] + ref[1], "f32_from_bf16", "dw accumulated")
+    check(host(outs[2]), base[2] + ref[2], "f32_from_bf16", "dgain accumulated")
 
 
 def test_full_bwd_no_tokens_zeroes_parameter_grads():
