@@ -206,6 +206,26 @@ def block_phase2_merge(o_i, lse_i, partial, w_i, g_i, eps: float = 1e-6, H: int 
     return ((a * oh + b * p.reshape(T, H, dh)) / (a + b)).reshape(T, d)
 
 
+def block_phase2_merge_update(o_i, lse_i, partial_prev, f_prev, w_i, g_i, eps: float = 1e-6, H: int = 1,
+                              norm_eps: float = 1e-6):
+    """Phase 2 fused with the intra-block partial-sum update and the next
+    sublayer's PreNorm statistic ([B-LAB] §3 and [REVIEW] §3-2 (4): the merge is
+    the fused step of two-phase inference; [B-LAB] §2: the partial sum
+    b_i = b_{i-1} + f_i).
+
+    partial_prev [T, d] (None for the block's first update, i.e. zero) and the
+    previous sublayer's output f_prev [T, d] give partial = partial_prev + f_prev,
+    the partial this sublayer reads; h_i = block_phase2_merge(o_i, lse_i, partial,
+    ...); inv_rms = 1 / sqrt(mean(h_i^2) + norm_eps), the scale a PreNorm sublayer
+    applies to h_i.  Returns (partial, h_i, inv_rms [T]).
+    """
+    f = _f64(f_prev)
+    partial = f if partial_prev is None else _f64(partial_prev) + f
+    h = block_phase2_merge(o_i, lse_i, partial, w_i, g_i, eps, H)
+    inv_rms = 1.0 / np.sqrt(np.mean(h * h, axis=-1) + norm_eps)
+    return partial, h, inv_rms
+
+
 def block_two_phase(reps, partials, w, gain=None, eps: float = 1e-6, H: int = 1):
     """Phase 1 for all S sublayers, then S-1 sequential Phase-2 merges."""
     w = _f64(w)
@@ -422,6 +442,6 @@ def tolerance_error(y, y_ref) -> float:
 
 __all__: Sequence[str] = (
     "rms_normalise", "depth_read", "full_fwd", "block_sources", "block_direct", "mhar_fwd",
-    "block_phase1", "block_phase2_merge", "block_two_phase", "block_bwd", "block_loss",
+    "block_phase1", "block_phase2_merge", "block_phase2_merge_update", "block_two_phase", "block_bwd", "block_loss",
     "finite_difference_grads", "full_loss", "full_bwd", "full_finite_difference_grads", "tolerance_error",
 )

@@ -220,6 +220,42 @@ def pin_two_phase_equals_direct():
             np.testing.assert_allclose(two, direct, rtol=1e-12, atol=1e-12)
 
 
+def pin_fused_update_chain_equals_direct():
+    """Running the fused merge-and-update through a block from a zero partial
+    (b_1 = f_1, b_i = b_{i-1} + f_i) reproduces the plain definition, whose
+    sublayer i reads the reps and the sum of f_1 .. f_{i-1} ([B-LAB] §2)."""
+    for H, gain in ((1, "per"), (2, "shared"), (4, None)):
+        rng = np.random.default_rng(60 + H)
+        T, d, N, S = 5, 16, 4, 4
+        reps = rng.standard_normal((N, T, d)) * (1 + 0.3 * np.arange(N))[:, None, None]
+        f = rng.standard_normal((S - 1, T, d))
+        w = rng.standard_normal((S, d)) / math.sqrt(d) * 3
+        g = {"per": 1 + 0.1 * rng.standard_normal((S, d)), "shared": 1 + 0.1 * rng.standard_normal(d),
+             None: None}[gain]
+        direct = orc.block_direct(reps, np.cumsum(f, axis=0), w, g, 1e-6, H)
+        o, lse = orc.block_phase1(reps, w, g, 1e-6, H)
+        b = None
+        for i in range(2, S + 1):
+            gi = None if g is None else (g if g.ndim == 1 else g[i - 1])
+            b, h, inv = orc.block_phase2_merge_update(o[i - 1], lse[i - 1], b, f[i - 2], w[i - 1], gi, 1e-6, H)
+            np.testing.assert_allclose(b, f[:i - 1].sum(axis=0), rtol=1e-14, atol=1e-14)
+            np.testing.assert_allclose(h, direct[i - 1], rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(inv, 1 / np.sqrt(np.mean(direct[i - 1] ** 2, axis=-1) + 1e-6), rtol=1e-12)
+
+
+def pin_fused_update_rms_example():
+    """With o_i equal to the partial the merge is a convex combination of two
+    equal vectors, so h = partial exactly; for e = [2, 0, 0] the PreNorm
+    statistic is the explainer's RMS([2, 0, 0]) = 2 / sqrt(3) (learned-query
+    section), i.e. inv_rms = sqrt(3) / 2 with eps 0."""
+    e = np.array([[2.0, 0.0, 0.0]])
+    for w in ([0.0, 0.0, 0.0], [0.3, -1.0, 2.0]):
+        b, h, inv = orc.block_phase2_merge_update(e, np.array([[0.7]]), None, e, np.array(w), None, 0.0, 1, 0.0)
+        np.testing.assert_array_equal(b, e)
+        np.testing.assert_allclose(h, e, rtol=0, atol=1e-15)
+        np.testing.assert_allclose(inv, [math.sqrt(3) / 2], rtol=1e-15)
+
+
 # --- MHAR (H heads; H = 1 is AttnRes exactly) -------------------------------------------
 
 def pin_mhar_h1_is_attnres():
@@ -381,7 +417,7 @@ ALL_FORWARD_PINS = [
     pin_softmax_simplex_and_permutation, pin_single_source_identity, pin_gain_fold_identity,
     pin_block_grouping_example, pin_block_s1_is_full, pin_later_sources_do_not_leak,
     pin_two_phase_equals_direct, pin_mhar_h1_is_attnres, pin_mhar_per_head_worked_example,
-    pin_mhar_zero_query_heads_are_means,
+    pin_mhar_zero_query_heads_are_means, pin_fused_update_chain_equals_direct, pin_fused_update_rms_example,
 ]
 ALL_BACKWARD_PINS = [
     lambda: pin_bwd_finite_differences(1, "per"),

@@ -37,6 +37,10 @@ MUTATIONS = [
      "n_j = n_src - n_dst + j + 1", "n_j = min(n_src, n_src - n_dst + j + 2)", FWD),
     ("merge_sign_error", "block_phase2_merge",
      "b = np.exp(s_p - m)[..., None]", "b = np.exp(m - s_p)[..., None]", FWD),
+    ("fused_update_ignores_previous_partial", "block_phase2_merge_update",
+     "partial = f if partial_prev is None else _f64(partial_prev) + f", "partial = f", FWD),
+    ("fused_update_rms_without_mean", "block_phase2_merge_update",
+     "np.mean(h * h, axis=-1)", "np.sum(h * h, axis=-1)", FWD),
     ("lse_drops_max", "block_phase1",
      "lse[l] = (m + np.log(", "lse[l] = (0.0 + np.log(", FWD),
     ("bwd_drops_norm_path", "block_bwd",
