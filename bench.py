@@ -10,7 +10,8 @@ in HBM before timing starts.
 Prints ONE JSON line on stdout.  Everything else goes to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                  [--no-extra] [--workload block|mhar|full|bwd] [--copy-calibration]
+                  [--no-extra] [--workload block|mhar|full|bwd|full_bwd|block_update]
+                  [--copy-calibration]
 """
 
 from __future__ import annotations
@@ -37,7 +38,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="block", choices=["block", "mhar", "full", "bwd", "full_bwd"])
+    p.add_argument("--workload", default="block", choices=["block", "mhar", "full", "bwd", "full_bwd", "block_update"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     p.add_argument("--copy-calibration", action="store_true",
@@ -175,6 +176,76 @@ def bench_block(args, H=1, T=16384, name=None, with_events=True):
         phase2=dict(bytes_per_launch=p2_b, avg_us=p2_avg * 1e6, gbs=p2_b / p2_avg / 1e9),
     )
     return res
+
+
+def update_bytes(T, d, H, first, es=2, state_es=2):
+    """Algorithmic bytes of one fused Phase-2 update: reads the state row, H lse
+    values, the scale, the previous partial (absent for the block's first
+    update) and f; writes the updated partial, h_i and one fp32 inverse RMS."""
+    return T * (d * state_es + H * 4 + 4 + (0 if first else d * es) + d * es + 2 * d * es + 4)
+
+
+def bench_update(args, T=16384):
+    """Block two-phase as a model runs it: Phase 1, then per sublayer i >= 2 the
+    fused update b_{i-1} = b_{i-2} + f_{i-1} (in place), merge and inverse RMS."""
+    import torch
+    import depth_wise_attention_amd as ar
+    from workloads import synth
+
+    wl = synth.block_workload(T=T, d=4096, N=8, S=4, H=1, rep_std_step=0.3, dtype="bf16", seed=0, with_f=True)
+    N, S, d, H = wl.N, wl.S, wl.d, 1
+    reps = to_dev(wl.reps, torch.bfloat16)
+    f = to_dev(wl.f, torch.bfloat16)
+    w = to_dev(wl.w, torch.float32)
+    g = to_dev(wl.gain, torch.float32)
+    del wl
+    h = torch.empty((S, T, d), dtype=torch.bfloat16, device="cuda")
+    state = torch.empty((S - 1, T, d), dtype=torch.float16, device="cuda")
+    lse = torch.empty((S, H, T), dtype=torch.float32, device="cuda")
+    oscale = torch.empty((T,), dtype=torch.float32, device="cuda")
+    part = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    rms = torch.empty((S - 1, T), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(S + 1)] for _ in range(args.steps)]
+
+    def step(e=None):
+        if e:
+            e[0].record(stream)
+        ar.attnres_block_phase1(reps, w, g, 1e-6, H, h_first=h[0], o_state=state, lse=lse, o_scale=oscale,
+                                stream=stream)
+        if e:
+            e[1].record(stream)
+        for i in range(2, S + 1):
+            ar.attnres_block_phase2_merge_update(state[i - 2], lse[i - 1], None if i == 2 else part, f[i - 2],
+                                                 w[i - 1], g[i - 1], 1e-6, H, partial_out=part, h_i=h[i - 1],
+                                                 norm_eps=1e-6, h_inv_rms=rms[i - 2], o_scale=oscale,
+                                                 stream=stream)
+            if e:
+                e[i].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for s in range(args.steps):
+        step(ev[s])
+    end.record(stream)
+    torch.cuda.synchronize()
+    total = start.elapsed_time(end) / 1e3
+    p1_b, _, _ = block_bytes(T, d, N, S, H)
+    first_b, next_b = update_bytes(T, d, H, True), update_bytes(T, d, H, False)
+    first_us = sum(ev[s][1].elapsed_time(ev[s][2]) for s in range(args.steps)) / args.steps * 1e3
+    next_us = sum(ev[s][i - 1].elapsed_time(ev[s][i]) for s in range(args.steps)
+                  for i in range(3, S + 1)) / (args.steps * (S - 2)) * 1e3
+    step_b = p1_b + first_b + (S - 2) * next_b
+    return dict(
+        name=f"block_fused_update_bf16_T{T}_d{d}_N{N}_S{S}_H{H}", T=T, d=d, N=N, S=S, H=H, seconds=total,
+        tokens_per_s=T * args.steps / total, ms_per_step=total / args.steps * 1e3,
+        step_bytes=step_b, step_gbs=step_b * args.steps / total / 1e9,
+        update_first=dict(bytes_per_launch=first_b, avg_us=first_us, gbs=first_b / first_us / 1e3),
+        update=dict(bytes_per_launch=next_b, avg_us=next_us, gbs=next_b / next_us / 1e3),
+    )
 
 
 def bench_full(args, T=4096):
@@ -322,7 +393,8 @@ def main():
 
     if args.workload != "block":
         fn = {"mhar": lambda: bench_block(args, H=8, T=32768), "full": lambda: bench_full(args),
-              "bwd": lambda: bench_bwd(args), "full_bwd": lambda: bench_full_bwd(args)}[args.workload]
+              "bwd": lambda: bench_bwd(args), "full_bwd": lambda: bench_full_bwd(args),
+              "block_update": lambda: bench_update(args)}[args.workload]
         log(json.dumps(fn()))
         return
 
@@ -335,7 +407,7 @@ def main():
     if not args.no_extra:
         torch.cuda.empty_cache()
         for fn in (lambda: bench_block(args, H=8, T=32768, with_events=True), lambda: bench_full(args),
-                   lambda: bench_bwd(args), lambda: bench_full_bwd(args)):
+                   lambda: bench_bwd(args), lambda: bench_full_bwd(args), lambda: bench_update(args)):
             r = fn()
             extra[r.pop("name")] = {k: v for k, v in r.items() if k not in ("T", "d", "N", "S", "H")}
             torch.cuda.empty_cache()

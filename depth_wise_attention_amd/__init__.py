@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     AttnResError,
     attnres_block_phase1,
     attnres_block_phase2_merge,
+    attnres_block_phase2_merge_update,
     attnres_bwd,
     attnres_bwd_workspace_size,
     attnres_full_bwd,

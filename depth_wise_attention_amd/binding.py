@@ -44,6 +44,8 @@ def lib() -> ctypes.CDLL:
     L.attnres_block_phase1.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, f32, i32, i32, vp, vp, i32, vp, vp,
                                        vp]
     L.attnres_block_phase2_merge.argtypes = [vp, i32, vp, vp, vp, i64, i64, vp, vp, f32, i32, i32, vp, vp]
+    L.attnres_block_phase2_merge_update.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, vp, vp, f32, i32, i32,
+                                                    vp, vp, f32, vp, vp]
     L.mhar_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i32]
     L.mhar_fwd.argtypes = [vp, i64, vp, i64, i64, i64, vp, vp, i64, f32, i32, i32, vp, vp, sz, vp]
     L.attnres_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i32]
@@ -53,7 +55,8 @@ def lib() -> ctypes.CDLL:
     L.attnres_full_bwd.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, f32, i32, i32, vp, vp, vp, vp, i32, vp,
                                    sz, vp]
     L.attnres_set_kernel_policy.argtypes = [i32]
-    for name in ("attnres_full_fwd", "attnres_block_phase1", "attnres_block_phase2_merge", "mhar_fwd",
+    for name in ("attnres_full_fwd", "attnres_block_phase1", "attnres_block_phase2_merge",
+                 "attnres_block_phase2_merge_update", "mhar_fwd",
                  "attnres_bwd", "attnres_full_bwd", "attnres_version", "attnres_set_kernel_policy"):
         getattr(L, name).restype = ctypes.c_int
     L.attnres_full_fwd_workspace_size.restype = sz
@@ -205,6 +208,30 @@ def attnres_block_phase2_merge(o_i, lse_i, partial, w_i, gain_i=None, eps: float
                                             _p(w_i), _p(gain_i), eps, H, _code(partial), _p(h_i),
                                             _stream(stream)))
     return h_i
+
+
+def attnres_block_phase2_merge_update(o_i, lse_i, partial_prev, f_prev, w_i, gain_i=None, eps: float = 1e-6,
+                                      H: int = 1, partial_out=None, h_i=None, norm_eps: float = 1e-6,
+                                      h_inv_rms=None, o_scale=None, stream=None):
+    """Phase 2 merge fused with the partial-sum update and the inverse RMS of h_i.
+
+    partial_prev [T, d] or None (the block's first update); f_prev [T, d].
+    Returns (partial_out, h_i, h_inv_rms).  Pass partial_out=partial_prev to
+    update in place, and h_inv_rms=False to skip the statistic."""
+    torch = _torch()
+    T, d = f_prev.shape
+    dev = f_prev.device
+    if partial_out is None:
+        partial_out = torch.empty((T, d), dtype=f_prev.dtype, device=dev)
+    if h_i is None:
+        h_i = torch.empty((T, d), dtype=f_prev.dtype, device=dev)
+    if h_inv_rms is None:
+        h_inv_rms = torch.empty((T,), dtype=torch.float32, device=dev)
+    rms = None if h_inv_rms is False else h_inv_rms
+    _check(lib().attnres_block_phase2_merge_update(
+        _p(o_i), _code(o_i), _p(o_scale), _p(lse_i), _p(partial_prev), _p(f_prev), T, d, _p(w_i), _p(gain_i),
+        eps, H, _code(f_prev), _p(partial_out), _p(h_i), norm_eps, _p(rms), _stream(stream)))
+    return partial_out, h_i, rms
 
 
 def mhar_fwd(reps, partials, w, gain=None, eps: float = 1e-6, H: int = 1, h=None, ws=None,

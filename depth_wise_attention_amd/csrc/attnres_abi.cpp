@@ -161,7 +161,7 @@ extern "C" {
 
 const char* attnres_last_error(void) { return g_err; }
 
-int attnres_version(void) { return (2 << 16) | 1; }
+int attnres_version(void) { return (2 << 16) | 2; }
 
 int attnres_set_kernel_policy(int32_t policy) {
   if (policy != 0 && policy != 1) return fail(ATTNRES_ERR_INVALID, "unknown kernel policy %d", policy);
@@ -282,6 +282,54 @@ int attnres_block_phase2_merge(const void* o_i, int32_t o_dtype, const float* o_
   RETURN_IF(check_aliasing(ins, 6, outs, 1));
   Phase2Args a{o_i, o_dtype, o_dtype == ATTNRES_F16 ? o_scale : nullptr, lse_i, partial, T, d,
                w_i, gain_i, eps, H, dtype, h_i};
+  return run_phase2(a, stream);
+}
+
+int attnres_block_phase2_merge_update(const void* o_i, int32_t o_dtype, const float* o_scale,
+                                      const float* lse_i, const void* partial_prev, const void* f_prev,
+                                      int64_t T, int64_t d, const float* w_i, const float* gain_i,
+                                      float eps, int32_t H, int32_t dtype, void* partial_out, void* h_i,
+                                      float norm_eps, float* h_inv_rms, hipStream_t stream) {
+  clear_error();
+  int64_t td = 0;
+  RETURN_IF(check_common(T, d, H, dtype, eps, nullptr, 0, &td));
+  RETURN_IF(check_state_dtype(o_dtype, dtype));
+  if (h_inv_rms != nullptr && (!(norm_eps >= 0.0f) || !std::isfinite(norm_eps)))
+    return fail(ATTNRES_ERR_INVALID, "norm_eps must be finite and >= 0");
+  if (T == 0) return ATTNRES_OK;
+  REQUIRE_PTR(o_i, "o_i");
+  if (o_dtype == ATTNRES_F16) REQUIRE_PTR(o_scale, "o_scale");
+  REQUIRE_PTR(lse_i, "lse_i");
+  REQUIRE_PTR(f_prev, "f_prev");
+  REQUIRE_PTR(w_i, "w_i");
+  REQUIRE_PTR(partial_out, "partial_out");
+  REQUIRE_PTR(h_i, "h_i");
+  const int64_t es = (int64_t)dt_size(dtype), eo = (int64_t)dt_size(o_dtype);
+  size_t b_p, b_o, b_lse;
+  RETURN_IF(check_count(1, td, es, "partial_out", &b_p));
+  RETURN_IF(check_count(1, td, eo, "o_i", &b_o));
+  RETURN_IF(check_count(H, T, 4, "lse_i", &b_lse));
+  const bool o_in_place = (h_i == o_i);
+  if (o_in_place && o_dtype != dtype)
+    return fail(ATTNRES_ERR_INVALID, "in-place merge needs o_dtype == dtype");
+  const bool p_in_place = (partial_out == partial_prev);
+  const Range ins[] = {{o_in_place ? nullptr : o_i, b_o, "o_i"},
+                       {lse_i, b_lse, "lse_i"},
+                       {p_in_place ? nullptr : partial_prev, partial_prev ? b_p : 0, "partial_prev"},
+                       {f_prev, b_p, "f_prev"},
+                       {w_i, (size_t)(d * 4), "w_i"},
+                       {gain_i, gain_i ? (size_t)(d * 4) : 0, "gain_i"},
+                       {o_dtype == ATTNRES_F16 ? o_scale : nullptr, (size_t)T * 4, "o_scale"}};
+  const Range outs[] = {{partial_out, b_p, "partial_out"},
+                        {h_i, b_p, "h_i"},
+                        {h_inv_rms, h_inv_rms ? (size_t)T * 4 : 0, "h_inv_rms"}};
+  RETURN_IF(check_aliasing(ins, 7, outs, 3));
+  Phase2Args a{o_i, o_dtype, o_dtype == ATTNRES_F16 ? o_scale : nullptr, lse_i, partial_prev, T, d,
+               w_i, gain_i, eps, H, dtype, h_i};
+  a.f = f_prev;
+  a.partial_out = partial_out;
+  a.norm_eps = norm_eps;
+  a.h_inv_rms = h_inv_rms;
   return run_phase2(a, stream);
 }
 

@@ -19,6 +19,8 @@
 // the per-head dots reduce inside the wave, then each element is merged.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "xlane.hpp"
@@ -421,9 +423,14 @@ __device__ __forceinline__ void load_p2(uint4 (&p)[CPL], uint4 (&o)[CPL][StateWo
   }
 }
 
-template <int CPL, bool MH, typename OT>
+// UPD: 0 = plain merge; 1 = fused update partial + f; 2 = fused update with
+// no previous partial (the block's first update: the partial is f).  With a
+// fused update the kernel also stores the merged partial and the inverse RMS
+// of the stored h (see Phase2Args).
+template <int CPL, bool MH, typename OT, int UPD>
 __global__ __launch_bounds__(256, ATTNRES_P2_MINWAVES) void k_phase2_fast(Phase2Args a) {
   constexpr int OW = StateWords<OT>::kWords;
+  constexpr bool kPref = kP2Prefetch && UPD == 0;
   const int lane = lane_id();
   const int d = (int)a.d;
   const int64_t T = a.T;
@@ -451,19 +458,47 @@ __global__ __launch_bounds__(256, ATTNRES_P2_MINWAVES) void k_phase2_fast(Phase2
         qreg[kP2QLds ? 0 : c][e] = a.gain ? a.w[col] * a.gain[col] : a.w[col];
       }
   }
-  const bf16_t* part = static_cast<const bf16_t*>(a.partial);
+  // With UPD == 2 the partial loads read f itself.
+  const bf16_t* part = static_cast<const bf16_t*>(UPD == 2 ? a.f : a.partial);
+  const bf16_t* fin = static_cast<const bf16_t*>(a.f);
+  bf16_t* pout = static_cast<bf16_t*>(a.partial_out);
   const OT* oin = static_cast<const OT*>(a.o);
   bf16_t* hout = static_cast<bf16_t*>(a.h);
   const int64_t nw = (int64_t)gridDim.x * (blockDim.x >> 6);
   int64_t t = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   uint4 p[CPL];
   uint4 o[CPL][OW];
-  if (t < T) load_p2<CPL, OT>(p, o, part, oin, t, d, lane);
+  uint4 fv[UPD == 1 ? CPL : 1];
+  auto load_f = [&](int64_t tt) {
+    if constexpr (UPD == 1) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) fv[c] = ld16<kP2Nt>(fin + tt * d + (c * 64 + lane) * 8);
+    }
+  };
+  if (t < T) {
+    load_p2<CPL, OT>(p, o, part, oin, t, d, lane);
+    load_f(t);
+  }
   for (; t < T; t += nw) {
     const int64_t tn = t + nw;
     uint4 pn[CPL];
     uint4 on[CPL][OW];
-    if (kP2Prefetch && tn < T) load_p2<CPL, OT>(pn, on, part, oin, tn, d, lane);
+    if (kPref && tn < T) load_p2<CPL, OT>(pn, on, part, oin, tn, d, lane);
+
+    if constexpr (UPD != 0) {
+      // The partial this sublayer reads: partial + f rounded once (or f), stored.
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        if constexpr (UPD == 1) {
+          float x[8], y[8];
+          unpack8(p[c], x);
+          unpack8(fv[c], y);
+          p[c] = make_uint4(pack_bf2(x[0] + y[0], x[1] + y[1]), pack_bf2(x[2] + y[2], x[3] + y[3]),
+                            pack_bf2(x[4] + y[4], x[5] + y[5]), pack_bf2(x[6] + y[6], x[7] + y[7]));
+        }
+        st16<false>(pout + t * d + (c * 64 + lane) * 8, p[c]);
+      }
+    }
 
     float ss = 0.f;
     float dot[MH ? CPL : 1];
@@ -515,6 +550,7 @@ __global__ __launch_bounds__(256, ATTNRES_P2_MINWAVES) void k_phase2_fast(Phase2
       ca[c] = wa * inv * oscale;
       cb[c] = wb * inv;
     }
+    float sh = 0.f;  // sum of squares of the stored h (fused update only)
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       float x[8], ov[8], h[8];
@@ -522,9 +558,23 @@ __global__ __launch_bounds__(256, ATTNRES_P2_MINWAVES) void k_phase2_fast(Phase2
       state_unpack<OT>(o[c], ov);
 #pragma unroll
       for (int e = 0; e < 8; ++e) h[e] = fmaf(ca[MH ? c : 0], ov[e], cb[MH ? c : 0] * x[e]);
-      store8(hout + t * d + (c * 64 + lane) * 8, h);
+      if constexpr (UPD == 0) {
+        store8(hout + t * d + (c * 64 + lane) * 8, h);
+      } else {
+        const uint4 hv = make_uint4(pack_bf2(h[0], h[1]), pack_bf2(h[2], h[3]), pack_bf2(h[4], h[5]),
+                                    pack_bf2(h[6], h[7]));
+        st16<false>(hout + t * d + (c * 64 + lane) * 8, hv);
+        float hr[8];
+        unpack8(hv, hr);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sh = fmaf(hr[e], hr[e], sh);
+      }
     }
-    if constexpr (kP2Prefetch) {
+    if constexpr (UPD != 0) {
+      sh = wave_allsum(sh);
+      if (a.h_inv_rms != nullptr && lane == 0) a.h_inv_rms[t] = 1.0f / sqrtf(sh / (float)d + a.norm_eps);
+    }
+    if constexpr (kPref) {
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
         p[c] = pn[c];
@@ -532,7 +582,10 @@ __global__ __launch_bounds__(256, ATTNRES_P2_MINWAVES) void k_phase2_fast(Phase2
         for (int k = 0; k < OW; ++k) o[c][k] = on[c][k];
       }
     } else {
-      if (tn < T) load_p2<CPL, OT>(p, o, part, oin, tn, d, lane);
+      if (tn < T) {
+        load_p2<CPL, OT>(p, o, part, oin, tn, d, lane);
+        load_f(tn);
+      }
     }
   }
 }
@@ -608,11 +661,17 @@ hipError_t launch_p2(const Phase2Args& a, hipStream_t st) {
     return hipGetLastError();
   };
   const bool mh = a.H > 1;
-  if (a.o_dtype == kF32)
-    return mh ? pick(k_phase2_fast<CPL, true, float>) : pick(k_phase2_fast<CPL, false, float>);
-  if (a.o_dtype == kF16)
-    return mh ? pick(k_phase2_fast<CPL, true, f16_t>) : pick(k_phase2_fast<CPL, false, f16_t>);
-  return mh ? pick(k_phase2_fast<CPL, true, bf16_t>) : pick(k_phase2_fast<CPL, false, bf16_t>);
+  auto by_state = [&](auto upd) -> hipError_t {
+    constexpr int U = decltype(upd)::value;
+    if (a.o_dtype == kF32)
+      return mh ? pick(k_phase2_fast<CPL, true, float, U>) : pick(k_phase2_fast<CPL, false, float, U>);
+    if (a.o_dtype == kF16)
+      return mh ? pick(k_phase2_fast<CPL, true, f16_t, U>) : pick(k_phase2_fast<CPL, false, f16_t, U>);
+    return mh ? pick(k_phase2_fast<CPL, true, bf16_t, U>) : pick(k_phase2_fast<CPL, false, bf16_t, U>);
+  };
+  if (a.f == nullptr) return by_state(std::integral_constant<int, 0>());
+  if (a.partial != nullptr) return by_state(std::integral_constant<int, 1>());
+  return by_state(std::integral_constant<int, 2>());
 }
 
 bool heads_fit_segments(int64_t d, int H) { return (d / H) % 512 == 0; }
@@ -639,7 +698,7 @@ hipError_t launch_phase1_fast(const Phase1Args& a, hipStream_t st) {
 bool phase2_fast_ok(const Phase2Args& a) {
   if (a.dtype != kBF16 || a.T < 1 || !heads_fit_segments(a.d, a.H)) return false;
   if (!aligned16(a.o) || !aligned16(a.partial) || !aligned16(a.h) || !aligned16(a.w) ||
-      !aligned16(a.gain))
+      !aligned16(a.gain) || !aligned16(a.f) || !aligned16(a.partial_out))
     return false;
   const int64_t cpl = a.d / 512;
   return a.d % 512 == 0 && (cpl == 4 || cpl == 8);

@@ -145,6 +145,15 @@ __global__ __launch_bounds__(256) void k_phase2_generic(Phase2Args a) {
     const E* p = static_cast<const E*>(a.partial) + t * d;
     const O* o = static_cast<const O*>(a.o) + t * d;
     E* hout = static_cast<E*>(a.h) + t * d;
+    if (a.f != nullptr) {
+      // Fused update: the partial this sublayer reads is partial + f, rounded
+      // once and stored; the passes below read the stored values.  Each lane
+      // rereads only what it wrote, so in-place updates are consistent.
+      const E* fp = static_cast<const E*>(a.f) + t * d;
+      E* po = static_cast<E*>(a.partial_out) + t * d;
+      for (int k = lane; k < d; k += kWave) st(po + k, (a.partial ? ld(p + k) : 0.f) + ld(fp + k));
+      p = po;
+    }
     float ss = 0.f;
     for (int k = lane; k < d; k += kWave) {
       const float x = ld(p + k);
@@ -166,6 +175,16 @@ __global__ __launch_bounds__(256) void k_phase2_generic(Phase2Args a) {
       const float ca = wa * inv * (a.o_dtype == kF16 ? a.oscale[t] : 1.0f), cb = wb * inv;
       for (int k = c0 + lane; k < c1; k += kWave)
         st(hout + k, ca * ld(o + k) + cb * ld(p + k));
+    }
+    if (a.h_inv_rms != nullptr) {
+      // Inverse RMS of the stored h (this lane's own writes, read back).
+      float sh = 0.f;
+      for (int k = lane; k < d; k += kWave) {
+        const float x = ld(hout + k);
+        sh = fmaf(x, x, sh);
+      }
+      sh = wave_sum(sh);
+      if (lane == 0) a.h_inv_rms[t] = 1.0f / sqrtf(sh / (float)d + a.norm_eps);
     }
   }
 }

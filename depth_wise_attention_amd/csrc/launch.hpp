@@ -62,6 +62,14 @@ struct Phase2Args {
   int H;
   int dtype;
   void* h;
+  // Fused update (null f: plain merge).  The merged partial is
+  // partial + f (partial null: f alone), rounded to dtype once and written to
+  // partial_out (which may equal partial).  h_inv_rms[t] (may be null) is
+  // 1 / sqrt(mean(h_t^2) + norm_eps) over the stored h.
+  const void* f = nullptr;
+  void* partial_out = nullptr;
+  float norm_eps = 0.f;
+  float* h_inv_rms = nullptr;
 };
 
 struct BwdArgs {

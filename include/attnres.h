@@ -145,6 +145,34 @@ int attnres_block_phase2_merge(const void* o_i, int32_t o_dtype, const float* o_
                                int32_t dtype, void* h_i, hipStream_t stream);
 
 /*
+ * Phase 2 fused with the intra-block partial-sum update and the next
+ * sublayer's PreNorm statistic (b-lab.team summary §2: the partial sum is the
+ * running sum of the block's sublayer outputs; §3 Inference and Review §3-2 (4):
+ * the merge is the fused step of two-phase inference).  One pass over the
+ * token rows:
+ *   p = partial_prev + f_prev  (f_prev alone when partial_prev is NULL, the
+ *       block's first update), rounded once to dtype and stored to partial_out;
+ *   h_i = attnres_block_phase2_merge(o_i, ..., p, ...) exactly as above, from
+ *       the stored p;
+ *   h_inv_rms[t] = 1 / sqrt(mean_c h_i[t][c]^2 + norm_eps), over the stored h_i
+ *       (the scale an RMSNorm applied to h_i uses; not written when NULL).
+ *
+ *  partial_prev [T, d] dtype or NULL;  f_prev [T, d] dtype (the output of
+ *               sublayer i-1)
+ *  partial_out  [T, d] dtype; may equal partial_prev (in place), must not
+ *               otherwise overlap an input or another output
+ *  h_i          [T, d] dtype; may equal o_i when o_dtype == dtype
+ *  h_inv_rms    [T] fp32 or NULL;  norm_eps finite and >= 0 when it is used
+ * Other arguments as for attnres_block_phase2_merge.
+ */
+int attnres_block_phase2_merge_update(const void* o_i, int32_t o_dtype, const float* o_scale,
+                                      const float* lse_i, const void* partial_prev,
+                                      const void* f_prev, int64_t T, int64_t d, const float* w_i,
+                                      const float* gain_i, float eps, int32_t H, int32_t dtype,
+                                      void* partial_out, void* h_i, float norm_eps,
+                                      float* h_inv_rms, hipStream_t stream);
+
+/*
  * Bytes of device workspace mhar_fwd needs: room for an fp32 Phase-1 state of
  * sublayers 2..S ([S-1, T, d]), the statistics ([S, H, T]) and the per-token
  * state scale ([T]), each aligned to 256 bytes.  Returns 0 for invalid sizes.
@@ -242,7 +270,7 @@ int attnres_full_bwd(const void* src, int64_t n_src, int64_t T, int64_t d, const
                      int32_t accumulate, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ABI version: (major << 16) | minor.  Major 2 added the Full-forward workspace;
- * minor 1 added the Full backward. */
+ * minor 1 added the Full backward, minor 2 the fused Phase 2 update. */
 int attnres_version(void);
 
 /*

@@ -38,7 +38,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for want in ("attnres_full_fwd", "attnres_block_phase1", "attnres_block_phase2_merge", "mhar_fwd",
+    for want in ("attnres_full_fwd", "attnres_block_phase1", "attnres_block_phase2_merge",
+                 "attnres_block_phase2_merge_update", "mhar_fwd",
                  "attnres_bwd", "attnres_full_bwd", "attnres_full_fwd_workspace_size", "mhar_fwd_workspace_size",
                  "attnres_bwd_workspace_size", "attnres_full_bwd_workspace_size",
                  "attnres_last_error", "attnres_version", "attnres_set_kernel_policy"):
@@ -53,7 +54,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_policy():
     assert binding.attnres_version() >> 16 == 2
-    assert binding.attnres_version() & 0xFFFF >= 1
+    assert binding.attnres_version() & 0xFFFF >= 2
     prev = binding.attnres_set_kernel_policy(1)
     assert binding.attnres_set_kernel_policy(prev) == 1
     with pytest.raises(binding.AttnResError):
@@ -189,6 +190,33 @@ def test_phase2_in_place_needs_matching_dtype():
     assert _rc_phase2(h=FAKE) == EINVAL          # o is fp32, h bf16: cannot share storage
     assert "in-place" in binding.attnres_last_error()
     assert _rc_phase2(h=FAKE + (2 << 30)) == EINVAL  # h over the partial
+
+
+def _rc_update(**kw):
+    G = 1 << 30
+    a = dict(o=FAKE, o_dtype=BF16, scale=None, lse=FAKE + G, prev=FAKE + 2 * G, f=FAKE + 3 * G, T=8, d=64,
+             w=FAKE + 4 * G, gain=None, eps=1e-6, H=1, dtype=BF16, pout=FAKE + 5 * G, h=FAKE + 6 * G,
+             norm_eps=1e-6, rms=FAKE + 7 * G)
+    a.update(kw)
+    return binding.lib().attnres_block_phase2_merge_update(
+        a["o"], a["o_dtype"], a["scale"], a["lse"], a["prev"], a["f"], a["T"], a["d"], a["w"], a["gain"],
+        a["eps"], a["H"], a["dtype"], a["pout"], a["h"], a["norm_eps"], a["rms"], None)
+
+
+@fake_ptrs
+def test_phase2_update_rejects_bad_arguments():
+    G = 1 << 30
+    for c in [dict(f=None), dict(pout=None), dict(h=None), dict(o=None), dict(lse=None), dict(w=None),
+              dict(o_dtype=3), dict(H=7), dict(norm_eps=-1.0), dict(norm_eps=float("nan")),
+              dict(o_dtype=F16, scale=None)]:
+        assert _rc_update(**c) == EINVAL, c
+    # Overlaps: the updated partial over f, h over the updated partial, the
+    # statistic over h, and h over o with different dtypes.
+    for c in [dict(pout=FAKE + 3 * G), dict(h=FAKE + 5 * G + 64), dict(rms=FAKE + 6 * G),
+              dict(o_dtype=F32, h=FAKE), dict(prev=FAKE + 5 * G + 2), dict(f=FAKE + 6 * G)]:
+        assert _rc_update(**c) == EINVAL, c
+    assert _rc_update(T=0, o=None, f=None, pout=None, h=None) == OK
+    assert _rc_update(T=-1) == EINVAL
 
 
 def _rc_mhar(**kw):

@@ -137,6 +137,7 @@ class Workload:
     reps: Optional[np.ndarray] = None
     partials: Optional[np.ndarray] = None
     dh: Optional[np.ndarray] = None
+    f: Optional[np.ndarray] = None
     meta: dict = field(default_factory=dict)
 
     @property
@@ -186,29 +187,33 @@ def full_workload(T: int, d: int, L: int, std_step: float, dtype: str, seed: int
 
 def block_workload(T: int, d: int, N: int, S: int, H: int, rep_std_step: float, dtype: str,
                    seed: int = 0, gain_variance: Optional[float] = 0.02, eps: float = 1e-6,
-                   with_dh: bool = False, name: str = "block") -> Workload:
+                   with_dh: bool = False, name: str = "block", with_f: bool = False) -> Workload:
     """Block AttnRes inputs for one block.
 
     reps b_0..b_{N-1} ~ N(0, (1 + rep_std_step*n)^2); intra-block outputs
     f_1..f_{S-1} ~ N(0, 1); partials[k] = f_1 + ... + f_{k+1} accumulated in
     float32 and rounded once; w [S, d] ~ N(0, 1/d); gain [S, d] = 1 + N(0,
-    gain_variance); dh [S, T, d] ~ N(0, 1) when with_dh.
+    gain_variance); dh [S, T, d] ~ N(0, 1) when with_dh.  With with_f the
+    outputs themselves, each rounded to dtype, are kept in f [S-1, T, d] (the
+    inputs of the fused partial-sum update).
     """
     reps = normal_stack(N, (T, d), [1.0 + rep_std_step * n for n in range(N)], seed, _TID_SOURCES)
     reps = _maybe_round(reps, dtype)
     if S > 1:
         f = normal_stack(S - 1, (T, d), [1.0] * (S - 1), seed, _TID_F)
+        f_out = _maybe_round(f.copy(), dtype) if with_f else None
         np.cumsum(f, axis=0, out=f)  # running intra-block sum, float32
         partials = _maybe_round(f, dtype)
     else:
         partials = np.zeros((0, T, d), dtype=np.float32)
+        f_out = np.zeros((0, T, d), dtype=np.float32) if with_f else None
     w = _pseudo_queries(S, d, seed)
     gain = None if gain_variance is None else _gain(S, d, seed, gain_variance)
     dh = None
     if with_dh:
         dh = _maybe_round(normal_stack(S, (T, d), [1.0] * S, seed, _TID_DH), dtype)
     return Workload(name=name, kind="block", dtype=dtype, T=T, d=d, H=H, eps=eps, w=w,
-                    gain=gain, reps=reps, partials=partials, dh=dh,
+                    gain=gain, reps=reps, partials=partials, dh=dh, f=f_out,
                     meta=dict(N=N, S=S, rep_std_step=rep_std_step, seed=seed,
                               gain_variance=gain_variance))
 
