@@ -170,6 +170,24 @@ __device__ __forceinline__ void load_reps(uint4 (&v)[N][CH], const bf16_t* reps,
       v[i][c] = ld16<kP1Nt>(reps + ((int64_t)i * T + t) * d + (c * B + tid) * 8);
 }
 
+// q = w * g into this thread's own LDS slots (fp32, two float4 per chunk).  Kept
+// out of line so that the prologue's code shape cannot change how the token
+// loop is scheduled and allocated.
+template <int S, int CH, int B, bool G>
+__device__ __noinline__ void p1_fold_lds(const float* w, const float* gain, int64_t gain_ld, int d, int tid,
+                                         float4* qs) {
+#pragma unroll
+  for (int l = 0; l < S; ++l)
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      float qq[8];
+      const int col = (c * B + tid) * 8;
+      fold_q8<G>(w + (int64_t)l * d + col, gain + l * gain_ld + col, qq);
+      qs[((l * CH + c) * B + tid) * 2 + 0] = make_float4(qq[0], qq[1], qq[2], qq[3]);
+      qs[((l * CH + c) * B + tid) * 2 + 1] = make_float4(qq[4], qq[5], qq[6], qq[7]);
+    }
+}
+
 template <int N, int S, int CH, int B, bool MH, typename O0, typename OR>
 __global__ __launch_bounds__(B, ATTNRES_P1_MINWAVES) void k_phase1_fast(Phase1Args a) {
   constexpr int CHH = MH ? CH : 1;          // dot-product groups per thread
@@ -192,17 +210,14 @@ __global__ __launch_bounds__(B, ATTNRES_P1_MINWAVES) void k_phase1_fast(Phase1Ar
   // q = w * g for this thread's channels: registers, or this thread's own LDS
   // slots (each thread reads back only what it wrote, so no barrier is needed).
   float qreg[QR][CH][8];
+  auto fold = [&](auto with_gain) {
 #pragma unroll
   for (int l = 0; l < S; ++l)
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       float qq[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int col = (c * B + tid) * 8 + e;
-        const float wv = a.w[(int64_t)l * d + col];
-        qq[e] = a.gain ? wv * a.gain[l * a.gain_ld + col] : wv;
-      }
+      const int col = (c * B + tid) * 8;
+      fold_q8<decltype(with_gain)::value>(a.w + (int64_t)l * d + col, a.gain + l * a.gain_ld + col, qq);
       if constexpr (kP1Dot2) {
         // packed bf16 pairs: first 16 bytes q_hi, second 16 bytes q_lo = q - q_hi
         uint32_t hi[4], lo[4];
@@ -223,7 +238,20 @@ __global__ __launch_bounds__(B, ATTNRES_P1_MINWAVES) void k_phase1_fast(Phase1Ar
 #pragma unroll
         for (int e = 0; e < 8; ++e) qreg[QL ? 0 : l][c][e] = qq[e];
       }
+      // One query row's loads at a time: all rows at once spill registers.
+      if (c == CH - 1) __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  if constexpr (kP1QLds && !kP1Dot2) {
+    if (a.gain != nullptr)
+      p1_fold_lds<S, CH, B, true>(a.w, a.gain, a.gain_ld, d, tid, qs);
+    else
+      p1_fold_lds<S, CH, B, false>(a.w, a.gain, a.gain_ld, d, tid, qs);
+  } else if (a.gain != nullptr) {
+    fold(std::true_type());
+  } else {
+    fold(std::false_type());
+  }
 
   // The softmax lane of this wave: (cc, l, i) = decomposition of the lane.
   const int sm_cc = lane / (S * NP), sm_l = (lane / NP) % S, sm_i = lane % NP;
@@ -440,13 +468,18 @@ __global__ __launch_bounds__(256, ATTNRES_P2_MINWAVES) void k_phase2_fast(Phase2
   float qreg[QR][8];
   if constexpr (kP2QLds) {
     // Every wave uses the same lane -> channel map, so the block shares one copy.
-    for (int k = threadIdx.x; k < d / 4; k += blockDim.x) {
-      float4 q = reinterpret_cast<const float4*>(a.w)[k];
-      if (a.gain) {
-        const float4 g = reinterpret_cast<const float4*>(a.gain)[k];
+    // One branch on the gain outside the loop: loads in the loop are unconditional.
+    const float4* w4 = reinterpret_cast<const float4*>(a.w);
+    const float4* g4 = reinterpret_cast<const float4*>(a.gain);
+    if (a.gain != nullptr) {
+      for (int k = threadIdx.x; k < d / 4; k += blockDim.x) {
+        float4 q = w4[k];
+        const float4 g = g4[k];
         q.x *= g.x; q.y *= g.y; q.z *= g.z; q.w *= g.w;
+        qs[k] = q;
       }
-      qs[k] = q;
+    } else {
+      for (int k = threadIdx.x; k < d / 4; k += blockDim.x) qs[k] = w4[k];
     }
     __syncthreads();
   } else {
@@ -683,7 +716,9 @@ bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0
 
 bool phase1_fast_ok(const Phase1Args& a) {
   if (a.dtype != kBF16 || a.T < 1 || !heads_fit_segments(a.d, a.H)) return false;
-  if (!aligned16(a.reps) || !aligned16(a.o0) || !aligned16(a.orest)) return false;
+  if (!aligned16(a.reps) || !aligned16(a.o0) || !aligned16(a.orest) || !aligned16(a.w) ||
+      !aligned16(a.gain))
+    return false;
   const int ch = phase1_ch(a.d);
   if (ch == 0) return false;
   if (!((a.N == 8 && a.S == 4) || (a.N == 4 && a.S == 4))) return false;

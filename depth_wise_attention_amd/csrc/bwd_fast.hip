@@ -16,6 +16,8 @@
 // (k_bwd_reduce) turns the slabs into dw and dgain.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "xlane.hpp"
@@ -67,20 +69,22 @@ __global__ __launch_bounds__(B, ATTNRES_BWD_MINWAVES) void k_bwd_fast(BwdArgs a)
   const int64_t T = a.T;
 
   // q = w * g for this thread's channels, in this thread's own LDS slots.
+  auto fold = [&](auto with_gain) {
 #pragma unroll
   for (int j = 0; j < S; ++j)
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       float qq[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int col = (c * B + tid) * 8 + e;
-        const float wv = a.w[(int64_t)j * d + col];
-        qq[e] = a.gain ? wv * a.gain[j * a.gain_ld + col] : wv;
-      }
+      const int col = (c * B + tid) * 8;
+      fold_q8<decltype(with_gain)::value>(a.w + (int64_t)j * d + col, a.gain + j * a.gain_ld + col, qq);
       qs[((j * CH + c) * B + tid) * 2 + 0] = make_float4(qq[0], qq[1], qq[2], qq[3]);
       qs[((j * CH + c) * B + tid) * 2 + 1] = make_float4(qq[4], qq[5], qq[6], qq[7]);
     }
+  };
+  if (a.gain != nullptr)
+    fold(std::true_type());
+  else
+    fold(std::false_type());
 
   // This lane's pair in the table: destination pj, slot pu.
   const int pj = lane / NP, pu = lane % NP;
@@ -286,7 +290,7 @@ bool bwd_fast_ok(const BwdArgs& a) {
   if (a.dtype != kBF16 || a.H != 1 || a.N != 8 || a.S != 4 || a.T < 1) return false;
   if (bwd_ch(a.d) == 0 || a.slots < 1) return false;
   return aligned16b(a.reps) && aligned16b(a.partials) && aligned16b(a.dh) && aligned16b(a.d_reps) &&
-         aligned16b(a.d_partials) && aligned16b(a.zslots);
+         aligned16b(a.d_partials) && aligned16b(a.zslots) && aligned16b(a.w) && aligned16b(a.gain);
 }
 
 hipError_t launch_bwd_fast(const BwdArgs& a, int64_t* slots_used, hipStream_t st) {

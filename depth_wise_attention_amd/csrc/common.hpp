@@ -28,6 +28,23 @@ __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
+// q = w * g (G) or q = w for 8 consecutive channels, 16-byte aligned rows,
+// with vector loads.  Callers branch on the gain once, outside their fold
+// loops, and fold every chunk inside: a per-element branch on the gain makes
+// the compiler wait for each load in turn, and even a select lets it sink the
+// gain loads into a branch per chunk.
+template <bool G>
+__device__ __forceinline__ void fold_q8(const float* w, const float* g, float (&q)[8]) {
+  const float4 w0 = reinterpret_cast<const float4*>(w)[0], w1 = reinterpret_cast<const float4*>(w)[1];
+  q[0] = w0.x; q[1] = w0.y; q[2] = w0.z; q[3] = w0.w;
+  q[4] = w1.x; q[5] = w1.y; q[6] = w1.z; q[7] = w1.w;
+  if constexpr (G) {
+    const float4 g0 = reinterpret_cast<const float4*>(g)[0], g1 = reinterpret_cast<const float4*>(g)[1];
+    q[0] *= g0.x; q[1] *= g0.y; q[2] *= g0.z; q[3] *= g0.w;
+    q[4] *= g1.x; q[5] *= g1.y; q[6] *= g1.z; q[7] *= g1.w;
+  }
+}
+
 template <typename E> __device__ __forceinline__ float ld(const E* p);
 template <> __device__ __forceinline__ float ld<float>(const float* p) { return *p; }
 template <> __device__ __forceinline__ float ld<bf16_t>(const bf16_t* p) { return bf2f(*p); }

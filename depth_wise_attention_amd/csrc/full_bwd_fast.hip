@@ -46,15 +46,18 @@ __global__ __launch_bounds__(256) void k_full_qtsplit(FullBwdArgs a, uint4* qt) 
     const int b = (int)((x / 64) % 2);
     const int64_t c = x / 128;
     const int64_t k = 32 * c + n;
+    // Unconditional loads (rows past n_dst read row n_dst - 1, then store zero)
+    // so the 16 loads are in flight together.
+    const bool has_g = a.gain != nullptr;
+    const float* gsrc = has_g ? a.gain : a.w;
+    const int64_t gld = has_g ? a.gain_ld : a.d;
     float hi[8], lo[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int j = transposed_row(b, h, e);
-      float q = 0.f;
-      if (j < a.n_dst) {
-        q = a.w[j * a.d + k];
-        if (a.gain) q *= a.gain[j * a.gain_ld + k];
-      }
+      const int jc = j < a.n_dst ? j : (int)a.n_dst - 1;
+      const float wv = a.w[jc * a.d + k], gv = gsrc[jc * gld + k];
+      const float q = j < a.n_dst ? (has_g ? wv * gv : wv) : 0.f;
       hi[e] = bf2f(f2bf(q));
       lo[e] = q - hi[e];
     }
@@ -73,16 +76,18 @@ __global__ __launch_bounds__(256) void k_full_bwd_qsplit(FullBwdArgs a, uint4* q
     const int64_t gs = x / 64;
     const int j = lane % 32;
     const int64_t k0 = gs * 16 + 8 * (lane / 32);
-    float hi[8], lo[8];
+    const bool has_g = a.gain != nullptr;
+    const int jc = j < a.n_dst ? j : (int)a.n_dst - 1;
+    float q[8], hi[8], lo[8];
+    if (has_g)
+      fold_q8<true>(a.w + jc * a.d + k0, a.gain + jc * a.gain_ld + k0, q);
+    else
+      fold_q8<false>(a.w + jc * a.d + k0, nullptr, q);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float q = 0.f;
-      if (j < a.n_dst) {
-        q = a.w[j * a.d + k0 + e];
-        if (a.gain) q *= a.gain[j * a.gain_ld + k0 + e];
-      }
-      hi[e] = bf2f(f2bf(q));
-      lo[e] = q - hi[e];
+      const float qe = j < a.n_dst ? q[e] : 0.f;
+      hi[e] = bf2f(f2bf(qe));
+      lo[e] = qe - hi[e];
     }
     qpk[gs * 2 * 64 + lane] = pack8(hi[0], hi[1], hi[2], hi[3], hi[4], hi[5], hi[6], hi[7]);
     qpk[gs * 2 * 64 + 64 + lane] = pack8(lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]);
@@ -477,7 +482,7 @@ bool full_bwd_fast_ok(const FullBwdArgs& a) {
   if (a.n_src > kTile || a.n_dst > a.n_src) return false;
   if (a.d % (2 * kBW * kChunk) != 0 || a.d > ((int64_t)1 << 16)) return false;
   if (a.zslots == nullptr || a.ws_bytes < full_bwd_fast_workspace_bytes(a.n_dst, a.T, a.d)) return false;
-  return al16(a.src) && al16(a.dout) && al16(a.d_src) && al16(a.zslots);
+  return al16(a.src) && al16(a.dout) && al16(a.d_src) && al16(a.zslots) && al16(a.w) && al16(a.gain);
 }
 
 hipError_t launch_full_bwd_fast(const FullBwdArgs& a, const float** slabs, int64_t* n_slabs, hipStream_t st) {

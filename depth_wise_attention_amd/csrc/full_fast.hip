@@ -49,16 +49,19 @@ __global__ __launch_bounds__(256) void k_full_qsplit(FullArgs a, bf16_t* qpk) {
     const int64_t gs = x / 64;  // g * 4 + s
     const int j = lane % 32;
     const int64_t k0 = gs * 16 + 8 * (lane / 32);
-    float hi[8], lo[8];
+    // Rows past n_dst load row n_dst - 1 (in bounds, no branch) and store zeros.
+    const bool has_g = a.gain != nullptr;
+    const int jc = j < a.n_dst ? j : (int)a.n_dst - 1;
+    float q[8], hi[8], lo[8];
+    if (has_g)
+      fold_q8<true>(a.w + jc * a.d + k0, a.gain + jc * a.gain_ld + k0, q);
+    else
+      fold_q8<false>(a.w + jc * a.d + k0, nullptr, q);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float q = 0.f;
-      if (j < a.n_dst) {
-        q = a.w[j * a.d + k0 + e];
-        if (a.gain) q *= a.gain[j * a.gain_ld + k0 + e];
-      }
-      hi[e] = bf2f(f2bf(q));
-      lo[e] = q - hi[e];
+      const float qe = j < a.n_dst ? q[e] : 0.f;
+      hi[e] = bf2f(f2bf(qe));
+      lo[e] = qe - hi[e];
     }
     uint4* dst = reinterpret_cast<uint4*>(qpk) + gs * 2 * 64 + lane;
     dst[0] = pack8(hi[0], hi[1], hi[2], hi[3], hi[4], hi[5], hi[6], hi[7]);
@@ -529,7 +532,7 @@ bool full_fast_ok(const FullArgs& a) {
   if (a.d % (2 * kFW * kChunk) != 0 || a.d > ((int64_t)1 << 16)) return false;
   const size_t need = full_fast_workspace_bytes(a.n_src, a.n_dst, a.d, a.H, a.dtype);
   if (a.ws == nullptr || a.ws_bytes < need) return false;
-  return al16(a.src) && al16(a.out) && al16(a.ws);
+  return al16(a.src) && al16(a.out) && al16(a.ws) && al16(a.w) && al16(a.gain);
 }
 
 template <int NCH>

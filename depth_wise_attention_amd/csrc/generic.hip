@@ -55,7 +55,8 @@ __device__ void depth_read_wave(RowFn row, int n, float r_lane, int d, int H, co
       const E* v = row(i);
       float acc = 0.f;
       for (int k = c0 + lane; k < c1; k += kWave) {
-        const float q = g ? w[k] * g[k] : w[k];
+        const float gk = (g ? g : w)[k];  // unconditional load: no wait per channel
+        const float q = g ? w[k] * gk : w[k];
         acc = fmaf(q, ld(v + k), acc);
       }
       acc = wave_sum(acc);
@@ -164,7 +165,8 @@ __global__ __launch_bounds__(256) void k_phase2_generic(Phase2Args a) {
       const int c0 = h * hd, c1 = c0 + hd;
       float acc = 0.f;
       for (int k = c0 + lane; k < c1; k += kWave) {
-        const float q = a.gain ? a.w[k] * a.gain[k] : a.w[k];
+        const float gk = (a.gain ? a.gain : a.w)[k];  // unconditional load
+        const float q = a.gain ? a.w[k] * gk : a.w[k];
         acc = fmaf(q, ld(p + k), acc);
       }
       const float s_p = r * wave_sum(acc);
@@ -214,9 +216,11 @@ __global__ __launch_bounds__(256) void k_bwd_generic(BwdArgs a) {
   float* z = a.zslots + wave * (int64_t)S * d;
   for (int64_t k = lane; k < (int64_t)S * d; k += kWave) z[k] = 0.f;
 
+  const float* gq = a.gain ? a.gain : a.w;  // unconditional loads in q()
+  const int64_t gld = a.gain ? a.gain_ld : (int64_t)d;
   auto q = [&](int j, int k) {
-    const float wq = a.w[(int64_t)j * d + k];
-    return a.gain ? wq * a.gain[j * a.gain_ld + k] : wq;
+    const float wq = a.w[(int64_t)j * d + k], gv = gq[j * gld + k];
+    return a.gain ? wq * gv : wq;
   };
   for (int64_t t = wave; t < T; t += nw) {
     auto src = [&](int i) { return (i < N ? reps + i * td : parts + (i - N) * td) + t * d; };
@@ -334,9 +338,11 @@ __global__ __launch_bounds__(256) void k_full_bwd_generic(FullBwdArgs a) {
   float* z = a.zslots + wave * (int64_t)n_dst * d;
   for (int64_t k = lane; k < (int64_t)n_dst * d; k += kWave) z[k] = 0.f;
 
+  const float* gq = a.gain ? a.gain : a.w;  // unconditional loads in q()
+  const int64_t gld = a.gain ? a.gain_ld : (int64_t)d;
   auto q = [&](int j, int k) {
-    const float wq = a.w[(int64_t)j * d + k];
-    return a.gain ? wq * a.gain[j * a.gain_ld + k] : wq;
+    const float wq = a.w[(int64_t)j * d + k], gv = gq[j * gld + k];
+    return a.gain ? wq * gv : wq;
   };
   for (int64_t t = wave; t < T; t += nw) {
     auto row = [&](int i) { return src + i * td + t * d; };
