@@ -10,7 +10,7 @@ in HBM before timing starts.
 Prints ONE JSON line on stdout.  Everything else goes to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                  [--no-extra] [--workload block|mhar|full|bwd|full_bwd|block_update]
+                  [--no-extra] [--workload block|mhar|full|bwd|full_bwd|block_update|decode]
                   [--copy-calibration]
 """
 
@@ -38,7 +38,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="block", choices=["block", "mhar", "full", "bwd", "full_bwd", "block_update"])
+    p.add_argument("--workload", default="block", choices=["block", "mhar", "full", "bwd", "full_bwd", "block_update",
+                                                                "decode"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     p.add_argument("--copy-calibration", action="store_true",
@@ -248,6 +249,74 @@ def bench_update(args, T=16384):
     )
 
 
+def bench_decode(args, Ts=(1, 16, 64, 256), iters=200):
+    """Decode-size latency: one block step (Phase 1 + S-1 fused updates, d=4096,
+    N=8, S=4) and one Full AttnRes sublayer (one destination over 32 sources,
+    d=2048), per call, launched eagerly and replayed from a captured HIP graph."""
+    import torch
+    import depth_wise_attention_amd as ar
+
+    def timed(fn):
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / iters
+
+    def graphed(fn):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        return timed(g.replay)
+
+    out = {}
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    for T in Ts:
+        N, S, d = 8, 4, 4096
+        reps = torch.randn((N, T, d), device="cuda", generator=gen).to(torch.bfloat16)
+        f = torch.randn((S - 1, T, d), device="cuda", generator=gen).to(torch.bfloat16)
+        w = torch.randn((S, d), device="cuda", generator=gen) / d ** 0.5
+        g = 1 + 0.1 * torch.randn((S, d), device="cuda", generator=gen)
+        h = torch.empty((S, T, d), dtype=torch.bfloat16, device="cuda")
+        st = torch.empty((S - 1, T, d), dtype=torch.float16, device="cuda")
+        lse = torch.empty((S, 1, T), device="cuda")
+        sc = torch.empty((T,), device="cuda")
+        part = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+        rms = torch.empty((S - 1, T), device="cuda")
+
+        def block_step():
+            ar.attnres_block_phase1(reps, w, g, 1e-6, 1, h_first=h[0], o_state=st, lse=lse, o_scale=sc)
+            for i in range(2, S + 1):
+                ar.attnres_block_phase2_merge_update(st[i - 2], lse[i - 1], None if i == 2 else part, f[i - 2],
+                                                     w[i - 1], g[i - 1], 1e-6, 1, partial_out=part, h_i=h[i - 1],
+                                                     norm_eps=1e-6, h_inv_rms=rms[i - 2], o_scale=sc)
+
+        L, dF = 32, 2048
+        src = torch.randn((L, T, dF), device="cuda", generator=gen).to(torch.bfloat16)
+        wF = torch.randn((1, dF), device="cuda", generator=gen) / dF ** 0.5
+        outF = torch.empty((1, T, dF), dtype=torch.bfloat16, device="cuda")
+        wsF = torch.empty(max(1, ar.attnres_full_fwd_workspace_size(L, 1, dF, 1, ar.BF16)), dtype=torch.uint8,
+                          device="cuda")
+
+        def full_sublayer():
+            ar.attnres_full_fwd(src, wF, None, 1e-6, 1, out=outF, ws=wsF)
+
+        out[f"T{T}"] = dict(block_step_eager_us=timed(block_step), block_step_graph_us=graphed(block_step),
+                            full_sublayer_eager_us=timed(full_sublayer), full_sublayer_graph_us=graphed(full_sublayer))
+    return dict(name="decode_latency_block_d4096_N8_S4_full_d2048_L32", **out)
+
+
 def bench_full(args, T=4096):
     import torch
     import depth_wise_attention_amd as ar
@@ -394,7 +463,7 @@ def main():
     if args.workload != "block":
         fn = {"mhar": lambda: bench_block(args, H=8, T=32768), "full": lambda: bench_full(args),
               "bwd": lambda: bench_bwd(args), "full_bwd": lambda: bench_full_bwd(args),
-              "block_update": lambda: bench_update(args)}[args.workload]
+              "block_update": lambda: bench_update(args), "decode": lambda: bench_decode(args)}[args.workload]
         log(json.dumps(fn()))
         return
 
@@ -407,7 +476,8 @@ def main():
     if not args.no_extra:
         torch.cuda.empty_cache()
         for fn in (lambda: bench_block(args, H=8, T=32768, with_events=True), lambda: bench_full(args),
-                   lambda: bench_bwd(args), lambda: bench_full_bwd(args), lambda: bench_update(args)):
+                   lambda: bench_bwd(args), lambda: bench_full_bwd(args), lambda: bench_update(args),
+                   lambda: bench_decode(args)):
             r = fn()
             extra[r.pop("name")] = {k: v for k, v in r.items() if k not in ("T", "d", "N", "S", "H")}
             torch.cuda.empty_cache()

@@ -24,5 +24,6 @@ from .binding import (  # noqa: F401
     attnres_version,
     lib,
     mhar_fwd,
+    mhar_fwd_chunked,
     mhar_fwd_workspace_size,
 )

@@ -48,6 +48,7 @@ def lib() -> ctypes.CDLL:
                                                     vp, vp, f32, vp, vp]
     L.mhar_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i32]
     L.mhar_fwd.argtypes = [vp, i64, vp, i64, i64, i64, vp, vp, i64, f32, i32, i32, vp, vp, sz, vp]
+    L.mhar_fwd_chunked.argtypes = [vp, i64, vp, i64, i64, i64, vp, vp, i64, f32, i32, i32, vp, i64, vp, sz, vp]
     L.attnres_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i32]
     L.attnres_bwd.argtypes = [vp, i64, vp, i64, i64, i64, vp, vp, i64, f32, i32, i32, vp, vp, vp, vp,
                               vp, i32, vp, sz, vp]
@@ -56,7 +57,7 @@ def lib() -> ctypes.CDLL:
                                    sz, vp]
     L.attnres_set_kernel_policy.argtypes = [i32]
     for name in ("attnres_full_fwd", "attnres_block_phase1", "attnres_block_phase2_merge",
-                 "attnres_block_phase2_merge_update", "mhar_fwd",
+                 "attnres_block_phase2_merge_update", "mhar_fwd", "mhar_fwd_chunked",
                  "attnres_bwd", "attnres_full_bwd", "attnres_version", "attnres_set_kernel_policy"):
         getattr(L, name).restype = ctypes.c_int
     L.attnres_full_fwd_workspace_size.restype = sz
@@ -107,15 +108,17 @@ def _torch():
     return torch
 
 
+_CODES = {}
+
+
 def _code(t) -> int:
-    torch = _torch()
-    if t.dtype == torch.float32:
-        return F32
-    if t.dtype == torch.bfloat16:
-        return BF16
-    if t.dtype == torch.float16:
-        return F16
-    raise TypeError(f"unsupported dtype {t.dtype}")
+    if not _CODES:
+        torch = _torch()
+        _CODES.update({torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16})
+    code = _CODES.get(t.dtype)
+    if code is None:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return code
 
 
 def _nbytes(t) -> int:
@@ -131,9 +134,13 @@ def _p(t) -> Optional[int]:
 
 
 def _stream(stream) -> int:
-    torch = _torch()
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return s.cuda_stream
+    """Raw HIP stream: the given torch stream, else torch's current stream on the
+    current device (read without building a Stream object: at decode sizes the
+    call overhead is comparable to the kernels)."""
+    if stream is not None:
+        return stream.cuda_stream
+    C = _torch()._C
+    return C._cuda_getCurrentRawStream(C._cuda_getDevice())
 
 
 def _gain(gain, rows: int, d: int):
@@ -248,6 +255,24 @@ def mhar_fwd(reps, partials, w, gain=None, eps: float = 1e-6, H: int = 1, h=None
     gp, gld = _gain(gain, S, d)
     _check(lib().mhar_fwd(_p(reps), N, _p(partials) if S > 1 else None, S, T, d, _p(w), gp, gld, eps, H,
                           _code(reps), _p(h), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return h
+
+
+def mhar_fwd_chunked(reps, partials, w, chunk_T: int, gain=None, eps: float = 1e-6, H: int = 1, h=None, ws=None,
+                     stream=None):
+    """mhar_fwd over T-chunks of chunk_T tokens, with a workspace sized for one chunk."""
+    torch = _torch()
+    N, T, d = reps.shape
+    S = w.shape[0]
+    if h is None:
+        h = torch.empty((S, T, d), dtype=reps.dtype, device=reps.device)
+    need = mhar_fwd_workspace_size(N, S, max(1, min(T, chunk_T)), d, H)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=reps.device)
+    gp, gld = _gain(gain, S, d)
+    _check(lib().mhar_fwd_chunked(_p(reps), N, _p(partials) if S > 1 else None, S, T, d, _p(w), gp, gld, eps, H,
+                                  _code(reps), _p(h), chunk_T, _p(ws), ws.numel() * ws.element_size(),
+                                  _stream(stream)))
     return h
 
 

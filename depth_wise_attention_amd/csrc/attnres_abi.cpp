@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -155,13 +156,46 @@ int num_cus() {
   cache[dev].store(v, std::memory_order_relaxed);
   return v;
 }
+
+// The occupancy query is a host call that costs microseconds; at decode sizes
+// a launch is itself a few microseconds, so the answer is kept per device,
+// kernel and block size.
+hipError_t blocks_per_cu(const void* kern, int block, int* out) {
+  struct Entry {
+    int dev;
+    const void* kern;
+    int block;
+    int value;
+  };
+  static std::mutex mu;
+  static Entry table[256];
+  static int used = 0;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used; ++i)
+      if (table[i].dev == dev && table[i].kern == kern && table[i].block == block) {
+        *out = table[i].value;
+        return hipSuccess;
+      }
+  }
+  int v = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kern, block, 0);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  if (used < 256) table[used++] = Entry{dev, kern, block, v};
+  *out = v;
+  return hipSuccess;
+}
 }  // namespace attnres
 
 extern "C" {
 
 const char* attnres_last_error(void) { return g_err; }
 
-int attnres_version(void) { return (2 << 16) | 2; }
+int attnres_version(void) { return (2 << 16) | 3; }
 
 int attnres_set_kernel_policy(int32_t policy) {
   if (policy != 0 && policy != 1) return fail(ATTNRES_ERR_INVALID, "unknown kernel policy %d", policy);
@@ -343,21 +377,65 @@ size_t mhar_fwd_workspace_size(int64_t N, int64_t S, int64_t T, int64_t d, int32
   return align_up((size_t)st) + align_up((size_t)ls) + align_up((size_t)sc);
 }
 
-int mhar_fwd(const void* reps, int64_t N, const void* partials, int64_t S, int64_t T, int64_t d,
-             const float* w, const float* gain, int64_t gain_ld, float eps, int32_t H, int32_t dtype,
-             void* h, void* ws, size_t ws_bytes, hipStream_t stream) {
-  clear_error();
+namespace {
+
+// One block over tokens [t0, t0 + C) of a T-token sequence: Phase 1, then the
+// S - 1 merges, with the state and statistics of those C tokens in ws.
+int run_block_chunk(const void* reps, int64_t N, const void* partials, int64_t S, int64_t T, int64_t t0,
+                    int64_t C, int64_t d, const float* w, const float* gain, int64_t gain_ld, float eps,
+                    int32_t H, int32_t dtype, void* h, void* ws, hipStream_t stream) {
+  (void)N;
+  const int64_t es = (int64_t)dt_size(dtype), td = T * d, cd = C * d;
+  // State between the phases: the scaled fp16 state for bf16 I/O, fp32 for fp32 I/O.
+  const int sdt = dtype == ATTNRES_BF16 ? ATTNRES_F16 : ATTNRES_F32;
+  const int64_t se = (int64_t)dt_size(sdt);
+  char* state = static_cast<char*>(ws);                                     // [S-1, C, d]
+  char* base = static_cast<char*>(ws) + align_up((size_t)((S - 1) * cd * 4));
+  float* lse = reinterpret_cast<float*>(base);                              // [S, H, C]
+  float* oscale = reinterpret_cast<float*>(base + align_up((size_t)(S * H * C * 4)));  // [C]
+  const char* r0 = static_cast<const char*>(reps) + t0 * d * es;
+  char* h0 = static_cast<char*>(h) + t0 * d * es;
+  const int64_t gld = gain ? gain_ld : 0;
+  Phase1Args p1{r0, N, C, d, w, S, gain, gld, eps, H, dtype, h0, dtype, state, sdt, lse,
+                sdt == ATTNRES_F16 ? oscale : nullptr};
+  p1.rep_stride = td;
+  RETURN_IF(run_phase1(p1, stream));
+  for (int64_t i = 2; i <= S; ++i) {
+    Phase2Args p2{state + (i - 2) * cd * se,
+                  sdt,
+                  sdt == ATTNRES_F16 ? oscale : nullptr,
+                  lse + (i - 1) * H * C,
+                  static_cast<const char*>(partials) + ((i - 2) * td + t0 * d) * es,
+                  C,
+                  d,
+                  w + (i - 1) * d,
+                  gain ? gain + (i - 1) * gld : nullptr,
+                  eps,
+                  H,
+                  dtype,
+                  h0 + (i - 1) * td * es};
+    RETURN_IF(run_phase2(p2, stream));
+  }
+  return ATTNRES_OK;
+}
+
+// Validation shared by mhar_fwd and mhar_fwd_chunked; chunk tokens per pass.
+int mhar_common(const void* reps, int64_t N, const void* partials, int64_t S, int64_t T, int64_t d,
+                const float* w, const float* gain, int64_t gain_ld, float eps, int32_t H, int32_t dtype,
+                void* h, int64_t chunk, void* ws, size_t ws_bytes, hipStream_t stream) {
   int64_t td = 0;
   RETURN_IF(check_common(T, d, H, dtype, eps, gain, gain_ld, &td));
   if (N < 1 || N > kMaxSources - 1)
     return fail(ATTNRES_ERR_INVALID, "N = %lld must be in [1, %d]", (long long)N, kMaxSources - 1);
   if (S < 1) return fail(ATTNRES_ERR_INVALID, "S = %lld must be >= 1", (long long)S);
+  if (chunk < 1) return fail(ATTNRES_ERR_INVALID, "chunk_T = %lld must be >= 1", (long long)chunk);
   if (T == 0) return ATTNRES_OK;
   REQUIRE_PTR(reps, "reps");
   REQUIRE_PTR(w, "w");
   REQUIRE_PTR(h, "h");
   if (S > 1) REQUIRE_PTR(partials, "partials");
-  const size_t need = mhar_fwd_workspace_size(N, S, T, d, H);
+  const int64_t C = chunk < T ? chunk : T;
+  const size_t need = mhar_fwd_workspace_size(N, S, C, d, H);
   if (need == 0) return fail(ATTNRES_ERR_INVALID, "workspace size overflows");
   if (ws == nullptr || ws_bytes < need)
     return fail(ATTNRES_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? ws_bytes : 0,
@@ -373,36 +451,30 @@ int mhar_fwd(const void* reps, int64_t N, const void* partials, int64_t S, int64
                        {gain, gain ? (size_t)((gain_ld ? S : 1) * d * 4) : 0, "gain"}};
   const Range outs[] = {{h, b_h, "h"}, {ws, need, "ws"}};
   RETURN_IF(check_aliasing(ins, 4, outs, 2));
-
-  // State between the phases: the scaled fp16 state for bf16 I/O, fp32 for fp32 I/O.
-  const int sdt = dtype == ATTNRES_BF16 ? ATTNRES_F16 : ATTNRES_F32;
-  const int64_t se = (int64_t)dt_size(sdt);
-  char* state = static_cast<char*>(ws);                                     // [S-1, T, d]
-  char* base = static_cast<char*>(ws) + align_up((size_t)((S - 1) * td * 4));
-  float* lse = reinterpret_cast<float*>(base);                              // [S, H, T]
-  float* oscale = reinterpret_cast<float*>(base + align_up((size_t)(S * H * T * 4)));  // [T]
-  const float* g = gain;
-  const int64_t gld = gain ? gain_ld : 0;
-  Phase1Args p1{reps, N, T, d, w, S, g, gld, eps, H, dtype, h, dtype, state, sdt, lse,
-                sdt == ATTNRES_F16 ? oscale : nullptr};
-  RETURN_IF(run_phase1(p1, stream));
-  for (int64_t i = 2; i <= S; ++i) {
-    Phase2Args p2{state + (i - 2) * td * se,
-                  sdt,
-                  sdt == ATTNRES_F16 ? oscale : nullptr,
-                  lse + (i - 1) * H * T,
-                  static_cast<const char*>(partials) + (i - 2) * td * es,
-                  T,
-                  d,
-                  w + (i - 1) * d,
-                  g ? g + (i - 1) * gld : nullptr,
-                  eps,
-                  H,
-                  dtype,
-                  static_cast<char*>(h) + (i - 1) * td * es};
-    RETURN_IF(run_phase2(p2, stream));
+  for (int64_t t0 = 0; t0 < T; t0 += C) {
+    const int64_t c = T - t0 < C ? T - t0 : C;
+    RETURN_IF(run_block_chunk(reps, N, partials, S, T, t0, c, d, w, gain, gain_ld, eps, H, dtype, h, ws,
+                              stream));
   }
   return ATTNRES_OK;
+}
+
+}  // namespace
+
+int mhar_fwd(const void* reps, int64_t N, const void* partials, int64_t S, int64_t T, int64_t d,
+             const float* w, const float* gain, int64_t gain_ld, float eps, int32_t H, int32_t dtype,
+             void* h, void* ws, size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  return mhar_common(reps, N, partials, S, T, d, w, gain, gain_ld, eps, H, dtype, h, T > 0 ? T : 1, ws,
+                     ws_bytes, stream);
+}
+
+int mhar_fwd_chunked(const void* reps, int64_t N, const void* partials, int64_t S, int64_t T, int64_t d,
+                     const float* w, const float* gain, int64_t gain_ld, float eps, int32_t H,
+                     int32_t dtype, void* h, int64_t chunk_T, void* ws, size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  return mhar_common(reps, N, partials, S, T, d, w, gain, gain_ld, eps, H, dtype, h, chunk_T, ws, ws_bytes,
+                     stream);
 }
 
 size_t attnres_bwd_workspace_size(int64_t N, int64_t S, int64_t T, int64_t d, int32_t H) {

@@ -160,14 +160,15 @@ constexpr bool kP2Prefetch = ATTNRES_P2_PREFETCH != 0;
 constexpr bool kP2QLds = ATTNRES_P2_QLDS != 0;
 
 // ------------------------------------------------------------------ Phase 1
+// rs: elements between consecutive reps.
 template <int N, int CH, int B>
-__device__ __forceinline__ void load_reps(uint4 (&v)[N][CH], const bf16_t* reps, int64_t T, int d,
+__device__ __forceinline__ void load_reps(uint4 (&v)[N][CH], const bf16_t* reps, int64_t rs, int d,
                                           int64_t t, int tid) {
 #pragma unroll
   for (int i = 0; i < N; ++i)
 #pragma unroll
     for (int c = 0; c < CH; ++c)
-      v[i][c] = ld16<kP1Nt>(reps + ((int64_t)i * T + t) * d + (c * B + tid) * 8);
+      v[i][c] = ld16<kP1Nt>(reps + (int64_t)i * rs + t * d + (c * B + tid) * 8);
 }
 
 // q = w * g into this thread's own LDS slots (fp32, two float4 per chunk).  Kept
@@ -263,14 +264,15 @@ __global__ __launch_bounds__(B, ATTNRES_P1_MINWAVES) void k_phase1_fast(Phase1Ar
                              : (sm_valid && sm_i == 0 && wave == 0);
 
   const bf16_t* reps = static_cast<const bf16_t*>(a.reps);
+  const int64_t rs = a.rep_stride != 0 ? a.rep_stride : T * d;
   int buf = 0;
   uint4 v[N][CH];
   int64_t t = blockIdx.x;
-  if (t < T) load_reps<N, CH, B>(v, reps, T, d, t, tid);
+  if (t < T) load_reps<N, CH, B>(v, reps, rs, d, t, tid);
   for (; t < T; t += gridDim.x) {
     const int64_t tn = t + gridDim.x;
     uint4 vn[N][CH];
-    if (kP1Prefetch && tn < T) load_reps<N, CH, B>(vn, reps, T, d, tn, tid);
+    if (kP1Prefetch && tn < T) load_reps<N, CH, B>(vn, reps, rs, d, tn, tid);
 
     float part[P];
 #pragma unroll
@@ -413,7 +415,7 @@ __global__ __launch_bounds__(B, ATTNRES_P1_MINWAVES) void k_phase1_fast(Phase1Ar
 #pragma unroll
         for (int c = 0; c < CH; ++c) v[i][c] = vn[i][c];
     } else {
-      if (tn < T) load_reps<N, CH, B>(v, reps, T, d, tn, tid);
+      if (tn < T) load_reps<N, CH, B>(v, reps, rs, d, tn, tid);
     }
   }
 }
@@ -634,7 +636,7 @@ hipError_t launch_p1(const Phase1Args& a, hipStream_t st) {
   } else {
   auto pick = [&](auto kern) -> hipError_t {
     int per_cu = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, B, 0);
+    hipError_t e = blocks_per_cu(reinterpret_cast<const void*>(kern), B, &per_cu);
     if (e != hipSuccess) return e;
     if (per_cu < 1) per_cu = 1;
     int64_t grid = (int64_t)num_cus() * per_cu;
@@ -684,7 +686,7 @@ template <int CPL>
 hipError_t launch_p2(const Phase2Args& a, hipStream_t st) {
   auto pick = [&](auto kern) -> hipError_t {
     int per_cu = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0);
+    hipError_t e = blocks_per_cu(reinterpret_cast<const void*>(kern), 256, &per_cu);
     if (e != hipSuccess) return e;
     if (per_cu < 1) per_cu = 1;
     int64_t grid = (int64_t)num_cus() * per_cu;

@@ -263,7 +263,7 @@ template <int N, int S, int CH, int B>
 hipError_t launch_bwd_nsb(const BwdArgs& a, int64_t* slots_used, hipStream_t st) {
   auto kern = k_bwd_fast<N, S, CH, B>;
   int per_cu = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, B, 0);
+  hipError_t e = blocks_per_cu(reinterpret_cast<const void*>(kern), B, &per_cu);
   if (e != hipSuccess) return e;
   if (per_cu < 1) per_cu = 1;
   int64_t grid = (int64_t)num_cus() * per_cu;

@@ -495,8 +495,8 @@ hipError_t launch_full_bwd_fast(const FullBwdArgs& a, const float** slabs, int64
   hipLaunchKernelGGL(k_full_qtsplit, dim3(64), dim3(256), 0, st, a, qt);
   int per_cu = 0;
   hipError_t e = a.accumulate
-                     ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_full_bwd_fast<true>, kBB, 0)
-                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_full_bwd_fast<false>, kBB, 0);
+                     ? blocks_per_cu(reinterpret_cast<const void*>(k_full_bwd_fast<true>), kBB, &per_cu)
+                     : blocks_per_cu(reinterpret_cast<const void*>(k_full_bwd_fast<false>), kBB, &per_cu);
   if (e != hipSuccess) return e;
   if (per_cu < 1) per_cu = 1;
   int64_t grid = (int64_t)num_cus() * per_cu;

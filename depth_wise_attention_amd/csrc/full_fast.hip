@@ -556,7 +556,7 @@ hipError_t launch_full_fast(const FullArgs& a, hipStream_t st) {
     }
   }
   int per_cu = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_full_fast, kFB, 0);
+  hipError_t e = blocks_per_cu(reinterpret_cast<const void*>(k_full_fast), kFB, &per_cu);
   if (e != hipSuccess) return e;
   if (per_cu < 1) per_cu = 1;
   int64_t grid = (int64_t)num_cus() * per_cu;

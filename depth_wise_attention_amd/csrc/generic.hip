@@ -107,11 +107,11 @@ template <typename E, typename O0, typename OR>
 __global__ __launch_bounds__(256) void k_phase1_generic(Phase1Args a) {
   const E* reps = static_cast<const E*>(a.reps);
   const int d = (int)a.d;
-  const int64_t T = a.T, td = a.T * a.d;
+  const int64_t T = a.T, rs = a.rep_stride != 0 ? a.rep_stride : a.T * a.d;
   const int64_t wave = (int64_t)blockIdx.x * kGenWaves + (threadIdx.x >> 6);
   const int64_t nw = (int64_t)gridDim.x * kGenWaves;
   for (int64_t t = wave; t < T; t += nw) {
-    auto row = [&](int i) { return reps + i * td + t * d; };
+    auto row = [&](int i) { return reps + i * rs + t * d; };
     float max_ss = 0.f;
     const float r_lane = inv_rms_lanes<E>(row, (int)a.N, d, a.eps, &max_ss);
     // A scaled fp16 state: |o| <= max_i ||v_i||_2 = sqrt(max_i ss_i) bounds every value.

@@ -47,6 +47,9 @@ struct Phase1Args {
   int orest_dtype;
   float* lse;     // [S, H, T]
   float* oscale;  // [T], written when orest_dtype == kF16: orest = o * (1 / oscale[t])
+  // Elements between consecutive reps (0: T * d).  A T-chunk of a longer
+  // sequence passes the full sequence's T * d with reps at the chunk's first token.
+  int64_t rep_stride = 0;
 };
 
 struct Phase2Args {
@@ -154,5 +157,7 @@ hipError_t launch_bwd_fast(const BwdArgs& a, int64_t* slots_used, hipStream_t st
 hipError_t launch_full_fast(const FullArgs& a, hipStream_t st);
 
 int num_cus();  // compute units of the current device (cached per device)
+// Resident blocks per compute unit for a kernel and block size (cached).
+hipError_t blocks_per_cu(const void* kern, int block, int* out);
 
 }  // namespace attnres

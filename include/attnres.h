@@ -199,6 +199,23 @@ int mhar_fwd(const void* reps, int64_t N, const void* partials, int64_t S, int64
              int32_t dtype, void* h, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * mhar_fwd over the tokens in chunks of chunk_T (the last chunk may be
+ * shorter), for a workspace bounded by the chunk instead of the sequence
+ * (b-lab.team summary §3 Inference: prefill may run in chunks; tokens never
+ * interact in the routing, so the result is bit-identical to mhar_fwd).
+ * Each chunk is one Phase 1 launch and S - 1 merge launches, in token order,
+ * on the stream.
+ *
+ *  ws  device workspace of at least
+ *      mhar_fwd_workspace_size(N, S, min(T, chunk_T), d, H) bytes
+ * Other arguments as for mhar_fwd; chunk_T >= 1.
+ */
+int mhar_fwd_chunked(const void* reps, int64_t N, const void* partials, int64_t S, int64_t T,
+                     int64_t d, const float* w, const float* gain, int64_t gain_ld, float eps,
+                     int32_t H, int32_t dtype, void* h, int64_t chunk_T, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/*
  * Bytes of device workspace attnres_bwd needs (fp32 partial sums of the
  * pseudo-query gradient, one [S, d] slab per slot, min(T, 1024) slots).
  */
@@ -270,7 +287,8 @@ int attnres_full_bwd(const void* src, int64_t n_src, int64_t T, int64_t d, const
                      int32_t accumulate, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ABI version: (major << 16) | minor.  Major 2 added the Full-forward workspace;
- * minor 1 added the Full backward, minor 2 the fused Phase 2 update. */
+ * minor 1 added the Full backward, minor 2 the fused Phase 2 update, minor 3 the
+ * chunked block forward. */
 int attnres_version(void);
 
 /*

@@ -39,7 +39,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("attnres_full_fwd", "attnres_block_phase1", "attnres_block_phase2_merge",
-                 "attnres_block_phase2_merge_update", "mhar_fwd",
+                 "attnres_block_phase2_merge_update", "mhar_fwd", "mhar_fwd_chunked",
                  "attnres_bwd", "attnres_full_bwd", "attnres_full_fwd_workspace_size", "mhar_fwd_workspace_size",
                  "attnres_bwd_workspace_size", "attnres_full_bwd_workspace_size",
                  "attnres_last_error", "attnres_version", "attnres_set_kernel_policy"):
@@ -54,7 +54,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_policy():
     assert binding.attnres_version() >> 16 == 2
-    assert binding.attnres_version() & 0xFFFF >= 2
+    assert binding.attnres_version() & 0xFFFF >= 3
     prev = binding.attnres_set_kernel_policy(1)
     assert binding.attnres_set_kernel_policy(prev) == 1
     with pytest.raises(binding.AttnResError):
@@ -235,6 +235,28 @@ def test_mhar_rejects_bad_arguments():
     assert _rc_mhar(ws=None) == EWS
     assert _rc_mhar(ws_bytes=16) == EWS
     assert "workspace" in binding.attnres_last_error()
+
+
+def _rc_chunked(**kw):
+    a = dict(reps=FAKE, N=8, partials=FAKE + (1 << 30), S=4, T=1000, d=64, w=FAKE + (2 << 30), gain=None,
+             gain_ld=0, eps=1e-6, H=1, dtype=BF16, h=FAKE + (3 << 30), chunk=100, ws=FAKE + (4 << 30),
+             ws_bytes=1 << 20)
+    a.update(kw)
+    return binding.lib().mhar_fwd_chunked(a["reps"], a["N"], a["partials"], a["S"], a["T"], a["d"], a["w"],
+                                          a["gain"], a["gain_ld"], a["eps"], a["H"], a["dtype"], a["h"],
+                                          a["chunk"], a["ws"], a["ws_bytes"], None)
+
+
+@fake_ptrs
+def test_mhar_chunked_rejects_bad_arguments():
+    for c in [dict(chunk=0), dict(chunk=-5), dict(N=0), dict(S=0), dict(reps=None), dict(h=None),
+              dict(partials=None), dict(H=3), dict(ws=FAKE + (3 << 30))]:
+        assert _rc_chunked(**c) == EINVAL, c
+    # the workspace is sized by the chunk: one byte short of a 100-token chunk fails
+    need = binding.mhar_fwd_workspace_size(8, 4, 100, 64, 1)
+    assert _rc_chunked(ws_bytes=need - 1) == EWS
+    assert binding.mhar_fwd_workspace_size(8, 4, 1000, 64, 1) > 5 * need
+    assert _rc_chunked(T=0, reps=None, h=None) == OK
 
 
 @fake_ptrs

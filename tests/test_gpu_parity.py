@@ -304,6 +304,39 @@ def test_empty_tokens_no_op():
     assert torch.count_nonzero(dw).item() == 0
 
 
+# ----------------------------------------------------------------- chunked prefill
+@pytest.mark.parametrize("T,d,H,dtype,chunks", [
+    (37, 512, 1, "bf16", (1, 5, 36, 37, 100)),
+    (300, 4096, 1, "bf16", (64, 128, 299)),
+    (200, 4096, 8, "bf16", (3, 77)),
+    (20, 96, 3, "f32", (7, 19)),
+])
+def test_mhar_chunked_matches_whole(T, d, H, dtype, chunks, policy):
+    """Chunked prefill: every chunk size gives the bits of the whole-sequence call
+    (tokens never interact), from a workspace sized for one chunk."""
+    say(f"mhar chunked T={T} d={d} H={H} {dtype} chunks={chunks} policy={policy}")
+    wl = synth.block_workload(T=T, d=d, N=8, S=4, H=H, rep_std_step=0.3, dtype=dtype, seed=31)
+    reps, parts, w, g = _block_on_gpu(wl, dtype, wl.gain)
+    whole = ar.mhar_fwd(reps, parts, w, g, wl.eps, H)
+    for c in chunks:
+        h = ar.mhar_fwd_chunked(reps, parts, w, c, g, wl.eps, H)
+        assert torch.equal(h, whole), f"chunk_T={c} differs from the whole-sequence call"
+    ref = orc.block_direct(wl.reps, wl.partials, wl.w, wl.gain, wl.eps, H)
+    check(host(whole), ref, dtype, "mhar_fwd")
+
+
+def test_mhar_chunked_workspace_reuse():
+    """One chunk-sized workspace serves several calls and sequence lengths."""
+    wl = synth.block_workload(T=513, d=2048, N=8, S=4, H=2, rep_std_step=0.3, dtype="bf16", seed=32)
+    say(f"mhar chunked workspace reuse T={wl.T}")
+    reps, parts, w, g = _block_on_gpu(wl, "bf16", wl.gain)
+    ws = torch.empty(ar.mhar_fwd_workspace_size(8, 4, 128, 2048, 2), dtype=torch.uint8, device=DEV)
+    whole = ar.mhar_fwd(reps, parts, w, g, wl.eps, 2)
+    for T in (513, 128, 1, 200):
+        h = ar.mhar_fwd_chunked(reps[:, :T].contiguous(), parts[:, :T].contiguous(), w, 128, g, wl.eps, 2, ws=ws)
+        assert torch.equal(h, whole[:, :T]), f"T={T}"
+
+
 # ----------------------------------------------------------------- backward
 @pytest.mark.parametrize("T,d,N,S,H,dtype,gain", [
     (4, 16, 8, 4, 1, "f32", "per"),
