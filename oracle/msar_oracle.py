@@ -1,0 +1,118 @@
+"""CPU oracle for MSAR, multi-stream depth attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and
+the benchmark's CPU-baseline leg may import this module.  The product path
+(the HIP library and its Python binding) never calls it, and it imports
+nothing from the product path.
+
+Plain, slow, float64 numpy, written from the onedev.kr summary of the MSAR
+paper ("Extending depth-wise attention to multiple streams"), sections "How it
+differs" (the streams, the per-stream depth softmax, the H^pre mixer) and "How
+to use it" (Block MSAR keeps one stream per source and expands the others on
+demand).
+
+The method, as computed here:
+  * Each residual source v_i [T, d] expands into m = 4 full-width streams:
+    stream 0 is v_i itself, streams 1..3 are causal depthwise 1-D
+    convolutions of v_i along the token axis with kernel sizes 4, 8 and 12.
+  * Each stream runs its own depth softmax with its own pseudo-query:
+    s_i^(r) = w^(r) . RMSNorm(v_i^(r)),  alpha^(r) = softmax_i(s^(r)),
+    Z^(r) = sum_i alpha_i^(r) v_i^(r)  (the weights of each stream sum to 1).
+  * The H^pre mixer: beta = sigmoid(RMSNorm(Flatten(Z)) P), P [m d, m];
+    h = sum_r beta_r Z^(r).
+
+Readings where the summary is silent (each also listed in the design notes):
+  * Tap k of a stream's kernel multiplies the source k tokens back (tap 0 is
+    the current token); tokens before the first one of the call are zero.  No
+    bias.
+  * The expansion belongs to the source (the streams are written v_i^(r), with
+    no destination index): one set of taps per source, packed as
+    conv [n_src, 24, d] with rows 0-3 for stream 1, 4-11 for stream 2 and
+    12-23 for stream 3.  Pseudo-queries and mixer belong to the destination:
+    w [n_dst, 4, d], P [n_dst, 4 d, 4].
+  * RMSNorm as in AttnRes (x / sqrt(mean x^2 + eps)), with no gain in either
+    place: a gain folds exactly into w (scores) and into P (mixer).
+  * Flatten(Z) concatenates the streams in order: [Z^(0), Z^(1), Z^(2), Z^(3)].
+  * The mixer has no bias term (the summary names RMSNorm, the md x m
+    projection and the sigmoid only).
+  * Destinations read causal prefixes of the sources as in Full AttnRes:
+    destination j of n_dst reads sources 0 .. n_src - n_dst + j.  A Block
+    MSAR sublayer is the n_dst = 1 call over its block reps and partial sum.
+"""
+
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+
+from .attnres_oracle import rms_normalise
+
+MSAR_STREAMS = 4
+MSAR_KERNEL_SIZES = (4, 8, 12)     # streams 1, 2, 3
+MSAR_TAP_OFFSETS = (0, 4, 12)      # first packed row of each conv stream
+MSAR_TAPS = 24
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def msar_expand(v, conv) -> np.ndarray:
+    """Streams of one source: v [T, d], conv [24, d] -> [4, T, d].
+
+    Stream r >= 1 at token t is sum_k conv[off_r + k] * v[t - k] over its
+    K_r taps, with v[t - k] = 0 before the first token."""
+    v = _f64(v)
+    conv = _f64(conv)
+    T, d = v.shape
+    out = np.zeros((MSAR_STREAMS, T, d))
+    out[0] = v
+    for r in range(1, MSAR_STREAMS):
+        K, off = MSAR_KERNEL_SIZES[r - 1], MSAR_TAP_OFFSETS[r - 1]
+        for k in range(min(K, T)):
+            out[r, k:] += conv[off + k] * v[:T - k]
+    return out
+
+
+def sigmoid(x) -> np.ndarray:
+    return 1.0 / (1.0 + np.exp(-_f64(x)))
+
+
+def msar_fwd(src, w, conv, P, eps: float = 1e-6, return_parts: bool = False):
+    """MSAR routing for n_dst destinations with causal-prefix source sets.
+
+    src [n_src, T, d]; w [n_dst, 4, d]; conv [n_src, 24, d]; P [n_dst, 4 d, 4].
+    Returns h [n_dst, T, d]; with return_parts also Z [n_dst, 4, T, d] and
+    beta [n_dst, T, 4]."""
+    src = _f64(src)
+    w = _f64(w)
+    P = _f64(P)
+    n_src, T, d = src.shape
+    n_dst = w.shape[0]
+    assert w.shape == (n_dst, MSAR_STREAMS, d) and P.shape == (n_dst, MSAR_STREAMS * d, MSAR_STREAMS)
+    assert 1 <= n_dst <= n_src and np.shape(conv) == (n_src, MSAR_TAPS, d)
+    streams = np.stack([msar_expand(src[i], conv[i]) for i in range(n_src)])   # [n_src, 4, T, d]
+    h = np.zeros((n_dst, T, d))
+    Z = np.zeros((n_dst, MSAR_STREAMS, T, d))
+    beta = np.zeros((n_dst, T, MSAR_STREAMS))
+    for j in range(n_dst):
+        n = n_src - n_dst + j + 1
+        for r in range(MSAR_STREAMS):
+            vals = streams[:n, r]                                  # [n, T, d]
+            keys = rms_normalise(vals, eps)
+            s = np.einsum("itc,c->it", keys, w[j, r])
+            s = s - s.max(axis=0, keepdims=True)
+            a = np.exp(s)
+            a /= a.sum(axis=0, keepdims=True)
+            Z[j, r] = np.einsum("it,itc->tc", a, vals)
+        flat = np.concatenate([Z[j, r] for r in range(MSAR_STREAMS)], axis=-1)   # [T, 4 d]
+        beta[j] = sigmoid(rms_normalise(flat, eps) @ P[j])
+        h[j] = np.einsum("tr,rtc->tc", beta[j], Z[j])
+    if return_parts:
+        return h, Z, beta
+    return h
+
+
+__all__ = ["MSAR_STREAMS", "MSAR_KERNEL_SIZES", "MSAR_TAP_OFFSETS", "MSAR_TAPS", "msar_expand", "sigmoid",
+           "msar_fwd"]
