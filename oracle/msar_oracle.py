@@ -25,11 +25,13 @@ Readings where the summary is silent (each also listed in the design notes):
   * Tap k of a stream's kernel multiplies the source k tokens back (tap 0 is
     the current token); tokens before the first one of the call are zero.  No
     bias.
-  * The expansion belongs to the source (the streams are written v_i^(r), with
-    no destination index): one set of taps per source, packed as
-    conv [n_src, 24, d] with rows 0-3 for stream 1, 4-11 for stream 2 and
+  * One set of three convolutions serves every source: the summary applies
+    "the" convolution r to each source and writes the streams v_i^(r) with no
+    destination index, while the pseudo-queries w_l^(r) carry one.  The taps
+    are packed as conv [24, d]: rows 0-3 for stream 1, 4-11 for stream 2 and
     12-23 for stream 3.  Pseudo-queries and mixer belong to the destination:
-    w [n_dst, 4, d], P [n_dst, 4 d, 4].
+    w [n_dst, 4, d], P [n_dst, 4 d, 4].  A model whose layers own different
+    taps makes one call per layer.
   * RMSNorm as in AttnRes (x / sqrt(mean x^2 + eps)), with no gain in either
     place: a gain folds exactly into w (scores) and into P (mixer).
   * Flatten(Z) concatenates the streams in order: [Z^(0), Z^(1), Z^(2), Z^(3)].
@@ -82,7 +84,7 @@ def sigmoid(x) -> np.ndarray:
 def msar_fwd(src, w, conv, P, eps: float = 1e-6, return_parts: bool = False):
     """MSAR routing for n_dst destinations with causal-prefix source sets.
 
-    src [n_src, T, d]; w [n_dst, 4, d]; conv [n_src, 24, d]; P [n_dst, 4 d, 4].
+    src [n_src, T, d]; w [n_dst, 4, d]; conv [24, d]; P [n_dst, 4 d, 4].
     Returns h [n_dst, T, d]; with return_parts also Z [n_dst, 4, T, d] and
     beta [n_dst, T, 4]."""
     src = _f64(src)
@@ -91,8 +93,8 @@ def msar_fwd(src, w, conv, P, eps: float = 1e-6, return_parts: bool = False):
     n_src, T, d = src.shape
     n_dst = w.shape[0]
     assert w.shape == (n_dst, MSAR_STREAMS, d) and P.shape == (n_dst, MSAR_STREAMS * d, MSAR_STREAMS)
-    assert 1 <= n_dst <= n_src and np.shape(conv) == (n_src, MSAR_TAPS, d)
-    streams = np.stack([msar_expand(src[i], conv[i]) for i in range(n_src)])   # [n_src, 4, T, d]
+    assert 1 <= n_dst <= n_src and np.shape(conv) == (MSAR_TAPS, d)
+    streams = np.stack([msar_expand(src[i], conv) for i in range(n_src)])      # [n_src, 4, T, d]
     h = np.zeros((n_dst, T, d))
     Z = np.zeros((n_dst, MSAR_STREAMS, T, d))
     beta = np.zeros((n_dst, T, MSAR_STREAMS))

@@ -27,10 +27,10 @@ def _case(seed, n_src=5, n_dst=3, T=17, d=8, taps="random"):
     src = r.standard_normal((n_src, T, d)) * (1 + 0.3 * np.arange(n_src))[:, None, None]
     w = r.standard_normal((n_dst, 4, d)) / np.sqrt(d)
     if taps == "random":
-        conv = r.standard_normal((n_src, 24, d)) / 3
+        conv = r.standard_normal((24, d)) / 3
     else:  # one tap: every stream is the source itself
-        conv = np.zeros((n_src, 24, d))
-        conv[:, [0, 4, 12], :] = 1.0
+        conv = np.zeros((24, d))
+        conv[[0, 4, 12], :] = 1.0
     P = r.standard_normal((n_dst, 4 * d, 4)) / np.sqrt(4 * d)
     return src, w, conv, P
 
@@ -85,14 +85,14 @@ def pin_msar_mixer_closed_form():
 
 
 def pin_msar_identical_sources():
-    """Identical sources with identical taps: each stream's weights sum to 1,
-    so Z^(r) is the stream itself whatever the scores."""
+    """Identical sources: each stream's weights sum to 1, so Z^(r) is the
+    stream itself whatever the scores."""
     r = _rng(4)
     T, d = 15, 6
     u = r.standard_normal((T, d))
     taps = r.standard_normal((24, d))
     src = np.stack([u] * 4)
-    conv = np.stack([taps] * 4)
+    conv = taps
     w = r.standard_normal((2, 4, d))
     P = np.zeros((2, 4 * d, 4))
     h, Z, beta = mso.msar_fwd(src, w, conv, P, eps=1e-6, return_parts=True)
