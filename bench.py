@@ -10,7 +10,7 @@ in HBM before timing starts.
 Prints ONE JSON line on stdout.  Everything else goes to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                  [--no-extra] [--workload block|mhar|full|bwd|full_bwd|block_update|decode]
+                  [--no-extra] [--workload block|mhar|full|bwd|full_bwd|block_update|decode|msar]
                   [--copy-calibration]
 """
 
@@ -39,7 +39,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="block", choices=["block", "mhar", "full", "bwd", "full_bwd", "block_update",
-                                                                "decode"])
+                                                                "decode", "msar"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     p.add_argument("--copy-calibration", action="store_true",
@@ -317,6 +317,40 @@ def bench_decode(args, Ts=(1, 16, 64, 256), iters=200):
     return dict(name="decode_latency_block_d4096_N8_S4_full_d2048_L32", **out)
 
 
+def msar_flops(T, d, n):
+    """Algorithmic flops of one MSAR call with one destination over n sources:
+    per token and channel, 24 taps per source for the three convolved streams,
+    a square and a query product per source and stream for the scores, a
+    weighted sum per source and stream, and the mixer's squares (4), projections
+    (16) and output sum (4); two flops per multiply-add."""
+    return 2 * T * d * (n * (24 + 8 + 4) + 24)
+
+
+def bench_msar(args, T=16384, d=4096, n=9):
+    """A Block MSAR sublayer: one destination over 8 block reps and the partial."""
+    import torch
+    import depth_wise_attention_amd as ar
+    from workloads import synth
+
+    wl = synth.msar_workload(T=T, d=d, n_src=n, n_dst=1, dtype="bf16", seed=0)
+    src = to_dev(wl.src, torch.bfloat16)
+    w = to_dev(wl.w, torch.float32)
+    conv = to_dev(wl.meta["conv"], torch.float32)
+    mix = to_dev(wl.meta["mix"], torch.float32)
+    del wl
+    out = torch.empty((1, T, d), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(max(1, ar.attnres_msar_fwd_workspace_size(n, 1, T, d, ar.BF16)), dtype=torch.uint8,
+                     device="cuda")
+    fn = lambda: ar.attnres_msar_fwd(src, w, conv, mix, 1e-6, out=out, ws=ws)
+    total, wall = time_loop(fn, args.steps, args.warmup)
+    per = total / args.steps
+    flops = msar_flops(T, d, n)
+    nbytes = T * (n + 1) * d * 2
+    return dict(name=f"msar_block_sublayer_bf16_T{T}_d{d}_sources{n}", T=T, d=d, seconds=total,
+                tokens_per_s=T * args.steps / total, ms_per_call=per * 1e3, flops_per_call=flops,
+                tflops=flops / per / 1e12, bytes_per_call=nbytes, gbs=nbytes / per / 1e9)
+
+
 def bench_full(args, T=4096):
     import torch
     import depth_wise_attention_amd as ar
@@ -463,7 +497,8 @@ def main():
     if args.workload != "block":
         fn = {"mhar": lambda: bench_block(args, H=8, T=32768), "full": lambda: bench_full(args),
               "bwd": lambda: bench_bwd(args), "full_bwd": lambda: bench_full_bwd(args),
-              "block_update": lambda: bench_update(args), "decode": lambda: bench_decode(args)}[args.workload]
+              "block_update": lambda: bench_update(args), "decode": lambda: bench_decode(args),
+              "msar": lambda: bench_msar(args)}[args.workload]
         log(json.dumps(fn()))
         return
 
@@ -477,7 +512,7 @@ def main():
         torch.cuda.empty_cache()
         for fn in (lambda: bench_block(args, H=8, T=32768, with_events=True), lambda: bench_full(args),
                    lambda: bench_bwd(args), lambda: bench_full_bwd(args), lambda: bench_update(args),
-                   lambda: bench_decode(args)):
+                   lambda: bench_decode(args), lambda: bench_msar(args)):
             r = fn()
             extra[r.pop("name")] = {k: v for k, v in r.items() if k not in ("T", "d", "N", "S", "H")}
             torch.cuda.empty_cache()

@@ -20,6 +20,8 @@ from .binding import (  # noqa: F401
     attnres_full_fwd,
     attnres_full_fwd_workspace_size,
     attnres_last_error,
+    attnres_msar_fwd,
+    attnres_msar_fwd_workspace_size,
     attnres_set_kernel_policy,
     attnres_version,
     lib,

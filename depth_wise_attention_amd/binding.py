@@ -55,6 +55,10 @@ def lib() -> ctypes.CDLL:
     L.attnres_full_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i32]
     L.attnres_full_bwd.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, f32, i32, i32, vp, vp, vp, vp, i32, vp,
                                    sz, vp]
+    L.attnres_msar_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i32]
+    L.attnres_msar_fwd_workspace_size.restype = sz
+    L.attnres_msar_fwd.argtypes = [vp, i64, i64, i64, vp, vp, vp, i64, f32, i32, vp, vp, sz, vp]
+    L.attnres_msar_fwd.restype = ctypes.c_int
     L.attnres_set_kernel_policy.argtypes = [i32]
     for name in ("attnres_full_fwd", "attnres_block_phase1", "attnres_block_phase2_merge",
                  "attnres_block_phase2_merge_update", "mhar_fwd", "mhar_fwd_chunked",
@@ -274,6 +278,26 @@ def mhar_fwd_chunked(reps, partials, w, chunk_T: int, gain=None, eps: float = 1e
                                   _code(reps), _p(h), chunk_T, _p(ws), ws.numel() * ws.element_size(),
                                   _stream(stream)))
     return h
+
+
+def attnres_msar_fwd_workspace_size(n_src: int, n_dst: int, T: int, d: int, dtype: int) -> int:
+    return lib().attnres_msar_fwd_workspace_size(n_src, n_dst, T, d, dtype)
+
+
+def attnres_msar_fwd(src, w, conv, mix, eps: float = 1e-6, out=None, ws=None, stream=None):
+    """MSAR forward.  src [n_src, T, d]; w [n_dst, 4, d]; conv [24, d]; mix [n_dst, 4 d, 4]
+    -> out [n_dst, T, d]."""
+    torch = _torch()
+    n_src, T, d = src.shape
+    n_dst = w.shape[0]
+    if out is None:
+        out = torch.empty((n_dst, T, d), dtype=src.dtype, device=src.device)
+    need = attnres_msar_fwd_workspace_size(n_src, n_dst, T, d, _code(src))
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=src.device)
+    _check(lib().attnres_msar_fwd(_p(src), n_src, T, d, _p(w), _p(conv), _p(mix), n_dst, eps, _code(src), _p(out),
+                                  _p(ws), _nbytes(ws), _stream(stream)))
+    return out
 
 
 def attnres_bwd(reps, partials, w, dh, gain=None, eps: float = 1e-6, H: int = 1, d_reps=None,

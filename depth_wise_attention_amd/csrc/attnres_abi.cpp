@@ -195,7 +195,54 @@ extern "C" {
 
 const char* attnres_last_error(void) { return g_err; }
 
-int attnres_version(void) { return (2 << 16) | 3; }
+size_t attnres_msar_fwd_workspace_size(int64_t n_src, int64_t n_dst, int64_t T, int64_t d, int32_t dtype) {
+  (void)n_src;
+  (void)n_dst;
+  (void)T;
+  (void)d;
+  (void)dtype;
+  return 0;
+}
+
+int attnres_msar_fwd(const void* src, int64_t n_src, int64_t T, int64_t d, const float* w, const float* conv,
+                     const float* mix, int64_t n_dst, float eps, int32_t dtype, void* out, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  int64_t td = 0;
+  RETURN_IF(check_common(T, d, 1, dtype, eps, nullptr, 0, &td));
+  if (n_src < 1 || n_src > kMaxSources)
+    return fail(ATTNRES_ERR_INVALID, "n_src = %lld must be in [1, %d]", (long long)n_src, kMaxSources);
+  if (n_dst < 1 || n_dst > n_src)
+    return fail(ATTNRES_ERR_INVALID, "n_dst = %lld must be in [1, n_src = %lld]", (long long)n_dst,
+                (long long)n_src);
+  if (T == 0) return ATTNRES_OK;
+  REQUIRE_PTR(src, "src");
+  REQUIRE_PTR(w, "w");
+  REQUIRE_PTR(conv, "conv");
+  REQUIRE_PTR(mix, "mix");
+  REQUIRE_PTR(out, "out");
+  const size_t need = attnres_msar_fwd_workspace_size(n_src, n_dst, T, d, dtype);
+  if (need > 0 && (ws == nullptr || ws_bytes < need))
+    return fail(ATTNRES_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? ws_bytes : 0,
+                need);
+  const int64_t es = (int64_t)dt_size(dtype);
+  size_t b_src, b_out, b_w, b_mix;
+  RETURN_IF(check_count(n_src, td, es, "src", &b_src));
+  RETURN_IF(check_count(n_dst, td, es, "out", &b_out));
+  RETURN_IF(check_count(n_dst * kMsarStreams, d, 4, "w", &b_w));
+  RETURN_IF(check_count(n_dst * kMsarStreams * kMsarStreams, d, 4, "mix", &b_mix));
+  const Range ins[] = {{src, b_src, "src"},
+                       {w, b_w, "w"},
+                       {conv, (size_t)(kMsarTaps * d * 4), "conv"},
+                       {mix, b_mix, "mix"}};
+  const Range outs[] = {{out, b_out, "out"}, {need > 0 ? ws : nullptr, need, "ws"}};
+  RETURN_IF(check_aliasing(ins, 4, outs, 2));
+  MsarArgs a{src, n_src, T, d, w, conv, mix, n_dst, eps, dtype, out, need > 0 ? ws : nullptr, need};
+  const hipError_t e = launch_msar_generic(a, stream);
+  return e == hipSuccess ? ATTNRES_OK : hip_fail(e, "MSAR forward launch");
+}
+
+int attnres_version(void) { return (2 << 16) | 4; }
 
 int attnres_set_kernel_policy(int32_t policy) {
   if (policy != 0 && policy != 1) return fail(ATTNRES_ERR_INVALID, "unknown kernel policy %d", policy);

@@ -75,6 +75,28 @@ struct Phase2Args {
   float* h_inv_rms = nullptr;
 };
 
+// MSAR: four streams per source (identity, then causal depthwise convolutions
+// with kernel sizes 4, 8, 12 along the tokens); taps packed as [24, d].
+constexpr int kMsarStreams = 4;
+constexpr int kMsarMaxTaps = 12;
+constexpr int kMsarTaps = 24;
+__host__ __device__ constexpr int msar_kernel(int r) { return r == 1 ? 4 : (r == 2 ? 8 : 12); }  // r = 1..3
+__host__ __device__ constexpr int msar_offset(int r) { return r == 1 ? 0 : (r == 2 ? 4 : 12); }
+
+struct MsarArgs {
+  const void* src;     // [n_src, T, d]
+  int64_t n_src, T, d;
+  const float* w;      // [n_dst, 4, d]
+  const float* conv;   // [24, d]
+  const float* mix;    // [n_dst, 4 d, 4]
+  int64_t n_dst;
+  float eps;
+  int dtype;
+  void* out;           // [n_dst, T, d]
+  void* ws;            // specialised kernels' partial sums (may be null)
+  size_t ws_bytes;
+};
+
 struct BwdArgs {
   const void* reps;
   int64_t N;
@@ -155,6 +177,8 @@ hipError_t launch_phase1_fast(const Phase1Args& a, hipStream_t st);
 hipError_t launch_phase2_fast(const Phase2Args& a, hipStream_t st);
 hipError_t launch_bwd_fast(const BwdArgs& a, int64_t* slots_used, hipStream_t st);
 hipError_t launch_full_fast(const FullArgs& a, hipStream_t st);
+
+hipError_t launch_msar_generic(const MsarArgs& a, hipStream_t st);
 
 int num_cus();  // compute units of the current device (cached per device)
 // Resident blocks per compute unit for a kernel and block size (cached).

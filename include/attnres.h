@@ -286,9 +286,44 @@ int attnres_full_bwd(const void* src, int64_t n_src, int64_t T, int64_t d, const
                      int32_t dtype, const void* dout, void* d_src, float* dw, float* dgain,
                      int32_t accumulate, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Bytes of device workspace attnres_msar_fwd needs (0: none).
+ */
+size_t attnres_msar_fwd_workspace_size(int64_t n_src, int64_t n_dst, int64_t T, int64_t d,
+                                       int32_t dtype);
+
+/*
+ * MSAR multi-stream depth attention (onedev.kr summary of the MSAR paper,
+ * "How it differs"; "How to use it" for the on-demand expansion).  Every
+ * source expands into four full-width streams, never written to memory:
+ *   v^(0) = v,  v^(r)[t] = sum_{k < K_r} conv_r[k] * v[t - k]  (K = 4, 8, 12
+ *   for r = 1, 2, 3; elementwise over channels; zero before the first token).
+ * Destination j reads sources 0 .. n_src - n_dst + j; per stream r:
+ *   s_i = w_j^(r) . RMSNorm(v_i^(r)),  alpha = softmax_i(s),
+ *   Z^(r) = sum_i alpha_i v_i^(r);
+ * then the H^pre mixer: beta = sigmoid(RMSNorm([Z^(0) .. Z^(3)]) P_j) and
+ *   out_j = sum_r beta_r Z^(r).
+ * RMSNorm is x / sqrt(mean x^2 + eps) without gain (a gain folds into w and P).
+ *
+ *  src   [n_src, T, d] dtype    the T tokens are the sequence from its first
+ *                               token (the convolutions see zeros before it)
+ *  w     [n_dst, 4, d] fp32     pseudo-queries, stream-major
+ *  conv  [24, d] fp32           taps: rows 0-3 stream 1, 4-11 stream 2,
+ *                               12-23 stream 3; row k of a stream multiplies
+ *                               the source k tokens back; shared by the sources
+ *  mix   [n_dst, 4 d, 4] fp32   P_j, row r*d + c is channel c of stream r
+ *  out   [n_dst, T, d] dtype
+ *  ws    device workspace of attnres_msar_fwd_workspace_size() bytes (may be
+ *        NULL when that is 0)
+ * Requires 1 <= n_dst <= n_src <= 64.
+ */
+int attnres_msar_fwd(const void* src, int64_t n_src, int64_t T, int64_t d, const float* w,
+                     const float* conv, const float* mix, int64_t n_dst, float eps, int32_t dtype,
+                     void* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* ABI version: (major << 16) | minor.  Major 2 added the Full-forward workspace;
  * minor 1 added the Full backward, minor 2 the fused Phase 2 update, minor 3 the
- * chunked block forward. */
+ * chunked block forward, minor 4 MSAR. */
 int attnres_version(void);
 
 /*

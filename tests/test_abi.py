@@ -39,7 +39,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("attnres_full_fwd", "attnres_block_phase1", "attnres_block_phase2_merge",
-                 "attnres_block_phase2_merge_update", "mhar_fwd", "mhar_fwd_chunked",
+                 "attnres_block_phase2_merge_update", "mhar_fwd", "mhar_fwd_chunked", "attnres_msar_fwd",
+                 "attnres_msar_fwd_workspace_size",
                  "attnres_bwd", "attnres_full_bwd", "attnres_full_fwd_workspace_size", "mhar_fwd_workspace_size",
                  "attnres_bwd_workspace_size", "attnres_full_bwd_workspace_size",
                  "attnres_last_error", "attnres_version", "attnres_set_kernel_policy"):
@@ -54,7 +55,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_policy():
     assert binding.attnres_version() >> 16 == 2
-    assert binding.attnres_version() & 0xFFFF >= 3
+    assert binding.attnres_version() & 0xFFFF >= 4
     prev = binding.attnres_set_kernel_policy(1)
     assert binding.attnres_set_kernel_policy(prev) == 1
     with pytest.raises(binding.AttnResError):
@@ -346,3 +347,22 @@ def test_full_bwd_rejects_bad_arguments():
     # n_dst * H * n_src beyond the general kernel's 1024-entry tables
     assert _rc_full_bwd(n_src=64, n_dst=17, d=64) == EUNSUP
     assert "1024" in binding.attnres_last_error()
+
+
+def _rc_msar(**kw):
+    G = 1 << 30
+    a = dict(src=FAKE, n_src=9, T=100, d=64, w=FAKE + G, conv=FAKE + 2 * G, mix=FAKE + 3 * G, n_dst=1, eps=1e-6,
+             dtype=BF16, out=FAKE + 4 * G, ws=None, ws_bytes=0)
+    a.update(kw)
+    return binding.lib().attnres_msar_fwd(a["src"], a["n_src"], a["T"], a["d"], a["w"], a["conv"], a["mix"],
+                                          a["n_dst"], a["eps"], a["dtype"], a["out"], a["ws"], a["ws_bytes"], None)
+
+
+@fake_ptrs
+def test_msar_rejects_bad_arguments():
+    G = 1 << 30
+    for c in [dict(n_src=0), dict(n_src=65), dict(n_dst=0), dict(n_dst=10), dict(src=None), dict(w=None),
+              dict(conv=None), dict(mix=None), dict(out=None), dict(eps=-1.0), dict(dtype=7), dict(d=0),
+              dict(T=-1), dict(out=FAKE + 1000), dict(out=FAKE + 2 * G + 8), dict(out=FAKE + 3 * G)]:
+        assert _rc_msar(**c) == EINVAL, c
+    assert _rc_msar(T=0, src=None, out=None) == OK

@@ -37,6 +37,8 @@ _TID_F = 2
 _TID_W = 3
 _TID_GAIN = 4
 _TID_DH = 5
+_TID_CONV = 6
+_TID_MIX = 7
 
 _CHUNK = 1 << 24  # elements per stream chunk; chunks are separate sub-streams
 
@@ -216,6 +218,23 @@ def block_workload(T: int, d: int, N: int, S: int, H: int, rep_std_step: float, 
                     gain=gain, reps=reps, partials=partials, dh=dh, f=f_out,
                     meta=dict(N=N, S=S, rep_std_step=rep_std_step, seed=seed,
                               gain_variance=gain_variance))
+
+
+def msar_workload(T: int, d: int, n_src: int, n_dst: int, dtype: str, seed: int = 0, std_step: float = 0.1,
+                  eps: float = 1e-6, name: str = "msar") -> Workload:
+    """MSAR inputs: sources v_i ~ N(0, (1 + std_step*i)^2), i = 0..n_src-1;
+    pseudo-queries w [n_dst, 4, d] ~ N(0, 1/d); convolution taps conv [24, d]
+    with stream r's K_r taps ~ N(0, 1/K_r) (K = 4, 8, 12), so every stream keeps
+    roughly the source's scale; mixer P [n_dst, 4 d, 4] ~ N(0, 1/(4 d)).
+    The taps and P are kept in meta['conv'] and meta['mix']."""
+    src = normal_stack(n_src, (T, d), [1.0 + std_step * i for i in range(n_src)], seed, _TID_SOURCES)
+    src = _maybe_round(src, dtype)
+    w = _pseudo_queries(n_dst * 4, d, seed).reshape(n_dst, 4, d)
+    conv = np.concatenate([normal_stack(1, (K, d), [1.0 / math.sqrt(K)], seed, _TID_CONV + 16 * r)[0]
+                           for r, K in enumerate((4, 8, 12))])
+    mix = normal_stack(n_dst, (4 * d, 4), [1.0 / math.sqrt(4 * d)] * n_dst, seed, _TID_MIX)
+    return Workload(name=name, kind="msar", dtype=dtype, T=T, d=d, H=1, eps=eps, w=w, gain=None, src=src,
+                    n_dst=n_dst, meta=dict(conv=conv, mix=mix, std_step=std_step, seed=seed))
 
 
 # ---------------------------------------------------------------------------
