@@ -196,12 +196,8 @@ extern "C" {
 const char* attnres_last_error(void) { return g_err; }
 
 size_t attnres_msar_fwd_workspace_size(int64_t n_src, int64_t n_dst, int64_t T, int64_t d, int32_t dtype) {
-  (void)n_src;
-  (void)n_dst;
-  (void)T;
-  (void)d;
-  (void)dtype;
-  return 0;
+  if (n_src < 1 || n_src > kMaxSources || n_dst < 1 || n_dst > n_src || T < 1 || d < 1 || d > kMaxD) return 0;
+  return msar_fast_workspace_bytes(n_src, n_dst, T, d, dtype);
 }
 
 int attnres_msar_fwd(const void* src, int64_t n_src, int64_t T, int64_t d, const float* w, const float* conv,
@@ -238,7 +234,7 @@ int attnres_msar_fwd(const void* src, int64_t n_src, int64_t T, int64_t d, const
   const Range outs[] = {{out, b_out, "out"}, {need > 0 ? ws : nullptr, need, "ws"}};
   RETURN_IF(check_aliasing(ins, 4, outs, 2));
   MsarArgs a{src, n_src, T, d, w, conv, mix, n_dst, eps, dtype, out, need > 0 ? ws : nullptr, need};
-  const hipError_t e = launch_msar_generic(a, stream);
+  const hipError_t e = (use_fast() && msar_fast_ok(a)) ? launch_msar_fast(a, stream) : launch_msar_generic(a, stream);
   return e == hipSuccess ? ATTNRES_OK : hip_fail(e, "MSAR forward launch");
 }
 

@@ -179,6 +179,10 @@ hipError_t launch_bwd_fast(const BwdArgs& a, int64_t* slots_used, hipStream_t st
 hipError_t launch_full_fast(const FullArgs& a, hipStream_t st);
 
 hipError_t launch_msar_generic(const MsarArgs& a, hipStream_t st);
+constexpr int kMsarFastMaxSources = 12;
+size_t msar_fast_workspace_bytes(int64_t n_src, int64_t n_dst, int64_t T, int64_t d, int dtype);
+bool msar_fast_ok(const MsarArgs& a);
+hipError_t launch_msar_fast(const MsarArgs& a, hipStream_t st);
 
 int num_cus();  // compute units of the current device (cached per device)
 // Resident blocks per compute unit for a kernel and block size (cached).

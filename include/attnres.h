@@ -287,7 +287,11 @@ int attnres_full_bwd(const void* src, int64_t n_src, int64_t T, int64_t d, const
                      int32_t accumulate, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * Bytes of device workspace attnres_msar_fwd needs (0: none).
+ * Bytes of device workspace attnres_msar_fwd needs (0: none).  The
+ * specialised bf16 path for one destination over at most 12 sources with d a
+ * multiple of 512 keeps per-token partial sums and the retrieved states
+ * (4 d fp32 per token) there: about 16 d + 32 n_src d / 512 + 300 bytes per
+ * token.  Returns 0 for invalid sizes and for shapes the general kernel runs.
  */
 size_t attnres_msar_fwd_workspace_size(int64_t n_src, int64_t n_dst, int64_t T, int64_t d,
                                        int32_t dtype);

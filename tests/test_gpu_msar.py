@@ -1,4 +1,5 @@
-"""Parity of the MSAR forward (attnres_msar_fwd) with the MSAR oracle on MI355X.
+"""Parity of the MSAR forward (attnres_msar_fwd) with the MSAR oracle on MI355X,
+through both the specialised and the general kernels (the policy fixture).
 
 Element by element over every output at small sizes (ragged d, sequences
 shorter than the longest kernel, Full-style prefix sets and Block-style single
@@ -62,6 +63,11 @@ def _run(wl):
     (64, 2048, 9, 1, "bf16"),
     (24, 4096, 9, 1, "bf16"),
     (9, 1024, 64, 4, "bf16"),   # the most sources
+    # the specialised path (bf16, one destination, <= 12 sources, d % 512 == 0):
+    (5, 512, 3, 1, "bf16"),     # shorter than the history
+    (300, 1024, 12, 1, "bf16"), # several token ranges and a ragged last one
+    (257, 512, 1, 1, "bf16"),
+    (130, 1536, 6, 1, "bf16"),
 ])
 def test_msar_shapes(T, d, n_src, n_dst, dtype, policy):
     say(f"msar T={T} d={d} n_src={n_src} n_dst={n_dst} {dtype} policy={policy}")
