@@ -2,22 +2,20 @@
 // most 12 sources, d a multiple of 512.
 //
 // The streams of a source at token t need the source's rows t-11 .. t, and
-// the routing needs sums over all d channels per token.  The work is split
-// over channel slices of 512 so that a workgroup keeps the 12-token history of
-// every source for its slice in LDS and the 24 taps of its channels in
-// registers, while walking a range of consecutive tokens:
-//   k_msar_slice<N, 0>  per token and slice: each source's per-stream sum of
-//                       squares and query product (8 N values)      -> part
-//   k_msar_alpha<N>     per token: sum the slices, scores, the four depth
-//                       softmaxes                                   -> alpha
-//   k_msar_slice<N, 1>  per token and slice: Z^(r) for the slice's channels
-//                       (stored once, fp32), the sum of squares of Flatten(Z)
-//                       and its four projections by P               -> zbuf, part2
-//   k_msar_out          per token: sum the slices, beta = sigmoid(...), and
-//                       h = sum_r beta_r Z^(r)                      -> out
-// The streams themselves are never stored.  Thread tid of a slice owns the two
-// channels 2 tid, 2 tid + 1; its ring words in LDS are private to it, so the
-// ring needs no barrier (LDS operations of a wave complete in order).
+// the routing needs sums over all d channels per token.  Workgroups own a
+// 512-channel slice (two channels per thread) over a range of consecutive
+// tokens, walked in chunks of 8 tokens; within a chunk the sources are taken
+// one at a time, so a thread holds the 19 rows (t0-11 .. t0+7) of one source's
+// two channels in registers, unpacked once, and the 24 taps of its channels:
+//   k_msar_slice<0>  per token and slice: each source's per-stream sum of
+//                    squares and query product (8 values per source) -> part
+//   k_msar_alpha<N>  per token: sum the slices, scores, four depth softmaxes -> alpha
+//   k_msar_slice<1>  per token and slice: Z^(r) for the slice's channels
+//                    (stored once, fp32), the sum of squares of Flatten(Z)
+//                    and its four projections by P                   -> zbuf, part2
+//   k_msar_out       per token: sum the slices, beta = sigmoid(...), and
+//                    h = sum_r beta_r Z^(r)                          -> out
+// The streams themselves are never stored.
 
 #include <math.h>
 
@@ -31,27 +29,37 @@ namespace {
 constexpr int kMfB = 256;        // threads per workgroup
 constexpr int kMfSlice = 512;    // channels per slice (2 per thread)
 constexpr int kMfRange = 128;    // tokens per workgroup
-constexpr int kMfHist = 12;      // history ring slots (the longest kernel)
+constexpr int kMfTC = 8;         // tokens per chunk
+constexpr int kMfHalo = 11;      // rows before a token that its longest stream reads
+constexpr int kMfWin = kMfTC + kMfHalo;
 constexpr int kMfAlphaRow = 16;  // alpha[t][r][16]
 constexpr int kMfPart2 = 8;      // part2[t][slice][8] (5 used)
 
 struct MsarFastBufs {
-  float* part;    // [T][S][8 N]: per source i, [i*8 + r] sum of squares, [i*8 + 4 + r] query product
+  float* part;    // [T][S][8 n]: per source i, [i*8 + r] sum of squares, [i*8 + 4 + r] query product
   float* alpha;   // [T][4][16]
   float* part2;   // [T][S][8]: [0] sum of squares of Z, [1 + q] projection q
   float* zbuf;    // [T][4][d]
 };
 
-__device__ __forceinline__ float2 bf2_to_f2(uint32_t u) { return make_float2(bf_lo(u), bf_hi(u)); }
-
-template <int N, int PASS>
-__global__ __launch_bounds__(kMfB, 2) void k_msar_slice(MsarArgs a, MsarFastBufs b) {
-  constexpr int NV = 8 * N;                 // values reduced per token in pass 0
-  constexpr int NG = (NV + 63) / 64;
-  __shared__ uint32_t ring[kMfHist * N * kMfB];
-  __shared__ float red[2][4][PASS == 0 ? NG * 64 : kMfPart2];
+// Sum of v[p] over the workgroup's 256 threads, for p < 64, into the
+// returned value of thread p (other threads return garbage).  One barrier;
+// red is double-buffered by the caller's buf.
+__device__ __forceinline__ float block_reduce64(const float (&v)[64], float (&red)[2][4][64], int buf) {
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  red[buf][wave][lane] = transpose_reduce64(v);
+  lds_barrier();
+  const int p = tid & 63;
+  return (red[buf][0][p] + red[buf][1][p]) + (red[buf][2][p] + red[buf][3][p]);
+}
+
+template <int PASS>
+__global__ __launch_bounds__(kMfB, 2) void k_msar_slice(MsarArgs a, MsarFastBufs b) {
+  __shared__ float red[2][4][64];
+  __shared__ float alpha_s[PASS == 1 ? kMfTC * kMsarStreams * kMfAlphaRow : 1];
+  const int tid = threadIdx.x;
   const int64_t d = a.d, T = a.T;
+  const int n = (int)a.n_src;
   const int S = (int)(d / kMfSlice);
   const int slice = blockIdx.x;
   const int64_t c0 = (int64_t)slice * kMfSlice + 2 * tid;
@@ -74,114 +82,120 @@ __global__ __launch_bounds__(kMfB, 2) void k_msar_slice(MsarArgs a, MsarFastBufs
     }
   }
 
-  // Zero the history, so positions before the first token read as zero.
-#pragma unroll
-  for (int s = 0; s < kMfHist * N; ++s) ring[s * kMfB + tid] = 0u;
-
   const int64_t t_begin = (int64_t)blockIdx.y * kMfRange;
   const int64_t t_end = t_begin + kMfRange < T ? t_begin + kMfRange : T;
-  const int64_t t_warm = t_begin >= kMfHist - 1 ? t_begin - (kMfHist - 1) : 0;
-  uint32_t nxt[N];
-#pragma unroll
-  for (int i = 0; i < N; ++i) nxt[i] = *reinterpret_cast<const uint32_t*>(src + ((int64_t)i * T + t_warm) * d + c0);
   int buf = 0;
-  for (int64_t t = t_warm; t < t_end; ++t) {
-    const int slot = (int)(t % kMfHist);
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += kMfTC) {
+    float2 z[kMfTC][kMsarStreams];
+    if constexpr (PASS == 1) {
 #pragma unroll
-    for (int i = 0; i < N; ++i) ring[(slot * N + i) * kMfB + tid] = nxt[i];
-    if (t + 1 < t_end) {
+      for (int q = 0; q < kMfTC; ++q)
 #pragma unroll
-      for (int i = 0; i < N; ++i)
-        nxt[i] = *reinterpret_cast<const uint32_t*>(src + ((int64_t)i * T + t + 1) * d + c0);
+        for (int r = 0; r < kMsarStreams; ++r) z[q][r] = make_float2(0.f, 0.f);
+      // The chunk's softmax weights, into LDS: per-source reads then go through
+      // the LDS counter instead of queueing behind the prefetched rows.  The
+      // barrier also orders the previous chunk's reads before these writes.
+      lds_barrier();
+      for (int e = tid; e < kMfTC * kMsarStreams * kMfAlphaRow; e += kMfB) {
+        const int64_t tq = t0 + e / (kMsarStreams * kMfAlphaRow);
+        alpha_s[e] = b.alpha[(tq < T ? tq : T - 1) * (kMsarStreams * kMfAlphaRow) + e % (kMsarStreams * kMfAlphaRow)];
+      }
+      lds_barrier();
     }
-    if (t < t_begin) continue;  // warm-up rows of the history only
-
-    // Ring offset of lag k for this token (slot of token t - k).
-    int base[kMfHist];
+    // Rows t0-11 .. t0+7 of source i; rows outside [0, T) read as zero (before
+    // the first token: the causal zero; past the end: unused).  Loads are
+    // unconditional (clamped row and source), so the next source's rows stay
+    // in flight while this one computes.
+    auto load_rows = [&](int i, uint32_t (&raw)[kMfWin]) {
+      const bf16_t* col = src + (int64_t)(i < n ? i : n - 1) * T * d + c0;
 #pragma unroll
-    for (int k = 0; k < kMfHist; ++k) base[k] = ((slot - k + kMfHist) % kMfHist) * N * kMfB + tid;
-
-    // The four streams of source i at this thread's two channels.
-    auto streams = [&](int i, float2 (&x)[kMsarStreams]) {
-      float2 win[kMfHist];
-#pragma unroll
-      for (int k = 0; k < kMfHist; ++k) win[k] = bf2_to_f2(ring[base[k] + i * kMfB]);
-      x[0] = win[0];
-#pragma unroll
-      for (int r = 1; r < kMsarStreams; ++r) {
-        const int K = msar_kernel(r), off = msar_offset(r);
-        float2 acc = make_float2(0.f, 0.f);
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-          acc.x = fmaf(tap[off + k].x, win[k].x, acc.x);
-          acc.y = fmaf(tap[off + k].y, win[k].y, acc.y);
-        }
-        x[r] = acc;
+      for (int h = 0; h < kMfWin; ++h) {
+        const int64_t row = t0 - kMfHalo + h;
+        const int64_t rc = row < 0 ? 0 : (row >= T ? T - 1 : row);
+        raw[h] = *reinterpret_cast<const uint32_t*>(col + rc * d);
       }
     };
-
-    if constexpr (PASS == 0) {
-      float v[NV];
+    auto source = [&](int i, const uint32_t (&raw)[kMfWin]) {
+      float2 x[kMfWin];
 #pragma unroll
-      for (int i = 0; i < N; ++i) {
-        float2 x[kMsarStreams];
-        streams(i, x);
+      for (int h = 0; h < kMfWin; ++h) {
+        const int64_t row = t0 - kMfHalo + h;
+        const uint32_t u = (row >= 0 && row < T) ? raw[h] : 0u;
+        x[h] = make_float2(bf_lo(u), bf_hi(u));
+      }
+      float v[64];  // pass 0: [token q][8]
 #pragma unroll
-        for (int r = 0; r < kMsarStreams; ++r) {
-          v[i * 8 + r] = fmaf(x[r].x, x[r].x, x[r].y * x[r].y);
-          v[i * 8 + 4 + r] = fmaf(wq[r].x, x[r].x, wq[r].y * x[r].y);
+      for (int q = 0; q < kMfTC; ++q) {
+        // Token t0 + q is window row q + 11; lag k is row q + 11 - k.
+        float2 sv[kMsarStreams];
+        sv[0] = x[q + kMfHalo];
+#pragma unroll
+        for (int r = 1; r < kMsarStreams; ++r) {
+          const int K = msar_kernel(r), off = msar_offset(r);
+          float2 acc = make_float2(0.f, 0.f);
+#pragma unroll
+          for (int k = 0; k < K; ++k) {
+            acc.x = fmaf(tap[off + k].x, x[q + kMfHalo - k].x, acc.x);
+            acc.y = fmaf(tap[off + k].y, x[q + kMfHalo - k].y, acc.y);
+          }
+          sv[r] = acc;
+        }
+        if constexpr (PASS == 0) {
+#pragma unroll
+          for (int r = 0; r < kMsarStreams; ++r) {
+            v[q * 8 + r] = fmaf(sv[r].x, sv[r].x, sv[r].y * sv[r].y);
+            v[q * 8 + 4 + r] = fmaf(wq[r].x, sv[r].x, wq[r].y * sv[r].y);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < kMsarStreams; ++r) {
+            const float w_ri = alpha_s[(q * kMsarStreams + r) * kMfAlphaRow + i];
+            z[q][r].x = fmaf(w_ri, sv[r].x, z[q][r].x);
+            z[q][r].y = fmaf(w_ri, sv[r].y, z[q][r].y);
+          }
         }
       }
-      float tot[NG];
-      wave_reduce_values<NV>(v, tot);
-#pragma unroll
-      for (int g = 0; g < NG; ++g) red[buf][wave][g * 64 + lane] = tot[g];
-      lds_barrier();
-      if (tid < NV) {
-        const float s = (red[buf][0][tid] + red[buf][1][tid]) + (red[buf][2][tid] + red[buf][3][tid]);
-        b.part[(t * S + slice) * NV + tid] = s;
+      if constexpr (PASS == 0) {
+        const float tot = block_reduce64(v, red, buf);
+        buf ^= 1;
+        const int p = tid;
+        if (p < 64 && t0 + p / 8 < t_end) b.part[((t0 + p / 8) * S + slice) * (8 * n) + i * 8 + (p & 7)] = tot;
       }
-    } else {
-      const float* al = b.alpha + t * (kMsarStreams * kMfAlphaRow);  // wave-uniform
-      float2 z[kMsarStreams];
-#pragma unroll
-      for (int r = 0; r < kMsarStreams; ++r) z[r] = make_float2(0.f, 0.f);
-#pragma unroll
-      for (int i = 0; i < N; ++i) {
-        float2 x[kMsarStreams];
-        streams(i, x);
-#pragma unroll
-        for (int r = 0; r < kMsarStreams; ++r) {
-          const float w_ri = al[r * kMfAlphaRow + i];
-          z[r].x = fmaf(w_ri, x[r].x, z[r].x);
-          z[r].y = fmaf(w_ri, x[r].y, z[r].y);
-        }
-      }
-      float v[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int r = 0; r < kMsarStreams; ++r) {
-        *reinterpret_cast<float2*>(b.zbuf + (t * kMsarStreams + r) * d + c0) = z[r];
-        v[0] = fmaf(z[r].x, z[r].x, fmaf(z[r].y, z[r].y, v[0]));
-        v[1] = fmaf(z[r].x, pm[r][0].x, fmaf(z[r].y, pm[r][1].x, v[1]));
-        v[2] = fmaf(z[r].x, pm[r][0].y, fmaf(z[r].y, pm[r][1].y, v[2]));
-        v[3] = fmaf(z[r].x, pm[r][0].z, fmaf(z[r].y, pm[r][1].z, v[3]));
-        v[4] = fmaf(z[r].x, pm[r][0].w, fmaf(z[r].y, pm[r][1].w, v[4]));
-      }
-#pragma unroll
-      for (int q = 0; q < 5; ++q) v[q] = wave_allsum(v[q]);
-      if (lane < 5) {
-        float mine = v[0];
-#pragma unroll
-        for (int q = 1; q < 5; ++q) mine = lane == q ? v[q] : mine;
-        red[buf][wave][lane] = mine;
-      }
-      lds_barrier();
-      if (tid < 5) {
-        const float s = (red[buf][0][tid] + red[buf][1][tid]) + (red[buf][2][tid] + red[buf][3][tid]);
-        b.part2[(t * S + slice) * kMfPart2 + tid] = s;
-      }
+    };
+    // Ping-pong over pairs of sources: each buffer's loads are issued one
+    // source ahead of its use.
+    uint32_t ra[kMfWin], rb[kMfWin];
+    load_rows(0, ra);
+    for (int i = 0; i < n; i += 2) {
+      load_rows(i + 1, rb);
+      source(i, ra);
+      load_rows(i + 2, ra);
+      if (i + 1 < n) source(i + 1, rb);
     }
-    buf ^= 1;
+    if constexpr (PASS == 1) {
+      float v[64];
+#pragma unroll
+      for (int q = 0; q < kMfTC; ++q) {
+        float e[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < kMsarStreams; ++r) {
+          const float2 zr = z[q][r];
+          if (t0 + q < t_end) *reinterpret_cast<float2*>(b.zbuf + ((t0 + q) * kMsarStreams + r) * d + c0) = zr;
+          e[0] = fmaf(zr.x, zr.x, fmaf(zr.y, zr.y, e[0]));
+          e[1] = fmaf(zr.x, pm[r][0].x, fmaf(zr.y, pm[r][1].x, e[1]));
+          e[2] = fmaf(zr.x, pm[r][0].y, fmaf(zr.y, pm[r][1].y, e[2]));
+          e[3] = fmaf(zr.x, pm[r][0].z, fmaf(zr.y, pm[r][1].z, e[3]));
+          e[4] = fmaf(zr.x, pm[r][0].w, fmaf(zr.y, pm[r][1].w, e[4]));
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[q * 8 + j] = j < 5 ? e[j] : 0.f;
+      }
+      const float tot = block_reduce64(v, red, buf);
+      buf ^= 1;
+      const int p = tid;
+      if (p < 64 && (p & 7) < 5 && t0 + p / 8 < t_end)
+        b.part2[((t0 + p / 8) * S + slice) * kMfPart2 + (p & 7)] = tot;
+    }
   }
 }
 
@@ -267,11 +281,11 @@ template <int N>
 hipError_t launch_n(const MsarArgs& a, hipStream_t st) {
   const MsarFastBufs b = carve(a);
   const dim3 grid((unsigned)(a.d / kMfSlice), (unsigned)((a.T + kMfRange - 1) / kMfRange));
-  hipLaunchKernelGGL((k_msar_slice<N, 0>), grid, dim3(kMfB), 0, st, a, b);
+  hipLaunchKernelGGL(k_msar_slice<0>, grid, dim3(kMfB), 0, st, a, b);
   int64_t ablocks = (a.T + 3) / 4;
   if (ablocks > 8 * (int64_t)num_cus()) ablocks = 8 * (int64_t)num_cus();
   hipLaunchKernelGGL((k_msar_alpha<N>), dim3((unsigned)ablocks), dim3(256), 0, st, a, b);
-  hipLaunchKernelGGL((k_msar_slice<N, 1>), grid, dim3(kMfB), 0, st, a, b);
+  hipLaunchKernelGGL(k_msar_slice<1>, grid, dim3(kMfB), 0, st, a, b);
   int64_t oblocks = a.T < 4 * (int64_t)num_cus() ? a.T : 4 * (int64_t)num_cus();
   hipLaunchKernelGGL(k_msar_out, dim3((unsigned)oblocks), dim3(256), 0, st, a, b);
   return hipGetLastError();
