@@ -363,19 +363,16 @@ __global__ __launch_bounds__(B, ATTNRES_P1_MINWAVES) void k_phase1_fast(Phase1Ar
       const float r = 1.0f / sqrtf(ss / (float)d + a.eps);
       const float s = sm_valid ? r * dot : -INFINITY;
       float m = s;
-#pragma unroll
-      for (int off = 1; off < NP; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+      m = group_max<NP>(m);
       const float e = sm_valid ? expf(s - m) : 0.f;
       float l = e;
-#pragma unroll
-      for (int off = 1; off < NP; off <<= 1) l += __shfl_xor(l, off, kWave);
+      l = group_sum<NP>(l);
       alpha = e / l;
       if (lse_writer) a.lse[((int64_t)sm_l * a.H + sm_head) * T + t] = m + logf(l);
       if constexpr (__is_same(OR, f16_t)) {
         // Scaled fp16 state for layers >= 2: every |o| <= sqrt(max_i ss_i).
         float mss = ss;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) mss = fmaxf(mss, __shfl_xor(mss, off, kWave));
+        mss = group_max<64>(mss);
         const float scale = f16_state_scale(sqrtf(mss));
         if (sm_l >= 1) alpha *= 1.0f / scale;  // exact: a power of two
         if (wave == 0 && lane == 0) a.oscale[t] = scale;

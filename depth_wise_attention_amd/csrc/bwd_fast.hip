@@ -180,23 +180,19 @@ __global__ __launch_bounds__(B, ATTNRES_BWD_MINWAVES) void k_bwd_fast(BwdArgs a)
       const float s = pvalid ? r * sd : -INFINITY;
       const float av = pvalid ? ad : 0.f;
       float m = s;
-#pragma unroll
-      for (int off = 1; off < NP; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+      m = group_max<NP>(m);
       const float e = pvalid ? expf(s - m) : 0.f;
       float l = e;
-#pragma unroll
-      for (int off = 1; off < NP; off <<= 1) l += __shfl_xor(l, off, kWave);
+      l = group_sum<NP>(l);
       alpha = e / l;
       float sa = alpha * av;
-#pragma unroll
-      for (int off = 1; off < NP; off <<= 1) sa += __shfl_xor(sa, off, kWave);
+      sa = group_sum<NP>(sa);
       const float c = alpha * (av - sa);
       cr = c * r;
       // sum_j c s over the destinations reading the same rep (same slot, other groups)
       const float cs = pvalid ? c * s : 0.f;
       float csum = cs;
-#pragma unroll
-      for (int off = NP; off < 64; off <<= 1) csum += __shfl_xor(csum, off, kWave);
+      csum = butterfly<NP, 64>(csum, SumOp());
       coef = pvalid ? r * r * (pu < N ? csum : cs) / (float)d : 0.f;
     }
 

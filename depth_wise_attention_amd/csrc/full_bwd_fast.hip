@@ -25,6 +25,7 @@
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "xlane.hpp"
 #include "mfma_tiles.hpp"
 
 namespace attnres {
@@ -214,16 +215,14 @@ __global__ __launch_bounds__(kBB, 2) void k_full_bwd_fast(FullBwdArgs a, const u
         av[q] = aa;
         m = fmaxf(m, sc[q]);
       }
-#pragma unroll
-      for (int off = 1; off < 8; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+      m = group_max<8>(m);
       float e[4], l = 0.f;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         e[q] = ok[q] ? expf(sc[q] - m) : 0.f;
         l += e[q];
       }
-#pragma unroll
-      for (int off = 1; off < 8; off <<= 1) l += __shfl_xor(l, off, kWave);
+      l = group_sum<8>(l);
       const float inv = l > 0.f ? 1.0f / l : 0.f;
       float al[4], sa = 0.f;
 #pragma unroll
@@ -231,8 +230,7 @@ __global__ __launch_bounds__(kBB, 2) void k_full_bwd_fast(FullBwdArgs a, const u
         al[q] = e[q] * inv;
         sa = fmaf(al[q], av[q], sa);
       }
-#pragma unroll
-      for (int off = 1; off < 8; off <<= 1) sa += __shfl_xor(sa, off, kWave);
+      sa = group_sum<8>(sa);
       float cc[4], rcv[4], csv[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {

@@ -29,6 +29,7 @@
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "xlane.hpp"
 #include "mfma_tiles.hpp"
 
 namespace attnres {
@@ -186,16 +187,14 @@ __global__ __launch_bounds__(kFB, 2) void k_full_fast(FullArgs a, const bf16_t* 
         sc[q] = (j < n_dst && i <= lim) ? r * sv : -INFINITY;
         m = fmaxf(m, sc[q]);
       }
-#pragma unroll
-      for (int off = 1; off < 8; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+      m = group_max<8>(m);
       float e[4], l = 0.f;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         e[q] = (sc[q] == -INFINITY) ? 0.f : expf(sc[q] - m);
         l += e[q];
       }
-#pragma unroll
-      for (int off = 1; off < 8; off <<= 1) l += __shfl_xor(l, off, kWave);
+      l = group_sum<8>(l);
       const float inv = l > 0.f ? 1.0f / l : 0.f;
       *reinterpret_cast<float4*>(&sm.alpha[j][i0]) = make_float4(e[0] * inv, e[1] * inv, e[2] * inv, e[3] * inv);
     }
@@ -422,16 +421,14 @@ __global__ __launch_bounds__(kRB, 1) void k_full_resident(FullArgs a, const bf16
         sc[q] = (j < n_dst && i <= lim) ? r * sv : -INFINITY;
         m = fmaxf(m, sc[q]);
       }
-#pragma unroll
-      for (int off = 1; off < 8; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+      m = group_max<8>(m);
       float e[4], l = 0.f;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         e[q] = (sc[q] == -INFINITY) ? 0.f : expf(sc[q] - m);
         l += e[q];
       }
-#pragma unroll
-      for (int off = 1; off < 8; off <<= 1) l += __shfl_xor(l, off, kWave);
+      l = group_sum<8>(l);
       const float inv = l > 0.f ? 1.0f / l : 0.f;
       *reinterpret_cast<float4*>(&sm.alpha[j][i0]) = make_float4(e[0] * inv, e[1] * inv, e[2] * inv, e[3] * inv);
     }

@@ -51,6 +51,52 @@ __device__ __forceinline__ float wave_allsum(float v) {
   return v;
 }
 
+// op(v, v of lane ^ OFF) for OFF in {1, 2, 4, 8, 16, 32}, without LDS.  For 16
+// and 32 the permlane swap of v with itself leaves {v, v[lane ^ OFF]} in its
+// two results (in some order), so the op must be symmetric.
+template <int OFF, typename Op>
+__device__ __forceinline__ float xor_combine(float v, Op op) {
+  if constexpr (OFF == 1) {
+    return op(v, dpp_move<dpp::kXor1>(0.f, v));
+  } else if constexpr (OFF == 2) {
+    return op(v, dpp_move<dpp::kXor2>(0.f, v));
+  } else if constexpr (OFF == 4) {
+    return op(v, xor4(v));
+  } else if constexpr (OFF == 8) {
+    return op(v, dpp_move<dpp::kRor8>(0.f, v));
+  } else if constexpr (OFF == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  } else {
+    static_assert(OFF == 32, "offset must be a power of two below 64");
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+}
+
+struct SumOp {
+  __device__ __forceinline__ float operator()(float x, float y) const { return x + y; }
+};
+struct MaxOp {
+  __device__ __forceinline__ float operator()(float x, float y) const { return fmaxf(x, y); }
+};
+
+// Butterfly over lane offsets LO, 2 LO, ..., < HI: with LO = 1 every lane of a
+// group of HI consecutive lanes ends with the group's total; with LO = G, HI =
+// 64 every lane ends with the total over the lanes congruent to it mod G.
+template <int LO, int HI, typename Op>
+__device__ __forceinline__ float butterfly(float v, Op op) {
+  if constexpr (LO < HI) {
+    v = xor_combine<LO>(v, op);
+    return butterfly<2 * LO, HI>(v, op);
+  } else {
+    return v;
+  }
+}
+
+template <int G> __device__ __forceinline__ float group_sum(float v) { return butterfly<1, G>(v, SumOp()); }
+template <int G> __device__ __forceinline__ float group_max(float v) { return butterfly<1, G>(v, MaxOp()); }
+
 // Transpose-reduce of 64 values per lane: on return, lane L holds the sum over
 // all 64 lanes of value index L.  Each halving stage keeps, per lane, the half
 // of the values selected by one lane bit and adds the partner lane's copy.
