@@ -110,8 +110,12 @@ struct BwdSmem {
 };
 
 
+#ifndef ATTNRES_FBWD_MINBLOCKS
+#define ATTNRES_FBWD_MINBLOCKS 2
+#endif
+
 template <bool ACC>
-__global__ __launch_bounds__(kBB, 2) void k_full_bwd_fast(FullBwdArgs a, const uint4* qpk, const uint4* qt,
+__global__ __launch_bounds__(kBB, ATTNRES_FBWD_MINBLOCKS) void k_full_bwd_fast(FullBwdArgs a, const uint4* qpk, const uint4* qt,
                                                           float* cws) {
   __shared__ BwdSmem sm;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
