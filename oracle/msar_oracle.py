@@ -116,5 +116,71 @@ def msar_fwd(src, w, conv, P, eps: float = 1e-6, return_parts: bool = False):
     return h
 
 
+def _mixer(Z, P, eps):
+    """h = sum_r beta_r Z^(r), beta = sigmoid(RMSNorm(Flatten(Z)) P); Z [4, T, d], P [4 d, 4]."""
+    flat = np.concatenate([Z[r] for r in range(MSAR_STREAMS)], axis=-1)
+    beta = sigmoid(rms_normalise(flat, eps) @ _f64(P))
+    return np.einsum("tr,rtc->tc", beta, Z)
+
+
+def block_msar_phase1(reps, w, conv, P1, eps: float = 1e-6):
+    """Block MSAR, Phase 1 ([MSAR] "How to use it": AttnRes's two-phase
+    computation carries over): the block's S sublayers' per-stream queries
+    against the N cached reps, each rep's streams expanded once for all of them.
+
+    reps [N, T, d]; w [S, 4, d]; conv [24, d]; P1 [4 d, 4] (sublayer 1's mixer).
+    Returns (h1 [T, d], o [S-1, 4, T, d], lse [S-1, 4, T]): sublayer 1 reads the
+    reps only, so its output is final; sublayers 2..S keep, per stream, the
+    softmax-weighted state over the reps and its log-sum-exp."""
+    reps = _f64(reps)
+    w = _f64(w)
+    N, T, d = reps.shape
+    S = w.shape[0]
+    streams = np.stack([msar_expand(reps[n], conv) for n in range(N)])       # [N, 4, T, d]
+    o = np.zeros((S, MSAR_STREAMS, T, d))
+    lse = np.zeros((S, MSAR_STREAMS, T))
+    for i in range(S):
+        for r in range(MSAR_STREAMS):
+            vals = streams[:, r]
+            s = np.einsum("ntc,c->nt", rms_normalise(vals, eps), w[i, r])
+            m = s.max(axis=0)
+            e = np.exp(s - m)
+            l = e.sum(axis=0)
+            o[i, r] = np.einsum("nt,ntc->tc", e / l, vals)
+            lse[i, r] = m + np.log(l)
+    return _mixer(o[0], P1, eps), o[1:], lse[1:]
+
+
+def block_msar_phase2(o_i, lse_i, partial, w_i, conv, P_i, eps: float = 1e-6):
+    """Block MSAR, Phase 2 for sublayer i >= 2: the partial sum's streams are
+    scored with the sublayer's queries and merged into Phase 1's per-stream
+    states by online softmax (exact), then the mixer gives h_i.
+
+    o_i [4, T, d]; lse_i [4, T]; partial [T, d]; w_i [4, d]; P_i [4 d, 4]."""
+    o_i = _f64(o_i)
+    lse_i = _f64(lse_i)
+    xp = msar_expand(partial, conv)                                           # [4, T, d]
+    Z = np.zeros_like(o_i)
+    for r in range(MSAR_STREAMS):
+        sp = rms_normalise(xp[r], eps) @ _f64(w_i)[r]
+        m = np.maximum(lse_i[r], sp)
+        a = np.exp(lse_i[r] - m)[:, None]
+        b = np.exp(sp - m)[:, None]
+        Z[r] = (a * o_i[r] + b * xp[r]) / (a + b)
+    return _mixer(Z, P_i, eps)
+
+
+def block_msar_direct(reps, partials, w, conv, P, eps: float = 1e-6):
+    """Every sublayer of one block by the plain definition: sublayer i reads
+    the reps and (i >= 2) the partial sum b_{i-1} as one more source."""
+    reps = _f64(reps)
+    S = _f64(w).shape[0]
+    out = []
+    for i in range(1, S + 1):
+        src = reps if i == 1 else np.concatenate([reps, _f64(partials)[i - 2][None]])
+        out.append(msar_fwd(src, _f64(w)[i - 1:i], conv, _f64(P)[i - 1:i], eps)[0])
+    return np.stack(out)
+
+
 __all__ = ["MSAR_STREAMS", "MSAR_KERNEL_SIZES", "MSAR_TAP_OFFSETS", "MSAR_TAPS", "msar_expand", "sigmoid",
-           "msar_fwd"]
+           "msar_fwd", "block_msar_phase1", "block_msar_phase2", "block_msar_direct"]

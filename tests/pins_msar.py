@@ -138,7 +138,49 @@ def pin_msar_prefix_sets():
     assert np.max(np.abs(h2[2] - h[2])) > 1e-3
 
 
+def pin_block_msar_two_phase_equals_direct():
+    """[MSAR] "How to use it": the two-phase computation carries over.  Phase 1
+    over the reps plus the online-softmax merge of each partial equals the
+    direct routing over reps + partial, for every sublayer of the block."""
+    r = _rng(8)
+    N, S, T, d = 5, 4, 20, 8
+    reps = r.standard_normal((N, T, d)) * (1 + 0.3 * np.arange(N))[:, None, None]
+    partials = np.cumsum(r.standard_normal((S - 1, T, d)), axis=0)
+    w = r.standard_normal((S, 4, d)) / np.sqrt(d)
+    conv = r.standard_normal((24, d)) / 3
+    P = r.standard_normal((S, 4 * d, 4)) / np.sqrt(4 * d)
+    direct = mso.block_msar_direct(reps, partials, w, conv, P)
+    h1, o, lse = mso.block_msar_phase1(reps, w, conv, P[0])
+    np.testing.assert_allclose(h1, direct[0], rtol=1e-12, atol=1e-12)
+    for i in range(2, S + 1):
+        hi = mso.block_msar_phase2(o[i - 2], lse[i - 2], partials[i - 2], w[i - 1], conv, P[i - 1])
+        np.testing.assert_allclose(hi, direct[i - 1], rtol=1e-11, atol=1e-12)
+
+
+def pin_block_msar_merge_with_dominant_partial():
+    """A partial whose score dominates every rep's makes each stream's merged
+    state the partial's own stream (the reps' weight underflows): with one-tap
+    streams and P = 0, h = 4 * (1/2) * partial.  One token; the query is a
+    large multiple of the partial's normalised key, so by Cauchy-Schwarz its
+    score exceeds every rep's by a wide margin."""
+    r = _rng(9)
+    N, T, d = 3, 1, 8
+    reps = r.standard_normal((N, T, d))
+    part = r.standard_normal((T, d))
+    conv = np.zeros((24, d))
+    conv[[0, 4, 12], :] = 1.0                        # one-tap streams: every stream is the source
+    kp = aro.rms_normalise(part, 1e-6)[0]
+    w = np.zeros((2, 4, d))
+    w[1] = 60.0 * kp
+    s_rep = aro.rms_normalise(reps, 1e-6)[:, 0] @ w[1, 0]
+    assert kp @ w[1, 0] - s_rep.max() > 100.0        # the construction holds
+    _, o, lse = mso.block_msar_phase1(reps, w, conv, np.zeros((4 * d, 4)))
+    h2 = mso.block_msar_phase2(o[0], lse[0], part, w[1], conv, np.zeros((4 * d, 4)))
+    np.testing.assert_allclose(h2, 2.0 * part, rtol=1e-12, atol=1e-12)
+
+
 ALL_MSAR_PINS = [
     pin_msar_expand_is_causal_convolution, pin_msar_one_tap_streams_reduce_to_attnres, pin_msar_mixer_closed_form,
     pin_msar_identical_sources, pin_msar_token_window, pin_msar_magnitude_invariance, pin_msar_prefix_sets,
+    pin_block_msar_two_phase_equals_direct, pin_block_msar_merge_with_dominant_partial,
 ]

@@ -41,6 +41,14 @@ MUTATIONS = [
      "beta[j] = np.exp(rms_normalise(flat, eps) @ P[j]); beta[j] /= beta[j].sum(-1, keepdims=True)"),
     ("prefix_one_too_long", "msar_fwd",
      "n = n_src - n_dst + j + 1", "n = min(n_src, n_src - n_dst + j + 2)"),
+    ("phase1_lse_drops_max", "block_msar_phase1",
+     "lse[i, r] = m + np.log(l)", "lse[i, r] = np.log(l)"),
+    ("phase2_merge_sign_error", "block_msar_phase2",
+     "b = np.exp(sp - m)[:, None]", "b = np.exp(m - sp)[:, None]"),
+    ("phase2_merges_raw_partial", "block_msar_phase2",
+     "Z[r] = (a * o_i[r] + b * xp[r]) / (a + b)", "Z[r] = (a * o_i[r] + b * xp[0]) / (a + b)"),
+    ("phase1_sublayer1_mixer_from_wrong_state", "block_msar_phase1",
+     "return _mixer(o[0], P1, eps), o[1:], lse[1:]", "return _mixer(o[1], P1, eps), o[1:], lse[1:]"),
 ]
 
 
