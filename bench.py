@@ -10,7 +10,7 @@ in HBM before timing starts.
 Prints ONE JSON line on stdout.  Everything else goes to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                  [--no-extra] [--workload block|mhar|full|bwd|full_bwd|block_update|decode|msar]
+                  [--no-extra] [--workload block|mhar|full|bwd|full_bwd|block_update|decode|msar|block_msar]
                   [--copy-calibration]
 """
 
@@ -39,7 +39,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="block", choices=["block", "mhar", "full", "bwd", "full_bwd", "block_update",
-                                                                "decode", "msar"])
+                                                                "decode", "msar", "block_msar"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     p.add_argument("--copy-calibration", action="store_true",
@@ -351,6 +351,59 @@ def bench_msar(args, T=16384, d=4096, n=9):
                 tflops=flops / per / 1e12, bytes_per_call=nbytes, gbs=nbytes / per / 1e9)
 
 
+def bench_block_msar(args, T=16384, d=4096, N=8, S=4):
+    """One Block MSAR block, two-phase: Phase 1 over the 8 reps for the 4
+    sublayers, then 3 Phase-2 merges (the reps' streams are expanded once per
+    block instead of once per sublayer)."""
+    import torch
+    import depth_wise_attention_amd as ar
+    from workloads import synth
+
+    wl = synth.block_msar_workload(T=T, d=d, N=N, S=S, seed=0)
+    reps = to_dev(wl.reps, torch.bfloat16)
+    parts = to_dev(wl.partials, torch.bfloat16)
+    w = to_dev(wl.w, torch.float32)
+    conv = to_dev(wl.meta["conv"], torch.float32)
+    mix = to_dev(wl.meta["mix"], torch.float32)
+    del wl
+    h = torch.empty((S, T, d), dtype=torch.bfloat16, device="cuda")
+    o = torch.empty((S - 1, 4, T, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((S - 1, 4, T), dtype=torch.float32, device="cuda")
+    ws1 = torch.empty(ar.attnres_block_msar_phase1_workspace_size(N, S, T, d), dtype=torch.uint8, device="cuda")
+    ws2 = torch.empty(ar.attnres_block_msar_phase2_workspace_size(T, d), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(S + 1)] for _ in range(args.steps)]
+
+    def step(e=None):
+        if e:
+            e[0].record(stream)
+        ar.attnres_block_msar_phase1(reps, w, conv, mix[0], 1e-6, h1=h[0], o_state=o, lse=lse, ws=ws1, stream=stream)
+        if e:
+            e[1].record(stream)
+        for i in range(2, S + 1):
+            ar.attnres_block_msar_phase2(o[i - 2], lse[i - 2], parts[i - 2], w[i - 1], conv, mix[i - 1], 1e-6,
+                                         h_i=h[i - 1], ws=ws2, stream=stream)
+            if e:
+                e[i].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for s_ in range(args.steps):
+        step(ev[s_])
+    end.record(stream)
+    torch.cuda.synchronize()
+    total = start.elapsed_time(end) / 1e3
+    p1 = sum(ev[k][0].elapsed_time(ev[k][1]) for k in range(args.steps)) / args.steps
+    p2 = sum(ev[k][i - 1].elapsed_time(ev[k][i]) for k in range(args.steps) for i in range(2, S + 1)) / (
+        args.steps * (S - 1))
+    return dict(name=f"block_msar_two_phase_bf16_T{T}_d{d}_N{N}_S{S}", T=T, d=d, N=N, S=S, seconds=total,
+                tokens_per_s=T * args.steps / total, ms_per_step=total / args.steps * 1e3, phase1_ms=p1,
+                phase2_ms=p2)
+
+
 def bench_full(args, T=4096):
     import torch
     import depth_wise_attention_amd as ar
@@ -498,7 +551,7 @@ def main():
         fn = {"mhar": lambda: bench_block(args, H=8, T=32768), "full": lambda: bench_full(args),
               "bwd": lambda: bench_bwd(args), "full_bwd": lambda: bench_full_bwd(args),
               "block_update": lambda: bench_update(args), "decode": lambda: bench_decode(args),
-              "msar": lambda: bench_msar(args)}[args.workload]
+              "msar": lambda: bench_msar(args), "block_msar": lambda: bench_block_msar(args)}[args.workload]
         log(json.dumps(fn()))
         return
 
@@ -512,7 +565,7 @@ def main():
         torch.cuda.empty_cache()
         for fn in (lambda: bench_block(args, H=8, T=32768, with_events=True), lambda: bench_full(args),
                    lambda: bench_bwd(args), lambda: bench_full_bwd(args), lambda: bench_update(args),
-                   lambda: bench_decode(args), lambda: bench_msar(args)):
+                   lambda: bench_decode(args), lambda: bench_msar(args), lambda: bench_block_msar(args)):
             r = fn()
             extra[r.pop("name")] = {k: v for k, v in r.items() if k not in ("T", "d", "N", "S", "H")}
             torch.cuda.empty_cache()

@@ -13,6 +13,10 @@ from .binding import (  # noqa: F401
     attnres_block_phase1,
     attnres_block_phase2_merge,
     attnres_block_phase2_merge_update,
+    attnres_block_msar_phase1,
+    attnres_block_msar_phase1_workspace_size,
+    attnres_block_msar_phase2,
+    attnres_block_msar_phase2_workspace_size,
     attnres_bwd,
     attnres_bwd_workspace_size,
     attnres_full_bwd,

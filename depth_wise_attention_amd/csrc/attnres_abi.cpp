@@ -238,7 +238,103 @@ int attnres_msar_fwd(const void* src, int64_t n_src, int64_t T, int64_t d, const
   return e == hipSuccess ? ATTNRES_OK : hip_fail(e, "MSAR forward launch");
 }
 
-int attnres_version(void) { return (2 << 16) | 4; }
+namespace {
+int check_bmsar_shape(int64_t T, int64_t d, int32_t dtype, float eps) {
+  if (dtype != ATTNRES_BF16)
+    return fail(ATTNRES_ERR_UNSUPPORTED, "Block MSAR takes bf16 activations (dtype %d)", dtype);
+  if (T < 0) return fail(ATTNRES_ERR_INVALID, "T = %lld is negative", (long long)T);
+  if (d < 1 || d % 512 != 0 || d > ((int64_t)1 << 20))
+    return fail(ATTNRES_ERR_UNSUPPORTED, "Block MSAR needs d a multiple of 512 up to 2^20 (d = %lld)", (long long)d);
+  if (T > ((int64_t)1 << 30)) return fail(ATTNRES_ERR_UNSUPPORTED, "T = %lld exceeds 2^30", (long long)T);
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(ATTNRES_ERR_INVALID, "eps must be finite and >= 0");
+  return ATTNRES_OK;
+}
+
+bool aligned16p(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
+}  // namespace
+
+size_t attnres_block_msar_phase1_workspace_size(int64_t N, int64_t S, int64_t T, int64_t d) {
+  return bmsar_phase1_workspace_bytes(N, S, T, d);
+}
+
+int attnres_block_msar_phase1(const void* reps, int64_t N, int64_t T, int64_t d, const float* w, int64_t S,
+                              const float* conv, const float* mix1, float eps, int32_t dtype, void* h1,
+                              float* o_state, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  RETURN_IF(check_bmsar_shape(T, d, dtype, eps));
+  if (N < 1) return fail(ATTNRES_ERR_INVALID, "N = %lld must be >= 1", (long long)N);
+  if (N > kMsarFastMaxSources)
+    return fail(ATTNRES_ERR_UNSUPPORTED, "Block MSAR takes at most %d reps (N = %lld)", kMsarFastMaxSources,
+                (long long)N);
+  if (S < 1) return fail(ATTNRES_ERR_INVALID, "S = %lld must be >= 1", (long long)S);
+  if (S > 4) return fail(ATTNRES_ERR_UNSUPPORTED, "Block MSAR takes at most 4 sublayers (S = %lld)", (long long)S);
+  if (T == 0) return ATTNRES_OK;
+  REQUIRE_PTR(reps, "reps");
+  REQUIRE_PTR(w, "w");
+  REQUIRE_PTR(conv, "conv");
+  REQUIRE_PTR(mix1, "mix1");
+  REQUIRE_PTR(h1, "h1");
+  if (S > 1) {
+    REQUIRE_PTR(o_state, "o_state");
+    REQUIRE_PTR(lse, "lse");
+  }
+  const size_t need = attnres_block_msar_phase1_workspace_size(N, S, T, d);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(ATTNRES_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? ws_bytes : 0, need);
+  for (const void* q : {reps, (const void*)w, (const void*)conv, (const void*)mix1, (const void*)h1,
+                        (const void*)o_state, (const void*)lse, (const void*)ws})
+    if (!aligned16p(q)) return fail(ATTNRES_ERR_INVALID, "Block MSAR pointers must be 16-byte aligned");
+  const size_t td = (size_t)(T * d);
+  const Range ins[] = {{reps, (size_t)N * td * 2, "reps"},
+                       {w, (size_t)(S * kMsarStreams * d * 4), "w"},
+                       {conv, (size_t)(kMsarTaps * d * 4), "conv"},
+                       {mix1, (size_t)(kMsarStreams * d * kMsarStreams * 4), "mix1"}};
+  const Range outs[] = {{h1, td * 2, "h1"},
+                        {S > 1 ? o_state : nullptr, (size_t)(S - 1) * kMsarStreams * td * 4, "o_state"},
+                        {S > 1 ? lse : nullptr, (size_t)((S - 1) * kMsarStreams * T * 4), "lse"},
+                        {ws, need, "ws"}};
+  RETURN_IF(check_aliasing(ins, 4, outs, 4));
+  BmsarCall c{reps, N, T, d, w, S, conv, mix1, eps, h1, o_state, lse, ws};
+  const hipError_t e = launch_bmsar_phase1(c, stream);
+  return e == hipSuccess ? ATTNRES_OK : hip_fail(e, "Block MSAR phase 1 launch");
+}
+
+size_t attnres_block_msar_phase2_workspace_size(int64_t T, int64_t d) { return bmsar_phase2_workspace_bytes(T, d); }
+
+int attnres_block_msar_phase2(const float* o_i, const float* lse_i, const void* partial, int64_t T, int64_t d,
+                              const float* w_i, const float* conv, const float* mix_i, float eps, int32_t dtype,
+                              void* h_i, void* ws, size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  RETURN_IF(check_bmsar_shape(T, d, dtype, eps));
+  if (T == 0) return ATTNRES_OK;
+  REQUIRE_PTR(o_i, "o_i");
+  REQUIRE_PTR(lse_i, "lse_i");
+  REQUIRE_PTR(partial, "partial");
+  REQUIRE_PTR(w_i, "w_i");
+  REQUIRE_PTR(conv, "conv");
+  REQUIRE_PTR(mix_i, "mix_i");
+  REQUIRE_PTR(h_i, "h_i");
+  const size_t need = attnres_block_msar_phase2_workspace_size(T, d);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(ATTNRES_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? ws_bytes : 0, need);
+  for (const void* q : {(const void*)o_i, (const void*)lse_i, partial, (const void*)w_i, (const void*)conv,
+                        (const void*)mix_i, (const void*)h_i, (const void*)ws})
+    if (!aligned16p(q)) return fail(ATTNRES_ERR_INVALID, "Block MSAR pointers must be 16-byte aligned");
+  const size_t td = (size_t)(T * d);
+  const Range ins[] = {{o_i, kMsarStreams * td * 4, "o_i"},
+                       {lse_i, (size_t)(kMsarStreams * T * 4), "lse_i"},
+                       {partial, td * 2, "partial"},
+                       {w_i, (size_t)(kMsarStreams * d * 4), "w_i"},
+                       {conv, (size_t)(kMsarTaps * d * 4), "conv"},
+                       {mix_i, (size_t)(kMsarStreams * d * kMsarStreams * 4), "mix_i"}};
+  const Range outs[] = {{h_i, td * 2, "h_i"}, {ws, need, "ws"}};
+  RETURN_IF(check_aliasing(ins, 6, outs, 2));
+  Bmsar2Call c{o_i, lse_i, partial, T, d, w_i, conv, mix_i, eps, h_i, ws};
+  const hipError_t e = launch_bmsar_phase2(c, stream);
+  return e == hipSuccess ? ATTNRES_OK : hip_fail(e, "Block MSAR phase 2 launch");
+}
+
+int attnres_version(void) { return (2 << 16) | 5; }
 
 int attnres_set_kernel_policy(int32_t policy) {
   if (policy != 0 && policy != 1) return fail(ATTNRES_ERR_INVALID, "unknown kernel policy %d", policy);

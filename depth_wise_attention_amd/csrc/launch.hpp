@@ -184,6 +184,37 @@ size_t msar_fast_workspace_bytes(int64_t n_src, int64_t n_dst, int64_t T, int64_
 bool msar_fast_ok(const MsarArgs& a);
 hipError_t launch_msar_fast(const MsarArgs& a, hipStream_t st);
 
+// Block MSAR two-phase (bf16, N <= 12 reps, SB <= 4 sublayers, d % 512 == 0).
+struct BmsarCall {
+  const void* reps;
+  int64_t N, T, d;
+  const float* w;      // [SB][4][d]
+  int64_t SB;
+  const float* conv;   // [24][d]
+  const float* mix1;   // [4 d][4]
+  float eps;
+  void* h1;            // [T][d] bf16
+  float* o_state;      // [SB-1][4][T][d]
+  float* lse;          // [SB-1][4][T]
+  void* ws;
+};
+struct Bmsar2Call {
+  const float* o_i;    // [4][T][d]
+  const float* lse_i;  // [4][T]
+  const void* partial; // [T][d] bf16
+  int64_t T, d;
+  const float* w_i;    // [4][d]
+  const float* conv;
+  const float* mix_i;  // [4 d][4]
+  float eps;
+  void* h_i;           // [T][d] bf16
+  void* ws;
+};
+size_t bmsar_phase1_workspace_bytes(int64_t N, int64_t SB, int64_t T, int64_t d);
+hipError_t launch_bmsar_phase1(const BmsarCall& c, hipStream_t st);
+size_t bmsar_phase2_workspace_bytes(int64_t T, int64_t d);
+hipError_t launch_bmsar_phase2(const Bmsar2Call& c, hipStream_t st);
+
 int num_cus();  // compute units of the current device (cached per device)
 // Resident blocks per compute unit for a kernel and block size (cached).
 hipError_t blocks_per_cu(const void* kern, int block, int* out);

@@ -40,6 +40,10 @@ struct MsarFastBufs {
   float* alpha;   // [T][4][16]
   float* part2;   // [T][S][8]: [0] sum of squares of Z, [1 + q] projection q
   float* zbuf;    // [T][4][d]
+  // Optional state the weighted sum starts from (Block MSAR Phase 2):
+  // Z^(r) = base_coef[t][r] * base[r][t] + sum_i alpha x_i^(r).
+  const float* base = nullptr;       // [4][T][d] fp32
+  const float* base_coef = nullptr;  // [T][4]
 };
 
 // Sum of v[p] over the workgroup's 256 threads, for p < 64, into the
@@ -92,6 +96,18 @@ __global__ __launch_bounds__(kMfB, 2) void k_msar_slice(MsarArgs a, MsarFastBufs
       for (int q = 0; q < kMfTC; ++q)
 #pragma unroll
         for (int r = 0; r < kMsarStreams; ++r) z[q][r] = make_float2(0.f, 0.f);
+      if (b.base != nullptr) {
+#pragma unroll
+        for (int q = 0; q < kMfTC; ++q) {
+          const int64_t tq = t0 + q < T ? t0 + q : T - 1;
+#pragma unroll
+          for (int r = 0; r < kMsarStreams; ++r) {
+            const float2 o = *reinterpret_cast<const float2*>(b.base + (r * T + tq) * d + c0);
+            const float cf = b.base_coef[tq * kMsarStreams + r];
+            z[q][r] = make_float2(cf * o.x, cf * o.y);
+          }
+        }
+      }
       // The chunk's softmax weights, into LDS: per-source reads then go through
       // the LDS counter instead of queueing behind the prefetched rows.  The
       // barrier also orders the previous chunk's reads before these writes.
@@ -217,13 +233,9 @@ __global__ __launch_bounds__(256) void k_msar_alpha(MsarArgs a, MsarFastBufs b) 
       dot += p[ii * 8 + 4 + r];
     }
     const float score = valid ? dot / sqrtf(ss / (float)d + a.eps) : -INFINITY;
-    float m = score;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+    const float m = group_max<16>(score);
     const float e = valid ? expf(score - m) : 0.f;
-    float l = e;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) l += __shfl_xor(l, o, kWave);
+    const float l = group_sum<16>(e);
     b.alpha[t * (kMsarStreams * kMfAlphaRow) + r * kMfAlphaRow + i] = e / l;
   }
 }
@@ -256,6 +268,253 @@ __global__ __launch_bounds__(256) void k_msar_out(MsarArgs a, MsarFastBufs b) {
       }
       *reinterpret_cast<uint2*>(out + t * d + c) = make_uint2(pack_bf2(h.x, h.y), pack_bf2(h.z, h.w));
     }
+  }
+}
+
+// ------------------------------------------------------------ Block MSAR
+// Phase 1 ([MSAR] "How to use it": AttnRes's two-phase computation carries
+// over): the block's SB sublayers' queries against the N reps, each rep's
+// streams expanded once per pass for all of them.  Same slicing as
+// k_msar_slice, with 4-token chunks (the state pass keeps SB x 4 streams of
+// weighted sums per token).
+constexpr int kBmTC = 4;
+constexpr int kBmWin = kBmTC + kMfHalo;
+
+struct BmsarArgs {
+  const void* reps;    // [N][T][d] bf16
+  int64_t N, T, d;
+  const float* w;      // [SB][4][d]
+  const float* conv;   // [24][d]
+  const float* mix1;   // [4 d][4], sublayer 1's mixer
+  float eps;
+  float* o_state;      // [SB-1][4][T][d] fp32
+  float* lse;          // [SB-1][4][T]
+  float* part;         // [T][slices][N][4 + 4 SB]
+  float* alpha;        // [T][SB][4][16]
+  float* part2;        // [T][slices][8]
+  float* zbuf;         // [T][4][d], sublayer 1's retrieved states
+};
+
+// Workgroup sum of NV <= 256 values per thread: thread p < NV returns value p's total.
+template <int NV>
+__device__ __forceinline__ float block_reduce_values(const float (&v)[NV], float (&red)[2][4][256], int buf) {
+  constexpr int NG = (NV + 63) / 64;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  float tot[NG];
+  wave_reduce_values<NV>(v, tot);
+#pragma unroll
+  for (int g = 0; g < NG; ++g) red[buf][wave][g * 64 + lane] = tot[g];
+  lds_barrier();
+  return (red[buf][0][tid] + red[buf][1][tid]) + (red[buf][2][tid] + red[buf][3][tid]);
+}
+
+template <int SB, int PASS>
+__global__ __launch_bounds__(kMfB, 2) void k_bmsar_p1(BmsarArgs a) {
+  constexpr int V = 4 + 4 * SB;          // per rep and token: 4 sums of squares, 4 SB query products
+  constexpr int NV = PASS == 0 ? kBmTC * V : 64;
+  __shared__ float red[2][4][256];
+  __shared__ float alpha_s[PASS == 1 ? kBmTC * SB * kMsarStreams * kMfAlphaRow : 1];
+  const int tid = threadIdx.x;
+  const int64_t d = a.d, T = a.T;
+  const int n = (int)a.N;
+  const int S = (int)(d / kMfSlice);
+  const int slice = blockIdx.x;
+  const int64_t c0 = (int64_t)slice * kMfSlice + 2 * tid;
+  const bf16_t* src = static_cast<const bf16_t*>(a.reps);
+
+  float2 tap[kMsarTaps];
+#pragma unroll
+  for (int k = 0; k < kMsarTaps; ++k) tap[k] = *reinterpret_cast<const float2*>(a.conv + k * d + c0);
+  float2 wq[PASS == 0 ? SB : 1][kMsarStreams];
+  float4 pm[kMsarStreams][2];
+#pragma unroll
+  for (int r = 0; r < kMsarStreams; ++r) {
+    if constexpr (PASS == 0) {
+#pragma unroll
+      for (int i = 0; i < SB; ++i) wq[i][r] = *reinterpret_cast<const float2*>(a.w + (i * kMsarStreams + r) * d + c0);
+    } else {
+      pm[r][0] = *reinterpret_cast<const float4*>(a.mix1 + (r * d + c0) * kMsarStreams);
+      pm[r][1] = *reinterpret_cast<const float4*>(a.mix1 + (r * d + c0 + 1) * kMsarStreams);
+    }
+  }
+
+  const int64_t t_begin = (int64_t)blockIdx.y * kMfRange;
+  const int64_t t_end = t_begin + kMfRange < T ? t_begin + kMfRange : T;
+  int buf = 0;
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += kBmTC) {
+    float2 z[kBmTC][SB][kMsarStreams];
+    if constexpr (PASS == 1) {
+#pragma unroll
+      for (int q = 0; q < kBmTC; ++q)
+#pragma unroll
+        for (int i = 0; i < SB; ++i)
+#pragma unroll
+          for (int r = 0; r < kMsarStreams; ++r) z[q][i][r] = make_float2(0.f, 0.f);
+      lds_barrier();
+      constexpr int NA = kBmTC * SB * kMsarStreams * kMfAlphaRow;
+      for (int e = tid; e < NA; e += kMfB) {
+        const int64_t tq = t0 + e / (SB * kMsarStreams * kMfAlphaRow);
+        alpha_s[e] = a.alpha[(tq < T ? tq : T - 1) * (SB * kMsarStreams * kMfAlphaRow) +
+                             e % (SB * kMsarStreams * kMfAlphaRow)];
+      }
+      lds_barrier();
+    }
+    auto load_rows = [&](int i, uint32_t (&raw)[kBmWin]) {
+      const bf16_t* col = src + (int64_t)(i < n ? i : n - 1) * T * d + c0;
+#pragma unroll
+      for (int h = 0; h < kBmWin; ++h) {
+        const int64_t row = t0 - kMfHalo + h;
+        const int64_t rc = row < 0 ? 0 : (row >= T ? T - 1 : row);
+        raw[h] = *reinterpret_cast<const uint32_t*>(col + rc * d);
+      }
+    };
+    auto source = [&](int i, const uint32_t (&raw)[kBmWin]) {
+      float2 x[kBmWin];
+#pragma unroll
+      for (int h = 0; h < kBmWin; ++h) {
+        const int64_t row = t0 - kMfHalo + h;
+        const uint32_t u = (row >= 0 && row < T) ? raw[h] : 0u;
+        x[h] = make_float2(bf_lo(u), bf_hi(u));
+      }
+      float v[PASS == 0 ? NV : 1];
+#pragma unroll
+      for (int q = 0; q < kBmTC; ++q) {
+        float2 sv[kMsarStreams];
+        sv[0] = x[q + kMfHalo];
+#pragma unroll
+        for (int r = 1; r < kMsarStreams; ++r) {
+          const int K = msar_kernel(r), off = msar_offset(r);
+          float2 acc = make_float2(0.f, 0.f);
+#pragma unroll
+          for (int k = 0; k < K; ++k) {
+            acc.x = fmaf(tap[off + k].x, x[q + kMfHalo - k].x, acc.x);
+            acc.y = fmaf(tap[off + k].y, x[q + kMfHalo - k].y, acc.y);
+          }
+          sv[r] = acc;
+        }
+        if constexpr (PASS == 0) {
+#pragma unroll
+          for (int r = 0; r < kMsarStreams; ++r) {
+            v[q * V + r] = fmaf(sv[r].x, sv[r].x, sv[r].y * sv[r].y);
+#pragma unroll
+            for (int j = 0; j < SB; ++j)
+              v[q * V + 4 + j * kMsarStreams + r] = fmaf(wq[j][r].x, sv[r].x, wq[j][r].y * sv[r].y);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < SB; ++j)
+#pragma unroll
+            for (int r = 0; r < kMsarStreams; ++r) {
+              const float w_ri = alpha_s[((q * SB + j) * kMsarStreams + r) * kMfAlphaRow + i];
+              z[q][j][r].x = fmaf(w_ri, sv[r].x, z[q][j][r].x);
+              z[q][j][r].y = fmaf(w_ri, sv[r].y, z[q][j][r].y);
+            }
+        }
+      }
+      if constexpr (PASS == 0) {
+        const float tot = block_reduce_values<NV>(v, red, buf);
+        buf ^= 1;
+        const int p = tid;
+        if (p < NV && t0 + p / V < t_end)
+          a.part[(((t0 + p / V) * S + slice) * n + i) * V + p % V] = tot;
+      }
+    };
+    uint32_t ra[kBmWin], rb[kBmWin];
+    load_rows(0, ra);
+    for (int i = 0; i < n; i += 2) {
+      load_rows(i + 1, rb);
+      source(i, ra);
+      load_rows(i + 2, ra);
+      if (i + 1 < n) source(i + 1, rb);
+    }
+    if constexpr (PASS == 1) {
+      // Sublayers 2..SB: the per-stream states; sublayer 1: its retrieved
+      // states and the mixer's sums.
+      float v[64];
+#pragma unroll
+      for (int q = 0; q < kBmTC; ++q) {
+        const bool ok = t0 + q < t_end;
+#pragma unroll
+        for (int j = 1; j < SB; ++j)
+#pragma unroll
+          for (int r = 0; r < kMsarStreams; ++r)
+            if (ok) *reinterpret_cast<float2*>(a.o_state + (((j - 1) * kMsarStreams + r) * T + t0 + q) * d + c0) = z[q][j][r];
+        float e[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < kMsarStreams; ++r) {
+          const float2 zr = z[q][0][r];
+          if (ok) *reinterpret_cast<float2*>(a.zbuf + ((t0 + q) * kMsarStreams + r) * d + c0) = zr;
+          e[0] = fmaf(zr.x, zr.x, fmaf(zr.y, zr.y, e[0]));
+          e[1] = fmaf(zr.x, pm[r][0].x, fmaf(zr.y, pm[r][1].x, e[1]));
+          e[2] = fmaf(zr.x, pm[r][0].y, fmaf(zr.y, pm[r][1].y, e[2]));
+          e[3] = fmaf(zr.x, pm[r][0].z, fmaf(zr.y, pm[r][1].z, e[3]));
+          e[4] = fmaf(zr.x, pm[r][0].w, fmaf(zr.y, pm[r][1].w, e[4]));
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[q * 8 + j] = j < 5 ? e[j] : 0.f;
+      }
+#pragma unroll
+      for (int q = kBmTC * 8; q < 64; ++q) v[q] = 0.f;
+      const float tot = block_reduce_values<64>(v, red, buf);
+      buf ^= 1;
+      const int p = tid;
+      if (p < kBmTC * 8 && (p & 7) < 5 && t0 + p / 8 < t_end)
+        a.part2[((t0 + p / 8) * S + slice) * kMfPart2 + (p & 7)] = tot;
+    }
+  }
+}
+
+// Per token, wave j handles sublayer j: lane r*16 + n holds rep n of stream r.
+// Writes the weights, and for sublayers 2..SB the log-sum-exp Phase 2 merges with.
+template <int SB>
+__global__ __launch_bounds__(256) void k_bmsar_alpha(BmsarArgs a) {
+  constexpr int V = 4 + 4 * SB;
+  const int lane = lane_id(), j = threadIdx.x >> 6;
+  const int64_t T = a.T, d = a.d;
+  const int S = (int)(d / kMfSlice), n = (int)a.N;
+  const int r = lane >> 4, i = lane & 15;
+  const bool valid = i < n;
+  const int ii = valid ? i : 0;
+  if (j >= SB) return;  // whole waves: no cross-lane work below in a partial wave
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    float ss = 0.f, dot = 0.f;
+    for (int s = 0; s < S; ++s) {
+      const float* p = a.part + ((t * S + s) * n + ii) * V;
+      ss += p[r];
+      dot += p[4 + j * kMsarStreams + r];
+    }
+    const float score = valid ? dot / sqrtf(ss / (float)d + a.eps) : -INFINITY;
+    const float m = group_max<16>(score);
+    const float e = valid ? expf(score - m) : 0.f;
+    const float l = group_sum<16>(e);
+    a.alpha[((t * SB + j) * kMsarStreams + r) * kMfAlphaRow + i] = e / l;
+    if (j >= 1 && i == 0) a.lse[((j - 1) * kMsarStreams + r) * T + t] = m + logf(l);
+  }
+}
+
+// Block MSAR Phase 2 merge coefficients: the partial is source 0 of a
+// one-source pass; base_coef = e^{lse-m}/(...), alpha[.][r][0] = e^{s_p-m}/(...).
+__global__ __launch_bounds__(256) void k_bmsar_p2_coef(MsarArgs a, MsarFastBufs b, const float* lse_i,
+                                                       float* coef) {
+  const int64_t T = a.T, d = a.d;
+  const int S = (int)(d / kMfSlice);
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < T * kMsarStreams;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = e / kMsarStreams;
+    const int r = (int)(e % kMsarStreams);
+    float ss = 0.f, dot = 0.f;
+    for (int s = 0; s < S; ++s) {
+      const float* p = b.part + (t * S + s) * 8;
+      ss += p[r];
+      dot += p[4 + r];
+    }
+    const float sp = dot / sqrtf(ss / (float)d + a.eps);
+    const float L = lse_i[r * T + t];
+    const float m = fmaxf(L, sp);
+    const float wa = expf(L - m), wb = expf(sp - m);
+    const float inv = 1.0f / (wa + wb);
+    coef[t * kMsarStreams + r] = wa * inv;
+    b.alpha[t * (kMsarStreams * kMfAlphaRow) + r * kMfAlphaRow] = wb * inv;
   }
 }
 
@@ -306,6 +565,102 @@ bool msar_fast_ok(const MsarArgs& a) {
   if (need == 0 || a.ws == nullptr || a.ws_bytes < need) return false;
   if (a.T > ((int64_t)1 << 30) || a.d > ((int64_t)1 << 20)) return false;
   return al16(a.src) && al16(a.out) && al16(a.w) && al16(a.conv) && al16(a.mix) && al16(a.ws);
+}
+
+namespace {
+
+template <int SB>
+hipError_t launch_bmsar_p1_sb(const BmsarArgs& a, void* h1, hipStream_t st) {
+  const dim3 grid((unsigned)(a.d / kMfSlice), (unsigned)((a.T + kMfRange - 1) / kMfRange));
+  hipLaunchKernelGGL((k_bmsar_p1<SB, 0>), grid, dim3(kMfB), 0, st, a);
+  int64_t blocks = a.T < 8 * (int64_t)num_cus() ? a.T : 8 * (int64_t)num_cus();
+  hipLaunchKernelGGL((k_bmsar_alpha<SB>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_bmsar_p1<SB, 1>), grid, dim3(kMfB), 0, st, a);
+  MsarArgs ma{nullptr, a.N, a.T, a.d, a.w, a.conv, a.mix1, 1, a.eps, kBF16, h1, nullptr, 0};
+  MsarFastBufs mb{nullptr, nullptr, a.part2, a.zbuf};
+  int64_t oblocks = a.T < 4 * (int64_t)num_cus() ? a.T : 4 * (int64_t)num_cus();
+  hipLaunchKernelGGL(k_msar_out, dim3((unsigned)oblocks), dim3(256), 0, st, ma, mb);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t bmsar_phase1_workspace_bytes(int64_t N, int64_t SB, int64_t T, int64_t d) {
+  if (N < 1 || N > kMsarFastMaxSources || SB < 1 || SB > 4 || T < 1 || T > ((int64_t)1 << 30) ||
+      d % kMfSlice != 0 || d > ((int64_t)1 << 20))
+    return 0;
+  const int64_t S = d / kMfSlice, V = 4 + 4 * SB;
+  return align256((size_t)(T * S * N * V) * 4) + align256((size_t)(T * SB * kMsarStreams * kMfAlphaRow) * 4) +
+         align256((size_t)(T * S * kMfPart2) * 4) + align256((size_t)(T * kMsarStreams * d) * 4);
+}
+
+hipError_t launch_bmsar_phase1(const BmsarCall& c, hipStream_t st) {
+  const int64_t S = c.d / kMfSlice, V = 4 + 4 * c.SB;
+  char* p = static_cast<char*>(c.ws);
+  BmsarArgs a;
+  a.reps = c.reps;
+  a.N = c.N;
+  a.T = c.T;
+  a.d = c.d;
+  a.w = c.w;
+  a.conv = c.conv;
+  a.mix1 = c.mix1;
+  a.eps = c.eps;
+  a.o_state = c.o_state;
+  a.lse = c.lse;
+  a.part = reinterpret_cast<float*>(p);
+  p += align256((size_t)(c.T * S * c.N * V) * 4);
+  a.alpha = reinterpret_cast<float*>(p);
+  p += align256((size_t)(c.T * c.SB * kMsarStreams * kMfAlphaRow) * 4);
+  a.part2 = reinterpret_cast<float*>(p);
+  p += align256((size_t)(c.T * S * kMfPart2) * 4);
+  a.zbuf = reinterpret_cast<float*>(p);
+  switch (c.SB) {
+    case 1: return launch_bmsar_p1_sb<1>(a, c.h1, st);
+    case 2: return launch_bmsar_p1_sb<2>(a, c.h1, st);
+    case 3: return launch_bmsar_p1_sb<3>(a, c.h1, st);
+    case 4: return launch_bmsar_p1_sb<4>(a, c.h1, st);
+    default: return hipErrorNotSupported;
+  }
+}
+
+size_t bmsar_phase2_workspace_bytes(int64_t T, int64_t d) {
+  if (T < 1 || T > ((int64_t)1 << 30) || d % kMfSlice != 0 || d > ((int64_t)1 << 20)) return 0;
+  const int64_t S = d / kMfSlice;
+  return align256((size_t)(T * S * 8) * 4) + align256((size_t)(T * kMsarStreams * kMfAlphaRow) * 4) +
+         align256((size_t)(T * kMsarStreams) * 4) + align256((size_t)(T * S * kMfPart2) * 4) +
+         align256((size_t)(T * kMsarStreams * d) * 4);
+}
+
+hipError_t launch_bmsar_phase2(const Bmsar2Call& c, hipStream_t st) {
+  const int64_t S = c.d / kMfSlice;
+  char* p = static_cast<char*>(c.ws);
+  MsarFastBufs b;
+  b.part = reinterpret_cast<float*>(p);
+  p += align256((size_t)(c.T * S * 8) * 4);
+  b.alpha = reinterpret_cast<float*>(p);
+  p += align256((size_t)(c.T * kMsarStreams * kMfAlphaRow) * 4);
+  float* coef = reinterpret_cast<float*>(p);
+  p += align256((size_t)(c.T * kMsarStreams) * 4);
+  b.part2 = reinterpret_cast<float*>(p);
+  p += align256((size_t)(c.T * S * kMfPart2) * 4);
+  b.zbuf = reinterpret_cast<float*>(p);
+  b.base = c.o_i;
+  b.base_coef = coef;
+  MsarArgs a{c.partial, 1, c.T, c.d, c.w_i, c.conv, c.mix_i, 1, c.eps, kBF16, c.h_i, c.ws, 0};
+  const dim3 grid((unsigned)(c.d / kMfSlice), (unsigned)((c.T + kMfRange - 1) / kMfRange));
+  MsarFastBufs b0 = b;
+  b0.base = nullptr;
+  b0.base_coef = nullptr;
+  hipLaunchKernelGGL(k_msar_slice<0>, grid, dim3(kMfB), 0, st, a, b0);
+  const int64_t ce = c.T * kMsarStreams;
+  int64_t cblocks = (ce + 255) / 256;
+  if (cblocks > 8 * (int64_t)num_cus()) cblocks = 8 * (int64_t)num_cus();
+  hipLaunchKernelGGL(k_bmsar_p2_coef, dim3((unsigned)cblocks), dim3(256), 0, st, a, b0, c.lse_i, coef);
+  hipLaunchKernelGGL(k_msar_slice<1>, grid, dim3(kMfB), 0, st, a, b);
+  int64_t oblocks = c.T < 4 * (int64_t)num_cus() ? c.T : 4 * (int64_t)num_cus();
+  hipLaunchKernelGGL(k_msar_out, dim3((unsigned)oblocks), dim3(256), 0, st, a, b);
+  return hipGetLastError();
 }
 
 hipError_t launch_msar_fast(const MsarArgs& a, hipStream_t st) {

@@ -325,9 +325,58 @@ int attnres_msar_fwd(const void* src, int64_t n_src, int64_t T, int64_t d, const
                      const float* conv, const float* mix, int64_t n_dst, float eps, int32_t dtype,
                      void* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Block MSAR, two-phase ([MSAR] onedev.kr summary, "How to use it": Block MSAR
+ * keeps one stream per block and expands on demand, and AttnRes's two-phase
+ * computation carries over).  The streams and mixer are those of
+ * attnres_msar_fwd.  Sublayer i of a block reads the N reps b_0..b_{N-1} and,
+ * for i >= 2, the partial sum b_{i-1}.
+ *
+ * Phase 1: the S sublayers' per-stream queries against the N reps, each rep's
+ * streams expanded once for all of them.  Per sublayer i and stream r:
+ *   s_n = w_i^(r) . RMSNorm(v_n^(r)),  o_i^(r) = sum_n softmax_n(s)_n v_n^(r),
+ *   lse_i^(r) = log sum_n exp(s_n).
+ * Sublayer 1 reads the reps only, so h1 = mixer_1(o_1) is final; sublayers
+ * 2..S keep o and lse for Phase 2.
+ *
+ *  reps     [N, T, d] bf16 (T tokens from the sequence start)
+ *  w        [S, 4, d] fp32;  conv [24, d] fp32 (as attnres_msar_fwd)
+ *  mix1     [4 d, 4] fp32    sublayer 1's mixer
+ *  h1       [T, d] bf16
+ *  o_state  [S-1, 4, T, d] fp32;  lse [S-1, 4, T] fp32 (NULL allowed when S == 1)
+ *  ws       device workspace of attnres_block_msar_phase1_workspace_size() bytes
+ * Requires bf16, 1 <= N <= 12, 1 <= S <= 4, d a multiple of 512 (else
+ * ATTNRES_ERR_UNSUPPORTED) and 16-byte-aligned pointers.
+ */
+size_t attnres_block_msar_phase1_workspace_size(int64_t N, int64_t S, int64_t T, int64_t d);
+int attnres_block_msar_phase1(const void* reps, int64_t N, int64_t T, int64_t d, const float* w,
+                              int64_t S, const float* conv, const float* mix1, float eps,
+                              int32_t dtype, void* h1, float* o_state, float* lse, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Block MSAR Phase 2 for sublayer i >= 2: the partial's streams are scored
+ * with w_i and merged into Phase 1's state by online softmax, per stream
+ * (exact: the result equals attnres_msar_fwd over the reps and the partial):
+ *   m = max(lse, s_p),  Z^(r) = (e^{lse-m} o^(r) + e^{s_p-m} p^(r)) / (e^{lse-m} + e^{s_p-m}),
+ * then h_i = sum_r beta_r Z^(r) with beta = sigmoid(RMSNorm(Flatten(Z)) P_i).
+ *
+ *  o_i      [4, T, d] fp32 and lse_i [4, T] fp32: Phase 1's o_state[i-2], lse[i-2]
+ *  partial  [T, d] bf16 (the block's partial sum before sublayer i)
+ *  w_i      [4, d];  conv [24, d];  mix_i [4 d, 4] (fp32)
+ *  h_i      [T, d] bf16
+ *  ws       device workspace of attnres_block_msar_phase2_workspace_size() bytes
+ * Same requirements as Phase 1.
+ */
+size_t attnres_block_msar_phase2_workspace_size(int64_t T, int64_t d);
+int attnres_block_msar_phase2(const float* o_i, const float* lse_i, const void* partial, int64_t T,
+                              int64_t d, const float* w_i, const float* conv, const float* mix_i,
+                              float eps, int32_t dtype, void* h_i, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
+
 /* ABI version: (major << 16) | minor.  Major 2 added the Full-forward workspace;
  * minor 1 added the Full backward, minor 2 the fused Phase 2 update, minor 3 the
- * chunked block forward, minor 4 MSAR. */
+ * chunked block forward, minor 4 MSAR, minor 5 the two-phase Block MSAR. */
 int attnres_version(void);
 
 /*

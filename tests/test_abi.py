@@ -40,7 +40,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("attnres_full_fwd", "attnres_block_phase1", "attnres_block_phase2_merge",
                  "attnres_block_phase2_merge_update", "mhar_fwd", "mhar_fwd_chunked", "attnres_msar_fwd",
-                 "attnres_msar_fwd_workspace_size",
+                 "attnres_msar_fwd_workspace_size", "attnres_block_msar_phase1", "attnres_block_msar_phase2",
+                 "attnres_block_msar_phase1_workspace_size", "attnres_block_msar_phase2_workspace_size",
                  "attnres_bwd", "attnres_full_bwd", "attnres_full_fwd_workspace_size", "mhar_fwd_workspace_size",
                  "attnres_bwd_workspace_size", "attnres_full_bwd_workspace_size",
                  "attnres_last_error", "attnres_version", "attnres_set_kernel_policy"):
@@ -55,7 +56,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_policy():
     assert binding.attnres_version() >> 16 == 2
-    assert binding.attnres_version() & 0xFFFF >= 4
+    assert binding.attnres_version() & 0xFFFF >= 5
     prev = binding.attnres_set_kernel_policy(1)
     assert binding.attnres_set_kernel_policy(prev) == 1
     with pytest.raises(binding.AttnResError):
@@ -366,3 +367,40 @@ def test_msar_rejects_bad_arguments():
               dict(T=-1), dict(out=FAKE + 1000), dict(out=FAKE + 2 * G + 8), dict(out=FAKE + 3 * G)]:
         assert _rc_msar(**c) == EINVAL, c
     assert _rc_msar(T=0, src=None, out=None) == OK
+
+
+def _rc_bm1(**kw):
+    G = 1 << 30
+    a = dict(reps=FAKE, N=8, T=100, d=512, w=FAKE + G, S=4, conv=FAKE + 2 * G, mix=FAKE + 3 * G, eps=1e-6,
+             dtype=BF16, h1=FAKE + 4 * G, o=FAKE + 5 * G, lse=FAKE + 6 * G, ws=FAKE + 7 * G, ws_bytes=1 << 30)
+    a.update(kw)
+    return binding.lib().attnres_block_msar_phase1(a["reps"], a["N"], a["T"], a["d"], a["w"], a["S"], a["conv"],
+                                                   a["mix"], a["eps"], a["dtype"], a["h1"], a["o"], a["lse"],
+                                                   a["ws"], a["ws_bytes"], None)
+
+
+def _rc_bm2(**kw):
+    G = 1 << 30
+    a = dict(o=FAKE, lse=FAKE + G, p=FAKE + 2 * G, T=100, d=512, w=FAKE + 3 * G, conv=FAKE + 4 * G,
+             mix=FAKE + 5 * G, eps=1e-6, dtype=BF16, h=FAKE + 6 * G, ws=FAKE + 7 * G, ws_bytes=1 << 30)
+    a.update(kw)
+    return binding.lib().attnres_block_msar_phase2(a["o"], a["lse"], a["p"], a["T"], a["d"], a["w"], a["conv"],
+                                                   a["mix"], a["eps"], a["dtype"], a["h"], a["ws"], a["ws_bytes"], None)
+
+
+@fake_ptrs
+def test_block_msar_rejects_bad_arguments():
+    G = 1 << 30
+    for c, want in [(dict(dtype=F32), EUNSUP), (dict(N=13), EUNSUP), (dict(S=5), EUNSUP), (dict(d=500), EUNSUP),
+                    (dict(N=0), EINVAL), (dict(S=0), EINVAL), (dict(reps=None), EINVAL), (dict(h1=None), EINVAL),
+                    (dict(o=None), EINVAL), (dict(eps=-1.0), EINVAL), (dict(ws_bytes=16), EWS),
+                    (dict(h1=FAKE + 8), EINVAL), (dict(lse=FAKE + 4 * G + 64), EINVAL),
+                    (dict(ws=FAKE + 5 * G), EINVAL)]:
+        assert _rc_bm1(**c) == want, c
+    assert _rc_bm1(S=1, o=None, lse=None, ws_bytes=16) == EWS     # S == 1 needs no state
+    assert _rc_bm1(T=0, reps=None) == OK
+    for c, want in [(dict(dtype=F32), EUNSUP), (dict(d=1000), EUNSUP), (dict(o=None), EINVAL),
+                    (dict(p=None), EINVAL), (dict(h=None), EINVAL), (dict(ws_bytes=16), EWS),
+                    (dict(h=FAKE + 2 * G + 32), EINVAL), (dict(ws=FAKE + G), EINVAL)]:
+        assert _rc_bm2(**c) == want, c
+    assert _rc_bm2(T=0, o=None) == OK

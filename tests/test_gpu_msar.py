@@ -97,3 +97,51 @@ def test_msar_block_sublayer_sampled():
         lo = max(0, int(t) - 11)      # the window its streams read
         ref = mso.msar_fwd(wl.src[:, lo:t + 1], wl.w, wl.meta["conv"], wl.meta["mix"], wl.eps)[:, -1]
         check(host(out[:, t]), ref, "bf16", f"msar token {t}")
+
+
+# ----------------------------------------------------------------- Block MSAR, two-phase
+def _bm_run(wl, N, S):
+    reps = dev(wl.reps, torch.bfloat16)
+    parts = dev(wl.partials, torch.bfloat16) if S > 1 else None
+    w, conv, mix = dev(wl.w), dev(wl.meta["conv"]), dev(wl.meta["mix"])
+    h1, o, lse = ar.attnres_block_msar_phase1(reps, w, conv, mix[0], wl.eps)
+    hs = [h1]
+    for i in range(2, S + 1):
+        hs.append(ar.attnres_block_msar_phase2(o[i - 2], lse[i - 2], parts[i - 2], w[i - 1], conv, mix[i - 1], wl.eps))
+    return torch.stack(hs), o, lse
+
+
+@pytest.mark.parametrize("T,d,N,S", [
+    (5, 512, 1, 1),
+    (20, 512, 3, 4),
+    (130, 1024, 8, 4),
+    (257, 512, 12, 2),
+    (300, 1536, 5, 3),
+    (64, 4096, 8, 4),
+])
+def test_block_msar_two_phase(T, d, N, S):
+    say(f"block msar two-phase T={T} d={d} N={N} S={S}")
+    wl = synth.block_msar_workload(T=T, d=d, N=N, S=S, seed=70)
+    ref = mso.block_msar_direct(wl.reps, wl.partials, wl.w, wl.meta["conv"], wl.meta["mix"], wl.eps)
+    h, o, lse = _bm_run(wl, N, S)
+    for i in range(S):
+        check(host(h[i]), ref[i], "bf16", f"h_{i + 1}")
+    if S > 1:
+        _, o_ref, lse_ref = mso.block_msar_phase1(wl.reps, wl.w, wl.meta["conv"], wl.meta["mix"][0], wl.eps)
+        check(host(o), o_ref, "f32_from_bf16", "phase 1 state")
+        np.testing.assert_allclose(host(lse), lse_ref, rtol=0, atol=1e-4)
+    h2, _, _ = _bm_run(wl, N, S)
+    assert torch.equal(h, h2), "not deterministic"
+
+
+def test_block_msar_sampled():
+    """Block MSAR at the Block size: T=16384, d=4096, N=8 reps, S=4, on sampled
+    tokens (each with the 11 tokens its streams read)."""
+    wl = synth.block_msar_workload(T=16384, d=4096, N=8, S=4, seed=0)
+    say(f"block msar two-phase T={wl.T} d={wl.d} N=8 S=4 (sampled tokens)")
+    h, _, _ = _bm_run(wl, 8, 4)
+    for t in np.concatenate([[0, 11, 12], synth.sample_tokens(wl.T, 40)]):
+        lo = max(0, int(t) - 11)
+        ref = mso.block_msar_direct(wl.reps[:, lo:t + 1], wl.partials[:, lo:t + 1], wl.w, wl.meta["conv"],
+                                    wl.meta["mix"], wl.eps)[:, -1]
+        check(host(h[:, t]), ref, "bf16", f"block msar token {t}")

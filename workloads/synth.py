@@ -237,6 +237,24 @@ def msar_workload(T: int, d: int, n_src: int, n_dst: int, dtype: str, seed: int 
                     n_dst=n_dst, meta=dict(conv=conv, mix=mix, std_step=std_step, seed=seed))
 
 
+def block_msar_workload(T: int, d: int, N: int, S: int, seed: int = 0, rep_std_step: float = 0.3,
+                        eps: float = 1e-6, name: str = "block_msar") -> Workload:
+    """Block MSAR inputs: the block reps and partial sums of block_workload
+    (bf16), with MSAR parameters as in msar_workload: w [S, 4, d] ~ N(0, 1/d),
+    taps conv [24, d] (stream r's K_r taps ~ N(0, 1/K_r)), one mixer per
+    sublayer P [S, 4 d, 4] ~ N(0, 1/(4 d))."""
+    wl = block_workload(T=T, d=d, N=N, S=S, H=1, rep_std_step=rep_std_step, dtype="bf16", seed=seed,
+                        gain_variance=None, eps=eps, name=name)
+    w = _pseudo_queries(S * 4, d, seed).reshape(S, 4, d)
+    conv = np.concatenate([normal_stack(1, (K, d), [1.0 / math.sqrt(K)], seed, _TID_CONV + 16 * r)[0]
+                           for r, K in enumerate((4, 8, 12))])
+    mix = normal_stack(S, (4 * d, 4), [1.0 / math.sqrt(4 * d)] * S, seed, _TID_MIX)
+    wl.w = w
+    wl.kind = "block_msar"
+    wl.meta.update(conv=conv, mix=mix)
+    return wl
+
+
 # ---------------------------------------------------------------------------
 # The five named workloads (shapes and distributions of the benchmark configs).
 # ---------------------------------------------------------------------------
