@@ -367,7 +367,8 @@ def bench_block_msar(args, T=16384, d=4096, N=8, S=4):
     mix = to_dev(wl.meta["mix"], torch.float32)
     del wl
     h = torch.empty((S, T, d), dtype=torch.bfloat16, device="cuda")
-    o = torch.empty((S - 1, 4, T, d), dtype=torch.float32, device="cuda")
+    o = torch.empty((S - 1, 4, T, d), dtype=torch.float16, device="cuda")
+    osc = torch.empty((T,), dtype=torch.float32, device="cuda")
     lse = torch.empty((S - 1, 4, T), dtype=torch.float32, device="cuda")
     ws1 = torch.empty(ar.attnres_block_msar_phase1_workspace_size(N, S, T, d), dtype=torch.uint8, device="cuda")
     ws2 = torch.empty(ar.attnres_block_msar_phase2_workspace_size(T, d), dtype=torch.uint8, device="cuda")
@@ -377,11 +378,12 @@ def bench_block_msar(args, T=16384, d=4096, N=8, S=4):
     def step(e=None):
         if e:
             e[0].record(stream)
-        ar.attnres_block_msar_phase1(reps, w, conv, mix[0], 1e-6, h1=h[0], o_state=o, lse=lse, ws=ws1, stream=stream)
+        ar.attnres_block_msar_phase1(reps, w, conv, mix[0], 1e-6, h1=h[0], o_state=o, o_scale=osc, lse=lse, ws=ws1,
+                                     stream=stream)
         if e:
             e[1].record(stream)
         for i in range(2, S + 1):
-            ar.attnres_block_msar_phase2(o[i - 2], lse[i - 2], parts[i - 2], w[i - 1], conv, mix[i - 1], 1e-6,
+            ar.attnres_block_msar_phase2(o[i - 2], osc, lse[i - 2], parts[i - 2], w[i - 1], conv, mix[i - 1], 1e-6,
                                          h_i=h[i - 1], ws=ws2, stream=stream)
             if e:
                 e[i].record(stream)

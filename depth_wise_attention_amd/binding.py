@@ -61,11 +61,12 @@ def lib() -> ctypes.CDLL:
     L.attnres_msar_fwd.restype = ctypes.c_int
     L.attnres_block_msar_phase1_workspace_size.argtypes = [i64, i64, i64, i64]
     L.attnres_block_msar_phase1_workspace_size.restype = sz
-    L.attnres_block_msar_phase1.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp, f32, i32, vp, vp, vp, vp, sz, vp]
+    L.attnres_block_msar_phase1.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp, f32, i32, vp, vp, vp, vp, vp, sz,
+                                            vp]
     L.attnres_block_msar_phase1.restype = ctypes.c_int
     L.attnres_block_msar_phase2_workspace_size.argtypes = [i64, i64]
     L.attnres_block_msar_phase2_workspace_size.restype = sz
-    L.attnres_block_msar_phase2.argtypes = [vp, vp, vp, i64, i64, vp, vp, vp, f32, i32, vp, vp, sz, vp]
+    L.attnres_block_msar_phase2.argtypes = [vp, vp, vp, vp, i64, i64, vp, vp, vp, f32, i32, vp, vp, sz, vp]
     L.attnres_block_msar_phase2.restype = ctypes.c_int
     L.attnres_set_kernel_policy.argtypes = [i32]
     for name in ("attnres_full_fwd", "attnres_block_phase1", "attnres_block_phase2_merge",
@@ -316,10 +317,10 @@ def attnres_block_msar_phase2_workspace_size(T: int, d: int) -> int:
     return lib().attnres_block_msar_phase2_workspace_size(T, d)
 
 
-def attnres_block_msar_phase1(reps, w, conv, mix1, eps: float = 1e-6, h1=None, o_state=None, lse=None, ws=None,
-                              stream=None):
+def attnres_block_msar_phase1(reps, w, conv, mix1, eps: float = 1e-6, h1=None, o_state=None, o_scale=None, lse=None,
+                              ws=None, stream=None):
     """Block MSAR Phase 1.  reps [N, T, d] bf16; w [S, 4, d]; conv [24, d]; mix1 [4 d, 4]
-    -> (h1 [T, d], o_state [S-1, 4, T, d] fp32, lse [S-1, 4, T] fp32)."""
+    -> (h1 [T, d], o_state [S-1, 4, T, d] fp16, o_scale [T] fp32, lse [S-1, 4, T] fp32)."""
     torch = _torch()
     N, T, d = reps.shape
     S = w.shape[0]
@@ -327,21 +328,24 @@ def attnres_block_msar_phase1(reps, w, conv, mix1, eps: float = 1e-6, h1=None, o
     if h1 is None:
         h1 = torch.empty((T, d), dtype=reps.dtype, device=dev)
     if o_state is None:
-        o_state = torch.empty((max(S - 1, 0), 4, T, d), dtype=torch.float32, device=dev)
+        o_state = torch.empty((max(S - 1, 0), 4, T, d), dtype=torch.float16, device=dev)
+    if o_scale is None:
+        o_scale = torch.empty((T,), dtype=torch.float32, device=dev)
     if lse is None:
         lse = torch.empty((max(S - 1, 0), 4, T), dtype=torch.float32, device=dev)
     if ws is None:
         ws = torch.empty(max(1, attnres_block_msar_phase1_workspace_size(N, S, T, d)), dtype=torch.uint8,
                          device=dev)
     _check(lib().attnres_block_msar_phase1(_p(reps), N, T, d, _p(w), S, _p(conv), _p(mix1), eps, _code(reps),
-                                           _p(h1), _p(o_state) if S > 1 else None, _p(lse) if S > 1 else None,
-                                           _p(ws), _nbytes(ws), _stream(stream)))
-    return h1, o_state, lse
+                                           _p(h1), _p(o_state) if S > 1 else None, _p(o_scale),
+                                           _p(lse) if S > 1 else None, _p(ws), _nbytes(ws), _stream(stream)))
+    return h1, o_state, o_scale, lse
 
 
-def attnres_block_msar_phase2(o_i, lse_i, partial, w_i, conv, mix_i, eps: float = 1e-6, h_i=None, ws=None,
+def attnres_block_msar_phase2(o_i, o_scale, lse_i, partial, w_i, conv, mix_i, eps: float = 1e-6, h_i=None, ws=None,
                               stream=None):
-    """Block MSAR Phase 2 for one sublayer: o_i [4, T, d], lse_i [4, T], partial [T, d] -> h_i [T, d]."""
+    """Block MSAR Phase 2 for one sublayer: o_i [4, T, d] fp16, o_scale [T], lse_i [4, T], partial [T, d]
+    -> h_i [T, d]."""
     torch = _torch()
     T, d = partial.shape
     if h_i is None:
@@ -349,7 +353,7 @@ def attnres_block_msar_phase2(o_i, lse_i, partial, w_i, conv, mix_i, eps: float 
     if ws is None:
         ws = torch.empty(max(1, attnres_block_msar_phase2_workspace_size(T, d)), dtype=torch.uint8,
                          device=partial.device)
-    _check(lib().attnres_block_msar_phase2(_p(o_i), _p(lse_i), _p(partial), T, d, _p(w_i), _p(conv), _p(mix_i), eps,
+    _check(lib().attnres_block_msar_phase2(_p(o_i), _p(o_scale), _p(lse_i), _p(partial), T, d, _p(w_i), _p(conv), _p(mix_i), eps,
                                            _code(partial), _p(h_i), _p(ws), _nbytes(ws), _stream(stream)))
     return h_i
 

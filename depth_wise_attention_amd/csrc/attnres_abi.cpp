@@ -259,7 +259,8 @@ size_t attnres_block_msar_phase1_workspace_size(int64_t N, int64_t S, int64_t T,
 
 int attnres_block_msar_phase1(const void* reps, int64_t N, int64_t T, int64_t d, const float* w, int64_t S,
                               const float* conv, const float* mix1, float eps, int32_t dtype, void* h1,
-                              float* o_state, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+                              void* o_state, float* o_scale, float* lse, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
   clear_error();
   RETURN_IF(check_bmsar_shape(T, d, dtype, eps));
   if (N < 1) return fail(ATTNRES_ERR_INVALID, "N = %lld must be >= 1", (long long)N);
@@ -274,6 +275,7 @@ int attnres_block_msar_phase1(const void* reps, int64_t N, int64_t T, int64_t d,
   REQUIRE_PTR(conv, "conv");
   REQUIRE_PTR(mix1, "mix1");
   REQUIRE_PTR(h1, "h1");
+  REQUIRE_PTR(o_scale, "o_scale");
   if (S > 1) {
     REQUIRE_PTR(o_state, "o_state");
     REQUIRE_PTR(lse, "lse");
@@ -282,7 +284,7 @@ int attnres_block_msar_phase1(const void* reps, int64_t N, int64_t T, int64_t d,
   if (ws == nullptr || ws_bytes < need)
     return fail(ATTNRES_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? ws_bytes : 0, need);
   for (const void* q : {reps, (const void*)w, (const void*)conv, (const void*)mix1, (const void*)h1,
-                        (const void*)o_state, (const void*)lse, (const void*)ws})
+                        (const void*)o_state, (const void*)o_scale, (const void*)lse, (const void*)ws})
     if (!aligned16p(q)) return fail(ATTNRES_ERR_INVALID, "Block MSAR pointers must be 16-byte aligned");
   const size_t td = (size_t)(T * d);
   const Range ins[] = {{reps, (size_t)N * td * 2, "reps"},
@@ -290,24 +292,26 @@ int attnres_block_msar_phase1(const void* reps, int64_t N, int64_t T, int64_t d,
                        {conv, (size_t)(kMsarTaps * d * 4), "conv"},
                        {mix1, (size_t)(kMsarStreams * d * kMsarStreams * 4), "mix1"}};
   const Range outs[] = {{h1, td * 2, "h1"},
-                        {S > 1 ? o_state : nullptr, (size_t)(S - 1) * kMsarStreams * td * 4, "o_state"},
+                        {S > 1 ? o_state : nullptr, (size_t)(S - 1) * kMsarStreams * td * 2, "o_state"},
+                        {o_scale, (size_t)T * 4, "o_scale"},
                         {S > 1 ? lse : nullptr, (size_t)((S - 1) * kMsarStreams * T * 4), "lse"},
                         {ws, need, "ws"}};
-  RETURN_IF(check_aliasing(ins, 4, outs, 4));
-  BmsarCall c{reps, N, T, d, w, S, conv, mix1, eps, h1, o_state, lse, ws};
+  RETURN_IF(check_aliasing(ins, 4, outs, 5));
+  BmsarCall c{reps, N, T, d, w, S, conv, mix1, eps, h1, o_state, o_scale, lse, ws};
   const hipError_t e = launch_bmsar_phase1(c, stream);
   return e == hipSuccess ? ATTNRES_OK : hip_fail(e, "Block MSAR phase 1 launch");
 }
 
 size_t attnres_block_msar_phase2_workspace_size(int64_t T, int64_t d) { return bmsar_phase2_workspace_bytes(T, d); }
 
-int attnres_block_msar_phase2(const float* o_i, const float* lse_i, const void* partial, int64_t T, int64_t d,
-                              const float* w_i, const float* conv, const float* mix_i, float eps, int32_t dtype,
-                              void* h_i, void* ws, size_t ws_bytes, hipStream_t stream) {
+int attnres_block_msar_phase2(const void* o_i, const float* o_scale, const float* lse_i, const void* partial,
+                              int64_t T, int64_t d, const float* w_i, const float* conv, const float* mix_i, float eps,
+                              int32_t dtype, void* h_i, void* ws, size_t ws_bytes, hipStream_t stream) {
   clear_error();
   RETURN_IF(check_bmsar_shape(T, d, dtype, eps));
   if (T == 0) return ATTNRES_OK;
   REQUIRE_PTR(o_i, "o_i");
+  REQUIRE_PTR(o_scale, "o_scale");
   REQUIRE_PTR(lse_i, "lse_i");
   REQUIRE_PTR(partial, "partial");
   REQUIRE_PTR(w_i, "w_i");
@@ -317,19 +321,20 @@ int attnres_block_msar_phase2(const float* o_i, const float* lse_i, const void* 
   const size_t need = attnres_block_msar_phase2_workspace_size(T, d);
   if (ws == nullptr || ws_bytes < need)
     return fail(ATTNRES_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? ws_bytes : 0, need);
-  for (const void* q : {(const void*)o_i, (const void*)lse_i, partial, (const void*)w_i, (const void*)conv,
-                        (const void*)mix_i, (const void*)h_i, (const void*)ws})
+  for (const void* q : {o_i, (const void*)o_scale, (const void*)lse_i, partial, (const void*)w_i,
+                        (const void*)conv, (const void*)mix_i, (const void*)h_i, (const void*)ws})
     if (!aligned16p(q)) return fail(ATTNRES_ERR_INVALID, "Block MSAR pointers must be 16-byte aligned");
   const size_t td = (size_t)(T * d);
-  const Range ins[] = {{o_i, kMsarStreams * td * 4, "o_i"},
+  const Range ins[] = {{o_i, kMsarStreams * td * 2, "o_i"},
+                       {o_scale, (size_t)T * 4, "o_scale"},
                        {lse_i, (size_t)(kMsarStreams * T * 4), "lse_i"},
                        {partial, td * 2, "partial"},
                        {w_i, (size_t)(kMsarStreams * d * 4), "w_i"},
                        {conv, (size_t)(kMsarTaps * d * 4), "conv"},
                        {mix_i, (size_t)(kMsarStreams * d * kMsarStreams * 4), "mix_i"}};
   const Range outs[] = {{h_i, td * 2, "h_i"}, {ws, need, "ws"}};
-  RETURN_IF(check_aliasing(ins, 6, outs, 2));
-  Bmsar2Call c{o_i, lse_i, partial, T, d, w_i, conv, mix_i, eps, h_i, ws};
+  RETURN_IF(check_aliasing(ins, 7, outs, 2));
+  Bmsar2Call c{o_i, o_scale, lse_i, partial, T, d, w_i, conv, mix_i, eps, h_i, ws};
   const hipError_t e = launch_bmsar_phase2(c, stream);
   return e == hipSuccess ? ATTNRES_OK : hip_fail(e, "Block MSAR phase 2 launch");
 }

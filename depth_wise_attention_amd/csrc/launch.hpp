@@ -194,12 +194,14 @@ struct BmsarCall {
   const float* mix1;   // [4 d][4]
   float eps;
   void* h1;            // [T][d] bf16
-  float* o_state;      // [SB-1][4][T][d]
+  void* o_state;       // [SB-1][4][T][d] fp16, scaled per token
+  float* o_scale;      // [T]
   float* lse;          // [SB-1][4][T]
   void* ws;
 };
 struct Bmsar2Call {
-  const float* o_i;    // [4][T][d]
+  const void* o_i;     // [4][T][d] fp16, scaled per token
+  const float* o_scale;  // [T]
   const float* lse_i;  // [4][T]
   const void* partial; // [T][d] bf16
   int64_t T, d;

@@ -41,9 +41,10 @@ struct MsarFastBufs {
   float* part2;   // [T][S][8]: [0] sum of squares of Z, [1 + q] projection q
   float* zbuf;    // [T][4][d]
   // Optional state the weighted sum starts from (Block MSAR Phase 2):
-  // Z^(r) = base_coef[t][r] * base[r][t] + sum_i alpha x_i^(r).
-  const float* base = nullptr;       // [4][T][d] fp32
-  const float* base_coef = nullptr;  // [T][4]
+  // Z^(r) = base_coef[t][r] * base_scale[t] * base[r][t] + sum_i alpha x_i^(r).
+  const f16_t* base = nullptr;        // [4][T][d], fp16 scaled per token
+  const float* base_scale = nullptr;  // [T]
+  const float* base_coef = nullptr;   // [T][4]
 };
 
 // Sum of v[p] over the workgroup's 256 threads, for p < 64, into the
@@ -57,10 +58,14 @@ __device__ __forceinline__ float block_reduce64(const float (&v)[64], float (&re
   return (red[buf][0][p] + red[buf][1][p]) + (red[buf][2][p] + red[buf][3][p]);
 }
 
+// PASS 0: per-source statistics; PASS 1: retrieved states (stored to zbuf
+// unless it is null) and the mixer's sums; PASS 2: the retrieved states again,
+// weighted by the mixer into out (no zbuf round trip).
 template <int PASS>
 __global__ __launch_bounds__(kMfB, 2) void k_msar_slice(MsarArgs a, MsarFastBufs b) {
   __shared__ float red[2][4][64];
-  __shared__ float alpha_s[PASS == 1 ? kMfTC * kMsarStreams * kMfAlphaRow : 1];
+  __shared__ float alpha_s[PASS >= 1 ? kMfTC * kMsarStreams * kMfAlphaRow : 1];
+  __shared__ float beta_s[PASS == 2 ? kMfTC * kMsarStreams : 1];
   const int tid = threadIdx.x;
   const int64_t d = a.d, T = a.T;
   const int n = (int)a.n_src;
@@ -91,7 +96,7 @@ __global__ __launch_bounds__(kMfB, 2) void k_msar_slice(MsarArgs a, MsarFastBufs
   int buf = 0;
   for (int64_t t0 = t_begin; t0 < t_end; t0 += kMfTC) {
     float2 z[kMfTC][kMsarStreams];
-    if constexpr (PASS == 1) {
+    if constexpr (PASS >= 1) {
 #pragma unroll
       for (int q = 0; q < kMfTC; ++q)
 #pragma unroll
@@ -100,11 +105,14 @@ __global__ __launch_bounds__(kMfB, 2) void k_msar_slice(MsarArgs a, MsarFastBufs
 #pragma unroll
         for (int q = 0; q < kMfTC; ++q) {
           const int64_t tq = t0 + q < T ? t0 + q : T - 1;
+          const float sc = b.base_scale[tq];
 #pragma unroll
           for (int r = 0; r < kMsarStreams; ++r) {
-            const float2 o = *reinterpret_cast<const float2*>(b.base + (r * T + tq) * d + c0);
-            const float cf = b.base_coef[tq * kMsarStreams + r];
-            z[q][r] = make_float2(cf * o.x, cf * o.y);
+            const uint32_t u = *reinterpret_cast<const uint32_t*>(b.base + (r * T + tq) * d + c0);
+            const float cf = b.base_coef[tq * kMsarStreams + r] * sc;
+            const float ox = (float)__builtin_bit_cast(f16_t, (uint16_t)(u & 0xffffu));
+            const float oy = (float)__builtin_bit_cast(f16_t, (uint16_t)(u >> 16));
+            z[q][r] = make_float2(cf * ox, cf * oy);
           }
         }
       }
@@ -178,6 +186,20 @@ __global__ __launch_bounds__(kMfB, 2) void k_msar_slice(MsarArgs a, MsarFastBufs
         if (p < 64 && t0 + p / 8 < t_end) b.part[((t0 + p / 8) * S + slice) * (8 * n) + i * 8 + (p & 7)] = tot;
       }
     };
+    if constexpr (PASS == 2) {
+      // The mixer weights of the chunk's tokens, from the slices' sums.
+      if (tid < kMfTC) {
+        const int64_t tq = t0 + tid < T ? t0 + tid : T - 1;
+        float e[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int s2 = 0; s2 < S; ++s2)
+#pragma unroll
+          for (int q = 0; q < 5; ++q) e[q] += b.part2[(tq * S + s2) * kMfPart2 + q];
+        const float inv = 1.0f / sqrtf(e[0] / (float)(kMsarStreams * d) + a.eps);
+#pragma unroll
+        for (int q = 0; q < kMsarStreams; ++q) beta_s[tid * kMsarStreams + q] = 1.0f / (1.0f + expf(-e[1 + q] * inv));
+      }
+      lds_barrier();
+    }
     // Ping-pong over pairs of sources: each buffer's loads are issued one
     // source ahead of its use.
     uint32_t ra[kMfWin], rb[kMfWin];
@@ -196,7 +218,8 @@ __global__ __launch_bounds__(kMfB, 2) void k_msar_slice(MsarArgs a, MsarFastBufs
 #pragma unroll
         for (int r = 0; r < kMsarStreams; ++r) {
           const float2 zr = z[q][r];
-          if (t0 + q < t_end) *reinterpret_cast<float2*>(b.zbuf + ((t0 + q) * kMsarStreams + r) * d + c0) = zr;
+          if (b.zbuf != nullptr && t0 + q < t_end)
+            *reinterpret_cast<float2*>(b.zbuf + ((t0 + q) * kMsarStreams + r) * d + c0) = zr;
           e[0] = fmaf(zr.x, zr.x, fmaf(zr.y, zr.y, e[0]));
           e[1] = fmaf(zr.x, pm[r][0].x, fmaf(zr.y, pm[r][1].x, e[1]));
           e[2] = fmaf(zr.x, pm[r][0].y, fmaf(zr.y, pm[r][1].y, e[2]));
@@ -211,6 +234,20 @@ __global__ __launch_bounds__(kMfB, 2) void k_msar_slice(MsarArgs a, MsarFastBufs
       const int p = tid;
       if (p < 64 && (p & 7) < 5 && t0 + p / 8 < t_end)
         b.part2[((t0 + p / 8) * S + slice) * kMfPart2 + (p & 7)] = tot;
+    }
+    if constexpr (PASS == 2) {
+      bf16_t* out = static_cast<bf16_t*>(a.out);
+#pragma unroll
+      for (int q = 0; q < kMfTC; ++q) {
+        float2 h = make_float2(0.f, 0.f);
+#pragma unroll
+        for (int r = 0; r < kMsarStreams; ++r) {
+          const float bq = beta_s[q * kMsarStreams + r];
+          h.x = fmaf(bq, z[q][r].x, h.x);
+          h.y = fmaf(bq, z[q][r].y, h.y);
+        }
+        if (t0 + q < t_end) *reinterpret_cast<uint32_t*>(out + (t0 + q) * d + c0) = pack_bf2(h.x, h.y);
+      }
     }
   }
 }
@@ -287,7 +324,8 @@ struct BmsarArgs {
   const float* conv;   // [24][d]
   const float* mix1;   // [4 d][4], sublayer 1's mixer
   float eps;
-  float* o_state;      // [SB-1][4][T][d] fp32
+  f16_t* o_state;      // [SB-1][4][T][d], fp16 scaled per token
+  float* o_scale;      // [T]: o_state * o_scale[t] is the state
   float* lse;          // [SB-1][4][T]
   float* part;         // [T][slices][N][4 + 4 SB]
   float* alpha;        // [T][SB][4][16]
@@ -314,6 +352,7 @@ __global__ __launch_bounds__(kMfB, 2) void k_bmsar_p1(BmsarArgs a) {
   constexpr int NV = PASS == 0 ? kBmTC * V : 64;
   __shared__ float red[2][4][256];
   __shared__ float alpha_s[PASS == 1 ? kBmTC * SB * kMsarStreams * kMfAlphaRow : 1];
+  __shared__ float iscale_s[kBmTC];
   const int tid = threadIdx.x;
   const int64_t d = a.d, T = a.T;
   const int n = (int)a.N;
@@ -357,6 +396,7 @@ __global__ __launch_bounds__(kMfB, 2) void k_bmsar_p1(BmsarArgs a) {
         alpha_s[e] = a.alpha[(tq < T ? tq : T - 1) * (SB * kMsarStreams * kMfAlphaRow) +
                              e % (SB * kMsarStreams * kMfAlphaRow)];
       }
+      if (tid < kBmTC) iscale_s[tid] = 1.0f / a.o_scale[t0 + tid < T ? t0 + tid : T - 1];
       lds_barrier();
     }
     auto load_rows = [&](int i, uint32_t (&raw)[kBmWin]) {
@@ -434,11 +474,17 @@ __global__ __launch_bounds__(kMfB, 2) void k_bmsar_p1(BmsarArgs a) {
 #pragma unroll
       for (int q = 0; q < kBmTC; ++q) {
         const bool ok = t0 + q < t_end;
+        const float isc = iscale_s[q];  // a power of two: exact
 #pragma unroll
         for (int j = 1; j < SB; ++j)
 #pragma unroll
-          for (int r = 0; r < kMsarStreams; ++r)
-            if (ok) *reinterpret_cast<float2*>(a.o_state + (((j - 1) * kMsarStreams + r) * T + t0 + q) * d + c0) = z[q][j][r];
+          for (int r = 0; r < kMsarStreams; ++r) {
+            typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+            const h2 hv = {(f16_t)(z[q][j][r].x * isc), (f16_t)(z[q][j][r].y * isc)};
+            if (ok)
+              *reinterpret_cast<uint32_t*>(a.o_state + (((j - 1) * kMsarStreams + r) * T + t0 + q) * d + c0) =
+                  __builtin_bit_cast(uint32_t, hv);
+          }
         float e[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int r = 0; r < kMsarStreams; ++r) {
@@ -489,6 +535,9 @@ __global__ __launch_bounds__(256) void k_bmsar_alpha(BmsarArgs a) {
     const float l = group_sum<16>(e);
     a.alpha[((t * SB + j) * kMsarStreams + r) * kMfAlphaRow + i] = e / l;
     if (j >= 1 && i == 0) a.lse[((j - 1) * kMsarStreams + r) * T + t] = m + logf(l);
+    // fp16 state scale: every |o^(r)| <= max_n sqrt(ss_n^(r)), a power of two.
+    const float mss = group_max<64>(valid ? ss : 0.f);
+    if (j == 0 && lane == 0) a.o_scale[t] = f16_state_scale(sqrtf(mss));
   }
 }
 
@@ -606,7 +655,8 @@ hipError_t launch_bmsar_phase1(const BmsarCall& c, hipStream_t st) {
   a.conv = c.conv;
   a.mix1 = c.mix1;
   a.eps = c.eps;
-  a.o_state = c.o_state;
+  a.o_state = static_cast<f16_t*>(c.o_state);
+  a.o_scale = c.o_scale;
   a.lse = c.lse;
   a.part = reinterpret_cast<float*>(p);
   p += align256((size_t)(c.T * S * c.N * V) * 4);
@@ -628,8 +678,7 @@ size_t bmsar_phase2_workspace_bytes(int64_t T, int64_t d) {
   if (T < 1 || T > ((int64_t)1 << 30) || d % kMfSlice != 0 || d > ((int64_t)1 << 20)) return 0;
   const int64_t S = d / kMfSlice;
   return align256((size_t)(T * S * 8) * 4) + align256((size_t)(T * kMsarStreams * kMfAlphaRow) * 4) +
-         align256((size_t)(T * kMsarStreams) * 4) + align256((size_t)(T * S * kMfPart2) * 4) +
-         align256((size_t)(T * kMsarStreams * d) * 4);
+         align256((size_t)(T * kMsarStreams) * 4) + align256((size_t)(T * S * kMfPart2) * 4);
 }
 
 hipError_t launch_bmsar_phase2(const Bmsar2Call& c, hipStream_t st) {
@@ -644,8 +693,9 @@ hipError_t launch_bmsar_phase2(const Bmsar2Call& c, hipStream_t st) {
   p += align256((size_t)(c.T * kMsarStreams) * 4);
   b.part2 = reinterpret_cast<float*>(p);
   p += align256((size_t)(c.T * S * kMfPart2) * 4);
-  b.zbuf = reinterpret_cast<float*>(p);
-  b.base = c.o_i;
+  b.zbuf = nullptr;  // the output pass recomputes the states instead
+  b.base = static_cast<const f16_t*>(c.o_i);
+  b.base_scale = c.o_scale;
   b.base_coef = coef;
   MsarArgs a{c.partial, 1, c.T, c.d, c.w_i, c.conv, c.mix_i, 1, c.eps, kBF16, c.h_i, c.ws, 0};
   const dim3 grid((unsigned)(c.d / kMfSlice), (unsigned)((c.T + kMfRange - 1) / kMfRange));
@@ -658,8 +708,7 @@ hipError_t launch_bmsar_phase2(const Bmsar2Call& c, hipStream_t st) {
   if (cblocks > 8 * (int64_t)num_cus()) cblocks = 8 * (int64_t)num_cus();
   hipLaunchKernelGGL(k_bmsar_p2_coef, dim3((unsigned)cblocks), dim3(256), 0, st, a, b0, c.lse_i, coef);
   hipLaunchKernelGGL(k_msar_slice<1>, grid, dim3(kMfB), 0, st, a, b);
-  int64_t oblocks = c.T < 4 * (int64_t)num_cus() ? c.T : 4 * (int64_t)num_cus();
-  hipLaunchKernelGGL(k_msar_out, dim3((unsigned)oblocks), dim3(256), 0, st, a, b);
+  hipLaunchKernelGGL(k_msar_slice<2>, grid, dim3(kMfB), 0, st, a, b);
   return hipGetLastError();
 }
 

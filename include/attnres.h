@@ -343,7 +343,10 @@ int attnres_msar_fwd(const void* src, int64_t n_src, int64_t T, int64_t d, const
  *  w        [S, 4, d] fp32;  conv [24, d] fp32 (as attnres_msar_fwd)
  *  mix1     [4 d, 4] fp32    sublayer 1's mixer
  *  h1       [T, d] bf16
- *  o_state  [S-1, 4, T, d] fp32;  lse [S-1, 4, T] fp32 (NULL allowed when S == 1)
+ *  o_state  [S-1, 4, T, d] fp16 and o_scale [T] fp32: the state is
+ *           o_state * o_scale[t], the scale a power of two that bounds every
+ *           value of the token (as the Phase-1 state of Block AttnRes)
+ *  lse      [S-1, 4, T] fp32 (o_state and lse may be NULL when S == 1)
  *  ws       device workspace of attnres_block_msar_phase1_workspace_size() bytes
  * Requires bf16, 1 <= N <= 12, 1 <= S <= 4, d a multiple of 512 (else
  * ATTNRES_ERR_UNSUPPORTED) and 16-byte-aligned pointers.
@@ -351,8 +354,8 @@ int attnres_msar_fwd(const void* src, int64_t n_src, int64_t T, int64_t d, const
 size_t attnres_block_msar_phase1_workspace_size(int64_t N, int64_t S, int64_t T, int64_t d);
 int attnres_block_msar_phase1(const void* reps, int64_t N, int64_t T, int64_t d, const float* w,
                               int64_t S, const float* conv, const float* mix1, float eps,
-                              int32_t dtype, void* h1, float* o_state, float* lse, void* ws,
-                              size_t ws_bytes, hipStream_t stream);
+                              int32_t dtype, void* h1, void* o_state, float* o_scale, float* lse,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Block MSAR Phase 2 for sublayer i >= 2: the partial's streams are scored
@@ -361,7 +364,8 @@ int attnres_block_msar_phase1(const void* reps, int64_t N, int64_t T, int64_t d,
  *   m = max(lse, s_p),  Z^(r) = (e^{lse-m} o^(r) + e^{s_p-m} p^(r)) / (e^{lse-m} + e^{s_p-m}),
  * then h_i = sum_r beta_r Z^(r) with beta = sigmoid(RMSNorm(Flatten(Z)) P_i).
  *
- *  o_i      [4, T, d] fp32 and lse_i [4, T] fp32: Phase 1's o_state[i-2], lse[i-2]
+ *  o_i      [4, T, d] fp16, o_scale [T], lse_i [4, T] fp32: Phase 1's
+ *           o_state[i-2], o_scale and lse[i-2]
  *  partial  [T, d] bf16 (the block's partial sum before sublayer i)
  *  w_i      [4, d];  conv [24, d];  mix_i [4 d, 4] (fp32)
  *  h_i      [T, d] bf16
@@ -369,10 +373,10 @@ int attnres_block_msar_phase1(const void* reps, int64_t N, int64_t T, int64_t d,
  * Same requirements as Phase 1.
  */
 size_t attnres_block_msar_phase2_workspace_size(int64_t T, int64_t d);
-int attnres_block_msar_phase2(const float* o_i, const float* lse_i, const void* partial, int64_t T,
-                              int64_t d, const float* w_i, const float* conv, const float* mix_i,
-                              float eps, int32_t dtype, void* h_i, void* ws, size_t ws_bytes,
-                              hipStream_t stream);
+int attnres_block_msar_phase2(const void* o_i, const float* o_scale, const float* lse_i,
+                              const void* partial, int64_t T, int64_t d, const float* w_i,
+                              const float* conv, const float* mix_i, float eps, int32_t dtype,
+                              void* h_i, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ABI version: (major << 16) | minor.  Major 2 added the Full-forward workspace;
  * minor 1 added the Full backward, minor 2 the fused Phase 2 update, minor 3 the

@@ -372,20 +372,23 @@ def test_msar_rejects_bad_arguments():
 def _rc_bm1(**kw):
     G = 1 << 30
     a = dict(reps=FAKE, N=8, T=100, d=512, w=FAKE + G, S=4, conv=FAKE + 2 * G, mix=FAKE + 3 * G, eps=1e-6,
-             dtype=BF16, h1=FAKE + 4 * G, o=FAKE + 5 * G, lse=FAKE + 6 * G, ws=FAKE + 7 * G, ws_bytes=1 << 30)
+             dtype=BF16, h1=FAKE + 4 * G, o=FAKE + 5 * G, sc=FAKE + 8 * G, lse=FAKE + 6 * G, ws=FAKE + 7 * G,
+             ws_bytes=1 << 30)
     a.update(kw)
     return binding.lib().attnres_block_msar_phase1(a["reps"], a["N"], a["T"], a["d"], a["w"], a["S"], a["conv"],
-                                                   a["mix"], a["eps"], a["dtype"], a["h1"], a["o"], a["lse"],
+                                                   a["mix"], a["eps"], a["dtype"], a["h1"], a["o"], a["sc"], a["lse"],
                                                    a["ws"], a["ws_bytes"], None)
 
 
 def _rc_bm2(**kw):
     G = 1 << 30
-    a = dict(o=FAKE, lse=FAKE + G, p=FAKE + 2 * G, T=100, d=512, w=FAKE + 3 * G, conv=FAKE + 4 * G,
-             mix=FAKE + 5 * G, eps=1e-6, dtype=BF16, h=FAKE + 6 * G, ws=FAKE + 7 * G, ws_bytes=1 << 30)
+    a = dict(o=FAKE, sc=FAKE + 8 * G, lse=FAKE + G, p=FAKE + 2 * G, T=100, d=512, w=FAKE + 3 * G,
+             conv=FAKE + 4 * G, mix=FAKE + 5 * G, eps=1e-6, dtype=BF16, h=FAKE + 6 * G, ws=FAKE + 7 * G,
+             ws_bytes=1 << 30)
     a.update(kw)
-    return binding.lib().attnres_block_msar_phase2(a["o"], a["lse"], a["p"], a["T"], a["d"], a["w"], a["conv"],
-                                                   a["mix"], a["eps"], a["dtype"], a["h"], a["ws"], a["ws_bytes"], None)
+    return binding.lib().attnres_block_msar_phase2(a["o"], a["sc"], a["lse"], a["p"], a["T"], a["d"], a["w"],
+                                                   a["conv"], a["mix"], a["eps"], a["dtype"], a["h"], a["ws"],
+                                                   a["ws_bytes"], None)
 
 
 @fake_ptrs
@@ -398,6 +401,8 @@ def test_block_msar_rejects_bad_arguments():
                     (dict(ws=FAKE + 5 * G), EINVAL)]:
         assert _rc_bm1(**c) == want, c
     assert _rc_bm1(S=1, o=None, lse=None, ws_bytes=16) == EWS     # S == 1 needs no state
+    assert _rc_bm1(sc=None) == EINVAL
+    assert _rc_bm2(sc=None) == EINVAL
     assert _rc_bm1(T=0, reps=None) == OK
     for c, want in [(dict(dtype=F32), EUNSUP), (dict(d=1000), EUNSUP), (dict(o=None), EINVAL),
                     (dict(p=None), EINVAL), (dict(h=None), EINVAL), (dict(ws_bytes=16), EWS),
