@@ -38,7 +38,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="block", choices=["block", "mhar", "full", "bwd", "full_bwd", "block_update",
+    p.add_argument("--workload", default="block", choices=["block", "mhar", "full", "bwd", "mhar_bwd", "full_bwd", "block_update",
                                                                 "decode", "msar", "block_msar"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads")
@@ -428,32 +428,33 @@ def bench_full(args, T=4096):
                 step_bytes=b, step_gbs=b * n / sec / 1e9)
 
 
-def bench_bwd(args, T=8192):
+def bench_bwd(args, T=8192, H=1):
     import torch
     import depth_wise_attention_amd as ar
     from workloads import synth
 
-    wl = synth.config_block_fwd_bwd(T=T)
+    wl = synth.config_block_fwd_bwd(T=T) if H == 1 else synth.config_mhar_fwd_bwd(T=T, H=H)
     reps, parts, dh = (to_dev(x, torch.bfloat16) for x in (wl.reps, wl.partials, wl.dh))
     w, g = to_dev(wl.w, torch.float32), to_dev(wl.gain, torch.float32)
     N, S, d = wl.N, wl.S, wl.d
     del wl
     h = torch.empty((S, T, d), dtype=torch.bfloat16, device="cuda")
-    ws_f = torch.empty(ar.mhar_fwd_workspace_size(N, S, T, d, 1), dtype=torch.uint8, device="cuda")
-    ws_b = torch.empty(ar.attnres_bwd_workspace_size(N, S, T, d, 1), dtype=torch.uint8, device="cuda")
+    ws_f = torch.empty(ar.mhar_fwd_workspace_size(N, S, T, d, H), dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(ar.attnres_bwd_workspace_size(N, S, T, d, H), dtype=torch.uint8, device="cuda")
     d_reps, d_parts = torch.empty_like(reps), torch.empty_like(parts)
     dw, dg = torch.empty_like(w), torch.empty_like(g)
 
     def step():
-        ar.mhar_fwd(reps, parts, w, g, 1e-6, 1, h=h, ws=ws_f)
-        ar.attnres_bwd(reps, parts, w, dh, g, 1e-6, 1, d_reps=d_reps, d_partials=d_parts, dw=dw, dgain=dg,
+        ar.mhar_fwd(reps, parts, w, g, 1e-6, H, h=h, ws=ws_f)
+        ar.attnres_bwd(reps, parts, w, dh, g, 1e-6, H, d_reps=d_reps, d_partials=d_parts, dw=dw, dgain=dg,
                        ws=ws_b)
 
     n = max(3, args.steps // 4)
     sec, wall = time_loop(step, n, 2)
-    fwd_b = block_bytes(T, d, N, S, 1)[2]
+    fwd_b = block_bytes(T, d, N, S, H)[2]
     b = fwd_b + bwd_bytes(T, d, N, S)
-    return dict(name=f"block_fwd_bwd_bf16_T{T}_d{d}_N{N}_S{S}", tokens_per_s=T * n / sec,
+    kind = "block" if H == 1 else f"mhar_H{H}"
+    return dict(name=f"{kind}_fwd_bwd_bf16_T{T}_d{d}_N{N}_S{S}", tokens_per_s=T * n / sec,
                 ms_per_step=sec / n * 1e3, step_bytes=b, step_gbs=b * n / sec / 1e9)
 
 
@@ -551,7 +552,7 @@ def main():
 
     if args.workload != "block":
         fn = {"mhar": lambda: bench_block(args, H=8, T=32768), "full": lambda: bench_full(args),
-              "bwd": lambda: bench_bwd(args), "full_bwd": lambda: bench_full_bwd(args),
+              "bwd": lambda: bench_bwd(args), "mhar_bwd": lambda: bench_bwd(args, H=8), "full_bwd": lambda: bench_full_bwd(args),
               "block_update": lambda: bench_update(args), "decode": lambda: bench_decode(args),
               "msar": lambda: bench_msar(args), "block_msar": lambda: bench_block_msar(args)}[args.workload]
         log(json.dumps(fn()))
@@ -566,7 +567,7 @@ def main():
     if not args.no_extra:
         torch.cuda.empty_cache()
         for fn in (lambda: bench_block(args, H=8, T=32768, with_events=True), lambda: bench_full(args),
-                   lambda: bench_bwd(args), lambda: bench_full_bwd(args), lambda: bench_update(args),
+                   lambda: bench_bwd(args), lambda: bench_bwd(args, H=8), lambda: bench_full_bwd(args), lambda: bench_update(args),
                    lambda: bench_decode(args), lambda: bench_msar(args), lambda: bench_block_msar(args)):
             r = fn()
             extra[r.pop("name")] = {k: v for k, v in r.items() if k not in ("T", "d", "N", "S", "H")}

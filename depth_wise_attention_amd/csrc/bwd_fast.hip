@@ -1,4 +1,4 @@
-// Specialised Block AttnRes backward for gfx950 (bf16 I/O, fp32 arithmetic, H = 1).
+// Specialised Block AttnRes backward for gfx950 (bf16 I/O, fp32 arithmetic).
 //
 // Gradient of L = sum_j <dh_j, h_j> for one block (the analytic form in
 // attnres.h).  Like Phase 1, a persistent workgroup of B = d/(8*CH) threads owns
@@ -14,6 +14,14 @@
 //   6. accumulates Z_j += sum_i c r_i v_i in registers across its tokens.
 // At the end each workgroup writes its Z slab; the fixed-order reduction
 // (k_bwd_reduce) turns the slabs into dw and dgain.
+//
+// Heads (MHAR, chatpaper.ai abstract): with one chunk of 8 channels per thread,
+// wave w owns channels [512 w, 512 w + 512), so a head of d/H channels is
+// exactly WH = (B/64)/H consecutive waves.  The sums of
+// squares are reduced over the whole workgroup (the RMS spans all of d), the
+// dot products only over the head's waves, and every lane table then holds the
+// wave's own head.  The one quantity mixing heads, sum over (j, h) of c s in
+// the normalisation path, takes a second LDS exchange per token.
 #include <math.h>
 
 #include <type_traits>
@@ -52,7 +60,7 @@ __device__ __forceinline__ uint4 pack8b(const float (&x)[8]) {
 template <int N>
 constexpr int pair_index(int j, int u) { return j == 0 ? u : N + (j - 1) * (N + 1) + u; }
 
-template <int N, int S, int CH, int B>
+template <int N, int S, int CH, int B, int HH>
 __global__ __launch_bounds__(B, ATTNRES_BWD_MINWAVES) void k_bwd_fast(BwdArgs a) {
   constexpr int NS = N + S - 1;                   // sources: N reps, then S-1 partials
   constexpr int NPAIR = N + (S - 1) * (N + 1);    // (destination, source) pairs
@@ -61,7 +69,10 @@ __global__ __launch_bounds__(B, ATTNRES_BWD_MINWAVES) void k_bwd_fast(BwdArgs a)
   constexpr int NP = next_pow2b(N + 1);           // lanes per destination group
   static_assert(S * NP <= 64, "pair table must fit one wave");
   constexpr int W = B / 64;
+  static_assert(HH == 1 || (CH == 1 && W % HH == 0), "a head must be whole waves");
+  constexpr int WH = W / HH;                      // waves per head
   __shared__ float red[2][W][NG * 64];
+  __shared__ float csx[2][HH > 1 ? HH : 1][64];   // per-head sum of c s, heads > 1 only
   __shared__ float4 qs[S * CH * B * 2];
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
@@ -170,10 +181,13 @@ __global__ __launch_bounds__(B, ATTNRES_BWD_MINWAVES) void k_bwd_fast(BwdArgs a)
     {
       float ss = 0.f, sd = 0.f, ad = 0.f;
       if (pvalid) {
-        for (int w2 = 0; w2 < W; ++w2) {
-          ss += red[buf][w2][psrc];
-          sd += red[buf][w2][NS + pidx];
-          ad += red[buf][w2][NS + NPAIR + pidx];
+        const int h0 = (wave / WH) * WH;                    // first wave of this head
+#pragma unroll
+        for (int w2 = 0; w2 < W; ++w2) ss += red[buf][w2][psrc];
+#pragma unroll
+        for (int w2 = 0; w2 < WH; ++w2) {
+          sd += red[buf][h0 + w2][NS + pidx];
+          ad += red[buf][h0 + w2][NS + NPAIR + pidx];
         }
       }
       const float r = 1.0f / sqrtf(ss / (float)d + a.eps);
@@ -193,7 +207,16 @@ __global__ __launch_bounds__(B, ATTNRES_BWD_MINWAVES) void k_bwd_fast(BwdArgs a)
       const float cs = pvalid ? c * s : 0.f;
       float csum = cs;
       csum = butterfly<NP, 64>(csum, SumOp());
-      coef = pvalid ? r * r * (pu < N ? csum : cs) / (float)d : 0.f;
+      float csh = pu < N ? csum : cs;
+      if constexpr (HH > 1) {
+        // Sum over heads, in head order, from the first wave of each head.
+        if (wave % WH == 0) csx[buf][wave / WH][lane] = csh;
+        __syncthreads();
+        csh = 0.f;
+#pragma unroll
+        for (int h = 0; h < HH; ++h) csh += csx[buf][h][lane];
+      }
+      coef = pvalid ? r * r * csh / (float)d : 0.f;
     }
 
     // ---- source gradients and Z, from registers
@@ -255,9 +278,9 @@ __global__ __launch_bounds__(B, ATTNRES_BWD_MINWAVES) void k_bwd_fast(BwdArgs a)
     }
 }
 
-template <int N, int S, int CH, int B>
+template <int N, int S, int CH, int B, int HH>
 hipError_t launch_bwd_nsb(const BwdArgs& a, int64_t* slots_used, hipStream_t st) {
-  auto kern = k_bwd_fast<N, S, CH, B>;
+  auto kern = k_bwd_fast<N, S, CH, B, HH>;
   int per_cu = 0;
   hipError_t e = blocks_per_cu(reinterpret_cast<const void*>(kern), B, &per_cu);
   if (e != hipSuccess) return e;
@@ -271,34 +294,43 @@ hipError_t launch_bwd_nsb(const BwdArgs& a, int64_t* slots_used, hipStream_t st)
 }
 
 // One chunk of 8 channels per thread (B = d/8 threads) keeps the kernel within
-// 2 waves per SIMD without spills; two chunks are used only where d/8 > 512.
-int bwd_ch(int64_t d) {
-  if (d % 8 == 0 && (d / 8 == 128 || d / 8 == 256 || d / 8 == 512)) return 1;
-  if (d % 16 == 0 && (d / 16 == 128 || d / 16 == 256)) return 2;
-  return 0;
-}
+// 2 waves per SIMD without spills.
+bool bwd_width_ok(int64_t d) { return d == 1024 || d == 2048 || d == 4096; }
 
 bool aligned16b(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace
 
 bool bwd_fast_ok(const BwdArgs& a) {
-  if (a.dtype != kBF16 || a.H != 1 || a.N != 8 || a.S != 4 || a.T < 1) return false;
-  if (bwd_ch(a.d) == 0 || a.slots < 1) return false;
+  if (a.dtype != kBF16 || a.N != 8 || a.S != 4 || a.T < 1) return false;
+  if (!bwd_width_ok(a.d) || a.slots < 1) return false;
+  // Heads of whole waves: H in {1, 2, 4, 8} dividing the d/512 waves.
+  const int64_t waves = a.d / 512;
+  if (a.H != 1 && a.H != 2 && a.H != 4 && a.H != 8) return false;
+  if (waves % a.H != 0) return false;
   return aligned16b(a.reps) && aligned16b(a.partials) && aligned16b(a.dh) && aligned16b(a.d_reps) &&
          aligned16b(a.d_partials) && aligned16b(a.zslots) && aligned16b(a.w) && aligned16b(a.gain);
 }
 
-hipError_t launch_bwd_fast(const BwdArgs& a, int64_t* slots_used, hipStream_t st) {
-  const int ch = bwd_ch(a.d);
-  const int64_t B = a.d / (8 * ch);
-  if (ch == 2) {
-    if (B == 128) return launch_bwd_nsb<8, 4, 2, 128>(a, slots_used, st);
-    return launch_bwd_nsb<8, 4, 2, 256>(a, slots_used, st);
+template <int B>
+hipError_t launch_bwd_b(const BwdArgs& a, int64_t* slots_used, hipStream_t st) {
+  switch (a.H) {
+    case 1: return launch_bwd_nsb<8, 4, 1, B, 1>(a, slots_used, st);
+    case 2: return launch_bwd_nsb<8, 4, 1, B, 2>(a, slots_used, st);
+    case 4:
+      if constexpr (B >= 256) return launch_bwd_nsb<8, 4, 1, B, 4>(a, slots_used, st);
+      break;
+    case 8:
+      if constexpr (B >= 512) return launch_bwd_nsb<8, 4, 1, B, 8>(a, slots_used, st);
+      break;
   }
-  if (B == 128) return launch_bwd_nsb<8, 4, 1, 128>(a, slots_used, st);
-  if (B == 256) return launch_bwd_nsb<8, 4, 1, 256>(a, slots_used, st);
-  return launch_bwd_nsb<8, 4, 1, 512>(a, slots_used, st);
+  return hipErrorInvalidValue;  // excluded by bwd_fast_ok
+}
+
+hipError_t launch_bwd_fast(const BwdArgs& a, int64_t* slots_used, hipStream_t st) {
+  if (a.d == 1024) return launch_bwd_b<128>(a, slots_used, st);
+  if (a.d == 2048) return launch_bwd_b<256>(a, slots_used, st);
+  return launch_bwd_b<512>(a, slots_used, st);
 }
 
 }  // namespace attnres

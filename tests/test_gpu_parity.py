@@ -345,6 +345,10 @@ def test_mhar_chunked_workspace_reuse():
     (37, 512, 8, 4, 1, "bf16", "per"),
     (21, 4096, 8, 4, 1, "bf16", "per"),
     (21, 4096, 8, 4, 8, "bf16", "shared"),
+    # heads of whole waves on the fast kernel: 512 channels per wave
+    (33, 4096, 8, 4, 2, "bf16", "per"),
+    (37, 2048, 8, 4, 4, "bf16", "per"),
+    (19, 1024, 8, 4, 2, "bf16", "none"),
     (10, 96, 3, 2, 3, "bf16", "per"),
     (6, 64, 5, 1, 1, "f32", "per"),
 ])
@@ -425,6 +429,35 @@ def test_bwd_config_sampled():
     # determinism
     again = ar.attnres_bwd(reps, parts, w, dh, g, wl.eps, 1)
     assert all(torch.equal(x, y) for x, y in zip(again, (d_reps, d_parts, dw, dg)))
+
+
+def test_mhar_bwd_config_sampled():
+    """MHAR Block backward bf16 at full size: T=8192, d=4096, H=8 heads of 512,
+    N=8, S=4.  Sampled tokens against the oracle; dw and dgain through the
+    closed form dw * w == dg * g and against the general kernel's sums."""
+    wl = synth.config_mhar_fwd_bwd()
+    say(f"mhar bwd config T={wl.T} H=8 (sampled tokens + properties)")
+    reps, parts, w, g = _block_on_gpu(wl, "bf16", wl.gain)
+    dh = dev(wl.dh, "bf16")
+    d_reps, d_parts, dw, dg = ar.attnres_bwd(reps, parts, w, dh, g, wl.eps, 8)
+    idx = synth.sample_tokens(wl.T, 48)
+    ref = orc.block_bwd(synth.take_tokens(wl.reps, idx), synth.take_tokens(wl.partials, idx), wl.w,
+                        wl.gain, wl.eps, 8, synth.take_tokens(wl.dh, idx))
+    check(host(d_reps[:, idx]), ref[0], "bf16", "d_reps (sampled)")
+    check(host(d_parts[:, idx]), ref[1], "bf16", "d_partials (sampled)")
+    lhs, rhs = host(dw) * wl.w, host(dg) * wl.gain
+    assert max_abs_over_rms(lhs, rhs) < 1e-5
+    again = ar.attnres_bwd(reps, parts, w, dh, g, wl.eps, 8)
+    assert all(torch.equal(x, y) for x, y in zip(again, (d_reps, d_parts, dw, dg)))
+    prev = ar.attnres_set_kernel_policy(1)
+    try:
+        gen = ar.attnres_bwd(reps, parts, w, dh, g, wl.eps, 8)
+    finally:
+        ar.attnres_set_kernel_policy(prev)
+    for name, x, y in (("dw", dw, gen[2]), ("dgain", dg, gen[3])):   # sums over all 8192 tokens
+        err = max_abs_over_rms(host(x), host(y))
+        print(f"  fast vs general {name}: {err:.2e}")
+        assert err < 1e-4, name
 
 
 # ----------------------------------------------------------------- Full backward

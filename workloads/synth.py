@@ -295,6 +295,12 @@ def config_block_fwd_bwd(seed: int = 0, T: int = 8192) -> Workload:
                           seed=seed, with_dh=True, name=f"block_bwd_bf16_T{T}_d4096_N8_S4")
 
 
+def config_mhar_fwd_bwd(seed: int = 0, T: int = 8192, H: int = 8) -> Workload:
+    """MHAR Block fwd+bwd, bf16: the MHAR workload (d=4096, H=8, N=8, S=4) at T=8192 with dh ~ N(0,1)."""
+    return block_workload(T=T, d=4096, N=8, S=4, H=H, rep_std_step=0.1, dtype="bf16",
+                          seed=seed, with_dh=True, name=f"mhar_bwd_bf16_T{T}_d4096_H{H}_N8_S4")
+
+
 def take_tokens(x: Optional[np.ndarray], idx: np.ndarray) -> Optional[np.ndarray]:
     """Select tokens (axis -2) of a [k, T, d] array; None passes through."""
     if x is None:
