@@ -307,6 +307,17 @@ __global__ __launch_bounds__(kBB, ATTNRES_FBWD_MINBLOCKS) void k_full_bwd_fast(F
       // One chunk ahead (this pass reads from cache); the next chunk loads into
       // the registers just staged.
       auto chunk2 = [&](int c, uint4 (&v)[4], uint4 (&g)[4]) {
+        const int tile32 = (ch_base + c * kChunk) / 32;
+        // Q^T operands of both halves, issued before the next chunk's loads: the
+        // vector-memory counter retires in order, so a load issued after the
+        // prefetch would make its first use wait for the prefetch as well.
+        uint4 qq[2][4];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const uint4* qtt = qt + (int64_t)(tile32 + half) * 4 * 64 + lane;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) qq[half][k] = qtt[64 * k];
+        }
         stage_chunk(vt, v, vmask);
         stage_chunk(dt, g, dmask);
         const int cn = min(c + 1, nch - 1) * kChunk;
@@ -317,7 +328,6 @@ __global__ __launch_bounds__(kBB, ATTNRES_FBWD_MINBLOCKS) void k_full_bwd_fast(F
 #pragma unroll
         for (int s = 0; s < 4; ++s) ov[s] = tile_operand(vt, s);
         wave_lds_sync();  // the source tile becomes the output tile below
-        const int tile32 = (ch_base + c * kChunk) / 32;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const uint4 od0 = tile_operand(dt, 2 * half), od1 = tile_operand(dt, 2 * half + 1);
@@ -331,13 +341,12 @@ __global__ __launch_bounds__(kBB, ATTNRES_FBWD_MINBLOCKS) void k_full_bwd_fast(F
           D3 = mfma(od1, ident_operand(1), D3);
           const uint4 td0 = pack8(D3[0], D3[1], D3[2], D3[3], D3[4], D3[5], D3[6], D3[7]);
           const uint4 td1 = pack8(D3[8], D3[9], D3[10], D3[11], D3[12], D3[13], D3[14], D3[15]);
-          const uint4* qtt = qt + (int64_t)(tile32 + half) * 4 * 64 + lane;
           f16acc D = {};
           D = mfma(td0, bl[0 * 64], D);   // alpha, b = 0, hi
           D = mfma(td0, bl[1 * 64], D);   //               lo
           D = mfma(td1, bl[2 * 64], D);   // alpha, b = 1, hi
           D = mfma(td1, bl[3 * 64], D);   //               lo
-          const uint4 q0h = qtt[0], q0l = qtt[64], q1h = qtt[128], q1l = qtt[192];
+          const uint4 q0h = qq[half][0], q0l = qq[half][1], q1h = qq[half][2], q1l = qq[half][3];
           D = mfma(q0h, bl[4 * 64], D);   // r c, b = 0: (q_hi + q_lo)(rc_hi + rc_lo) less lo * lo
           D = mfma(q0h, bl[5 * 64], D);
           D = mfma(q0l, bl[4 * 64], D);
@@ -409,34 +418,47 @@ __global__ __launch_bounds__(64) void k_full_bwd_z(FullBwdArgs a, const float* c
 #pragma unroll
   for (int u = 0; u < 4; ++u) vmask[u] = 8 * u + (lane >> 3) < n_src ? 0xFFFFFFFFu : 0u;
   f16acc Z0 = {}, Z1 = {};
-  for (int64_t t = grp; t < T; t += groups) {
+  // One token ahead: the next token's source rows and (r c) row are loaded
+  // while this token's products run (the last token reloads itself, so every
+  // iteration has the same loads outstanding).
+  auto load_token = [&](int64_t t, uint4 (&v)[4], float4 (&x)[4]) {
     const bf16_t* vrow[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int r = 8 * u + (lane >> 3);
       vrow[u] = src + ((int64_t)(r < n_src ? r : 0) * T + t) * d + ch0;
     }
-    uint4 v[4];
     load_chunk(vrow, 0, v);
     // A operands: lane (h, j = n) holds (r c)[j][transposed_row(b, h, e)].
     const float* cj = cws + t * (kTile * kTile) + n * kTile + 4 * h;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      x[2 * b] = *reinterpret_cast<const float4*>(cj + 16 * b);
+      x[2 * b + 1] = *reinterpret_cast<const float4*>(cj + 16 * b + 8);
+    }
+  };
+  uint4 v[4];
+  float4 x[4];
+  if (grp < T) load_token(grp, v, x);
+  for (int64_t t = grp; t < T; t += groups) {
     uint4 cA[2][2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const float4 x0 = *reinterpret_cast<const float4*>(cj + 16 * b);
-      const float4 x1 = *reinterpret_cast<const float4*>(cj + 16 * b + 8);
-      const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      const float xs[8] = {x[2 * b].x, x[2 * b].y, x[2 * b].z, x[2 * b].w,
+                           x[2 * b + 1].x, x[2 * b + 1].y, x[2 * b + 1].z, x[2 * b + 1].w};
       float hi[8], lo[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        hi[e] = bf2f(f2bf(x[e]));
-        lo[e] = x[e] - hi[e];
+        hi[e] = bf2f(f2bf(xs[e]));
+        lo[e] = xs[e] - hi[e];
       }
       cA[b][0] = pack8(hi[0], hi[1], hi[2], hi[3], hi[4], hi[5], hi[6], hi[7]);
       cA[b][1] = pack8(lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]);
     }
     wave_lds_sync();
     stage_chunk(tile, v, vmask);
+    const int64_t tn = t + groups < T ? t + groups : t;
+    load_token(tn, v, x);
     wave_lds_sync();
     uint4 op[4];
 #pragma unroll
