@@ -40,11 +40,6 @@ struct MsarFastBufs {
   float* alpha;   // [T][4][16]
   float* part2;   // [T][S][8]: [0] sum of squares of Z, [1 + q] projection q
   float* zbuf;    // [T][4][d]
-  // Optional state the weighted sum starts from (Block MSAR Phase 2):
-  // Z^(r) = base_coef[t][r] * base_scale[t] * base[r][t] + sum_i alpha x_i^(r).
-  const f16_t* base = nullptr;        // [4][T][d], fp16 scaled per token
-  const float* base_scale = nullptr;  // [T]
-  const float* base_coef = nullptr;   // [T][4]
 };
 
 // Sum of v[p] over the workgroup's 256 threads, for p < 64, into the
@@ -58,14 +53,12 @@ __device__ __forceinline__ float block_reduce64(const float (&v)[64], float (&re
   return (red[buf][0][p] + red[buf][1][p]) + (red[buf][2][p] + red[buf][3][p]);
 }
 
-// PASS 0: per-source statistics; PASS 1: retrieved states (stored to zbuf
-// unless it is null) and the mixer's sums; PASS 2: the retrieved states again,
-// weighted by the mixer into out (no zbuf round trip).
+// PASS 0: per-source statistics; PASS 1: retrieved states (stored to zbuf)
+// and the mixer's sums.
 template <int PASS>
 __global__ __launch_bounds__(kMfB, 2) void k_msar_slice(MsarArgs a, MsarFastBufs b) {
   __shared__ float red[2][4][64];
-  __shared__ float alpha_s[PASS >= 1 ? kMfTC * kMsarStreams * kMfAlphaRow : 1];
-  __shared__ float beta_s[PASS == 2 ? kMfTC * kMsarStreams : 1];
+  __shared__ float alpha_s[PASS == 1 ? kMfTC * kMsarStreams * kMfAlphaRow : 1];
   const int tid = threadIdx.x;
   const int64_t d = a.d, T = a.T;
   const int n = (int)a.n_src;
@@ -96,26 +89,11 @@ __global__ __launch_bounds__(kMfB, 2) void k_msar_slice(MsarArgs a, MsarFastBufs
   int buf = 0;
   for (int64_t t0 = t_begin; t0 < t_end; t0 += kMfTC) {
     float2 z[kMfTC][kMsarStreams];
-    if constexpr (PASS >= 1) {
+    if constexpr (PASS == 1) {
 #pragma unroll
       for (int q = 0; q < kMfTC; ++q)
 #pragma unroll
         for (int r = 0; r < kMsarStreams; ++r) z[q][r] = make_float2(0.f, 0.f);
-      if (b.base != nullptr) {
-#pragma unroll
-        for (int q = 0; q < kMfTC; ++q) {
-          const int64_t tq = t0 + q < T ? t0 + q : T - 1;
-          const float sc = b.base_scale[tq];
-#pragma unroll
-          for (int r = 0; r < kMsarStreams; ++r) {
-            const uint32_t u = *reinterpret_cast<const uint32_t*>(b.base + (r * T + tq) * d + c0);
-            const float cf = b.base_coef[tq * kMsarStreams + r] * sc;
-            const float ox = (float)__builtin_bit_cast(f16_t, (uint16_t)(u & 0xffffu));
-            const float oy = (float)__builtin_bit_cast(f16_t, (uint16_t)(u >> 16));
-            z[q][r] = make_float2(cf * ox, cf * oy);
-          }
-        }
-      }
       // The chunk's softmax weights, into LDS: per-source reads then go through
       // the LDS counter instead of queueing behind the prefetched rows.  The
       // barrier also orders the previous chunk's reads before these writes.
@@ -186,20 +164,6 @@ __global__ __launch_bounds__(kMfB, 2) void k_msar_slice(MsarArgs a, MsarFastBufs
         if (p < 64 && t0 + p / 8 < t_end) b.part[((t0 + p / 8) * S + slice) * (8 * n) + i * 8 + (p & 7)] = tot;
       }
     };
-    if constexpr (PASS == 2) {
-      // The mixer weights of the chunk's tokens, from the slices' sums.
-      if (tid < kMfTC) {
-        const int64_t tq = t0 + tid < T ? t0 + tid : T - 1;
-        float e[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int s2 = 0; s2 < S; ++s2)
-#pragma unroll
-          for (int q = 0; q < 5; ++q) e[q] += b.part2[(tq * S + s2) * kMfPart2 + q];
-        const float inv = 1.0f / sqrtf(e[0] / (float)(kMsarStreams * d) + a.eps);
-#pragma unroll
-        for (int q = 0; q < kMsarStreams; ++q) beta_s[tid * kMsarStreams + q] = 1.0f / (1.0f + expf(-e[1 + q] * inv));
-      }
-      lds_barrier();
-    }
     // Ping-pong over pairs of sources: each buffer's loads are issued one
     // source ahead of its use.
     uint32_t ra[kMfWin], rb[kMfWin];
@@ -218,7 +182,7 @@ __global__ __launch_bounds__(kMfB, 2) void k_msar_slice(MsarArgs a, MsarFastBufs
 #pragma unroll
         for (int r = 0; r < kMsarStreams; ++r) {
           const float2 zr = z[q][r];
-          if (b.zbuf != nullptr && t0 + q < t_end)
+          if (t0 + q < t_end)
             *reinterpret_cast<float2*>(b.zbuf + ((t0 + q) * kMsarStreams + r) * d + c0) = zr;
           e[0] = fmaf(zr.x, zr.x, fmaf(zr.y, zr.y, e[0]));
           e[1] = fmaf(zr.x, pm[r][0].x, fmaf(zr.y, pm[r][1].x, e[1]));
@@ -234,20 +198,6 @@ __global__ __launch_bounds__(kMfB, 2) void k_msar_slice(MsarArgs a, MsarFastBufs
       const int p = tid;
       if (p < 64 && (p & 7) < 5 && t0 + p / 8 < t_end)
         b.part2[((t0 + p / 8) * S + slice) * kMfPart2 + (p & 7)] = tot;
-    }
-    if constexpr (PASS == 2) {
-      bf16_t* out = static_cast<bf16_t*>(a.out);
-#pragma unroll
-      for (int q = 0; q < kMfTC; ++q) {
-        float2 h = make_float2(0.f, 0.f);
-#pragma unroll
-        for (int r = 0; r < kMsarStreams; ++r) {
-          const float bq = beta_s[q * kMsarStreams + r];
-          h.x = fmaf(bq, z[q][r].x, h.x);
-          h.y = fmaf(bq, z[q][r].y, h.y);
-        }
-        if (t0 + q < t_end) *reinterpret_cast<uint32_t*>(out + (t0 + q) * d + c0) = pack_bf2(h.x, h.y);
-      }
     }
   }
 }
@@ -541,11 +491,229 @@ __global__ __launch_bounds__(256) void k_bmsar_alpha(BmsarArgs a) {
   }
 }
 
-// Block MSAR Phase 2 merge coefficients: the partial is source 0 of a
-// one-source pass; base_coef = e^{lse-m}/(...), alpha[.][r][0] = e^{s_p-m}/(...).
-__global__ __launch_bounds__(256) void k_bmsar_p2_coef(MsarArgs a, MsarFastBufs b, const float* lse_i,
-                                                       float* coef) {
-  const int64_t T = a.T, d = a.d;
+// ------------------------------------------------------------ Block MSAR Phase 2
+// One source, the intra-block partial b, merged by online softmax into the
+// Phase-1 state of each stream ([MSAR] "How to use it"; the merge is Block
+// AttnRes's, per stream): Z^(r) = a_r o^(r) + b_r x^(r), with a_r, b_r from
+// the state's log-sum-exp and the partial's score.  Same slicing as the
+// other passes, but with one source each thread keeps a sliding window of the
+// partial's rows (t0-11 .. t0+TC-1 of its two channels) in registers across
+// its chunks and prefetches the next chunk's rows and state one chunk ahead:
+// no halo row is read twice, and every wait finds loads issued a chunk
+// earlier.  Per-token weights are read with uniform (scalar) loads.
+//   k_bmsar_p2<0>       the partial's per-stream sum of squares and query
+//                       product per token and slice                  -> part
+//   k_bmsar_p2_merge    per token: a_r * state scale, b_r            -> mw
+//   k_bmsar_p2<1>       Z^(r) per token, the sum of squares of Flatten(Z)
+//                       and its four projections by P, per slice     -> part2
+//   k_bmsar_p2_beta     per token: beta = sigmoid(RMSNorm(Flatten(Z)) P)
+//   k_bmsar_p2<2>       Z^(r) again and h = sum_r beta_r Z^(r)       -> out
+constexpr int kP2Range = 256;  // tokens per workgroup
+
+template <int PASS, int TC>
+__global__ __launch_bounds__(kMfB, 2) void k_bmsar_p2(const bf16_t* __restrict__ part,
+                                                      const f16_t* __restrict__ base,
+                                                      const float* __restrict__ conv,
+                                                      const float* __restrict__ w,
+                                                      const float* __restrict__ mix,
+                                                      const float* __restrict__ mw,
+                                                      const float* __restrict__ beta,
+                                                      float* __restrict__ sums, bf16_t* __restrict__ out,
+                                                      int64_t T, int64_t d) {
+  constexpr int WIN = TC + kMfHalo;
+  constexpr int NV = TC * 8;
+  __shared__ float red[2][4][256];
+  const int tid = threadIdx.x;
+  const int S = (int)(d / kMfSlice);
+  const int slice = blockIdx.x;
+  const int64_t c0 = (int64_t)slice * kMfSlice + 2 * tid;
+
+  float2 tap[kMsarTaps];
+#pragma unroll
+  for (int k = 0; k < kMsarTaps; ++k) tap[k] = *reinterpret_cast<const float2*>(conv + k * d + c0);
+  float2 wq[kMsarStreams];
+  float4 pm[kMsarStreams][2];
+#pragma unroll
+  for (int r = 0; r < kMsarStreams; ++r) {
+    if constexpr (PASS == 0) {
+      wq[r] = *reinterpret_cast<const float2*>(w + r * d + c0);
+    } else if constexpr (PASS == 1) {
+      pm[r][0] = *reinterpret_cast<const float4*>(mix + (r * d + c0) * kMsarStreams);
+      pm[r][1] = *reinterpret_cast<const float4*>(mix + (r * d + c0 + 1) * kMsarStreams);
+    }
+  }
+
+  const int64_t t_begin = (int64_t)blockIdx.y * kP2Range;
+  const int64_t t_end = t_begin + kP2Range < T ? t_begin + kP2Range : T;
+  const bf16_t* col = part + c0;
+  // Unconditional loads of clamped rows; rows outside [0, T) are zeroed when
+  // unpacked (before the first token: the causal zero; past the end: unused).
+  auto row_ld = [&](int64_t row) {
+    const int64_t rc = row < 0 ? 0 : (row >= T ? T - 1 : row);
+    return *reinterpret_cast<const uint32_t*>(col + rc * d);
+  };
+  auto unpack_row = [&](int64_t row, uint32_t u) {
+    u = (row >= 0 && row < T) ? u : 0u;
+    return make_float2(bf_lo(u), bf_hi(u));
+  };
+  auto base_ld = [&](int64_t t0, uint32_t (&bb)[TC][kMsarStreams]) {
+#pragma unroll
+    for (int q = 0; q < TC; ++q) {
+      const int64_t tq = t0 + q < T ? t0 + q : T - 1;
+#pragma unroll
+      for (int r = 0; r < kMsarStreams; ++r)
+        bb[q][r] = *reinterpret_cast<const uint32_t*>(base + (r * T + tq) * d + c0);
+    }
+  };
+
+  float2 win[WIN];
+  {
+    uint32_t raw[WIN];
+#pragma unroll
+    for (int h = 0; h < WIN; ++h) raw[h] = row_ld(t_begin - kMfHalo + h);
+#pragma unroll
+    for (int h = 0; h < WIN; ++h) win[h] = unpack_row(t_begin - kMfHalo + h, raw[h]);
+  }
+  uint32_t bcur[PASS >= 1 ? TC : 1][kMsarStreams], bnxt[PASS >= 1 ? TC : 1][kMsarStreams];
+  if constexpr (PASS >= 1) base_ld(t_begin, bcur);
+
+  // The previous chunk's results, stored at the start of the next chunk (see
+  // below): pass 2 keeps its packed outputs, passes 0 and 1 their sums.
+  uint32_t hprev[PASS == 2 ? TC : 1];
+  float sprev = 0.f;
+  int buf = 0;
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += TC) {
+    // One wait per chunk, for everything issued at the start of the previous
+    // one: this chunk's rows and state, and the chunk before's stores.  The
+    // vector-memory counter retires in order and counts stores, so stores
+    // left pending here would make any later wait also wait for the prefetch
+    // issued below; issuing them only now, together with the prefetch, keeps
+    // the next chunk's single wait just as far from its loads.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    if (t0 != t_begin) {
+      const int64_t tp = t0 - TC;
+      if constexpr (PASS == 2) {
+#pragma unroll
+        for (int q = 0; q < TC; ++q)
+          if (tp + q < t_end) *reinterpret_cast<uint32_t*>(out + (tp + q) * d + c0) = hprev[q];
+      } else {
+        const int p = tid;
+        if (p < NV && tp + p / 8 < t_end) sums[((tp + p / 8) * S + slice) * 8 + (p & 7)] = sprev;
+      }
+    }
+    // The next chunk's rows and state, in flight during this chunk.
+    uint32_t nxt[TC];
+#pragma unroll
+    for (int q = 0; q < TC; ++q) nxt[q] = row_ld(t0 + TC + q);
+    if constexpr (PASS >= 1) base_ld(t0 + TC, bnxt);
+    // Keep the prefetch here: without this the compiler may sink the loads to
+    // their first use in the next chunk, where their latency is exposed.
+    asm volatile("" ::: "memory");
+
+    float v[PASS <= 1 ? NV : 1];
+#pragma unroll
+    for (int q = 0; q < TC; ++q) {
+      // Token t0 + q is window row q + 11; lag k is row q + 11 - k.
+      float2 sv[kMsarStreams];
+      sv[0] = win[q + kMfHalo];
+#pragma unroll
+      for (int r = 1; r < kMsarStreams; ++r) {
+        const int K = msar_kernel(r), off = msar_offset(r);
+        float2 acc = make_float2(0.f, 0.f);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          acc.x = fmaf(tap[off + k].x, win[q + kMfHalo - k].x, acc.x);
+          acc.y = fmaf(tap[off + k].y, win[q + kMfHalo - k].y, acc.y);
+        }
+        sv[r] = acc;
+      }
+      if constexpr (PASS == 0) {
+#pragma unroll
+        for (int r = 0; r < kMsarStreams; ++r) {
+          v[q * 8 + r] = fmaf(sv[r].x, sv[r].x, sv[r].y * sv[r].y);
+          v[q * 8 + 4 + r] = fmaf(wq[r].x, sv[r].x, wq[r].y * sv[r].y);
+        }
+      } else {
+        const int64_t tq = t0 + q < T ? t0 + q : T - 1;
+        const float* mq = mw + tq * 8;
+        float2 z[kMsarStreams];
+#pragma unroll
+        for (int r = 0; r < kMsarStreams; ++r) {
+          const uint32_t u = bcur[q][r];
+          const float ox = (float)__builtin_bit_cast(f16_t, (uint16_t)(u & 0xffffu));
+          const float oy = (float)__builtin_bit_cast(f16_t, (uint16_t)(u >> 16));
+          const float ca = mq[r], cb = mq[4 + r];
+          z[r] = make_float2(fmaf(cb, sv[r].x, ca * ox), fmaf(cb, sv[r].y, ca * oy));
+        }
+        if constexpr (PASS == 1) {
+          float e[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int r = 0; r < kMsarStreams; ++r) {
+            const float2 zr = z[r];
+            e[0] = fmaf(zr.x, zr.x, fmaf(zr.y, zr.y, e[0]));
+            e[1] = fmaf(zr.x, pm[r][0].x, fmaf(zr.y, pm[r][1].x, e[1]));
+            e[2] = fmaf(zr.x, pm[r][0].y, fmaf(zr.y, pm[r][1].y, e[2]));
+            e[3] = fmaf(zr.x, pm[r][0].z, fmaf(zr.y, pm[r][1].z, e[3]));
+            e[4] = fmaf(zr.x, pm[r][0].w, fmaf(zr.y, pm[r][1].w, e[4]));
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[q * 8 + j] = j < 5 ? e[j] : 0.f;
+        } else {
+          const float* bq = beta + tq * kMsarStreams;
+          float2 h = make_float2(0.f, 0.f);
+#pragma unroll
+          for (int r = 0; r < kMsarStreams; ++r) {
+            h.x = fmaf(bq[r], z[r].x, h.x);
+            h.y = fmaf(bq[r], z[r].y, h.y);
+          }
+          hprev[q] = pack_bf2(h.x, h.y);
+        }
+      }
+    }
+    if constexpr (PASS <= 1) {
+      sprev = block_reduce_values<NV>(v, red, buf);
+      buf ^= 1;
+    }
+    // The prefetched values are consumed here, at the end of this chunk.
+#pragma unroll
+    for (int q = 0; q < TC; ++q) asm volatile("" ::"v"(nxt[q]));
+    if constexpr (PASS >= 1) {
+#pragma unroll
+      for (int q = 0; q < TC; ++q)
+#pragma unroll
+        for (int r = 0; r < kMsarStreams; ++r) asm volatile("" ::"v"(bnxt[q][r]));
+    }
+    // Slide the window by one chunk.
+#pragma unroll
+    for (int h = 0; h < kMfHalo; ++h) win[h] = win[h + TC];
+#pragma unroll
+    for (int q = 0; q < TC; ++q) win[kMfHalo + q] = unpack_row(t0 + TC + q, nxt[q]);
+    if constexpr (PASS >= 1) {
+#pragma unroll
+      for (int q = 0; q < TC; ++q)
+#pragma unroll
+        for (int r = 0; r < kMsarStreams; ++r) bcur[q][r] = bnxt[q][r];
+    }
+  }
+  // The last chunk's results.
+  if (t_begin < t_end) {
+    const int64_t tp = t_begin + (t_end - 1 - t_begin) / TC * TC;
+    if constexpr (PASS == 2) {
+#pragma unroll
+      for (int q = 0; q < TC; ++q)
+        if (tp + q < t_end) *reinterpret_cast<uint32_t*>(out + (tp + q) * d + c0) = hprev[q];
+    } else {
+      const int p = tid;
+      if (p < NV && tp + p / 8 < t_end) sums[((tp + p / 8) * S + slice) * 8 + (p & 7)] = sprev;
+    }
+  }
+}
+
+// Per (token, stream): the partial's score from the slices' sums and the
+// online-softmax merge weights a = e^{lse-m}/(...) (times the state's scale)
+// and b = e^{s_p-m}/(...).
+__global__ __launch_bounds__(256) void k_bmsar_p2_merge(const float* stats, const float* lse_i, const float* o_scale,
+                                                        float* mw, int64_t T, int64_t d, float eps) {
   const int S = (int)(d / kMfSlice);
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < T * kMsarStreams;
        e += (int64_t)gridDim.x * blockDim.x) {
@@ -553,17 +721,33 @@ __global__ __launch_bounds__(256) void k_bmsar_p2_coef(MsarArgs a, MsarFastBufs 
     const int r = (int)(e % kMsarStreams);
     float ss = 0.f, dot = 0.f;
     for (int s = 0; s < S; ++s) {
-      const float* p = b.part + (t * S + s) * 8;
+      const float* p = stats + (t * S + s) * 8;
       ss += p[r];
       dot += p[4 + r];
     }
-    const float sp = dot / sqrtf(ss / (float)d + a.eps);
+    const float sp = dot / sqrtf(ss / (float)d + eps);
     const float L = lse_i[r * T + t];
     const float m = fmaxf(L, sp);
     const float wa = expf(L - m), wb = expf(sp - m);
     const float inv = 1.0f / (wa + wb);
-    coef[t * kMsarStreams + r] = wa * inv;
-    b.alpha[t * (kMsarStreams * kMfAlphaRow) + r * kMfAlphaRow] = wb * inv;
+    mw[t * 8 + r] = (wa * inv) * o_scale[t];
+    mw[t * 8 + 4 + r] = wb * inv;
+  }
+}
+
+// Per token: beta_q = sigmoid((Flatten(Z) . P_q) / RMS(Flatten(Z))) from the
+// slices' sums, summed in slice order.
+__global__ __launch_bounds__(256) void k_bmsar_p2_beta(const float* sums, float* beta, int64_t T, int64_t d,
+                                                       float eps) {
+  const int S = (int)(d / kMfSlice);
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < T; t += (int64_t)gridDim.x * blockDim.x) {
+    float e[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+      for (int q = 0; q < 5; ++q) e[q] += sums[(t * S + s) * 8 + q];
+    const float inv = 1.0f / sqrtf(e[0] / (float)(kMsarStreams * d) + eps);
+#pragma unroll
+    for (int q = 0; q < kMsarStreams; ++q) beta[t * kMsarStreams + q] = 1.0f / (1.0f + expf(-e[1 + q] * inv));
   }
 }
 
@@ -677,38 +861,39 @@ hipError_t launch_bmsar_phase1(const BmsarCall& c, hipStream_t st) {
 size_t bmsar_phase2_workspace_bytes(int64_t T, int64_t d) {
   if (T < 1 || T > ((int64_t)1 << 30) || d % kMfSlice != 0 || d > ((int64_t)1 << 20)) return 0;
   const int64_t S = d / kMfSlice;
-  return align256((size_t)(T * S * 8) * 4) + align256((size_t)(T * kMsarStreams * kMfAlphaRow) * 4) +
-         align256((size_t)(T * kMsarStreams) * 4) + align256((size_t)(T * S * kMfPart2) * 4);
+  // stats [T][S][8], merge weights [T][8], mixer sums [T][S][8], beta [T][4]
+  return align256((size_t)(T * S * 8) * 4) + align256((size_t)(T * 8) * 4) + align256((size_t)(T * S * 8) * 4) +
+         align256((size_t)(T * kMsarStreams) * 4);
 }
 
 hipError_t launch_bmsar_phase2(const Bmsar2Call& c, hipStream_t st) {
-  const int64_t S = c.d / kMfSlice;
+  const int64_t S = c.d / kMfSlice, T = c.T, d = c.d;
   char* p = static_cast<char*>(c.ws);
-  MsarFastBufs b;
-  b.part = reinterpret_cast<float*>(p);
-  p += align256((size_t)(c.T * S * 8) * 4);
-  b.alpha = reinterpret_cast<float*>(p);
-  p += align256((size_t)(c.T * kMsarStreams * kMfAlphaRow) * 4);
-  float* coef = reinterpret_cast<float*>(p);
-  p += align256((size_t)(c.T * kMsarStreams) * 4);
-  b.part2 = reinterpret_cast<float*>(p);
-  p += align256((size_t)(c.T * S * kMfPart2) * 4);
-  b.zbuf = nullptr;  // the output pass recomputes the states instead
-  b.base = static_cast<const f16_t*>(c.o_i);
-  b.base_scale = c.o_scale;
-  b.base_coef = coef;
-  MsarArgs a{c.partial, 1, c.T, c.d, c.w_i, c.conv, c.mix_i, 1, c.eps, kBF16, c.h_i, c.ws, 0};
-  const dim3 grid((unsigned)(c.d / kMfSlice), (unsigned)((c.T + kMfRange - 1) / kMfRange));
-  MsarFastBufs b0 = b;
-  b0.base = nullptr;
-  b0.base_coef = nullptr;
-  hipLaunchKernelGGL(k_msar_slice<0>, grid, dim3(kMfB), 0, st, a, b0);
-  const int64_t ce = c.T * kMsarStreams;
-  int64_t cblocks = (ce + 255) / 256;
-  if (cblocks > 8 * (int64_t)num_cus()) cblocks = 8 * (int64_t)num_cus();
-  hipLaunchKernelGGL(k_bmsar_p2_coef, dim3((unsigned)cblocks), dim3(256), 0, st, a, b0, c.lse_i, coef);
-  hipLaunchKernelGGL(k_msar_slice<1>, grid, dim3(kMfB), 0, st, a, b);
-  hipLaunchKernelGGL(k_msar_slice<2>, grid, dim3(kMfB), 0, st, a, b);
+  float* stats = reinterpret_cast<float*>(p);
+  p += align256((size_t)(T * S * 8) * 4);
+  float* mw = reinterpret_cast<float*>(p);
+  p += align256((size_t)(T * 8) * 4);
+  float* sums = reinterpret_cast<float*>(p);
+  p += align256((size_t)(T * S * 8) * 4);
+  float* beta = reinterpret_cast<float*>(p);
+  const bf16_t* part = static_cast<const bf16_t*>(c.partial);
+  const f16_t* base = static_cast<const f16_t*>(c.o_i);
+  bf16_t* out = static_cast<bf16_t*>(c.h_i);
+  const dim3 grid((unsigned)S, (unsigned)((T + kP2Range - 1) / kP2Range));
+  const int64_t cap = 8 * (int64_t)num_cus();
+  int64_t mblocks = (T * kMsarStreams + 255) / 256, bblocks = (T + 255) / 256;
+  if (mblocks > cap) mblocks = cap;
+  if (bblocks > cap) bblocks = cap;
+  hipLaunchKernelGGL((k_bmsar_p2<0, 8>), grid, dim3(kMfB), 0, st, part, base, c.conv, c.w_i, c.mix_i,
+                     (const float*)nullptr, (const float*)nullptr, stats, (bf16_t*)nullptr, T, d);
+  hipLaunchKernelGGL(k_bmsar_p2_merge, dim3((unsigned)mblocks), dim3(256), 0, st, (const float*)stats, c.lse_i,
+                     c.o_scale, mw, T, d, c.eps);
+  hipLaunchKernelGGL((k_bmsar_p2<1, 4>), grid, dim3(kMfB), 0, st, part, base, c.conv, c.w_i, c.mix_i,
+                     (const float*)mw, (const float*)nullptr, sums, (bf16_t*)nullptr, T, d);
+  hipLaunchKernelGGL(k_bmsar_p2_beta, dim3((unsigned)bblocks), dim3(256), 0, st, (const float*)sums, beta, T, d,
+                     c.eps);
+  hipLaunchKernelGGL((k_bmsar_p2<2, 8>), grid, dim3(kMfB), 0, st, part, base, c.conv, c.w_i, c.mix_i,
+                     (const float*)mw, (const float*)beta, (float*)nullptr, out, T, d);
   return hipGetLastError();
 }
 
