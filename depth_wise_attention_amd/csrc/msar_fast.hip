@@ -303,6 +303,9 @@ __global__ __launch_bounds__(kMfB, 2) void k_bmsar_p1(BmsarArgs a) {
   __shared__ float red[2][4][256];
   __shared__ float alpha_s[PASS == 1 ? kBmTC * SB * kMsarStreams * kMfAlphaRow : 1];
   __shared__ float iscale_s[kBmTC];
+  // Pass 1: this thread's rows of sublayer 1's mixer P, in LDS rather than in
+  // registers (the weighted sums of SB sublayers fill the register file).
+  __shared__ float4 pm_s[PASS == 1 ? kMsarStreams * 2 * kMfB : 1];
   const int tid = threadIdx.x;
   const int64_t d = a.d, T = a.T;
   const int n = (int)a.N;
@@ -315,15 +318,15 @@ __global__ __launch_bounds__(kMfB, 2) void k_bmsar_p1(BmsarArgs a) {
 #pragma unroll
   for (int k = 0; k < kMsarTaps; ++k) tap[k] = *reinterpret_cast<const float2*>(a.conv + k * d + c0);
   float2 wq[PASS == 0 ? SB : 1][kMsarStreams];
-  float4 pm[kMsarStreams][2];
 #pragma unroll
   for (int r = 0; r < kMsarStreams; ++r) {
     if constexpr (PASS == 0) {
 #pragma unroll
       for (int i = 0; i < SB; ++i) wq[i][r] = *reinterpret_cast<const float2*>(a.w + (i * kMsarStreams + r) * d + c0);
     } else {
-      pm[r][0] = *reinterpret_cast<const float4*>(a.mix1 + (r * d + c0) * kMsarStreams);
-      pm[r][1] = *reinterpret_cast<const float4*>(a.mix1 + (r * d + c0 + 1) * kMsarStreams);
+      // Read back only by this thread: no barrier needed.
+      pm_s[(r * 2 + 0) * kMfB + tid] = *reinterpret_cast<const float4*>(a.mix1 + (r * d + c0) * kMsarStreams);
+      pm_s[(r * 2 + 1) * kMfB + tid] = *reinterpret_cast<const float4*>(a.mix1 + (r * d + c0 + 1) * kMsarStreams);
     }
   }
 
@@ -439,12 +442,13 @@ __global__ __launch_bounds__(kMfB, 2) void k_bmsar_p1(BmsarArgs a) {
 #pragma unroll
         for (int r = 0; r < kMsarStreams; ++r) {
           const float2 zr = z[q][0][r];
+          const float4 pm0 = pm_s[(r * 2 + 0) * kMfB + tid], pm1 = pm_s[(r * 2 + 1) * kMfB + tid];
           if (ok) *reinterpret_cast<float2*>(a.zbuf + ((t0 + q) * kMsarStreams + r) * d + c0) = zr;
           e[0] = fmaf(zr.x, zr.x, fmaf(zr.y, zr.y, e[0]));
-          e[1] = fmaf(zr.x, pm[r][0].x, fmaf(zr.y, pm[r][1].x, e[1]));
-          e[2] = fmaf(zr.x, pm[r][0].y, fmaf(zr.y, pm[r][1].y, e[2]));
-          e[3] = fmaf(zr.x, pm[r][0].z, fmaf(zr.y, pm[r][1].z, e[3]));
-          e[4] = fmaf(zr.x, pm[r][0].w, fmaf(zr.y, pm[r][1].w, e[4]));
+          e[1] = fmaf(zr.x, pm0.x, fmaf(zr.y, pm1.x, e[1]));
+          e[2] = fmaf(zr.x, pm0.y, fmaf(zr.y, pm1.y, e[2]));
+          e[3] = fmaf(zr.x, pm0.z, fmaf(zr.y, pm1.z, e[3]));
+          e[4] = fmaf(zr.x, pm0.w, fmaf(zr.y, pm1.w, e[4]));
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[q * 8 + j] = j < 5 ? e[j] : 0.f;
