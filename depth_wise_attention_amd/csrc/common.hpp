@@ -101,6 +101,10 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Compiler barrier: keeps the memory operations before it (a prefetch) where
+// they are instead of letting the compiler sink them towards their first use.
+__device__ __forceinline__ void keep_memory_order() { asm volatile("" ::: "memory"); }
+
 // Orders this wave's LDS writes before its later LDS reads by other lanes.
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

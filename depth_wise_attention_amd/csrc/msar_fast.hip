@@ -503,8 +503,8 @@ __global__ __launch_bounds__(256) void k_bmsar_alpha(BmsarArgs a) {
 // other passes, but with one source each thread keeps a sliding window of the
 // partial's rows (t0-11 .. t0+TC-1 of its two channels) in registers across
 // its chunks and prefetches the next chunk's rows and state one chunk ahead:
-// no halo row is read twice, and every wait finds loads issued a chunk
-// earlier.  Per-token weights are read with uniform (scalar) loads.
+// no halo row is read twice, and each chunk's loads have the previous chunk's
+// work to arrive.  Per-token weights are read with uniform (scalar) loads.
 //   k_bmsar_p2<0>       the partial's per-stream sum of squares and query
 //                       product per token and slice                  -> part
 //   k_bmsar_p2_merge    per token: a_r * state scale, b_r            -> mw
@@ -581,30 +581,8 @@ __global__ __launch_bounds__(kMfB, 2) void k_bmsar_p2(const bf16_t* __restrict__
   uint32_t bcur[PASS >= 1 ? TC : 1][kMsarStreams], bnxt[PASS >= 1 ? TC : 1][kMsarStreams];
   if constexpr (PASS >= 1) base_ld(t_begin, bcur);
 
-  // The previous chunk's results, stored at the start of the next chunk (see
-  // below): pass 2 keeps its packed outputs, passes 0 and 1 their sums.
-  uint32_t hprev[PASS == 2 ? TC : 1];
-  float sprev = 0.f;
   int buf = 0;
   for (int64_t t0 = t_begin; t0 < t_end; t0 += TC) {
-    // One wait per chunk, for everything issued at the start of the previous
-    // one: this chunk's rows and state, and the chunk before's stores.  The
-    // vector-memory counter retires in order and counts stores, so stores
-    // left pending here would make any later wait also wait for the prefetch
-    // issued below; issuing them only now, together with the prefetch, keeps
-    // the next chunk's single wait just as far from its loads.
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    if (t0 != t_begin) {
-      const int64_t tp = t0 - TC;
-      if constexpr (PASS == 2) {
-#pragma unroll
-        for (int q = 0; q < TC; ++q)
-          if (tp + q < t_end) *reinterpret_cast<uint32_t*>(out + (tp + q) * d + c0) = hprev[q];
-      } else {
-        const int p = tid;
-        if (p < NV && tp + p / 8 < t_end) sums[((tp + p / 8) * S + slice) * 8 + (p & 7)] = sprev;
-      }
-    }
     // The next chunk's rows and state, in flight during this chunk.
     uint32_t nxt[TC];
 #pragma unroll
@@ -612,7 +590,7 @@ __global__ __launch_bounds__(kMfB, 2) void k_bmsar_p2(const bf16_t* __restrict__
     if constexpr (PASS >= 1) base_ld(t0 + TC, bnxt);
     // Keep the prefetch here: without this the compiler may sink the loads to
     // their first use in the next chunk, where their latency is exposed.
-    asm volatile("" ::: "memory");
+    keep_memory_order();
 
     float v[PASS <= 1 ? NV : 1];
 #pragma unroll
@@ -670,13 +648,15 @@ __global__ __launch_bounds__(kMfB, 2) void k_bmsar_p2(const bf16_t* __restrict__
             h.x = fmaf(bq[r], z[r].x, h.x);
             h.y = fmaf(bq[r], z[r].y, h.y);
           }
-          hprev[q] = pack_bf2(h.x, h.y);
+          if (t0 + q < t_end) *reinterpret_cast<uint32_t*>(out + (t0 + q) * d + c0) = pack_bf2(h.x, h.y);
         }
       }
     }
     if constexpr (PASS <= 1) {
-      sprev = block_reduce_values<NV>(v, red, buf);
+      const float tot = block_reduce_values<NV>(v, red, buf);
       buf ^= 1;
+      const int p = tid;
+      if (p < NV && t0 + p / 8 < t_end) sums[((t0 + p / 8) * S + slice) * 8 + (p & 7)] = tot;
     }
     // The prefetched values are consumed here, at the end of this chunk.
 #pragma unroll
@@ -697,18 +677,6 @@ __global__ __launch_bounds__(kMfB, 2) void k_bmsar_p2(const bf16_t* __restrict__
       for (int q = 0; q < TC; ++q)
 #pragma unroll
         for (int r = 0; r < kMsarStreams; ++r) bcur[q][r] = bnxt[q][r];
-    }
-  }
-  // The last chunk's results.
-  if (t_begin < t_end) {
-    const int64_t tp = t_begin + (t_end - 1 - t_begin) / TC * TC;
-    if constexpr (PASS == 2) {
-#pragma unroll
-      for (int q = 0; q < TC; ++q)
-        if (tp + q < t_end) *reinterpret_cast<uint32_t*>(out + (tp + q) * d + c0) = hprev[q];
-    } else {
-      const int p = tid;
-      if (p < NV && tp + p / 8 < t_end) sums[((tp + p / 8) * S + slice) * 8 + (p & 7)] = sprev;
     }
   }
 }
