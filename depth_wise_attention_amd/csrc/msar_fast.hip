@@ -296,10 +296,28 @@ __device__ __forceinline__ float block_reduce_values(const float (&v)[NV], float
   return (red[buf][0][tid] + red[buf][1][tid]) + (red[buf][2][tid] + red[buf][3][tid]);
 }
 
+// Workgroup sums of ND query products and 16 sums of squares per thread, one
+// barrier: thread p < ND returns product p, thread R + s (R = ND rounded up to
+// 64, s < 16) sum of squares s; other threads return garbage.
+template <int ND>
+__device__ __forceinline__ float block_reduce_stats(const float (&dv)[ND], const float (&sq)[16],
+                                                    float (&red)[2][4][256], int buf) {
+  constexpr int NG = (ND + 63) / 64;
+  static_assert(NG * 64 + 16 <= 256, "reduction table");
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  float td[NG];
+  wave_reduce_values<ND>(dv, td);
+  const float ts = transpose_reduce16(sq);  // lane L: sum of squares L >> 2
+#pragma unroll
+  for (int g = 0; g < NG; ++g) red[buf][wave][g * 64 + lane] = td[g];
+  if ((lane & 3) == 0) red[buf][wave][NG * 64 + (lane >> 2)] = ts;
+  lds_barrier();
+  return (red[buf][0][tid] + red[buf][1][tid]) + (red[buf][2][tid] + red[buf][3][tid]);
+}
+
 template <int SB, int PASS>
 __global__ __launch_bounds__(kMfB, 2) void k_bmsar_p1(BmsarArgs a) {
   constexpr int V = 4 + 4 * SB;          // per rep and token: 4 sums of squares, 4 SB query products
-  constexpr int NV = PASS == 0 ? kBmTC * V : 64;
   __shared__ float red[2][4][256];
   __shared__ float alpha_s[PASS == 1 ? kBmTC * SB * kMsarStreams * kMfAlphaRow : 1];
   __shared__ float iscale_s[kBmTC];
@@ -369,7 +387,9 @@ __global__ __launch_bounds__(kMfB, 2) void k_bmsar_p1(BmsarArgs a) {
         const uint32_t u = (row >= 0 && row < T) ? raw[h] : 0u;
         x[h] = make_float2(bf_lo(u), bf_hi(u));
       }
-      float v[PASS == 0 ? NV : 1];
+      // Pass 0: the chunk's query products [token][sublayer][stream] and sums
+      // of squares [token][stream], reduced separately (no padded group).
+      float dv[PASS == 0 ? kBmTC * 4 * SB : 1], sq[PASS == 0 ? kBmTC * kMsarStreams : 1];
 #pragma unroll
       for (int q = 0; q < kBmTC; ++q) {
         float2 sv[kMsarStreams];
@@ -388,10 +408,10 @@ __global__ __launch_bounds__(kMfB, 2) void k_bmsar_p1(BmsarArgs a) {
         if constexpr (PASS == 0) {
 #pragma unroll
           for (int r = 0; r < kMsarStreams; ++r) {
-            v[q * V + r] = fmaf(sv[r].x, sv[r].x, sv[r].y * sv[r].y);
+            sq[q * kMsarStreams + r] = fmaf(sv[r].x, sv[r].x, sv[r].y * sv[r].y);
 #pragma unroll
             for (int j = 0; j < SB; ++j)
-              v[q * V + 4 + j * kMsarStreams + r] = fmaf(wq[j][r].x, sv[r].x, wq[j][r].y * sv[r].y);
+              dv[(q * SB + j) * kMsarStreams + r] = fmaf(wq[j][r].x, sv[r].x, wq[j][r].y * sv[r].y);
           }
         } else {
 #pragma unroll
@@ -405,11 +425,19 @@ __global__ __launch_bounds__(kMfB, 2) void k_bmsar_p1(BmsarArgs a) {
         }
       }
       if constexpr (PASS == 0) {
-        const float tot = block_reduce_values<NV>(v, red, buf);
+        constexpr int ND = kBmTC * 4 * SB, DROWS = (ND + 63) / 64 * 64;
+        const float tot = block_reduce_stats<ND>(dv, sq, red, buf);
         buf ^= 1;
         const int p = tid;
-        if (p < NV && t0 + p / V < t_end)
-          a.part[(((t0 + p / V) * S + slice) * n + i) * V + p % V] = tot;
+        int q = -1, k = 0;
+        if (p < ND) {
+          q = p / (4 * SB);
+          k = 4 + p % (4 * SB);
+        } else if (p >= DROWS && p < DROWS + kBmTC * kMsarStreams) {
+          q = (p - DROWS) / kMsarStreams;
+          k = (p - DROWS) % kMsarStreams;
+        }
+        if (q >= 0 && t0 + q < t_end) a.part[(((t0 + q) * S + slice) * n + i) * V + k] = tot;
       }
     };
     uint32_t ra[kBmWin], rb[kBmWin];

@@ -129,6 +129,33 @@ __device__ __forceinline__ float transpose_reduce64(const float (&v)[64]) {
   return r;
 }
 
+// Transpose-reduce of 16 values per lane: on return, lane L holds the sum over
+// all 64 lanes of value index L >> 2.  Lane bits 5, 4, 3 and 2 select index
+// bits 3, 2, 1 and 0 in four halving stages; the last two lane bits are
+// summed out.
+__device__ __forceinline__ float transpose_reduce16(const float (&v)[16]) {
+  const int lane = lane_id();
+  float a[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) a[m] = swap32_add(v[m], v[m + 8]);    // lane bit 5 -> index bit 3
+  float b[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) b[m] = swap16_add(a[m], a[m + 4]);    // lane bit 4 -> index bit 2
+  float c[2];
+  const bool hi8 = (lane & 8) != 0;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {                                      // lane bit 3 -> index bit 1
+    const float send = hi8 ? b[m] : b[m + 2];
+    const float keep = hi8 ? b[m + 2] : b[m];
+    c[m] = keep + dpp_move<dpp::kRor8>(0.f, send);
+  }
+  const bool hi4 = (lane & 4) != 0;                                  // lane bit 2 -> index bit 0
+  float e = (hi4 ? c[1] : c[0]) + xor4(hi4 ? c[0] : c[1]);
+  e += dpp_move<dpp::kXor1>(0.f, e);
+  e += dpp_move<dpp::kXor2>(0.f, e);
+  return e;
+}
+
 // Reduce P values per lane over the wave.  out[g] in lane L is the total of
 // value 64*g + L (zero for indices >= P).
 template <int P>
