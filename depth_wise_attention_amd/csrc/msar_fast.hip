@@ -58,7 +58,7 @@ __device__ __forceinline__ float block_reduce64(const float (&v)[64], float (&re
 template <int PASS>
 __global__ __launch_bounds__(kMfB, 2) void k_msar_slice(MsarArgs a, MsarFastBufs b) {
   __shared__ float red[2][4][64];
-  __shared__ float alpha_s[PASS == 1 ? kMfTC * kMsarStreams * kMfAlphaRow : 1];
+  __shared__ __attribute__((aligned(16))) float alpha_s[PASS == 1 ? kMfTC * kMsarStreams * kMfAlphaRow : 4];
   const int tid = threadIdx.x;
   const int64_t d = a.d, T = a.T;
   const int n = (int)a.n_src;
@@ -98,9 +98,13 @@ __global__ __launch_bounds__(kMfB, 2) void k_msar_slice(MsarArgs a, MsarFastBufs
       // the LDS counter instead of queueing behind the prefetched rows.  The
       // barrier also orders the previous chunk's reads before these writes.
       lds_barrier();
+      // Stored [token][source][stream]: one 16-byte LDS read per (token, source).
       for (int e = tid; e < kMfTC * kMsarStreams * kMfAlphaRow; e += kMfB) {
-        const int64_t tq = t0 + e / (kMsarStreams * kMfAlphaRow);
-        alpha_s[e] = b.alpha[(tq < T ? tq : T - 1) * (kMsarStreams * kMfAlphaRow) + e % (kMsarStreams * kMfAlphaRow)];
+        const int q = e / (kMsarStreams * kMfAlphaRow), rem = e % (kMsarStreams * kMfAlphaRow);
+        const int r = rem / kMfAlphaRow, i = rem % kMfAlphaRow;
+        const int64_t tq = t0 + q;
+        alpha_s[(q * kMfAlphaRow + i) * kMsarStreams + r] =
+            b.alpha[(tq < T ? tq : T - 1) * (kMsarStreams * kMfAlphaRow) + rem];
       }
       lds_barrier();
     }
@@ -149,11 +153,12 @@ __global__ __launch_bounds__(kMfB, 2) void k_msar_slice(MsarArgs a, MsarFastBufs
             v[q * 8 + 4 + r] = fmaf(wq[r].x, sv[r].x, wq[r].y * sv[r].y);
           }
         } else {
+          const float4 wv = *reinterpret_cast<const float4*>(&alpha_s[(q * kMfAlphaRow + i) * kMsarStreams]);
+          const float wr[kMsarStreams] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
           for (int r = 0; r < kMsarStreams; ++r) {
-            const float w_ri = alpha_s[(q * kMsarStreams + r) * kMfAlphaRow + i];
-            z[q][r].x = fmaf(w_ri, sv[r].x, z[q][r].x);
-            z[q][r].y = fmaf(w_ri, sv[r].y, z[q][r].y);
+            z[q][r].x = fmaf(wr[r], sv[r].x, z[q][r].x);
+            z[q][r].y = fmaf(wr[r], sv[r].y, z[q][r].y);
           }
         }
       }
@@ -167,12 +172,16 @@ __global__ __launch_bounds__(kMfB, 2) void k_msar_slice(MsarArgs a, MsarFastBufs
     // Ping-pong over pairs of sources: each buffer's loads are issued one
     // source ahead of its use.
     uint32_t ra[kMfWin], rb[kMfWin];
+    // One source per iteration: the next source's rows load into rb while
+    // this one computes, then move to ra.  (A two-buffer ping-pong inlines the
+    // source twice, and the weighted sums then change registers between the
+    // two copies: more moves than the row copy.)
     load_rows(0, ra);
-    for (int i = 0; i < n; i += 2) {
+    for (int i = 0; i < n; ++i) {
       load_rows(i + 1, rb);
       source(i, ra);
-      load_rows(i + 2, ra);
-      if (i + 1 < n) source(i + 1, rb);
+#pragma unroll
+      for (int h = 0; h < kMfWin; ++h) ra[h] = rb[h];
     }
     if constexpr (PASS == 1) {
       float v[64];
@@ -441,12 +450,16 @@ __global__ __launch_bounds__(kMfB, 2) void k_bmsar_p1(BmsarArgs a) {
       }
     };
     uint32_t ra[kBmWin], rb[kBmWin];
+    // One source per iteration: the next source's rows load into rb while
+    // this one computes, then move to ra.  (A two-buffer ping-pong inlines the
+    // source twice, and the weighted sums then change registers between the
+    // two copies: more moves than the row copy.)
     load_rows(0, ra);
-    for (int i = 0; i < n; i += 2) {
+    for (int i = 0; i < n; ++i) {
       load_rows(i + 1, rb);
       source(i, ra);
-      load_rows(i + 2, ra);
-      if (i + 1 < n) source(i + 1, rb);
+#pragma unroll
+      for (int h = 0; h < kBmWin; ++h) ra[h] = rb[h];
     }
     if constexpr (PASS == 1) {
       // Sublayers 2..SB: the per-stream states; sublayer 1: its retrieved
