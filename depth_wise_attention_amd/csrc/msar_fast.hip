@@ -9,10 +9,11 @@
 // two channels in registers, unpacked once, and the 24 taps of its channels:
 //   k_msar_slice<0>  per token and slice: each source's per-stream sum of
 //                    squares and query product (8 values per source) -> part
-//   k_msar_alpha<N>  per token: sum the slices, scores, four depth softmaxes -> alpha
+//   k_msar_alpha<N>  per token: sum the slices, scores, four depth softmaxes,
+//                    and the power-of-two scale of the stored Z      -> alpha, zscale
 //   k_msar_slice<1>  per token and slice: Z^(r) for the slice's channels
-//                    (stored once, fp32), the sum of squares of Flatten(Z)
-//                    and its four projections by P                   -> zbuf, part2
+//                    (stored once, fp16 scaled per token), the sum of squares
+//                    of Flatten(Z) and its four projections by P     -> zbuf, part2
 //   k_msar_out       per token: sum the slices, beta = sigmoid(...), and
 //                    h = sum_r beta_r Z^(r)                          -> out
 // The streams themselves are never stored.
@@ -39,7 +40,14 @@ struct MsarFastBufs {
   float* part;    // [T][S][8 n]: per source i, [i*8 + r] sum of squares, [i*8 + 4 + r] query product
   float* alpha;   // [T][4][16]
   float* part2;   // [T][S][8]: [0] sum of squares of Z, [1 + q] projection q
-  float* zbuf;    // [T][4][d]
+  // Z^(r) in fp16, divided per token by zscale[t], a power of two that maps a
+  // bound on every |Z| (the largest stream norm over the sources: Z is a
+  // convex combination of the streams) to [16384, 32768).  The Block MSAR
+  // Phase 1 keeps its sublayer-1 states in fp32 instead (zbuf32, no scale):
+  // the conversion in its weighting pass costs registers it does not have.
+  f16_t* zbuf;      // [T][4][d]
+  float* zscale;    // [T]
+  float* zbuf32;    // [T][4][d]
 };
 
 // Sum of v[p] over the workgroup's 256 threads, for p < 64, into the
@@ -59,6 +67,7 @@ template <int PASS>
 __global__ __launch_bounds__(kMfB, 2) void k_msar_slice(MsarArgs a, MsarFastBufs b) {
   __shared__ float red[2][4][64];
   __shared__ __attribute__((aligned(16))) float alpha_s[PASS == 1 ? kMfTC * kMsarStreams * kMfAlphaRow : 4];
+  __shared__ float zis_s[kMfTC];
   const int tid = threadIdx.x;
   const int64_t d = a.d, T = a.T;
   const int n = (int)a.n_src;
@@ -106,6 +115,7 @@ __global__ __launch_bounds__(kMfB, 2) void k_msar_slice(MsarArgs a, MsarFastBufs
         alpha_s[(q * kMfAlphaRow + i) * kMsarStreams + r] =
             b.alpha[(tq < T ? tq : T - 1) * (kMsarStreams * kMfAlphaRow) + rem];
       }
+      if (tid < kMfTC) zis_s[tid] = 1.0f / b.zscale[t0 + tid < T ? t0 + tid : T - 1];
       lds_barrier();
     }
     // Rows t0-11 .. t0+7 of source i; rows outside [0, T) read as zero (before
@@ -191,8 +201,13 @@ __global__ __launch_bounds__(kMfB, 2) void k_msar_slice(MsarArgs a, MsarFastBufs
 #pragma unroll
         for (int r = 0; r < kMsarStreams; ++r) {
           const float2 zr = z[q][r];
-          if (t0 + q < t_end)
-            *reinterpret_cast<float2*>(b.zbuf + ((t0 + q) * kMsarStreams + r) * d + c0) = zr;
+          if (t0 + q < t_end) {
+            typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+            const float isc = zis_s[q];  // a power of two: exact
+            const h2 hv = {(f16_t)(zr.x * isc), (f16_t)(zr.y * isc)};
+            *reinterpret_cast<uint32_t*>(b.zbuf + ((t0 + q) * kMsarStreams + r) * d + c0) =
+                __builtin_bit_cast(uint32_t, hv);
+          }
           e[0] = fmaf(zr.x, zr.x, fmaf(zr.y, zr.y, e[0]));
           e[1] = fmaf(zr.x, pm[r][0].x, fmaf(zr.y, pm[r][1].x, e[1]));
           e[2] = fmaf(zr.x, pm[r][0].y, fmaf(zr.y, pm[r][1].y, e[2]));
@@ -233,10 +248,14 @@ __global__ __launch_bounds__(256) void k_msar_alpha(MsarArgs a, MsarFastBufs b) 
     const float e = valid ? expf(score - m) : 0.f;
     const float l = group_sum<16>(e);
     b.alpha[t * (kMsarStreams * kMfAlphaRow) + r * kMfAlphaRow + i] = e / l;
+    const float mss = group_max<64>(valid ? ss : 0.f);
+    if (lane == 0) b.zscale[t] = f16_state_scale(sqrtf(mss));
   }
 }
 
-// Per token: beta from the slices' sums, then h = sum_r beta_r Z^(r).
+// Per token: beta from the slices' sums, then h = sum_r beta_r Z^(r) (with
+// the fp16 Z, its per-token scale is applied once at the end: exact).
+template <bool F16>
 __global__ __launch_bounds__(256) void k_msar_out(MsarArgs a, MsarFastBufs b) {
   const int64_t T = a.T, d = a.d;
   const int S = (int)(d / kMfSlice);
@@ -251,16 +270,28 @@ __global__ __launch_bounds__(256) void k_msar_out(MsarArgs a, MsarFastBufs b) {
     float beta[kMsarStreams];
 #pragma unroll
     for (int q = 0; q < kMsarStreams; ++q) beta[q] = 1.0f / (1.0f + expf(-v[1 + q] * inv));
-    const float* z = b.zbuf + t * kMsarStreams * d;
+    const float sc = F16 ? b.zscale[t] : 1.0f;
     for (int64_t c = (int64_t)threadIdx.x * 4; c < d; c += (int64_t)blockDim.x * 4) {
       float4 h = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int r = 0; r < kMsarStreams; ++r) {
-        const float4 zr = *reinterpret_cast<const float4*>(z + r * d + c);
+        float4 zr;
+        if constexpr (F16) {
+          const uint2 u = *reinterpret_cast<const uint2*>(b.zbuf + (t * kMsarStreams + r) * d + c);
+          zr.x = (float)__builtin_bit_cast(f16_t, (uint16_t)(u.x & 0xffffu));
+          zr.y = (float)__builtin_bit_cast(f16_t, (uint16_t)(u.x >> 16));
+          zr.z = (float)__builtin_bit_cast(f16_t, (uint16_t)(u.y & 0xffffu));
+          zr.w = (float)__builtin_bit_cast(f16_t, (uint16_t)(u.y >> 16));
+        } else {
+          zr = *reinterpret_cast<const float4*>(b.zbuf32 + (t * kMsarStreams + r) * d + c);
+        }
         h.x = fmaf(beta[r], zr.x, h.x);
         h.y = fmaf(beta[r], zr.y, h.y);
         h.z = fmaf(beta[r], zr.z, h.z);
         h.w = fmaf(beta[r], zr.w, h.w);
+      }
+      if constexpr (F16) {
+        h.x *= sc; h.y *= sc; h.z *= sc; h.w *= sc;
       }
       *reinterpret_cast<uint2*>(out + t * d + c) = make_uint2(pack_bf2(h.x, h.y), pack_bf2(h.z, h.w));
     }
@@ -778,7 +809,10 @@ MsarFastBufs carve(const MsarArgs& a) {
   p += align256((size_t)(T * kMsarStreams * kMfAlphaRow) * 4);
   b.part2 = reinterpret_cast<float*>(p);
   p += align256((size_t)(T * S * kMfPart2) * 4);
-  b.zbuf = reinterpret_cast<float*>(p);
+  b.zscale = reinterpret_cast<float*>(p);
+  p += align256((size_t)T * 4);
+  b.zbuf = reinterpret_cast<f16_t*>(p);
+  b.zbuf32 = nullptr;
   return b;
 }
 
@@ -792,7 +826,7 @@ hipError_t launch_n(const MsarArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((k_msar_alpha<N>), dim3((unsigned)ablocks), dim3(256), 0, st, a, b);
   hipLaunchKernelGGL(k_msar_slice<1>, grid, dim3(kMfB), 0, st, a, b);
   int64_t oblocks = a.T < 4 * (int64_t)num_cus() ? a.T : 4 * (int64_t)num_cus();
-  hipLaunchKernelGGL(k_msar_out, dim3((unsigned)oblocks), dim3(256), 0, st, a, b);
+  hipLaunchKernelGGL(k_msar_out<true>, dim3((unsigned)oblocks), dim3(256), 0, st, a, b);
   return hipGetLastError();
 }
 
@@ -803,7 +837,7 @@ size_t msar_fast_workspace_bytes(int64_t n_src, int64_t n_dst, int64_t T, int64_
     return 0;
   const int64_t S = d / kMfSlice;
   return align256((size_t)(T * S * 8 * n_src) * 4) + align256((size_t)(T * kMsarStreams * kMfAlphaRow) * 4) +
-         align256((size_t)(T * S * kMfPart2) * 4) + align256((size_t)(T * kMsarStreams * d) * 4);
+         align256((size_t)(T * S * kMfPart2) * 4) + align256((size_t)T * 4) + align256((size_t)(T * kMsarStreams * d) * 2);
 }
 
 bool msar_fast_ok(const MsarArgs& a) {
@@ -823,9 +857,9 @@ hipError_t launch_bmsar_p1_sb(const BmsarArgs& a, void* h1, hipStream_t st) {
   hipLaunchKernelGGL((k_bmsar_alpha<SB>), dim3((unsigned)blocks), dim3(256), 0, st, a);
   hipLaunchKernelGGL((k_bmsar_p1<SB, 1>), grid, dim3(kMfB), 0, st, a);
   MsarArgs ma{nullptr, a.N, a.T, a.d, a.w, a.conv, a.mix1, 1, a.eps, kBF16, h1, nullptr, 0};
-  MsarFastBufs mb{nullptr, nullptr, a.part2, a.zbuf};
+  MsarFastBufs mb{nullptr, nullptr, a.part2, nullptr, nullptr, a.zbuf};
   int64_t oblocks = a.T < 4 * (int64_t)num_cus() ? a.T : 4 * (int64_t)num_cus();
-  hipLaunchKernelGGL(k_msar_out, dim3((unsigned)oblocks), dim3(256), 0, st, ma, mb);
+  hipLaunchKernelGGL(k_msar_out<false>, dim3((unsigned)oblocks), dim3(256), 0, st, ma, mb);
   return hipGetLastError();
 }
 
