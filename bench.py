@@ -42,6 +42,8 @@ def parse():
                                                                 "decode", "msar", "block_msar"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    p.add_argument("--ceilings", action="store_true",
+                   help="measure the streaming ceilings of the kernels' read/write patterns and exit")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (counter calibration)")
     return p.parse_args()
@@ -532,6 +534,68 @@ def copy_calibration(n=1 << 31, reps=10):
     return res
 
 
+# Streaming-pattern ceilings: each routing kernel's per-token read/write mix
+# with no arithmetic (libattnres_probe.so), for the roofline discussion.
+# Every pattern moves at least 1 GiB per pass, four times the 256 MiB
+# last-level cache, so repeated passes are not served from it.
+CEILING_PATTERNS = [
+    # name, rows read, rows written, T, d
+    ("read_only", 8, 0, 16384, 4096),
+    ("write_only", 0, 4, 32768, 4096),
+    ("copy_1_to_1", 1, 1, 65536, 4096),
+    ("block_phase1", 8, 4, 16384, 4096),
+    ("block_phase2", 2, 1, 65536, 4096),
+    ("block_backward", 15, 11, 8192, 4096),
+    ("full_forward", 32, 32, 4096, 2048),
+]
+
+
+def pattern_ceilings(reps=10):
+    import ctypes
+    import torch
+    from depth_wise_attention_amd import build as b
+
+    if not os.path.exists(b.PROBE_LIB):
+        raise RuntimeError(f"{b.PROBE_LIB} is missing: run __graft_entry__.build() first")
+    probe = ctypes.CDLL(b.PROBE_LIB)
+    probe.attnres_probe_stream.restype = ctypes.c_int
+    probe.attnres_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                           ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                           ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    sink = torch.zeros(64, dtype=torch.int32, device="cuda")
+    out = []
+    for name, nr, nw, T, d in CEILING_PATTERNS:
+        src = torch.randint(-2**15, 2**15, (max(nr, 1), T, d), dtype=torch.int16, device="cuda")
+        dst = torch.empty((max(nw, 1), T, d), dtype=torch.int16, device="cuda")
+        best = None
+        for per_cu in (2, 4, 8, 16, 32):
+            blocks = cus * per_cu
+            run = lambda: probe.attnres_probe_stream(ctypes.c_void_p(src.data_ptr()), nr, ctypes.c_void_p(dst.data_ptr()),
+                                                     nw, T, d, ctypes.c_void_p(sink.data_ptr()), blocks,
+                                                     ctypes.c_void_p(stream.cuda_stream))
+            for _ in range(2):
+                if run() != 0:
+                    raise RuntimeError(f"probe launch failed for {name}")
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            gbs = (nr + nw) * T * d * 2 / (us * 1e-6) / 1e9
+            if best is None or gbs > best["gbs"]:
+                best = dict(pattern=name, rows_read=nr, rows_written=nw, T=T, d=d, bytes=(nr + nw) * T * d * 2,
+                            us=us, gbs=gbs, blocks_per_cu=per_cu)
+        log(f"[bench] ceiling {json.dumps(best)}")
+        out.append(best)
+        del src, dst
+        torch.cuda.empty_cache()
+    return {"pattern_ceilings": out}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -548,6 +612,9 @@ def main():
     ar.lib()  # fail loudly if the HIP library is missing
     if args.copy_calibration:
         print(json.dumps(copy_calibration()), flush=True)
+        return
+    if args.ceilings:
+        print(json.dumps(pattern_ceilings()), flush=True)
         return
 
     if args.workload != "block":

@@ -75,6 +75,26 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     return out
 
 
+PROBE_SRC = os.path.join(CSRC, "probe", "stream_pattern.hip")
+PROBE_LIB = os.path.join(PKG, "libattnres_probe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """Build the streaming-pattern probe (bench.py --ceilings) into its own
+    library; it is not part of libattnres.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    cc = hipcc()
+    obj = os.path.join(BUILD, "stream_pattern.hip.o")
+    out_ = _run([cc, *COMMON, "-c", PROBE_SRC, "-o", obj])
+    if verbose and out_.strip():
+        print(out_)
+    tmp = PROBE_LIB + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, obj])
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 if __name__ == "__main__":
     path = build(verbose="-v" in sys.argv)
     print(path)
+    print(build_probe(verbose="-v" in sys.argv))
