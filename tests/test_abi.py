@@ -409,3 +409,24 @@ def test_block_msar_rejects_bad_arguments():
                     (dict(h=FAKE + 2 * G + 32), EINVAL), (dict(ws=FAKE + G), EINVAL)]:
         assert _rc_bm2(**c) == want, c
     assert _rc_bm2(T=0, o=None) == OK
+
+
+def test_stream_probe_library_validates_before_launch():
+    """The streaming-pattern probe (bench.py --ceilings) lives in its own library;
+    invalid arguments are rejected with -1 before any HIP call."""
+    from depth_wise_attention_amd import build as b
+
+    if not os.path.exists(b.PROBE_LIB):
+        pytest.skip("probe library not built")
+    probe = ctypes.CDLL(b.PROBE_LIB)
+    fn = probe.attnres_probe_stream
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                   ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below is rejected first
+    assert fn(fake, 0, fake, 0, 8, 64, fake, 1, None) == -1       # nothing to move
+    assert fn(fake, 1, fake, 1, 8, 60, fake, 1, None) == -1       # d not a multiple of 8
+    assert fn(fake, 65, fake, 1, 8, 64, fake, 1, None) == -1      # too many rows
+    assert fn(None, 1, fake, 1, 8, 64, fake, 1, None) == -1       # missing source
+    assert fn(fake, 1, fake, 1, 8, 64, None, 1, None) == -1       # missing sink
+    assert fn(ctypes.c_void_p((1 << 20) + 4), 1, fake, 1, 8, 64, fake, 1, None) == -1  # misaligned
