@@ -304,8 +304,11 @@ __global__ __launch_bounds__(256) void k_msar_out(MsarArgs a, MsarFastBufs b) {
 // streams expanded once per pass for all of them.  Same slicing as
 // k_msar_slice, with 4-token chunks (the state pass keeps SB x 4 streams of
 // weighted sums per token).
-constexpr int kBmTC = 4;
-constexpr int kBmWin = kBmTC + kMfHalo;
+constexpr int kBmTC = 4;   // statistics pass (its reductions are shaped for 4 tokens)
+#ifndef ATTNRES_BM_TC1
+#define ATTNRES_BM_TC1 4
+#endif
+constexpr int kBmTC1 = ATTNRES_BM_TC1;  // weighting pass (measured: 2 tokens is 16% slower)
 
 struct BmsarArgs {
   const void* reps;    // [N][T][d] bf16
@@ -358,9 +361,11 @@ __device__ __forceinline__ float block_reduce_stats(const float (&dv)[ND], const
 template <int SB, int PASS>
 __global__ __launch_bounds__(kMfB, 2) void k_bmsar_p1(BmsarArgs a) {
   constexpr int V = 4 + 4 * SB;          // per rep and token: 4 sums of squares, 4 SB query products
+  constexpr int TC = PASS == 0 ? kBmTC : kBmTC1;  // tokens per chunk
+  constexpr int WIN = TC + kMfHalo;
   __shared__ float red[2][4][256];
-  __shared__ float alpha_s[PASS == 1 ? kBmTC * SB * kMsarStreams * kMfAlphaRow : 1];
-  __shared__ float iscale_s[kBmTC];
+  __shared__ float alpha_s[PASS == 1 ? TC * SB * kMsarStreams * kMfAlphaRow : 1];
+  __shared__ float iscale_s[TC];
   // Pass 1: this thread's rows of sublayer 1's mixer P, in LDS rather than in
   // registers (the weighted sums of SB sublayers fill the register file).
   __shared__ float4 pm_s[PASS == 1 ? kMsarStreams * 2 * kMfB : 1];
@@ -391,47 +396,47 @@ __global__ __launch_bounds__(kMfB, 2) void k_bmsar_p1(BmsarArgs a) {
   const int64_t t_begin = (int64_t)blockIdx.y * kMfRange;
   const int64_t t_end = t_begin + kMfRange < T ? t_begin + kMfRange : T;
   int buf = 0;
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += kBmTC) {
-    float2 z[kBmTC][SB][kMsarStreams];
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += TC) {
+    float2 z[TC][SB][kMsarStreams];
     if constexpr (PASS == 1) {
 #pragma unroll
-      for (int q = 0; q < kBmTC; ++q)
+      for (int q = 0; q < TC; ++q)
 #pragma unroll
         for (int i = 0; i < SB; ++i)
 #pragma unroll
           for (int r = 0; r < kMsarStreams; ++r) z[q][i][r] = make_float2(0.f, 0.f);
       lds_barrier();
-      constexpr int NA = kBmTC * SB * kMsarStreams * kMfAlphaRow;
+      constexpr int NA = TC * SB * kMsarStreams * kMfAlphaRow;
       for (int e = tid; e < NA; e += kMfB) {
         const int64_t tq = t0 + e / (SB * kMsarStreams * kMfAlphaRow);
         alpha_s[e] = a.alpha[(tq < T ? tq : T - 1) * (SB * kMsarStreams * kMfAlphaRow) +
                              e % (SB * kMsarStreams * kMfAlphaRow)];
       }
-      if (tid < kBmTC) iscale_s[tid] = 1.0f / a.o_scale[t0 + tid < T ? t0 + tid : T - 1];
+      if (tid < TC) iscale_s[tid] = 1.0f / a.o_scale[t0 + tid < T ? t0 + tid : T - 1];
       lds_barrier();
     }
-    auto load_rows = [&](int i, uint32_t (&raw)[kBmWin]) {
+    auto load_rows = [&](int i, uint32_t (&raw)[WIN]) {
       const bf16_t* col = src + (int64_t)(i < n ? i : n - 1) * T * d + c0;
 #pragma unroll
-      for (int h = 0; h < kBmWin; ++h) {
+      for (int h = 0; h < WIN; ++h) {
         const int64_t row = t0 - kMfHalo + h;
         const int64_t rc = row < 0 ? 0 : (row >= T ? T - 1 : row);
         raw[h] = *reinterpret_cast<const uint32_t*>(col + rc * d);
       }
     };
-    auto source = [&](int i, const uint32_t (&raw)[kBmWin]) {
-      float2 x[kBmWin];
+    auto source = [&](int i, const uint32_t (&raw)[WIN]) {
+      float2 x[WIN];
 #pragma unroll
-      for (int h = 0; h < kBmWin; ++h) {
+      for (int h = 0; h < WIN; ++h) {
         const int64_t row = t0 - kMfHalo + h;
         const uint32_t u = (row >= 0 && row < T) ? raw[h] : 0u;
         x[h] = make_float2(bf_lo(u), bf_hi(u));
       }
       // Pass 0: the chunk's query products [token][sublayer][stream] and sums
       // of squares [token][stream], reduced separately (no padded group).
-      float dv[PASS == 0 ? kBmTC * 4 * SB : 1], sq[PASS == 0 ? kBmTC * kMsarStreams : 1];
+      float dv[PASS == 0 ? TC * 4 * SB : 1], sq[PASS == 0 ? TC * kMsarStreams : 1];
 #pragma unroll
-      for (int q = 0; q < kBmTC; ++q) {
+      for (int q = 0; q < TC; ++q) {
         float2 sv[kMsarStreams];
         sv[0] = x[q + kMfHalo];
 #pragma unroll
@@ -465,7 +470,7 @@ __global__ __launch_bounds__(kMfB, 2) void k_bmsar_p1(BmsarArgs a) {
         }
       }
       if constexpr (PASS == 0) {
-        constexpr int ND = kBmTC * 4 * SB, DROWS = (ND + 63) / 64 * 64;
+        constexpr int ND = TC * 4 * SB, DROWS = (ND + 63) / 64 * 64;
         const float tot = block_reduce_stats<ND>(dv, sq, red, buf);
         buf ^= 1;
         const int p = tid;
@@ -473,14 +478,14 @@ __global__ __launch_bounds__(kMfB, 2) void k_bmsar_p1(BmsarArgs a) {
         if (p < ND) {
           q = p / (4 * SB);
           k = 4 + p % (4 * SB);
-        } else if (p >= DROWS && p < DROWS + kBmTC * kMsarStreams) {
+        } else if (p >= DROWS && p < DROWS + TC * kMsarStreams) {
           q = (p - DROWS) / kMsarStreams;
           k = (p - DROWS) % kMsarStreams;
         }
         if (q >= 0 && t0 + q < t_end) a.part[(((t0 + q) * S + slice) * n + i) * V + k] = tot;
       }
     };
-    uint32_t ra[kBmWin], rb[kBmWin];
+    uint32_t ra[WIN], rb[WIN];
     // One source per iteration: the next source's rows load into rb while
     // this one computes, then move to ra.  (A two-buffer ping-pong inlines the
     // source twice, and the weighted sums then change registers between the
@@ -490,14 +495,14 @@ __global__ __launch_bounds__(kMfB, 2) void k_bmsar_p1(BmsarArgs a) {
       load_rows(i + 1, rb);
       source(i, ra);
 #pragma unroll
-      for (int h = 0; h < kBmWin; ++h) ra[h] = rb[h];
+      for (int h = 0; h < WIN; ++h) ra[h] = rb[h];
     }
     if constexpr (PASS == 1) {
       // Sublayers 2..SB: the per-stream states; sublayer 1: its retrieved
       // states and the mixer's sums.
       float v[64];
 #pragma unroll
-      for (int q = 0; q < kBmTC; ++q) {
+      for (int q = 0; q < TC; ++q) {
         const bool ok = t0 + q < t_end;
         const float isc = iscale_s[q];  // a power of two: exact
 #pragma unroll
@@ -526,11 +531,11 @@ __global__ __launch_bounds__(kMfB, 2) void k_bmsar_p1(BmsarArgs a) {
         for (int j = 0; j < 8; ++j) v[q * 8 + j] = j < 5 ? e[j] : 0.f;
       }
 #pragma unroll
-      for (int q = kBmTC * 8; q < 64; ++q) v[q] = 0.f;
+      for (int q = TC * 8; q < 64; ++q) v[q] = 0.f;
       const float tot = block_reduce_values<64>(v, red, buf);
       buf ^= 1;
       const int p = tid;
-      if (p < kBmTC * 8 && (p & 7) < 5 && t0 + p / 8 < t_end)
+      if (p < TC * 8 && (p & 7) < 5 && t0 + p / 8 < t_end)
         a.part2[((t0 + p / 8) * S + slice) * kMfPart2 + (p & 7)] = tot;
     }
   }
