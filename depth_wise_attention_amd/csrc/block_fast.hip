@@ -393,6 +393,13 @@ __global__ __launch_bounds__(B, ATTNRES_P1_MINWAVES) void k_phase1_fast(Phase1Ar
       for (int i = 0; i < N; ++i) {
         float x[8];
         unpack8(v[i][c], x);
+        if constexpr (!kP1Prefetch && !MH) {
+          // The next token's rows go into each register as soon as its last
+          // use here is done: the loads overlap the rest of the weighted sums
+          // and the stores instead of starting after them.  (With heads the
+          // kernel has no registers to spare for it: it would spill.)
+          if (tn < T) v[i][c] = ld16<kP1Nt>(reps + (int64_t)i * rs + tn * d + (c * B + tid) * 8);
+        }
 #pragma unroll
         for (int l = 0; l < S; ++l) {
           const float al = read_lane(alpha, (cc * S + l) * NP + i);
@@ -411,7 +418,7 @@ __global__ __launch_bounds__(B, ATTNRES_P1_MINWAVES) void k_phase1_fast(Phase1Ar
       for (int i = 0; i < N; ++i)
 #pragma unroll
         for (int c = 0; c < CH; ++c) v[i][c] = vn[i][c];
-    } else {
+    } else if constexpr (MH) {
       if (tn < T) load_reps<N, CH, B>(v, reps, rs, d, tn, tid);
     }
   }
