@@ -550,7 +550,7 @@ CEILING_PATTERNS = [
 ]
 
 
-def pattern_ceilings(reps=10):
+def pattern_ceilings(reps=10, only=None, blocks=(2, 4, 8, 16, 32)):
     import ctypes
     import torch
     from depth_wise_attention_amd import build as b
@@ -567,10 +567,12 @@ def pattern_ceilings(reps=10):
     sink = torch.zeros(64, dtype=torch.int32, device="cuda")
     out = []
     for name, nr, nw, T, d in CEILING_PATTERNS:
+        if only is not None and name not in only:
+            continue
         src = torch.randint(-2**15, 2**15, (max(nr, 1), T, d), dtype=torch.int16, device="cuda")
         dst = torch.empty((max(nw, 1), T, d), dtype=torch.int16, device="cuda")
         best = None
-        for per_cu in (2, 4, 8, 16, 32):
+        for per_cu in blocks:
             blocks = cus * per_cu
             run = lambda: probe.attnres_probe_stream(ctypes.c_void_p(src.data_ptr()), nr, ctypes.c_void_p(dst.data_ptr()),
                                                      nw, T, d, ctypes.c_void_p(sink.data_ptr()), blocks,
@@ -674,6 +676,15 @@ def main():
         },
         "extra_workloads": extra,
     }
+    # The same box's streaming ceiling for Phase 1's read/write pattern (no
+    # arithmetic), so that frac can be read against what the pattern reaches.
+    try:
+        ceil = pattern_ceilings(only=("block_phase1",), blocks=(8, 16))["pattern_ceilings"][0]
+        line["roofline"]["pattern_ceiling_gbs"] = ceil["gbs"]
+        line["roofline"]["frac_of_pattern_ceiling"] = p1["gbs"] / ceil["gbs"]
+    except (RuntimeError, OSError) as e:
+        log(f"[bench] pattern ceiling not measured: {e}")
+        line["roofline"]["pattern_ceiling_gbs"] = None
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)
