@@ -117,7 +117,7 @@ def counters_for(kernel_key, src_hash):
 
 
 # ------------------------------------------------------------------ workloads
-def bench_block(args, H=1, T=16384, name=None, with_events=True):
+def bench_block(args, H=1, T=16384, name=None, with_events=True, cold_steps=0):
     import torch
     import depth_wise_attention_amd as ar
     from workloads import synth
@@ -178,6 +178,24 @@ def bench_block(args, H=1, T=16384, name=None, with_events=True):
         phase1=dict(bytes_per_launch=p1_b, avg_us=p1_avg * 1e6, gbs=p1_b / p1_avg / 1e9),
         phase2=dict(bytes_per_launch=p2_b, avg_us=p2_avg * 1e6, gbs=p2_b / p2_avg / 1e9),
     )
+    if cold_steps:
+        # Cold-cache steps: before each, 1 GiB is written to a scratch buffer
+        # (four times the 256 MiB last-level cache), outside the timed events.
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        ms = []
+        for _ in range(cold_steps):
+            flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        del flush
+        ms.sort()
+        q = lambda f: ms[min(len(ms) - 1, int(f * len(ms)))]
+        res["cold"] = dict(steps=cold_steps, ms_median=q(0.5), ms_p10=q(0.1), ms_p90=q(0.9),
+                           tokens_per_s_median=T / (q(0.5) / 1e3))
     return res
 
 
@@ -627,7 +645,7 @@ def main():
         log(json.dumps(fn()))
         return
 
-    head = bench_block(args)
+    head = bench_block(args, cold_steps=10)
     log(f"[bench] headline: {json.dumps(head)}")
     src_hash = kernel_source_hash("block_fast.hip", "xlane.hpp", "common.hpp")
     traffic = counters_for("phase1_block_T16384_d4096_N8_S4_H1", src_hash)
@@ -661,6 +679,7 @@ def main():
             "step_bytes_per_token": head["step_bytes"] // head["T"],
             "step_gbs": head["step_gbs"], "step_frac_of_peak": head["step_gbs"] / PEAK_HBM_GBS,
             "phase2_gbs": head["phase2"]["gbs"], "phase2_avg_us": head["phase2"]["avg_us"],
+            "cold_cache_steps": head.get("cold"),
         },
         "roofline": {
             "kernel": "k_phase1_fast (Block Phase 1)",
