@@ -339,10 +339,28 @@ __global__ __launch_bounds__(B, ATTNRES_P1_MINWAVES) void k_phase1_fast(Phase1Ar
         }
       }
     }
-    float tot[NG];
-    wave_reduce_values<P>(part, tot);
+    if constexpr ((NDOT == 32 || NDOT == 64) && N == 8) {
+      // The dot products and the sums of squares reduced separately, each with
+      // a transposing reduction of its own size: no padded 64-value group.
+      float dv[NDOT], sv[N];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) red[buf][wave][g * 64 + lane] = tot[g];
+      for (int p = 0; p < NDOT; ++p) dv[p] = part[p];
+#pragma unroll
+      for (int i = 0; i < N; ++i) sv[i] = part[NDOT + i];
+      if constexpr (NDOT == 64) {
+        red[buf][wave][lane] = transpose_reduce64(dv);
+      } else {
+        const float td = transpose_reduce_pow2<32>(dv);  // lane L: dot product L >> 1
+        if ((lane & 1) == 0) red[buf][wave][lane >> 1] = td;
+      }
+      const float ts = transpose_reduce_pow2<8>(sv);     // lane L: sum of squares L >> 3
+      if ((lane & 7) == 0) red[buf][wave][NDOT + (lane >> 3)] = ts;
+    } else {
+      float tot[NG];
+      wave_reduce_values<P>(part, tot);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) red[buf][wave][g * 64 + lane] = tot[g];
+    }
     __syncthreads();
 
     // Scores, softmax and lse for this wave's (chunk, layer, rep) lanes.

@@ -129,6 +129,59 @@ __device__ __forceinline__ float transpose_reduce64(const float (&v)[64]) {
   return r;
 }
 
+// One halving stage of a transposing reduction over lane bit OFF (8, 4, 2 or
+// 1): the lane keeps the value selected by its own bit and adds its partner's
+// copy of that value.
+template <int OFF>
+__device__ __forceinline__ float exchange_add(float lo, float hi) {
+  const bool up = (lane_id() & OFF) != 0;
+  const float keep = up ? hi : lo, send = up ? lo : hi;
+  float got;
+  if constexpr (OFF == 8) {
+    got = dpp_move<dpp::kRor8>(0.f, send);
+  } else if constexpr (OFF == 4) {
+    got = xor4(send);
+  } else if constexpr (OFF == 2) {
+    got = dpp_move<dpp::kXor2>(0.f, send);
+  } else {
+    static_assert(OFF == 1, "lane bit below 16");
+    got = dpp_move<dpp::kXor1>(0.f, send);
+  }
+  return keep + got;
+}
+
+// Transpose-reduce of P = 2^k values per lane (P = 8, 32; 16 and 64 have their
+// own forms below): on return, lane L holds the sum over all 64 lanes of value
+// index L >> (6 - k).  Lane bits 5, 4, ... select index bits k-1, k-2, ... in k
+// halving stages; the 6 - k lowest lane bits are summed out.
+template <int P>
+__device__ __forceinline__ float transpose_reduce_pow2(const float (&v)[P]) {
+  static_assert(P == 8 || P == 32, "8 or 32 values");
+  float a[P / 2];
+#pragma unroll
+  for (int m = 0; m < P / 2; ++m) a[m] = swap32_add(v[m], v[m + P / 2]);      // lane bit 5
+  float b[P / 4];
+#pragma unroll
+  for (int m = 0; m < P / 4; ++m) b[m] = swap16_add(a[m], a[m + P / 4]);      // lane bit 4
+  if constexpr (P == 8) {
+    float e = exchange_add<8>(b[0], b[1]);                                     // lane bit 3
+    e += xor4(e);                                                              // sum bits 2..0
+    e += dpp_move<dpp::kXor2>(0.f, e);
+    e += dpp_move<dpp::kXor1>(0.f, e);
+    return e;
+  } else {
+    float c[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) c[m] = exchange_add<8>(b[m], b[m + 4]);       // lane bit 3
+    float e2[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) e2[m] = exchange_add<4>(c[m], c[m + 2]);      // lane bit 2
+    float e = exchange_add<2>(e2[0], e2[1]);                                   // lane bit 1
+    e += dpp_move<dpp::kXor1>(0.f, e);                                         // sum bit 0
+    return e;
+  }
+}
+
 // Transpose-reduce of 16 values per lane: on return, lane L holds the sum over
 // all 64 lanes of value index L >> 2.  Lane bits 5, 4, 3 and 2 select index
 // bits 3, 2, 1 and 0 in four halving stages; the last two lane bits are
