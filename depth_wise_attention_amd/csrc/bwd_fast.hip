@@ -170,10 +170,26 @@ __global__ __launch_bounds__(B, ATTNRES_BWD_MINWAVES) void k_bwd_fast(BwdArgs a)
         }
       }
     }
-    float tot[NG];
-    wave_reduce_values<P>(part, tot);
+    if constexpr (P == 64 + 16 + 1) {
+      // 81 values (N = 8, S = 4): one full 64-value transposing reduction, a
+      // 16-value one and a single wave sum, instead of a second 64-value group
+      // padded from 17.
+      float a64[64], a16[16];
 #pragma unroll
-    for (int gi = 0; gi < NG; ++gi) red[buf][wave][gi * 64 + lane] = tot[gi];
+      for (int p = 0; p < 64; ++p) a64[p] = part[p];
+#pragma unroll
+      for (int p = 0; p < 16; ++p) a16[p] = part[64 + p];
+      red[buf][wave][lane] = transpose_reduce64(a64);
+      const float t16 = transpose_reduce16(a16);  // lane L: value 64 + (L >> 2)
+      if ((lane & 3) == 0) red[buf][wave][64 + (lane >> 2)] = t16;
+      const float t80 = wave_allsum(part[80]);
+      if (lane == 0) red[buf][wave][80] = t80;
+    } else {
+      float tot[NG];
+      wave_reduce_values<P>(part, tot);
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) red[buf][wave][gi * 64 + lane] = tot[gi];
+    }
     __syncthreads();
 
     // ---- per-pair scalars, one lane per (destination, source)
