@@ -339,6 +339,17 @@ __device__ __forceinline__ float block_reduce_values(const float (&v)[NV], float
   return (red[buf][0][tid] + red[buf][1][tid]) + (red[buf][2][tid] + red[buf][3][tid]);
 }
 
+// Workgroup sums of 32 values per thread, one barrier: thread p < 32 returns
+// value p (other threads return garbage).  A 32-value transposing reduction
+// instead of a 64-value one padded with zeros.
+__device__ __forceinline__ float block_reduce32(const float (&v)[32], float (&red)[2][4][256], int buf) {
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const float t = transpose_reduce_pow2<32>(v);  // lane L: value L >> 1
+  if ((lane & 1) == 0) red[buf][wave][lane >> 1] = t;
+  lds_barrier();
+  return (red[buf][0][tid & 31] + red[buf][1][tid & 31]) + (red[buf][2][tid & 31] + red[buf][3][tid & 31]);
+}
+
 // Workgroup sums of ND query products and 16 sums of squares per thread, one
 // barrier: thread p < ND returns product p, thread R + s (R = ND rounded up to
 // 64, s < 16) sum of squares s; other threads return garbage.
@@ -500,7 +511,7 @@ __global__ __launch_bounds__(kMfB, 2) void k_bmsar_p1(BmsarArgs a) {
     if constexpr (PASS == 1) {
       // Sublayers 2..SB: the per-stream states; sublayer 1: its retrieved
       // states and the mixer's sums.
-      float v[64];
+      float v[TC * 8];
 #pragma unroll
       for (int q = 0; q < TC; ++q) {
         const bool ok = t0 + q < t_end;
@@ -530,9 +541,11 @@ __global__ __launch_bounds__(kMfB, 2) void k_bmsar_p1(BmsarArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[q * 8 + j] = j < 5 ? e[j] : 0.f;
       }
-#pragma unroll
-      for (int q = TC * 8; q < 64; ++q) v[q] = 0.f;
-      const float tot = block_reduce_values<64>(v, red, buf);
+      float tot;
+      if constexpr (TC * 8 == 32)
+        tot = block_reduce32(v, red, buf);
+      else
+        tot = block_reduce_values<TC * 8>(v, red, buf);
       buf ^= 1;
       const int p = tid;
       if (p < TC * 8 && (p & 7) < 5 && t0 + p / 8 < t_end)
@@ -730,7 +743,11 @@ __global__ __launch_bounds__(kMfB, 2) void k_bmsar_p2(const bf16_t* __restrict__
       }
     }
     if constexpr (PASS <= 1) {
-      const float tot = block_reduce_values<NV>(v, red, buf);
+      float tot;
+      if constexpr (NV == 32)
+        tot = block_reduce32(v, red, buf);
+      else
+        tot = block_reduce_values<NV>(v, red, buf);
       buf ^= 1;
       const int p = tid;
       if (p < NV && t0 + p / 8 < t_end) sums[((t0 + p / 8) * S + slice) * 8 + (p & 7)] = tot;
