@@ -274,6 +274,12 @@ __global__ __launch_bounds__(B, ATTNRES_P1_MINWAVES) void k_phase1_fast(Phase1Ar
     uint4 vn[N][CH];
     if (kP1Prefetch && tn < T) load_reps<N, CH, B>(vn, reps, rs, d, tn, tid);
 
+    // Wave priority: the scores, reductions and softmax of a token run at a
+    // higher priority than the weighted sums and stores.  With two workgroups
+    // per CU, the one heading for its barrier then issues first, which shortens
+    // the time its waves wait for each other there; the weighted sums issue the
+    // next token's loads and fill the gaps.
+    __builtin_amdgcn_s_setprio(2);
     float part[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) part[p] = 0.f;
@@ -397,6 +403,7 @@ __global__ __launch_bounds__(B, ATTNRES_P1_MINWAVES) void k_phase1_fast(Phase1Ar
       }
     }
 
+    __builtin_amdgcn_s_setprio(0);
     // o_l = sum_i alpha_{l,i} v_i for each of this thread's chunks, from registers.
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
