@@ -132,6 +132,7 @@ __global__ __launch_bounds__(kMfB, 2) void k_msar_slice(MsarArgs a, MsarFastBufs
       }
     };
     auto source = [&](int i, const uint32_t (&raw)[kMfWin]) {
+      __builtin_amdgcn_s_setprio(0);
       float2 x[kMfWin];
 #pragma unroll
       for (int h = 0; h < kMfWin; ++h) {
@@ -173,6 +174,7 @@ __global__ __launch_bounds__(kMfB, 2) void k_msar_slice(MsarArgs a, MsarFastBufs
         }
       }
       if constexpr (PASS == 0) {
+        __builtin_amdgcn_s_setprio(2);
         const float tot = block_reduce64(v, red, buf);
         buf ^= 1;
         const int p = tid;
@@ -194,6 +196,7 @@ __global__ __launch_bounds__(kMfB, 2) void k_msar_slice(MsarArgs a, MsarFastBufs
       for (int h = 0; h < kMfWin; ++h) ra[h] = rb[h];
     }
     if constexpr (PASS == 1) {
+      __builtin_amdgcn_s_setprio(2);
       float v[64];
 #pragma unroll
       for (int q = 0; q < kMfTC; ++q) {
@@ -436,6 +439,7 @@ __global__ __launch_bounds__(kMfB, 2) void k_bmsar_p1(BmsarArgs a) {
       }
     };
     auto source = [&](int i, const uint32_t (&raw)[WIN]) {
+      __builtin_amdgcn_s_setprio(0);
       float2 x[WIN];
 #pragma unroll
       for (int h = 0; h < WIN; ++h) {
@@ -481,6 +485,7 @@ __global__ __launch_bounds__(kMfB, 2) void k_bmsar_p1(BmsarArgs a) {
         }
       }
       if constexpr (PASS == 0) {
+        __builtin_amdgcn_s_setprio(2);
         constexpr int ND = TC * 4 * SB, DROWS = (ND + 63) / 64 * 64;
         const float tot = block_reduce_stats<ND>(dv, sq, red, buf);
         buf ^= 1;
@@ -509,6 +514,7 @@ __global__ __launch_bounds__(kMfB, 2) void k_bmsar_p1(BmsarArgs a) {
       for (int h = 0; h < WIN; ++h) ra[h] = rb[h];
     }
     if constexpr (PASS == 1) {
+      __builtin_amdgcn_s_setprio(2);
       // Sublayers 2..SB: the per-stream states; sublayer 1: its retrieved
       // states and the mixer's sums.
       float v[TC * 8];
@@ -681,6 +687,7 @@ __global__ __launch_bounds__(kMfB, 2) void k_bmsar_p2(const bf16_t* __restrict__
     // Keep the prefetch here: without this the compiler may sink the loads to
     // their first use in the next chunk, where their latency is exposed.
     keep_memory_order();
+    if constexpr (PASS <= 1) __builtin_amdgcn_s_setprio(0);
 
     float v[PASS <= 1 ? NV : 1];
 #pragma unroll
@@ -743,6 +750,7 @@ __global__ __launch_bounds__(kMfB, 2) void k_bmsar_p2(const bf16_t* __restrict__
       }
     }
     if constexpr (PASS <= 1) {
+      __builtin_amdgcn_s_setprio(2);
       float tot;
       if constexpr (NV == 32)
         tot = block_reduce32(v, red, buf);
