@@ -274,12 +274,12 @@ __global__ __launch_bounds__(B, ATTNRES_P1_MINWAVES) void k_phase1_fast(Phase1Ar
     uint4 vn[N][CH];
     if (kP1Prefetch && tn < T) load_reps<N, CH, B>(vn, reps, rs, d, tn, tid);
 
-    // Wave priority: the scores, reductions and softmax of a token run at a
-    // higher priority than the weighted sums and stores.  With two workgroups
-    // per CU, the one heading for its barrier then issues first, which shortens
-    // the time its waves wait for each other there; the weighted sums issue the
-    // next token's loads and fill the gaps.
-    __builtin_amdgcn_s_setprio(2);
+    // Wave priority: a token's scores run at 1, its reductions and softmax at 3
+    // and its weighted sums and stores at 0.  With two workgroups per CU, the
+    // one heading for its barrier then issues first, which shortens the time
+    // its waves wait for each other there; the weighted sums issue the next
+    // token's loads and fill the gaps.
+    __builtin_amdgcn_s_setprio(1);
     float part[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) part[p] = 0.f;
@@ -345,6 +345,7 @@ __global__ __launch_bounds__(B, ATTNRES_P1_MINWAVES) void k_phase1_fast(Phase1Ar
         }
       }
     }
+    __builtin_amdgcn_s_setprio(3);
     if constexpr ((NDOT == 32 || NDOT == 64) && N == 8) {
       // The dot products and the sums of squares reduced separately, each with
       // a transposing reduction of its own size: no padded 64-value group.

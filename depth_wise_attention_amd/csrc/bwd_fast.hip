@@ -125,6 +125,10 @@ __global__ __launch_bounds__(B, ATTNRES_BWD_MINWAVES) void k_bwd_fast(BwdArgs a)
 
   int buf = 0;
   for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    // Wave priority: the loads and partial sums of a token at 0, its source
+    // gradients and stores at 2 (measured about 1% faster than either the
+    // opposite order or none).
+    __builtin_amdgcn_s_setprio(0);
     uint4 v[NS][CH], g[S][CH];
 #pragma unroll
     for (int i = 0; i < NS; ++i)
@@ -235,6 +239,7 @@ __global__ __launch_bounds__(B, ATTNRES_BWD_MINWAVES) void k_bwd_fast(BwdArgs a)
       coef = pvalid ? r * r * csh / (float)d : 0.f;
     }
 
+    __builtin_amdgcn_s_setprio(2);
     // ---- source gradients and Z, from registers
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
