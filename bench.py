@@ -138,7 +138,8 @@ def bench_block(args, H=1, T=16384, name=None, with_events=True, cold_steps=0):
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(S + 1)] for _ in range(args.steps)]
     k = {"i": -1}
 
-    def step(record=False):
+    # record: None, "p1" (events around Phase 1 only) or "all" (also after each merge).
+    def step(record=None):
         e = ev[k["i"]] if record else None
         if e:
             e[0].record(stream)
@@ -149,7 +150,7 @@ def bench_block(args, H=1, T=16384, name=None, with_events=True, cold_steps=0):
         for i in range(2, S + 1):
             ar.attnres_block_phase2_merge(state[i - 2], lse[i - 1], parts[i - 2], w[i - 1], g[i - 1], 1e-6,
                                           H, h_i=h[i - 1], o_scale=oscale, stream=stream)
-            if e:
+            if e and record == "all":
                 e[i].record(stream)
 
     for _ in range(args.warmup):
@@ -160,12 +161,19 @@ def bench_block(args, H=1, T=16384, name=None, with_events=True, cold_steps=0):
     start.record(stream)
     for s in range(args.steps):
         k["i"] = s
-        step(record=with_events)
+        step(record="p1" if with_events else None)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total = start.elapsed_time(end) / 1e3
     p1_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in range(args.steps)]
+    # The merges' own durations come from a second pass with an event after each
+    # launch, outside the timed region: every recorded event adds a gap to the
+    # step, so the timed steps carry only the two events around Phase 1.
+    for s in range(args.steps):
+        k["i"] = s
+        step(record="all" if with_events else None)
+    torch.cuda.synchronize()
     p2_ms = [ev[s][i - 1].elapsed_time(ev[s][i]) for s in range(args.steps) for i in range(2, S + 1)]
     p1_b, p2_b, step_b = block_bytes(T, d, N, S, H)
     p1_avg = sum(p1_ms) / len(p1_ms) / 1e3
