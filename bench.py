@@ -576,7 +576,15 @@ CEILING_PATTERNS = [
 ]
 
 
-def pattern_ceilings(reps=10, only=None, blocks=(2, 4, 8, 16, 32)):
+# Flavours of the probe's memory operations (its `mode` argument).
+PROBE_MODES = {0: "nt loads, nt stores, 16 B per lane", 1: "plain loads, nt stores, 16 B per lane",
+               2: "nt loads, plain stores, 16 B per lane", 3: "plain loads, plain stores, 16 B per lane",
+               4: "nt loads, nt stores, 32 B per lane", 5: "plain loads, nt stores, 32 B per lane",
+               6: "nt loads, plain stores, 32 B per lane", 7: "plain loads, plain stores, 32 B per lane"}
+
+
+def pattern_ceilings(reps=10, only=None, blocks=(2, 4, 8, 16, 32), modes=(0,)):
+    """Best rate of each pattern over the given workgroups per CU and probe modes."""
     import ctypes
     import torch
     from depth_wise_attention_amd import build as b
@@ -587,7 +595,7 @@ def pattern_ceilings(reps=10, only=None, blocks=(2, 4, 8, 16, 32)):
     probe.attnres_probe_stream.restype = ctypes.c_int
     probe.attnres_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
                                            ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
-                                           ctypes.c_void_p]
+                                           ctypes.c_int32, ctypes.c_void_p]
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     stream = torch.cuda.current_stream()
     sink = torch.zeros(64, dtype=torch.int32, device="cuda")
@@ -598,25 +606,32 @@ def pattern_ceilings(reps=10, only=None, blocks=(2, 4, 8, 16, 32)):
         src = torch.randint(-2**15, 2**15, (max(nr, 1), T, d), dtype=torch.int16, device="cuda")
         dst = torch.empty((max(nw, 1), T, d), dtype=torch.int16, device="cuda")
         best = None
-        for per_cu in blocks:
-            blocks = cus * per_cu
-            run = lambda: probe.attnres_probe_stream(ctypes.c_void_p(src.data_ptr()), nr, ctypes.c_void_p(dst.data_ptr()),
-                                                     nw, T, d, ctypes.c_void_p(sink.data_ptr()), blocks,
-                                                     ctypes.c_void_p(stream.cuda_stream))
-            for _ in range(2):
-                if run() != 0:
-                    raise RuntimeError(f"probe launch failed for {name}")
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(reps):
-                run()
-            e1.record()
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / reps
-            gbs = (nr + nw) * T * d * 2 / (us * 1e-6) / 1e9
-            if best is None or gbs > best["gbs"]:
-                best = dict(pattern=name, rows_read=nr, rows_written=nw, T=T, d=d, bytes=(nr + nw) * T * d * 2,
-                            us=us, gbs=gbs, blocks_per_cu=per_cu)
+        per_mode = {}
+        for mode in modes:
+            for per_cu in blocks:
+                nblk = cus * per_cu
+                run = lambda: probe.attnres_probe_stream(ctypes.c_void_p(src.data_ptr()), nr,
+                                                         ctypes.c_void_p(dst.data_ptr()), nw, T, d,
+                                                         ctypes.c_void_p(sink.data_ptr()), nblk, mode,
+                                                         ctypes.c_void_p(stream.cuda_stream))
+                for _ in range(2):
+                    if run() != 0:
+                        raise RuntimeError(f"probe launch failed for {name}")
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    run()
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / reps
+                gbs = (nr + nw) * T * d * 2 / (us * 1e-6) / 1e9
+                if mode not in per_mode or gbs > per_mode[mode]["gbs"]:
+                    per_mode[mode] = dict(gbs=gbs, us=us, blocks_per_cu=per_cu)
+                if best is None or gbs > best["gbs"]:
+                    best = dict(pattern=name, rows_read=nr, rows_written=nw, T=T, d=d, bytes=(nr + nw) * T * d * 2,
+                                us=us, gbs=gbs, blocks_per_cu=per_cu, mode=PROBE_MODES[mode])
+        if len(modes) > 1:
+            best["by_mode"] = {PROBE_MODES[m]: v for m, v in per_mode.items()}
         log(f"[bench] ceiling {json.dumps(best)}")
         out.append(best)
         del src, dst
@@ -642,7 +657,7 @@ def main():
         print(json.dumps(copy_calibration()), flush=True)
         return
     if args.ceilings:
-        print(json.dumps(pattern_ceilings()), flush=True)
+        print(json.dumps(pattern_ceilings(modes=tuple(range(8)))), flush=True)
         return
 
     if args.workload != "block":
@@ -678,7 +693,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {
             "workload": head["name"], "T": head["T"], "d": head["d"], "N": head["N"], "S": head["S"],
@@ -706,7 +721,7 @@ def main():
     # The same box's streaming ceiling for Phase 1's read/write pattern (no
     # arithmetic), so that frac can be read against what the pattern reaches.
     try:
-        ceil = pattern_ceilings(only=("block_phase1",), blocks=(8, 16))["pattern_ceilings"][0]
+        ceil = pattern_ceilings(only=("block_phase1",), blocks=(8, 16), modes=(0, 2))["pattern_ceilings"][0]
         line["roofline"]["pattern_ceiling_gbs"] = ceil["gbs"]
         line["roofline"]["frac_of_pattern_ceiling"] = p1["gbs"] / ceil["gbs"]
     except (RuntimeError, OSError) as e:

@@ -94,12 +94,16 @@ int check_common(int64_t T, int64_t d, int32_t H, int32_t dtype, float eps, cons
   return ATTNRES_OK;
 }
 
-// Phase-1 state: fp32, the I/O dtype, or (bf16 I/O only) the scaled fp16 state.
+// Phase-1 state: fp32, or with bf16 I/O the scaled fp16 state.  A bf16 state
+// keeps 8 significant bits, and the merge's second rounding then exceeds the
+// bf16 tolerance at full size, so it is refused.
 int check_state_dtype(int32_t o_dtype, int32_t dtype) {
-  if (o_dtype == ATTNRES_F32 || o_dtype == dtype) return ATTNRES_OK;
+  if (o_dtype == ATTNRES_F32) return ATTNRES_OK;
   if (o_dtype == ATTNRES_F16 && dtype == ATTNRES_BF16) return ATTNRES_OK;
-  return fail(ATTNRES_ERR_INVALID,
-              "o_dtype %d must be ATTNRES_F32, the call's dtype, or ATTNRES_F16 with bf16 I/O", o_dtype);
+  if (o_dtype == ATTNRES_BF16 && dtype == ATTNRES_BF16)
+    return fail(ATTNRES_ERR_UNSUPPORTED,
+                "a bf16 Phase-1 state is not supported (use ATTNRES_F16, the scaled fp16 state, or ATTNRES_F32)");
+  return fail(ATTNRES_ERR_INVALID, "o_dtype %d must be ATTNRES_F32, or ATTNRES_F16 with bf16 I/O", o_dtype);
 }
 
 int check_count(int64_t n, int64_t td, int64_t es, const char* name, size_t* bytes) {
@@ -160,15 +164,16 @@ int num_cus() {
 // The occupancy query is a host call that costs microseconds; at decode sizes
 // a launch is itself a few microseconds, so the answer is kept per device,
 // kernel and block size.
-hipError_t blocks_per_cu(const void* kern, int block, int* out) {
+hipError_t blocks_per_cu(const void* kern, int block, int* out, size_t dyn_lds) {
   struct Entry {
     int dev;
     const void* kern;
     int block;
+    size_t lds;
     int value;
   };
   static std::mutex mu;
-  static Entry table[256];
+  static Entry table[512];
   static int used = 0;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -176,16 +181,16 @@ hipError_t blocks_per_cu(const void* kern, int block, int* out) {
   {
     std::lock_guard<std::mutex> lock(mu);
     for (int i = 0; i < used; ++i)
-      if (table[i].dev == dev && table[i].kern == kern && table[i].block == block) {
+      if (table[i].dev == dev && table[i].kern == kern && table[i].block == block && table[i].lds == dyn_lds) {
         *out = table[i].value;
         return hipSuccess;
       }
   }
   int v = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kern, block, 0);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kern, block, dyn_lds);
   if (e != hipSuccess) return e;
   std::lock_guard<std::mutex> lock(mu);
-  if (used < 256) table[used++] = Entry{dev, kern, block, v};
+  if (used < 512) table[used++] = Entry{dev, kern, block, dyn_lds, v};
   *out = v;
   return hipSuccess;
 }
@@ -339,7 +344,55 @@ int attnres_block_msar_phase2(const void* o_i, const float* o_scale, const float
   return e == hipSuccess ? ATTNRES_OK : hip_fail(e, "Block MSAR phase 2 launch");
 }
 
-int attnres_version(void) { return (2 << 16) | 5; }
+int attnres_version(void) { return (2 << 16) | 6; }
+
+int attnres_kernel_variant(int32_t op, int64_t N, int64_t S, int64_t T, int64_t d, int32_t H, int32_t dtype,
+                           int32_t o_dtype, char* buf, size_t len) {
+  clear_error();
+  if (buf == nullptr || len == 0) return fail(ATTNRES_ERR_INVALID, "buf is NULL or empty");
+  buf[0] = '\0';
+  // Any 16-byte-aligned address: the predicates below only test alignment.
+  void* p = reinterpret_cast<void*>((uintptr_t)4096);
+  const float* fp = static_cast<const float*>(p);
+  const bool fast = use_fast();
+  switch (op) {
+    case ATTNRES_OP_PHASE1: {
+      Phase1Args a{p, N, T, d, fp, S, fp, d, 1e-6f, H, dtype, p, dtype, p, o_dtype, static_cast<float*>(p),
+                   static_cast<float*>(p)};
+      if (fast) phase1_fast_variant(a, buf, len);
+      if (buf[0] == '\0') snprintf(buf, len, "phase1_generic");
+      return ATTNRES_OK;
+    }
+    case ATTNRES_OP_PHASE2: {
+      Phase2Args a{p, o_dtype, fp, fp, p, T, d, fp, fp, 1e-6f, H, dtype, p};
+      snprintf(buf, len, fast && phase2_fast_ok(a) ? "phase2_fast<CPL=%lld,MH=%d>" : "phase2_generic",
+               (long long)(d / 512), H > 1 ? 1 : 0);
+      return ATTNRES_OK;
+    }
+    case ATTNRES_OP_BWD: {
+      BwdArgs a{p, N, p, S, T, d, fp, fp, d, 1e-6f, H, dtype, p, p, p, static_cast<float*>(p),
+                static_cast<float*>(p), 0, static_cast<float*>(p), T > 0 ? bwd_slots(T) : 0};
+      if (fast) bwd_fast_variant(a, buf, len);
+      if (buf[0] == '\0') snprintf(buf, len, "bwd_generic");
+      return ATTNRES_OK;
+    }
+    case ATTNRES_OP_FULL_FWD: {
+      FullArgs a{p, N, T, d, fp, S, fp, d, 1e-6f, H, dtype, p, p,
+                 attnres_full_fwd_workspace_size(N, S, d, H, dtype)};
+      snprintf(buf, len, "%s", fast && full_fast_ok(a) ? "full_fast" : "full_generic");
+      return ATTNRES_OK;
+    }
+    case ATTNRES_OP_FULL_BWD: {
+      FullBwdArgs a{p, N, T, d, fp, S, fp, d, 1e-6f, H, dtype, p, p, static_cast<float*>(p),
+                    static_cast<float*>(p), 0, static_cast<float*>(p), T > 0 ? full_bwd_slots(T) : 0,
+                    attnres_full_bwd_workspace_size(N, S, T, d, H)};
+      snprintf(buf, len, "%s", fast && full_bwd_fast_ok(a) ? "full_bwd_fast" : "full_bwd_generic");
+      return ATTNRES_OK;
+    }
+    default:
+      return fail(ATTNRES_ERR_INVALID, "unknown op %d", op);
+  }
+}
 
 int attnres_set_kernel_policy(int32_t policy) {
   if (policy != 0 && policy != 1) return fail(ATTNRES_ERR_INVALID, "unknown kernel policy %d", policy);
@@ -448,8 +501,8 @@ int attnres_block_phase2_merge(const void* o_i, int32_t o_dtype, const float* o_
   RETURN_IF(check_count(1, td, eo, "o_i", &b_o));
   RETURN_IF(check_count(H, T, 4, "lse_i", &b_lse));
   const bool in_place = (h_i == o_i);
-  if (in_place && o_dtype != dtype)
-    return fail(ATTNRES_ERR_INVALID, "in-place merge needs o_dtype == dtype");
+  if (in_place && dt_size(o_dtype) != dt_size(dtype))
+    return fail(ATTNRES_ERR_INVALID, "in-place merge needs a state of the I/O element size");
   const Range ins[] = {{in_place ? nullptr : o_i, b_o, "o_i"},
                        {lse_i, b_lse, "lse_i"},
                        {partial, b_p, "partial"},
@@ -488,8 +541,8 @@ int attnres_block_phase2_merge_update(const void* o_i, int32_t o_dtype, const fl
   RETURN_IF(check_count(1, td, eo, "o_i", &b_o));
   RETURN_IF(check_count(H, T, 4, "lse_i", &b_lse));
   const bool o_in_place = (h_i == o_i);
-  if (o_in_place && o_dtype != dtype)
-    return fail(ATTNRES_ERR_INVALID, "in-place merge needs o_dtype == dtype");
+  if (o_in_place && dt_size(o_dtype) != dt_size(dtype))
+    return fail(ATTNRES_ERR_INVALID, "in-place merge needs a state of the I/O element size");
   const bool p_in_place = (partial_out == partial_prev);
   const Range ins[] = {{o_in_place ? nullptr : o_i, b_o, "o_i"},
                        {lse_i, b_lse, "lse_i"},
@@ -513,12 +566,12 @@ int attnres_block_phase2_merge_update(const void* o_i, int32_t o_dtype, const fl
 
 size_t mhar_fwd_workspace_size(int64_t N, int64_t S, int64_t T, int64_t d, int32_t H) {
   (void)N;
-  int64_t st, ls, sc;
+  (void)d;
+  int64_t ls, sc;
   if (S < 1 || T < 0 || d < 1 || H < 1) return 0;
-  if (!mul3(S - 1, T, d, &st) || !mul3(st, 4, 1, &st)) return 0;  // fp32 state (the largest)
   if (!mul3(S, H, T, &ls) || !mul3(ls, 4, 1, &ls)) return 0;
   if (!mul3(T, 4, 1, &sc)) return 0;
-  return align_up((size_t)st) + align_up((size_t)ls) + align_up((size_t)sc);
+  return align_up((size_t)ls) + align_up((size_t)sc);
 }
 
 namespace {
@@ -529,23 +582,26 @@ int run_block_chunk(const void* reps, int64_t N, const void* partials, int64_t S
                     int64_t C, int64_t d, const float* w, const float* gain, int64_t gain_ld, float eps,
                     int32_t H, int32_t dtype, void* h, void* ws, hipStream_t stream) {
   (void)N;
-  const int64_t es = (int64_t)dt_size(dtype), td = T * d, cd = C * d;
-  // State between the phases: the scaled fp16 state for bf16 I/O, fp32 for fp32 I/O.
+  const int64_t es = (int64_t)dt_size(dtype), td = T * d;
+  // State between the phases: the scaled fp16 state for bf16 I/O, fp32 for
+  // fp32 I/O -- the I/O element size either way, so Phase 1 writes sublayer
+  // i's state into h[i - 1] itself and merge i overwrites it in place.  The
+  // workspace holds only the statistics and the per-token scales.
   const int sdt = dtype == ATTNRES_BF16 ? ATTNRES_F16 : ATTNRES_F32;
-  const int64_t se = (int64_t)dt_size(sdt);
-  char* state = static_cast<char*>(ws);                                     // [S-1, C, d]
-  char* base = static_cast<char*>(ws) + align_up((size_t)((S - 1) * cd * 4));
-  float* lse = reinterpret_cast<float*>(base);                              // [S, H, C]
-  float* oscale = reinterpret_cast<float*>(base + align_up((size_t)(S * H * C * 4)));  // [C]
+  float* lse = static_cast<float*>(ws);                                                         // [S, H, C]
+  float* oscale = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)(S * H * C * 4)));  // [C]
   const char* r0 = static_cast<const char*>(reps) + t0 * d * es;
   char* h0 = static_cast<char*>(h) + t0 * d * es;
   const int64_t gld = gain ? gain_ld : 0;
-  Phase1Args p1{r0, N, C, d, w, S, gain, gld, eps, H, dtype, h0, dtype, state, sdt, lse,
+  // h is [S, T, d]: the chunk's rows of sublayers 2..S start T*d elements apart,
+  // which Phase 1 addresses as a state of stride T*d (orest_stride).
+  Phase1Args p1{r0, N, C, d, w, S, gain, gld, eps, H, dtype, h0, dtype, h0 + td * es, sdt, lse,
                 sdt == ATTNRES_F16 ? oscale : nullptr};
   p1.rep_stride = td;
+  p1.orest_stride = td;
   RETURN_IF(run_phase1(p1, stream));
   for (int64_t i = 2; i <= S; ++i) {
-    Phase2Args p2{state + (i - 2) * cd * se,
+    Phase2Args p2{h0 + (i - 1) * td * es,
                   sdt,
                   sdt == ATTNRES_F16 ? oscale : nullptr,
                   lse + (i - 1) * H * C,

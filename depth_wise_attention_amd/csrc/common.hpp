@@ -11,6 +11,11 @@ typedef _Float16 f16_t;
 
 constexpr int kWave = 64;
 
+// Buffer descriptors (gfx9 family): word 3 of a raw, unswizzled descriptor
+// with 32-bit data format, and the cache-policy bit of a nontemporal access.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kBufferNt = 2;
+
 // ---------------------------------------------------------------- element I/O
 __device__ __forceinline__ float bf2f(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
 

@@ -108,6 +108,7 @@ __global__ __launch_bounds__(256) void k_phase1_generic(Phase1Args a) {
   const E* reps = static_cast<const E*>(a.reps);
   const int d = (int)a.d;
   const int64_t T = a.T, rs = a.rep_stride != 0 ? a.rep_stride : a.T * a.d;
+  const int64_t os = a.orest_stride != 0 ? a.orest_stride : a.T * a.d;
   const int64_t wave = (int64_t)blockIdx.x * kGenWaves + (threadIdx.x >> 6);
   const int64_t nw = (int64_t)gridDim.x * kGenWaves;
   for (int64_t t = wave; t < T; t += nw) {
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(256) void k_phase1_generic(Phase1Args a) {
                                static_cast<O0*>(a.o0) + t * d, lse, T);
       else
         depth_read_wave<E, OR>(row, (int)a.N, r_lane, d, a.H, a.w + l * d, g,
-                               static_cast<OR*>(a.orest) + ((l - 1) * T + t) * d, lse, T, inv_scale);
+                               static_cast<OR*>(a.orest) + (l - 1) * os + t * d, lse, T, inv_scale);
     }
   }
 }
@@ -496,8 +497,6 @@ hipError_t launch_phase1_generic(const Phase1Args& a, hipStream_t st) {
   const dim3 grid((unsigned)gen_blocks(a.T)), block(kGenWaves * kWave);
   if (a.dtype == kF32) {
     hipLaunchKernelGGL((k_phase1_generic<float, float, float>), grid, block, 0, st, a);
-  } else if (a.o0_dtype == kBF16 && a.orest_dtype == kBF16) {
-    hipLaunchKernelGGL((k_phase1_generic<bf16_t, bf16_t, bf16_t>), grid, block, 0, st, a);
   } else if (a.o0_dtype == kBF16 && a.orest_dtype == kF32) {
     hipLaunchKernelGGL((k_phase1_generic<bf16_t, bf16_t, float>), grid, block, 0, st, a);
   } else if (a.o0_dtype == kBF16 && a.orest_dtype == kF16) {
@@ -517,7 +516,7 @@ hipError_t launch_phase2_generic(const Phase2Args& a, hipStream_t st) {
   else if (a.o_dtype == kF16)
     hipLaunchKernelGGL((k_phase2_generic<bf16_t, f16_t>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((k_phase2_generic<bf16_t, bf16_t>), grid, block, 0, st, a);
+    return hipErrorNotSupported;  // a bf16 state is refused before any launch
   return hipGetLastError();
 }
 

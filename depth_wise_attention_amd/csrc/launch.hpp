@@ -30,7 +30,7 @@ struct FullArgs {
 };
 
 // Phase 1: layer 0 is written to o0 (o0_dtype), layers 1..S-1 to
-// orest + (l-1)*T*d (orest_dtype).
+// orest + (l-1)*orest_stride (orest_dtype; orest_stride 0 means T*d).
 struct Phase1Args {
   const void* reps;
   int64_t N, T, d;
@@ -50,6 +50,9 @@ struct Phase1Args {
   // Elements between consecutive reps (0: T * d).  A T-chunk of a longer
   // sequence passes the full sequence's T * d with reps at the chunk's first token.
   int64_t rep_stride = 0;
+  // Elements between consecutive state rows (0: T * d).  mhar_fwd keeps the
+  // state of sublayer i in h[i - 1], whose rows are the whole sequence apart.
+  int64_t orest_stride = 0;
 };
 
 struct Phase2Args {
@@ -169,8 +172,12 @@ hipError_t launch_full_bwd_fast(const FullBwdArgs& a, const float** slabs, int64
 // arguments (no HIP calls); a launcher may only be called when its predicate
 // holds.
 bool phase1_fast_ok(const Phase1Args& a);
+// Name of the Phase 1 kernel variant a call would run ("" when not eligible).
+void phase1_fast_variant(const Phase1Args& a, char* buf, size_t len);
 bool phase2_fast_ok(const Phase2Args& a);
 bool bwd_fast_ok(const BwdArgs& a);
+// Name of the Block backward kernel variant a call would run ("" when not eligible).
+void bwd_fast_variant(const BwdArgs& a, char* buf, size_t len);
 bool full_fast_ok(const FullArgs& a);
 size_t full_fast_workspace_bytes(int64_t n_src, int64_t n_dst, int64_t d, int H, int dtype);
 hipError_t launch_phase1_fast(const Phase1Args& a, hipStream_t st);
@@ -219,6 +226,7 @@ hipError_t launch_bmsar_phase2(const Bmsar2Call& c, hipStream_t st);
 
 int num_cus();  // compute units of the current device (cached per device)
 // Resident blocks per compute unit for a kernel and block size (cached).
-hipError_t blocks_per_cu(const void* kern, int block, int* out);
+// dyn_lds: bytes of dynamic LDS per workgroup of the launch.
+hipError_t blocks_per_cu(const void* kern, int block, int* out, size_t dyn_lds = 0);
 
 }  // namespace attnres

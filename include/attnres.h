@@ -57,8 +57,17 @@ extern "C" {
  * chosen from the bound |o| <= max_i ||b_i||_2 so that every stored value is
  * below 32768 in magnitude and the bound sits in [16384, 32768): no fp16
  * overflow for any finite input, and 11 significant bits for the state
- * (bf16 keeps 8).  Requires each rep's sum of squares to be finite in fp32. */
+ * (bf16 keeps 8).  Requires each rep's sum of squares to be finite in fp32.
+ * A bf16 state is refused (ATTNRES_ERR_UNSUPPORTED): its 8 bits, rounded
+ * once more by the merge, exceed the bf16 tolerance at full size. */
 #define ATTNRES_F16 2
+
+/* Operations named by attnres_kernel_variant. */
+#define ATTNRES_OP_PHASE1 0   /* attnres_block_phase1 (N reps, S sublayers)       */
+#define ATTNRES_OP_PHASE2 1   /* attnres_block_phase2_merge                       */
+#define ATTNRES_OP_BWD 2      /* attnres_bwd (N reps, S sublayers)                */
+#define ATTNRES_OP_FULL_FWD 3 /* attnres_full_fwd (N = n_src, S = n_dst)          */
+#define ATTNRES_OP_FULL_BWD 4 /* attnres_full_bwd (N = n_src, S = n_dst)          */
 
 #define ATTNRES_OK 0
 #define ATTNRES_ERR_INVALID (-1)     /* bad pointer, size, flag, or aliasing   */
@@ -110,10 +119,10 @@ size_t attnres_full_fwd_workspace_size(int64_t n_src, int64_t n_dst, int64_t d, 
  *           sublayer (its source set has no partial sum)
  *  o_state  [S-1, T, d] in o_dtype: o_2 .. o_S, the state Phase 2 merges
  *           (may be NULL when S == 1)
- *  o_dtype  ATTNRES_F32, the call's dtype, or ATTNRES_F16 (bf16 I/O only; see
- *           its definition).  The merge rounds the state once more, so the
+ *  o_dtype  ATTNRES_F32, or ATTNRES_F16 (bf16 I/O only; see its
+ *           definition).  The merge rounds the state once more, so the
  *           state's precision adds to the error: fp32 adds nothing, the scaled
- *           fp16 state about 2^-12 of the value, a bf16 state about 2^-9.
+ *           fp16 state about 2^-12 of the value.
  *  lse      [S, H, T] fp32: lse_l = max_i s_i + log sum_i exp(s_i - max_i s_i)
  *  o_scale  [T] fp32, written when o_dtype == ATTNRES_F16 (else may be NULL)
  * Requires 1 <= N <= 63, S >= 1.
@@ -137,7 +146,9 @@ int attnres_block_phase1(const void* reps, int64_t N, int64_t T, int64_t d,
  *  lse_i    [H, T] fp32                       Phase 1 statistics row i
  *  partial  [T, d] dtype
  *  w_i      [d] fp32;  gain_i [d] fp32 or NULL (ones)
- *  h_i      [T, d] dtype.  h_i may equal o_i when o_dtype == dtype (in place).
+ *  h_i      [T, d] dtype.  h_i may equal o_i when the state's element has
+ *           the I/O size (fp32 state with fp32 I/O, scaled fp16 state with
+ *           bf16 I/O): every element is read before it is written (in place).
  */
 int attnres_block_phase2_merge(const void* o_i, int32_t o_dtype, const float* o_scale,
                                const float* lse_i, const void* partial, int64_t T, int64_t d,
@@ -161,7 +172,8 @@ int attnres_block_phase2_merge(const void* o_i, int32_t o_dtype, const float* o_
  *               sublayer i-1)
  *  partial_out  [T, d] dtype; may equal partial_prev (in place), must not
  *               otherwise overlap an input or another output
- *  h_i          [T, d] dtype; may equal o_i when o_dtype == dtype
+ *  h_i          [T, d] dtype; may equal o_i when the state's element has the
+ *               I/O size (as attnres_block_phase2_merge)
  *  h_inv_rms    [T] fp32 or NULL;  norm_eps finite and >= 0 when it is used
  * Other arguments as for attnres_block_phase2_merge.
  */
@@ -173,18 +185,20 @@ int attnres_block_phase2_merge_update(const void* o_i, int32_t o_dtype, const fl
                                       float* h_inv_rms, hipStream_t stream);
 
 /*
- * Bytes of device workspace mhar_fwd needs: room for an fp32 Phase-1 state of
- * sublayers 2..S ([S-1, T, d]), the statistics ([S, H, T]) and the per-token
- * state scale ([T]), each aligned to 256 bytes.  Returns 0 for invalid sizes.
+ * Bytes of device workspace mhar_fwd needs: the statistics ([S, H, T] fp32)
+ * and the per-token state scale ([T] fp32), each aligned to 256 bytes (the
+ * Phase-1 state itself lives in h; see mhar_fwd).  Returns 0 for invalid
+ * sizes.
  */
 size_t mhar_fwd_workspace_size(int64_t N, int64_t S, int64_t T, int64_t d, int32_t H);
 
 /*
  * One block of multi-head Block AttnRes routing (chatpaper.ai "Multi-Head
  * Attention Residuals" abstract; H = 1 is Block AttnRes): exactly the launches
- * of attnres_block_phase1 (h_first = h[0]; state in ws: the scaled fp16 state
- * ATTNRES_F16 for bf16 I/O, fp32 for fp32 I/O) followed by the S-1
- * attnres_block_phase2_merge calls for sublayers 2..S, in order.
+ * of attnres_block_phase1 (h_first = h[0]; the state of sublayer i >= 2
+ * written into h[i-1] itself: the scaled fp16 state ATTNRES_F16 for bf16 I/O,
+ * fp32 for fp32 I/O) followed by the S-1 attnres_block_phase2_merge calls for
+ * sublayers 2..S, in order, each in place (h_i == o_i = h[i-1]).
  *
  *  reps      [N, T, d] dtype            b_0 .. b_{N-1}
  *  partials  [S-1, T, d] dtype          partials[k] = b^{(n)}_{k+1}, the sum
@@ -380,8 +394,22 @@ int attnres_block_msar_phase2(const void* o_i, const float* o_scale, const float
 
 /* ABI version: (major << 16) | minor.  Major 2 added the Full-forward workspace;
  * minor 1 added the Full backward, minor 2 the fused Phase 2 update, minor 3 the
- * chunked block forward, minor 4 MSAR, minor 5 the two-phase Block MSAR. */
+ * chunked block forward, minor 4 MSAR, minor 5 the two-phase Block MSAR, minor 6
+ * attnres_kernel_variant (and mhar_fwd's state moved into h). */
 int attnres_version(void);
+
+/*
+ * Name of the kernel a call of `op` (ATTNRES_OP_*) with these sizes would run
+ * under the current kernel policy, written to buf (len bytes, truncated, NUL
+ * terminated): e.g. "phase1_fast<N=8,S=4,CH=2,MH=0> B=256 lds=67712" or
+ * "phase1_generic".  N and S are the rep and sublayer counts (n_src and n_dst
+ * for the Full ops); o_dtype is the Phase-1 state format (ignored by the other
+ * ops); every pointer is taken as 16-byte aligned.  Pure host logic: makes no
+ * HIP call, so it can be used (and tested) without a GPU.  Returns 0, or
+ * ATTNRES_ERR_INVALID for an unknown op or a NULL or empty buffer.
+ */
+int attnres_kernel_variant(int32_t op, int64_t N, int64_t S, int64_t T, int64_t d, int32_t H,
+                           int32_t dtype, int32_t o_dtype, char* buf, size_t len);
 
 /*
  * Kernel selection, process-wide.  0 (default): the specialised gfx950 kernels

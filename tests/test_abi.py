@@ -56,7 +56,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_policy():
     assert binding.attnres_version() >> 16 == 2
-    assert binding.attnres_version() & 0xFFFF >= 5
+    assert binding.attnres_version() & 0xFFFF >= 6
     prev = binding.attnres_set_kernel_policy(1)
     assert binding.attnres_set_kernel_policy(prev) == 1
     with pytest.raises(binding.AttnResError):
@@ -65,10 +65,11 @@ def test_version_and_policy():
 
 def test_workspace_sizes():
     N, S, T, d, H = 8, 4, 16384, 4096, 1
-    state = (S - 1) * T * d * 4
     lse = S * H * T * 4
     up = lambda x: (x + 255) // 256 * 256
-    assert binding.mhar_fwd_workspace_size(N, S, T, d, H) == up(state) + up(lse) + up(4 * T)
+    # The Phase-1 state lives in h (in place): the workspace holds lse and the scales only.
+    assert binding.mhar_fwd_workspace_size(N, S, T, d, H) == up(lse) + up(4 * T)
+    assert binding.mhar_fwd_workspace_size(N, 4, T, d, 8) == up(4 * 8 * T * 4) + up(4 * T)
     assert binding.mhar_fwd_workspace_size(N, 1, 5, 3, 1) == up(4 * 5) + up(4 * 5)
     assert binding.mhar_fwd_workspace_size(N, 0, T, d, H) == 0
     assert binding.attnres_bwd_workspace_size(N, S, 8192, d, H) == 1024 * S * d * 4
@@ -164,6 +165,16 @@ def test_phase1_rejects_bad_arguments():
 
 
 @fake_ptrs
+def test_bf16_state_is_refused():
+    """A bf16 Phase-1 state (8 bits, rounded again by the merge) misses the bf16
+    bar at full size, so every call that would take one refuses it."""
+    assert _rc_phase1(o_dtype=BF16) == EUNSUP
+    assert "bf16 Phase-1 state" in binding.attnres_last_error()
+    assert _rc_phase2(o_dtype=BF16) == EUNSUP
+    assert _rc_update(o_dtype=BF16) == EUNSUP
+
+
+@fake_ptrs
 def test_phase1_rejects_overlapping_outputs():
     assert _rc_phase1(lse=FAKE + (2 << 30) + 64) == EINVAL
     assert _rc_phase1(o=FAKE + 8) == EINVAL
@@ -191,12 +202,13 @@ def test_phase2_rejects_bad_arguments():
 def test_phase2_in_place_needs_matching_dtype():
     assert _rc_phase2(h=FAKE) == EINVAL          # o is fp32, h bf16: cannot share storage
     assert "in-place" in binding.attnres_last_error()
+    assert _rc_update(o_dtype=F32, h=FAKE) == EINVAL
     assert _rc_phase2(h=FAKE + (2 << 30)) == EINVAL  # h over the partial
 
 
 def _rc_update(**kw):
     G = 1 << 30
-    a = dict(o=FAKE, o_dtype=BF16, scale=None, lse=FAKE + G, prev=FAKE + 2 * G, f=FAKE + 3 * G, T=8, d=64,
+    a = dict(o=FAKE, o_dtype=F32, scale=None, lse=FAKE + G, prev=FAKE + 2 * G, f=FAKE + 3 * G, T=8, d=64,
              w=FAKE + 4 * G, gain=None, eps=1e-6, H=1, dtype=BF16, pout=FAKE + 5 * G, h=FAKE + 6 * G,
              norm_eps=1e-6, rms=FAKE + 7 * G)
     a.update(kw)
@@ -422,11 +434,13 @@ def test_stream_probe_library_validates_before_launch():
     fn = probe.attnres_probe_stream
     fn.restype = ctypes.c_int
     fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
-                   ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+                   ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]
     fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below is rejected first
-    assert fn(fake, 0, fake, 0, 8, 64, fake, 1, None) == -1       # nothing to move
-    assert fn(fake, 1, fake, 1, 8, 60, fake, 1, None) == -1       # d not a multiple of 8
-    assert fn(fake, 65, fake, 1, 8, 64, fake, 1, None) == -1      # too many rows
-    assert fn(None, 1, fake, 1, 8, 64, fake, 1, None) == -1       # missing source
-    assert fn(fake, 1, fake, 1, 8, 64, None, 1, None) == -1       # missing sink
-    assert fn(ctypes.c_void_p((1 << 20) + 4), 1, fake, 1, 8, 64, fake, 1, None) == -1  # misaligned
+    assert fn(fake, 0, fake, 0, 8, 64, fake, 1, 0, None) == -1       # nothing to move
+    assert fn(fake, 1, fake, 1, 8, 60, fake, 1, 0, None) == -1       # d not a multiple of 8
+    assert fn(fake, 65, fake, 1, 8, 64, fake, 1, 0, None) == -1      # too many rows
+    assert fn(None, 1, fake, 1, 8, 64, fake, 1, 0, None) == -1       # missing source
+    assert fn(fake, 1, fake, 1, 8, 64, None, 1, 0, None) == -1       # missing sink
+    assert fn(ctypes.c_void_p((1 << 20) + 4), 1, fake, 1, 8, 64, fake, 1, 0, None) == -1  # misaligned
+    assert fn(fake, 1, fake, 1, 8, 64, fake, 1, 8, None) == -1       # unknown mode
+    assert fn(fake, 1, fake, 1, 8, 72, fake, 1, 4, None) == -1       # 32-byte pieces need d % 16 == 0

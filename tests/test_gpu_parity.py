@@ -189,13 +189,13 @@ def test_block_shapes(T, d, N, S, H, dtype, gain, policy):
         assert np.all(np.abs(back - o_ref[1:]) <= bound)
 
 
-@pytest.mark.parametrize("state", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("state", ["f32", "f16"])
 def test_two_phase_state_formats(state, policy):
     """Every state format through the public calls, against the plain definition."""
     wl = synth.block_workload(T=257, d=4096, N=8, S=4, H=1, rep_std_step=0.3, dtype="bf16", seed=12)
     say(f"state format {state} T={wl.T} policy={policy}")
     reps, parts, w, g = _block_on_gpu(wl, "bf16", wl.gain)
-    sdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[state]
+    sdt = {"f32": torch.float32, "f16": torch.float16}[state]
     h_first, o_state, lse, o_scale = ar.attnres_block_phase1(reps, w, g, wl.eps, 1, o_dtype=sdt)
     ref = orc.block_direct(wl.reps, wl.partials, wl.w, wl.gain, wl.eps, 1)
     check(host(h_first), ref[0], "bf16", "h1")
@@ -205,10 +205,24 @@ def test_two_phase_state_formats(state, policy):
                                            o_scale=o_scale)
         errs.append(bf16_excess_over_rms(host(hi), ref[i - 1]))
     print(f"  state {state}: excess/RMS " + " ".join(f"{e:.2e}" for e in errs))
-    if state != "bf16":   # the bf16 state is reported, not held to the bar (see the design notes)
-        assert max(errs) <= 2e-2
+    assert max(errs) <= 2e-2
     if state == "f32":
         assert max(errs) < 1e-3
+
+
+def test_bf16_state_is_refused():
+    """A bf16 Phase-1 state would miss the bf16 bar at full size: refused before any launch."""
+    wl = synth.block_workload(T=8, d=512, N=8, S=4, H=1, rep_std_step=0.3, dtype="bf16", seed=12)
+    say("bf16 state refused")
+    reps, parts, w, g = _block_on_gpu(wl, "bf16", wl.gain)
+    with pytest.raises(ar.AttnResError) as e:
+        ar.attnres_block_phase1(reps, w, g, wl.eps, 1, o_dtype=torch.bfloat16)
+    assert e.value.code == -2
+    o = torch.zeros((8, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.zeros((1, 8), device=DEV)
+    with pytest.raises(ar.AttnResError) as e:
+        ar.attnres_block_phase2_merge(o, lse, parts[0], w[1], g[1], wl.eps, 1)
+    assert e.value.code == -2
 
 
 @pytest.mark.parametrize("magnitude", [1e-7, 1.0, 3e4, 1e12])
@@ -226,18 +240,23 @@ def test_scaled_state_range(magnitude, policy):
         check(h[i], ref[i], "bf16", f"h{i + 1} at magnitude {magnitude}")
 
 
-def test_phase2_in_place_and_bf16_state(policy):
-    """In-place merge (h_i == o_i, bf16 state) matches the out-of-place merge."""
-    wl = synth.block_workload(T=300, d=4096, N=8, S=4, H=2, rep_std_step=0.3, dtype="bf16", seed=9)
-    say(f"phase2 in place T={wl.T} policy={policy}")
-    reps, parts, w, g = _block_on_gpu(wl, "bf16", wl.gain)
-    _, o, lse, _ = ar.attnres_block_phase1(reps, w, g, wl.eps, 2, o_dtype=torch.bfloat16)
-    out_of_place = ar.attnres_block_phase2_merge(o[0], lse[1], parts[0], w[1], g[1], wl.eps, 2)
-    ar.attnres_block_phase2_merge(o[0], lse[1], parts[0], w[1], g[1], wl.eps, 2, h_i=o[0])
-    assert torch.equal(o[0], out_of_place)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_phase2_in_place(dtype, policy):
+    """In-place merge (h_i == o_i) with a state of the I/O element size (the
+    scaled fp16 state under bf16 I/O, fp32 under fp32 I/O) gives the bits of
+    the out-of-place merge."""
+    wl = synth.block_workload(T=300, d=4096 if dtype == "bf16" else 256, N=8, S=4, H=2, rep_std_step=0.3,
+                              dtype=dtype, seed=9)
+    say(f"phase2 in place {dtype} T={wl.T} policy={policy}")
+    reps, parts, w, g = _block_on_gpu(wl, dtype, wl.gain)
+    sdt = torch.float16 if dtype == "bf16" else torch.float32
+    _, o, lse, sc = ar.attnres_block_phase1(reps, w, g, wl.eps, 2, o_dtype=sdt)
+    out_of_place = ar.attnres_block_phase2_merge(o[0], lse[1], parts[0], w[1], g[1], wl.eps, 2, o_scale=sc)
+    view = o[0].view(TDT[dtype])
+    ar.attnres_block_phase2_merge(o[0], lse[1], parts[0], w[1], g[1], wl.eps, 2, h_i=o[0], o_scale=sc)
+    assert torch.equal(view, out_of_place)
     ref = orc.block_direct(wl.reps, wl.partials, wl.w, wl.gain, wl.eps, 2)
-    err = bf16_excess_over_rms(host(o[0]), ref[1])
-    print(f"  bf16-state merge excess/RMS {err:.2e} (fp32 state is the default)")
+    check(host(view), ref[1], dtype, "in-place merge")
 
 
 def test_block_two_phase_config_sampled():
@@ -396,6 +415,14 @@ def test_bwd_full_d_against_oracle():
         print(f"  {name}: {err:.2e}")
 
 
+def _param_grad_golden(H):
+    """The oracle's dw and dgain summed over every token of the full-size
+    backward workload (written by tests/golden/make_bwd_param_grads.py)."""
+    import os
+    z = np.load(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "bwd_param_grads.npz"))
+    return z[f"dw_H{H}"], z[f"dgain_H{H}"]
+
+
 def test_bwd_config_sampled():
     """Block fwd+bwd bf16 at full size: T=8192, d=4096, N=8, S=4.
 
@@ -429,6 +456,10 @@ def test_bwd_config_sampled():
     # determinism
     again = ar.attnres_bwd(reps, parts, w, dh, g, wl.eps, 1)
     assert all(torch.equal(x, y) for x, y in zip(again, (d_reps, d_parts, dw, dg)))
+    # dw and dgain over all 8192 tokens against the oracle's token sums
+    gold = _param_grad_golden(1)
+    print(f"  dw {check(host(dw), gold[0], 'f32_from_bf16', 'dw (all tokens)'):.2e}, "
+          f"dgain {check(host(dg), gold[1], 'f32_from_bf16', 'dgain (all tokens)'):.2e}")
 
 
 def test_mhar_bwd_config_sampled():
@@ -458,6 +489,9 @@ def test_mhar_bwd_config_sampled():
         err = max_abs_over_rms(host(x), host(y))
         print(f"  fast vs general {name}: {err:.2e}")
         assert err < 1e-4, name
+    gold = _param_grad_golden(8)
+    check(host(dw), gold[0], "f32_from_bf16", "dw (all tokens)")
+    check(host(dg), gold[1], "f32_from_bf16", "dgain (all tokens)")
 
 
 # ----------------------------------------------------------------- Full backward

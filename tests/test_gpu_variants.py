@@ -1,0 +1,149 @@
+"""Every specialised kernel variant the dispatcher can select, against the oracle.
+
+tests/test_dispatch.py fixes which kernel each shape runs (host logic, no
+GPU).  Here every one of those variants runs on the GPU through the C ABI and
+is compared with the oracle on the same seeded inputs:
+
+  * Block Phase 1 for every block depth N = 1..12 and S = 1..8 at d = 4096,
+    every width class (d = 512 .. 8192, one or two chunks per thread), and
+    heads of whole 512-channel segments;
+  * the Block backward for N = 1..12, S = 1..4, widths and heads;
+  * a sharply peaked depth softmax (scores in the hundreds), where the
+    merge's exp(lse - m) underflows to zero.
+
+Each case first asserts that the dispatcher picks the specialised kernel, so a
+shape that silently fell to the general kernel would fail here.  Cases with
+T above the number of resident workgroups give each workgroup several tokens
+and a ragged tail.
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import depth_wise_attention_amd as ar  # noqa: E402
+from metrics import check  # noqa: E402
+from oracle import attnres_oracle as orc  # noqa: E402
+from workloads import synth  # noqa: E402
+
+DEV = "cuda"
+
+
+def say(msg: str) -> None:
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def dev(x, bf16=False):
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV)
+    return t.to(torch.bfloat16) if bf16 else t
+
+
+def host(t) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+# (N, S, d, H, T)
+PHASE1_CASES = (
+    [(N, S, 4096, 1, 19) for N in range(1, 13) for S in range(1, 9)]
+    + [(8, 4, d, 1, 1100) for d in (512, 1024, 1536, 2048, 3072, 8192)]
+    + [(4, 4, d, 1, 700) for d in (1024, 2048, 4096, 8192)]
+    + [(9, 6, 2048, 1, 600), (12, 8, 512, 1, 900), (5, 3, 4096, 1, 1300), (1, 1, 4096, 1, 800)]
+    + [(8, 4, 4096, H, 700) for H in (2, 4, 8)]
+    + [(4, 4, 8192, 16, 300), (8, 4, 2048, 4, 500), (4, 4, 1024, 2, 600), (9, 4, 4096, 8, 400),
+       (12, 6, 4096, 8, 300), (3, 7, 2048, 2, 500), (8, 4, 8192, 8, 300)]
+)
+
+
+@pytest.mark.parametrize("N,S,d,H,T", PHASE1_CASES)
+def test_phase1_variant(N, S, d, H, T):
+    name = ar.attnres_kernel_variant(ar.OP_PHASE1, N, S, T, d, H)
+    say(f"phase1 N={N} S={S} d={d} H={H} T={T}: {name}")
+    assert name.startswith("phase1_fast"), name
+    wl = synth.block_workload(T=T, d=d, N=N, S=S, H=H, rep_std_step=0.3, dtype="bf16", seed=40 + N + 13 * S)
+    reps, w, g = dev(wl.reps, True), dev(wl.w), dev(wl.gain)
+    parts = dev(wl.partials, True) if S > 1 else None
+    # The block forward (Phase 1 with the scaled fp16 state kept in h, then the
+    # in-place merges) against the plain definition.
+    h = ar.mhar_fwd(reps, parts, w, g, wl.eps, H)
+    ref = orc.block_direct(wl.reps, wl.partials, wl.w, wl.gain, wl.eps, H)
+    check(host(h), ref, "bf16", "mhar_fwd")
+    # Phase 1 alone with the fp32 state: state and statistics against the oracle's Phase 1.
+    h_first, o32, lse, _ = ar.attnres_block_phase1(reps, w, g, wl.eps, H, o_dtype=torch.float32)
+    o_ref, lse_ref = orc.block_phase1(wl.reps, wl.w, wl.gain, wl.eps, H)
+    assert torch.equal(h_first, h[0])
+    if S > 1:
+        check(host(o32), o_ref[1:], "f32_from_bf16", "phase1 fp32 state")
+    np.testing.assert_allclose(host(lse), lse_ref, rtol=0, atol=2e-4)
+    if S > 1:
+        # the scaled fp16 state: within half an fp16 ulp of the exact state
+        _, o16, _, sc = ar.attnres_block_phase1(reps, w, g, wl.eps, H, o_dtype=torch.float16)
+        back = host(o16) * host(sc)[None, :, None]
+        bound = 2.0 ** -11 * np.abs(o_ref[1:]) * (1 + 1e-3) + 1e-5 * np.sqrt(np.mean(o_ref[1:] ** 2))
+        assert np.all(np.abs(back - o_ref[1:]) <= bound)
+
+
+# (N, S, d, H, T)
+BWD_CASES = (
+    [(N, S, 4096, 1, 7) for N in range(1, 13) for S in range(1, 5)]
+    + [(8, 4, d, 1, 600) for d in (512, 1024, 1536, 2048)]
+    + [(8, 4, 4096, H, 300) for H in (2, 4, 8)]
+    + [(12, 4, 4096, 8, 200), (3, 2, 2048, 4, 300), (9, 3, 1024, 2, 400), (5, 1, 4096, 1, 700)]
+)
+
+
+@pytest.mark.parametrize("N,S,d,H,T", BWD_CASES)
+def test_bwd_variant(N, S, d, H, T):
+    name = ar.attnres_kernel_variant(ar.OP_BWD, N, S, T, d, H)
+    say(f"bwd N={N} S={S} d={d} H={H} T={T}: {name}")
+    assert name.startswith("bwd_fast"), name
+    wl = synth.block_workload(T=T, d=d, N=N, S=S, H=H, rep_std_step=0.3, dtype="bf16", seed=60 + N + 13 * S,
+                              with_dh=True)
+    reps, w, g, dh = dev(wl.reps, True), dev(wl.w), dev(wl.gain), dev(wl.dh, True)
+    parts = dev(wl.partials, True) if S > 1 else None
+    got = ar.attnres_bwd(reps, parts, w, dh, g, wl.eps, H)
+    ref = orc.block_bwd(wl.reps, wl.partials, wl.w, wl.gain, wl.eps, H, wl.dh)
+    check(host(got[0]), ref[0], "bf16", "d_reps")
+    if S > 1:
+        check(host(got[1]), ref[1], "bf16", "d_partials")
+    check(host(got[2]), ref[2], "f32_from_bf16", "dw")
+    check(host(got[3]), ref[3], "f32_from_bf16", "dgain")
+    # shared gain: the dgain reduction over destinations
+    g1 = (1 + 0.1 * np.random.default_rng(N).standard_normal(d)).astype(np.float32)
+    got1 = ar.attnres_bwd(reps, parts, w, dh, dev(g1), wl.eps, H)
+    ref1 = orc.block_bwd(wl.reps, wl.partials, wl.w, g1, wl.eps, H, wl.dh)
+    check(host(got1[0]), ref1[0], "bf16", "d_reps (shared gain)")
+    check(host(got1[3]), ref1[3], "f32_from_bf16", "dgain (shared gain)")
+
+
+@pytest.mark.parametrize("H", [1, 8])
+@pytest.mark.parametrize("policy", [0, 1], ids=["auto", "general"])
+def test_peaked_softmax(H, policy):
+    """Scores in the hundreds: the depth softmax is all but one-hot, and the
+    merge weight exp(lse - m) or exp(s_p - m) underflows to zero."""
+    prev = ar.attnres_set_kernel_policy(policy)
+    try:
+        wl = synth.block_workload(T=300, d=4096, N=8, S=4, H=H, rep_std_step=0.3, dtype="bf16", seed=77,
+                                  with_dh=True)
+        wbig = (wl.w * 300.0).astype(np.float32)
+        s = orc.block_phase1(wl.reps[:, :4], wbig, wl.gain, wl.eps, H)[1]
+        say(f"peaked softmax H={H} policy={policy}: |lse| up to {np.abs(s).max():.0f}")
+        assert np.abs(s).max() > 100
+        reps, w, g = dev(wl.reps, True), dev(wbig), dev(wl.gain)
+        h = ar.mhar_fwd(reps, dev(wl.partials, True), w, g, wl.eps, H)
+        ref = orc.block_direct(wl.reps, wl.partials, wbig, wl.gain, wl.eps, H)
+        assert np.all(np.isfinite(host(h)))
+        check(host(h), ref, "bf16", "peaked mhar_fwd")
+        got = ar.attnres_bwd(reps, dev(wl.partials, True), w, dev(wl.dh, True), g, wl.eps, H)
+        ref_b = orc.block_bwd(wl.reps, wl.partials, wbig, wl.gain, wl.eps, H, wl.dh)
+        check(host(got[0]), ref_b[0], "bf16", "peaked d_reps")
+        check(host(got[1]), ref_b[1], "bf16", "peaked d_partials")
+    finally:
+        ar.attnres_set_kernel_policy(prev)
