@@ -23,6 +23,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -39,7 +41,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="block", choices=["block", "mhar", "full", "bwd", "mhar_bwd", "full_bwd", "block_update",
-                                                                "decode", "msar", "block_msar"])
+                                                                "decode", "msar", "block_msar", "depth_sweep"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     p.add_argument("--ceilings", action="store_true",
@@ -486,6 +488,73 @@ def bench_bwd(args, T=8192, H=1):
                 ms_per_step=sec / n * 1e3, step_bytes=b, step_gbs=b * n / sec / 1e9)
 
 
+def bench_depth_sweep(args, T=16384, Tb=8192, d=4096):
+    """Phase 1 at every block depth (block n of a model reads N = n reps), S = 4,
+    plus the 6-sublayer block of the 54-sublayer model (N = 9, S = 6), and the
+    Block backward at N = 1..12, S = 4.  Inputs are seeded normal draws made on
+    the device (rep n with std 1 + 0.3 n); each case's kernel is timed with HIP
+    events around its launches on the stream they run on."""
+    import torch
+    import depth_wise_attention_amd as ar
+
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    stream = torch.cuda.current_stream()
+
+    def reps_of(N, TT):
+        r = torch.randn((N, TT, d), generator=gen, device="cuda")
+        r *= (1 + 0.3 * torch.arange(N, device="cuda", dtype=torch.float32))[:, None, None]
+        return r.to(torch.bfloat16)
+
+    def timed(fn, n):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / n
+
+    n = max(5, args.steps // 2)
+    phase1, bwd = [], []
+    for N, S in [(k, 4) for k in range(1, 13)] + [(9, 6)]:
+        reps = reps_of(N, T)
+        w = torch.randn((S, d), generator=gen, device="cuda") / 64
+        g = 1 + 0.1414 * torch.randn((S, d), generator=gen, device="cuda")
+        h0 = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+        st = torch.empty((S - 1, T, d), dtype=torch.float16, device="cuda")
+        lse = torch.empty((S, 1, T), device="cuda")
+        sc = torch.empty((T,), device="cuda")
+        sec = timed(lambda: ar.attnres_block_phase1(reps, w, g, 1e-6, 1, h_first=h0, o_state=st, lse=lse,
+                                                    o_scale=sc, stream=stream), n)
+        b = block_bytes(T, d, N, S, 1)[0]
+        phase1.append(dict(N=N, S=S, kernel=ar.attnres_kernel_variant(ar.OP_PHASE1, N, S, T, d, 1),
+                           us=sec * 1e6, gbs=b / sec / 1e9, frac_of_peak=b / sec / 1e9 / PEAK_HBM_GBS))
+        log(f"[bench] depth sweep phase1 {json.dumps(phase1[-1])}")
+        del reps, h0, st
+        torch.cuda.empty_cache()
+    for N in range(1, 13):
+        S = 4
+        reps = reps_of(N, Tb)
+        parts = torch.randn((S - 1, Tb, d), generator=gen, device="cuda").to(torch.bfloat16)
+        dh = torch.randn((S, Tb, d), generator=gen, device="cuda").to(torch.bfloat16)
+        w = torch.randn((S, d), generator=gen, device="cuda") / 64
+        g = 1 + 0.1414 * torch.randn((S, d), generator=gen, device="cuda")
+        outs = (torch.empty_like(reps), torch.empty_like(parts), torch.empty_like(w), torch.empty_like(g))
+        ws = torch.empty(ar.attnres_bwd_workspace_size(N, S, Tb, d, 1), dtype=torch.uint8, device="cuda")
+        sec = timed(lambda: ar.attnres_bwd(reps, parts, w, dh, g, 1e-6, 1, d_reps=outs[0], d_partials=outs[1],
+                                           dw=outs[2], dgain=outs[3], ws=ws, stream=stream), n)
+        b = bwd_bytes(Tb, d, N, S)
+        bwd.append(dict(N=N, S=S, kernel=ar.attnres_kernel_variant(ar.OP_BWD, N, S, Tb, d, 1), us=sec * 1e6,
+                        gbs=b / sec / 1e9, frac_of_peak=b / sec / 1e9 / PEAK_HBM_GBS))
+        log(f"[bench] depth sweep bwd {json.dumps(bwd[-1])}")
+        del reps, parts, dh, outs, ws
+        torch.cuda.empty_cache()
+    return dict(name=f"depth_sweep_d{d}", T_phase1=T, T_bwd=Tb, phase1=phase1, bwd=bwd)
+
+
 def full_bwd_bytes(T, d, L, es=2):
     # read src and dout, write d_src (the dw/dgain slabs are small)
     return T * d * es * (L + L + L)
@@ -518,25 +587,67 @@ def bench_full_bwd(args, T=4096):
                 ms_per_step=sec / n * 1e3, step_bytes=b, step_gbs=b * n / sec / 1e9)
 
 
-def cpu_baseline(T=16384, chunk=2048):
-    """The float64 oracle (as it stands) over the headline batch, in token chunks.
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    Tokens are independent, so chunking changes nothing but peak memory.  About
-    10 s of single-thread numpy work on a server core."""
+
+def _oracle_chunk(args):
+    """One token chunk of the headline workload through the oracle (a worker
+    process of the P-core baseline, BLAS at one thread)."""
+    reps, parts, w, gain, eps = args
+    from threadpoolctl import threadpool_limits
+    from oracle import attnres_oracle as orc
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        orc.block_direct(reps, parts, w, gain, eps, 1)
+        return time.perf_counter() - t0
+
+
+def cpu_baseline(T=16384, chunk=256, sample=4096):
+    """The float64 oracle (as it stands) on the headline block workload, on the
+    host's cores: (1) one process with BLAS pinned to one thread over a bounded
+    sample of `sample` tokens, and (2) a pool of P worker processes (P = the
+    cores this process may run on, at most 16), each with BLAS at one thread,
+    over the same sample split into token chunks.  Tokens are independent, so
+    chunking changes nothing but peak memory; tokens/s scales to the full T."""
+    from concurrent.futures import ProcessPoolExecutor
+    import multiprocessing as mp
+
+    from threadpoolctl import threadpool_limits
     from oracle import attnres_oracle as orc
     from workloads import synth
 
     wl = synth.config_block_two_phase(T=T)
-    sec = 0.0
-    for lo in range(0, T, chunk):
-        sl = slice(lo, min(T, lo + chunk))
-        reps, parts = wl.reps[:, sl], wl.partials[:, sl]
+    n = min(sample, T)
+    tasks = [(np.ascontiguousarray(wl.reps[:, lo:lo + chunk]), np.ascontiguousarray(wl.partials[:, lo:lo + chunk]),
+              wl.w, wl.gain, wl.eps) for lo in range(0, n, chunk)]
+    del wl
+    with threadpool_limits(1):
         t0 = time.perf_counter()
-        orc.block_direct(reps, parts, wl.w, wl.gain, wl.eps, 1)
-        sec += time.perf_counter() - t0
-    return dict(value=T / sec, unit="tokens/s", cores=1, kind="oracle",
-                sample=f"all {T} tokens of the d=4096 N=8 S=4 H=1 block workload in chunks of {chunk}, "
-                       f"float64 numpy oracle (plain definition), single thread, {sec:.1f} s")
+        for reps, parts, w, gain, eps in tasks:
+            orc.block_direct(reps, parts, w, gain, eps, 1)
+        one = time.perf_counter() - t0
+    P = max(1, min(16, len(os.sched_getaffinity(0)))) if hasattr(os, "sched_getaffinity") else 1
+    with ProcessPoolExecutor(P, mp_context=mp.get_context("spawn")) as ex:
+        list(ex.map(_oracle_chunk, tasks[:P]))  # start the workers and import the oracle
+        t0 = time.perf_counter()
+        list(ex.map(_oracle_chunk, tasks))
+        many = time.perf_counter() - t0
+    model = _cpu_model()
+    return dict(value=n / one, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"{n} of the {T} tokens of the d=4096 N=8 S=4 H=1 block workload in chunks of {chunk}, "
+                       f"float64 numpy oracle (plain definition), BLAS at one thread, {one:.1f} s",
+                cpu_model=model,
+                p_cores=dict(value=n / many, unit="tokens/s", cores=P, kind="oracle",
+                             sample=f"the same {n} tokens over {P} worker processes (one BLAS thread each), "
+                                    f"{many:.1f} s"))
 
 
 def copy_calibration(n=1 << 31, reps=10):
@@ -664,13 +775,14 @@ def main():
         fn = {"mhar": lambda: bench_block(args, H=8, T=32768), "full": lambda: bench_full(args),
               "bwd": lambda: bench_bwd(args), "mhar_bwd": lambda: bench_bwd(args, H=8), "full_bwd": lambda: bench_full_bwd(args),
               "block_update": lambda: bench_update(args), "decode": lambda: bench_decode(args),
-              "msar": lambda: bench_msar(args), "block_msar": lambda: bench_block_msar(args)}[args.workload]
+              "msar": lambda: bench_msar(args), "block_msar": lambda: bench_block_msar(args),
+              "depth_sweep": lambda: bench_depth_sweep(args)}[args.workload]
         log(json.dumps(fn()))
         return
 
     head = bench_block(args, cold_steps=10)
     log(f"[bench] headline: {json.dumps(head)}")
-    src_hash = kernel_source_hash("block_fast.hip", "xlane.hpp", "common.hpp")
+    src_hash = kernel_source_hash("p1_kernel.hpp", "p1_fast.hip", "xlane.hpp", "common.hpp")
     traffic = counters_for("phase1_block_T16384_d4096_N8_S4_H1", src_hash)
     p1 = head["phase1"]
     extra = {}
@@ -705,7 +817,7 @@ def main():
             "cold_cache_steps": head.get("cold"),
         },
         "roofline": {
-            "kernel": "k_phase1_fast (Block Phase 1)",
+            "kernel": "k_p1<8,4,2,false> (Block Phase 1)",
             "bound": "hbm",
             "achieved": p1["gbs"],
             "peak": PEAK_HBM_GBS,
