@@ -61,6 +61,7 @@ def lib() -> ctypes.CDLL:
         "mhar_fwd": ([vp, i64, vp, i64, i64, i64, vp, vp, i64, f32, i32, i32, vp, vp, sz, vp], ctypes.c_int),
         "mhar_fwd_chunked": ([vp, i64, vp, i64, i64, i64, vp, vp, i64, f32, i32, i32, vp, i64, vp, sz, vp],
                              ctypes.c_int),
+        "mhar_fwd_noalloc": ([vp, i64, vp, i64, i64, i64, vp, vp, i64, f32, i32, i32, vp, vp], ctypes.c_int),
         "attnres_bwd_workspace_size": ([i64, i64, i64, i64, i32], sz),
         "attnres_bwd": ([vp, i64, vp, i64, i64, i64, vp, vp, i64, f32, i32, i32, vp, vp, vp, vp, vp, i32, vp, sz,
                          vp], ctypes.c_int),
@@ -390,6 +391,17 @@ def mhar_fwd(reps, partials, w, gain=None, eps: float = 1e-6, H: int = 1, h=None
             ws = torch.empty(max(mhar_fwd_workspace_size(N, S, T, d, H), 1), dtype=torch.uint8, device=dev)
         _check(lib().mhar_fwd(_p(reps), N, _p(partials) if S > 1 else None, S, T, d, _p(w), gp, gld, eps, H,
                               _code(reps), _p(h), _p(ws), _nbytes(ws), _stream(stream)))
+    return h
+
+
+def mhar_fwd_noalloc(reps, partials, w, h, gain=None, eps: float = 1e-6, H: int = 1, stream=None):
+    """mhar_fwd with its workspace in the library's static per-device scratch:
+    the call allocates nothing (h is the caller's [S, T, d] output)."""
+    N, S, T, d, dev = _block_inputs(reps, partials, w)
+    gp, gld = _gain(gain, S, d, dev)
+    _chk(h, "h", (S, T, d), reps.dtype, dev)
+    _check(lib().mhar_fwd_noalloc(_p(reps), N, _p(partials) if S > 1 else None, S, T, d, _p(w), gp, gld, eps, H,
+                                  _code(reps), _p(h), _stream(stream)))
     return h
 
 

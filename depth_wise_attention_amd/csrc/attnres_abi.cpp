@@ -620,9 +620,38 @@ int run_block_chunk(const void* reps, int64_t N, const void* partials, int64_t S
 }
 
 // Validation shared by mhar_fwd and mhar_fwd_chunked; chunk tokens per pass.
+// The static scratch of mhar_fwd_noalloc: one array per device (each GPU
+// holds its own copy).  Host code never passes the array's name to a kernel --
+// in host code it only stands in for the symbol -- but the device address
+// hipGetSymbolAddress returns for the current device, kept per device.
+constexpr size_t kNoallocScratchBytes = (size_t)ATTNRES_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+static int noalloc_scratch(void** out) {
+  static std::mutex mu;
+  static void* ptr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(ATTNRES_ERR_UNSUPPORTED, "device %d is beyond the 64 the library tracks", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(ATTNRES_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return ATTNRES_OK;
+}
+
+// Validation shared by mhar_fwd, mhar_fwd_chunked and mhar_fwd_noalloc; chunk
+// tokens per pass.  With use_scratch the workspace is the device's static
+// scratch, resolved only after every argument has been checked.
 int mhar_common(const void* reps, int64_t N, const void* partials, int64_t S, int64_t T, int64_t d,
                 const float* w, const float* gain, int64_t gain_ld, float eps, int32_t H, int32_t dtype,
-                void* h, int64_t chunk, void* ws, size_t ws_bytes, hipStream_t stream) {
+                void* h, int64_t chunk, void* ws, size_t ws_bytes, hipStream_t stream, bool use_scratch = false) {
   int64_t td = 0;
   RETURN_IF(check_common(T, d, H, dtype, eps, gain, gain_ld, &td));
   if (N < 1 || N > kMaxSources - 1)
@@ -637,9 +666,16 @@ int mhar_common(const void* reps, int64_t N, const void* partials, int64_t S, in
   const int64_t C = chunk < T ? chunk : T;
   const size_t need = mhar_fwd_workspace_size(N, S, C, d, H);
   if (need == 0) return fail(ATTNRES_ERR_INVALID, "workspace size overflows");
-  if (ws == nullptr || ws_bytes < need)
+  if (use_scratch) {
+    if (need > kNoallocScratchBytes)
+      return fail(ATTNRES_ERR_UNSUPPORTED,
+                  "mhar_fwd_noalloc needs %zu bytes of scratch for S = %lld, H = %d, T = %lld, beyond its %zu; "
+                  "use mhar_fwd with a workspace",
+                  need, (long long)S, H, (long long)T, kNoallocScratchBytes);
+  } else if (ws == nullptr || ws_bytes < need) {
     return fail(ATTNRES_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? ws_bytes : 0,
                 need);
+  }
   const int64_t es = (int64_t)dt_size(dtype);
   size_t b_reps, b_parts, b_h;
   RETURN_IF(check_count(N, td, es, "reps", &b_reps));
@@ -649,8 +685,9 @@ int mhar_common(const void* reps, int64_t N, const void* partials, int64_t S, in
                        {partials, b_parts, "partials"},
                        {w, (size_t)(S * d * 4), "w"},
                        {gain, gain ? (size_t)((gain_ld ? S : 1) * d * 4) : 0, "gain"}};
-  const Range outs[] = {{h, b_h, "h"}, {ws, need, "ws"}};
+  const Range outs[] = {{h, b_h, "h"}, {use_scratch ? nullptr : ws, need, "ws"}};
   RETURN_IF(check_aliasing(ins, 4, outs, 2));
+  if (use_scratch) RETURN_IF(noalloc_scratch(&ws));
   for (int64_t t0 = 0; t0 < T; t0 += C) {
     const int64_t c = T - t0 < C ? T - t0 : C;
     RETURN_IF(run_block_chunk(reps, N, partials, S, T, t0, c, d, w, gain, gain_ld, eps, H, dtype, h, ws,
@@ -667,6 +704,14 @@ int mhar_fwd(const void* reps, int64_t N, const void* partials, int64_t S, int64
   clear_error();
   return mhar_common(reps, N, partials, S, T, d, w, gain, gain_ld, eps, H, dtype, h, T > 0 ? T : 1, ws,
                      ws_bytes, stream);
+}
+
+int mhar_fwd_noalloc(const void* reps, int64_t N, const void* partials, int64_t S, int64_t T, int64_t d,
+                     const float* w, const float* gain, int64_t gain_ld, float eps, int32_t H, int32_t dtype,
+                     void* h, hipStream_t stream) {
+  clear_error();
+  return mhar_common(reps, N, partials, S, T, d, w, gain, gain_ld, eps, H, dtype, h, T > 0 ? T : 1, nullptr, 0,
+                     stream, true);
 }
 
 int mhar_fwd_chunked(const void* reps, int64_t N, const void* partials, int64_t S, int64_t T, int64_t d,

@@ -230,6 +230,26 @@ int mhar_fwd_chunked(const void* reps, int64_t N, const void* partials, int64_t 
                      hipStream_t stream);
 
 /*
+ * mhar_fwd for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same launches as
+ * mhar_fwd, with the workspace -- the statistics and per-token scales, the
+ * bytes mhar_fwd_workspace_size() reports -- in a static scratch array the
+ * library owns on each device (ATTNRES_NOALLOC_SCRATCH_BYTES, held from the
+ * device's first use until the process ends).  Allocates nothing: no
+ * hipMalloc, hipFree or allocating library call.  A request needing more than
+ * the array returns ATTNRES_ERR_UNSUPPORTED before any HIP call (for S = 4,
+ * H = 1 the limit is about 400K tokens per call; chunk longer sequences or use
+ * mhar_fwd).  Every call on one device shares that device's array: calls that
+ * overlap in time on one device (other streams, concurrent graph replays)
+ * race and must not be issued.  Nothing in the array needs clearing: each
+ * call writes every value it reads.  Other arguments as for mhar_fwd.
+ */
+#define ATTNRES_NOALLOC_SCRATCH_BYTES (8u << 20)
+int mhar_fwd_noalloc(const void* reps, int64_t N, const void* partials, int64_t S, int64_t T, int64_t d,
+                     const float* w, const float* gain, int64_t gain_ld, float eps, int32_t H,
+                     int32_t dtype, void* h, hipStream_t stream);
+
+/*
  * Bytes of device workspace attnres_bwd needs (fp32 partial sums of the
  * pseudo-query gradient, one [S, d] slab per slot, min(T, 1024) slots).
  */

@@ -274,6 +274,20 @@ def test_mhar_chunked_rejects_bad_arguments():
 
 
 @fake_ptrs
+def test_noalloc_refuses_requests_beyond_its_scratch():
+    """mhar_fwd_noalloc takes no workspace; a request needing more scratch than
+    the static array is refused before any HIP call."""
+    L = binding.lib()
+    G = 1 << 30
+    call = lambda T, H: L.mhar_fwd_noalloc(FAKE, 1, FAKE + G, 4, T, 512, FAKE + 2 * G, None, 0, 1e-6, H, BF16,
+                                           FAKE + 3 * G, None)
+    assert call(70000, 8) == EUNSUP
+    assert "scratch" in binding.attnres_last_error()
+    assert L.mhar_fwd_noalloc(None, 1, None, 4, 0, 512, None, None, 0, 1e-6, 1, BF16, None, None) == OK
+    assert call(10, 3) == EINVAL  # 512 is not divisible by 3
+
+
+@fake_ptrs
 def test_mhar_rejects_workspace_over_inputs():
     assert _rc_mhar(ws=FAKE + 64) == EINVAL
 
