@@ -386,7 +386,8 @@ int attnres_kernel_variant(int32_t op, int64_t N, int64_t S, int64_t T, int64_t 
       FullBwdArgs a{p, N, T, d, fp, S, fp, d, 1e-6f, H, dtype, p, p, static_cast<float*>(p),
                     static_cast<float*>(p), 0, static_cast<float*>(p), T > 0 ? full_bwd_slots(T) : 0,
                     attnres_full_bwd_workspace_size(N, S, T, d, H)};
-      snprintf(buf, len, "%s", fast && full_bwd_fast_ok(a) ? "full_bwd_fast" : "full_bwd_generic");
+      const char* v = fast ? full_bwd_fast_variant(a) : nullptr;
+      snprintf(buf, len, "%s", v ? v : "full_bwd_generic");
       return ATTNRES_OK;
     }
     default:

@@ -1,5 +1,6 @@
 // Specialised Full AttnRes backward for gfx950 (bf16 I/O, H = 1, up to 32
-// sources and destinations, d a multiple of 512).
+// sources and destinations; d = 1024 .. 2048 in steps of 256 on the
+// register-resident kernel, else d a multiple of 512).
 //
 // The pages give no backward; these kernels evaluate the chain rule through
 // the Full forward (b-lab.team summary §1) for L = sum_j <dout_j, out_j>.  Per
@@ -23,6 +24,9 @@
 // them again (from cache).
 #include <math.h>
 
+#include <algorithm>
+#include <atomic>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "xlane.hpp"
@@ -35,10 +39,18 @@ constexpr int kBW = 4;            // waves per workgroup
 constexpr int kBB = kBW * 64;     // threads per workgroup
 constexpr int kZGroups = 64;      // token groups of the Z kernel (slabs)
 
+// Channel position (0..31 within a 32-channel block) that row m of a
+// transposed tile holds when the transpose multiplies by the permuted
+// identity of res_ident (below); the identity is res_ident's without PERM.
+__host__ __device__ constexpr int res_pos(int m) { return 16 * ((m & 7) >> 2) + 4 * (m >> 3) + (m & 3); }
+
 // Q^T in A-operand order with the destination index inside the lane: for
 // 32-channel tile c, k-step b and part p (0 = bf16 high, 1 = low), lane (h, n)
-// holds q_p[transposed_row(b, h, e)][32 c + n], e = 0..7, at
-// qt[((c * 2 + b) * 2 + p) * 64 + lane].  Rows past n_dst are zero.
+// holds q_p[transposed_row(b, h, e)][32 c + pos(n)], e = 0..7, at
+// qt[((c * 2 + b) * 2 + p) * 64 + lane], with pos(n) = n, or res_pos(n) for
+// the register-resident kernel's permuted transposes (PERM).  Rows past n_dst
+// are zero.
+template <bool PERM>
 __global__ __launch_bounds__(256) void k_full_qtsplit(FullBwdArgs a, uint4* qt) {
   const int64_t units = a.d / 32 * 2 * 64;  // (tile, b, lane)
   for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < units;
@@ -46,7 +58,7 @@ __global__ __launch_bounds__(256) void k_full_qtsplit(FullBwdArgs a, uint4* qt) 
     const int lane = (int)(x % 64), h = lane >> 5, n = lane & 31;
     const int b = (int)((x / 64) % 2);
     const int64_t c = x / 128;
-    const int64_t k = 32 * c + n;
+    const int64_t k = 32 * c + (PERM ? res_pos(n) : n);
     // Unconditional loads (rows past n_dst read row n_dst - 1, then store zero)
     // so the 16 loads are in flight together.
     const bool has_g = a.gain != nullptr;
@@ -490,6 +502,443 @@ __global__ __launch_bounds__(64) void k_full_bwd_z(FullBwdArgs a, const float* c
   }
 }
 
+// ---------------------------------------------------------------------------
+// Register-resident variant (d = 1024 .. 2048 in steps of 256): a workgroup of
+// d / 256 waves owns one token at a time, wave w channels 256 w .. 256 w + 255.
+// Lane (h, r) holds, for each of the wave's 16 k-steps s, channels
+// 256 w + 16 s + 8 h .. + 7 of source row r and of upstream-gradient row r in
+// registers: exactly the stage-1 B operand of V^T and A operand of dOut.  Stage
+// 1 runs from them, and stage 2 transposes them from the same registers, so
+// each byte of the sources and of dout crosses HBM once.  After stage 2 the
+// registers are refilled with the next token's rows.
+//
+// Stage 2 transposes with a permuted identity: row m of a transposed tile is
+// channel position res_pos(m) of its block, so that the 16 accumulator rows of
+// lane (h, i), m = 8 (r / 4) + 4 h + r % 4, are the 16 consecutive channels
+// 16 h .. 16 h + 15 of the block, and dV leaves the accumulators as two
+// 16-byte stores per lane.
+
+constexpr int kRK = 16;            // k-steps per wave
+constexpr int kRCh = 16 * kRK;     // channels per wave
+
+// res_ident(a2): the B operand of k-step a2 of the permuted transpose,
+// I[k][n] = 1 when n is the row that holds channel position 16 a2 + k, i.e.
+// res_pos(n) == 16 a2 + k.
+__device__ __forceinline__ uint4 res_ident(int a2) {
+  const int lane = lane_id(), hb = lane >> 5, n = lane & 31;
+  const int p = res_pos(n) - 16 * a2 - 8 * hb;  // element holding the one, if in 0..7
+  uint32_t wds[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t lo16 = p == 2 * q ? 0x3F80u : 0u;
+    const uint32_t hi16 = p == 2 * q + 1 ? 0x3F80u : 0u;
+    wds[q] = lo16 | (hi16 << 16);
+  }
+  return make_uint4(wds[0], wds[1], wds[2], wds[3]);
+}
+
+// LDS of the resident kernel for W waves: per-wave partials of S and A
+// (32 x 32 each) and of the sums of squares, then the per-token tables.
+struct ResLds {
+  int W;
+  __device__ float* sred(char* base, int w) const { return reinterpret_cast<float*>(base) + w * kTile * kTile; }
+  __device__ float* ared(char* base, int w) const {
+    return reinterpret_cast<float*>(base) + (W + w) * kTile * kTile;
+  }
+  // The whole 32 x 32 partial of G = V V^T (its diagonal holds the sums of squares).
+  __device__ float* gred(char* base, int w) const {
+    return reinterpret_cast<float*>(base) + (2 * W + w) * kTile * kTile;
+  }
+  __device__ float* table(char* base, int k) const {  // alpha (0), r c (1), c s (2): [32][kARow]
+    return reinterpret_cast<float*>(base) + 3 * W * kTile * kTile + k * kTile * kARow;
+  }
+  __device__ float* coef(char* base) const { return table(base, 3); }
+  static size_t bytes(int W) { return (size_t)4 * (3 * W * kTile * kTile + 3 * kTile * kARow + kTile); }
+};
+
+// 16-byte load at byte voff + soff of a buffer whose base is uniform over the
+// wave: the base and the (constant) soff live in scalar registers.
+__device__ __forceinline__ uint4 res_ld(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+  const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t res_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, kBufferWord3);
+}
+
+template <bool ACC>
+__global__ __launch_bounds__(512, 1) void k_full_bwd_res(FullBwdArgs a, const uint4* qpk, const uint4* qt,
+                                                          float* cws) {
+  extern __shared__ __attribute__((aligned(16))) char res_smem[];
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: the wave's buffer bases stay scalar
+  const int W = (int)blockDim.x >> 6;
+  const ResLds L{W};
+  const int d = (int)a.d, n_src = (int)a.n_src, n_dst = (int)a.n_dst;
+  const int64_t T = a.T;
+  const bf16_t* src = static_cast<const bf16_t*>(a.src);
+  const bf16_t* dout = static_cast<const bf16_t*>(a.dout);
+  bf16_t* dsrc = static_cast<bf16_t*>(a.d_src);
+  const int ch0 = wave * kRCh;
+  const int h = lane >> 5, n = lane & 31;
+  // Whole-row loads: instruction u of lane l reads 16-byte piece l % 8 of
+  // row 8 u + l / 8 of a 64-channel chunk (8 rows x 128 bytes per
+  // instruction).  Rows past n_src (n_dst) repeat the last real row; the
+  // tables give them zero weight and their gradients are not stored.  The
+  // token's rows start at a scalar base (src + t d); the per-lane byte offsets
+  // below fit 32 bits (checked when the kernel is chosen).
+  // Row 8 u + l / 8 is at voff0 + u * row8 bytes, or at the clamped row's
+  // offset when past the last real row.
+  const int r0 = lane >> 3;
+  const int64_t cbase = ch0 + 8 * (lane & 7);
+  const uint32_t row8 = (uint32_t)(8 * T * d * 2);
+  const uint32_t voff0 = (uint32_t)(((int64_t)r0 * T * d + cbase) * 2);
+  const uint32_t vclamp = (uint32_t)(((int64_t)(n_src - 1) * T * d + cbase) * 2);
+  const uint32_t dclamp = (uint32_t)(((int64_t)(n_dst - 1) * T * d + cbase) * 2);
+  auto voff = [&](int u) { return 8 * u + r0 < n_src ? voff0 + (uint32_t)u * row8 : vclamp; };
+  auto doff = [&](int u) { return 8 * u + r0 < n_dst ? voff0 + (uint32_t)u * row8 : dclamp; };
+  // Query operands of this wave's k-steps and 32-channel blocks: k-step s at
+  // byte 2048 s (+ 1024 for the low part), block b2 at 4096 b2 (+ 1024 per
+  // operand), lane at 16 lane.
+  const __amdgpu_buffer_rsrc_t qrs = res_rsrc(qpk + (int64_t)(ch0 / 16) * 2 * 64);
+  const __amdgpu_buffer_rsrc_t qtrs = res_rsrc(qt + (int64_t)(ch0 / 32) * 4 * 64);
+  const uint32_t loff = (uint32_t)lane * 16u;
+  const uint4 ip0 = res_ident(0), ip1 = res_ident(1);
+
+  // vr / dr hold the token's rows: as loaded (chunk c in registers 4 c .. 4 c
+  // + 3, instruction order) until stage 1 re-lays each chunk, through this
+  // wave's LDS tiles, into operand order (register 4 c + s = k-step s).
+  uint4 vr[kRK], dr[kRK];
+  auto load_rows = [&](int64_t t) {
+    const __amdgpu_buffer_rsrc_t vrs = res_rsrc(src + t * d), drs = res_rsrc(dout + t * d);
+#pragma unroll
+    for (int c = 0; c < kRK / 4; ++c)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        vr[4 * c + u] = res_ld(vrs, voff(u) + 128u * c, 0);
+        dr[4 * c + u] = res_ld(drs, doff(u) + 128u * c, 0);
+      }
+  };
+  if ((int64_t)blockIdx.x < T) load_rows(blockIdx.x);
+
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    const int64_t tn = t + gridDim.x;
+    const bool more = tn < T;
+
+    // ---------------- stage 1: S = Q V^T, G = V V^T, A = dOut V^T over this wave's channels
+    // The query operands stream from L2 two k-steps ahead; fences keep the
+    // compiler from issuing all of them at once (they would need 128 registers
+    // beside the resident rows).
+    f16acc S = {}, G = {}, A = {};
+    {
+      uint4 qh[kRK], ql[kRK];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        qh[s] = res_ld(qrs, loff, 2048 * s);
+        ql[s] = res_ld(qrs, loff, 2048 * s + 1024);
+      }
+      // This wave's staging tiles: the partial-sum rows of S and G, unused
+      // until the partials are written (after a barrier).
+      unsigned char* vt = reinterpret_cast<unsigned char*>(L.sred(res_smem, wave));
+      unsigned char* dt = reinterpret_cast<unsigned char*>(L.gred(res_smem, wave));
+#pragma unroll
+      for (int s = 0; s < kRK; ++s) {
+        if (s % 4 == 0) {
+          // Re-lay chunk s / 4 into operand order.  The swizzled addresses come
+          // from an opaque lane id, so they are recomputed here rather than
+          // held (spilled) across the token loop.
+          const int c = s / 4;
+          int ol = lane;
+          asm volatile("" : "+v"(ol));
+          const int wb = vpos(ol >> 3, ol & 7);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            *reinterpret_cast<uint4*>(vt + wb + u * 8 * kVRow) = vr[4 * c + u];
+            *reinterpret_cast<uint4*>(dt + wb + u * 8 * kVRow) = dr[4 * c + u];
+          }
+          wave_lds_sync();
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int rb = vpos(ol & 31, 2 * k + (ol >> 5));
+            vr[4 * c + k] = *reinterpret_cast<const uint4*>(vt + rb);
+            dr[4 * c + k] = *reinterpret_cast<const uint4*>(dt + rb);
+          }
+          wave_lds_sync();
+        }
+        if (s + 2 < kRK) {
+          qh[s + 2] = res_ld(qrs, loff, 2048 * (s + 2));
+          ql[s + 2] = res_ld(qrs, loff, 2048 * (s + 2) + 1024);
+        }
+        S = mfma(qh[s], vr[s], S);
+        S = mfma(ql[s], vr[s], S);
+        G = mfma(vr[s], vr[s], G);
+        A = mfma(dr[s], vr[s], A);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // The A partials share LDS with nothing, but the tables below are read by
+    // the previous token's stage 2: every wave must be past it.
+    lds_barrier();
+    {
+      // Element r of lane (h, n) is row 8 (r / 4) + 4 h + r % 4, column n: one
+      // per-lane base (row 4 h, column n) plus constant offsets.
+      int rl = lane;
+      asm volatile("" : "+v"(rl));
+      const int base = 4 * (rl >> 5) * kTile + (rl & 31);
+      float* sr = L.sred(res_smem, wave) + base;
+      float* ar = L.ared(res_smem, wave) + base;
+      float* gr = L.gred(res_smem, wave) + base;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = (8 * (r / 4) + (r % 4)) * kTile;
+        sr[off] = S[r];
+        ar[off] = A[r];
+        gr[off] = G[r];
+      }
+    }
+    lds_barrier();
+
+    // ---------------- per (destination, source): alpha, c, r c, c s (threads 0..255)
+    float* t_alpha = L.table(res_smem, 0);
+    float* t_rc = L.table(res_smem, 1);
+    float* t_cs = L.table(res_smem, 2);
+    float* coefp = L.coef(res_smem);
+    if (tid < 256) {
+      const int j = tid / 8, i0 = 4 * (tid % 8);
+      const int lim = n_src - n_dst + j;
+      float sc[4], av[4], rr[4];
+      bool ok[4];
+      float m = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = i0 + q;
+        float sv = 0.f, aa = 0.f, gv = 0.f;
+        for (int w2 = 0; w2 < W; ++w2) {
+          sv += L.sred(res_smem, w2)[j * kTile + i];
+          aa += L.ared(res_smem, w2)[j * kTile + i];
+          gv += L.gred(res_smem, w2)[i * kTile + i];
+        }
+        rr[q] = 1.0f / sqrtf(gv / (float)d + a.eps);
+        ok[q] = j < n_dst && i <= lim;
+        sc[q] = ok[q] ? rr[q] * sv : -INFINITY;
+        av[q] = aa;
+        m = fmaxf(m, sc[q]);
+      }
+      m = group_max<8>(m);
+      float e[4], l = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        e[q] = ok[q] ? expf(sc[q] - m) : 0.f;
+        l += e[q];
+      }
+      l = group_sum<8>(l);
+      const float inv = l > 0.f ? 1.0f / l : 0.f;
+      float al[4], sa = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        al[q] = e[q] * inv;
+        sa = fmaf(al[q], av[q], sa);
+      }
+      sa = group_sum<8>(sa);
+      float rcv[4], csv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float cc = al[q] * (av[q] - sa);
+        rcv[q] = ok[q] ? rr[q] * cc : 0.f;
+        csv[q] = ok[q] ? cc * sc[q] : 0.f;
+      }
+      *reinterpret_cast<float4*>(&t_alpha[j * kARow + i0]) = make_float4(al[0], al[1], al[2], al[3]);
+      *reinterpret_cast<float4*>(&t_rc[j * kARow + i0]) = make_float4(rcv[0], rcv[1], rcv[2], rcv[3]);
+      *reinterpret_cast<float4*>(&t_cs[j * kARow + i0]) = make_float4(csv[0], csv[1], csv[2], csv[3]);
+      // r c for the Z kernel: [T][32][32] fp32.
+      *reinterpret_cast<float4*>(cws + t * (kTile * kTile) + j * kTile + i0) =
+          make_float4(rcv[0], rcv[1], rcv[2], rcv[3]);
+    }
+    lds_barrier();
+    if (tid < kTile) {
+      const int i = tid;
+      float cs = 0.f, gv = 0.f;
+      for (int j = 0; j < kTile; ++j) cs += t_cs[j * kARow + i];
+      for (int w2 = 0; w2 < W; ++w2) gv += L.gred(res_smem, w2)[i * kTile + i];
+      const float r2 = 1.0f / (gv / (float)d + a.eps);
+      coefp[i] = i < n_src ? r2 * cs / (float)d : 0.f;
+    }
+    lds_barrier();
+
+    // ---------------- stage 2 B operands, built once per token (into the A
+    // partials' space, dead now): lane (h, n = source i), element e <-> row
+    // k = transposed_row(b, h, e) of alpha[k][i] (slots 0..3), (r c)[k][i]
+    // (4..7) and diag(-coef) (8..11), each split into bf16 high and low parts.
+    const uint4* bpk_r = reinterpret_cast<const uint4*>(L.ared(res_smem, 0));
+    uint4* bpk = reinterpret_cast<uint4*>(L.ared(res_smem, 0));
+    {
+      auto store_split = [&](const float (&x)[8], int slot) {
+        float hi[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          hi[e] = bf2f(f2bf(x[e]));
+          lo[e] = x[e] - hi[e];
+        }
+        bpk[slot * 64 + lane] = pack8(hi[0], hi[1], hi[2], hi[3], hi[4], hi[5], hi[6], hi[7]);
+        bpk[(slot + 1) * 64 + lane] = pack8(lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]);
+      };
+      if (wave < 2) {
+        const float* base = (wave == 0 ? t_alpha : t_rc) + 4 * h * kARow + n;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = base[(16 * b + 8 * (e / 4) + (e % 4)) * kARow];
+          store_split(x, 4 * wave + 2 * b);
+        }
+      } else if (wave == 2) {
+        const float cn = -coefp[n];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = transposed_row(b, h, e) == n ? cn : 0.f;
+          store_split(x, 8 + 2 * b);
+        }
+      }
+    }
+    lds_barrier();
+
+    // ---------------- stage 2: dV^T = dOut^T alpha^T + Q^T (r c)^T - V^T diag(coef), per 32 channels
+    // Block b uses the rows in registers 2 b, 2 b + 1 of vr and dr.  Every L2
+    // load (the Q^T operands) is issued before the first load of the next
+    // token's rows: the vector-memory counter retires in order, so a Q^T load
+    // issued after such a prefetch would wait for an HBM round trip.  Blocks
+    // 0..3 load the next block's Q^T after their own last use of it and park
+    // the Q^T of blocks 4..7 in their own freed registers; after each of
+    // blocks 4..7 the
+    // registers of that block and of the block four earlier are free, and the
+    // next token's rows go into them (register x of vr / dr holds instruction
+    // x % 4 of chunk x / 4, so the refill needs no other bookkeeping).
+    // dV is staged through this wave's LDS tile (a 64-channel chunk at a
+    // time) and leaves as whole-row stores.
+    {
+      unsigned char* ot = reinterpret_cast<unsigned char*>(L.sred(res_smem, wave));
+      const __amdgpu_buffer_rsrc_t ors = res_rsrc(dsrc + t * d);
+      const __amdgpu_buffer_rsrc_t nvrs = res_rsrc(src + (more ? tn : t) * d);
+      const __amdgpu_buffer_rsrc_t ndrs = res_rsrc(dout + (more ? tn : t) * d);
+      auto refill = [&](int x) {
+        vr[x] = res_ld(nvrs, voff(x % 4) + 128u * (x / 4), 0);
+        dr[x] = res_ld(ndrs, doff(x % 4) + 128u * (x / 4), 0);
+      };
+      uint4 qc[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) qc[k] = res_ld(qtrs, loff, 1024 * k);
+#pragma unroll
+      for (int b2 = 0; b2 < kRK / 2; ++b2) {
+        const int s0 = 2 * b2, s1 = 2 * b2 + 1;
+        // The tables are the same for every block: an opaque offset keeps the
+        // compiler from loading them once and holding 48 registers.
+        int boff = lane;
+        asm volatile("" : "+v"(boff));
+        const uint4* bl = bpk + boff;
+        f16acc D = {};
+        {
+          f16acc D3 = {};
+          D3 = mfma(dr[s0], ip0, D3);
+          D3 = mfma(dr[s1], ip1, D3);
+          const uint4 td0 = pack8(D3[0], D3[1], D3[2], D3[3], D3[4], D3[5], D3[6], D3[7]);
+          const uint4 td1 = pack8(D3[8], D3[9], D3[10], D3[11], D3[12], D3[13], D3[14], D3[15]);
+          D = mfma(td0, bl[0 * 64], D);   // alpha, b = 0, hi
+          D = mfma(td0, bl[1 * 64], D);   //               lo
+          D = mfma(td1, bl[2 * 64], D);   // alpha, b = 1, hi
+          D = mfma(td1, bl[3 * 64], D);   //               lo
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        {
+          f16acc D1 = {};
+          D1 = mfma(vr[s0], ip0, D1);
+          D1 = mfma(vr[s1], ip1, D1);
+          const uint4 tv0 = pack8(D1[0], D1[1], D1[2], D1[3], D1[4], D1[5], D1[6], D1[7]);
+          const uint4 tv1 = pack8(D1[8], D1[9], D1[10], D1[11], D1[12], D1[13], D1[14], D1[15]);
+          D = mfma(tv0, bl[8 * 64], D);   // -coef, b = 0
+          D = mfma(tv0, bl[9 * 64], D);
+          D = mfma(tv1, bl[10 * 64], D);  // -coef, b = 1
+          D = mfma(tv1, bl[11 * 64], D);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        {
+          // Q^T of this block: in flight (blocks 0..3) or parked in the
+          // registers of block b2 - 4 (blocks 4..7).
+          uint4 q0h, q0l, q1h, q1l;
+          if (b2 < 4) {
+            q0h = qc[0]; q0l = qc[1]; q1h = qc[2]; q1l = qc[3];
+          } else {
+            const int p = b2 - 4;
+            q0h = dr[2 * p]; q0l = dr[2 * p + 1]; q1h = vr[2 * p]; q1l = vr[2 * p + 1];
+          }
+          D = mfma(q0h, bl[4 * 64], D);   // r c, b = 0: (q_hi + q_lo)(rc_hi + rc_lo) less lo * lo
+          D = mfma(q0h, bl[5 * 64], D);
+          D = mfma(q0l, bl[4 * 64], D);
+          D = mfma(q1h, bl[6 * 64], D);   // r c, b = 1
+          D = mfma(q1h, bl[7 * 64], D);
+          D = mfma(q1l, bl[6 * 64], D);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (b2 < 4) {
+          // The next block's Q^T (its other products cover the latency), and
+          // the Q^T of block b2 + 4 parked in this block's freed registers.
+          if (b2 + 1 < 4) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) qc[k] = res_ld(qtrs, loff, 4096 * (b2 + 1) + 1024 * k);
+          }
+          dr[s0] = res_ld(qtrs, loff, 4096 * (b2 + 4));
+          dr[s1] = res_ld(qtrs, loff, 4096 * (b2 + 4) + 1024);
+          vr[s0] = res_ld(qtrs, loff, 4096 * (b2 + 4) + 2048);
+          vr[s1] = res_ld(qtrs, loff, 4096 * (b2 + 4) + 3072);
+        } else if (more) {
+          refill(2 * (b2 - 4));
+          refill(2 * (b2 - 4) + 1);
+          refill(s0);
+          refill(s1);
+        }
+        // Element r of lane (h, i) is channel 32 (b2 % 2) + 16 h + r of the
+        // chunk: two 16-byte pieces of tile row i.
+        int ol = lane;
+        asm volatile("" : "+v"(ol));
+        {
+          const int on = ol & 31, piece = 4 * (b2 & 1) + 2 * (ol >> 5);
+          *reinterpret_cast<uint4*>(ot + vpos(on, piece)) = pack8(D[0], D[1], D[2], D[3], D[4], D[5], D[6], D[7]);
+          *reinterpret_cast<uint4*>(ot + vpos(on, piece + 1)) =
+              pack8(D[8], D[9], D[10], D[11], D[12], D[13], D[14], D[15]);
+        }
+        if (b2 & 1) {
+          // The chunk's tile is complete: whole-row stores, instruction u of
+          // lane l writing piece l % 8 of row 8 u + l / 8 (rows past n_src
+          // are not stored).
+          const int c = b2 >> 1;
+          wave_lds_sync();
+          const int rb = vpos(ol >> 3, ol & 7);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int row = 8 * u + (ol >> 3);
+            uint4 y = *reinterpret_cast<const uint4*>(ot + rb + u * 8 * kVRow);
+            if (row < n_src) {
+              const uint32_t off = voff(u) + 128u * c;
+              if constexpr (ACC) {
+                const uint4 o = res_ld(ors, off, 0);
+                const uint32_t yw[4] = {y.x, y.y, y.z, y.w}, ow[4] = {o.x, o.y, o.z, o.w};
+                uint32_t rw[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                  rw[k] = pack_bf2(bf_lo(yw[k]) + bf_lo(ow[k]), bf_hi(yw[k]) + bf_hi(ow[k]));
+                y = make_uint4(rw[0], rw[1], rw[2], rw[3]);
+              }
+              __builtin_amdgcn_raw_buffer_store_b128(v4u{y.x, y.y, y.z, y.w}, ors, (int)off, 0, 0);
+            }
+          }
+          wave_lds_sync();  // the tile is rewritten by the next chunk
+        }
+      }
+    }
+  }
+}
+
 bool al16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
 
 int64_t z_groups(int64_t T) { return T < kZGroups ? T : kZGroups; }
@@ -501,12 +950,25 @@ size_t full_bwd_fast_workspace_bytes(int64_t n_dst, int64_t T, int64_t d) {
   return (size_t)256 * (size_t)d + (size_t)T * kTile * kTile * 4 + (size_t)z_groups(T) * n_dst * d * 4;
 }
 
+// The register-resident kernel: d = 1024 .. 2048 in steps of 256 (d / 256
+// waves of 256 channels each).
+bool full_bwd_res_ok(const FullBwdArgs& a) {
+  // Per-lane byte offsets of the rows from a token's base are 32-bit.
+  const int64_t span = std::max(a.n_src, a.n_dst) * a.T * a.d * 2;
+  return a.d >= 1024 && a.d <= 2048 && a.d % 256 == 0 && span < ((int64_t)1 << 31);
+}
+
 bool full_bwd_fast_ok(const FullBwdArgs& a) {
   if (a.dtype != kBF16 || a.H != 1 || a.T < 1) return false;
   if (a.n_src > kTile || a.n_dst > a.n_src) return false;
-  if (a.d % (2 * kBW * kChunk) != 0 || a.d > ((int64_t)1 << 16)) return false;
+  if ((!full_bwd_res_ok(a) && a.d % (2 * kBW * kChunk) != 0) || a.d > ((int64_t)1 << 16)) return false;
   if (a.zslots == nullptr || a.ws_bytes < full_bwd_fast_workspace_bytes(a.n_dst, a.T, a.d)) return false;
   return al16(a.src) && al16(a.dout) && al16(a.d_src) && al16(a.zslots) && al16(a.w) && al16(a.gain);
+}
+
+const char* full_bwd_fast_variant(const FullBwdArgs& a) {
+  if (!full_bwd_fast_ok(a)) return nullptr;
+  return full_bwd_res_ok(a) ? "full_bwd_res" : "full_bwd_fast";
 }
 
 hipError_t launch_full_bwd_fast(const FullBwdArgs& a, const float** slabs, int64_t* n_slabs, hipStream_t st) {
@@ -516,7 +978,35 @@ hipError_t launch_full_bwd_fast(const FullBwdArgs& a, const float** slabs, int64
   float* cws = reinterpret_cast<float*>(ws + 256 * a.d);
   float* zs = cws + a.T * kTile * kTile;
   hipLaunchKernelGGL(k_full_bwd_qsplit, dim3(64), dim3(256), 0, st, a, qpk);
-  hipLaunchKernelGGL(k_full_qtsplit, dim3(64), dim3(256), 0, st, a, qt);
+  if (full_bwd_res_ok(a)) {
+    hipLaunchKernelGGL(k_full_qtsplit<true>, dim3(64), dim3(256), 0, st, a, qt);
+    const int W = (int)(a.d / kRCh);
+    const size_t lds = ResLds::bytes(W);
+    auto kern = a.accumulate ? k_full_bwd_res<true> : k_full_bwd_res<false>;
+    static std::atomic<bool> allowed[2] = {false, false};
+    if (!allowed[a.accumulate ? 1 : 0].load(std::memory_order_relaxed)) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)ResLds::bytes(2048 / kRCh));
+      if (e != hipSuccess) return e;
+      allowed[a.accumulate ? 1 : 0].store(true, std::memory_order_relaxed);
+    }
+    int per_cu = 0;
+    const hipError_t e = blocks_per_cu(reinterpret_cast<const void*>(kern), W * 64, &per_cu, lds);
+    if (e != hipSuccess) return e;
+    if (per_cu < 1) per_cu = 1;
+    int64_t grid = (int64_t)num_cus() * per_cu;
+    if (grid > a.T) grid = a.T;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(W * 64), lds, st, a, (const uint4*)qpk, (const uint4*)qt,
+                       cws);
+    const int groups = (int)z_groups(a.T);
+    hipLaunchKernelGGL(k_full_bwd_z, dim3((unsigned)(a.d / kChunk), (unsigned)groups), dim3(64), 0, st, a,
+                       (const float*)cws, zs, groups);
+    *slabs = zs;
+    *n_slabs = groups;
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(k_full_qtsplit<false>, dim3(64), dim3(256), 0, st, a, qt);
   int per_cu = 0;
   hipError_t e = a.accumulate
                      ? blocks_per_cu(reinterpret_cast<const void*>(k_full_bwd_fast<true>), kBB, &per_cu)

@@ -165,6 +165,8 @@ hipError_t launch_full_bwd_reduce(const FullBwdArgs& a, const float* slabs, int6
 // Matrix-core Full backward (bf16, H = 1, n_src <= 32, d % 512 == 0); leaves
 // its Z slabs at *slabs (n_slabs of them) inside the workspace.
 bool full_bwd_fast_ok(const FullBwdArgs& a);
+// Name of the specialised Full backward variant a call runs (nullptr: the general kernel).
+const char* full_bwd_fast_variant(const FullBwdArgs& a);
 size_t full_bwd_fast_workspace_bytes(int64_t n_dst, int64_t T, int64_t d);
 hipError_t launch_full_bwd_fast(const FullBwdArgs& a, const float** slabs, int64_t* n_slabs, hipStream_t st);
 

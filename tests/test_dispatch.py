@@ -93,7 +93,12 @@ def test_phase2_full_and_policy():
     assert variant(binding.OP_PHASE2, 8, 4, 100, 1024) == "phase2_generic"
     assert variant(binding.OP_FULL_FWD, 32, 32, 100, 2048) == "full_fast"
     assert variant(binding.OP_FULL_FWD, 33, 33, 100, 2048) == "full_generic"
-    assert variant(binding.OP_FULL_BWD, 32, 32, 100, 2048) == "full_bwd_fast"
+    assert variant(binding.OP_FULL_BWD, 32, 32, 100, 2048) == "full_bwd_res"
+    for d in (1024, 1280, 1536, 1792):
+        assert variant(binding.OP_FULL_BWD, 17, 5, 100, d) == "full_bwd_res"
+    assert variant(binding.OP_FULL_BWD, 32, 32, 100, 4096) == "full_bwd_fast"
+    assert variant(binding.OP_FULL_BWD, 32, 32, 100, 512) == "full_bwd_fast"
+    assert variant(binding.OP_FULL_BWD, 33, 33, 100, 2048) == "full_bwd_generic"
     prev = binding.attnres_set_kernel_policy(1)
     try:
         assert phase1(8, 4, 4096) == "phase1_generic"

@@ -8,6 +8,8 @@ is compared with the oracle on the same seeded inputs:
     every width class (d = 512 .. 8192, one or two chunks per thread), and
     heads of whole 512-channel segments;
   * the Block backward for N = 1..12, S = 1..4, widths and heads;
+  * the Full backward's register-resident kernel (d = 1024 .. 2048) and the
+    staged one, over source / destination counts, gains and accumulation;
   * a sharply peaked depth softmax (scores in the hundreds), where the
     merge's exp(lse - m) underflows to zero.
 
@@ -147,3 +149,55 @@ def test_peaked_softmax(H, policy):
         check(host(got[1]), ref_b[1], "bf16", "peaked d_partials")
     finally:
         ar.attnres_set_kernel_policy(prev)
+
+
+# (T, d, L, n_dst, gain, kernel)
+FULL_BWD_CASES = [
+    (300, 2048, 32, 32, "per", "full_bwd_res"),
+    (517, 1024, 17, 5, "shared", "full_bwd_res"),
+    (403, 1280, 9, 9, "none", "full_bwd_res"),
+    (300, 1536, 32, 1, "per", "full_bwd_res"),
+    (290, 1792, 1, 1, "per", "full_bwd_res"),
+    (261, 2048, 20, 13, "shared", "full_bwd_res"),
+    (40, 4096, 32, 32, "per", "full_bwd_fast"),
+    (333, 512, 12, 7, "per", "full_bwd_fast"),
+]
+
+
+def _gain_arg(wl, gain, n_dst, d):
+    if gain == "none":
+        return None
+    if gain == "shared":
+        return (1 + 0.1 * np.random.default_rng(d).standard_normal(d)).astype(np.float32)
+    return wl.gain
+
+
+@pytest.mark.parametrize("T,d,L,n_dst,gain,kernel", FULL_BWD_CASES)
+def test_full_bwd_variant(T, d, L, n_dst, gain, kernel):
+    name = ar.attnres_kernel_variant(ar.OP_FULL_BWD, L, n_dst, T, d, 1)
+    say(f"full bwd T={T} d={d} L={L} n_dst={n_dst} gain={gain}: {name}")
+    assert name == kernel, name
+    wl = synth.full_workload(T=T, d=d, L=L, std_step=0.2, dtype="bf16", seed=90 + L + n_dst, gain_variance=0.02,
+                             n_dst=n_dst, with_dout=True)
+    g = _gain_arg(wl, gain, n_dst, d)
+    ref = orc.full_bwd(wl.src, wl.w, g, wl.eps, 1, wl.dh)
+    src, w, dout = dev(wl.src, True), dev(wl.w), dev(wl.dh, True)
+    gd = dev(g) if g is not None else None
+    got = ar.attnres_full_bwd(src, w, dout, gd, wl.eps, 1)
+    check(host(got[0]), ref[0], "bf16", "d_src")
+    check(host(got[1]), ref[1], "f32_from_bf16", "dw")
+    if g is not None:
+        check(host(got[2]), ref[2], "f32_from_bf16", "dgain")
+    # accumulate: the gradient is added in fp32 to the given d_src before one rounding
+    rng = np.random.default_rng(T)
+    base = synth.bf16_round(rng.standard_normal(wl.src.shape).astype(np.float32))
+    d_src = dev(base, True)
+    ar.attnres_full_bwd(src, w, dout, gd, wl.eps, 1, d_src=d_src, accumulate=True)
+    check(host(d_src), base + ref[0], "bf16", "d_src accumulated")
+    # the general kernel on the same inputs: the same d_src within the bar
+    prev = ar.attnres_set_kernel_policy(1)
+    try:
+        gen = ar.attnres_full_bwd(src, w, dout, gd, wl.eps, 1)
+    finally:
+        ar.attnres_set_kernel_policy(prev)
+    check(host(gen[0]), ref[0], "bf16", "d_src (general kernel)")
