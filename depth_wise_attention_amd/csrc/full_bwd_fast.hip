@@ -552,7 +552,6 @@ struct ResLds {
   __device__ float* table(char* base, int k) const {  // alpha (0), r c (1), c s (2): [32][kARow]
     return reinterpret_cast<float*>(base) + 3 * W * kTile * kTile + k * kTile * kARow;
   }
-  __device__ float* coef(char* base) const { return table(base, 3); }
   static size_t bytes(int W) { return (size_t)4 * (3 * W * kTile * kTile + 3 * kTile * kARow + kTile); }
 };
 
@@ -702,26 +701,31 @@ __global__ __launch_bounds__(512, 1) void k_full_bwd_res(FullBwdArgs a, const ui
     float* t_alpha = L.table(res_smem, 0);
     float* t_rc = L.table(res_smem, 1);
     float* t_cs = L.table(res_smem, 2);
-    float* coefp = L.coef(res_smem);
     if (tid < 256) {
       const int j = tid / 8, i0 = 4 * (tid % 8);
       const int lim = n_src - n_dst + j;
       float sc[4], av[4], rr[4];
       bool ok[4];
       float m = -INFINITY;
+      // The waves' partials, four sources at a time.
+      float4 sv4 = make_float4(0.f, 0.f, 0.f, 0.f), av4 = sv4, gv4 = sv4;
+      for (int w2 = 0; w2 < W; ++w2) {
+        const float4 x = *reinterpret_cast<const float4*>(L.sred(res_smem, w2) + j * kTile + i0);
+        const float4 y = *reinterpret_cast<const float4*>(L.ared(res_smem, w2) + j * kTile + i0);
+        const float* g = L.gred(res_smem, w2) + i0 * (kTile + 1);
+        sv4.x += x.x; sv4.y += x.y; sv4.z += x.z; sv4.w += x.w;
+        av4.x += y.x; av4.y += y.y; av4.z += y.z; av4.w += y.w;
+        gv4.x += g[0]; gv4.y += g[kTile + 1]; gv4.z += g[2 * (kTile + 1)]; gv4.w += g[3 * (kTile + 1)];
+      }
+      const float svs[4] = {sv4.x, sv4.y, sv4.z, sv4.w}, avs[4] = {av4.x, av4.y, av4.z, av4.w};
+      const float gvs[4] = {gv4.x, gv4.y, gv4.z, gv4.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int i = i0 + q;
-        float sv = 0.f, aa = 0.f, gv = 0.f;
-        for (int w2 = 0; w2 < W; ++w2) {
-          sv += L.sred(res_smem, w2)[j * kTile + i];
-          aa += L.ared(res_smem, w2)[j * kTile + i];
-          gv += L.gred(res_smem, w2)[i * kTile + i];
-        }
-        rr[q] = 1.0f / sqrtf(gv / (float)d + a.eps);
+        rr[q] = 1.0f / sqrtf(gvs[q] / (float)d + a.eps);
         ok[q] = j < n_dst && i <= lim;
-        sc[q] = ok[q] ? rr[q] * sv : -INFINITY;
-        av[q] = aa;
+        sc[q] = ok[q] ? rr[q] * svs[q] : -INFINITY;
+        av[q] = avs[q];
         m = fmaxf(m, sc[q]);
       }
       m = group_max<8>(m);
@@ -755,15 +759,6 @@ __global__ __launch_bounds__(512, 1) void k_full_bwd_res(FullBwdArgs a, const ui
           make_float4(rcv[0], rcv[1], rcv[2], rcv[3]);
     }
     lds_barrier();
-    if (tid < kTile) {
-      const int i = tid;
-      float cs = 0.f, gv = 0.f;
-      for (int j = 0; j < kTile; ++j) cs += t_cs[j * kARow + i];
-      for (int w2 = 0; w2 < W; ++w2) gv += L.gred(res_smem, w2)[i * kTile + i];
-      const float r2 = 1.0f / (gv / (float)d + a.eps);
-      coefp[i] = i < n_src ? r2 * cs / (float)d : 0.f;
-    }
-    lds_barrier();
 
     // ---------------- stage 2 B operands, built once per token (into the A
     // partials' space, dead now): lane (h, n = source i), element e <-> row
@@ -792,7 +787,12 @@ __global__ __launch_bounds__(512, 1) void k_full_bwd_res(FullBwdArgs a, const ui
           store_split(x, 4 * wave + 2 * b);
         }
       } else if (wave == 2) {
-        const float cn = -coefp[n];
+        // coef_i = r_i^2 (sum_j c_ji s_ji) / d for source i = n.
+        float cs = 0.f, gv = 0.f;
+        for (int j = 0; j < kTile; ++j) cs += t_cs[j * kARow + n];
+        for (int w2 = 0; w2 < W; ++w2) gv += L.gred(res_smem, w2)[n * (kTile + 1)];
+        const float r2 = 1.0f / (gv / (float)d + a.eps);
+        const float cn = n < n_src ? -(r2 * cs / (float)d) : 0.f;
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
           float x[8];
