@@ -124,33 +124,8 @@ __global__ __launch_bounds__(256, ATTNRES_P2_MINWAVES) void k_phase2_fast(Phase2
   const int64_t T = a.T;
   const int segs_per_head = (d / a.H) / 512;
   constexpr int QR = kP2QLds ? 1 : CPL;
-  __shared__ float4 qs[kP2QLds ? CPL * 64 * 2 : 1];
-  float qreg[QR][8];
-  if constexpr (kP2QLds) {
-    // Every wave uses the same lane -> channel map, so the block shares one copy.
-    // One branch on the gain outside the loop: loads in the loop are unconditional.
-    const float4* w4 = reinterpret_cast<const float4*>(a.w);
-    const float4* g4 = reinterpret_cast<const float4*>(a.gain);
-    if (a.gain != nullptr) {
-      for (int k = threadIdx.x; k < d / 4; k += blockDim.x) {
-        float4 q = w4[k];
-        const float4 g = g4[k];
-        q.x *= g.x; q.y *= g.y; q.z *= g.z; q.w *= g.w;
-        qs[k] = q;
-      }
-    } else {
-      for (int k = threadIdx.x; k < d / 4; k += blockDim.x) qs[k] = w4[k];
-    }
-    __syncthreads();
-  } else {
-#pragma unroll
-    for (int c = 0; c < CPL; ++c)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int col = (c * 64 + lane) * 8 + e;
-        qreg[kP2QLds ? 0 : c][e] = a.gain ? a.w[col] * a.gain[col] : a.w[col];
-      }
-  }
+  // The first token's loads go out before the fold of q, so that at small T
+  // (one token per wave) the two memory latencies overlap.
   // With UPD == 2 the partial loads read f itself.
   const bf16_t* part = static_cast<const bf16_t*>(UPD == 2 ? a.f : a.partial);
   const bf16_t* fin = static_cast<const bf16_t*>(a.f);
@@ -171,6 +146,33 @@ __global__ __launch_bounds__(256, ATTNRES_P2_MINWAVES) void k_phase2_fast(Phase2
   if (t < T) {
     load_p2<CPL, OT>(p, o, part, oin, t, d, lane);
     load_f(t);
+  }
+  __shared__ float4 qs[kP2QLds ? CPL * 64 * 2 : 1];
+  float qreg[QR][8];
+  if constexpr (kP2QLds) {
+    // Every wave uses the same lane -> channel map, so the block shares one copy.
+    // One branch on the gain outside the loop: loads in the loop are unconditional.
+    const float4* w4 = reinterpret_cast<const float4*>(a.w);
+    const float4* g4 = reinterpret_cast<const float4*>(a.gain);
+    if (a.gain != nullptr) {
+      for (int k = threadIdx.x; k < d / 4; k += blockDim.x) {
+        float4 q = w4[k];
+        const float4 g = g4[k];
+        q.x *= g.x; q.y *= g.y; q.z *= g.z; q.w *= g.w;
+        qs[k] = q;
+      }
+    } else {
+      for (int k = threadIdx.x; k < d / 4; k += blockDim.x) qs[k] = w4[k];
+    }
+    lds_barrier();  // orders the LDS copy only: the token's loads stay in flight
+  } else {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int col = (c * 64 + lane) * 8 + e;
+        qreg[kP2QLds ? 0 : c][e] = a.gain ? a.w[col] * a.gain[col] : a.w[col];
+      }
   }
   for (; t < T; t += nw) {
     const int64_t tn = t + nw;

@@ -299,7 +299,31 @@ struct ResidentSmem {
   __attribute__((aligned(16))) float alpha[kTile][kARow];  // alpha[j][i]
 };
 
-template <int NCH>
+// The query operand of chunk g, k-step s and part p (0 = bf16 high, 1 =
+// low) for this lane, formed from w and g exactly as k_full_qsplit forms it
+// (used when each workgroup has a single token, so no packing launch runs).
+__device__ __forceinline__ void full_q_operand(const FullArgs& a, int64_t g, int s, uint4& hi4, uint4& lo4) {
+  const int lane = lane_id(), j = lane % 32;
+  const int64_t k0 = (g * 4 + s) * 16 + 8 * (lane / 32);
+  const int jc = j < a.n_dst ? j : (int)a.n_dst - 1;
+  float q[8], hi[8], lo[8];
+  if (a.gain != nullptr)
+    fold_q8<true>(a.w + jc * a.d + k0, a.gain + jc * a.gain_ld + k0, q);
+  else
+    fold_q8<false>(a.w + jc * a.d + k0, nullptr, q);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float qe = j < a.n_dst ? q[e] : 0.f;
+    hi[e] = bf2f(f2bf(qe));
+    lo[e] = qe - hi[e];
+  }
+  hi4 = pack8(hi[0], hi[1], hi[2], hi[3], hi[4], hi[5], hi[6], hi[7]);
+  lo4 = pack8(lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]);
+}
+
+// FQ: form the query operands in the kernel (one token per workgroup) instead
+// of reading them from the packed workspace.
+template <int NCH, bool FQ>
 __global__ __launch_bounds__(kRB, 1) void k_full_resident(FullArgs a, const bf16_t* qpk) {
   __shared__ ResidentSmem sm;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
@@ -356,14 +380,20 @@ __global__ __launch_bounds__(kRB, 1) void k_full_resident(FullArgs a, const bf16
     // next-token registers are free during this stage).
     {
       uint4 q[2][8];
+      auto load_q = [&](int c, uint4 (&dst)[8]) {
+        const int64_t g = ch_base / kChunk + c;
+        if constexpr (FQ) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) q[0][k] = qv[(int64_t)((ch_base / kChunk) * 8 + k) * 64];
+          for (int s2 = 0; s2 < 4; ++s2) full_q_operand(a, g, s2, dst[2 * s2], dst[2 * s2 + 1]);
+        } else {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) dst[k] = qv[(g * 8 + k) * 64];
+        }
+      };
+      load_q(0, q[0]);
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        if (c + 1 < NCH) {
-#pragma unroll
-          for (int k = 0; k < 8; ++k) q[(c + 1) & 1][k] = qv[(int64_t)((ch_base / kChunk + c + 1) * 8 + k) * 64];
-        }
+        if (c + 1 < NCH) load_q(c + 1, q[(c + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);  // issue them now, not next to their use
         uint4 b[4];
 #pragma unroll
@@ -532,17 +562,22 @@ bool full_fast_ok(const FullArgs& a) {
   return al16(a.src) && al16(a.out) && al16(a.ws) && al16(a.w) && al16(a.gain);
 }
 
+// With at most one token per workgroup the resident kernel forms the query
+// operands itself and the packing launch is skipped (one launch per call).
 template <int NCH>
 hipError_t launch_resident(const FullArgs& a, const bf16_t* qpk, hipStream_t st) {
   int64_t grid = num_cus();
-  if (grid > a.T) grid = a.T;
-  hipLaunchKernelGGL(k_full_resident<NCH>, dim3((unsigned)grid), dim3(kRB), 0, st, a, qpk);
+  if (grid >= a.T) {
+    hipLaunchKernelGGL((k_full_resident<NCH, true>), dim3((unsigned)a.T), dim3(kRB), 0, st, a, qpk);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(k_full_qsplit, dim3(64), dim3(256), 0, st, a, const_cast<bf16_t*>(qpk));
+  hipLaunchKernelGGL((k_full_resident<NCH, false>), dim3((unsigned)grid), dim3(kRB), 0, st, a, qpk);
   return hipGetLastError();
 }
 
 hipError_t launch_full_fast(const FullArgs& a, hipStream_t st) {
   bf16_t* qpk = static_cast<bf16_t*>(a.ws);
-  hipLaunchKernelGGL(k_full_qsplit, dim3(64), dim3(256), 0, st, a, qpk);
   if (a.d <= kRW * kRMaxCh * kChunk && full_resident_enabled()) {
     switch (a.d / (kRW * kChunk)) {
       case 1: return launch_resident<1>(a, qpk, st);
@@ -552,6 +587,7 @@ hipError_t launch_full_fast(const FullArgs& a, hipStream_t st) {
       default: break;
     }
   }
+  hipLaunchKernelGGL(k_full_qsplit, dim3(64), dim3(256), 0, st, a, qpk);
   int per_cu = 0;
   hipError_t e = blocks_per_cu(reinterpret_cast<const void*>(k_full_fast), kFB, &per_cu);
   if (e != hipSuccess) return e;

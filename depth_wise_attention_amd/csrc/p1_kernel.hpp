@@ -141,8 +141,27 @@ constexpr int p1_row_len() {
   return (((MH ? CH : 1) * S * N + N) + 7) / 8 * 8;
 }
 
-// The token loop; q = w * g is already in the thread's LDS slots.
-template <int N, int S, int CH, bool MH>
+// q = w * g into this thread's own LDS slots, inline (the small-T kernel
+// issues its token's rep loads first, so both latencies overlap).
+template <int S, int CH, bool G>
+__device__ __forceinline__ void p1_fold_inline(const float* w, const float* gain, int64_t gain_ld, int d, int B,
+                                               int tid, float4* qs) {
+#pragma unroll
+  for (int l = 0; l < S; ++l)
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      float qq[8];
+      const int col = (c * B + tid) * 8;
+      fold_q8<G>(w + (int64_t)l * d + col, gain + l * gain_ld + col, qq);
+      qs[((l * CH + c) * B + tid) * 2 + 0] = make_float4(qq[0], qq[1], qq[2], qq[3]);
+      qs[((l * CH + c) * B + tid) * 2 + 1] = make_float4(qq[4], qq[5], qq[6], qq[7]);
+    }
+}
+
+// The token loop; q = w * g is already in the thread's LDS slots, or, with
+// FOLD (one token per workgroup), is folded right after the first token's
+// rep loads are issued, so that the two memory latencies overlap.
+template <int N, int S, int CH, bool MH, bool FOLD = false>
 __device__ __forceinline__ void p1_body(const Phase1Args& a, float4* smem) {
   constexpr int CHH = MH ? CH : 1;           // dot-product groups per thread
   constexpr int NDOT = CHH * S * N;
@@ -325,6 +344,13 @@ __device__ __forceinline__ void p1_body(const Phase1Args& a, float4* smem) {
   uint4 v[N][CH];
   int64_t t = blockIdx.x;
   if (t < T) load_all(v, t);
+  if constexpr (FOLD) {
+    // Each thread reads back only its own slots, so no barrier is needed.
+    if (a.gain != nullptr)
+      p1_fold_inline<S, CH, true>(a.w, a.gain, a.gain_ld, d, B, tid, qs);
+    else
+      p1_fold_inline<S, CH, false>(a.w, a.gain, a.gain_ld, d, B, tid, qs);
+  }
   for (; t < T; t += Gs) token(v, t);
 }
 
@@ -336,6 +362,16 @@ __global__ __launch_bounds__(512, 2) void k_p1(Phase1Args a) {
   else
     p1_fold<S, CH, false>(a.w, a.gain, a.gain_ld, (int)a.d, (int)blockDim.x, (int)threadIdx.x, p1_smem);
   p1_body<N, S, CH, MH>(a, p1_smem);
+}
+
+// Small T (every workgroup gets at most one token): the same kernel with the
+// fold of q moved after the issue of the token's rep loads (inline), instead
+// of a prologue that completes before the rows are requested.  Same channel
+// map and reductions as k_p1, so the same bits.
+template <int N, int S, int CH, bool MH>
+__global__ __launch_bounds__(512, 2) void k_p1s(Phase1Args a) {
+  extern __shared__ float4 p1_smem[];
+  p1_body<N, S, CH, MH, true>(a, p1_smem);
 }
 
 template <int N, int S, int CH, bool MH>
@@ -354,7 +390,19 @@ hipError_t p1_go(const Phase1Args& a, const P1Plan& p, hipStream_t st) {
   if (e != hipSuccess) return e;
   if (per_cu < 1) per_cu = 1;
   int64_t grid = (int64_t)num_cus() * per_cu;
-  if (grid > a.T) grid = a.T;
+  if (grid >= a.T) {
+    // One token per workgroup: the small-T kernel.
+    auto ks = k_p1s<N, S, CH, MH>;
+    static std::atomic<size_t> allowed_s{64 * 1024};
+    if (p.lds > allowed_s.load(std::memory_order_relaxed)) {
+      const hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(ks),
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
+      if (e2 != hipSuccess) return e2;
+      allowed_s.store(p.lds, std::memory_order_relaxed);
+    }
+    hipLaunchKernelGGL(ks, dim3((unsigned)a.T), dim3((unsigned)p.B), p.lds, st, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3((unsigned)p.B), p.lds, st, a);
   return hipGetLastError();
 }
