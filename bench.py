@@ -10,7 +10,7 @@ in HBM before timing starts.
 Prints ONE JSON line on stdout.  Everything else goes to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                  [--no-extra] [--workload block|mhar|full|bwd|full_bwd|block_update|decode|msar|block_msar]
+                  [--no-extra] [--workload block|mhar|full|full_h8|bwd|full_bwd|block_update|decode|msar|block_msar]
                   [--copy-calibration]
 """
 
@@ -40,7 +40,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="block", choices=["block", "mhar", "full", "bwd", "mhar_bwd", "full_bwd", "block_update",
+    p.add_argument("--workload", default="block", choices=["block", "mhar", "full", "full_h8", "bwd", "mhar_bwd", "full_bwd", "block_update",
                                                                 "decode", "msar", "block_msar", "depth_sweep"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads")
@@ -436,7 +436,9 @@ def bench_block_msar(args, T=16384, d=4096, N=8, S=4):
                 phase2_ms=p2)
 
 
-def bench_full(args, T=4096):
+def bench_full(args, T=4096, H=1):
+    """Full AttnRes forward at the C2 shape (T=4096, d=2048, L=32), one head or
+    H heads of d/H channels (each with its own depth softmax)."""
     import torch
     import depth_wise_attention_amd as ar
     from workloads import synth
@@ -448,14 +450,16 @@ def bench_full(args, T=4096):
     L, d = wl.src.shape[0], wl.d
     del wl
     out = torch.empty((L, T, d), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(max(1, ar.attnres_full_fwd_workspace_size(L, L, d, 1, ar.BF16)), dtype=torch.uint8,
+    ws = torch.empty(max(1, ar.attnres_full_fwd_workspace_size(L, L, d, H, ar.BF16)), dtype=torch.uint8,
                      device="cuda")
-    sec, wall = time_loop(lambda: ar.attnres_full_fwd(src, w, g, 1e-6, 1, out=out, ws=ws),
+    sec, wall = time_loop(lambda: ar.attnres_full_fwd(src, w, g, 1e-6, H, out=out, ws=ws),
                           max(3, args.steps // 4), 2)
     n = max(3, args.steps // 4)
     b = full_bytes(T, d, L)
-    return dict(name=f"full_bf16_T{T}_d{d}_L{L}", tokens_per_s=T * n / sec, ms_per_step=sec / n * 1e3,
-                step_bytes=b, step_gbs=b * n / sec / 1e9)
+    tag = "" if H == 1 else f"_H{H}"
+    return dict(name=f"full_bf16_T{T}_d{d}_L{L}{tag}", tokens_per_s=T * n / sec, ms_per_step=sec / n * 1e3,
+                step_bytes=b, step_gbs=b * n / sec / 1e9,
+                kernel=ar.attnres_kernel_variant(ar.OP_FULL_FWD, L, L, T, d, H))
 
 
 def bench_bwd(args, T=8192, H=1):
@@ -773,6 +777,7 @@ def main():
 
     if args.workload != "block":
         fn = {"mhar": lambda: bench_block(args, H=8, T=32768), "full": lambda: bench_full(args),
+              "full_h8": lambda: bench_full(args, H=8),
               "bwd": lambda: bench_bwd(args), "mhar_bwd": lambda: bench_bwd(args, H=8), "full_bwd": lambda: bench_full_bwd(args),
               "block_update": lambda: bench_update(args), "decode": lambda: bench_decode(args),
               "msar": lambda: bench_msar(args), "block_msar": lambda: bench_block_msar(args),

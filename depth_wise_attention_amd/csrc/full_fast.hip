@@ -323,10 +323,19 @@ __device__ __forceinline__ void full_q_operand(const FullArgs& a, int64_t g, int
 
 // FQ: form the query operands in the kernel (one token per workgroup) instead
 // of reading them from the packed workspace.
-template <int NCH, bool FQ>
+// MH: H = 2, 4 or 8 heads (MHAR abstract), a head being 8 / H consecutive
+// waves (d / H channels), each with its own depth softmax.  Each head's score
+// partials are summed into its first wave through LDS, halving the waves per
+// round; that wave forms the head's softmax in registers (a max and a sum
+// over the 32 lanes holding one destination's sources), transposes alpha
+// (bf16 high and low parts, exact) with a permuted identity into stage 2's
+// operand order, and hands the operands to the head's other waves.  The sums
+// of squares stay over the whole d.
+template <int NCH, bool FQ, bool MH>
 __global__ __launch_bounds__(kRB, 1) void k_full_resident(FullArgs a, const bf16_t* qpk) {
   __shared__ ResidentSmem sm;
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: buffer offsets from it stay scalar
   const int d = (int)a.d, n_src = (int)a.n_src, n_dst = (int)a.n_dst;
   const int64_t T = a.T;
   const bf16_t* src = static_cast<const bf16_t*>(a.src);
@@ -356,10 +365,14 @@ __global__ __launch_bounds__(kRB, 1) void k_full_resident(FullArgs a, const bf16
   // so every load is unconditional and the wait counts stay exact.
   uint4 P[NCH][4];
   auto load_slice = [&](int64_t tt) {
-    const int piece = lane & 7;
+    // Addresses from an opaque lane id: recomputed per token instead of held
+    // (and spilled) across the token loop.
+    int ol = lane;
+    asm volatile("" : "+v"(ol));
+    const int piece = ol & 7;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int r = 8 * u + (lane >> 3);
+      const int r = 8 * u + (ol >> 3);
       const bf16_t* rp = src + ((int64_t)(r < n_src ? r : 0) * T + tt) * d + ch_base + 8 * piece;
 #pragma unroll
       for (int c = 0; c < NCH; ++c) P[c][u] = *reinterpret_cast<const uint4*>(rp + c * kChunk);
@@ -386,8 +399,15 @@ __global__ __launch_bounds__(kRB, 1) void k_full_resident(FullArgs a, const bf16
 #pragma unroll
           for (int s2 = 0; s2 < 4; ++s2) full_q_operand(a, g, s2, dst[2 * s2], dst[2 * s2 + 1]);
         } else {
+          // Buffer loads: the packed operands' base and offsets are scalar, so no
+          // per-lane 64-bit address is held across the token loop.
+          const __amdgpu_buffer_rsrc_t qr =
+              __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(qpk), 0, 0x7fffffff, kBufferWord3);
 #pragma unroll
-          for (int k = 0; k < 8; ++k) dst[k] = qv[(g * 8 + k) * 64];
+          for (int k = 0; k < 8; ++k) {
+            const v4u v = __builtin_amdgcn_raw_buffer_load_b128(qr, lane * 16, (int)((g * 8 + k) * 1024), 0);
+            dst[k] = make_uint4(v.x, v.y, v.z, v.w);
+          }
         }
       };
       load_q(0, q[0]);
@@ -415,6 +435,100 @@ __global__ __launch_bounds__(kRB, 1) void k_full_resident(FullArgs a, const bf16
       const int64_t tn = t + gridDim.x;
       load_slice(tn < T ? tn : t);
     }
+    uint4 ahi[2], alo[2];
+    if constexpr (MH) {
+      const int g = kRW / a.H;  // waves per head
+      const int wh = wave % g, head = wave / g;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r / 4) + 4 * h + (r % 4) == n) sm.gred[wave][n] = G[r];
+      // Head partials: round with `half` moves waves [half, 2 half) of each head
+      // onto waves [0, half) through slot head * half + (wh - half).
+      for (int half = g / 2; half >= 1; half /= 2) {
+        if (wh >= half && wh < 2 * half) {
+          float* sl = sm.sred[head * half + (wh - half)];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sl[(8 * (r / 4) + 4 * h + (r % 4)) * kTile + n] = S[r];
+        }
+        lds_barrier();
+        if (wh < half) {
+          const float* sl = sm.sred[head * half + wh];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) S[r] += sl[(8 * (r / 4) + 4 * h + (r % 4)) * kTile + n];
+        }
+        lds_barrier();
+      }
+      if (g == 1) lds_barrier();  // the sums of squares
+      uint4* share = reinterpret_cast<uint4*>(sm.sred[head]);  // a head's operands: 4 x 64 uint4
+      if (wh == 0) {
+        float gv = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < kRW; ++w2) gv += sm.gred[w2][n];
+        const float ri = 1.0f / sqrtf(gv / (float)d + a.eps);
+        // Lane (h, i = n), element r: destination j = 8 (r / 4) + 4 h + r % 4.
+        float al[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = 8 * (r / 4) + 4 * h + (r % 4);
+          const bool valid = j < n_dst && n <= n_src - n_dst + j;
+          const float sc = valid ? ri * S[r] : -INFINITY;
+          const float m = group_max<32>(sc);
+          const float e = valid ? expf(sc - m) : 0.f;
+          const float l = group_sum<32>(e);
+          al[r] = l > 0.f ? e / l : 0.f;
+        }
+        // alpha^T as A operands (row i = n, k-step b holding destinations
+        // transposed_row(b, h, e)), times I[k][j] = 1 when transposed_row
+        // maps k to j: D[i][j] = alpha[j][i] with lane (h, j) holding the
+        // sources transposed_row(b2, h, e) of destination j.
+        uint4 ip[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          uint32_t wds[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t lo16 = transposed_row(b, h, 2 * q) == n ? 0x3F80u : 0u;
+            const uint32_t hi16 = transposed_row(b, h, 2 * q + 1) == n ? 0x3F80u : 0u;
+            wds[q] = lo16 | (hi16 << 16);
+          }
+          ip[b] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+        }
+        // part 0: bf16(alpha); part 1: alpha - bf16(alpha), one at a time.
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+          f16acc D = {};
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float hi = bf2f(f2bf(al[8 * b + e]));
+              x[e] = part == 0 ? hi : al[8 * b + e] - hi;
+            }
+            D = mfma(pack8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]), ip[b], D);
+          }
+          uint4* dst = part == 0 ? ahi : alo;
+          dst[0] = pack8(D[0], D[1], D[2], D[3], D[4], D[5], D[6], D[7]);
+          dst[1] = pack8(D[8], D[9], D[10], D[11], D[12], D[13], D[14], D[15]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (g > 1) {
+          share[0 * 64 + lane] = ahi[0];
+          share[1 * 64 + lane] = ahi[1];
+          share[2 * 64 + lane] = alo[0];
+          share[3 * 64 + lane] = alo[1];
+        }
+      }
+      if (g > 1) {
+        lds_barrier();
+        if (wh != 0) {
+          ahi[0] = share[0 * 64 + lane];
+          ahi[1] = share[1 * 64 + lane];
+          alo[0] = share[2 * 64 + lane];
+          alo[1] = share[3 * 64 + lane];
+        }
+      }
+    } else {
     // ---------------- cross-wave sums: waves 4..7 hand their partials to waves 0..3
     if (wave >= kRW / 2) {
 #pragma unroll
@@ -464,8 +578,7 @@ __global__ __launch_bounds__(kRB, 1) void k_full_resident(FullArgs a, const bf16
     }
     lds_barrier();
 
-    // ---------------- stage 2: H = alpha V from the resident slots
-    uint4 ahi[2], alo[2];
+    // ---------------- stage 2 operands: alpha in operand order, split hi + lo
 #pragma unroll
     for (int b2 = 0; b2 < 2; ++b2) {
       const float4 x0 = *reinterpret_cast<const float4*>(&sm.alpha[n][16 * b2 + 4 * h]);
@@ -480,6 +593,9 @@ __global__ __launch_bounds__(kRB, 1) void k_full_resident(FullArgs a, const bf16
       ahi[b2] = pack8(hi[0], hi[1], hi[2], hi[3], hi[4], hi[5], hi[6], hi[7]);
       alo[b2] = pack8(lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]);
     }
+    }  // H == 1
+
+    // ---------------- stage 2: H = alpha V from the resident slots
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       unsigned char* slot = sm.slots[wave][c];
@@ -535,25 +651,25 @@ __global__ __launch_bounds__(kRB, 1) void k_full_resident(FullArgs a, const bf16
 
 bool al16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
 
-// The resident kernel can be switched off (ATTNRES_FULL_RESIDENT=0) to compare
-// it with the streaming kernel on the same build.
-bool full_resident_enabled() {
-  static const bool on = [] {
-    const char* e = getenv("ATTNRES_FULL_RESIDENT");
-    return e == nullptr || e[0] != '0';
-  }();
-  return on;
+// Shapes the resident kernel takes: d = 512 .. 2048 in steps of 512 (whole
+// 64-channel chunks for each of the 8 waves); with heads, H = 2, 4 or 8 so
+// that a head is a run of whole waves.
+bool resident_shape(int64_t d, int H) {
+  if (d % (kRW * kChunk) != 0 || d > kRW * kRMaxCh * kChunk) return false;
+  return H == 1 || H == 2 || H == 4 || H == 8;
 }
 
 }  // namespace
 
 size_t full_fast_workspace_bytes(int64_t n_src, int64_t n_dst, int64_t d, int H, int dtype) {
-  if (dtype != kBF16 || H != 1 || n_src > kTile || n_dst > n_src) return 0;
+  if (dtype != kBF16 || n_src > kTile || n_dst > n_src) return 0;
+  if (H != 1 && !resident_shape(d, H)) return 0;
   return (size_t)2 * kTile * (size_t)d * sizeof(bf16_t);
 }
 
 bool full_fast_ok(const FullArgs& a) {
-  if (a.dtype != kBF16 || a.H != 1 || a.T < 1) return false;
+  if (a.dtype != kBF16 || a.T < 1) return false;
+  if (a.H != 1 && !resident_shape(a.d, a.H)) return false;  // heads: the resident kernel only
   if (a.n_src > kTile || a.n_dst > a.n_src) return false;
   // Each wave streams an even number of whole 64-channel chunks.
   if (a.d % (2 * kFW * kChunk) != 0 || a.d > ((int64_t)1 << 16)) return false;
@@ -564,26 +680,31 @@ bool full_fast_ok(const FullArgs& a) {
 
 // With at most one token per workgroup the resident kernel forms the query
 // operands itself and the packing launch is skipped (one launch per call).
-template <int NCH>
+template <int NCH, bool MH>
 hipError_t launch_resident(const FullArgs& a, const bf16_t* qpk, hipStream_t st) {
   int64_t grid = num_cus();
   if (grid >= a.T) {
-    hipLaunchKernelGGL((k_full_resident<NCH, true>), dim3((unsigned)a.T), dim3(kRB), 0, st, a, qpk);
+    hipLaunchKernelGGL((k_full_resident<NCH, true, MH>), dim3((unsigned)a.T), dim3(kRB), 0, st, a, qpk);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(k_full_qsplit, dim3(64), dim3(256), 0, st, a, const_cast<bf16_t*>(qpk));
-  hipLaunchKernelGGL((k_full_resident<NCH, false>), dim3((unsigned)grid), dim3(kRB), 0, st, a, qpk);
+  hipLaunchKernelGGL((k_full_resident<NCH, false, MH>), dim3((unsigned)grid), dim3(kRB), 0, st, a, qpk);
   return hipGetLastError();
+}
+
+template <int NCH>
+hipError_t launch_resident_h(const FullArgs& a, const bf16_t* qpk, hipStream_t st) {
+  return a.H > 1 ? launch_resident<NCH, true>(a, qpk, st) : launch_resident<NCH, false>(a, qpk, st);
 }
 
 hipError_t launch_full_fast(const FullArgs& a, hipStream_t st) {
   bf16_t* qpk = static_cast<bf16_t*>(a.ws);
-  if (a.d <= kRW * kRMaxCh * kChunk && full_resident_enabled()) {
+  if (resident_shape(a.d, a.H)) {
     switch (a.d / (kRW * kChunk)) {
-      case 1: return launch_resident<1>(a, qpk, st);
-      case 2: return launch_resident<2>(a, qpk, st);
-      case 3: return launch_resident<3>(a, qpk, st);
-      case 4: return launch_resident<4>(a, qpk, st);
+      case 1: return launch_resident_h<1>(a, qpk, st);
+      case 2: return launch_resident_h<2>(a, qpk, st);
+      case 3: return launch_resident_h<3>(a, qpk, st);
+      case 4: return launch_resident_h<4>(a, qpk, st);
       default: break;
     }
   }

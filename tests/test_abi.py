@@ -88,11 +88,15 @@ def _rc_full(**kw):
 
 
 def test_full_workspace_size():
-    # bf16, one head, at most 32 sources: q = w * gain as two bf16 parts, [2, 32, d].
+    # bf16, at most 32 sources, one head (any d) or H = 2, 4, 8 heads with d = 512 .. 2048 in steps
+    # of 512: q = w * gain as two bf16 parts, [2, 32, d].
     assert binding.attnres_full_fwd_workspace_size(32, 32, 2048, 1, BF16) == 2 * 32 * 2048 * 2
     assert binding.attnres_full_fwd_workspace_size(8, 1, 4096, 1, BF16) == 2 * 32 * 4096 * 2
-    for args in [(32, 32, 2048, 1, F32), (33, 1, 2048, 1, BF16), (8, 8, 2048, 2, BF16), (4, 5, 64, 1, BF16),
-                 (0, 0, 64, 1, BF16), (4, 4, 0, 1, BF16)]:
+    for H in (2, 4, 8):
+        assert binding.attnres_full_fwd_workspace_size(8, 8, 2048, H, BF16) == 2 * 32 * 2048 * 2
+        assert binding.attnres_full_fwd_workspace_size(32, 1, 512, H, BF16) == 2 * 32 * 512 * 2
+    for args in [(32, 32, 2048, 1, F32), (33, 1, 2048, 1, BF16), (8, 8, 2048, 16, BF16), (8, 8, 4096, 8, BF16),
+                 (8, 8, 2048, 3, BF16), (4, 5, 64, 1, BF16), (0, 0, 64, 1, BF16), (4, 4, 0, 1, BF16)]:
         assert binding.attnres_full_fwd_workspace_size(*args) == 0, args
 
 

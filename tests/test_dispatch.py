@@ -93,6 +93,13 @@ def test_phase2_full_and_policy():
     assert variant(binding.OP_PHASE2, 8, 4, 100, 1024) == "phase2_generic"
     assert variant(binding.OP_FULL_FWD, 32, 32, 100, 2048) == "full_fast"
     assert variant(binding.OP_FULL_FWD, 33, 33, 100, 2048) == "full_generic"
+    # heads on the matrix cores: whole waves of the resident kernel (d <= 2048)
+    for H in (2, 4, 8):
+        for d in (512, 1024, 1536, 2048):
+            assert variant(binding.OP_FULL_FWD, 32, 32, 100, d, H=H) == "full_fast"
+    assert variant(binding.OP_FULL_FWD, 32, 32, 100, 2048, H=16) == "full_generic"
+    assert variant(binding.OP_FULL_FWD, 32, 32, 100, 4096, H=8) == "full_generic"
+    assert variant(binding.OP_FULL_FWD, 32, 32, 100, 2048, H=3) == "full_generic"
     assert variant(binding.OP_FULL_BWD, 32, 32, 100, 2048) == "full_bwd_res"
     for d in (1024, 1280, 1536, 1792):
         assert variant(binding.OP_FULL_BWD, 17, 5, 100, d) == "full_bwd_res"

@@ -8,6 +8,9 @@ is compared with the oracle on the same seeded inputs:
     every width class (d = 512 .. 8192, one or two chunks per thread), and
     heads of whole 512-channel segments;
   * the Block backward for N = 1..12, S = 1..4, widths and heads;
+  * the Full forward's matrix-core kernel with heads (H = 2, 4, 8; d = 512 ..
+    2048), with one token per workgroup (query operands formed in the
+    kernel) and with several;
   * the Full backward's register-resident kernel (d = 1024 .. 2048) and the
     staged one, over source / destination counts, gains and accumulation;
   * a sharply peaked depth softmax (scores in the hundreds), where the
@@ -201,3 +204,38 @@ def test_full_bwd_variant(T, d, L, n_dst, gain, kernel):
     finally:
         ar.attnres_set_kernel_policy(prev)
     check(host(gen[0]), ref[0], "bf16", "d_src (general kernel)")
+
+
+# (T, d, L, n_dst, H, gain)
+FULL_FWD_HEAD_CASES = [
+    (700, 2048, 32, 32, 8, "per"),
+    (19, 2048, 32, 32, 8, "per"),
+    (600, 2048, 32, 32, 4, "shared"),
+    (530, 2048, 32, 32, 2, "none"),
+    (300, 1024, 17, 5, 8, "per"),
+    (290, 1536, 9, 9, 4, "per"),
+    (1, 512, 32, 1, 8, "shared"),
+    (333, 512, 20, 13, 2, "per"),
+    (7, 1024, 1, 1, 4, "none"),
+]
+
+
+@pytest.mark.parametrize("T,d,L,n_dst,H,gain", FULL_FWD_HEAD_CASES)
+def test_full_fwd_heads(T, d, L, n_dst, H, gain):
+    name = ar.attnres_kernel_variant(ar.OP_FULL_FWD, L, n_dst, T, d, H)
+    say(f"full fwd heads T={T} d={d} L={L} n_dst={n_dst} H={H} gain={gain}: {name}")
+    assert name == "full_fast", name
+    wl = synth.full_workload(T=T, d=d, L=L, std_step=0.2, dtype="bf16", seed=120 + H + L, gain_variance=0.02,
+                             n_dst=n_dst)
+    g = _gain_arg(wl, gain, n_dst, d)
+    ref = orc.full_fwd(wl.src, wl.w, g, wl.eps, H)
+    src, w = dev(wl.src, True), dev(wl.w)
+    gd = dev(g) if g is not None else None
+    out = ar.attnres_full_fwd(src, w, gd, wl.eps, H)
+    check(host(out), ref, "bf16", "out")
+    prev = ar.attnres_set_kernel_policy(1)
+    try:
+        gen = ar.attnres_full_fwd(src, w, gd, wl.eps, H)
+    finally:
+        ar.attnres_set_kernel_policy(prev)
+    check(host(gen), ref, "bf16", "out (general kernel)")
