@@ -10,7 +10,7 @@ in HBM before timing starts.
 Prints ONE JSON line on stdout.  Everything else goes to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                  [--no-extra] [--workload block|mhar|full|full_h8|bwd|full_bwd|block_update|decode|msar|block_msar]
+                  [--no-extra] [--workload block|mhar|full|full_h8|bwd|full_bwd|full_bwd_h8|block_update|decode|msar|block_msar]
                   [--copy-calibration]
 """
 
@@ -40,7 +40,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="block", choices=["block", "mhar", "full", "full_h8", "bwd", "mhar_bwd", "full_bwd", "block_update",
+    p.add_argument("--workload", default="block", choices=["block", "mhar", "full", "full_h8", "bwd", "mhar_bwd", "full_bwd", "full_bwd_h8", "block_update",
                                                                 "decode", "msar", "block_msar", "depth_sweep"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads")
@@ -564,7 +564,7 @@ def full_bwd_bytes(T, d, L, es=2):
     return T * d * es * (L + L + L)
 
 
-def bench_full_bwd(args, T=4096):
+def bench_full_bwd(args, T=4096, H=1):
     import torch
     import depth_wise_attention_amd as ar
     from workloads import synth
@@ -575,20 +575,23 @@ def bench_full_bwd(args, T=4096):
     L, d = wl.src.shape[0], wl.d
     del wl
     out = torch.empty((L, T, d), dtype=torch.bfloat16, device="cuda")
-    ws_f = torch.empty(max(1, ar.attnres_full_fwd_workspace_size(L, L, d, 1, ar.BF16)), dtype=torch.uint8,
+    ws_f = torch.empty(max(1, ar.attnres_full_fwd_workspace_size(L, L, d, H, ar.BF16)), dtype=torch.uint8,
                        device="cuda")
-    ws_b = torch.empty(ar.attnres_full_bwd_workspace_size(L, L, T, d, 1), dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(ar.attnres_full_bwd_workspace_size(L, L, T, d, H), dtype=torch.uint8, device="cuda")
     d_src, dw, dg = torch.empty_like(src), torch.empty_like(w), torch.empty_like(g)
 
     def step():
-        ar.attnres_full_fwd(src, w, g, 1e-6, 1, out=out, ws=ws_f)
-        ar.attnres_full_bwd(src, w, dout, g, 1e-6, 1, d_src=d_src, dw=dw, dgain=dg, ws=ws_b)
+        ar.attnres_full_fwd(src, w, g, 1e-6, H, out=out, ws=ws_f)
+        ar.attnres_full_bwd(src, w, dout, g, 1e-6, H, d_src=d_src, dw=dw, dgain=dg, ws=ws_b)
 
     n = max(3, args.steps // 4)
     sec, wall = time_loop(step, n, 2)
     b = full_bytes(T, d, L) + full_bwd_bytes(T, d, L)
-    return dict(name=f"full_fwd_bwd_bf16_T{T}_d{d}_L{L}", tokens_per_s=T * n / sec,
-                ms_per_step=sec / n * 1e3, step_bytes=b, step_gbs=b * n / sec / 1e9)
+    tag = "" if H == 1 else f"_H{H}"
+    return dict(name=f"full_fwd_bwd_bf16_T{T}_d{d}_L{L}{tag}", tokens_per_s=T * n / sec,
+                ms_per_step=sec / n * 1e3, step_bytes=b, step_gbs=b * n / sec / 1e9,
+                kernels=[ar.attnres_kernel_variant(ar.OP_FULL_FWD, L, L, T, d, H),
+                         ar.attnres_kernel_variant(ar.OP_FULL_BWD, L, L, T, d, H)])
 
 
 def _cpu_model() -> str:
@@ -777,7 +780,7 @@ def main():
 
     if args.workload != "block":
         fn = {"mhar": lambda: bench_block(args, H=8, T=32768), "full": lambda: bench_full(args),
-              "full_h8": lambda: bench_full(args, H=8),
+              "full_h8": lambda: bench_full(args, H=8), "full_bwd_h8": lambda: bench_full_bwd(args, H=8),
               "bwd": lambda: bench_bwd(args), "mhar_bwd": lambda: bench_bwd(args, H=8), "full_bwd": lambda: bench_full_bwd(args),
               "block_update": lambda: bench_update(args), "decode": lambda: bench_decode(args),
               "msar": lambda: bench_msar(args), "block_msar": lambda: bench_block_msar(args),

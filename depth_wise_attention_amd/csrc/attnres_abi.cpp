@@ -800,12 +800,11 @@ int attnres_bwd(const void* reps, int64_t N, const void* partials, int64_t S, in
 
 size_t attnres_full_bwd_workspace_size(int64_t n_src, int64_t n_dst, int64_t T, int64_t d, int32_t H) {
   (void)n_src;
-  (void)H;
   int64_t b, c;
-  if (n_dst < 1 || T < 1 || d < 1 || d > kMaxD) return 0;  // T == 0 needs none
+  if (n_dst < 1 || T < 1 || d < 1 || d > kMaxD || H < 1 || H > d) return 0;  // T == 0 needs none
   if (!mul3(full_bwd_slots(T), n_dst, d, &b) || !mul3(b, 4, 1, &b)) return 0;  // general path
-  if (!mul3(T, 4096, 1, &c)) return 0;                                      // matrix-core path
-  const size_t fast = full_bwd_fast_workspace_bytes(n_dst, T, d);
+  if (!mul3(T, 4096, H, &c)) return 0;                                      // matrix-core path
+  const size_t fast = full_bwd_fast_workspace_bytes(n_dst, T, d, H);
   return (size_t)b > fast ? (size_t)b : fast;
 }
 
@@ -823,9 +822,6 @@ int attnres_full_bwd(const void* src, int64_t n_src, int64_t T, int64_t d, const
                 (long long)n_src);
   if (accumulate != 0 && accumulate != 1)
     return fail(ATTNRES_ERR_INVALID, "accumulate = %d must be 0 or 1", accumulate);
-  if (n_dst * (int64_t)H * n_src > kBwdTable)
-    return fail(ATTNRES_ERR_UNSUPPORTED, "n_dst * H * n_src = %lld exceeds %d", (long long)(n_dst * H * n_src),
-                kBwdTable);
   REQUIRE_PTR(w, "w");
   REQUIRE_PTR(dw, "dw");
   if (gain != nullptr) REQUIRE_PTR(dgain, "dgain");
@@ -856,11 +852,17 @@ int attnres_full_bwd(const void* src, int64_t n_src, int64_t T, int64_t d, const
   FullBwdArgs a{src,   n_src, T,    d,     w,     n_dst,      gain,    gain ? gain_ld : 0, eps,
                 H,     dtype, dout, d_src, dw,    dgain,      accumulate, static_cast<float*>(ws),
                 T ? full_bwd_slots(T) : 0, T ? ws_bytes : 0};
+  const bool fast = T > 0 && use_fast() && full_bwd_fast_ok(a);
+  // The general kernel keeps a per-wave table of (destination, head, source)
+  // entries; the matrix-core kernels have no such limit.
+  if (T > 0 && !fast && n_dst * (int64_t)H * n_src > kBwdTable)
+    return fail(ATTNRES_ERR_UNSUPPORTED, "n_dst * H * n_src = %lld exceeds %d on the general path",
+                (long long)(n_dst * H * n_src), kBwdTable);
   const float* slabs = static_cast<const float*>(ws);
   int64_t n_slabs = 0;
   if (T > 0) {
     hipError_t e;
-    if (use_fast() && full_bwd_fast_ok(a)) {
+    if (fast) {
       e = launch_full_bwd_fast(a, &slabs, &n_slabs, stream);
     } else {
       e = launch_full_bwd_generic(a, stream);

@@ -424,6 +424,7 @@ __global__ __launch_bounds__(64) void k_full_bwd_z(FullBwdArgs a, const float* c
   const int64_t T = a.T;
   const int ch0 = blockIdx.x * kChunk;
   const int grp = blockIdx.y;
+  const int zhead = ch0 / (d / a.H);  // the head of this tile's channels (r c is per head)
   const bf16_t* src = static_cast<const bf16_t*>(a.src);
   const uint4 ident0 = ident_operand(0), ident1 = ident_operand(1);
   uint32_t vmask[4];
@@ -442,7 +443,7 @@ __global__ __launch_bounds__(64) void k_full_bwd_z(FullBwdArgs a, const float* c
     }
     load_chunk(vrow, 0, v);
     // A operands: lane (h, j = n) holds (r c)[j][transposed_row(b, h, e)].
-    const float* cj = cws + t * (kTile * kTile) + n * kTile + 4 * h;
+    const float* cj = cws + (t * a.H + zhead) * (kTile * kTile) + n * kTile + 4 * h;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       x[2 * b] = *reinterpret_cast<const float4*>(cj + 16 * b);
@@ -555,6 +556,32 @@ struct ResLds {
   static size_t bytes(int W) { return (size_t)4 * (3 * W * kTile * kTile + 3 * kTile * kARow + kTile); }
 };
 
+// LDS of the resident kernel with H heads (MH): per wave a V tile (staging,
+// then the S partial, then the dV output tile) and a dout tile (staging, then
+// the A partial), the diagonal of each wave's G partial, each head's stage-2
+// operands (alpha and r c, 8 x 64 uint4), the diag(-coef) operands shared by
+// the heads (4 x 64 uint4) and each head's partial coef sums.
+struct ResLdsMH {
+  int W, H;
+  __device__ float* tile_v(char* base, int w) const { return reinterpret_cast<float*>(base) + w * kTile * kTile; }
+  __device__ float* tile_d(char* base, int w) const {
+    return reinterpret_cast<float*>(base) + (W + w) * kTile * kTile;
+  }
+  __device__ float* gdiag(char* base, int w) const {
+    return reinterpret_cast<float*>(base) + 2 * W * kTile * kTile + w * kTile;
+  }
+  __device__ uint4* bpk(char* base, int hh) const {
+    return reinterpret_cast<uint4*>(gdiag(base, W)) + hh * 8 * 64;
+  }
+  __device__ uint4* cdiag(char* base) const { return bpk(base, H); }
+  __device__ float* cpart(char* base, int hh) const {
+    return reinterpret_cast<float*>(cdiag(base) + 4 * 64) + hh * kTile;
+  }
+  static size_t bytes(int W, int H) {
+    return (size_t)4 * (2 * W * kTile * kTile + W * kTile) + (size_t)16 * 64 * (8 * H + 4) + (size_t)4 * H * kTile;
+  }
+};
+
 // 16-byte load at byte voff + soff of a buffer whose base is uniform over the
 // wave: the base and the (constant) soff live in scalar registers.
 __device__ __forceinline__ uint4 res_ld(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
@@ -565,7 +592,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t res_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, kBufferWord3);
 }
 
-template <bool ACC>
+// MH: H = 2, 4 or 8 heads of whole waves (W / H waves each, d / H channels),
+// each with its own depth softmax (MHAR abstract); the RMS and its term in dv
+// stay over the whole d.  The first wave of each head sums the head's S and A
+// partials and forms alpha, c, r c and c s in registers: its accumulators
+// already hold one source per lane and the destinations in stage 2's operand
+// order, so the operands are written as they are.  r c goes to the Z kernel
+// per head ([T][H][32][32]).
+template <bool ACC, bool MH>
 __global__ __launch_bounds__(512, 1) void k_full_bwd_res(FullBwdArgs a, const uint4* qpk, const uint4* qt,
                                                           float* cws) {
   extern __shared__ __attribute__((aligned(16))) char res_smem[];
@@ -573,6 +607,9 @@ __global__ __launch_bounds__(512, 1) void k_full_bwd_res(FullBwdArgs a, const ui
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: the wave's buffer bases stay scalar
   const int W = (int)blockDim.x >> 6;
   const ResLds L{W};
+  const ResLdsMH M{W, MH ? a.H : 1};
+  const int gw = MH ? W / a.H : W;        // waves per head
+  const int head = MH ? wave / gw : 0;
   const int d = (int)a.d, n_src = (int)a.n_src, n_dst = (int)a.n_dst;
   const int64_t T = a.T;
   const bf16_t* src = static_cast<const bf16_t*>(a.src);
@@ -594,8 +631,19 @@ __global__ __launch_bounds__(512, 1) void k_full_bwd_res(FullBwdArgs a, const ui
   const uint32_t voff0 = (uint32_t)(((int64_t)r0 * T * d + cbase) * 2);
   const uint32_t vclamp = (uint32_t)(((int64_t)(n_src - 1) * T * d + cbase) * 2);
   const uint32_t dclamp = (uint32_t)(((int64_t)(n_dst - 1) * T * d + cbase) * 2);
-  auto voff = [&](int u) { return 8 * u + r0 < n_src ? voff0 + (uint32_t)u * row8 : vclamp; };
-  auto doff = [&](int u) { return 8 * u + r0 < n_dst ? voff0 + (uint32_t)u * row8 : dclamp; };
+  // Recomputed at each use from an opaque copy of the base, so that the
+  // compiler does not keep all eight offsets live (and spill them) across the
+  // token loop.
+  auto voff = [&](int u) {
+    uint32_t b = voff0;
+    asm volatile("" : "+v"(b));
+    return 8 * u + r0 < n_src ? b + (uint32_t)u * row8 : vclamp;
+  };
+  auto doff = [&](int u) {
+    uint32_t b = voff0;
+    asm volatile("" : "+v"(b));
+    return 8 * u + r0 < n_dst ? b + (uint32_t)u * row8 : dclamp;
+  };
   // Query operands of this wave's k-steps and 32-channel blocks: k-step s at
   // byte 2048 s (+ 1024 for the low part), block b2 at 4096 b2 (+ 1024 per
   // operand), lane at 16 lane.
@@ -614,8 +662,8 @@ __global__ __launch_bounds__(512, 1) void k_full_bwd_res(FullBwdArgs a, const ui
     for (int c = 0; c < kRK / 4; ++c)
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        vr[4 * c + u] = res_ld(vrs, voff(u) + 128u * c, 0);
-        dr[4 * c + u] = res_ld(drs, doff(u) + 128u * c, 0);
+        vr[4 * c + u] = res_ld(vrs, voff(u), 128 * c);
+        dr[4 * c + u] = res_ld(drs, doff(u), 128 * c);
       }
   };
   if ((int64_t)blockIdx.x < T) load_rows(blockIdx.x);
@@ -638,8 +686,8 @@ __global__ __launch_bounds__(512, 1) void k_full_bwd_res(FullBwdArgs a, const ui
       }
       // This wave's staging tiles: the partial-sum rows of S and G, unused
       // until the partials are written (after a barrier).
-      unsigned char* vt = reinterpret_cast<unsigned char*>(L.sred(res_smem, wave));
-      unsigned char* dt = reinterpret_cast<unsigned char*>(L.gred(res_smem, wave));
+      unsigned char* vt = reinterpret_cast<unsigned char*>(MH ? M.tile_v(res_smem, wave) : L.sred(res_smem, wave));
+      unsigned char* dt = reinterpret_cast<unsigned char*>(MH ? M.tile_d(res_smem, wave) : L.gred(res_smem, wave));
 #pragma unroll
       for (int s = 0; s < kRK; ++s) {
         if (s % 4 == 0) {
@@ -684,19 +732,111 @@ __global__ __launch_bounds__(512, 1) void k_full_bwd_res(FullBwdArgs a, const ui
       int rl = lane;
       asm volatile("" : "+v"(rl));
       const int base = 4 * (rl >> 5) * kTile + (rl & 31);
-      float* sr = L.sred(res_smem, wave) + base;
-      float* ar = L.ared(res_smem, wave) + base;
-      float* gr = L.gred(res_smem, wave) + base;
+      if constexpr (MH) {
+        float* sr = M.tile_v(res_smem, wave) + base;
+        float* ar = M.tile_d(res_smem, wave) + base;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int off = (8 * (r / 4) + (r % 4)) * kTile;
-        sr[off] = S[r];
-        ar[off] = A[r];
-        gr[off] = G[r];
+        for (int r = 0; r < 16; ++r) {
+          const int off = (8 * (r / 4) + (r % 4)) * kTile;
+          sr[off] = S[r];
+          ar[off] = A[r];
+          if (8 * (r / 4) + 4 * (rl >> 5) + (r % 4) == (rl & 31)) M.gdiag(res_smem, wave)[rl & 31] = G[r];
+        }
+      } else {
+        float* sr = L.sred(res_smem, wave) + base;
+        float* ar = L.ared(res_smem, wave) + base;
+        float* gr = L.gred(res_smem, wave) + base;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = (8 * (r / 4) + (r % 4)) * kTile;
+          sr[off] = S[r];
+          ar[off] = A[r];
+          gr[off] = G[r];
+        }
       }
     }
     lds_barrier();
 
+    if constexpr (MH) {
+      // ---------------- each head's first wave: alpha, c, r c, c s from its accumulators' layout
+      if (wave % gw == 0) {
+        int rl = lane;
+        asm volatile("" : "+v"(rl));
+        const int base = 4 * (rl >> 5) * kTile + (rl & 31);
+        float gv = 0.f;
+        for (int w2 = 0; w2 < W; ++w2) gv += M.gdiag(res_smem, w2)[n];
+        const float ri = 1.0f / sqrtf(gv / (float)d + a.eps);
+        // Lane (h, i = n), element r: destination j = 8 (r / 4) + 4 h + r % 4.
+        float al[16], rcv[16], csum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          // The head's S and A at (destination j, source n): the sum of its waves' partials.
+          float sv = 0.f, av = 0.f;
+          for (int w2 = head * gw; w2 < head * gw + gw; ++w2) {
+            sv += M.tile_v(res_smem, w2)[base + (8 * (r / 4) + (r % 4)) * kTile];
+            av += M.tile_d(res_smem, w2)[base + (8 * (r / 4) + (r % 4)) * kTile];
+          }
+          const int j = 8 * (r / 4) + 4 * h + (r % 4);
+          const bool ok = j < n_dst && n <= n_src - n_dst + j;
+          const float sc = ok ? ri * sv : -INFINITY;
+          const float m = group_max<32>(sc);
+          const float e = ok ? expf(sc - m) : 0.f;
+          const float l = group_sum<32>(e);
+          al[r] = l > 0.f ? e / l : 0.f;
+          const float sa = group_sum<32>(al[r] * av);
+          const float cc = al[r] * (av - sa);
+          rcv[r] = ok ? ri * cc : 0.f;
+          csum += ok ? cc * sc : 0.f;
+        }
+        // Operands: k-step b, element e is destination transposed_row(b, h, e) = element 8 b + e.
+        uint4* bp = M.bpk(res_smem, head);
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const float* x = k2 == 0 ? al : rcv;
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            float hi[8], lo[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              hi[e] = bf2f(f2bf(x[8 * b + e]));
+              lo[e] = x[8 * b + e] - hi[e];
+            }
+            bp[(4 * k2 + 2 * b) * 64 + lane] = pack8(hi[0], hi[1], hi[2], hi[3], hi[4], hi[5], hi[6], hi[7]);
+            bp[(4 * k2 + 2 * b + 1) * 64 + lane] = pack8(lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]);
+          }
+        }
+        // r c for the Z kernel: [T][H][32][32] fp32, row j, column i = n.
+        float* cw = cws + ((t * a.H + head) * kTile) * kTile + n;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cw[(8 * (r / 4) + 4 * h + (r % 4)) * kTile] = rcv[r];
+        // sum over the destinations of c s for source n: this half's 16, then the other half's.
+        csum += __shfl_xor(csum, 32);
+        if (h == 0) M.cpart(res_smem, head)[n] = csum;
+      }
+      lds_barrier();
+      if (wave == 0) {
+        // coef_i = r_i^2 (sum over heads and destinations of c s) / d, as diag(-coef) operands.
+        float cs = 0.f, gv = 0.f;
+        for (int hh = 0; hh < a.H; ++hh) cs += M.cpart(res_smem, hh)[n];
+        for (int w2 = 0; w2 < W; ++w2) gv += M.gdiag(res_smem, w2)[n];
+        const float r2 = 1.0f / (gv / (float)d + a.eps);
+        const float cn = n < n_src ? -(r2 * cs / (float)d) : 0.f;
+        uint4* cd = M.cdiag(res_smem);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          float hi[8], lo[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float x = transposed_row(b, h, e) == n ? cn : 0.f;
+            hi[e] = bf2f(f2bf(x));
+            lo[e] = x - hi[e];
+          }
+          cd[(2 * b) * 64 + lane] = pack8(hi[0], hi[1], hi[2], hi[3], hi[4], hi[5], hi[6], hi[7]);
+          cd[(2 * b + 1) * 64 + lane] = pack8(lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]);
+        }
+      }
+      lds_barrier();
+    } else {
     // ---------------- per (destination, source): alpha, c, r c, c s (threads 0..255)
     float* t_alpha = L.table(res_smem, 0);
     float* t_rc = L.table(res_smem, 1);
@@ -764,7 +904,6 @@ __global__ __launch_bounds__(512, 1) void k_full_bwd_res(FullBwdArgs a, const ui
     // partials' space, dead now): lane (h, n = source i), element e <-> row
     // k = transposed_row(b, h, e) of alpha[k][i] (slots 0..3), (r c)[k][i]
     // (4..7) and diag(-coef) (8..11), each split into bf16 high and low parts.
-    const uint4* bpk_r = reinterpret_cast<const uint4*>(L.ared(res_smem, 0));
     uint4* bpk = reinterpret_cast<uint4*>(L.ared(res_smem, 0));
     {
       auto store_split = [&](const float (&x)[8], int slot) {
@@ -804,6 +943,8 @@ __global__ __launch_bounds__(512, 1) void k_full_bwd_res(FullBwdArgs a, const ui
     }
     lds_barrier();
 
+    }  // one head
+
     // ---------------- stage 2: dV^T = dOut^T alpha^T + Q^T (r c)^T - V^T diag(coef), per 32 channels
     // Block b uses the rows in registers 2 b, 2 b + 1 of vr and dr.  Every L2
     // load (the Q^T operands) is issued before the first load of the next
@@ -818,13 +959,18 @@ __global__ __launch_bounds__(512, 1) void k_full_bwd_res(FullBwdArgs a, const ui
     // dV is staged through this wave's LDS tile (a 64-channel chunk at a
     // time) and leaves as whole-row stores.
     {
-      unsigned char* ot = reinterpret_cast<unsigned char*>(L.sred(res_smem, wave));
+      unsigned char* ot = reinterpret_cast<unsigned char*>(MH ? M.tile_v(res_smem, wave) : L.sred(res_smem, wave));
+      // alpha and r c operands (slots 0..7) and diag(-coef) (slots 8..11).
+      const uint4* opa = MH ? M.bpk(res_smem, head) : reinterpret_cast<const uint4*>(L.ared(res_smem, 0));
+      const uint4* opc = MH ? M.cdiag(res_smem) : reinterpret_cast<const uint4*>(L.ared(res_smem, 0)) + 8 * 64;
       const __amdgpu_buffer_rsrc_t ors = res_rsrc(dsrc + t * d);
       const __amdgpu_buffer_rsrc_t nvrs = res_rsrc(src + (more ? tn : t) * d);
       const __amdgpu_buffer_rsrc_t ndrs = res_rsrc(dout + (more ? tn : t) * d);
       auto refill = [&](int x) {
-        vr[x] = res_ld(nvrs, voff(x % 4) + 128u * (x / 4), 0);
-        dr[x] = res_ld(ndrs, doff(x % 4) + 128u * (x / 4), 0);
+        // the chunk's 128-byte step as the scalar offset: only the row offsets
+        // (voff, doff) take vector registers
+        vr[x] = res_ld(nvrs, voff(x % 4), 128 * (x / 4));
+        dr[x] = res_ld(ndrs, doff(x % 4), 128 * (x / 4));
       };
       uint4 qc[4];
 #pragma unroll
@@ -836,7 +982,8 @@ __global__ __launch_bounds__(512, 1) void k_full_bwd_res(FullBwdArgs a, const ui
         // compiler from loading them once and holding 48 registers.
         int boff = lane;
         asm volatile("" : "+v"(boff));
-        const uint4* bl = bpk + boff;
+        const uint4* bl = opa + boff;
+        const uint4* blc = opc + boff - 8 * 64;  // blc[k * 64] for slots k = 8 .. 11
         f16acc D = {};
         {
           f16acc D3 = {};
@@ -856,10 +1003,10 @@ __global__ __launch_bounds__(512, 1) void k_full_bwd_res(FullBwdArgs a, const ui
           D1 = mfma(vr[s1], ip1, D1);
           const uint4 tv0 = pack8(D1[0], D1[1], D1[2], D1[3], D1[4], D1[5], D1[6], D1[7]);
           const uint4 tv1 = pack8(D1[8], D1[9], D1[10], D1[11], D1[12], D1[13], D1[14], D1[15]);
-          D = mfma(tv0, bl[8 * 64], D);   // -coef, b = 0
-          D = mfma(tv0, bl[9 * 64], D);
-          D = mfma(tv1, bl[10 * 64], D);  // -coef, b = 1
-          D = mfma(tv1, bl[11 * 64], D);
+          D = mfma(tv0, blc[8 * 64], D);   // -coef, b = 0
+          D = mfma(tv0, blc[9 * 64], D);
+          D = mfma(tv1, blc[10 * 64], D);  // -coef, b = 1
+          D = mfma(tv1, blc[11 * 64], D);
         }
         __builtin_amdgcn_sched_barrier(0);
         {
@@ -919,9 +1066,9 @@ __global__ __launch_bounds__(512, 1) void k_full_bwd_res(FullBwdArgs a, const ui
             const int row = 8 * u + (ol >> 3);
             uint4 y = *reinterpret_cast<const uint4*>(ot + rb + u * 8 * kVRow);
             if (row < n_src) {
-              const uint32_t off = voff(u) + 128u * c;
+              const uint32_t off = voff(u);
               if constexpr (ACC) {
-                const uint4 o = res_ld(ors, off, 0);
+                const uint4 o = res_ld(ors, off, 128 * c);
                 const uint32_t yw[4] = {y.x, y.y, y.z, y.w}, ow[4] = {o.x, o.y, o.z, o.w};
                 uint32_t rw[4];
 #pragma unroll
@@ -929,7 +1076,7 @@ __global__ __launch_bounds__(512, 1) void k_full_bwd_res(FullBwdArgs a, const ui
                   rw[k] = pack_bf2(bf_lo(yw[k]) + bf_lo(ow[k]), bf_hi(yw[k]) + bf_hi(ow[k]));
                 y = make_uint4(rw[0], rw[1], rw[2], rw[3]);
               }
-              __builtin_amdgcn_raw_buffer_store_b128(v4u{y.x, y.y, y.z, y.w}, ors, (int)off, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b128(v4u{y.x, y.y, y.z, y.w}, ors, (int)off, 128 * c, 0);
             }
           }
           wave_lds_sync();  // the tile is rewritten by the next chunk
@@ -945,9 +1092,9 @@ int64_t z_groups(int64_t T) { return T < kZGroups ? T : kZGroups; }
 
 }  // namespace
 
-size_t full_bwd_fast_workspace_bytes(int64_t n_dst, int64_t T, int64_t d) {
-  // qpk [128 d] + qt [128 d] + (r c) [T][32][32] fp32 + Z slabs [groups][n_dst][d] fp32
-  return (size_t)256 * (size_t)d + (size_t)T * kTile * kTile * 4 + (size_t)z_groups(T) * n_dst * d * 4;
+size_t full_bwd_fast_workspace_bytes(int64_t n_dst, int64_t T, int64_t d, int H) {
+  // qpk [128 d] + qt [128 d] + (r c) [T][H][32][32] fp32 + Z slabs [groups][n_dst][d] fp32
+  return (size_t)256 * (size_t)d + (size_t)T * H * kTile * kTile * 4 + (size_t)z_groups(T) * n_dst * d * 4;
 }
 
 // The register-resident kernel: d = 1024 .. 2048 in steps of 256 (d / 256
@@ -955,14 +1102,17 @@ size_t full_bwd_fast_workspace_bytes(int64_t n_dst, int64_t T, int64_t d) {
 bool full_bwd_res_ok(const FullBwdArgs& a) {
   // Per-lane byte offsets of the rows from a token's base are 32-bit.
   const int64_t span = std::max(a.n_src, a.n_dst) * a.T * a.d * 2;
-  return a.d >= 1024 && a.d <= 2048 && a.d % 256 == 0 && span < ((int64_t)1 << 31);
+  if (a.d < 1024 || a.d > 2048 || a.d % 256 != 0 || span >= ((int64_t)1 << 31)) return false;
+  // Heads: H = 2, 4 or 8 runs of whole waves (d / 256 waves).
+  return a.H == 1 || ((a.H == 2 || a.H == 4 || a.H == 8) && (a.d / kRCh) % a.H == 0);
 }
 
 bool full_bwd_fast_ok(const FullBwdArgs& a) {
-  if (a.dtype != kBF16 || a.H != 1 || a.T < 1) return false;
+  if (a.dtype != kBF16 || a.T < 1) return false;
+  if (a.H != 1 && !full_bwd_res_ok(a)) return false;  // heads: the resident kernel only
   if (a.n_src > kTile || a.n_dst > a.n_src) return false;
   if ((!full_bwd_res_ok(a) && a.d % (2 * kBW * kChunk) != 0) || a.d > ((int64_t)1 << 16)) return false;
-  if (a.zslots == nullptr || a.ws_bytes < full_bwd_fast_workspace_bytes(a.n_dst, a.T, a.d)) return false;
+  if (a.zslots == nullptr || a.ws_bytes < full_bwd_fast_workspace_bytes(a.n_dst, a.T, a.d, a.H)) return false;
   return al16(a.src) && al16(a.dout) && al16(a.d_src) && al16(a.zslots) && al16(a.w) && al16(a.gain);
 }
 
@@ -976,20 +1126,23 @@ hipError_t launch_full_bwd_fast(const FullBwdArgs& a, const float** slabs, int64
   uint4* qpk = reinterpret_cast<uint4*>(ws);
   uint4* qt = reinterpret_cast<uint4*>(ws + 128 * a.d);
   float* cws = reinterpret_cast<float*>(ws + 256 * a.d);
-  float* zs = cws + a.T * kTile * kTile;
+  float* zs = cws + a.T * a.H * kTile * kTile;  // (r c) is [T][H][32][32]
   hipLaunchKernelGGL(k_full_bwd_qsplit, dim3(64), dim3(256), 0, st, a, qpk);
   if (full_bwd_res_ok(a)) {
     hipLaunchKernelGGL(k_full_qtsplit<true>, dim3(64), dim3(256), 0, st, a, qt);
     const int W = (int)(a.d / kRCh);
-    const size_t lds = ResLds::bytes(W);
-    auto kern = a.accumulate ? k_full_bwd_res<true> : k_full_bwd_res<false>;
-    static std::atomic<bool> allowed[2] = {false, false};
-    if (!allowed[a.accumulate ? 1 : 0].load(std::memory_order_relaxed)) {
+    const bool mh = a.H > 1;
+    const size_t lds = mh ? ResLdsMH::bytes(W, (int)a.H) : ResLds::bytes(W);
+    const int which = (a.accumulate ? 1 : 0) + (mh ? 2 : 0);
+    auto kern = a.accumulate ? (mh ? k_full_bwd_res<true, true> : k_full_bwd_res<true, false>)
+                             : (mh ? k_full_bwd_res<false, true> : k_full_bwd_res<false, false>);
+    static std::atomic<bool> allowed[4] = {false, false, false, false};
+    if (!allowed[which].load(std::memory_order_relaxed)) {
+      const size_t most = std::max(ResLds::bytes(2048 / kRCh), ResLdsMH::bytes(2048 / kRCh, 8));
       const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (int)ResLds::bytes(2048 / kRCh));
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)most);
       if (e != hipSuccess) return e;
-      allowed[a.accumulate ? 1 : 0].store(true, std::memory_order_relaxed);
+      allowed[which].store(true, std::memory_order_relaxed);
     }
     int per_cu = 0;
     const hipError_t e = blocks_per_cu(reinterpret_cast<const void*>(kern), W * 64, &per_cu, lds);

@@ -167,7 +167,7 @@ hipError_t launch_full_bwd_reduce(const FullBwdArgs& a, const float* slabs, int6
 bool full_bwd_fast_ok(const FullBwdArgs& a);
 // Name of the specialised Full backward variant a call runs (nullptr: the general kernel).
 const char* full_bwd_fast_variant(const FullBwdArgs& a);
-size_t full_bwd_fast_workspace_bytes(int64_t n_dst, int64_t T, int64_t d);
+size_t full_bwd_fast_workspace_bytes(int64_t n_dst, int64_t T, int64_t d, int H);
 hipError_t launch_full_bwd_fast(const FullBwdArgs& a, const float** slabs, int64_t* n_slabs, hipStream_t st);
 
 // Specialised gfx950 kernels.  The *_ok predicates are pure functions of the

@@ -351,6 +351,12 @@ def test_full_bwd_workspace_size():
         want = max(general(n_dst, T, d), fast(n_dst, T, d))
         assert binding.attnres_full_bwd_workspace_size(n_src, n_dst, T, d, 1) == want
     assert binding.attnres_full_bwd_workspace_size(32, 32, 4096, 2048, 1) == 1024 * 32 * 2048 * 4
+    # heads: r * c per head, T x H x 32 x 32 fp32
+    fast_h = lambda n_dst, T, d, H: 256 * d + T * 4096 * H + min(T, 64) * n_dst * d * 4
+    assert binding.attnres_full_bwd_workspace_size(8, 8, 1000, 2048, 8) == max(
+        general(8, 1000, 2048), fast_h(8, 1000, 2048, 8))
+    assert binding.attnres_full_bwd_workspace_size(32, 1, 40, 1024, 4) == max(
+        general(1, 40, 1024), fast_h(1, 40, 1024, 4))
     assert binding.attnres_full_bwd_workspace_size(8, 3, 0, 64, 1) == 0
     assert binding.attnres_full_bwd_workspace_size(8, 0, 16, 64, 1) == 0
 

@@ -106,6 +106,13 @@ def test_phase2_full_and_policy():
     assert variant(binding.OP_FULL_BWD, 32, 32, 100, 4096) == "full_bwd_fast"
     assert variant(binding.OP_FULL_BWD, 32, 32, 100, 512) == "full_bwd_fast"
     assert variant(binding.OP_FULL_BWD, 33, 33, 100, 2048) == "full_bwd_generic"
+    # heads on the resident kernel: runs of whole 256-channel waves
+    assert variant(binding.OP_FULL_BWD, 32, 32, 100, 2048, H=8) == "full_bwd_res"
+    assert variant(binding.OP_FULL_BWD, 32, 32, 100, 1024, H=4) == "full_bwd_res"
+    assert variant(binding.OP_FULL_BWD, 32, 32, 100, 1536, H=2) == "full_bwd_res"
+    assert variant(binding.OP_FULL_BWD, 32, 32, 100, 1024, H=8) == "full_bwd_generic"
+    assert variant(binding.OP_FULL_BWD, 32, 32, 100, 1536, H=4) == "full_bwd_generic"
+    assert variant(binding.OP_FULL_BWD, 32, 32, 100, 4096, H=8) == "full_bwd_generic"
     prev = binding.attnres_set_kernel_policy(1)
     try:
         assert phase1(8, 4, 4096) == "phase1_generic"

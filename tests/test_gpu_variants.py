@@ -11,8 +11,9 @@ is compared with the oracle on the same seeded inputs:
   * the Full forward's matrix-core kernel with heads (H = 2, 4, 8; d = 512 ..
     2048), with one token per workgroup (query operands formed in the
     kernel) and with several;
-  * the Full backward's register-resident kernel (d = 1024 .. 2048) and the
-    staged one, over source / destination counts, gains and accumulation;
+  * the Full backward's register-resident kernel (d = 1024 .. 2048, one head
+    or H = 2, 4, 8 heads of whole waves) and the staged one, over source /
+    destination counts, gains and accumulation;
   * a sharply peaked depth softmax (scores in the hundreds), where the
     merge's exp(lse - m) underflows to zero.
 
@@ -154,7 +155,7 @@ def test_peaked_softmax(H, policy):
         ar.attnres_set_kernel_policy(prev)
 
 
-# (T, d, L, n_dst, gain, kernel)
+# (T, d, L, n_dst, gain, kernel[, H])
 FULL_BWD_CASES = [
     (300, 2048, 32, 32, "per", "full_bwd_res"),
     (517, 1024, 17, 5, "shared", "full_bwd_res"),
@@ -164,6 +165,13 @@ FULL_BWD_CASES = [
     (261, 2048, 20, 13, "shared", "full_bwd_res"),
     (40, 4096, 32, 32, "per", "full_bwd_fast"),
     (333, 512, 12, 7, "per", "full_bwd_fast"),
+    (300, 2048, 16, 16, "per", "full_bwd_res", 8),
+    (261, 2048, 20, 13, "shared", "full_bwd_res", 4),
+    (517, 1024, 17, 5, "none", "full_bwd_res", 2),
+    (403, 1024, 9, 9, "per", "full_bwd_res", 4),
+    (290, 1536, 12, 1, "per", "full_bwd_res", 2),
+    (7, 2048, 1, 1, "none", "full_bwd_res", 8),
+    (19, 2048, 32, 32, "per", "full_bwd_res", 8),
 ]
 
 
@@ -175,18 +183,20 @@ def _gain_arg(wl, gain, n_dst, d):
     return wl.gain
 
 
-@pytest.mark.parametrize("T,d,L,n_dst,gain,kernel", FULL_BWD_CASES)
-def test_full_bwd_variant(T, d, L, n_dst, gain, kernel):
-    name = ar.attnres_kernel_variant(ar.OP_FULL_BWD, L, n_dst, T, d, 1)
-    say(f"full bwd T={T} d={d} L={L} n_dst={n_dst} gain={gain}: {name}")
+@pytest.mark.parametrize("case", FULL_BWD_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_full_bwd_variant(case):
+    T, d, L, n_dst, gain, kernel = case[:6]
+    H = case[6] if len(case) > 6 else 1
+    name = ar.attnres_kernel_variant(ar.OP_FULL_BWD, L, n_dst, T, d, H)
+    say(f"full bwd T={T} d={d} L={L} n_dst={n_dst} H={H} gain={gain}: {name}")
     assert name == kernel, name
-    wl = synth.full_workload(T=T, d=d, L=L, std_step=0.2, dtype="bf16", seed=90 + L + n_dst, gain_variance=0.02,
+    wl = synth.full_workload(T=T, d=d, L=L, std_step=0.2, dtype="bf16", seed=90 + L + n_dst + H, gain_variance=0.02,
                              n_dst=n_dst, with_dout=True)
     g = _gain_arg(wl, gain, n_dst, d)
-    ref = orc.full_bwd(wl.src, wl.w, g, wl.eps, 1, wl.dh)
+    ref = orc.full_bwd(wl.src, wl.w, g, wl.eps, H, wl.dh)
     src, w, dout = dev(wl.src, True), dev(wl.w), dev(wl.dh, True)
     gd = dev(g) if g is not None else None
-    got = ar.attnres_full_bwd(src, w, dout, gd, wl.eps, 1)
+    got = ar.attnres_full_bwd(src, w, dout, gd, wl.eps, H)
     check(host(got[0]), ref[0], "bf16", "d_src")
     check(host(got[1]), ref[1], "f32_from_bf16", "dw")
     if g is not None:
@@ -195,15 +205,17 @@ def test_full_bwd_variant(T, d, L, n_dst, gain, kernel):
     rng = np.random.default_rng(T)
     base = synth.bf16_round(rng.standard_normal(wl.src.shape).astype(np.float32))
     d_src = dev(base, True)
-    ar.attnres_full_bwd(src, w, dout, gd, wl.eps, 1, d_src=d_src, accumulate=True)
+    ar.attnres_full_bwd(src, w, dout, gd, wl.eps, H, d_src=d_src, accumulate=True)
     check(host(d_src), base + ref[0], "bf16", "d_src accumulated")
-    # the general kernel on the same inputs: the same d_src within the bar
-    prev = ar.attnres_set_kernel_policy(1)
-    try:
-        gen = ar.attnres_full_bwd(src, w, dout, gd, wl.eps, 1)
-    finally:
-        ar.attnres_set_kernel_policy(prev)
-    check(host(gen[0]), ref[0], "bf16", "d_src (general kernel)")
+    # the general kernel on the same inputs (where its tables hold the shape):
+    # the same d_src within the bar
+    if n_dst * H * L <= 1024:
+        prev = ar.attnres_set_kernel_policy(1)
+        try:
+            gen = ar.attnres_full_bwd(src, w, dout, gd, wl.eps, H)
+        finally:
+            ar.attnres_set_kernel_policy(prev)
+        check(host(gen[0]), ref[0], "bf16", "d_src (general kernel)")
 
 
 # (T, d, L, n_dst, H, gain)
