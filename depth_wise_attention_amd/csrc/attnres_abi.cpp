@@ -379,7 +379,7 @@ int attnres_kernel_variant(int32_t op, int64_t N, int64_t S, int64_t T, int64_t 
     case ATTNRES_OP_FULL_FWD: {
       FullArgs a{p, N, T, d, fp, S, fp, d, 1e-6f, H, dtype, p, p,
                  attnres_full_fwd_workspace_size(N, S, d, H, dtype)};
-      snprintf(buf, len, "%s", fast && full_fast_ok(a) ? "full_fast" : "full_generic");
+      snprintf(buf, len, "%s", fast && full_fast_ok(a) ? full_fast_variant(a) : "full_generic");
       return ATTNRES_OK;
     }
     case ATTNRES_OP_FULL_BWD: {

@@ -662,6 +662,7 @@ bool resident_shape(int64_t d, int H) {
 }  // namespace
 
 size_t full_fast_workspace_bytes(int64_t n_src, int64_t n_dst, int64_t d, int H, int dtype) {
+  if (full_wide_shape(n_src, n_dst, d, H, dtype)) return full_wide_workspace_bytes(n_dst, d);
   if (dtype != kBF16 || n_src > kTile || n_dst > n_src) return 0;
   if (H != 1 && !resident_shape(d, H)) return 0;
   return (size_t)2 * kTile * (size_t)d * sizeof(bf16_t);
@@ -669,6 +670,10 @@ size_t full_fast_workspace_bytes(int64_t n_src, int64_t n_dst, int64_t d, int H,
 
 bool full_fast_ok(const FullArgs& a) {
   if (a.dtype != kBF16 || a.T < 1) return false;
+  if (full_wide_shape(a.n_src, a.n_dst, a.d, a.H, a.dtype)) {
+    if (a.ws == nullptr || a.ws_bytes < full_wide_workspace_bytes(a.n_dst, a.d)) return false;
+    return al16(a.src) && al16(a.out) && al16(a.ws) && al16(a.w) && al16(a.gain);
+  }
   if (a.H != 1 && !resident_shape(a.d, a.H)) return false;  // heads: the resident kernel only
   if (a.n_src > kTile || a.n_dst > a.n_src) return false;
   // Each wave streams an even number of whole 64-channel chunks.
@@ -697,7 +702,12 @@ hipError_t launch_resident_h(const FullArgs& a, const bf16_t* qpk, hipStream_t s
   return a.H > 1 ? launch_resident<NCH, true>(a, qpk, st) : launch_resident<NCH, false>(a, qpk, st);
 }
 
+const char* full_fast_variant(const FullArgs& a) {
+  return full_wide_shape(a.n_src, a.n_dst, a.d, a.H, a.dtype) ? "full_wide" : "full_fast";
+}
+
 hipError_t launch_full_fast(const FullArgs& a, hipStream_t st) {
+  if (full_wide_shape(a.n_src, a.n_dst, a.d, a.H, a.dtype)) return launch_full_wide(a, st);
   bf16_t* qpk = static_cast<bf16_t*>(a.ws);
   if (resident_shape(a.d, a.H)) {
     switch (a.d / (kRW * kChunk)) {

@@ -100,8 +100,10 @@ int attnres_full_fwd(const void* src, int64_t n_src, int64_t T, int64_t d,
  * Bytes of device workspace attnres_full_fwd needs.  bf16 calls with n_src <=
  * 32 and either one head or H = 2, 4 or 8 heads with d = 512 .. 2048 in steps
  * of 512 may run the contractions on the matrix cores, which take q = w * gain
- * as a bf16 high part plus a bf16 low part ([2, 32, d] bf16, 128 * d bytes);
- * every other request needs none and gets 0.
+ * as a bf16 high part plus a bf16 low part ([2, 32, d] bf16, 128 * d bytes).
+ * So may one-head bf16 calls with 33 .. 64 sources and d a multiple of 512:
+ * [2, 32, d] for n_dst <= 32, [2, 64, d] (256 * d bytes) above.  Every other
+ * request needs none and gets 0.
  */
 size_t attnres_full_fwd_workspace_size(int64_t n_src, int64_t n_dst, int64_t d, int32_t H,
                                        int32_t dtype);

@@ -95,7 +95,13 @@ def test_full_workspace_size():
     for H in (2, 4, 8):
         assert binding.attnres_full_fwd_workspace_size(8, 8, 2048, H, BF16) == 2 * 32 * 2048 * 2
         assert binding.attnres_full_fwd_workspace_size(32, 1, 512, H, BF16) == 2 * 32 * 512 * 2
-    for args in [(32, 32, 2048, 1, F32), (33, 1, 2048, 1, BF16), (8, 8, 2048, 16, BF16), (8, 8, 4096, 8, BF16),
+    # 33 .. 64 sources, one head, d a multiple of 512: one [2, 32, d] block per 32 destinations.
+    assert binding.attnres_full_fwd_workspace_size(33, 1, 2048, 1, BF16) == 2 * 32 * 2048 * 2
+    assert binding.attnres_full_fwd_workspace_size(55, 32, 4096, 1, BF16) == 2 * 32 * 4096 * 2
+    assert binding.attnres_full_fwd_workspace_size(55, 54, 2048, 1, BF16) == 2 * 64 * 2048 * 2
+    assert binding.attnres_full_fwd_workspace_size(64, 33, 512, 1, BF16) == 2 * 64 * 512 * 2
+    for args in [(32, 32, 2048, 1, F32), (33, 1, 2048, 2, BF16), (33, 1, 768, 1, BF16), (65, 1, 2048, 1, BF16),
+                 (40, 40, 2048, 1, F32), (8, 8, 2048, 16, BF16), (8, 8, 4096, 8, BF16),
                  (8, 8, 2048, 3, BF16), (4, 5, 64, 1, BF16), (0, 0, 64, 1, BF16), (4, 4, 0, 1, BF16)]:
         assert binding.attnres_full_fwd_workspace_size(*args) == 0, args
 

@@ -92,7 +92,12 @@ def test_phase2_full_and_policy():
     assert variant(binding.OP_PHASE2, 8, 4, 100, 2048, H=4) == "phase2_fast<CPL=4,MH=1>"
     assert variant(binding.OP_PHASE2, 8, 4, 100, 1024) == "phase2_generic"
     assert variant(binding.OP_FULL_FWD, 32, 32, 100, 2048) == "full_fast"
-    assert variant(binding.OP_FULL_FWD, 33, 33, 100, 2048) == "full_generic"
+    # 33 .. 64 sources: the two-tile kernel (one head, bf16, d a multiple of 512)
+    for L, n_dst, d in ((33, 33, 2048), (55, 54, 2048), (55, 1, 2048), (64, 64, 512), (40, 32, 4096),
+                        (47, 20, 1536), (64, 1, 2560)):
+        assert variant(binding.OP_FULL_FWD, L, n_dst, 100, d) == "full_wide", (L, n_dst, d)
+    assert variant(binding.OP_FULL_FWD, 55, 54, 100, 2048, H=8) == "full_generic"
+    assert variant(binding.OP_FULL_FWD, 55, 54, 100, 768) == "full_generic"
     # heads on the matrix cores: whole waves of the resident kernel (d <= 2048)
     for H in (2, 4, 8):
         for d in (512, 1024, 1536, 2048):

@@ -11,6 +11,8 @@ is compared with the oracle on the same seeded inputs:
   * the Full forward's matrix-core kernel with heads (H = 2, 4, 8; d = 512 ..
     2048), with one token per workgroup (query operands formed in the
     kernel) and with several;
+  * the Full forward over 33 .. 64 sources (two source tiles, one or two
+    destination tiles);
   * the Full backward's register-resident kernel (d = 1024 .. 2048, one head
     or H = 2, 4, 8 heads of whole waves) and the staged one, over source /
     destination counts, gains and accumulation;
@@ -248,6 +250,42 @@ def test_full_fwd_heads(T, d, L, n_dst, H, gain):
     prev = ar.attnres_set_kernel_policy(1)
     try:
         gen = ar.attnres_full_fwd(src, w, gd, wl.eps, H)
+    finally:
+        ar.attnres_set_kernel_policy(prev)
+    check(host(gen), ref, "bf16", "out (general kernel)")
+
+
+# Full forward over 33 .. 64 sources: (T, d, L, n_dst, gain).  Two source
+# tiles; n_dst > 32 takes two destination tiles.  T above the 512 resident
+# workgroups gives each several tokens and a ragged tail.
+FULL_WIDE_CASES = [
+    (530, 2048, 55, 54, "per"),
+    (1100, 1024, 33, 33, "shared"),
+    (600, 2048, 55, 1, "per"),
+    (300, 512, 64, 64, "none"),
+    (300, 4096, 40, 32, "per"),
+    (1, 2048, 55, 1, "none"),
+    (37, 1536, 47, 20, "shared"),
+    (513, 2560, 64, 1, "per"),
+]
+
+
+@pytest.mark.parametrize("T,d,L,n_dst,gain", FULL_WIDE_CASES)
+def test_full_fwd_wide(T, d, L, n_dst, gain):
+    name = ar.attnres_kernel_variant(ar.OP_FULL_FWD, L, n_dst, T, d, 1)
+    say(f"full fwd wide T={T} d={d} L={L} n_dst={n_dst} gain={gain}: {name}")
+    assert name == "full_wide", name
+    wl = synth.full_workload(T=T, d=d, L=L, std_step=0.2, dtype="bf16", seed=140 + L + n_dst, gain_variance=0.02,
+                             n_dst=n_dst)
+    g = _gain_arg(wl, gain, n_dst, d)
+    ref = orc.full_fwd(wl.src, wl.w, g, wl.eps, 1)
+    src, w = dev(wl.src, True), dev(wl.w)
+    gd = dev(g) if g is not None else None
+    out = ar.attnres_full_fwd(src, w, gd, wl.eps, 1)
+    check(host(out), ref, "bf16", "out")
+    prev = ar.attnres_set_kernel_policy(1)
+    try:
+        gen = ar.attnres_full_fwd(src, w, gd, wl.eps, 1)
     finally:
         ar.attnres_set_kernel_policy(prev)
     check(host(gen), ref, "bf16", "out (general kernel)")
