@@ -160,8 +160,22 @@ __global__ __launch_bounds__(kWB, 2) void k_full_wide(FullArgs a, const uint4* q
   const __amdgpu_buffer_rsrc_t qrs = wide_rsrc(qpk + (int64_t)(ch_base / kChunk) * 4 * TD * 2 * 64);
   const uint4 ident0 = ident_operand(0), ident1 = ident_operand(1);
 
-  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+  // Two chunks are always in flight: each chunk's slot is refilled with the
+  // chunk two ahead in the order stage 1 (chunks 0 .. nch - 1), stage 2 (0 ..
+  // nch - 1), the next token's stage 1, ...  So neither stage starts cold,
+  // and the loads stay in flight across the barriers and the softmax.
+  int64_t t = blockIdx.x;
+  uint4 va[8], vb[8];
+  if (t < T) {
+    wide_load(src + t * d + ch_base, plane, n_src, 0, va);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loop's load order (va, then vb)
+    wide_load(src + t * d + ch_base, plane, n_src, kChunk, vb);
+  }
+  for (; t < T; t += gridDim.x) {
     const bf16_t* tok = src + t * d + ch_base;
+    // The next token's rows (this token's again after the last one: loaded,
+    // never used, so that every path has the same loads in flight).
+    const bf16_t* tokn = src + (t + gridDim.x < T ? t + gridDim.x : t) * d + ch_base;
 
     // ---------------- stage 1: S = Q V^T and G = V V^T over this wave's channels
     f16acc S[TD][2], G[2];
@@ -177,7 +191,8 @@ __global__ __launch_bounds__(kWB, 2) void k_full_wide(FullArgs a, const uint4* q
         asm volatile("" : "+v"(ol));
         const uint32_t qoff = (uint32_t)ol * 16u + (uint32_t)c * (uint32_t)(4 * TD * 2 * 1024);
         wide_stage(vt, v, n_src);
-        wide_load(tok, plane, n_src, min(c + 2, nch - 1) * kChunk, v);  // unconditional: exact wait counts
+        // Chunk c + 2, or stage 2's chunk c + 2 - nch (the same rows again).
+        wide_load(tok, plane, n_src, (c + 2 < nch ? c + 2 : c + 2 - nch) * kChunk, v);
         wave_lds_sync();
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -203,10 +218,6 @@ __global__ __launch_bounds__(kWB, 2) void k_full_wide(FullArgs a, const uint4* q
         }
         wave_lds_sync();  // operand reads done before the tile is rewritten
       };
-      uint4 va[8], vb[8];
-      wide_load(tok, plane, n_src, 0, va);
-      __builtin_amdgcn_sched_barrier(0);  // keep the loop's load order (va, then vb)
-      wide_load(tok, plane, n_src, kChunk, vb);
       // The first pair is peeled so that the loop head sees the same
       // outstanding loads on entry as on the back edge.
       chunk1(0, va);
@@ -291,7 +302,8 @@ __global__ __launch_bounds__(kWB, 2) void k_full_wide(FullArgs a, const uint4* q
       unsigned char* obase = vt + 4 * h * kORow + 2 * n;
       auto chunk2 = [&](int c, uint4 (&v)[8]) {
         wide_stage(vt, v, n_src);
-        wide_load(tok, plane, n_src, min(c + 2, nch - 1) * kChunk, v);
+        // Chunk c + 2, or the next token's stage-1 chunk c + 2 - nch.
+        wide_load(c + 2 < nch ? tok : tokn, plane, n_src, (c + 2 < nch ? c + 2 : c + 2 - nch) * kChunk, v);
         wave_lds_sync();
         int ol = lane;
         asm volatile("" : "+v"(ol));
@@ -343,10 +355,6 @@ __global__ __launch_bounds__(kWB, 2) void k_full_wide(FullArgs a, const uint4* q
         }
         wave_lds_sync();  // the tile is rewritten by the next chunk
       };
-      uint4 va[8], vb[8];
-      wide_load(tok, plane, n_src, 0, va);
-      __builtin_amdgcn_sched_barrier(0);
-      wide_load(tok, plane, n_src, kChunk, vb);
       chunk2(0, va);
       chunk2(1, vb);
       for (int c = 2; c < nch; c += 2) {
