@@ -799,12 +799,11 @@ int attnres_bwd(const void* reps, int64_t N, const void* partials, int64_t S, in
 }
 
 size_t attnres_full_bwd_workspace_size(int64_t n_src, int64_t n_dst, int64_t T, int64_t d, int32_t H) {
-  (void)n_src;
   int64_t b, c;
-  if (n_dst < 1 || T < 1 || d < 1 || d > kMaxD || H < 1 || H > d) return 0;  // T == 0 needs none
+  if (n_src < 1 || n_dst < 1 || T < 1 || d < 1 || d > kMaxD || H < 1 || H > d) return 0;  // T == 0 needs none
   if (!mul3(full_bwd_slots(T), n_dst, d, &b) || !mul3(b, 4, 1, &b)) return 0;  // general path
-  if (!mul3(T, 4096, H, &c)) return 0;                                      // matrix-core path
-  const size_t fast = full_bwd_fast_workspace_bytes(n_dst, T, d, H);
+  if (!mul3(T, 8192, H, &c)) return 0;                                      // matrix-core path
+  const size_t fast = full_bwd_fast_workspace_bytes(n_src, n_dst, T, d, H);
   return (size_t)b > fast ? (size_t)b : fast;
 }
 

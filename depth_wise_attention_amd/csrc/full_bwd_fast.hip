@@ -1092,9 +1092,12 @@ int64_t z_groups(int64_t T) { return T < kZGroups ? T : kZGroups; }
 
 }  // namespace
 
-size_t full_bwd_fast_workspace_bytes(int64_t n_dst, int64_t T, int64_t d, int H) {
-  // qpk [128 d] + qt [128 d] + (r c) [T][H][32][32] fp32 + Z slabs [groups][n_dst][d] fp32
-  return (size_t)256 * (size_t)d + (size_t)T * H * kTile * kTile * 4 + (size_t)z_groups(T) * n_dst * d * 4;
+// Sources per row of the (r c) table: 32, or 64 for the two-tile kernel.
+int64_t rc_cols(int64_t n_src) { return n_src > kTile ? 2 * kTile : kTile; }
+
+size_t full_bwd_fast_workspace_bytes(int64_t n_src, int64_t n_dst, int64_t T, int64_t d, int H) {
+  // qpk [128 d] + qt [128 d] + (r c) [T][H][32][rc_cols] fp32 + Z slabs [groups][n_dst][d] fp32
+  return (size_t)256 * (size_t)d + (size_t)T * H * kTile * rc_cols(n_src) * 4 + (size_t)z_groups(T) * n_dst * d * 4;
 }
 
 // The register-resident kernel: d = 1024 .. 2048 in steps of 256 (d / 256
@@ -1109,15 +1112,22 @@ bool full_bwd_res_ok(const FullBwdArgs& a) {
 
 bool full_bwd_fast_ok(const FullBwdArgs& a) {
   if (a.dtype != kBF16 || a.T < 1) return false;
+  if (full_bwd_wide_shape(a)) {
+    if (a.zslots == nullptr || a.ws_bytes < full_bwd_fast_workspace_bytes(a.n_src, a.n_dst, a.T, a.d, a.H))
+      return false;
+    return al16(a.src) && al16(a.dout) && al16(a.d_src) && al16(a.zslots) && al16(a.w) && al16(a.gain);
+  }
   if (a.H != 1 && !full_bwd_res_ok(a)) return false;  // heads: the resident kernel only
   if (a.n_src > kTile || a.n_dst > a.n_src) return false;
   if ((!full_bwd_res_ok(a) && a.d % (2 * kBW * kChunk) != 0) || a.d > ((int64_t)1 << 16)) return false;
-  if (a.zslots == nullptr || a.ws_bytes < full_bwd_fast_workspace_bytes(a.n_dst, a.T, a.d, a.H)) return false;
+  if (a.zslots == nullptr || a.ws_bytes < full_bwd_fast_workspace_bytes(a.n_src, a.n_dst, a.T, a.d, a.H))
+    return false;
   return al16(a.src) && al16(a.dout) && al16(a.d_src) && al16(a.zslots) && al16(a.w) && al16(a.gain);
 }
 
 const char* full_bwd_fast_variant(const FullBwdArgs& a) {
   if (!full_bwd_fast_ok(a)) return nullptr;
+  if (full_bwd_wide_shape(a)) return "full_bwd_wide";
   return full_bwd_res_ok(a) ? "full_bwd_res" : "full_bwd_fast";
 }
 
@@ -1126,8 +1136,16 @@ hipError_t launch_full_bwd_fast(const FullBwdArgs& a, const float** slabs, int64
   uint4* qpk = reinterpret_cast<uint4*>(ws);
   uint4* qt = reinterpret_cast<uint4*>(ws + 128 * a.d);
   float* cws = reinterpret_cast<float*>(ws + 256 * a.d);
-  float* zs = cws + a.T * a.H * kTile * kTile;  // (r c) is [T][H][32][32]
+  float* zs = cws + a.T * a.H * kTile * rc_cols(a.n_src);  // (r c) is [T][H][32][rc_cols]
   hipLaunchKernelGGL(k_full_bwd_qsplit, dim3(64), dim3(256), 0, st, a, qpk);
+  if (full_bwd_wide_shape(a)) {
+    hipLaunchKernelGGL(k_full_qtsplit<false>, dim3(64), dim3(256), 0, st, a, qt);
+    const int groups = (int)z_groups(a.T);
+    const hipError_t e = launch_full_bwd_wide(a, qpk, qt, cws, zs, groups, st);
+    *slabs = zs;
+    *n_slabs = groups;
+    return e;
+  }
   if (full_bwd_res_ok(a)) {
     hipLaunchKernelGGL(k_full_qtsplit<true>, dim3(64), dim3(256), 0, st, a, qt);
     const int W = (int)(a.d / kRCh);

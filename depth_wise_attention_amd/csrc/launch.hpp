@@ -167,7 +167,13 @@ hipError_t launch_full_bwd_reduce(const FullBwdArgs& a, const float* slabs, int6
 bool full_bwd_fast_ok(const FullBwdArgs& a);
 // Name of the specialised Full backward variant a call runs (nullptr: the general kernel).
 const char* full_bwd_fast_variant(const FullBwdArgs& a);
-size_t full_bwd_fast_workspace_bytes(int64_t n_dst, int64_t T, int64_t d, int H);
+size_t full_bwd_fast_workspace_bytes(int64_t n_src, int64_t n_dst, int64_t T, int64_t d, int H);
+// Matrix-core Full backward over 33 .. 64 sources and up to 32 destinations
+// (full_bwd_wide.hip): the shapes it takes, and its two kernels after the query
+// packing (qpk, qt and the (r c) table cws and Z slabs zs in the workspace).
+bool full_bwd_wide_shape(const FullBwdArgs& a);
+hipError_t launch_full_bwd_wide(const FullBwdArgs& a, const uint4* qpk, const uint4* qt, float* cws, float* zs,
+                                int groups, hipStream_t st);
 hipError_t launch_full_bwd_fast(const FullBwdArgs& a, const float** slabs, int64_t* n_slabs, hipStream_t st);
 
 // Specialised gfx950 kernels.  The *_ok predicates are pure functions of the

@@ -349,7 +349,8 @@ def test_error_message_is_thread_local():
 def test_full_bwd_workspace_size():
     # the larger of the two paths' needs:
     #   general: one [n_dst, d] fp32 slab per wavefront, T rounded up to 4, at most 1024 slabs;
-    #   matrix cores: split q and q^T (256 d bytes) + r*c per token (T x 32 x 32 fp32)
+    #   matrix cores: split q and q^T (256 d bytes) + r*c per token (T x 32 x 32 fp32, or
+    #                 T x 32 x 64 with more than 32 sources)
     #                 + one [n_dst, d] fp32 slab per token group (min(T, 64) groups)
     general = lambda n_dst, T, d: min((T + 3) // 4 * 4, 1024) * n_dst * d * 4
     fast = lambda n_dst, T, d: 256 * d + T * 4096 + min(T, 64) * n_dst * d * 4
@@ -363,6 +364,11 @@ def test_full_bwd_workspace_size():
         general(8, 1000, 2048), fast_h(8, 1000, 2048, 8))
     assert binding.attnres_full_bwd_workspace_size(32, 1, 40, 1024, 4) == max(
         general(1, 40, 1024), fast_h(1, 40, 1024, 4))
+    # 33 .. 64 sources: r * c per token is T x 32 x 64 fp32
+    fast_w = lambda n_dst, T, d: 256 * d + T * 8192 + min(T, 64) * n_dst * d * 4
+    for n_src, n_dst, T, d in [(55, 1, 4096, 2048), (64, 32, 300, 512), (33, 33, 7, 1024)]:
+        want = max(general(n_dst, T, d), fast_w(n_dst, T, d))
+        assert binding.attnres_full_bwd_workspace_size(n_src, n_dst, T, d, 1) == want, (n_src, n_dst, T, d)
     assert binding.attnres_full_bwd_workspace_size(8, 3, 0, 64, 1) == 0
     assert binding.attnres_full_bwd_workspace_size(8, 0, 16, 64, 1) == 0
 

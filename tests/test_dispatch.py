@@ -110,7 +110,12 @@ def test_phase2_full_and_policy():
         assert variant(binding.OP_FULL_BWD, 17, 5, 100, d) == "full_bwd_res"
     assert variant(binding.OP_FULL_BWD, 32, 32, 100, 4096) == "full_bwd_fast"
     assert variant(binding.OP_FULL_BWD, 32, 32, 100, 512) == "full_bwd_fast"
+    # 33 .. 64 sources and up to 32 destinations: the two-tile backward (one head, d a multiple of 512)
+    for L, n_dst, d in ((33, 32, 2048), (55, 1, 2048), (64, 32, 512), (40, 7, 4096), (47, 20, 1536)):
+        assert variant(binding.OP_FULL_BWD, L, n_dst, 100, d) == "full_bwd_wide", (L, n_dst, d)
     assert variant(binding.OP_FULL_BWD, 33, 33, 100, 2048) == "full_bwd_generic"
+    assert variant(binding.OP_FULL_BWD, 55, 1, 100, 2048, H=2) == "full_bwd_generic"
+    assert variant(binding.OP_FULL_BWD, 55, 1, 100, 768) == "full_bwd_generic"
     # heads on the resident kernel: runs of whole 256-channel waves
     assert variant(binding.OP_FULL_BWD, 32, 32, 100, 2048, H=8) == "full_bwd_res"
     assert variant(binding.OP_FULL_BWD, 32, 32, 100, 1024, H=4) == "full_bwd_res"

@@ -12,7 +12,8 @@ is compared with the oracle on the same seeded inputs:
     2048), with one token per workgroup (query operands formed in the
     kernel) and with several;
   * the Full forward over 33 .. 64 sources (two source tiles, one or two
-    destination tiles);
+    destination tiles) and the backward over 33 .. 64 sources and up to 32
+    destinations;
   * the Full backward's register-resident kernel (d = 1024 .. 2048, one head
     or H = 2, 4, 8 heads of whole waves) and the staged one, over source /
     destination counts, gains and accumulation;
@@ -174,6 +175,13 @@ FULL_BWD_CASES = [
     (290, 1536, 12, 1, "per", "full_bwd_res", 2),
     (7, 2048, 1, 1, "none", "full_bwd_res", 8),
     (19, 2048, 32, 32, "per", "full_bwd_res", 8),
+    # 33 .. 64 sources, up to 32 destinations: two source tiles
+    (300, 2048, 55, 1, "per", "full_bwd_wide"),
+    (261, 1024, 33, 32, "shared", "full_bwd_wide"),
+    (530, 2048, 64, 32, "per", "full_bwd_wide"),
+    (40, 4096, 40, 7, "none", "full_bwd_wide"),
+    (7, 1536, 47, 20, "per", "full_bwd_wide"),
+    (1, 2048, 55, 1, "none", "full_bwd_wide"),
 ]
 
 
