@@ -10,7 +10,7 @@ in HBM before timing starts.
 Prints ONE JSON line on stdout.  Everything else goes to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                  [--no-extra] [--workload block|mhar|full|full_h8|bwd|full_bwd|full_bwd_h8|block_update|decode|msar|block_msar]
+                  [--no-extra] [--workload block|mhar|full|full_h8|full_wide|bwd|full_bwd|full_bwd_h8|block_update|decode|msar|block_msar]
                   [--copy-calibration]
 """
 
@@ -40,7 +40,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="block", choices=["block", "mhar", "full", "full_h8", "bwd", "mhar_bwd", "full_bwd", "full_bwd_h8", "block_update",
+    p.add_argument("--workload", default="block", choices=["block", "mhar", "full", "full_h8", "full_wide", "bwd", "mhar_bwd", "full_bwd", "full_bwd_h8", "block_update",
                                                                 "decode", "msar", "block_msar", "depth_sweep"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads")
@@ -462,6 +462,63 @@ def bench_full(args, T=4096, H=1):
                 kernel=ar.attnres_kernel_variant(ar.OP_FULL_FWD, L, L, T, d, H))
 
 
+def bench_full_wide(args, T=4096, d=2048, L=55):
+    """Full AttnRes with more sources than one 32-source tile: the deepest
+    sublayer of a 54-sublayer model reads L = 55 sources.  The forward with one
+    destination (the per-sublayer call) and with 54 (every destination at once),
+    and the backward with one and with 32 destinations, each timed with HIP
+    events around its launches.  Sources are seeded normal draws made on the
+    device, source i with standard deviation 1 + 0.2 i (the residual stream
+    grows with depth), w ~ N(0, 1/d), gain ~ 1 + N(0, 0.01)."""
+    import torch
+    import depth_wise_attention_amd as ar
+
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    stream = torch.cuda.current_stream()
+    src = torch.randn((L, T, d), generator=gen, device="cuda")
+    src *= (1 + 0.2 * torch.arange(L, device="cuda", dtype=torch.float32))[:, None, None]
+    src = src.to(torch.bfloat16)
+
+    def timed(fn, n):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3  # us
+
+    n = max(3, args.steps // 2)
+    cases = {}
+    for nd in (1, L - 1):
+        w = torch.randn((nd, d), generator=gen, device="cuda") / d ** 0.5
+        g = 1 + 0.1 * torch.randn((nd, d), generator=gen, device="cuda")
+        out = torch.empty((nd, T, d), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(max(1, ar.attnres_full_fwd_workspace_size(L, nd, d, 1, ar.BF16)), dtype=torch.uint8,
+                         device="cuda")
+        us = timed(lambda: ar.attnres_full_fwd(src, w, g, 1e-6, 1, out=out, ws=ws), n)
+        b = T * d * 2 * (L + nd)
+        cases[f"fwd_n_dst{nd}"] = dict(us=us, bytes=b, gbs=b / us / 1e3,
+                                       kernel=ar.attnres_kernel_variant(ar.OP_FULL_FWD, L, nd, T, d, 1))
+        del out, ws
+    for nd in (1, 32):
+        w = torch.randn((nd, d), generator=gen, device="cuda") / d ** 0.5
+        g = 1 + 0.1 * torch.randn((nd, d), generator=gen, device="cuda")
+        dout = torch.randn((nd, T, d), generator=gen, device="cuda").to(torch.bfloat16)
+        d_src = torch.empty_like(src)
+        dw, dg = torch.empty_like(w), torch.empty_like(g)
+        ws = torch.empty(ar.attnres_full_bwd_workspace_size(L, nd, T, d, 1), dtype=torch.uint8, device="cuda")
+        us = timed(lambda: ar.attnres_full_bwd(src, w, dout, g, 1e-6, 1, d_src=d_src, dw=dw, dgain=dg, ws=ws), n)
+        b = T * d * 2 * (2 * L + nd)  # read src and dout, write d_src
+        cases[f"bwd_n_dst{nd}"] = dict(us=us, bytes=b, gbs=b / us / 1e3,
+                                       kernel=ar.attnres_kernel_variant(ar.OP_FULL_BWD, L, nd, T, d, 1))
+        del dout, d_src, ws
+    return dict(name=f"full_wide_bf16_T{T}_d{d}_L{L}", **cases)
+
+
 def bench_bwd(args, T=8192, H=1):
     import torch
     import depth_wise_attention_amd as ar
@@ -784,7 +841,7 @@ def main():
               "bwd": lambda: bench_bwd(args), "mhar_bwd": lambda: bench_bwd(args, H=8), "full_bwd": lambda: bench_full_bwd(args),
               "block_update": lambda: bench_update(args), "decode": lambda: bench_decode(args),
               "msar": lambda: bench_msar(args), "block_msar": lambda: bench_block_msar(args),
-              "depth_sweep": lambda: bench_depth_sweep(args)}[args.workload]
+              "depth_sweep": lambda: bench_depth_sweep(args), "full_wide": lambda: bench_full_wide(args)}[args.workload]
         log(json.dumps(fn()))
         return
 

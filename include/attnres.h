@@ -316,10 +316,11 @@ size_t attnres_full_bwd_workspace_size(int64_t n_src, int64_t n_dst, int64_t T, 
  *  accumulate  0: overwrite d_src, dw and dgain; 1: add into them
  *  ws          device workspace of at least attnres_full_bwd_workspace_size()
  * Requires 1 <= n_dst <= n_src <= 64, and n_dst * H * n_src <= 1024 when the
- * call runs on the general kernel (the matrix-core kernels, for bf16 with
- * n_src <= 32 and one head, or H = 2, 4 or 8 heads of whole 256-channel runs
- * with d = 1024 .. 2048, have no such limit).  dw and dgain are fixed-order
- * sums over tokens (no atomics).
+ * call runs on the general kernel.  The matrix-core kernels have no such
+ * limit; they take bf16 with n_src <= 32 and one head, or H = 2, 4 or 8
+ * heads of whole 256-channel runs with d = 1024 .. 2048, and bf16 with
+ * 33 <= n_src <= 64, n_dst <= 32, one head and d a multiple of 512.  dw and
+ * dgain are fixed-order sums over tokens (no atomics).
  */
 int attnres_full_bwd(const void* src, int64_t n_src, int64_t T, int64_t d, const float* w,
                      int64_t n_dst, const float* gain, int64_t gain_ld, float eps, int32_t H,
