@@ -422,8 +422,11 @@ __global__ __launch_bounds__(64) void k_full_bwd_z(FullBwdArgs a, const float* c
   const int lane = lane_id(), h = lane >> 5, n = lane & 31;
   const int d = (int)a.d, n_src = (int)a.n_src, n_dst = (int)a.n_dst;
   const int64_t T = a.T;
-  const int ch0 = blockIdx.x * kChunk;
-  const int grp = blockIdx.y;
+  // The token group is the fast grid index: workgroups go to the XCDs round
+  // robin, so every channel tile of a group runs on one XCD and that L2 holds
+  // the group's (r c) rows once (each wave reads the whole row of its token).
+  const int grp = blockIdx.x;
+  const int ch0 = blockIdx.y * kChunk;
   const int zhead = ch0 / (d / a.H);  // the head of this tile's channels (r c is per head)
   const bf16_t* src = static_cast<const bf16_t*>(a.src);
   const uint4 ident0 = ident_operand(0), ident1 = ident_operand(1);
@@ -1171,7 +1174,7 @@ hipError_t launch_full_bwd_fast(const FullBwdArgs& a, const float** slabs, int64
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(W * 64), lds, st, a, (const uint4*)qpk, (const uint4*)qt,
                        cws);
     const int groups = (int)z_groups(a.T);
-    hipLaunchKernelGGL(k_full_bwd_z, dim3((unsigned)(a.d / kChunk), (unsigned)groups), dim3(64), 0, st, a,
+    hipLaunchKernelGGL(k_full_bwd_z, dim3((unsigned)groups, (unsigned)(a.d / kChunk)), dim3(64), 0, st, a,
                        (const float*)cws, zs, groups);
     *slabs = zs;
     *n_slabs = groups;
@@ -1193,7 +1196,7 @@ hipError_t launch_full_bwd_fast(const FullBwdArgs& a, const float** slabs, int64
     hipLaunchKernelGGL(k_full_bwd_fast<false>, dim3((unsigned)grid), dim3(kBB), 0, st, a, (const uint4*)qpk,
                        (const uint4*)qt, cws);
   const int groups = (int)z_groups(a.T);
-  hipLaunchKernelGGL(k_full_bwd_z, dim3((unsigned)(a.d / kChunk), (unsigned)groups), dim3(64), 0, st, a,
+  hipLaunchKernelGGL(k_full_bwd_z, dim3((unsigned)groups, (unsigned)(a.d / kChunk)), dim3(64), 0, st, a,
                      (const float*)cws, zs, groups);
   *slabs = zs;
   *n_slabs = groups;

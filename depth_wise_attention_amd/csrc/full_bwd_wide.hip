@@ -400,8 +400,11 @@ __global__ __launch_bounds__(64) void k_full_bwd_zw(FullBwdArgs a, const float* 
   const int lane = lane_id(), h = lane >> 5, n = lane & 31;
   const int d = (int)a.d, n_src = (int)a.n_src, n_dst = (int)a.n_dst;
   const int64_t T = a.T, plane = T * d;
-  const int ch0 = blockIdx.x * kChunk;
-  const int grp = blockIdx.y;
+  // The token group is the fast grid index: workgroups go to the XCDs round
+  // robin, so every channel tile of a group runs on one XCD and that L2 holds
+  // the group's (r c) rows once (each wave reads the whole row of its token).
+  const int grp = blockIdx.x;
+  const int ch0 = blockIdx.y * kChunk;
   const bf16_t* src = static_cast<const bf16_t*>(a.src);
   const uint4 ident0 = ident_operand(0), ident1 = ident_operand(1);
   f16acc Z0 = {}, Z1 = {};
@@ -508,7 +511,7 @@ hipError_t launch_full_bwd_wide(const FullBwdArgs& a, const uint4* qpk, const ui
   int64_t grid = (int64_t)num_cus() * per_cu;
   if (grid > a.T) grid = a.T;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kXB), kXLds, st, a, qpk, qt, cws);
-  hipLaunchKernelGGL(k_full_bwd_zw, dim3((unsigned)(a.d / kChunk), (unsigned)groups), dim3(64), 0, st, a,
+  hipLaunchKernelGGL(k_full_bwd_zw, dim3((unsigned)groups, (unsigned)(a.d / kChunk)), dim3(64), 0, st, a,
                      (const float*)cws, zs, groups);
   return hipGetLastError();
 }
