@@ -782,6 +782,7 @@ def pattern_ceilings(reps=10, only=None, blocks=(2, 4, 8, 16, 32), modes=(0,)):
         dst = torch.empty((max(nw, 1), T, d), dtype=torch.int16, device="cuda")
         best = None
         per_mode = {}
+        by_blocks = {}  # the kernels' flavour (mode 0) at each occupancy
         for mode in modes:
             for per_cu in blocks:
                 nblk = cus * per_cu
@@ -802,11 +803,15 @@ def pattern_ceilings(reps=10, only=None, blocks=(2, 4, 8, 16, 32), modes=(0,)):
                 gbs = (nr + nw) * T * d * 2 / (us * 1e-6) / 1e9
                 if mode not in per_mode or gbs > per_mode[mode]["gbs"]:
                     per_mode[mode] = dict(gbs=gbs, us=us, blocks_per_cu=per_cu)
+                if mode == 0:
+                    by_blocks[per_cu] = dict(gbs=gbs, us=us)
                 if best is None or gbs > best["gbs"]:
                     best = dict(pattern=name, rows_read=nr, rows_written=nw, T=T, d=d, bytes=(nr + nw) * T * d * 2,
                                 us=us, gbs=gbs, blocks_per_cu=per_cu, mode=PROBE_MODES[mode])
         if len(modes) > 1:
             best["by_mode"] = {PROBE_MODES[m]: v for m, v in per_mode.items()}
+        if by_blocks:
+            best["mode0_by_blocks_per_cu"] = by_blocks
         log(f"[bench] ceiling {json.dumps(best)}")
         out.append(best)
         del src, dst
