@@ -1,6 +1,8 @@
-// Specialised Full AttnRes backward for gfx950 (bf16 I/O, H = 1, up to 32
-// sources and destinations; d = 1024 .. 2048 in steps of 256 on the
-// register-resident kernel, else d a multiple of 512).
+// Specialised Full AttnRes backward for gfx950 (bf16 I/O, up to 32 sources
+// and destinations): the register-resident kernel (d = 1024 .. 2048 in steps
+// of 256, one head or H = 2, 4, 8), the query packing and the Z kernel shared
+// with the staged kernel of full_bwd_wide.hip (one head, d a multiple of 512,
+// one or two 32-source tiles), and the dispatch between them.
 //
 // The pages give no backward; these kernels evaluate the chain rule through
 // the Full forward (b-lab.team summary §1) for L = sum_j <dout_j, out_j>.  Per
@@ -19,9 +21,9 @@
 //            low parts, and Q^T is packed once per call in operand order;
 //   Z        a second kernel forms (r c) V per token and sums it over token
 //            groups into fixed slabs, summed in order by the shared reduction.
-// Each 64-channel chunk of the sources and of dout is staged through LDS with
-// whole-row loads (see mfma_tiles.hpp) in both stages; the second stage reads
-// them again (from cache).
+// The resident kernel keeps each token's sources and dout in registers
+// through both stages; the staged kernel streams 64-channel chunks through LDS
+// and reads them again in the second stage (from cache).
 #include <math.h>
 
 #include <algorithm>
@@ -35,8 +37,7 @@
 namespace attnres {
 namespace {
 
-constexpr int kBW = 4;            // waves per workgroup
-constexpr int kBB = kBW * 64;     // threads per workgroup
+constexpr int kBW = 4;            // waves per workgroup of the staged kernel
 constexpr int kZGroups = 64;      // token groups of the Z kernel (slabs)
 
 // Channel position (0..31 within a 32-channel block) that row m of a
@@ -104,312 +105,6 @@ __global__ __launch_bounds__(256) void k_full_bwd_qsplit(FullBwdArgs a, uint4* q
     }
     qpk[gs * 2 * 64 + lane] = pack8(hi[0], hi[1], hi[2], hi[3], hi[4], hi[5], hi[6], hi[7]);
     qpk[gs * 2 * 64 + 64 + lane] = pack8(lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]);
-  }
-}
-
-struct BwdSmem {
-  // Per wave: source tile (also the bf16 output tile of stage 2) and dout tile.
-  __attribute__((aligned(16))) unsigned char tiles[kBW][2][kTile * kVRow];
-  float sred[kBW][kTile * kTile];   // partial S[j][i]
-  // Partial A[j][i] during stage 1; afterwards the per-token stage-2 B
-  // operands, 12 slots x 64 lanes (uint4), slot (type * 2 + b) * 2 + part.
-  __attribute__((aligned(16))) float ared[kBW][kTile * kTile];
-  float gred[kBW][kTile];           // partial sums of squares
-  __attribute__((aligned(16))) float alpha[kTile][kARow];
-  __attribute__((aligned(16))) float rc[kTile][kARow];    // r_i c_ji
-  __attribute__((aligned(16))) float cst[kTile][kARow];   // c_ji s_ji
-  float coef[kTile];                                       // r_i^2 sum_j c_ji s_ji / d
-};
-
-
-#ifndef ATTNRES_FBWD_MINBLOCKS
-#define ATTNRES_FBWD_MINBLOCKS 2
-#endif
-
-template <bool ACC>
-__global__ __launch_bounds__(kBB, ATTNRES_FBWD_MINBLOCKS) void k_full_bwd_fast(FullBwdArgs a, const uint4* qpk, const uint4* qt,
-                                                          float* cws) {
-  __shared__ BwdSmem sm;
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const int d = (int)a.d, n_src = (int)a.n_src, n_dst = (int)a.n_dst;
-  const int64_t T = a.T;
-  const bf16_t* src = static_cast<const bf16_t*>(a.src);
-  const bf16_t* dout = static_cast<const bf16_t*>(a.dout);
-  bf16_t* dsrc = static_cast<bf16_t*>(a.d_src);
-  const int kw = d / kBW;
-  const int nch = kw / kChunk;  // even, >= 2
-  const int ch_base = wave * kw;
-  unsigned char* vt = sm.tiles[wave][0];
-  unsigned char* dt = sm.tiles[wave][1];
-  const int h = lane >> 5, n = lane & 31;
-  const uint4* qv = qpk + lane;
-  uint32_t vmask[4], dmask[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int r = 8 * u + (lane >> 3);
-    vmask[u] = r < n_src ? 0xFFFFFFFFu : 0u;
-    dmask[u] = r < n_dst ? 0xFFFFFFFFu : 0u;
-  }
-
-  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
-    const bf16_t* vrow[4];
-    const bf16_t* drow[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r = 8 * u + (lane >> 3);
-      vrow[u] = src + ((int64_t)(r < n_src ? r : 0) * T + t) * d + ch_base;
-      drow[u] = dout + ((int64_t)(r < n_dst ? r : 0) * T + t) * d + ch_base;
-    }
-
-    // ---------------- stage 1: S = Q V^T, G = V V^T, A = dOut V^T
-    f16acc S = {}, G = {}, A = {};
-    {
-      auto chunk1 = [&](int c, uint4 (&v)[4], uint4 (&g)[4]) {
-        const uint4* qc = qv + (int64_t)(ch_base / kChunk + c) * 8 * 64;
-        uint4 q[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) q[k] = qc[k * 64];
-        stage_chunk(vt, v, vmask);
-        stage_chunk(dt, g, dmask);
-        const int cn = min(c + 1, nch - 1) * kChunk;  // unconditional: exact wait counts
-        load_chunk(vrow, cn, v);
-        load_chunk(drow, cn, g);
-        wave_lds_sync();
-        uint4 bv[4], bd[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          bv[s] = tile_operand(vt, s);
-          bd[s] = tile_operand(dt, s);
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          S = mfma(q[2 * s], bv[s], S);
-          S = mfma(q[2 * s + 1], bv[s], S);
-          G = mfma(bv[s], bv[s], G);
-          A = mfma(bd[s], bv[s], A);
-        }
-        wave_lds_sync();
-      };
-      uint4 v1[4], g1[4];
-      load_chunk(vrow, 0, v1);
-      load_chunk(drow, 0, g1);
-      chunk1(0, v1, g1);  // peeled (see stage 2)
-      for (int c = 1; c < nch; ++c) chunk1(c, v1, g1);
-    }
-    // The A partials share LDS with the previous token's stage-2 operands, which
-    // other waves may still be reading: wait for every wave first.
-    lds_barrier();
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = 8 * (r / 4) + 4 * h + (r % 4);
-      sm.sred[wave][m * kTile + n] = S[r];
-      sm.ared[wave][m * kTile + n] = A[r];
-      if (m == n) sm.gred[wave][n] = G[r];
-    }
-    lds_barrier();
-
-    // ---------------- per (destination, source): alpha, c, r c, c s
-    {
-      const int j = tid / 8, i0 = 4 * (tid % 8);
-      const int lim = n_src - n_dst + j;
-      float sc[4], av[4], rr[4];
-      bool ok[4];
-      float m = -INFINITY;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int i = i0 + q;
-        float sv = 0.f, aa = 0.f, gv = 0.f;
-#pragma unroll
-        for (int w2 = 0; w2 < kBW; ++w2) {
-          sv += sm.sred[w2][j * kTile + i];
-          aa += sm.ared[w2][j * kTile + i];
-          gv += sm.gred[w2][i];
-        }
-        rr[q] = 1.0f / sqrtf(gv / (float)d + a.eps);
-        ok[q] = j < n_dst && i <= lim;
-        sc[q] = ok[q] ? rr[q] * sv : -INFINITY;
-        av[q] = aa;
-        m = fmaxf(m, sc[q]);
-      }
-      m = group_max<8>(m);
-      float e[4], l = 0.f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        e[q] = ok[q] ? expf(sc[q] - m) : 0.f;
-        l += e[q];
-      }
-      l = group_sum<8>(l);
-      const float inv = l > 0.f ? 1.0f / l : 0.f;
-      float al[4], sa = 0.f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        al[q] = e[q] * inv;
-        sa = fmaf(al[q], av[q], sa);
-      }
-      sa = group_sum<8>(sa);
-      float cc[4], rcv[4], csv[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        cc[q] = al[q] * (av[q] - sa);
-        rcv[q] = ok[q] ? rr[q] * cc[q] : 0.f;
-        csv[q] = ok[q] ? cc[q] * sc[q] : 0.f;
-      }
-      *reinterpret_cast<float4*>(&sm.alpha[j][i0]) = make_float4(al[0], al[1], al[2], al[3]);
-      *reinterpret_cast<float4*>(&sm.rc[j][i0]) = make_float4(rcv[0], rcv[1], rcv[2], rcv[3]);
-      *reinterpret_cast<float4*>(&sm.cst[j][i0]) = make_float4(csv[0], csv[1], csv[2], csv[3]);
-      // r c for the Z kernel: [T][32][32] fp32.
-      *reinterpret_cast<float4*>(cws + t * (kTile * kTile) + j * kTile + i0) =
-          make_float4(rcv[0], rcv[1], rcv[2], rcv[3]);
-    }
-    lds_barrier();
-    if (tid < kTile) {
-      const int i = tid;
-      float cs = 0.f, gv = 0.f;
-      for (int j = 0; j < kTile; ++j) cs += sm.cst[j][i];
-#pragma unroll
-      for (int w2 = 0; w2 < kBW; ++w2) gv += sm.gred[w2][i];
-      const float r2 = 1.0f / (gv / (float)d + a.eps);
-      sm.coef[i] = i < n_src ? r2 * cs / (float)d : 0.f;
-    }
-    lds_barrier();
-
-    // ---------------- stage 2: dV^T = dOut^T alpha^T + Q^T (r c)^T - V^T diag(coef)
-    // B operands, built once per token into LDS (the A partials are dead now):
-    // lane (h, n = source i), element e <-> row k = transposed_row(b, h, e) of
-    // alpha[k][i] (type 0), (r c)[k][i] (type 1) and diag(-coef) (type 2),
-    // each split into bf16 high (part 0) and low (part 1).  Waves 0, 1 and 2
-    // build the three types.
-    uint4* bpk = reinterpret_cast<uint4*>(&sm.ared[0][0]);
-    {
-      // Row k = transposed_row(b, h, e) = 16 b + 8 (e / 4) + 4 h + e % 4: one
-      // per-lane base (row 4 h, column n) plus compile-time offsets.
-      auto store_split = [&](const float (&x)[8], int slot) {
-        float hi[8], lo[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          hi[e] = bf2f(f2bf(x[e]));
-          lo[e] = x[e] - hi[e];
-        }
-        bpk[slot * 64 + lane] = pack8(hi[0], hi[1], hi[2], hi[3], hi[4], hi[5], hi[6], hi[7]);
-        bpk[(slot + 1) * 64 + lane] = pack8(lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]);
-      };
-      if (wave < 2) {  // wave 0: alpha (slots 0..3), wave 1: r c (slots 4..7)
-        const float* base = wave == 0 ? &sm.alpha[4 * h][n] : &sm.rc[4 * h][n];
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          float x[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = base[(16 * b + 8 * (e / 4) + (e % 4)) * kARow];
-          store_split(x, 4 * wave + 2 * b);
-        }
-      } else if (wave == 2) {  // diag(-coef) (slots 8..11)
-        const float cn = -sm.coef[n];
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          float x[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = transposed_row(b, h, e) == n ? cn : 0.f;
-          store_split(x, 8 + 2 * b);
-        }
-      }
-    }
-    lds_barrier();
-    {
-      const uint4* bl = bpk + lane;
-      // One chunk ahead (this pass reads from cache); the next chunk loads into
-      // the registers just staged.
-      auto chunk2 = [&](int c, uint4 (&v)[4], uint4 (&g)[4]) {
-        const int tile32 = (ch_base + c * kChunk) / 32;
-        // Q^T operands of both halves, issued before the next chunk's loads: the
-        // vector-memory counter retires in order, so a load issued after the
-        // prefetch would make its first use wait for the prefetch as well.
-        uint4 qq[2][4];
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const uint4* qtt = qt + (int64_t)(tile32 + half) * 4 * 64 + lane;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) qq[half][k] = qtt[64 * k];
-        }
-        stage_chunk(vt, v, vmask);
-        stage_chunk(dt, g, dmask);
-        const int cn = min(c + 1, nch - 1) * kChunk;
-        load_chunk(vrow, cn, v);
-        load_chunk(drow, cn, g);
-        wave_lds_sync();
-        uint4 ov[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) ov[s] = tile_operand(vt, s);
-        wave_lds_sync();  // the source tile becomes the output tile below
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const uint4 od0 = tile_operand(dt, 2 * half), od1 = tile_operand(dt, 2 * half + 1);
-          f16acc D1 = {};
-          D1 = mfma(ov[2 * half], ident_operand(0), D1);
-          D1 = mfma(ov[2 * half + 1], ident_operand(1), D1);
-          const uint4 tv0 = pack8(D1[0], D1[1], D1[2], D1[3], D1[4], D1[5], D1[6], D1[7]);
-          const uint4 tv1 = pack8(D1[8], D1[9], D1[10], D1[11], D1[12], D1[13], D1[14], D1[15]);
-          f16acc D3 = {};
-          D3 = mfma(od0, ident_operand(0), D3);
-          D3 = mfma(od1, ident_operand(1), D3);
-          const uint4 td0 = pack8(D3[0], D3[1], D3[2], D3[3], D3[4], D3[5], D3[6], D3[7]);
-          const uint4 td1 = pack8(D3[8], D3[9], D3[10], D3[11], D3[12], D3[13], D3[14], D3[15]);
-          f16acc D = {};
-          D = mfma(td0, bl[0 * 64], D);   // alpha, b = 0, hi
-          D = mfma(td0, bl[1 * 64], D);   //               lo
-          D = mfma(td1, bl[2 * 64], D);   // alpha, b = 1, hi
-          D = mfma(td1, bl[3 * 64], D);   //               lo
-          const uint4 q0h = qq[half][0], q0l = qq[half][1], q1h = qq[half][2], q1l = qq[half][3];
-          D = mfma(q0h, bl[4 * 64], D);   // r c, b = 0: (q_hi + q_lo)(rc_hi + rc_lo) less lo * lo
-          D = mfma(q0h, bl[5 * 64], D);
-          D = mfma(q0l, bl[4 * 64], D);
-          D = mfma(q1h, bl[6 * 64], D);   // r c, b = 1
-          D = mfma(q1h, bl[7 * 64], D);
-          D = mfma(q1l, bl[6 * 64], D);
-          D = mfma(tv0, bl[8 * 64], D);   // -coef, b = 0
-          D = mfma(tv0, bl[9 * 64], D);
-          D = mfma(tv1, bl[10 * 64], D);  // -coef, b = 1
-          D = mfma(tv1, bl[11 * 64], D);
-          // D[c'][i]: lane (h, i = n) holds channels 8q + 4h .. + 3 (of this half)
-          // of source i in elements 4q .. 4q + 3 -> bf16 tile row i, channel
-          // 32 half + 8q + 4h: 8 bytes at offset 8h of 16-byte piece 4 half + q.
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            float y0 = D[4 * q], y1 = D[4 * q + 1], y2 = D[4 * q + 2], y3 = D[4 * q + 3];
-            if constexpr (ACC) {
-              const int i = n < n_src ? n : n_src - 1;
-              const uint2 old = *reinterpret_cast<const uint2*>(
-                  dsrc + ((int64_t)i * T + t) * d + ch_base + c * kChunk + 32 * half + 8 * q + 4 * h);
-              y0 += bf_lo(old.x); y1 += bf_hi(old.x); y2 += bf_lo(old.y); y3 += bf_hi(old.y);
-            }
-            *reinterpret_cast<uint2*>(vt + vpos(n, 4 * half + q) + 8 * h) = make_uint2(pack_bf2(y0, y1), pack_bf2(y2, y3));
-          }
-          __builtin_amdgcn_sched_barrier(0);  // one half's registers at a time
-        }
-        wave_lds_sync();
-        // Rows past n_src store row n_src - 1 again (identical bytes): no branch.
-        const int chn = ch_base + c * kChunk + 8 * (lane & 7);
-        uint4 o[4];
-        int ir[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          ir[u] = min(8 * u + (lane >> 3), n_src - 1);
-          o[u] = *reinterpret_cast<const uint4*>(vt + vpos(ir[u], lane & 7));
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          __builtin_nontemporal_store(v4u{o[u].x, o[u].y, o[u].z, o[u].w},
-                                      reinterpret_cast<v4u*>(dsrc + ((int64_t)ir[u] * T + t) * d + chn));
-        wave_lds_sync();  // tiles are rewritten by the next chunk
-      };
-      uint4 v2[4], g2[4];
-      load_chunk(vrow, 0, v2);
-      load_chunk(drow, 0, g2);
-      chunk2(0, v2, g2);  // peeled: the loop head then sees the same outstanding operations on both edges
-      for (int c = 1; c < nch; ++c) chunk2(c, v2, g2);
-    }
-    // The next token writes its partials only after a barrier that every wave
-    // reaches after finishing this stage, and the alpha/rc/cst/coef tables only
-    // after its second barrier: every read of them here comes before.
   }
 }
 
@@ -1144,7 +839,8 @@ hipError_t launch_full_bwd_fast(const FullBwdArgs& a, const float** slabs, int64
   if (full_bwd_wide_shape(a)) {
     hipLaunchKernelGGL(k_full_qtsplit<false>, dim3(64), dim3(256), 0, st, a, qt);
     const int groups = (int)z_groups(a.T);
-    const hipError_t e = launch_full_bwd_wide(a, qpk, qt, cws, zs, groups, st);
+    hipError_t e = launch_full_bwd_staged(a, qpk, qt, cws, st);
+    if (e == hipSuccess) e = launch_full_bwd_zw(a, cws, zs, groups, st);
     *slabs = zs;
     *n_slabs = groups;
     return e;
@@ -1180,21 +876,10 @@ hipError_t launch_full_bwd_fast(const FullBwdArgs& a, const float** slabs, int64
     *n_slabs = groups;
     return hipGetLastError();
   }
+  // The staged kernel with one source tile (d outside the resident range).
   hipLaunchKernelGGL(k_full_qtsplit<false>, dim3(64), dim3(256), 0, st, a, qt);
-  int per_cu = 0;
-  hipError_t e = a.accumulate
-                     ? blocks_per_cu(reinterpret_cast<const void*>(k_full_bwd_fast<true>), kBB, &per_cu)
-                     : blocks_per_cu(reinterpret_cast<const void*>(k_full_bwd_fast<false>), kBB, &per_cu);
+  const hipError_t e = launch_full_bwd_staged(a, qpk, qt, cws, st);
   if (e != hipSuccess) return e;
-  if (per_cu < 1) per_cu = 1;
-  int64_t grid = (int64_t)num_cus() * per_cu;
-  if (grid > a.T) grid = a.T;
-  if (a.accumulate)
-    hipLaunchKernelGGL(k_full_bwd_fast<true>, dim3((unsigned)grid), dim3(kBB), 0, st, a, (const uint4*)qpk,
-                       (const uint4*)qt, cws);
-  else
-    hipLaunchKernelGGL(k_full_bwd_fast<false>, dim3((unsigned)grid), dim3(kBB), 0, st, a, (const uint4*)qpk,
-                       (const uint4*)qt, cws);
   const int groups = (int)z_groups(a.T);
   hipLaunchKernelGGL(k_full_bwd_z, dim3((unsigned)groups, (unsigned)(a.d / kChunk)), dim3(64), 0, st, a,
                      (const float*)cws, zs, groups);

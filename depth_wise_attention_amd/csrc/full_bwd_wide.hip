@@ -37,19 +37,27 @@ namespace {
 
 constexpr int kXW = 4;                        // waves per workgroup
 constexpr int kXB = kXW * 64;                 // threads per workgroup
-constexpr int kXS = 2 * kTile;                // source rows (two tiles)
-constexpr int kXRow = kXS + 4;                // floats per table row (64 + pad, 16-byte aligned)
-constexpr int kXTileV = kXS * kVRow;          // a wave's staged source tile (then its dV tile)
-constexpr int kXTileD = kTile * kVRow;        // a wave's staged dout tile
-constexpr int kXOps = kXW * (kXTileV + kXTileD);  // stage-2 operands follow the tiles
-constexpr int kXOpsBytes = 2 * 12 * 64 * 16;      // per source tile 12 slots of 64 lanes x 16 bytes
-constexpr int kXPart = kXW * kTile * kXS * 4;     // one array of per-wave partials ([wave][j][i])
-constexpr int kXUnion = kXOps + kXOpsBytes > 2 * kXPart ? kXOps + kXOpsBytes : 2 * kXPart;
-constexpr int kXGred = kXUnion;               // [wave][i] partial sums of squares
-constexpr int kXCoef = kXGred + kXW * kXS * 4;  // coef_i
-constexpr int kXLds = kXCoef + kXS * 4;
-static_assert(3 * kTile * kXRow * 4 <= kXOps, "the tables must not reach the operands");
-static_assert(2 * kXLds <= 160 * 1024, "two workgroups per compute unit");
+
+// Sizes and LDS layout for TS 32-source tiles.  The regions of the tiles, the
+// per-wave partials, the per-token tables and the stage-2 operands overlap
+// where their lifetimes do not.
+template <int TS>
+struct XL {
+  static constexpr int S = TS * kTile;                 // source rows
+  static constexpr int Row = S + 4;                    // floats per table row (16-byte aligned)
+  static constexpr int TileV = S * kVRow;              // a wave's staged source tile (then its dV tile)
+  static constexpr int TileD = kTile * kVRow;          // a wave's staged dout tile
+  static constexpr int Ops = kXW * (TileV + TileD);    // stage-2 operands follow the tiles
+  static constexpr int OpsBytes = TS * 12 * 64 * 16;   // per source tile 12 slots of 64 lanes x 16 bytes
+  static constexpr int Part = kXW * kTile * S * 4;     // one array of per-wave partials ([wave][j][i])
+  static constexpr int Union = Ops + OpsBytes > 2 * Part ? Ops + OpsBytes : 2 * Part;
+  static constexpr int Gred = Union;                   // [wave][i] partial sums of squares
+  static constexpr int Coef = Gred + kXW * S * 4;      // coef_i
+  static constexpr int Lds = Coef + S * 4;
+  static_assert(3 * kTile * Row * 4 <= Ops, "the tables must not reach the operands");
+  static_assert(2 * Lds <= 160 * 1024, "two workgroups per compute unit");
+};
+constexpr int kXS = XL<2>::S;  // the two-tile Z pass
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t x_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, kBufferWord3);
@@ -86,10 +94,13 @@ __device__ __forceinline__ uint4 x_operand(const unsigned char* tile, int ol, in
   return *reinterpret_cast<const uint4*>(tile + vpos(ol & 31, 2 * s + (ol >> 5)));
 }
 
-template <bool ACC>
+template <bool ACC, int TS>
 __global__ __launch_bounds__(kXB, 2) void k_full_bwd_wide(FullBwdArgs a, const uint4* qpk, const uint4* qt,
                                                           float* cws) {
   extern __shared__ __attribute__((aligned(16))) unsigned char xsm[];
+  using L = XL<TS>;
+  constexpr int kS = L::S;                 // source rows of the tiles
+  constexpr int SPT = kS / 8;              // softmax sources per thread (8 threads per destination)
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int d = (int)a.d, n_src = (int)a.n_src, n_dst = (int)a.n_dst;
@@ -100,16 +111,16 @@ __global__ __launch_bounds__(kXB, 2) void k_full_bwd_wide(FullBwdArgs a, const u
   const int kw = d / kXW;
   const int nch = kw / kChunk;
   const int ch_base = wave * kw;
-  unsigned char* vt = xsm + wave * (kXTileV + kXTileD);
-  unsigned char* dt = vt + kXTileV;
+  unsigned char* vt = xsm + wave * (L::TileV + L::TileD);
+  unsigned char* dt = vt + L::TileV;
   float* sred = reinterpret_cast<float*>(xsm);            // [wave][j][i], after stage 1
-  float* ared = reinterpret_cast<float*>(xsm + kXPart);   // [wave][j][i]
-  float* t_alpha = reinterpret_cast<float*>(xsm);         // [j][kXRow], after the partials are read
-  float* t_rc = t_alpha + kTile * kXRow;
-  float* t_cs = t_rc + kTile * kXRow;
-  uint4* bpk = reinterpret_cast<uint4*>(xsm + kXOps);     // [ts][slot][lane]
-  float* gred = reinterpret_cast<float*>(xsm + kXGred);
-  float* coef = reinterpret_cast<float*>(xsm + kXCoef);
+  float* ared = reinterpret_cast<float*>(xsm + L::Part);   // [wave][j][i]
+  float* t_alpha = reinterpret_cast<float*>(xsm);         // [j][L::Row], after the partials are read
+  float* t_rc = t_alpha + kTile * L::Row;
+  float* t_cs = t_rc + kTile * L::Row;
+  uint4* bpk = reinterpret_cast<uint4*>(xsm + L::Ops);     // [ts][slot][lane]
+  float* gred = reinterpret_cast<float*>(xsm + L::Gred);
+  float* coef = reinterpret_cast<float*>(xsm + L::Coef);
   const int h = lane >> 5, n = lane & 31;
   // Query operands of this wave's chunks: chunk c at byte 8 KiB c, k-step s
   // and part p at (2 s + p) KiB, lane at 16 lane.  Q^T operands: 32-channel
@@ -121,11 +132,11 @@ __global__ __launch_bounds__(kXB, 2) void k_full_bwd_wide(FullBwdArgs a, const u
   // One chunk in flight, in the order stage 1 (chunks 0 .. nch - 1), stage 2
   // (0 .. nch - 1), the next token's stage 1, ...
   int64_t t = blockIdx.x;
-  uint4 v[8], g[4];
+  uint4 v[kS / 8], g[4];
   if (t < T) {
     int ol = lane;
     asm volatile("" : "+v"(ol));
-    x_load<kXS>(src + t * d + ch_base, plane, n_src, 0, ol, v);
+    x_load<kS>(src + t * d + ch_base, plane, n_src, 0, ol, v);
     x_load<kTile>(dout + t * d + ch_base, plane, n_dst, 0, ol, g);
   }
   for (; t < T; t += gridDim.x) {
@@ -136,17 +147,17 @@ __global__ __launch_bounds__(kXB, 2) void k_full_bwd_wide(FullBwdArgs a, const u
     const bf16_t* tdn = dout + tn * d + ch_base;
 
     // ---------------- stage 1: S = Q V^T, G = V V^T, A = dOut V^T, per source tile
-    f16acc S[2], G[2], A[2];
+    f16acc S[TS], G[TS], A[TS];
 #pragma unroll
-    for (int ts = 0; ts < 2; ++ts) S[ts] = G[ts] = A[ts] = f16acc{};
+    for (int ts = 0; ts < TS; ++ts) S[ts] = G[ts] = A[ts] = f16acc{};
     for (int c = 0; c < nch; ++c) {
       int ol = lane;
       asm volatile("" : "+v"(ol));
       const uint32_t qoff = (uint32_t)ol * 16u + (uint32_t)c * 8192u;
-      x_stage<kXS>(vt, v, n_src, ol);
+      x_stage<kS>(vt, v, n_src, ol);
       x_stage<kTile>(dt, g, n_dst, ol);
       const int cn = c + 1 < nch ? c + 1 : 0;  // after the last chunk: stage 2's first
-      x_load<kXS>(tv_, plane, n_src, cn * kChunk, ol, v);
+      x_load<kS>(tv_, plane, n_src, cn * kChunk, ol, v);
       x_load<kTile>(td_, plane, n_dst, cn * kChunk, ol, g);
       wave_lds_sync();
 #pragma unroll
@@ -154,7 +165,7 @@ __global__ __launch_bounds__(kXB, 2) void k_full_bwd_wide(FullBwdArgs a, const u
         const uint4 qh = x_ld(qrs, qoff, (2 * s) * 1024), ql = x_ld(qrs, qoff, (2 * s + 1) * 1024);
         const uint4 bd = x_operand(dt, ol, s);
 #pragma unroll
-        for (int ts = 0; ts < 2; ++ts) {
+        for (int ts = 0; ts < TS; ++ts) {
           const uint4 bv = x_operand(vt + ts * kTile * kVRow, ol, s);
           S[ts] = mfma(qh, bv, S[ts]);
           S[ts] = mfma(ql, bv, S[ts]);
@@ -176,10 +187,10 @@ __global__ __launch_bounds__(kXB, 2) void k_full_bwd_wide(FullBwdArgs a, const u
       for (int r = 0; r < 16; ++r) {
         const int m = 8 * (r / 4) + 4 * rh + (r % 4);
 #pragma unroll
-        for (int ts = 0; ts < 2; ++ts) {
-          sred[(wave * kTile + m) * kXS + ts * kTile + rn] = S[ts][r];
-          ared[(wave * kTile + m) * kXS + ts * kTile + rn] = A[ts][r];
-          if (m == rn) gred[wave * kXS + ts * kTile + rn] = G[ts][r];
+        for (int ts = 0; ts < TS; ++ts) {
+          sred[(wave * kTile + m) * kS + ts * kTile + rn] = S[ts][r];
+          ared[(wave * kTile + m) * kS + ts * kTile + rn] = A[ts][r];
+          if (m == rn) gred[wave * kS + ts * kTile + rn] = G[ts][r];
         }
       }
     }
@@ -187,20 +198,20 @@ __global__ __launch_bounds__(kXB, 2) void k_full_bwd_wide(FullBwdArgs a, const u
 
     // ---------------- per (destination, source): alpha, c, r c, c s
     {
-      const int j = tid / 8, i0 = 8 * (tid % 8);
+      const int j = tid / 8, i0 = SPT * (tid % 8);
       const int lim = n_src - n_dst + j;
-      float sc[8], av[8], rr[8];
-      bool ok[8];
+      float sc[SPT], av[SPT], rr[SPT];
+      bool ok[SPT];
       float m = -INFINITY;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q = 0; q < SPT; ++q) {
         const int i = i0 + q;
         float sv = 0.f, aa = 0.f, gv = 0.f;
 #pragma unroll
         for (int w2 = 0; w2 < kXW; ++w2) {
-          sv += sred[(w2 * kTile + j) * kXS + i];
-          aa += ared[(w2 * kTile + j) * kXS + i];
-          gv += gred[w2 * kXS + i];
+          sv += sred[(w2 * kTile + j) * kS + i];
+          aa += ared[(w2 * kTile + j) * kS + i];
+          gv += gred[w2 * kS + i];
         }
         rr[q] = 1.0f / sqrtf(gv / (float)d + a.eps);
         ok[q] = j < n_dst && i <= lim;
@@ -209,47 +220,47 @@ __global__ __launch_bounds__(kXB, 2) void k_full_bwd_wide(FullBwdArgs a, const u
         m = fmaxf(m, sc[q]);
       }
       m = group_max<8>(m);
-      float e[8], l = 0.f;
+      float e[SPT], l = 0.f;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q = 0; q < SPT; ++q) {
         e[q] = ok[q] ? expf(sc[q] - m) : 0.f;
         l += e[q];
       }
       l = group_sum<8>(l);
       const float inv = l > 0.f ? 1.0f / l : 0.f;
-      float al[8], sa = 0.f;
+      float al[SPT], sa = 0.f;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q = 0; q < SPT; ++q) {
         al[q] = e[q] * inv;
         sa = fmaf(al[q], av[q], sa);
       }
       sa = group_sum<8>(sa);
-      float rcv[8], csv[8];
+      float rcv[SPT], csv[SPT];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q = 0; q < SPT; ++q) {
         const float cc = al[q] * (av[q] - sa);
         rcv[q] = ok[q] ? rr[q] * cc : 0.f;
         csv[q] = ok[q] ? cc * sc[q] : 0.f;
       }
       lds_barrier();  // every partial has been read: the tables overwrite them
 #pragma unroll
-      for (int q = 0; q < 8; q += 4) {
-        *reinterpret_cast<float4*>(&t_alpha[j * kXRow + i0 + q]) = make_float4(al[q], al[q + 1], al[q + 2], al[q + 3]);
-        *reinterpret_cast<float4*>(&t_rc[j * kXRow + i0 + q]) = make_float4(rcv[q], rcv[q + 1], rcv[q + 2], rcv[q + 3]);
-        *reinterpret_cast<float4*>(&t_cs[j * kXRow + i0 + q]) = make_float4(csv[q], csv[q + 1], csv[q + 2], csv[q + 3]);
-        // r c for the Z kernel: [T][32][64] fp32.
-        *reinterpret_cast<float4*>(cws + (t * kTile + j) * kXS + i0 + q) =
+      for (int q = 0; q < SPT; q += 4) {
+        *reinterpret_cast<float4*>(&t_alpha[j * L::Row + i0 + q]) = make_float4(al[q], al[q + 1], al[q + 2], al[q + 3]);
+        *reinterpret_cast<float4*>(&t_rc[j * L::Row + i0 + q]) = make_float4(rcv[q], rcv[q + 1], rcv[q + 2], rcv[q + 3]);
+        *reinterpret_cast<float4*>(&t_cs[j * L::Row + i0 + q]) = make_float4(csv[q], csv[q + 1], csv[q + 2], csv[q + 3]);
+        // r c for the Z kernel: [T][32][32 TS] fp32.
+        *reinterpret_cast<float4*>(cws + (t * kTile + j) * kS + i0 + q) =
             make_float4(rcv[q], rcv[q + 1], rcv[q + 2], rcv[q + 3]);
       }
     }
     lds_barrier();
-    if (tid < kXS) {
+    if (tid < kS) {
       // coef_i = r_i^2 (sum_j c_ji s_ji) / d
       const int i = tid;
       float cs = 0.f, gv = 0.f;
-      for (int j = 0; j < kTile; ++j) cs += t_cs[j * kXRow + i];
+      for (int j = 0; j < kTile; ++j) cs += t_cs[j * L::Row + i];
 #pragma unroll
-      for (int w2 = 0; w2 < kXW; ++w2) gv += gred[w2 * kXS + i];
+      for (int w2 = 0; w2 < kXW; ++w2) gv += gred[w2 * kS + i];
       const float r2 = 1.0f / (gv / (float)d + a.eps);
       coef[i] = i < n_src ? r2 * cs / (float)d : 0.f;
     }
@@ -273,17 +284,17 @@ __global__ __launch_bounds__(kXB, 2) void k_full_bwd_wide(FullBwdArgs a, const u
       if (wave < 2) {  // wave 0: alpha, wave 1: r c
         const float* tab = wave == 0 ? t_alpha : t_rc;
 #pragma unroll
-        for (int ts = 0; ts < 2; ++ts)
+        for (int ts = 0; ts < TS; ++ts)
 #pragma unroll
           for (int b = 0; b < 2; ++b) {
             float x[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = tab[transposed_row(b, h, e) * kXRow + ts * kTile + n];
+            for (int e = 0; e < 8; ++e) x[e] = tab[transposed_row(b, h, e) * L::Row + ts * kTile + n];
             store_split(x, ts * 12 + 4 * wave + 2 * b);
           }
       } else if (wave == 2) {
 #pragma unroll
-        for (int ts = 0; ts < 2; ++ts) {
+        for (int ts = 0; ts < TS; ++ts) {
           const float cn = -coef[ts * kTile + n];
 #pragma unroll
           for (int b = 0; b < 2; ++b) {
@@ -310,16 +321,16 @@ __global__ __launch_bounds__(kXB, 2) void k_full_bwd_wide(FullBwdArgs a, const u
       for (int half = 0; half < 2; ++half)
 #pragma unroll
         for (int k = 0; k < 4; ++k) qq[half][k] = x_ld(qtrs, qtoff, half * 4096 + k * 1024);
-      x_stage<kXS>(vt, v, n_src, ol);
+      x_stage<kS>(vt, v, n_src, ol);
       x_stage<kTile>(dt, g, n_dst, ol);
       // The next chunk, or after the last one the next token's first.
       const bool last = c + 1 == nch;
-      x_load<kXS>(last ? tvn : tv_, plane, n_src, last ? 0 : (c + 1) * kChunk, ol, v);
+      x_load<kS>(last ? tvn : tv_, plane, n_src, last ? 0 : (c + 1) * kChunk, ol, v);
       x_load<kTile>(last ? tdn : td_, plane, n_dst, last ? 0 : (c + 1) * kChunk, ol, g);
       wave_lds_sync();
-      uint4 ov[2][4];
+      uint4 ov[TS][4];
 #pragma unroll
-      for (int ts = 0; ts < 2; ++ts)
+      for (int ts = 0; ts < TS; ++ts)
 #pragma unroll
         for (int s = 0; s < 4; ++s) ov[ts][s] = x_operand(vt + ts * kTile * kVRow, ol, s);
       wave_lds_sync();  // the source tile becomes the output tile below
@@ -331,7 +342,7 @@ __global__ __launch_bounds__(kXB, 2) void k_full_bwd_wide(FullBwdArgs a, const u
         const uint4 td0 = pack8(D3[0], D3[1], D3[2], D3[3], D3[4], D3[5], D3[6], D3[7]);
         const uint4 td1 = pack8(D3[8], D3[9], D3[10], D3[11], D3[12], D3[13], D3[14], D3[15]);
 #pragma unroll
-        for (int ts = 0; ts < 2; ++ts) {
+        for (int ts = 0; ts < TS; ++ts) {
           f16acc D1 = {};
           D1 = mfma(ov[ts][2 * half], ident0, D1);
           D1 = mfma(ov[ts][2 * half + 1], ident1, D1);
@@ -376,7 +387,7 @@ __global__ __launch_bounds__(kXB, 2) void k_full_bwd_wide(FullBwdArgs a, const u
       // Whole-row stores; rows past n_src store row n_src - 1 again (identical bytes).
       const int chn = ch_base + c * kChunk + 8 * (ol & 7);
 #pragma unroll
-      for (int u = 0; u < kXS / 8; ++u) {
+      for (int u = 0; u < kS / 8; ++u) {
         const int ir = min(8 * u + (ol >> 3), n_src - 1);
         const uint4 o = *reinterpret_cast<const uint4*>(vt + vpos(ir, ol & 7));
         __builtin_nontemporal_store(v4u{o.x, o.y, o.z, o.w},
@@ -486,6 +497,30 @@ __global__ __launch_bounds__(64) void k_full_bwd_zw(FullBwdArgs a, const float* 
   }
 }
 
+template <int TS>
+hipError_t launch_staged(const FullBwdArgs& a, const uint4* qpk, const uint4* qt, float* cws, hipStream_t st) {
+  auto kern = a.accumulate ? k_full_bwd_wide<true, TS> : k_full_bwd_wide<false, TS>;
+  constexpr int lds = XL<TS>::Lds;
+  if constexpr (lds > 64 * 1024) {
+    static std::atomic<bool> allowed[2] = {false, false};  // dynamic LDS above 64 KiB, once per kernel
+    const int which = a.accumulate ? 1 : 0;
+    if (!allowed[which].load(std::memory_order_relaxed)) {
+      const hipError_t e =
+          hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      if (e != hipSuccess) return e;
+      allowed[which].store(true, std::memory_order_relaxed);
+    }
+  }
+  int per_cu = 0;
+  const hipError_t e = blocks_per_cu(reinterpret_cast<const void*>(kern), kXB, &per_cu, lds);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) per_cu = 1;
+  int64_t grid = (int64_t)num_cus() * per_cu;
+  if (grid > a.T) grid = a.T;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kXB), lds, st, a, qpk, qt, cws);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool full_bwd_wide_shape(const FullBwdArgs& a) {
@@ -493,26 +528,14 @@ bool full_bwd_wide_shape(const FullBwdArgs& a) {
          a.n_dst <= a.n_src && a.d % (2 * kXW * kChunk) == 0 && a.d <= ((int64_t)1 << 16);
 }
 
-hipError_t launch_full_bwd_wide(const FullBwdArgs& a, const uint4* qpk, const uint4* qt, float* cws, float* zs,
-                                int groups, hipStream_t st) {
-  auto kern = a.accumulate ? k_full_bwd_wide<true> : k_full_bwd_wide<false>;
-  static std::atomic<bool> allowed[2] = {false, false};  // dynamic LDS above 64 KiB, once per kernel
-  const int which = a.accumulate ? 1 : 0;
-  if (!allowed[which].load(std::memory_order_relaxed)) {
-    const hipError_t e =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, kXLds);
-    if (e != hipSuccess) return e;
-    allowed[which].store(true, std::memory_order_relaxed);
-  }
-  int per_cu = 0;
-  const hipError_t e = blocks_per_cu(reinterpret_cast<const void*>(kern), kXB, &per_cu, kXLds);
-  if (e != hipSuccess) return e;
-  if (per_cu < 1) per_cu = 1;
-  int64_t grid = (int64_t)num_cus() * per_cu;
-  if (grid > a.T) grid = a.T;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kXB), kXLds, st, a, qpk, qt, cws);
-  hipLaunchKernelGGL(k_full_bwd_zw, dim3((unsigned)groups, (unsigned)(a.d / kChunk)), dim3(64), 0, st, a,
-                     (const float*)cws, zs, groups);
+hipError_t launch_full_bwd_staged(const FullBwdArgs& a, const uint4* qpk, const uint4* qt, float* cws,
+                                  hipStream_t st) {
+  return a.n_src > kTile ? launch_staged<2>(a, qpk, qt, cws, st) : launch_staged<1>(a, qpk, qt, cws, st);
+}
+
+hipError_t launch_full_bwd_zw(const FullBwdArgs& a, const float* cws, float* zs, int groups, hipStream_t st) {
+  hipLaunchKernelGGL(k_full_bwd_zw, dim3((unsigned)groups, (unsigned)(a.d / kChunk)), dim3(64), 0, st, a, cws, zs,
+                     groups);
   return hipGetLastError();
 }
 

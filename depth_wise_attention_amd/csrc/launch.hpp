@@ -168,12 +168,14 @@ bool full_bwd_fast_ok(const FullBwdArgs& a);
 // Name of the specialised Full backward variant a call runs (nullptr: the general kernel).
 const char* full_bwd_fast_variant(const FullBwdArgs& a);
 size_t full_bwd_fast_workspace_bytes(int64_t n_src, int64_t n_dst, int64_t T, int64_t d, int H);
-// Matrix-core Full backward over 33 .. 64 sources and up to 32 destinations
-// (full_bwd_wide.hip): the shapes it takes, and its two kernels after the query
-// packing (qpk, qt and the (r c) table cws and Z slabs zs in the workspace).
+// Staged matrix-core Full backward (full_bwd_wide.hip), one or two 32-source
+// tiles: the shapes that need two (33 .. 64 sources, up to 32 destinations),
+// the main kernel after the query packing (qpk, qt; writes the (r c) table
+// cws, [T][32][32 tiles]), and the two-tile Z pass over cws into slabs zs.
 bool full_bwd_wide_shape(const FullBwdArgs& a);
-hipError_t launch_full_bwd_wide(const FullBwdArgs& a, const uint4* qpk, const uint4* qt, float* cws, float* zs,
-                                int groups, hipStream_t st);
+hipError_t launch_full_bwd_staged(const FullBwdArgs& a, const uint4* qpk, const uint4* qt, float* cws,
+                                  hipStream_t st);
+hipError_t launch_full_bwd_zw(const FullBwdArgs& a, const float* cws, float* zs, int groups, hipStream_t st);
 hipError_t launch_full_bwd_fast(const FullBwdArgs& a, const float** slabs, int64_t* n_slabs, hipStream_t st);
 
 // Specialised gfx950 kernels.  The *_ok predicates are pure functions of the
