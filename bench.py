@@ -688,7 +688,7 @@ def _oracle_chunk(args):
         return time.perf_counter() - t0
 
 
-def cpu_baseline(T=16384, chunk=256, sample=4096):
+def cpu_baseline(T=16384, chunk=256, sample=16384):
     """The float64 oracle (as it stands) on the headline block workload, on the
     host's cores: (1) one process with BLAS pinned to one thread over a bounded
     sample of `sample` tokens, and (2) a pool of P worker processes (P = the
@@ -874,7 +874,8 @@ def main():
         torch.cuda.empty_cache()
         for fn in (lambda: bench_block(args, H=8, T=32768, with_events=True), lambda: bench_full(args),
                    lambda: bench_bwd(args), lambda: bench_bwd(args, H=8), lambda: bench_full_bwd(args), lambda: bench_update(args),
-                   lambda: bench_decode(args), lambda: bench_msar(args), lambda: bench_block_msar(args)):
+                   lambda: bench_decode(args), lambda: bench_msar(args), lambda: bench_block_msar(args),
+                   lambda: bench_full_wide(args)):
             r = fn()
             extra[r.pop("name")] = {k: v for k, v in r.items() if k not in ("T", "d", "N", "S", "H")}
             torch.cuda.empty_cache()
