@@ -670,6 +670,7 @@ size_t full_fast_workspace_bytes(int64_t n_src, int64_t n_dst, int64_t d, int H,
 
 bool full_fast_ok(const FullArgs& a) {
   if (a.dtype != kBF16 || a.T < 1) return false;
+  if (full_one_ok(a)) return true;  // needs no workspace
   if (full_wide_shape(a.n_src, a.n_dst, a.d, a.H, a.dtype)) {
     if (a.ws == nullptr || a.ws_bytes < full_wide_workspace_bytes(a.n_dst, a.d)) return false;
     return al16(a.src) && al16(a.out) && al16(a.ws) && al16(a.w) && al16(a.gain);
@@ -703,10 +704,12 @@ hipError_t launch_resident_h(const FullArgs& a, const bf16_t* qpk, hipStream_t s
 }
 
 const char* full_fast_variant(const FullArgs& a) {
+  if (full_one_ok(a)) return "full_one";
   return full_wide_shape(a.n_src, a.n_dst, a.d, a.H, a.dtype) ? "full_wide" : "full_fast";
 }
 
 hipError_t launch_full_fast(const FullArgs& a, hipStream_t st) {
+  if (full_one_ok(a)) return launch_full_one(a, st);
   if (full_wide_shape(a.n_src, a.n_dst, a.d, a.H, a.dtype)) return launch_full_wide(a, st);
   bf16_t* qpk = static_cast<bf16_t*>(a.ws);
   if (resident_shape(a.d, a.H)) {

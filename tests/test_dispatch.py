@@ -93,9 +93,12 @@ def test_phase2_full_and_policy():
     assert variant(binding.OP_PHASE2, 8, 4, 100, 1024) == "phase2_generic"
     assert variant(binding.OP_FULL_FWD, 32, 32, 100, 2048) == "full_fast"
     # 33 .. 64 sources: the two-tile kernel (one head, bf16, d a multiple of 512)
-    for L, n_dst, d in ((33, 33, 2048), (55, 54, 2048), (55, 1, 2048), (64, 64, 512), (40, 32, 4096),
-                        (47, 20, 1536), (64, 1, 2560)):
+    for L, n_dst, d in ((33, 33, 2048), (55, 54, 2048), (64, 64, 512), (40, 32, 4096), (47, 20, 1536),
+                        (40, 1, 8192), (33, 2, 2048)):
         assert variant(binding.OP_FULL_FWD, L, n_dst, 100, d) == "full_wide", (L, n_dst, d)
+    # one destination, d <= 4096: the vector kernel that reads each row once
+    for L, d in ((55, 2048), (64, 2560), (33, 512), (64, 4096)):
+        assert variant(binding.OP_FULL_FWD, L, 1, 100, d) == "full_one", (L, d)
     assert variant(binding.OP_FULL_FWD, 55, 54, 100, 2048, H=8) == "full_generic"
     assert variant(binding.OP_FULL_FWD, 55, 54, 100, 768) == "full_generic"
     # heads on the matrix cores: whole waves of the resident kernel (d <= 2048)

@@ -265,7 +265,8 @@ def test_full_fwd_heads(T, d, L, n_dst, H, gain):
 
 # Full forward over 33 .. 64 sources: (T, d, L, n_dst, gain).  Two source
 # tiles; n_dst > 32 takes two destination tiles.  T above the 512 resident
-# workgroups gives each several tokens and a ragged tail.
+# workgroups gives each several tokens and a ragged tail.  One destination with
+# d <= 4096 runs the vector kernel that reads each row once.
 FULL_WIDE_CASES = [
     (530, 2048, 55, 54, "per"),
     (1100, 1024, 33, 33, "shared"),
@@ -275,6 +276,10 @@ FULL_WIDE_CASES = [
     (1, 2048, 55, 1, "none"),
     (37, 1536, 47, 20, "shared"),
     (513, 2560, 64, 1, "per"),
+    (2000, 4096, 64, 1, "per"),
+    (777, 512, 33, 1, "shared"),
+    (1025, 1024, 48, 1, "none"),
+    (64, 8192, 40, 1, "per"),
 ]
 
 
@@ -282,7 +287,7 @@ FULL_WIDE_CASES = [
 def test_full_fwd_wide(T, d, L, n_dst, gain):
     name = ar.attnres_kernel_variant(ar.OP_FULL_FWD, L, n_dst, T, d, 1)
     say(f"full fwd wide T={T} d={d} L={L} n_dst={n_dst} gain={gain}: {name}")
-    assert name == "full_wide", name
+    assert name == ("full_one" if n_dst == 1 and d <= 4096 else "full_wide"), name
     wl = synth.full_workload(T=T, d=d, L=L, std_step=0.2, dtype="bf16", seed=140 + L + n_dst, gain_variance=0.02,
                              n_dst=n_dst)
     g = _gain_arg(wl, gain, n_dst, d)
