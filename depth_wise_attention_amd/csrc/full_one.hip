@@ -1,13 +1,15 @@
-// Full AttnRes forward for one destination over 33 .. 64 sources (gfx950, bf16
-// I/O, one head): the call a model makes per sublayer once it is deeper than
-// 32 sublayers (b-lab.team summary §1; dimensionstp "Attention Residuals
+// Full AttnRes forward for one destination over up to 64 sources (gfx950,
+// bf16 I/O, one head): the call a model makes per sublayer, at any depth up
+// to 63 sublayers (b-lab.team summary §1; dimensionstp "Attention Residuals
 // Review" §3 (2) runs 54).  With one query the contractions per token are two
 // vectors of n_src dot products over d, far too small for the matrix cores;
 // what matters is reading each source row once.
 //
 // One workgroup of d / 8 threads owns one token at a time; thread tid owns
-// channels 8 tid .. 8 tid + 7.  The sources are taken in two tiles of 32 rows,
-// each held in registers (16-byte buffer loads, one register per row):
+// channels 8 tid .. 8 tid + 7.  The sources are taken in NT = 1 or 2 tiles of
+// 32 rows, each held in registers (16-byte buffer loads, one register per
+// row; a row past n_src is loaded with a zero-record descriptor, which reads
+// nothing and gives zeros):
 //   1. per row, the sum of squares and q . v over the thread's channels;
 //   2. transposing reductions over the wave (16 rows at a time) and a sum
 //      over the waves through LDS (one barrier per tile);
@@ -67,8 +69,8 @@ __global__ __launch_bounds__(512, 2) void k_full_one(FullArgs a) {
   else
     fold_q8<false>(a.w + 8 * tid, nullptr, q);
 
-  // Row r of token t (rows past n_src read the last real row: in bounds, and
-  // their weights are zero), from opaque scalar copies of the plane size and
+  // Row r of token t (the address of a row past n_src is the last real row's,
+  // which its zero-record load never reads), from opaque scalar copies of the plane size and
   // the source count taken per tile: the 64 row offsets are loop-invariant,
   // and held across the token loop they would take more scalar registers
   // than there are.
@@ -77,7 +79,7 @@ __global__ __launch_bounds__(512, 2) void k_full_one(FullArgs a) {
   int64_t t = blockIdx.x;
   if (t < T) {
 #pragma unroll
-    for (int k = 0; k < kOTile; ++k) v[k] = o_ld(row(plane, n_src, t, k), coff);
+    for (int k = 0; k < kOTile; ++k) v[k] = o_ld(row(plane, n_src, t, k), coff, k < n_src ? 0x7fffffff : 0);
   }
   // One flat loop over (token, tile) pairs, so that the row registers take
   // the same physical registers in every iteration.
@@ -95,7 +97,6 @@ __global__ __launch_bounds__(512, 2) void k_full_one(FullArgs a) {
     const int rn0 = last ? 0 : (tl + 1) * kOTile;
     const bool more = tn < T;
     const int64_t tr = more ? tn : t;       // a real token for the row addresses
-    const int recs = more ? 0x7fffffff : 0;  // past the last token the refill loads read nothing
     int64_t pl = plane;
     int ns = n_src;
     asm volatile("" : "+s"(pl), "+s"(ns));
@@ -151,7 +152,8 @@ __global__ __launch_bounds__(512, 2) void k_full_one(FullArgs a) {
       asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
       float x[8];
       o_unpack(u, x);
-      v[k] = o_ld(row(pl, ns, tr, rn0 + k), coff, recs);
+      // Past the last token, and for rows past n_src, the load reads nothing.
+      v[k] = o_ld(row(pl, ns, tr, rn0 + k), coff, more && rn0 + k < ns ? 0x7fffffff : 0);
       const float al = read_lane(e, k);
 #pragma unroll
       for (int c = 0; c < 8; ++c) acc[c] = fmaf(al, x[c], acc[c]);
@@ -181,20 +183,27 @@ __global__ __launch_bounds__(512, 2) void k_full_one(FullArgs a) {
 
 bool full_one_ok(const FullArgs& a) {
   auto al16 = [](const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; };
-  return a.dtype == kBF16 && a.H == 1 && a.n_dst == 1 && a.n_src > kOTile && a.n_src <= 2 * kOTile && a.T >= 1 &&
+  return a.dtype == kBF16 && a.H == 1 && a.n_dst == 1 && a.n_src >= 1 && a.n_src <= 2 * kOTile && a.T >= 1 &&
          a.d >= 512 && a.d % 512 == 0 && a.d <= 8 * 64 * kOMaxW && al16(a.src) && al16(a.out) && al16(a.w) &&
          al16(a.gain);
 }
 
-hipError_t launch_full_one(const FullArgs& a, hipStream_t st) {
+namespace {
+template <int NT>
+hipError_t launch_one(const FullArgs& a, hipStream_t st) {
   const int B = (int)(a.d / 8);
   int per_cu = 0;
-  const hipError_t e = blocks_per_cu(reinterpret_cast<const void*>(k_full_one<2>), B, &per_cu);
+  const hipError_t e = blocks_per_cu(reinterpret_cast<const void*>(k_full_one<NT>), B, &per_cu);
   if (e != hipSuccess) return e;
   int64_t grid = (int64_t)num_cus() * (per_cu < 1 ? 1 : per_cu);
   if (grid > a.T) grid = a.T;
-  hipLaunchKernelGGL(k_full_one<2>, dim3((unsigned)grid), dim3((unsigned)B), 0, st, a);
+  hipLaunchKernelGGL(k_full_one<NT>, dim3((unsigned)grid), dim3((unsigned)B), 0, st, a);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_full_one(const FullArgs& a, hipStream_t st) {
+  return a.n_src > kOTile ? launch_one<2>(a, st) : launch_one<1>(a, st);
 }
 
 }  // namespace attnres

@@ -194,17 +194,17 @@ hipError_t launch_phase1_fast(const Phase1Args& a, hipStream_t st);
 hipError_t launch_phase2_fast(const Phase2Args& a, hipStream_t st);
 hipError_t launch_bwd_fast(const BwdArgs& a, int64_t* slots_used, hipStream_t st);
 hipError_t launch_full_fast(const FullArgs& a, hipStream_t st);
-// Name of the specialised Full forward kernel a call runs ("full_fast" for up
-// to 32 sources, "full_one" for one destination over 33 .. 64 with d <= 4096,
-// "full_wide" for the other 33 .. 64 source calls); only meaningful when
-// full_fast_ok.
+// Name of the specialised Full forward kernel a call runs ("full_one" for one
+// destination and one head over up to 64 sources with d <= 4096, else
+// "full_fast" for up to 32 sources and "full_wide" for 33 .. 64); only
+// meaningful when full_fast_ok.
 const char* full_fast_variant(const FullArgs& a);
 // Matrix-core Full forward over 33 .. 64 sources (full_wide.hip): the shapes
 // it takes, its workspace (the packed query) and its launch.
 bool full_wide_shape(int64_t n_src, int64_t n_dst, int64_t d, int H, int dtype);
 size_t full_wide_workspace_bytes(int64_t n_dst, int64_t d);
 hipError_t launch_full_wide(const FullArgs& a, hipStream_t st);
-// Vector Full forward for one destination over 33 .. 64 sources (full_one.hip):
+// Vector Full forward for one destination over up to 64 sources (full_one.hip):
 // reads each source row once and needs no workspace.
 bool full_one_ok(const FullArgs& a);
 hipError_t launch_full_one(const FullArgs& a, hipStream_t st);

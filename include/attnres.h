@@ -103,9 +103,10 @@ int attnres_full_fwd(const void* src, int64_t n_src, int64_t T, int64_t d,
  * as a bf16 high part plus a bf16 low part ([2, 32, d] bf16, 128 * d bytes).
  * So may one-head bf16 calls with 33 .. 64 sources and d a multiple of 512:
  * [2, 32, d] for n_dst <= 32, [2, 64, d] (256 * d bytes) above.  Every other
- * request needs none and gets 0.  (One destination over 33 .. 64 sources with
- * d <= 4096 runs a vector kernel that ignores the workspace; the size returned
- * still covers the matrix-core kernel, so a caller need not know which runs.)
+ * request needs none and gets 0.  (One destination and one head over up to 64
+ * sources with d <= 4096 runs a vector kernel that ignores the workspace; the
+ * size returned still covers the matrix-core kernels, so a caller need not
+ * know which runs.)
  */
 size_t attnres_full_fwd_workspace_size(int64_t n_src, int64_t n_dst, int64_t d, int32_t H,
                                        int32_t dtype);

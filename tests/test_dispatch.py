@@ -96,9 +96,12 @@ def test_phase2_full_and_policy():
     for L, n_dst, d in ((33, 33, 2048), (55, 54, 2048), (64, 64, 512), (40, 32, 4096), (47, 20, 1536),
                         (40, 1, 8192), (33, 2, 2048)):
         assert variant(binding.OP_FULL_FWD, L, n_dst, 100, d) == "full_wide", (L, n_dst, d)
-    # one destination, d <= 4096: the vector kernel that reads each row once
-    for L, d in ((55, 2048), (64, 2560), (33, 512), (64, 4096)):
+    # one destination, one head, d <= 4096: the vector kernel that reads each row once
+    for L, d in ((55, 2048), (64, 2560), (33, 512), (64, 4096), (32, 2048), (9, 4096), (1, 512), (17, 1536)):
         assert variant(binding.OP_FULL_FWD, L, 1, 100, d) == "full_one", (L, d)
+    assert variant(binding.OP_FULL_FWD, 32, 1, 100, 8192) == "full_fast"
+    assert variant(binding.OP_FULL_FWD, 32, 1, 100, 2048, H=2) == "full_fast"
+    assert variant(binding.OP_FULL_FWD, 32, 1, 100, 2048, dtype=F32) == "full_generic"
     assert variant(binding.OP_FULL_FWD, 55, 54, 100, 2048, H=8) == "full_generic"
     assert variant(binding.OP_FULL_FWD, 55, 54, 100, 768) == "full_generic"
     # heads on the matrix cores: whole waves of the resident kernel (d <= 2048)
