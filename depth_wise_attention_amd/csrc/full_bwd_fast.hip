@@ -795,7 +795,9 @@ int64_t rc_cols(int64_t n_src) { return n_src > kTile ? 2 * kTile : kTile; }
 
 size_t full_bwd_fast_workspace_bytes(int64_t n_src, int64_t n_dst, int64_t T, int64_t d, int H) {
   // qpk [128 d] + qt [128 d] + (r c) [T][H][32][rc_cols] fp32 + Z slabs [groups][n_dst][d] fp32
-  return (size_t)256 * (size_t)d + (size_t)T * H * kTile * rc_cols(n_src) * 4 + (size_t)z_groups(T) * n_dst * d * 4;
+  const size_t mfma =
+      (size_t)256 * (size_t)d + (size_t)T * H * kTile * rc_cols(n_src) * 4 + (size_t)z_groups(T) * n_dst * d * 4;
+  return std::max(mfma, full_bwd_one_workspace_bytes(n_src, n_dst, T, d, H));
 }
 
 // The register-resident kernel: d = 1024 .. 2048 in steps of 256 (d / 256
@@ -810,6 +812,7 @@ bool full_bwd_res_ok(const FullBwdArgs& a) {
 
 bool full_bwd_fast_ok(const FullBwdArgs& a) {
   if (a.dtype != kBF16 || a.T < 1) return false;
+  if (full_bwd_one_ok(a)) return true;
   if (full_bwd_wide_shape(a)) {
     if (a.zslots == nullptr || a.ws_bytes < full_bwd_fast_workspace_bytes(a.n_src, a.n_dst, a.T, a.d, a.H))
       return false;
@@ -825,11 +828,13 @@ bool full_bwd_fast_ok(const FullBwdArgs& a) {
 
 const char* full_bwd_fast_variant(const FullBwdArgs& a) {
   if (!full_bwd_fast_ok(a)) return nullptr;
+  if (full_bwd_one_ok(a)) return "full_bwd_one";
   if (full_bwd_wide_shape(a)) return "full_bwd_wide";
   return full_bwd_res_ok(a) ? "full_bwd_res" : "full_bwd_fast";
 }
 
 hipError_t launch_full_bwd_fast(const FullBwdArgs& a, const float** slabs, int64_t* n_slabs, hipStream_t st) {
+  if (full_bwd_one_ok(a)) return launch_full_bwd_one(a, slabs, n_slabs, st);
   char* ws = reinterpret_cast<char*>(a.zslots);
   uint4* qpk = reinterpret_cast<uint4*>(ws);
   uint4* qt = reinterpret_cast<uint4*>(ws + 128 * a.d);

@@ -33,23 +33,6 @@ namespace {
 constexpr int kOTile = 32;   // source rows per register tile
 constexpr int kOMaxW = 8;    // waves per workgroup at most (d <= 4096)
 
-typedef unsigned int o4u __attribute__((ext_vector_type(4)));
-
-// 16 bytes at byte offset off of a row; with a record count of zero the load
-// reads nothing and returns zeros.
-__device__ __forceinline__ uint4 o_ld(const void* row, uint32_t off, int records = 0x7fffffff) {
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row), 0, records, kBufferWord3);
-  const o4u v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kBufferNt);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-__device__ __forceinline__ void o_unpack(const uint4 u, float (&x)[8]) {
-  x[0] = bf_lo(u.x); x[1] = bf_hi(u.x);
-  x[2] = bf_lo(u.y); x[3] = bf_hi(u.y);
-  x[4] = bf_lo(u.z); x[5] = bf_hi(u.z);
-  x[6] = bf_lo(u.w); x[7] = bf_hi(u.w);
-}
-
 template <int NT>
 __global__ __launch_bounds__(512, 2) void k_full_one(FullArgs a) {
   __shared__ float red[2][kOMaxW][2 * kOTile];  // per buffer and wave: 32 sums of squares, then 32 dot products
@@ -79,7 +62,7 @@ __global__ __launch_bounds__(512, 2) void k_full_one(FullArgs a) {
   int64_t t = blockIdx.x;
   if (t < T) {
 #pragma unroll
-    for (int k = 0; k < kOTile; ++k) v[k] = o_ld(row(plane, n_src, t, k), coff, k < n_src ? 0x7fffffff : 0);
+    for (int k = 0; k < kOTile; ++k) v[k] = ld16_rec(row(plane, n_src, t, k), coff, k < n_src ? 0x7fffffff : 0);
   }
   // One flat loop over (token, tile) pairs, so that the row registers take
   // the same physical registers in every iteration.
@@ -112,7 +95,7 @@ __global__ __launch_bounds__(512, 2) void k_full_one(FullArgs a) {
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         float x[8];
-        o_unpack(v[16 * h + k], x);
+        unpack_bf8(v[16 * h + k], x);
         float ss = 0.f, dt = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -151,9 +134,9 @@ __global__ __launch_bounds__(512, 2) void k_full_one(FullArgs a) {
       uint4 u = v[k];
       asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
       float x[8];
-      o_unpack(u, x);
+      unpack_bf8(u, x);
       // Past the last token, and for rows past n_src, the load reads nothing.
-      v[k] = o_ld(row(pl, ns, tr, rn0 + k), coff, more && rn0 + k < ns ? 0x7fffffff : 0);
+      v[k] = ld16_rec(row(pl, ns, tr, rn0 + k), coff, more && rn0 + k < ns ? 0x7fffffff : 0);
       const float al = read_lane(e, k);
 #pragma unroll
       for (int c = 0; c < 8; ++c) acc[c] = fmaf(al, x[c], acc[c]);
@@ -164,9 +147,7 @@ __global__ __launch_bounds__(512, 2) void k_full_one(FullArgs a) {
       const float inv = 1.0f / lsum;
       const uint4 o = make_uint4(pack_bf2(acc[0] * inv, acc[1] * inv), pack_bf2(acc[2] * inv, acc[3] * inv),
                                  pack_bf2(acc[4] * inv, acc[5] * inv), pack_bf2(acc[6] * inv, acc[7] * inv));
-      const __amdgpu_buffer_rsrc_t orow =
-          __builtin_amdgcn_make_buffer_rsrc(out + t * d, 0, 0x7fffffff, kBufferWord3);
-      __builtin_amdgcn_raw_buffer_store_b128(o4u{o.x, o.y, o.z, o.w}, orow, (int)coff, 0, kBufferNt);
+      st16_rec(out + t * d, coff, 0x7fffffff, o);
       m = -INFINITY;
       lsum = 0.f;
 #pragma unroll

@@ -369,6 +369,13 @@ def test_full_bwd_workspace_size():
     for n_src, n_dst, T, d in [(55, 1, 4096, 2048), (64, 32, 300, 512), (33, 33, 7, 1024)]:
         want = max(general(n_dst, T, d), fast_w(n_dst, T, d))
         assert binding.attnres_full_bwd_workspace_size(n_src, n_dst, T, d, 1) == want, (n_src, n_dst, T, d)
+    # one destination, one head, up to 32 sources, d = 512 .. 4096 in steps of 512: the vector kernel
+    # keeps one [d] fp32 slab per workgroup, at most min(T, 1024) of them (never more than the
+    # general path's slabs)
+    one = lambda T, d: min(T, 1024) * d * 4
+    for n_src, T, d in [(32, 4096, 4096), (9, 4096, 2048), (32, 5, 512), (1, 1, 1024), (17, 100000, 3072)]:
+        want = max(general(1, T, d), fast(1, T, d), one(T, d))
+        assert binding.attnres_full_bwd_workspace_size(n_src, 1, T, d, 1) == want, (n_src, T, d)
     assert binding.attnres_full_bwd_workspace_size(8, 3, 0, 64, 1) == 0
     assert binding.attnres_full_bwd_workspace_size(8, 0, 16, 64, 1) == 0
 

@@ -163,7 +163,7 @@ FULL_BWD_CASES = [
     (300, 2048, 32, 32, "per", "full_bwd_res"),
     (517, 1024, 17, 5, "shared", "full_bwd_res"),
     (403, 1280, 9, 9, "none", "full_bwd_res"),
-    (300, 1536, 32, 1, "per", "full_bwd_res"),
+    (300, 1536, 32, 1, "per", "full_bwd_one"),
     (290, 1792, 1, 1, "per", "full_bwd_res"),
     (261, 2048, 20, 13, "shared", "full_bwd_res"),
     (40, 4096, 32, 32, "per", "full_bwd_fast"),
@@ -182,6 +182,14 @@ FULL_BWD_CASES = [
     (40, 4096, 40, 7, "none", "full_bwd_wide"),
     (7, 1536, 47, 20, "per", "full_bwd_wide"),
     (1, 2048, 55, 1, "none", "full_bwd_wide"),
+    # one destination, one head, up to 32 sources, d <= 4096: the vector kernel (T past its
+    # workgroup count gives each several tokens and a ragged tail)
+    (2000, 4096, 32, 1, "shared", "full_bwd_one"),
+    (1100, 512, 9, 1, "none", "full_bwd_one"),
+    (1, 2048, 32, 1, "per", "full_bwd_one"),
+    (777, 1024, 17, 1, "per", "full_bwd_one"),
+    (1500, 3072, 5, 1, "shared", "full_bwd_one"),
+    (600, 2048, 1, 1, "per", "full_bwd_one"),
 ]
 
 
