@@ -1,4 +1,4 @@
-// Full AttnRes backward for one destination over up to 32 sources (gfx950,
+// Full AttnRes backward for one destination over up to 64 sources (gfx950,
 // bf16 I/O, one head): the backward of the call a model makes per sublayer
 // (b-lab.team summary §1 for the forward; the gradient is the chain rule
 // through it).  Per token, with p_i = q . v_i, r_i = 1 / sqrt(mean(v_i^2) +
@@ -10,11 +10,12 @@
 // little arithmetic for the matrix cores, so this runs on the vector units
 // and reads each source row and the token's dout row once.
 //
-// One workgroup of d / 8 threads owns one token at a time; thread tid owns
-// channels 8 tid .. 8 tid + 7.  The token's 32 source rows sit in registers
-// (16-byte buffer loads, one register quad per row; a row past n_src has a
-// zero-record descriptor, so it is never read and its gradient never
-// written):
+// One workgroup of d / C threads owns one token at a time; thread tid owns
+// channels C tid .. C tid + C - 1.  All R = 256 / C source rows of the token
+// sit in registers (R = 32 rows of 8 channels, or 64 rows of 4 channels for
+// 33 .. 64 sources; one register quad per row either way).  A row past n_src
+// has a zero-record descriptor, so it is never read and its gradient never
+// written:
 //   1. per row, the sum of squares, q . v and dout . v over the thread's
 //      channels, reduced over the wave by transposing reductions and over the
 //      waves through double-buffered LDS (one barrier per token);
@@ -33,15 +34,74 @@
 namespace attnres {
 namespace {
 
-constexpr int kBTile = 32;    // source rows held in registers
-constexpr int kBMaxW = 8;     // waves per workgroup at most (d <= 4096)
+constexpr int kBMaxW = 8;     // waves per workgroup at most
 constexpr int kBSlabs = 1024; // workgroups (and Z slabs) at most
 constexpr int kBRing = 8;     // accumulate: old d_src rows in flight ahead of their use
 constexpr int kAll = 0x7fffffff;
 
-template <bool ACC>
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// One thread's C channels of a bf16 row: 16 bytes (C = 8, a uint4) or 8
+// bytes (C = 4, a uint2), through a buffer descriptor of `records` bytes
+// (zero: nothing is read or written, and a load returns zeros).
+template <int C> struct PieceOf { typedef uint4 type; };
+template <> struct PieceOf<4> { typedef uint2 type; };
+
+template <int C>
+__device__ __forceinline__ typename PieceOf<C>::type piece_ld(const void* row, uint32_t off, int records) {
+  if constexpr (C == 8) {
+    return ld16_rec(row, off, records);
+  } else {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row), 0, records, kBufferWord3);
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kBufferNt);
+    return make_uint2(v.x, v.y);
+  }
+}
+
+__device__ __forceinline__ void piece_st(void* row, uint32_t off, int records, const float (&x)[8]) {
+  st16_rec(row, off, records,
+           make_uint4(pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3]), pack_bf2(x[4], x[5]), pack_bf2(x[6], x[7])));
+}
+__device__ __forceinline__ void piece_st(void* row, uint32_t off, int records, const float (&x)[4]) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(row, 0, records, kBufferWord3);
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3])}, r, (int)off, 0, kBufferNt);
+}
+
+__device__ __forceinline__ void piece_unpack(const uint4 u, float (&x)[8]) { unpack_bf8(u, x); }
+__device__ __forceinline__ void piece_unpack(const uint2 u, float (&x)[4]) {
+  x[0] = bf_lo(u.x); x[1] = bf_hi(u.x);
+  x[2] = bf_lo(u.y); x[3] = bf_hi(u.y);
+}
+
+// An opaque copy: the compiler cannot reuse an earlier unpacking of it.
+__device__ __forceinline__ uint4 piece_opaque(uint4 u) {
+  asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
+  return u;
+}
+__device__ __forceinline__ uint2 piece_opaque(uint2 u) {
+  asm volatile("" : "+v"(u.x), "+v"(u.y));
+  return u;
+}
+
+// q = w * g (or w) for C consecutive channels.
+template <int C>
+__device__ __forceinline__ void fold_q(const float* w, const float* g, float (&q)[C]) {
+#pragma unroll
+  for (int k = 0; k < C; k += 4) {
+    const float4 wv = *reinterpret_cast<const float4*>(w + k);
+    q[k] = wv.x; q[k + 1] = wv.y; q[k + 2] = wv.z; q[k + 3] = wv.w;
+    if (g != nullptr) {
+      const float4 gv = *reinterpret_cast<const float4*>(g + k);
+      q[k] *= gv.x; q[k + 1] *= gv.y; q[k + 2] *= gv.z; q[k + 3] *= gv.w;
+    }
+  }
+}
+
+template <bool ACC, int R>
 __global__ __launch_bounds__(512, 2) void k_full_bwd_one(FullBwdArgs a, float* zs) {
-  __shared__ float red[2][kBMaxW][3 * kBTile];  // per buffer and wave: sums of squares, q . v, dout . v
+  constexpr int C = 256 / R;  // channels per thread
+  typedef typename PieceOf<C>::type P;
+  __shared__ float red[2][kBMaxW][3 * R];  // per buffer and wave: sums of squares, q . v, dout . v
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int W = (int)blockDim.x >> 6;
@@ -50,32 +110,32 @@ __global__ __launch_bounds__(512, 2) void k_full_bwd_one(FullBwdArgs a, float* z
   const bf16_t* src = static_cast<const bf16_t*>(a.src);
   const bf16_t* dout = static_cast<const bf16_t*>(a.dout);
   bf16_t* dsrc = static_cast<bf16_t*>(a.d_src);
-  const uint32_t coff = (uint32_t)tid * 16u;  // this thread's byte offset in a row
+  const uint32_t coff = (uint32_t)tid * (2u * C);  // this thread's byte offset in a row
   // 1/d is read from LDS where it is used: a register copy held across the
   // token loop gets spilled.  (Written before the loop; every read follows
   // the loop's barrier.)
   __shared__ float lds_inv_d;
   if (tid == 0) lds_inv_d = 1.0f / (float)d;
 
-  float q[8];  // q = w * g of the destination, for this thread's channels
+  float q[C];  // q = w * g of the destination, for this thread's channels
   if (a.gain != nullptr)
-    fold_q8<true>(a.w + 8 * tid, a.gain + 8 * tid, q);
+    fold_q<C>(a.w + C * tid, a.gain + C * tid, q);
   else
-    fold_q8<false>(a.w + 8 * tid, nullptr, q);
-  float z[8];
+    fold_q<C>(a.w + C * tid, nullptr, q);
+  float z[C];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) z[c] = 0.f;
+  for (int c = 0; c < C; ++c) z[c] = 0.f;
 
   // Element offset of row r of token t (a row past n_src takes the last real
   // row's address, which its zero-record access never touches), from opaque
   // scalar copies of the plane size and the source count taken per token.
   auto row = [&](int64_t pl, int ns, int64_t t, int r) { return (int64_t)(r < ns ? r : ns - 1) * pl + t * d; };
-  uint4 v[kBTile], go;
+  P v[R], go;
   int64_t t = blockIdx.x;
   if (t < T) {
 #pragma unroll
-    for (int k = 0; k < kBTile; ++k) v[k] = ld16_rec(src + row(plane, n_src, t, k), coff, k < n_src ? kAll : 0);
-    go = ld16_rec(dout + t * d, coff);
+    for (int k = 0; k < R; ++k) v[k] = piece_ld<C>(src + row(plane, n_src, t, k), coff, k < n_src ? kAll : 0);
+    go = piece_ld<C>(dout + t * d, coff, kAll);
   }
   int buf = 0;
 #pragma unroll 1
@@ -93,120 +153,141 @@ __global__ __launch_bounds__(512, 2) void k_full_bwd_one(FullBwdArgs a, float* z
 
     // 1. sums of squares and q . v, 16 rows at a time (32 partials)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      float part[kBTile];
+    for (int h = 0; h < R / 16; ++h) {
+      float part[32];
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
-        float x[8];
-        unpack_bf8(v[16 * h + k], x);
+        float x[C];
+        piece_unpack(v[16 * h + k], x);
         float ss = 0.f, p = 0.f;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
+        for (int c = 0; c < C; ++c) {
           ss = fmaf(x[c], x[c], ss);
           p = fmaf(q[c], x[c], p);
         }
         part[k] = ss;
         part[16 + k] = p;
       }
-      const float tot = transpose_reduce_pow2<kBTile>(part);
-      if ((rl & 1) == 0) red[buf][wave][pv < 16 ? 16 * h + pv : kBTile + 16 * h + (pv - 16)] = tot;
+      const float tot = transpose_reduce_pow2<32>(part);
+      if ((rl & 1) == 0) red[buf][wave][pv < 16 ? 16 * h + pv : R + 16 * h + (pv - 16)] = tot;
     }
-    // ... and dout . v for the 32 rows
+    // ... and dout . v, 32 rows at a time
     {
-      float g[8], part[kBTile];
-      unpack_bf8(go, g);
+      float g[C];
+      piece_unpack(go, g);
 #pragma unroll
-      for (int k = 0; k < kBTile; ++k) {
-        // Unpack the row afresh: sharing the unpacked rows with the loop above
-        // would keep 256 floats live between the two.
-        uint4 u = v[k];
-        asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
-        float x[8];
-        unpack_bf8(u, x);
-        float da = 0.f;
+      for (int h = 0; h < R / 32; ++h) {
+        float part[32];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) da = fmaf(g[c], x[c], da);
-        part[k] = da;
+        for (int k = 0; k < 32; ++k) {
+          // Unpack afresh: sharing the unpacked rows with the pass above
+          // would keep 256 floats live between the two.
+          float x[C];
+          piece_unpack(piece_opaque(v[32 * h + k]), x);
+          float da = 0.f;
+#pragma unroll
+          for (int c = 0; c < C; ++c) da = fmaf(g[c], x[c], da);
+          part[k] = da;
+        }
+        const float tot = transpose_reduce_pow2<32>(part);
+        if ((rl & 1) == 0) red[buf][wave][2 * R + 32 * h + pv] = tot;
       }
-      const float tot = transpose_reduce_pow2<kBTile>(part);
-      if ((rl & 1) == 0) red[buf][wave][2 * kBTile + pv] = tot;
     }
     // With accumulate, the first old d_src rows are read while the waves meet.
-    uint4 ring[ACC ? kBRing : 1];
+    P ring[ACC ? kBRing : 1];
     if constexpr (ACC) {
 #pragma unroll
-      for (int k = 0; k < kBRing; ++k) ring[k] = ld16_rec(dsrc + row(pl, ns, t, k), coff, k < ns ? kAll : 0);
+      for (int k = 0; k < kBRing; ++k) ring[k] = piece_ld<C>(dsrc + row(pl, ns, t, k), coff, k < ns ? kAll : 0);
     }
     lds_barrier();
 
-    // 2. the softmax and the coefficients, row li on lanes li and li + 32
-    const int li = rl & (kBTile - 1);
+    // 2. the softmax and the coefficients, row li on lane li (and li + 32 when R = 32)
+    const int li = rl & (R - 1);
     float ss = 0.f, p = 0.f, da = 0.f;
     for (int w2 = 0; w2 < W; ++w2) {
       ss += red[buf][w2][li];
-      p += red[buf][w2][kBTile + li];
-      da += red[buf][w2][2 * kBTile + li];
+      p += red[buf][w2][R + li];
+      da += red[buf][w2][2 * R + li];
     }
     const bool valid = li < n_src;
     const float inv_d = lds_inv_d;
     const float r = 1.0f / sqrtf(ss * inv_d + a.eps);
     const float s = valid ? r * p : -INFINITY;
-    const float mx = group_max<kBTile>(s);
+    const float mx = group_max<R>(s);
     const float e = valid ? expf(s - mx) : 0.f;
-    const float al = e / group_sum<kBTile>(e);
-    const float ds = al * (da - group_sum<kBTile>(al * da));
+    const float al = e / group_sum<R>(e);
+    const float ds = al * (da - group_sum<R>(al * da));
     const float cq = ds * r;                       // coefficient of q in dv, and of v in Z
     const float cv = -ds * p * r * r * r * inv_d;  // coefficient of v in dv (through the RMS)
 
     // 3. d_src, row by row; each row's register then takes the next token's row
-    float g[8];
-    unpack_bf8(go, g);
+    float g[C];
+    piece_unpack(go, g);
 #pragma unroll
-    for (int k = 0; k < kBTile; ++k) {
-      uint4 u = v[k];
-      asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
-      float x[8];
-      unpack_bf8(u, x);
-      v[k] = ld16_rec(src + row(pl, ns, tr, k), coff, more && k < ns ? kAll : 0);
-      const float A = read_lane(al, k), B = read_lane(cq, k), C = read_lane(cv, k);
-      float o[8];
+    for (int k = 0; k < R; ++k) {
+      float x[C];
+      piece_unpack(piece_opaque(v[k]), x);
+      v[k] = piece_ld<C>(src + row(pl, ns, tr, k), coff, more && k < ns ? kAll : 0);
+      const float A = read_lane(al, k), B = read_lane(cq, k), Cv = read_lane(cv, k);
+      float o[C];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        o[c] = fmaf(A, g[c], fmaf(B, q[c], C * x[c]));
+      for (int c = 0; c < C; ++c) {
+        o[c] = fmaf(A, g[c], fmaf(B, q[c], Cv * x[c]));
         z[c] = fmaf(B, x[c], z[c]);
       }
       if constexpr (ACC) {
-        float old[8];
-        unpack_bf8(ring[k % kBRing], old);
+        float old[C];
+        piece_unpack(ring[k % kBRing], old);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) o[c] += old[c];
-        if (k + kBRing < kBTile)
-          ring[k % kBRing] = ld16_rec(dsrc + row(pl, ns, t, k + kBRing), coff, k + kBRing < ns ? kAll : 0);
+        for (int c = 0; c < C; ++c) o[c] += old[c];
+        if (k + kBRing < R)
+          ring[k % kBRing] = piece_ld<C>(dsrc + row(pl, ns, t, k + kBRing), coff, k + kBRing < ns ? kAll : 0);
       }
-      st16_rec(dsrc + row(pl, ns, t, k), coff, k < ns ? kAll : 0,
-               make_uint4(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]), pack_bf2(o[4], o[5]), pack_bf2(o[6], o[7])));
-      __builtin_amdgcn_sched_barrier(0);  // one row's floats at a time
+      piece_st(dsrc + row(pl, ns, t, k), coff, k < ns ? kAll : 0, o);
     }
     // The next token's dout row, first needed after its rows' first pass.
-    go = ld16_rec(dout + tr * d, coff, more ? kAll : 0);
+    go = piece_ld<C>(dout + tr * d, coff, more ? kAll : 0);
     buf ^= 1;
     t = tn;
   }
-  // This workgroup's slab of Z (zeros if it had no token): 32 bytes per
+  // This workgroup's slab of Z (zeros if it had no token): 4 C bytes per
   // thread, at twice the thread's bf16 row offset.
   float* zrow = zs + (int64_t)blockIdx.x * d;
   uint32_t zoff = coff;
   asm volatile("" : "+v"(zoff));  // formed here, not held across the loop
   zoff *= 2;
-  st16_rec(zrow, zoff, kAll, make_uint4(__float_as_uint(z[0]), __float_as_uint(z[1]), __float_as_uint(z[2]), __float_as_uint(z[3])));
-  st16_rec(zrow, zoff + 16, kAll, make_uint4(__float_as_uint(z[4]), __float_as_uint(z[5]), __float_as_uint(z[6]), __float_as_uint(z[7])));
+#pragma unroll
+  for (int k = 0; k < C; k += 4)
+    st16_rec(zrow, zoff + 4 * k, kAll,
+             make_uint4(__float_as_uint(z[k]), __float_as_uint(z[k + 1]), __float_as_uint(z[k + 2]),
+                        __float_as_uint(z[k + 3])));
 }
 
+// Rows held per thread: 32 (8 channels, d up to 4096) for up to 32 sources,
+// 64 (4 channels, d up to 2048) for 33 .. 64.
+int one_rows(int64_t n_src) { return n_src > 32 ? 64 : 32; }
+
 bool one_shape(int64_t n_src, int64_t n_dst, int64_t d, int H) {
-  return H == 1 && n_dst == 1 && n_src >= 1 && n_src <= kBTile && d >= 512 && d % 512 == 0 && d <= 8 * 64 * kBMaxW;
+  if (H != 1 || n_dst != 1 || n_src < 1 || n_src > 64 || d < 512 || d % 512 != 0) return false;
+  return d <= (int64_t)(256 / one_rows(n_src)) * 64 * kBMaxW;
 }
 
 int64_t one_slabs(int64_t T) { return T < kBSlabs ? T : kBSlabs; }
+
+template <int R>
+hipError_t launch_rows(const FullBwdArgs& a, const float** slabs, int64_t* n_slabs, hipStream_t st) {
+  const int B = (int)(a.d / (256 / R));
+  auto kern = a.accumulate ? k_full_bwd_one<true, R> : k_full_bwd_one<false, R>;
+  int per_cu = 0;
+  const hipError_t e = blocks_per_cu(reinterpret_cast<const void*>(kern), B, &per_cu);
+  if (e != hipSuccess) return e;
+  int64_t grid = (int64_t)num_cus() * (per_cu < 1 ? 1 : per_cu);
+  if (grid > one_slabs(a.T)) grid = one_slabs(a.T);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3((unsigned)B), 0, st, a, a.zslots);
+  *slabs = a.zslots;
+  *n_slabs = grid;
+  return hipGetLastError();
+}
 
 }  // namespace
 
@@ -222,17 +303,7 @@ bool full_bwd_one_ok(const FullBwdArgs& a) {
 }
 
 hipError_t launch_full_bwd_one(const FullBwdArgs& a, const float** slabs, int64_t* n_slabs, hipStream_t st) {
-  const int B = (int)(a.d / 8);
-  auto kern = a.accumulate ? k_full_bwd_one<true> : k_full_bwd_one<false>;
-  int per_cu = 0;
-  const hipError_t e = blocks_per_cu(reinterpret_cast<const void*>(kern), B, &per_cu);
-  if (e != hipSuccess) return e;
-  int64_t grid = (int64_t)num_cus() * (per_cu < 1 ? 1 : per_cu);
-  if (grid > one_slabs(a.T)) grid = one_slabs(a.T);
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3((unsigned)B), 0, st, a, a.zslots);
-  *slabs = a.zslots;
-  *n_slabs = grid;
-  return hipGetLastError();
+  return one_rows(a.n_src) == 64 ? launch_rows<64>(a, slabs, n_slabs, st) : launch_rows<32>(a, slabs, n_slabs, st);
 }
 
 }  // namespace attnres

@@ -177,9 +177,9 @@ hipError_t launch_full_bwd_staged(const FullBwdArgs& a, const uint4* qpk, const 
                                   hipStream_t st);
 hipError_t launch_full_bwd_zw(const FullBwdArgs& a, const float* cws, float* zs, int groups, hipStream_t st);
 hipError_t launch_full_bwd_fast(const FullBwdArgs& a, const float** slabs, int64_t* n_slabs, hipStream_t st);
-// Vector Full backward for one destination over up to 32 sources
-// (full_bwd_one.hip): its Z slabs ([slabs, d] fp32, one per workgroup) are
-// the whole workspace.
+// Vector Full backward for one destination over up to 64 sources
+// (full_bwd_one.hip; d <= 4096 for up to 32 sources, d <= 2048 above): its Z
+// slabs ([slabs, d] fp32, one per workgroup) are the whole workspace.
 size_t full_bwd_one_workspace_bytes(int64_t n_src, int64_t n_dst, int64_t T, int64_t d, int H);
 bool full_bwd_one_ok(const FullBwdArgs& a);
 hipError_t launch_full_bwd_one(const FullBwdArgs& a, const float** slabs, int64_t* n_slabs, hipStream_t st);

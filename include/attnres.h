@@ -323,8 +323,8 @@ size_t attnres_full_bwd_workspace_size(int64_t n_src, int64_t n_dst, int64_t T, 
  * limit; they take bf16 with n_src <= 32 and one head, or H = 2, 4 or 8
  * heads of whole 256-channel runs with d = 1024 .. 2048, and bf16 with
  * 33 <= n_src <= 64, n_dst <= 32, one head and d a multiple of 512.  (One
- * destination with one head, n_src <= 32 and d = 512 .. 4096 runs on a vector
- * kernel.)  dw and dgain are fixed-order sums over tokens (no atomics).
+ * destination with one head and d a multiple of 512 runs on a vector kernel:
+ * n_src <= 32 with d <= 4096, or n_src <= 64 with d <= 2048.)  dw and dgain are fixed-order sums over tokens (no atomics).
  */
 int attnres_full_bwd(const void* src, int64_t n_src, int64_t T, int64_t d, const float* w,
                      int64_t n_dst, const float* gain, int64_t gain_ld, float eps, int32_t H,

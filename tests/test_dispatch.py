@@ -117,10 +117,11 @@ def test_phase2_full_and_policy():
     assert variant(binding.OP_FULL_BWD, 32, 32, 100, 4096) == "full_bwd_fast"
     assert variant(binding.OP_FULL_BWD, 32, 32, 100, 512) == "full_bwd_fast"
     # 33 .. 64 sources and up to 32 destinations: the two-tile backward (one head, d a multiple of 512)
-    for L, n_dst, d in ((33, 32, 2048), (55, 1, 2048), (64, 32, 512), (40, 7, 4096), (47, 20, 1536)):
+    for L, n_dst, d in ((33, 32, 2048), (55, 1, 4096), (64, 32, 512), (40, 7, 4096), (47, 20, 1536), (55, 2, 2048)):
         assert variant(binding.OP_FULL_BWD, L, n_dst, 100, d) == "full_bwd_wide", (L, n_dst, d)
-    # one destination, one head, up to 32 sources, d <= 4096: the vector kernel that reads each row once
-    for L, d in ((32, 2048), (1, 512), (9, 4096), (17, 1536), (32, 1024)):
+    # one destination, one head: the vector kernel that reads each row once (up to 32 sources with
+    # d <= 4096, 33 .. 64 with d <= 2048)
+    for L, d in ((32, 2048), (1, 512), (9, 4096), (17, 1536), (32, 1024), (55, 2048), (64, 512), (33, 1536)):
         assert variant(binding.OP_FULL_BWD, L, 1, 100, d) == "full_bwd_one", (L, d)
     assert variant(binding.OP_FULL_BWD, 32, 1, 100, 8192) == "full_bwd_fast"
     assert variant(binding.OP_FULL_BWD, 32, 1, 100, 2048, H=2) == "full_bwd_res"

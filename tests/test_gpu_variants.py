@@ -176,12 +176,13 @@ FULL_BWD_CASES = [
     (7, 2048, 1, 1, "none", "full_bwd_res", 8),
     (19, 2048, 32, 32, "per", "full_bwd_res", 8),
     # 33 .. 64 sources, up to 32 destinations: two source tiles
-    (300, 2048, 55, 1, "per", "full_bwd_wide"),
+    (300, 2048, 55, 1, "per", "full_bwd_one"),
     (261, 1024, 33, 32, "shared", "full_bwd_wide"),
     (530, 2048, 64, 32, "per", "full_bwd_wide"),
     (40, 4096, 40, 7, "none", "full_bwd_wide"),
     (7, 1536, 47, 20, "per", "full_bwd_wide"),
-    (1, 2048, 55, 1, "none", "full_bwd_wide"),
+    (1, 2048, 55, 1, "none", "full_bwd_one"),
+    (77, 4096, 48, 1, "per", "full_bwd_wide"),
     # one destination, one head, up to 32 sources, d <= 4096: the vector kernel (T past its
     # workgroup count gives each several tokens and a ragged tail)
     (2000, 4096, 32, 1, "shared", "full_bwd_one"),
@@ -190,6 +191,10 @@ FULL_BWD_CASES = [
     (777, 1024, 17, 1, "per", "full_bwd_one"),
     (1500, 3072, 5, 1, "shared", "full_bwd_one"),
     (600, 2048, 1, 1, "per", "full_bwd_one"),
+    # 33 .. 64 sources: 64 rows of 4 channels per thread (d <= 2048)
+    (1200, 1024, 64, 1, "shared", "full_bwd_one"),
+    (333, 512, 33, 1, "per", "full_bwd_one"),
+    (1030, 2048, 47, 1, "none", "full_bwd_one"),
 ]
 
 
