@@ -10,7 +10,7 @@ in HBM before timing starts.
 Prints ONE JSON line on stdout.  Everything else goes to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                  [--no-extra] [--workload block|mhar|full|full_h8|full_wide|bwd|full_bwd|full_bwd_h8|block_update|decode|msar|block_msar]
+                  [--no-extra] [--workload block|mhar|full|full_h8|full_wide|full_one|bwd|full_bwd|full_bwd_h8|block_update|decode|msar|block_msar]
                   [--copy-calibration]
 """
 
@@ -41,7 +41,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="block", choices=["block", "mhar", "full", "full_h8", "full_wide", "bwd", "mhar_bwd", "full_bwd", "full_bwd_h8", "block_update",
-                                                                "decode", "msar", "block_msar", "depth_sweep"])
+                                                                "decode", "msar", "block_msar", "depth_sweep", "full_one"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     p.add_argument("--ceilings", action="store_true",
@@ -533,6 +533,59 @@ def bench_full_wide(args, T=4096, d=2048, L=55):
     return dict(name=f"full_wide_bf16_T{T}_d{d}_L{L}", **cases)
 
 
+def bench_full_one(args, T=4096, d=2048, Ls=(9, 32, 55)):
+    """The per-sublayer Full AttnRes calls of a model: one destination over the
+    L sources before it, forward and backward (the backward accumulating into
+    d_src, as every later sublayer adds to a source's gradient), for a shallow,
+    a 32-source and a 55-source sublayer.  Each is timed with HIP events around
+    its launches.  Sources are seeded normal draws made on the device, source i
+    with standard deviation 1 + 0.2 i, w ~ N(0, 1/d), gain ~ 1 + N(0, 0.01)."""
+    import torch
+    import depth_wise_attention_amd as ar
+
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3  # us
+
+    n = max(3, args.steps // 2)
+    cases = {}
+    for L in Ls:
+        src = torch.randn((L, T, d), generator=gen, device="cuda")
+        src *= (1 + 0.2 * torch.arange(L, device="cuda", dtype=torch.float32))[:, None, None]
+        src = src.to(torch.bfloat16)
+        w = torch.randn((1, d), generator=gen, device="cuda") / d ** 0.5
+        g = 1 + 0.1 * torch.randn((1, d), generator=gen, device="cuda")
+        out = torch.empty((1, T, d), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(max(1, ar.attnres_full_fwd_workspace_size(L, 1, d, 1, ar.BF16)), dtype=torch.uint8,
+                         device="cuda")
+        us = timed(lambda: ar.attnres_full_fwd(src, w, g, 1e-6, 1, out=out, ws=ws), n)
+        b = T * d * 2 * (L + 1)
+        cases[f"fwd_L{L}"] = dict(us=us, bytes=b, gbs=b / us / 1e3,
+                                  kernel=ar.attnres_kernel_variant(ar.OP_FULL_FWD, L, 1, T, d, 1))
+        dout = torch.randn((1, T, d), generator=gen, device="cuda").to(torch.bfloat16)
+        d_src = torch.zeros_like(src)
+        dw, dg = torch.zeros_like(w), torch.zeros_like(g)
+        wsb = torch.empty(ar.attnres_full_bwd_workspace_size(L, 1, T, d, 1), dtype=torch.uint8, device="cuda")
+        us = timed(lambda: ar.attnres_full_bwd(src, w, dout, g, 1e-6, 1, d_src=d_src, dw=dw, dgain=dg, ws=wsb,
+                                               accumulate=True), n)
+        b = T * d * 2 * (3 * L + 1)  # read src, dout and the old d_src, write d_src
+        cases[f"bwd_acc_L{L}"] = dict(us=us, bytes=b, gbs=b / us / 1e3,
+                                      kernel=ar.attnres_kernel_variant(ar.OP_FULL_BWD, L, 1, T, d, 1))
+        del src, out, ws, dout, d_src, wsb
+    return dict(name=f"full_one_bf16_T{T}_d{d}", **cases)
+
+
 def bench_bwd(args, T=8192, H=1):
     import torch
     import depth_wise_attention_amd as ar
@@ -860,7 +913,8 @@ def main():
               "bwd": lambda: bench_bwd(args), "mhar_bwd": lambda: bench_bwd(args, H=8), "full_bwd": lambda: bench_full_bwd(args),
               "block_update": lambda: bench_update(args), "decode": lambda: bench_decode(args),
               "msar": lambda: bench_msar(args), "block_msar": lambda: bench_block_msar(args),
-              "depth_sweep": lambda: bench_depth_sweep(args), "full_wide": lambda: bench_full_wide(args)}[args.workload]
+              "depth_sweep": lambda: bench_depth_sweep(args), "full_wide": lambda: bench_full_wide(args),
+              "full_one": lambda: bench_full_one(args)}[args.workload]
         log(json.dumps(fn()))
         return
 
@@ -875,7 +929,7 @@ def main():
         for fn in (lambda: bench_block(args, H=8, T=32768, with_events=True), lambda: bench_full(args),
                    lambda: bench_bwd(args), lambda: bench_bwd(args, H=8), lambda: bench_full_bwd(args), lambda: bench_update(args),
                    lambda: bench_decode(args), lambda: bench_msar(args), lambda: bench_block_msar(args),
-                   lambda: bench_full_wide(args)):
+                   lambda: bench_full_wide(args), lambda: bench_full_one(args)):
             r = fn()
             extra[r.pop("name")] = {k: v for k, v in r.items() if k not in ("T", "d", "N", "S", "H")}
             torch.cuda.empty_cache()

@@ -433,9 +433,28 @@ __global__ __launch_bounds__(256) void k_full_bwd_generic(FullBwdArgs a) {
 }
 
 // dw_j = g_j * Z_j, dg_j = w_j * Z_j (summed over j for a shared gain), with
-// Z_j the fixed-order sum of the slot partials.  Block = 4 groups of 64 lanes
-// over 64 consecutive channels of one destination; group gi sums slots
-// gi, gi+4, ...; the four group sums are then added in order.
+// Z_j the fixed-order sum of the slot partials: slot s goes to group s % 4
+// and, within it, to accumulator (s / 4) % 8; each group adds its eight
+// accumulators pairwise, and the four group sums are added in order.  The
+// eight accumulators keep eight independent loads in flight per lane (a
+// single running sum waits for each load in turn).
+__device__ __forceinline__ float z_group_sum(const float* z, int64_t slots, int S, int j, int d, int k, int gi) {
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int64_t stride = (int64_t)S * d;
+  int64_t s = gi;
+  for (; s + 28 < slots; s += 32) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] += z[(s + 4 * u) * stride + (int64_t)j * d + k];
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    if (s + 4 * u < slots) acc[u] += z[(s + 4 * u) * stride + (int64_t)j * d + k];
+  return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+}
+
+// Block = 4 groups of 64 lanes over 64 consecutive channels of one
+// destination; group gi sums its slots, the four group sums are added in
+// order.  With one destination a shared gain's dg = w Z is written here too.
 __global__ __launch_bounds__(256) void k_bwd_reduce(const float* z, int64_t slots, int S, int d,
                                                     const float* w, const float* gain,
                                                     int64_t gain_ld, float* dw, float* dgain,
@@ -444,20 +463,19 @@ __global__ __launch_bounds__(256) void k_bwd_reduce(const float* z, int64_t slot
   const int lane = lane_id(), gi = threadIdx.x >> 6;
   const int k = blockIdx.x * 64 + lane;
   const int j = blockIdx.y;
-  float acc = 0.f;
-  if (k < d)
-    for (int64_t s = gi; s < slots; s += 4) acc += z[(s * S + j) * (int64_t)d + k];
-  part[gi][lane] = acc;
+  part[gi][lane] = k < d ? z_group_sum(z, slots, S, j, d, k, gi) : 0.f;
   __syncthreads();
   if (gi != 0 || k >= d) return;
   const float Z = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
   const int64_t jk = (int64_t)j * d + k;
   const float gj = gain ? gain[j * gain_ld + k] : 1.0f;
   dw[jk] = accumulate ? dw[jk] + gj * Z : gj * Z;
-  if (gain != nullptr && gain_ld != 0) dgain[jk] = accumulate ? dgain[jk] + w[jk] * Z : w[jk] * Z;
+  if (gain != nullptr && (gain_ld != 0 || S == 1))
+    dgain[jk] = accumulate ? dgain[jk] + w[jk] * Z : w[jk] * Z;
 }
 
-// Shared gain: dg = sum_j w_j * Z_j, summed over j in order (one thread per channel).
+// Shared gain over several destinations: dg = sum_j w_j * Z_j, summed over j
+// in order (one thread per channel).
 __global__ __launch_bounds__(256) void k_bwd_reduce_shared_gain(const float* z, int64_t slots,
                                                                 int S, int d, const float* w,
                                                                 float* dgain, int accumulate) {
@@ -465,12 +483,10 @@ __global__ __launch_bounds__(256) void k_bwd_reduce_shared_gain(const float* z, 
   if (k >= d) return;
   float total = 0.f;
   for (int j = 0; j < S; ++j) {
-    float Z = 0.f;
     // Same grouping and order as k_bwd_reduce, so Z matches it bit for bit.
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int gi = 0; gi < 4; ++gi)
-      for (int64_t s = gi; s < slots; s += 4) part[gi] += z[(s * S + j) * (int64_t)d + k];
-    Z = ((part[0] + part[1]) + part[2]) + part[3];
+    float part[4];
+    for (int gi = 0; gi < 4; ++gi) part[gi] = z_group_sum(z, slots, S, j, d, k, gi);
+    const float Z = ((part[0] + part[1]) + part[2]) + part[3];
     total = fmaf(w[(int64_t)j * d + k], Z, total);
   }
   dgain[k] = accumulate ? dgain[k] + total : total;
@@ -537,7 +553,7 @@ static hipError_t launch_z_reduce(const float* z, int64_t slots_used, int rows, 
   const bool shared = gain != nullptr && gain_ld == 0;
   hipLaunchKernelGGL(k_bwd_reduce, dim3((unsigned)((d + 63) / 64), (unsigned)rows), dim3(256), 0, st, z,
                      slots_used, rows, d, w, gain, gain_ld, dw, dgain, accumulate);
-  if (shared)
+  if (shared && rows > 1)
     hipLaunchKernelGGL(k_bwd_reduce_shared_gain, dim3((unsigned)((d + 255) / 256)), dim3(256), 0, st, z,
                        slots_used, rows, d, w, dgain, accumulate);
   return hipGetLastError();
