@@ -1,11 +1,14 @@
 // Full AttnRes backward for one destination over up to 64 sources (gfx950,
-// bf16 I/O, one head): the backward of the call a model makes per sublayer
-// (b-lab.team summary §1 for the forward; the gradient is the chain rule
-// through it).  Per token, with p_i = q . v_i, r_i = 1 / sqrt(mean(v_i^2) +
-// eps), s_i = r_i p_i, alpha = softmax(s) and a_i = dout . v_i:
+// bf16 I/O): the backward of the call a model makes per sublayer (b-lab.team
+// summary §1 for the forward; the gradient is the chain rule through it).
+// Per token, with p_i = q . v_i, r_i = 1 / sqrt(mean(v_i^2) + eps),
+// s_i = r_i p_i, alpha = softmax(s) and a_i = dout . v_i:
 //   ds_i  = alpha_i (a_i - sum_m alpha_m a_m)
 //   dv_i  = alpha_i dout + ds_i r_i q - ds_i p_i r_i^3 / d * v_i
 //   Z    += sum_i ds_i r_i v_i            (dw = g * Z, dgain = w * Z)
+// With H heads (chatpaper MHAR abstract) p, a, alpha and ds are per head over
+// the head's channels, r is over the whole d, and the v term of dv sums
+// ds p over the heads.
 // Three dot products per source row over d, then elementwise work: far too
 // little arithmetic for the matrix cores, so this runs on the vector units
 // and reads each source row and the token's dout row once.
@@ -97,14 +100,17 @@ __device__ __forceinline__ void fold_q(const float* w, const float* g, float (&q
   }
 }
 
-template <bool ACC, int R>
+template <bool ACC, int R, bool MH>
 __global__ __launch_bounds__(512, 2) void k_full_bwd_one(FullBwdArgs a, float* zs) {
   constexpr int C = 256 / R;  // channels per thread
   typedef typename PieceOf<C>::type P;
   __shared__ float red[2][kBMaxW][3 * R];  // per buffer and wave: sums of squares, q . v, dout . v
+  __shared__ float dsp[MH ? 2 : 1][MH ? kBMaxW : 1][R];  // heads: ds p per head and row
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int W = (int)blockDim.x >> 6;
+  // Heads are runs of W / H whole waves: this wave's head and its first wave.
+  const int wph = MH ? W / a.H : W, head = wave / wph, hw0 = head * wph;
   const int d = (int)a.d, n_src = (int)a.n_src;
   const int64_t T = a.T, plane = T * d;
   const bf16_t* src = static_cast<const bf16_t*>(a.src);
@@ -203,9 +209,11 @@ __global__ __launch_bounds__(512, 2) void k_full_bwd_one(FullBwdArgs a, float* z
 
     // 2. the softmax and the coefficients, row li on lane li (and li + 32 when R = 32)
     const int li = rl & (R - 1);
+    // The sum of squares is over every wave (the whole d); the products with
+    // q and dout are over this head's waves.
     float ss = 0.f, p = 0.f, da = 0.f;
-    for (int w2 = 0; w2 < W; ++w2) {
-      ss += red[buf][w2][li];
+    for (int w2 = 0; w2 < W; ++w2) ss += red[buf][w2][li];
+    for (int w2 = hw0; w2 < hw0 + wph; ++w2) {
       p += red[buf][w2][R + li];
       da += red[buf][w2][2 * R + li];
     }
@@ -217,8 +225,18 @@ __global__ __launch_bounds__(512, 2) void k_full_bwd_one(FullBwdArgs a, float* z
     const float e = valid ? expf(s - mx) : 0.f;
     const float al = e / group_sum<R>(e);
     const float ds = al * (da - group_sum<R>(al * da));
-    const float cq = ds * r;                       // coefficient of q in dv, and of v in Z
-    const float cv = -ds * p * r * r * r * inv_d;  // coefficient of v in dv (through the RMS)
+    const float cq = ds * r;  // coefficient of q in dv, and of v in Z
+    // The coefficient of v in dv comes through the RMS, which every head
+    // shares: -r^3 / d times the sum over heads of ds p, exchanged through LDS
+    // (a second barrier) when there are several.
+    float dsp_all = ds * p;
+    if constexpr (MH) {
+      if (wave == hw0 && rl < R) dsp[buf][head][li] = dsp_all;
+      lds_barrier();
+      dsp_all = 0.f;
+      for (int h2 = 0; h2 < a.H; ++h2) dsp_all += dsp[buf][h2][li];
+    }
+    const float cv = -dsp_all * r * r * r * inv_d;
 
     // 3. d_src, row by row; each row's register then takes the next token's row
     float g[C];
@@ -268,8 +286,11 @@ __global__ __launch_bounds__(512, 2) void k_full_bwd_one(FullBwdArgs a, float* z
 int one_rows(int64_t n_src) { return n_src > 32 ? 64 : 32; }
 
 bool one_shape(int64_t n_src, int64_t n_dst, int64_t d, int H) {
-  if (H != 1 || n_dst != 1 || n_src < 1 || n_src > 64 || d < 512 || d % 512 != 0) return false;
-  return d <= (int64_t)(256 / one_rows(n_src)) * 64 * kBMaxW;
+  if (n_dst != 1 || n_src < 1 || n_src > 64 || d < 512 || d % 512 != 0) return false;
+  const int64_t wave_ch = (int64_t)(256 / one_rows(n_src)) * 64;  // channels per wave
+  if (d > wave_ch * kBMaxW) return false;
+  // Heads of whole waves.
+  return H == 1 || ((H == 2 || H == 4 || H == 8) && (d / H) % wave_ch == 0);
 }
 
 int64_t one_slabs(int64_t T) { return T < kBSlabs ? T : kBSlabs; }
@@ -277,7 +298,8 @@ int64_t one_slabs(int64_t T) { return T < kBSlabs ? T : kBSlabs; }
 template <int R>
 hipError_t launch_rows(const FullBwdArgs& a, const float** slabs, int64_t* n_slabs, hipStream_t st) {
   const int B = (int)(a.d / (256 / R));
-  auto kern = a.accumulate ? k_full_bwd_one<true, R> : k_full_bwd_one<false, R>;
+  auto kern = a.H > 1 ? (a.accumulate ? k_full_bwd_one<true, R, true> : k_full_bwd_one<false, R, true>)
+                      : (a.accumulate ? k_full_bwd_one<true, R, false> : k_full_bwd_one<false, R, false>);
   int per_cu = 0;
   const hipError_t e = blocks_per_cu(reinterpret_cast<const void*>(kern), B, &per_cu);
   if (e != hipSuccess) return e;

@@ -1,7 +1,9 @@
 // Full AttnRes forward for one destination over up to 64 sources (gfx950,
-// bf16 I/O, one head): the call a model makes per sublayer, at any depth up
-// to 63 sublayers (b-lab.team summary §1; dimensionstp "Attention Residuals
-// Review" §3 (2) runs 54).  With one query the contractions per token are two
+// bf16 I/O): the call a model makes per sublayer, at any depth up to 63
+// sublayers (b-lab.team summary §1; dimensionstp "Attention Residuals Review"
+// §3 (2) runs 54).  With H heads (chatpaper MHAR abstract) each head is a run
+// of whole 512-channel waves with its own dot products and softmax; the RMS
+// is over the whole d.  With one query the contractions per token are two
 // vectors of n_src dot products over d, far too small for the matrix cores;
 // what matters is reading each source row once.
 //
@@ -39,6 +41,7 @@ __global__ __launch_bounds__(512, 2) void k_full_one(FullArgs a) {
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int W = (int)blockDim.x >> 6;
+  const int wph = W / a.H, hw0 = wave / wph * wph;  // waves per head; this head's first wave
   const int d = (int)a.d, n_src = (int)a.n_src;
   const int64_t T = a.T, plane = T * d;
   const bf16_t* src = static_cast<const bf16_t*>(a.src);
@@ -111,11 +114,11 @@ __global__ __launch_bounds__(512, 2) void k_full_one(FullArgs a) {
     }
     lds_barrier();
     const int li = rl & (kOTile - 1);  // both half-waves take rows 0..31: every lane holds the same totals
+    // The sum of squares is over every wave (the whole d), the dot product
+    // over the waves of this wave's head (H heads of W / H whole waves).
     float ss = 0.f, dt = 0.f;
-    for (int w2 = 0; w2 < W; ++w2) {
-      ss += red[buf][w2][li];
-      dt += red[buf][w2][kOTile + li];
-    }
+    for (int w2 = 0; w2 < W; ++w2) ss += red[buf][w2][li];
+    for (int w2 = hw0; w2 < hw0 + wph; ++w2) dt += red[buf][w2][kOTile + li];
     // 3. scores and the online depth softmax
     const bool valid = tl * kOTile + li < n_src;
     const float s = valid ? dt / sqrtf(ss * inv_d + a.eps) : -INFINITY;
@@ -164,7 +167,9 @@ __global__ __launch_bounds__(512, 2) void k_full_one(FullArgs a) {
 
 bool full_one_ok(const FullArgs& a) {
   auto al16 = [](const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; };
-  return a.dtype == kBF16 && a.H == 1 && a.n_dst == 1 && a.n_src >= 1 && a.n_src <= 2 * kOTile && a.T >= 1 &&
+  // Heads of whole 512-channel waves: H = 1, 2, 4 or 8 with d / H a multiple of 512.
+  const bool heads = (a.H == 1 || a.H == 2 || a.H == 4 || a.H == 8) && (a.d / a.H) % 512 == 0;
+  return a.dtype == kBF16 && heads && a.n_dst == 1 && a.n_src >= 1 && a.n_src <= 2 * kOTile && a.T >= 1 &&
          a.d >= 512 && a.d % 512 == 0 && a.d <= 8 * 64 * kOMaxW && al16(a.src) && al16(a.out) && al16(a.w) &&
          al16(a.gain);
 }

@@ -103,8 +103,9 @@ int attnres_full_fwd(const void* src, int64_t n_src, int64_t T, int64_t d,
  * as a bf16 high part plus a bf16 low part ([2, 32, d] bf16, 128 * d bytes).
  * So may one-head bf16 calls with 33 .. 64 sources and d a multiple of 512:
  * [2, 32, d] for n_dst <= 32, [2, 64, d] (256 * d bytes) above.  Every other
- * request needs none and gets 0.  (One destination and one head over up to 64
- * sources with d <= 4096 runs a vector kernel that ignores the workspace; the
+ * request needs none and gets 0.  (One destination over up to 64 sources
+ * with d <= 4096, and H = 1, 2, 4 or 8 with d / H a multiple of 512, runs a
+ * vector kernel that ignores the workspace; the
  * size returned still covers the matrix-core kernels, so a caller need not
  * know which runs.)
  */
@@ -323,8 +324,9 @@ size_t attnres_full_bwd_workspace_size(int64_t n_src, int64_t n_dst, int64_t T, 
  * limit; they take bf16 with n_src <= 32 and one head, or H = 2, 4 or 8
  * heads of whole 256-channel runs with d = 1024 .. 2048, and bf16 with
  * 33 <= n_src <= 64, n_dst <= 32, one head and d a multiple of 512.  (One
- * destination with one head and d a multiple of 512 runs on a vector kernel:
- * n_src <= 32 with d <= 4096, or n_src <= 64 with d <= 2048.)  dw and dgain are fixed-order sums over tokens (no atomics).
+ * destination with d a multiple of 512 runs on a vector kernel: n_src <= 32
+ * with d <= 4096, or n_src <= 64 with d <= 2048; H = 1, 2, 4 or 8 with d / H
+ * a multiple of 512 channels, or of 256 above 32 sources.)  dw and dgain are fixed-order sums over tokens (no atomics).
  */
 int attnres_full_bwd(const void* src, int64_t n_src, int64_t T, int64_t d, const float* w,
                      int64_t n_dst, const float* gain, int64_t gain_ld, float eps, int32_t H,

@@ -100,7 +100,11 @@ def test_phase2_full_and_policy():
     for L, d in ((55, 2048), (64, 2560), (33, 512), (64, 4096), (32, 2048), (9, 4096), (1, 512), (17, 1536)):
         assert variant(binding.OP_FULL_FWD, L, 1, 100, d) == "full_one", (L, d)
     assert variant(binding.OP_FULL_FWD, 32, 1, 100, 8192) == "full_fast"
-    assert variant(binding.OP_FULL_FWD, 32, 1, 100, 2048, H=2) == "full_fast"
+    # ... and with heads of whole 512-channel waves (d / H a multiple of 512)
+    for L, d, H in ((32, 2048, 2), (32, 4096, 8), (55, 4096, 4), (9, 1024, 2)):
+        assert variant(binding.OP_FULL_FWD, L, 1, 100, d, H=H) == "full_one", (L, d, H)
+    assert variant(binding.OP_FULL_FWD, 32, 1, 100, 2048, H=8) == "full_fast"
+    assert variant(binding.OP_FULL_FWD, 55, 1, 100, 2048, H=8) == "full_generic"
     assert variant(binding.OP_FULL_FWD, 32, 1, 100, 2048, dtype=F32) == "full_generic"
     assert variant(binding.OP_FULL_FWD, 55, 54, 100, 2048, H=8) == "full_generic"
     assert variant(binding.OP_FULL_FWD, 55, 54, 100, 768) == "full_generic"
@@ -124,11 +128,15 @@ def test_phase2_full_and_policy():
     for L, d in ((32, 2048), (1, 512), (9, 4096), (17, 1536), (32, 1024), (55, 2048), (64, 512), (33, 1536)):
         assert variant(binding.OP_FULL_BWD, L, 1, 100, d) == "full_bwd_one", (L, d)
     assert variant(binding.OP_FULL_BWD, 32, 1, 100, 8192) == "full_bwd_fast"
-    assert variant(binding.OP_FULL_BWD, 32, 1, 100, 2048, H=2) == "full_bwd_res"
+    # ... and with heads of whole waves (512 channels at up to 32 sources, 256 above)
+    for L, d, H in ((32, 2048, 2), (32, 4096, 8), (55, 2048, 8), (9, 1024, 2), (64, 512, 2)):
+        assert variant(binding.OP_FULL_BWD, L, 1, 100, d, H=H) == "full_bwd_one", (L, d, H)
+    assert variant(binding.OP_FULL_BWD, 32, 1, 100, 2048, H=8) == "full_bwd_res"
+    assert variant(binding.OP_FULL_BWD, 55, 1, 100, 4096, H=2) == "full_bwd_generic"
     assert variant(binding.OP_FULL_BWD, 32, 2, 100, 2048) == "full_bwd_res"
     assert variant(binding.OP_FULL_BWD, 32, 1, 100, 2048, dtype=F32) == "full_bwd_generic"
     assert variant(binding.OP_FULL_BWD, 33, 33, 100, 2048) == "full_bwd_generic"
-    assert variant(binding.OP_FULL_BWD, 55, 1, 100, 2048, H=2) == "full_bwd_generic"
+    assert variant(binding.OP_FULL_BWD, 55, 2, 100, 2048, H=2) == "full_bwd_generic"
     assert variant(binding.OP_FULL_BWD, 55, 1, 100, 768) == "full_bwd_generic"
     # heads on the resident kernel: runs of whole 256-channel waves
     assert variant(binding.OP_FULL_BWD, 32, 32, 100, 2048, H=8) == "full_bwd_res"

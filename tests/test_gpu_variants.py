@@ -195,6 +195,11 @@ FULL_BWD_CASES = [
     (1200, 1024, 64, 1, "shared", "full_bwd_one"),
     (333, 512, 33, 1, "per", "full_bwd_one"),
     (1030, 2048, 47, 1, "none", "full_bwd_one"),
+    # ... with heads of whole waves
+    (1000, 4096, 32, 1, "per", "full_bwd_one", 8),
+    (600, 2048, 55, 1, "shared", "full_bwd_one", 8),
+    (333, 2048, 20, 1, "none", "full_bwd_one", 4),
+    (1, 4096, 9, 1, "per", "full_bwd_one", 2),
 ]
 
 
@@ -252,6 +257,11 @@ FULL_FWD_HEAD_CASES = [
     (1, 512, 32, 1, 8, "shared"),
     (333, 512, 20, 13, 2, "per"),
     (7, 1024, 1, 1, 4, "none"),
+    # one destination with heads of whole 512-channel waves: the vector kernel
+    (1500, 4096, 32, 1, 8, "per"),
+    (700, 2048, 55, 1, 4, "shared"),
+    (300, 2048, 20, 1, 2, "none"),
+    (1, 4096, 64, 1, 8, "per"),
 ]
 
 
@@ -259,7 +269,7 @@ FULL_FWD_HEAD_CASES = [
 def test_full_fwd_heads(T, d, L, n_dst, H, gain):
     name = ar.attnres_kernel_variant(ar.OP_FULL_FWD, L, n_dst, T, d, H)
     say(f"full fwd heads T={T} d={d} L={L} n_dst={n_dst} H={H} gain={gain}: {name}")
-    assert name == "full_fast", name
+    assert name == ("full_one" if n_dst == 1 and (d // H) % 512 == 0 else "full_fast"), name
     wl = synth.full_workload(T=T, d=d, L=L, std_step=0.2, dtype="bf16", seed=120 + H + L, gain_variance=0.02,
                              n_dst=n_dst)
     g = _gain_arg(wl, gain, n_dst, d)
