@@ -32,6 +32,7 @@
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "row_piece.hpp"
 #include "xlane.hpp"
 
 namespace attnres {
@@ -41,64 +42,6 @@ constexpr int kBMaxW = 8;     // waves per workgroup at most
 constexpr int kBSlabs = 1024; // workgroups (and Z slabs) at most
 constexpr int kBRing = 8;     // accumulate: old d_src rows in flight ahead of their use
 constexpr int kAll = 0x7fffffff;
-
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-// One thread's C channels of a bf16 row: 16 bytes (C = 8, a uint4) or 8
-// bytes (C = 4, a uint2), through a buffer descriptor of `records` bytes
-// (zero: nothing is read or written, and a load returns zeros).
-template <int C> struct PieceOf { typedef uint4 type; };
-template <> struct PieceOf<4> { typedef uint2 type; };
-
-template <int C>
-__device__ __forceinline__ typename PieceOf<C>::type piece_ld(const void* row, uint32_t off, int records) {
-  if constexpr (C == 8) {
-    return ld16_rec(row, off, records);
-  } else {
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row), 0, records, kBufferWord3);
-    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kBufferNt);
-    return make_uint2(v.x, v.y);
-  }
-}
-
-__device__ __forceinline__ void piece_st(void* row, uint32_t off, int records, const float (&x)[8]) {
-  st16_rec(row, off, records,
-           make_uint4(pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3]), pack_bf2(x[4], x[5]), pack_bf2(x[6], x[7])));
-}
-__device__ __forceinline__ void piece_st(void* row, uint32_t off, int records, const float (&x)[4]) {
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(row, 0, records, kBufferWord3);
-  __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3])}, r, (int)off, 0, kBufferNt);
-}
-
-__device__ __forceinline__ void piece_unpack(const uint4 u, float (&x)[8]) { unpack_bf8(u, x); }
-__device__ __forceinline__ void piece_unpack(const uint2 u, float (&x)[4]) {
-  x[0] = bf_lo(u.x); x[1] = bf_hi(u.x);
-  x[2] = bf_lo(u.y); x[3] = bf_hi(u.y);
-}
-
-// An opaque copy: the compiler cannot reuse an earlier unpacking of it.
-__device__ __forceinline__ uint4 piece_opaque(uint4 u) {
-  asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
-  return u;
-}
-__device__ __forceinline__ uint2 piece_opaque(uint2 u) {
-  asm volatile("" : "+v"(u.x), "+v"(u.y));
-  return u;
-}
-
-// q = w * g (or w) for C consecutive channels.
-template <int C>
-__device__ __forceinline__ void fold_q(const float* w, const float* g, float (&q)[C]) {
-#pragma unroll
-  for (int k = 0; k < C; k += 4) {
-    const float4 wv = *reinterpret_cast<const float4*>(w + k);
-    q[k] = wv.x; q[k + 1] = wv.y; q[k + 2] = wv.z; q[k + 3] = wv.w;
-    if (g != nullptr) {
-      const float4 gv = *reinterpret_cast<const float4*>(g + k);
-      q[k] *= gv.x; q[k + 1] *= gv.y; q[k + 2] *= gv.z; q[k + 3] *= gv.w;
-    }
-  }
-}
 
 template <bool ACC, int R, bool MH>
 __global__ __launch_bounds__(512, 2) void k_full_bwd_one(FullBwdArgs a, float* zs) {

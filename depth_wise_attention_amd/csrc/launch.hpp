@@ -201,8 +201,8 @@ hipError_t launch_phase2_fast(const Phase2Args& a, hipStream_t st);
 hipError_t launch_bwd_fast(const BwdArgs& a, int64_t* slots_used, hipStream_t st);
 hipError_t launch_full_fast(const FullArgs& a, hipStream_t st);
 // Name of the specialised Full forward kernel a call runs ("full_one" for one
-// destination and one head over up to 64 sources with d <= 4096, else
-// "full_fast" for up to 32 sources and "full_wide" for 33 .. 64); only
+// destination over up to 64 sources with d <= 4096 and heads of whole waves,
+// else "full_fast" for up to 32 sources and "full_wide" for 33 .. 64); only
 // meaningful when full_fast_ok.
 const char* full_fast_variant(const FullArgs& a);
 // Matrix-core Full forward over 33 .. 64 sources (full_wide.hip): the shapes

@@ -104,8 +104,8 @@ int attnres_full_fwd(const void* src, int64_t n_src, int64_t T, int64_t d,
  * So may one-head bf16 calls with 33 .. 64 sources and d a multiple of 512:
  * [2, 32, d] for n_dst <= 32, [2, 64, d] (256 * d bytes) above.  Every other
  * request needs none and gets 0.  (One destination over up to 64 sources
- * with d <= 4096, and H = 1, 2, 4 or 8 with d / H a multiple of 512, runs a
- * vector kernel that ignores the workspace; the
+ * with d <= 4096, and H = 1, 2, 4 or 8 with d / H a multiple of 512 (or of
+ * 256 with d <= 2048), runs a vector kernel that ignores the workspace; the
  * size returned still covers the matrix-core kernels, so a caller need not
  * know which runs.)
  */

@@ -103,8 +103,12 @@ def test_phase2_full_and_policy():
     # ... and with heads of whole 512-channel waves (d / H a multiple of 512)
     for L, d, H in ((32, 2048, 2), (32, 4096, 8), (55, 4096, 4), (9, 1024, 2)):
         assert variant(binding.OP_FULL_FWD, L, 1, 100, d, H=H) == "full_one", (L, d, H)
-    assert variant(binding.OP_FULL_FWD, 32, 1, 100, 2048, H=8) == "full_fast"
-    assert variant(binding.OP_FULL_FWD, 55, 1, 100, 2048, H=8) == "full_generic"
+    # ... or of whole 256-channel waves (4 channels per thread) with d <= 2048
+    for L, d, H in ((32, 2048, 8), (55, 2048, 8), (64, 1024, 4), (1, 512, 2)):
+        assert variant(binding.OP_FULL_FWD, L, 1, 100, d, H=H) == "full_one", (L, d, H)
+    assert variant(binding.OP_FULL_FWD, 32, 1, 100, 1024, H=8) == "full_fast"
+    assert variant(binding.OP_FULL_FWD, 55, 1, 100, 1024, H=8) == "full_generic"
+    assert variant(binding.OP_FULL_FWD, 55, 1, 100, 4096, H=16) == "full_generic"
     assert variant(binding.OP_FULL_FWD, 32, 1, 100, 2048, dtype=F32) == "full_generic"
     assert variant(binding.OP_FULL_FWD, 55, 54, 100, 2048, H=8) == "full_generic"
     assert variant(binding.OP_FULL_FWD, 55, 54, 100, 768) == "full_generic"
