@@ -124,8 +124,6 @@ __global__ __launch_bounds__(256, ATTNRES_P2_MINWAVES) void k_phase2_fast(Phase2
   const int64_t T = a.T;
   const int segs_per_head = (d / a.H) / 512;
   constexpr int QR = kP2QLds ? 1 : CPL;
-  // The first token's loads go out before the fold of q, so that at small T
-  // (one token per wave) the two memory latencies overlap.
   // With UPD == 2 the partial loads read f itself.
   const bf16_t* part = static_cast<const bf16_t*>(UPD == 2 ? a.f : a.partial);
   const bf16_t* fin = static_cast<const bf16_t*>(a.f);
@@ -143,26 +141,54 @@ __global__ __launch_bounds__(256, ATTNRES_P2_MINWAVES) void k_phase2_fast(Phase2
       for (int c = 0; c < CPL; ++c) fv[c] = ld16<kP2Nt>(fin + tt * d + (c * 64 + lane) * 8);
     }
   };
-  if (t < T) {
-    load_p2<CPL, OT>(p, o, part, oin, t, d, lane);
-    load_f(t);
+  // The token's Phase 1 lse (per chunk's head) and state scale, loaded with
+  // its rows: read where they are used, they would add a memory round trip
+  // after the dot products.
+  float lse_t[MH ? CPL : 1], osc_t = 1.0f;
+  auto load_s = [&](int64_t tt) {
+#pragma unroll
+    for (int c = 0; c < (MH ? CPL : 1); ++c) lse_t[c] = a.lse[(int64_t)(MH ? c / segs_per_head : 0) * T + tt];
+    if constexpr (__is_same(OT, f16_t)) osc_t = a.oscale[tt];
+  };
+  // q = w * g, one copy per workgroup in LDS (every wave uses the same lane ->
+  // channel map).  Its loads go out first, unconditionally (w again when there
+  // is no gain), and the first token's after them: the in-order load counter
+  // then lets the fold finish while the token's loads are still in flight,
+  // which is most of a call's time when T is small.  256 threads cover the
+  // d / 4 = 128 CPL float4 of q in CPL / 2 each.
+  constexpr int FQ = kP2QLds ? CPL / 2 : 1;
+  float4 wq[FQ], gq[FQ];
+  const bool has_gain = a.gain != nullptr;
+  if constexpr (kP2QLds) {
+    const float4* w4 = reinterpret_cast<const float4*>(a.w);
+    const float4* g4 = reinterpret_cast<const float4*>(has_gain ? a.gain : a.w);
+#pragma unroll
+    for (int j = 0; j < FQ; ++j) {
+      wq[j] = w4[threadIdx.x + j * 256];
+      gq[j] = g4[threadIdx.x + j * 256];
+    }
+    keep_memory_order();  // the token's loads below go out after these
+  }
+  {
+    // Unconditional (a wave past the last token loads that token's rows and
+    // never uses them): a branch here would make the fold below wait for
+    // these loads too.
+    const int64_t t0 = t < T ? t : T - 1;
+    load_p2<CPL, OT>(p, o, part, oin, t0, d, lane);
+    load_f(t0);
+    load_s(t0);
   }
   __shared__ float4 qs[kP2QLds ? CPL * 64 * 2 : 1];
   float qreg[QR][8];
   if constexpr (kP2QLds) {
-    // Every wave uses the same lane -> channel map, so the block shares one copy.
-    // One branch on the gain outside the loop: loads in the loop are unconditional.
-    const float4* w4 = reinterpret_cast<const float4*>(a.w);
-    const float4* g4 = reinterpret_cast<const float4*>(a.gain);
-    if (a.gain != nullptr) {
-      for (int k = threadIdx.x; k < d / 4; k += blockDim.x) {
-        float4 q = w4[k];
-        const float4 g = g4[k];
-        q.x *= g.x; q.y *= g.y; q.z *= g.z; q.w *= g.w;
-        qs[k] = q;
-      }
-    } else {
-      for (int k = threadIdx.x; k < d / 4; k += blockDim.x) qs[k] = w4[k];
+#pragma unroll
+    for (int j = 0; j < FQ; ++j) {
+      float4 q = wq[j];
+      q.x *= has_gain ? gq[j].x : 1.0f;
+      q.y *= has_gain ? gq[j].y : 1.0f;
+      q.z *= has_gain ? gq[j].z : 1.0f;
+      q.w *= has_gain ? gq[j].w : 1.0f;
+      qs[threadIdx.x + j * 256] = q;
     }
     lds_barrier();  // orders the LDS copy only: the token's loads stay in flight
   } else {
@@ -225,7 +251,7 @@ __global__ __launch_bounds__(256, ATTNRES_P2_MINWAVES) void k_phase2_fast(Phase2
 
     // Merge weights per head: ca = e^{lse-m}/(..), cb = e^{s_p-m}/(..).
     float ca[MH ? CPL : 1], cb[MH ? CPL : 1];
-    const float oscale = __is_same(OT, f16_t) ? a.oscale[t] : 1.0f;
+    const float oscale = osc_t;
 #pragma unroll
     for (int c = 0; c < (MH ? CPL : 1); ++c) {
       const int head = MH ? c / segs_per_head : 0;
@@ -238,7 +264,7 @@ __global__ __launch_bounds__(256, ATTNRES_P2_MINWAVES) void k_phase2_fast(Phase2
         dh = dot[0];
       }
       const float s_p = r * dh;
-      const float L = a.lse[head * T + t];
+      const float L = lse_t[MH ? c : 0];
       const float m = fmaxf(L, s_p);
       const float wa = expf(L - m), wb = expf(s_p - m);
       const float inv = 1.0f / (wa + wb);
@@ -276,10 +302,12 @@ __global__ __launch_bounds__(256, ATTNRES_P2_MINWAVES) void k_phase2_fast(Phase2
 #pragma unroll
         for (int k = 0; k < OW; ++k) o[c][k] = on[c][k];
       }
+      if (tn < T) load_s(tn);
     } else {
       if (tn < T) {
         load_p2<CPL, OT>(p, o, part, oin, tn, d, lane);
         load_f(tn);
+        load_s(tn);
       }
     }
   }

@@ -172,7 +172,9 @@ __device__ __forceinline__ void p1_body(const Phase1Args& a, float4* smem) {
   constexpr int R = (TAB + 63) / 64;         // rounds of 64 lanes
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const int B = blockDim.x, W = B >> 6;
+  // d = 8 CH B: the block size from a kernel argument (blockDim.x is read
+  // from memory, a round trip at the start of every launch).
+  const int B = (int)a.d / (8 * CH), W = B >> 6;
   const int d = (int)a.d;
   const int64_t T = a.T;
   const int segs_per_head = (d / a.H) / 512;  // 512-channel segments per head
@@ -358,9 +360,9 @@ template <int N, int S, int CH, bool MH>
 __global__ __launch_bounds__(512, 2) void k_p1(Phase1Args a) {
   extern __shared__ float4 p1_smem[];
   if (a.gain != nullptr)
-    p1_fold<S, CH, true>(a.w, a.gain, a.gain_ld, (int)a.d, (int)blockDim.x, (int)threadIdx.x, p1_smem);
+    p1_fold<S, CH, true>(a.w, a.gain, a.gain_ld, (int)a.d, (int)a.d / (8 * CH), (int)threadIdx.x, p1_smem);
   else
-    p1_fold<S, CH, false>(a.w, a.gain, a.gain_ld, (int)a.d, (int)blockDim.x, (int)threadIdx.x, p1_smem);
+    p1_fold<S, CH, false>(a.w, a.gain, a.gain_ld, (int)a.d, (int)a.d / (8 * CH), (int)threadIdx.x, p1_smem);
   p1_body<N, S, CH, MH>(a, p1_smem);
 }
 

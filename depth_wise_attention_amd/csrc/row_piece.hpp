@@ -9,6 +9,29 @@
 
 namespace attnres {
 
+// 16 bytes at byte offset `off` of a row through a buffer descriptor of
+// `records` bytes (nontemporal).  With zero records the load reads nothing and
+// returns zeros, and the store writes nothing: a row that does not exist
+// costs no memory traffic and no branch.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_rec(const void* row, uint32_t off, int records = 0x7fffffff) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row), 0, records, kBufferWord3);
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kBufferNt);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st16_rec(void* row, uint32_t off, int records, const uint4 v) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(row, 0, records, kBufferWord3);
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, r, (int)off, 0, kBufferNt);
+}
+
+// Eight bf16 (one 16-byte piece) as fp32.
+__device__ __forceinline__ void unpack_bf8(const uint4 u, float (&x)[8]) {
+  x[0] = bf_lo(u.x); x[1] = bf_hi(u.x);
+  x[2] = bf_lo(u.y); x[3] = bf_hi(u.y);
+  x[4] = bf_lo(u.z); x[5] = bf_hi(u.z);
+  x[6] = bf_lo(u.w); x[7] = bf_hi(u.w);
+}
+
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // One thread's C channels of a bf16 row: 16 bytes (C = 8, a uint4) or 8
