@@ -211,6 +211,30 @@ def _gain_arg(wl, gain, n_dst, d):
     return wl.gain
 
 
+@pytest.mark.parametrize("L,d,gain,H", [(9, 1024, "shared", 1), (32, 2048, "per", 1), (47, 1024, "shared", 1),
+                                          (20, 2048, "shared", 4)])
+def test_full_bwd_one_accumulates_parameter_grads(L, d, gain, H):
+    """One destination: dw and dgain (shared or per destination) are added to
+    the given values, d_src too, each against the oracle."""
+    T = 700
+    name = ar.attnres_kernel_variant(ar.OP_FULL_BWD, L, 1, T, d, H)
+    say(f"full bwd one accumulate T={T} d={d} L={L} gain={gain} H={H}: {name}")
+    assert name == "full_bwd_one", name
+    wl = synth.full_workload(T=T, d=d, L=L, std_step=0.2, dtype="bf16", seed=300 + L, gain_variance=0.02, n_dst=1,
+                             with_dout=True)
+    g = _gain_arg(wl, gain, 1, d)
+    ref = orc.full_bwd(wl.src, wl.w, g, wl.eps, H, wl.dh)
+    rng = np.random.default_rng(L)
+    base = [synth.bf16_round(rng.standard_normal(wl.src.shape).astype(np.float32)),
+            rng.standard_normal(wl.w.shape).astype(np.float32), rng.standard_normal(g.shape).astype(np.float32)]
+    outs = [dev(base[0], True), dev(base[1]), dev(base[2])]
+    ar.attnres_full_bwd(dev(wl.src, True), dev(wl.w), dev(wl.dh, True), dev(g), wl.eps, H, d_src=outs[0],
+                        dw=outs[1], dgain=outs[2], accumulate=True)
+    check(host(outs[0]), base[0] + ref[0], "bf16", "d_src accumulated")
+    check(host(outs[1]), base[1] + ref[1], "f32_from_bf16", "dw accumulated")
+    check(host(outs[2]), base[2] + ref[2], "f32_from_bf16", "dgain accumulated")
+
+
 @pytest.mark.parametrize("case", FULL_BWD_CASES, ids=lambda c: "-".join(map(str, c)))
 def test_full_bwd_variant(case):
     T, d, L, n_dst, gain, kernel = case[:6]
