@@ -15,8 +15,9 @@
 //
 // One workgroup of d / C threads owns one token at a time; thread tid owns
 // channels C tid .. C tid + C - 1.  All R = 256 / C source rows of the token
-// sit in registers (R = 32 rows of 8 channels, or 64 rows of 4 channels for
-// 33 .. 64 sources; one register quad per row either way).  A row past n_src
+// sit in registers (R = 32 rows of 8 channels, four registers a row, or 64
+// rows of 4 channels, two a row, for 33 .. 64 sources: 128 registers either
+// way).  A row past n_src
 // has a zero-record descriptor, so it is never read and its gradient never
 // written:
 //   1. per row, the sum of squares, q . v and dout . v over the thread's

@@ -9,7 +9,8 @@
 //
 // One workgroup of d / C threads owns one token at a time; thread tid owns
 // channels C tid .. C tid + C - 1.  The sources are taken in NT register
-// tiles of R = 256 / C rows (one register quad per row): one 32-row tile of 8
+// tiles of R = 256 / C rows (128 registers a tile: four a row at C = 8, two at
+// C = 4): one 32-row tile of 8
 // channels for up to 32 sources, one 64-row tile of 4 channels for 33 .. 64
 // with d <= 2048, two 32-row tiles of 8 channels for 33 .. 64 above.  A row
 // past n_src is loaded with a zero-record descriptor, which reads nothing and
@@ -44,7 +45,7 @@ constexpr bool kOneRows64 = false;
 
 template <int NT, int C>
 __global__ __launch_bounds__(512, 2) void k_full_one(FullArgs a) {
-  constexpr int R = 256 / C;  // rows per register tile (one register quad per row)
+  constexpr int R = 256 / C;  // rows per register tile (128 registers)
   typedef typename PieceOf<C>::type P;
   __shared__ float red[2][kOMaxW][2 * R];  // per buffer and wave: R sums of squares, then R dot products
   const int tid = threadIdx.x, lane = lane_id();
