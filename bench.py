@@ -10,7 +10,7 @@ in HBM before timing starts.
 Prints ONE JSON line on stdout.  Everything else goes to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                  [--no-extra] [--workload block|mhar|full|full_h8|full_wide|full_one|bwd|full_bwd|full_bwd_h8|block_update|decode|msar|block_msar]
+                  [--no-extra] [--workload block|mhar|full|full_h8|full_wide|full_one|f32|bwd|full_bwd|full_bwd_h8|block_update|decode|msar|block_msar]
                   [--copy-calibration]
 """
 
@@ -44,7 +44,7 @@ def parse():
     # warm-up steps, Phase 1 measured 314-323 us, from 50 or 200, 298-300 us.
     p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--workload", default="block", choices=["block", "mhar", "full", "full_h8", "full_wide", "bwd", "mhar_bwd", "full_bwd", "full_bwd_h8", "block_update",
-                                                                "decode", "msar", "block_msar", "depth_sweep", "full_one"])
+                                                                "decode", "msar", "block_msar", "depth_sweep", "full_one", "f32"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     p.add_argument("--ceilings", action="store_true",
@@ -589,6 +589,49 @@ def bench_full_one(args, T=4096, d=2048, Ls=(9, 32, 55)):
     return dict(name=f"full_one_bf16_T{T}_d{d}", **cases)
 
 
+def bench_f32(args):
+    """fp32 I/O, which runs the general kernels at every shape: the headline
+    block step (mhar_fwd, T=16384, d=4096, N=8, S=4), the Full forward over 32
+    sources and destinations (T=4096, d=2048) and the one-destination Full
+    call over 32 sources, each timed with HIP events over 3 calls after one
+    warm-up call, on seeded normal inputs made on the device."""
+    import torch
+    import depth_wise_attention_amd as ar
+
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n=3):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    out = {}
+    T, d, N, S = 16384, 4096, 8, 4
+    reps = torch.randn((N, T, d), generator=gen, device="cuda")
+    parts = torch.randn((S - 1, T, d), generator=gen, device="cuda")
+    w = torch.randn((S, d), generator=gen, device="cuda") / d ** 0.5
+    g = 1 + 0.1 * torch.randn((S, d), generator=gen, device="cuda")
+    out["block_T16384_d4096_N8_S4_ms"] = timed(lambda: ar.mhar_fwd(reps, parts, w, g, 1e-6, 1))
+    out["block_kernel"] = ar.attnres_kernel_variant(ar.OP_PHASE1, N, S, T, d, 1, dtype=ar.F32, o_dtype=ar.F32)
+    del reps, parts
+    Tf, df, L = 4096, 2048, 32
+    src = torch.randn((L, Tf, df), generator=gen, device="cuda")
+    wf = torch.randn((L, df), generator=gen, device="cuda") / df ** 0.5
+    out["full_T4096_d2048_L32_ms"] = timed(lambda: ar.attnres_full_fwd(src, wf, None, 1e-6, 1))
+    w1 = wf[:1].contiguous()
+    out["full_one_destination_T4096_d2048_L32_ms"] = timed(lambda: ar.attnres_full_fwd(src, w1, None, 1e-6, 1))
+    out["full_kernel"] = ar.attnres_kernel_variant(ar.OP_FULL_FWD, L, L, Tf, df, 1, dtype=ar.F32)
+    return dict(name="f32_io_general_kernels", **out)
+
+
 def bench_bwd(args, T=8192, H=1):
     import torch
     import depth_wise_attention_amd as ar
@@ -917,7 +960,7 @@ def main():
               "block_update": lambda: bench_update(args), "decode": lambda: bench_decode(args),
               "msar": lambda: bench_msar(args), "block_msar": lambda: bench_block_msar(args),
               "depth_sweep": lambda: bench_depth_sweep(args), "full_wide": lambda: bench_full_wide(args),
-              "full_one": lambda: bench_full_one(args)}[args.workload]
+              "full_one": lambda: bench_full_one(args), "f32": lambda: bench_f32(args)}[args.workload]
         log(json.dumps(fn()))
         return
 
