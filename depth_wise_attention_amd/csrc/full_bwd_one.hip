@@ -14,10 +14,10 @@
 // and reads each source row and the token's dout row once.
 //
 // One workgroup of d / C threads owns one token at a time; thread tid owns
-// channels C tid .. C tid + C - 1.  All R = 256 / C source rows of the token
-// sit in registers (R = 32 rows of 8 channels, four registers a row, or 64
-// rows of 4 channels, two a row, for 33 .. 64 sources: 128 registers either
-// way).  A row past n_src
+// channels C tid .. C tid + C - 1.  All R source rows of the token sit in
+// registers: R = 16 or 32 rows of 8 channels (four registers a row) for up to
+// 16 or 32 sources, or 64 rows of 4 channels (two a row) for 33 .. 64.  A row
+// past n_src
 // has a zero-record descriptor, so it is never read and its gradient never
 // written:
 //   1. per row, the sum of squares, q . v and dout . v over the thread's
@@ -46,7 +46,7 @@ constexpr int kAll = 0x7fffffff;
 
 template <bool ACC, int R, bool MH>
 __global__ __launch_bounds__(512, 2) void k_full_bwd_one(FullBwdArgs a, float* zs) {
-  constexpr int C = 256 / R;  // channels per thread
+  constexpr int C = R == 64 ? 4 : 8;  // channels per thread
   typedef typename PieceOf<C>::type P;
   __shared__ float red[2][kBMaxW][3 * R];  // per buffer and wave: sums of squares, q . v, dout . v
   __shared__ float dsp[MH ? 2 : 1][MH ? kBMaxW : 1][R];  // heads: ds p per head and row
@@ -121,15 +121,19 @@ __global__ __launch_bounds__(512, 2) void k_full_bwd_one(FullBwdArgs a, float* z
       const float tot = transpose_reduce_pow2<32>(part);
       if ((rl & 1) == 0) red[buf][wave][pv < 16 ? 16 * h + pv : R + 16 * h + (pv - 16)] = tot;
     }
-    // ... and dout . v, 32 rows at a time
+    // ... and dout . v, 32 rows at a time (a 16-row tile pads with zeros)
     {
       float g[C];
       piece_unpack(go, g);
 #pragma unroll
-      for (int h = 0; h < R / 32; ++h) {
+      for (int h = 0; h < (R + 31) / 32; ++h) {
         float part[32];
 #pragma unroll
         for (int k = 0; k < 32; ++k) {
+          if (32 * h + k >= R) {
+            part[k] = 0.f;
+            continue;
+          }
           // Unpack afresh: sharing the unpacked rows with the pass above
           // would keep 256 floats live between the two.
           float x[C];
@@ -140,7 +144,7 @@ __global__ __launch_bounds__(512, 2) void k_full_bwd_one(FullBwdArgs a, float* z
           part[k] = da;
         }
         const float tot = transpose_reduce_pow2<32>(part);
-        if ((rl & 1) == 0) red[buf][wave][2 * R + 32 * h + pv] = tot;
+        if ((rl & 1) == 0 && 32 * h + pv < R) red[buf][wave][2 * R + 32 * h + pv] = tot;
       }
     }
     // With accumulate, the first old d_src rows are read while the waves meet.
@@ -225,13 +229,14 @@ __global__ __launch_bounds__(512, 2) void k_full_bwd_one(FullBwdArgs a, float* z
                         __float_as_uint(z[k + 3])));
 }
 
-// Rows held per thread: 32 (8 channels, d up to 4096) for up to 32 sources,
-// 64 (4 channels, d up to 2048) for 33 .. 64.
-int one_rows(int64_t n_src) { return n_src > 32 ? 64 : 32; }
+// Rows held per thread: 16 (8 channels, half the registers, so more tokens
+// in flight per CU) for up to 16 sources, 32 (8 channels) for up to 32, both
+// with d up to 4096; 64 (4 channels, d up to 2048) for 33 .. 64.
+int one_rows(int64_t n_src) { return n_src > 32 ? 64 : (n_src > 16 ? 32 : 16); }
 
 bool one_shape(int64_t n_src, int64_t n_dst, int64_t d, int H) {
   if (n_dst != 1 || n_src < 1 || n_src > 64 || d < 512 || d % 512 != 0) return false;
-  const int64_t wave_ch = (int64_t)(256 / one_rows(n_src)) * 64;  // channels per wave
+  const int64_t wave_ch = (one_rows(n_src) == 64 ? 4 : 8) * 64;  // channels per wave
   if (d > wave_ch * kBMaxW) return false;
   // Heads of whole waves.
   return H == 1 || ((H == 2 || H == 4 || H == 8) && (d / H) % wave_ch == 0);
@@ -241,7 +246,7 @@ int64_t one_slabs(int64_t T) { return T < kBSlabs ? T : kBSlabs; }
 
 template <int R>
 hipError_t launch_rows(const FullBwdArgs& a, const float** slabs, int64_t* n_slabs, hipStream_t st) {
-  const int B = (int)(a.d / (256 / R));
+  const int B = (int)(a.d / (R == 64 ? 4 : 8));
   auto kern = a.H > 1 ? (a.accumulate ? k_full_bwd_one<true, R, true> : k_full_bwd_one<false, R, true>)
                       : (a.accumulate ? k_full_bwd_one<true, R, false> : k_full_bwd_one<false, R, false>);
   int per_cu = 0;
@@ -269,7 +274,11 @@ bool full_bwd_one_ok(const FullBwdArgs& a) {
 }
 
 hipError_t launch_full_bwd_one(const FullBwdArgs& a, const float** slabs, int64_t* n_slabs, hipStream_t st) {
-  return one_rows(a.n_src) == 64 ? launch_rows<64>(a, slabs, n_slabs, st) : launch_rows<32>(a, slabs, n_slabs, st);
+  switch (one_rows(a.n_src)) {
+    case 16: return launch_rows<16>(a, slabs, n_slabs, st);
+    case 32: return launch_rows<32>(a, slabs, n_slabs, st);
+    default: return launch_rows<64>(a, slabs, n_slabs, st);
+  }
 }
 
 }  // namespace attnres

@@ -9,8 +9,8 @@
 //
 // One workgroup of d / C threads owns one token at a time; thread tid owns
 // channels C tid .. C tid + C - 1.  The sources are taken in NT register
-// tiles of R = 256 / C rows (128 registers a tile: four a row at C = 8, two at
-// C = 4): one 32-row tile of 8
+// tiles of R rows (four registers a row at C = 8, two at C = 4): one 16-row
+// tile of 8 channels for up to 16 sources, one 32-row tile of 8
 // channels for up to 32 sources, one 64-row tile of 4 channels for 33 .. 64
 // with d <= 2048, two 32-row tiles of 8 channels for 33 .. 64 above.  A row
 // past n_src is loaded with a zero-record descriptor, which reads nothing and
@@ -43,9 +43,11 @@ constexpr int kOMaxW = 8;    // waves per workgroup at most
 // so the 64-row tile is kept for heads of 256 channels.
 constexpr bool kOneRows64 = false;
 
-template <int NT, int C>
+template <int NT, int C, int R>
 __global__ __launch_bounds__(512, 2) void k_full_one(FullArgs a) {
-  constexpr int R = 256 / C;  // rows per register tile (128 registers)
+  // R rows per register tile: R C / 2 registers (128 for the full tiles, 64
+  // for the 16-row tile of shallow calls, which leaves room for more tokens
+  // in flight per CU).
   typedef typename PieceOf<C>::type P;
   __shared__ float red[2][kOMaxW][2 * R];  // per buffer and wave: R sums of squares, then R dot products
   const int tid = threadIdx.x, lane = lane_id();
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(512, 2) void k_full_one(FullArgs a) {
       if ((rl & 1) == 0) red[buf][wave][pv < 16 ? 16 * h + pv : R + 16 * h + (pv - 16)] = tot;
     }
     lds_barrier();
-    const int li = rl & (R - 1);  // row li on lane li (and li + 32 when R = 32)
+    const int li = rl & (R - 1);  // row li on lanes li, li + R, ...
     // The sum of squares is over every wave (the whole d), the dot product
     // over the waves of this wave's head (H heads of W / H whole waves).
     float ss = 0.f, dt = 0.f;
@@ -172,21 +174,23 @@ __global__ __launch_bounds__(512, 2) void k_full_one(FullArgs a) {
   }
 }
 
-// The kernel a call runs, as (tiles, channels per thread): 32-row tiles of 8
-// channels need heads of whole 512-channel waves and d <= 4096; 64-row tiles
-// of 4 channels take up to 64 sources in one tile, heads of whole 256-channel
-// waves and d <= 2048.  {0, 0}: none.
+// The kernel a call runs, as (tiles, channels per thread, rows per tile):
+// tiles of 8 channels (16 rows for up to 16 sources, else 32) need heads of
+// whole 512-channel waves and d <= 4096; 64-row tiles of 4 channels take up to
+// 64 sources in one tile, heads of whole 256-channel waves and d <= 2048.
+// {0, 0, 0}: none.
 struct OnePick {
-  int nt, c;
+  int nt, c, r;
 };
 OnePick one_pick(const FullArgs& a) {
-  if (!(a.H == 1 || a.H == 2 || a.H == 4 || a.H == 8) || a.d < 512 || a.d % 512 != 0) return {0, 0};
-  if (a.n_src < 1 || a.n_src > 64) return {0, 0};
+  if (!(a.H == 1 || a.H == 2 || a.H == 4 || a.H == 8) || a.d < 512 || a.d % 512 != 0) return {0, 0, 0};
+  if (a.n_src < 1 || a.n_src > 64) return {0, 0, 0};
   const bool c8 = (a.d / a.H) % 512 == 0 && a.d <= 8 * 64 * kOMaxW;
   const bool c4 = (a.d / a.H) % 256 == 0 && a.d <= 4 * 64 * kOMaxW;
-  if (a.n_src <= 32) return c8 ? OnePick{1, 8} : (c4 ? OnePick{1, 4} : OnePick{0, 0});
-  if (c4 && (kOneRows64 || !c8)) return {1, 4};
-  return c8 ? OnePick{2, 8} : OnePick{0, 0};
+  if (a.n_src <= 16 && c8) return {1, 8, 16};
+  if (a.n_src <= 32) return c8 ? OnePick{1, 8, 32} : (c4 ? OnePick{1, 4, 64} : OnePick{0, 0, 0});
+  if (c4 && (kOneRows64 || !c8)) return {1, 4, 64};
+  return c8 ? OnePick{2, 8, 32} : OnePick{0, 0, 0};
 }
 
 }  // namespace
@@ -198,23 +202,24 @@ bool full_one_ok(const FullArgs& a) {
 }
 
 namespace {
-template <int NT, int C>
+template <int NT, int C, int R>
 hipError_t launch_one(const FullArgs& a, hipStream_t st) {
   const int B = (int)(a.d / C);
   int per_cu = 0;
-  const hipError_t e = blocks_per_cu(reinterpret_cast<const void*>(k_full_one<NT, C>), B, &per_cu);
+  const hipError_t e = blocks_per_cu(reinterpret_cast<const void*>(k_full_one<NT, C, R>), B, &per_cu);
   if (e != hipSuccess) return e;
   int64_t grid = (int64_t)num_cus() * (per_cu < 1 ? 1 : per_cu);
   if (grid > a.T) grid = a.T;
-  hipLaunchKernelGGL((k_full_one<NT, C>), dim3((unsigned)grid), dim3((unsigned)B), 0, st, a);
+  hipLaunchKernelGGL((k_full_one<NT, C, R>), dim3((unsigned)grid), dim3((unsigned)B), 0, st, a);
   return hipGetLastError();
 }
 }  // namespace
 
 hipError_t launch_full_one(const FullArgs& a, hipStream_t st) {
   const OnePick p = one_pick(a);
-  if (p.c == 4) return launch_one<1, 4>(a, st);
-  return p.nt == 2 ? launch_one<2, 8>(a, st) : launch_one<1, 8>(a, st);
+  if (p.c == 4) return launch_one<1, 4, 64>(a, st);
+  if (p.r == 16) return launch_one<1, 8, 16>(a, st);
+  return p.nt == 2 ? launch_one<2, 8, 32>(a, st) : launch_one<1, 8, 32>(a, st);
 }
 
 }  // namespace attnres

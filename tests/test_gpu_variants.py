@@ -191,6 +191,8 @@ FULL_BWD_CASES = [
     (777, 1024, 17, 1, "per", "full_bwd_one"),
     (1500, 3072, 5, 1, "shared", "full_bwd_one"),
     (600, 2048, 1, 1, "per", "full_bwd_one"),
+    (2100, 2048, 16, 1, "shared", "full_bwd_one"),
+    (900, 4096, 12, 1, "per", "full_bwd_one"),
     # 33 .. 64 sources: 64 rows of 4 channels per thread (d <= 2048)
     (1200, 1024, 64, 1, "shared", "full_bwd_one"),
     (333, 512, 33, 1, "per", "full_bwd_one"),
@@ -330,6 +332,10 @@ FULL_WIDE_CASES = [
     (777, 512, 33, 1, "shared"),
     (1025, 1024, 48, 1, "none"),
     (64, 8192, 40, 1, "per"),
+    # up to 16 sources: the 16-row tile
+    (2500, 2048, 16, 1, "per"),
+    (333, 4096, 3, 1, "shared"),
+    (1, 512, 1, 1, "none"),
 ]
 
 
