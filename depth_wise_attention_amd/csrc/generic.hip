@@ -433,40 +433,60 @@ __global__ __launch_bounds__(256) void k_full_bwd_generic(FullBwdArgs a) {
 }
 
 // dw_j = g_j * Z_j, dg_j = w_j * Z_j (summed over j for a shared gain), with
-// Z_j the fixed-order sum of the slot partials: slot s goes to group s % 4
-// and, within it, to accumulator (s / 4) % 8; each group adds its eight
-// accumulators pairwise, and the four group sums are added in order.  The
-// eight accumulators keep eight independent loads in flight per lane (a
-// single running sum waits for each load in turn).
+// Z_j the fixed-order sum of the slot partials: slot s goes to group
+// s % kRedGroups and, within it, to accumulator (s / kRedGroups) % 8; each
+// group adds its eight accumulators pairwise, and the group sums are added
+// pairwise in group order.  Sixteen groups of eight accumulators keep 128
+// independent loads in flight per channel (a single running sum waits for
+// each load in turn, and the calls with a thousand slabs were bound by that).
+constexpr int kRedGroups = 16;
+
 __device__ __forceinline__ float z_group_sum(const float* z, int64_t slots, int S, int j, int d, int k, int gi) {
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const int64_t stride = (int64_t)S * d;
+  constexpr int kStep = 8 * kRedGroups;
   int64_t s = gi;
-  for (; s + 28 < slots; s += 32) {
+  for (; s + (kStep - kRedGroups) < slots; s += kStep) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc[u] += z[(s + 4 * u) * stride + (int64_t)j * d + k];
+    for (int u = 0; u < 8; ++u) acc[u] += z[(s + kRedGroups * u) * stride + (int64_t)j * d + k];
   }
 #pragma unroll
   for (int u = 0; u < 8; ++u)
-    if (s + 4 * u < slots) acc[u] += z[(s + 4 * u) * stride + (int64_t)j * d + k];
+    if (s + kRedGroups * u < slots) acc[u] += z[(s + kRedGroups * u) * stride + (int64_t)j * d + k];
   return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
 }
 
-// Block = 4 groups of 64 lanes over 64 consecutive channels of one
-// destination; group gi sums its slots, the four group sums are added in
-// order.  With one destination a shared gain's dg = w Z is written here too.
-__global__ __launch_bounds__(256) void k_bwd_reduce(const float* z, int64_t slots, int S, int d,
-                                                    const float* w, const float* gain,
-                                                    int64_t gain_ld, float* dw, float* dgain,
-                                                    int accumulate) {
-  __shared__ float part[4][64];
+// The group sums of one channel, added pairwise in group order.
+__device__ __forceinline__ float z_combine(const float (&g)[kRedGroups]) {
+  float h[kRedGroups / 2];
+#pragma unroll
+  for (int i = 0; i < kRedGroups / 2; ++i) h[i] = g[2 * i] + g[2 * i + 1];
+  float q4[kRedGroups / 4];
+#pragma unroll
+  for (int i = 0; i < kRedGroups / 4; ++i) q4[i] = h[2 * i] + h[2 * i + 1];
+  return ((q4[0] + q4[1]) + (q4[2] + q4[3]));
+}
+static_assert(kRedGroups == 16, "z_combine adds 16 group sums");
+
+// Block = kRedGroups groups of 64 lanes over 64 consecutive channels of one
+// destination; group gi sums its slots, then the group sums are combined in
+// a fixed order.  With one destination a shared gain's dg = w Z is written
+// here too.
+__global__ __launch_bounds__(64 * kRedGroups) void k_bwd_reduce(const float* z, int64_t slots, int S, int d,
+                                                                const float* w, const float* gain,
+                                                                int64_t gain_ld, float* dw, float* dgain,
+                                                                int accumulate) {
+  __shared__ float part[kRedGroups][64];
   const int lane = lane_id(), gi = threadIdx.x >> 6;
   const int k = blockIdx.x * 64 + lane;
   const int j = blockIdx.y;
   part[gi][lane] = k < d ? z_group_sum(z, slots, S, j, d, k, gi) : 0.f;
   __syncthreads();
   if (gi != 0 || k >= d) return;
-  const float Z = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+  float g[kRedGroups];
+#pragma unroll
+  for (int i = 0; i < kRedGroups; ++i) g[i] = part[i][lane];
+  const float Z = z_combine(g);
   const int64_t jk = (int64_t)j * d + k;
   const float gj = gain ? gain[j * gain_ld + k] : 1.0f;
   dw[jk] = accumulate ? dw[jk] + gj * Z : gj * Z;
@@ -484,10 +504,9 @@ __global__ __launch_bounds__(256) void k_bwd_reduce_shared_gain(const float* z, 
   float total = 0.f;
   for (int j = 0; j < S; ++j) {
     // Same grouping and order as k_bwd_reduce, so Z matches it bit for bit.
-    float part[4];
-    for (int gi = 0; gi < 4; ++gi) part[gi] = z_group_sum(z, slots, S, j, d, k, gi);
-    const float Z = ((part[0] + part[1]) + part[2]) + part[3];
-    total = fmaf(w[(int64_t)j * d + k], Z, total);
+    float g[kRedGroups];
+    for (int gi = 0; gi < kRedGroups; ++gi) g[gi] = z_group_sum(z, slots, S, j, d, k, gi);
+    total = fmaf(w[(int64_t)j * d + k], z_combine(g), total);
   }
   dgain[k] = accumulate ? dgain[k] + total : total;
 }
@@ -551,7 +570,7 @@ static hipError_t launch_z_reduce(const float* z, int64_t slots_used, int rows, 
                                   const float* gain, int64_t gain_ld, float* dw, float* dgain,
                                   int accumulate, hipStream_t st) {
   const bool shared = gain != nullptr && gain_ld == 0;
-  hipLaunchKernelGGL(k_bwd_reduce, dim3((unsigned)((d + 63) / 64), (unsigned)rows), dim3(256), 0, st, z,
+  hipLaunchKernelGGL(k_bwd_reduce, dim3((unsigned)((d + 63) / 64), (unsigned)rows), dim3(64 * kRedGroups), 0, st, z,
                      slots_used, rows, d, w, gain, gain_ld, dw, dgain, accumulate);
   if (shared && rows > 1)
     hipLaunchKernelGGL(k_bwd_reduce_shared_gain, dim3((unsigned)((d + 255) / 256)), dim3(256), 0, st, z,
