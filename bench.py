@@ -665,7 +665,8 @@ def bench_bwd(args, T=8192, H=1):
 def bench_depth_sweep(args, T=16384, Tb=8192, d=4096):
     """Phase 1 at every block depth (block n of a model reads N = n reps), S = 4,
     plus the 6-sublayer block of the 54-sublayer model (N = 9, S = 6), and the
-    Block backward at N = 1..12, S = 4.  Inputs are seeded normal draws made on
+    Block backward at N = 1..12, S = 4, and at (9, 6) and (8, 8), which run as two
+    destination chunks.  Inputs are seeded normal draws made on
     the device (rep n with std 1 + 0.3 n); each case's kernel is timed with HIP
     events around its launches on the stream they run on."""
     import torch
@@ -709,8 +710,7 @@ def bench_depth_sweep(args, T=16384, Tb=8192, d=4096):
         log(f"[bench] depth sweep phase1 {json.dumps(phase1[-1])}")
         del reps, h0, st
         torch.cuda.empty_cache()
-    for N in range(1, 13):
-        S = 4
+    for N, S in [(k, 4) for k in range(1, 13)] + [(9, 6), (8, 8)]:
         reps = reps_of(N, Tb)
         parts = torch.randn((S - 1, Tb, d), generator=gen, device="cuda").to(torch.bfloat16)
         dh = torch.randn((S, Tb, d), generator=gen, device="cuda").to(torch.bfloat16)

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <cstdint>
 
 #include "../../include/attnres.h"
 #include "launch.hpp"
@@ -724,12 +725,14 @@ int mhar_fwd_chunked(const void* reps, int64_t N, const void* partials, int64_t 
 }
 
 size_t attnres_bwd_workspace_size(int64_t N, int64_t S, int64_t T, int64_t d, int32_t H) {
-  (void)N;
   (void)H;
-  int64_t b;
+  int64_t b, r = 0;
   if (S < 1 || T < 0 || d < 1) return 0;
   if (!mul3(bwd_slots(T), S, d, &b) || !mul3(b, 4, 1, &b)) return 0;
-  return (size_t)b;
+  // A block of more than kBwdChunkMax destinations also keeps the first
+  // chunk's rep gradients in fp32 ([N, T, d]).
+  if (S > kBwdChunkMax && (N < 1 || !mul3(N, T, d, &r) || !mul3(r, 4, 1, &r) || b > INT64_MAX - r)) return 0;
+  return (size_t)(b + r);
 }
 
 int attnres_bwd(const void* reps, int64_t N, const void* partials, int64_t S, int64_t T, int64_t d,

@@ -9,7 +9,8 @@ hipError_t p1_launch_n<2>(const Phase1Args& a, const P1Plan& p, hipStream_t st) 
   return p1_launch_for<2>(a, p, st);
 }
 template <>
-hipError_t bwd_launch_n<2>(const BwdArgs& a, const BwdPlan& p, int64_t* slots_used, hipStream_t st) {
-  return bwd_launch_for<2>(a, p, slots_used, st);
+hipError_t bwd_launch_n<2>(const BwdArgs& a, const BwdPlan& p, int po, bool dry, int64_t* slots_used,
+                          hipStream_t st) {
+  return bwd_launch_for<2>(a, p, po, dry, slots_used, st);
 }
 }  // namespace attnres

@@ -4,12 +4,17 @@
 // block reads the N reps and, for j >= 1, the partial sum b_{j} (b-lab.team
 // summary §2, the value matrix); the pages give no backward, so this is the
 // chain rule through that forward.  One kernel per (N, S) with N = 1..12 and
-// S = 1..4.
+// S = 1..4.  A block of more than 4 sublayers runs as two chunks of
+// consecutive destinations: the first chunk writes its rep gradients in fp32
+// to the workspace, and the second chunk's kernel (PO = 0), whose first
+// destination reads a partial too, adds its own to them before the one
+// rounding to bf16 (the gradient is a sum over destinations) and writes its
+// Z rows into the same slabs.
 //
 // A persistent workgroup of B = d / 8 threads owns all channels of one token
 // at a time, thread `tid` owning the 8 channels at tid * 8.  Per token the
 // workgroup
-//   1. loads the N reps, the S-1 partials and the S upstream gradients once,
+//   1. loads the N reps, the S-PO partials and the S upstream gradients once,
 //   2. accumulates per-thread partial sums per source i -- its sum of squares
 //      and, for every destination j reading it, q_j . v_i and dh_j . v_i --
 //      and reduces them across the wave one source group at a time (at most
@@ -48,29 +53,33 @@ namespace attnres {
 struct BwdPlan {
   int B = 0;
   int hh = 1;
-  size_t lds = 0;
+  size_t lds = 0;  // the larger chunk's
+  int s0 = 0;      // destinations of the first chunk (all of them unless S > 4)
 };
 
 template <int N>
-hipError_t bwd_launch_n(const BwdArgs& a, const BwdPlan& p, int64_t* slots_used, hipStream_t st);
-#define ATTNRES_BWD_DECLARE(n) \
-  template <>                  \
-  hipError_t bwd_launch_n<n>(const BwdArgs& a, const BwdPlan& p, int64_t* slots_used, hipStream_t st);
+hipError_t bwd_launch_n(const BwdArgs& a, const BwdPlan& p, int po, bool dry, int64_t* slots_used, hipStream_t st);
+#define ATTNRES_BWD_DECLARE(n)                                                                  \
+  template <>                                                                                   \
+  hipError_t bwd_launch_n<n>(const BwdArgs& a, const BwdPlan& p, int po, bool dry, int64_t* slots_used, \
+                             hipStream_t st);
 ATTNRES_BWD_DECLARE(1) ATTNRES_BWD_DECLARE(2) ATTNRES_BWD_DECLARE(3) ATTNRES_BWD_DECLARE(4)
 ATTNRES_BWD_DECLARE(5) ATTNRES_BWD_DECLARE(6) ATTNRES_BWD_DECLARE(7) ATTNRES_BWD_DECLARE(8)
 ATTNRES_BWD_DECLARE(9) ATTNRES_BWD_DECLARE(10) ATTNRES_BWD_DECLARE(11) ATTNRES_BWD_DECLARE(12)
 #undef ATTNRES_BWD_DECLARE
 
 // Layout of one wave's reduction row: source i (i < N a rep, else partial
-// i - N, read only by destination i - N + 1) owns bwd_cnt(i) consecutive
+// i - N, read only by destination i - N + PO) owns bwd_cnt(i) consecutive
 // values from bwd_off(i): its sum of squares, then q_j . v_i and dh_j . v_i
 // for each destination j reading it, in destination order.
 template <int N, int S>
 constexpr int bwd_cnt(int i) { return i < N ? 1 + 2 * S : 3; }
 template <int N, int S>
 constexpr int bwd_off(int i) { return i < N ? i * (1 + 2 * S) : N * (1 + 2 * S) + (i - N) * 3; }
-template <int N, int S>
-constexpr int bwd_row_len() { return (bwd_off<N, S>(N + S - 1) + 7) / 8 * 8; }
+// PO = 1: partial k is read by destination k + 1 (a whole block, or its first
+// chunk); PO = 0: by destination k (a later chunk).  N + S - PO sources.
+template <int N, int S, int PO>
+constexpr int bwd_row_len() { return (bwd_off<N, S>(N + S - PO) + 7) / 8 * 8; }
 
 namespace {
 
@@ -87,6 +96,19 @@ __device__ __forceinline__ uint4 bwd_ld(const void* row, uint32_t off) {
 __device__ __forceinline__ void bwd_st(void* row, uint32_t off, uint4 u) {
   typedef unsigned int v4u __attribute__((ext_vector_type(4)));
   __builtin_amdgcn_raw_buffer_store_b128(v4u{u.x, u.y, u.z, u.w}, bwd_row(row), (int)off, 0, 0);
+}
+// 8 fp32 values at byte offset off of an fp32 row: stored, or added to x.
+__device__ __forceinline__ void bwd_st32(float* row, uint32_t off, const float (&x)[8]) {
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(v4f{x[0], x[1], x[2], x[3]}, bwd_row(row), (int)off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(v4f{x[4], x[5], x[6], x[7]}, bwd_row(row), (int)off + 16, 0, 0);
+}
+__device__ __forceinline__ void bwd_add32(const float* row, uint32_t off, float (&x)[8]) {
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  const v4f lo = __builtin_amdgcn_raw_buffer_load_b128(bwd_row(row), (int)off, 0, 0);
+  const v4f hi = __builtin_amdgcn_raw_buffer_load_b128(bwd_row(row), (int)off + 16, 0, 0);
+  x[0] += lo.x; x[1] += lo.y; x[2] += lo.z; x[3] += lo.w;
+  x[4] += hi.x; x[5] += hi.y; x[6] += hi.z; x[7] += hi.w;
 }
 __device__ __forceinline__ void bwd_unpack8(const uint4 u, float (&x)[8]) {
   x[0] = bf_lo(u.x); x[1] = bf_hi(u.x);
@@ -127,20 +149,20 @@ __device__ __forceinline__ void bwd_reduce_store(const float (&v)[P], float* dst
 
 // The end of the source group starting at I0: sources I0 .. I1-1 with at most
 // 64 values between them (at least one source).
-template <int N, int S>
+template <int N, int S, int PO>
 constexpr int bwd_group_end(int i0) {
   int i1 = i0 + 1;
-  while (i1 < N + S - 1 && bwd_off<N, S>(i1 + 1) - bwd_off<N, S>(i0) <= 64) ++i1;
+  while (i1 < N + S - PO && bwd_off<N, S>(i1 + 1) - bwd_off<N, S>(i0) <= 64) ++i1;
   return i1;
 }
 
 // Partial sums of the sources from I0 on, one group at a time, each group
 // reduced into its slots of the wave's row before the next is accumulated.
-template <int N, int S, int I0>
-__device__ __forceinline__ void bwd_partials(const uint4 (&v)[N + S - 1], const float (&qc)[S][8],
+template <int N, int S, int PO, int I0>
+__device__ __forceinline__ void bwd_partials(const uint4 (&v)[N + S - PO], const float (&qc)[S][8],
                                              const float (&dg)[S][8], float* row, int rl) {
-  if constexpr (I0 < N + S - 1) {
-    constexpr int I1 = bwd_group_end<N, S>(I0);
+  if constexpr (I0 < N + S - PO) {
+    constexpr int I1 = bwd_group_end<N, S, PO>(I0);
     constexpr int O0 = bwd_off<N, S>(I0);
     constexpr int GC = bwd_off<N, S>(I1) - O0;
     float part[GC];
@@ -161,14 +183,14 @@ __device__ __forceinline__ void bwd_partials(const uint4 (&v)[N + S - 1], const 
             part[o + 2 + 2 * j] = fmaf(dg[j][e], x[e], part[o + 2 + 2 * j]);
           }
         } else {
-          const int j = i - N + 1;
+          const int j = i - N + PO;
           part[o + 1] = fmaf(qc[j][e], x[e], part[o + 1]);
           part[o + 2] = fmaf(dg[j][e], x[e], part[o + 2]);
         }
       }
     }
     bwd_reduce_store<0, GC, GC>(part, row + O0, rl);
-    bwd_partials<N, S, I1>(v, qc, dg, row, rl);
+    bwd_partials<N, S, PO, I1>(v, qc, dg, row, rl);
   }
 }
 
@@ -189,10 +211,10 @@ __device__ __noinline__ void bwd_fold(const float* w, const float* gain, int64_t
   }
 }
 
-template <int N, int S, int HH>
+template <int N, int S, int HH, int PO>
 __global__ __launch_bounds__(512, 1) void k_bwd(BwdArgs a) {
-  constexpr int NS = N + S - 1;             // sources: N reps, then S-1 partials
-  constexpr int PR = bwd_row_len<N, S>();   // floats per wave row
+  constexpr int NS = N + S - PO;              // sources: N reps, then S-PO partials
+  constexpr int PR = bwd_row_len<N, S, PO>();  // floats per wave row
   constexpr int NP = bwd_pow2(N + 1);       // lanes per destination group
   static_assert(S * NP <= 64, "pair table must fit one wave");
   extern __shared__ float4 bwd_smem[];
@@ -248,19 +270,19 @@ __global__ __launch_bounds__(512, 1) void k_bwd(BwdArgs a) {
       // recomputed per token (held across the loop they cost registers).
       int rl = lane;
       asm volatile("" : "+v"(rl));
-      bwd_partials<N, S, 0>(v, qc, dg, red + (buf * W + wave) * PR, rl);
+      bwd_partials<N, S, PO, 0>(v, qc, dg, red + (buf * W + wave) * PR, rl);
     }
     __syncthreads();
 
     // Per-pair scalars, one lane per (destination pj, slot pu): slot pu < N
-    // is rep pu, slot N the partial destination pj >= 1 reads.
+    // is rep pu, slot N the partial destination pj >= PO reads.
     int sl = lane;
     asm volatile("" : "+v"(sl));
     const int pj = sl / NP, pu = sl % NP;
-    const bool pvalid = pj < S && (pu < N || (pu == N && pj >= 1));
+    const bool pvalid = pj < S && (pu < N || (pu == N && pj >= PO));
     // This pair's source values in the row: its sum of squares at soff, q . v
     // at pslot and dh . v right after.
-    const int soff = pu < N ? pu * (1 + 2 * S) : N * (1 + 2 * S) + (pj - 1) * 3;
+    const int soff = pu < N ? pu * (1 + 2 * S) : N * (1 + 2 * S) + (pj - PO) * 3;
     const int pslot = soff + 1 + (pu < N ? 2 * pj : 0);
     float alpha = 0.f, cr = 0.f, coef = 0.f;
     {
@@ -306,12 +328,12 @@ __global__ __launch_bounds__(512, 1) void k_bwd(BwdArgs a) {
       float x[8], gr[8];
       bwd_unpack8(v[i], x);
       const int u = i < N ? i : N;
-      const float cf = read_lane(coef, (i < N ? 0 : i - N + 1) * NP + u);
+      const float cf = read_lane(coef, (i < N ? 0 : i - N + PO) * NP + u);
 #pragma unroll
       for (int e = 0; e < 8; ++e) gr[e] = -cf * x[e];
 #pragma unroll
       for (int j = 0; j < S; ++j) {
-        if (i < N || i == N + j - 1) {
+        if (i < N || i == N + j - PO) {
           const float al = read_lane(alpha, j * NP + u);
           const float crl = read_lane(cr, j * NP + u);
 #pragma unroll
@@ -323,6 +345,15 @@ __global__ __launch_bounds__(512, 1) void k_bwd(BwdArgs a) {
         }
       }
       bf16_t* out = dsrc_row(i, t);
+      if (i < N && a.rep_mode != 0) {
+        // Rep gradients of a block split into destination chunks, in fp32.
+        float* r32 = a.rep32 + i * td + t * d;
+        if (a.rep_mode == 1) {
+          bwd_st32(r32, coff * 2u, gr);
+          continue;
+        }
+        bwd_add32(r32, coff * 2u, gr);
+      }
       if (a.accumulate) {
         float old[8];
         bwd_unpack8(bwd_ld(out, coff), old);
@@ -334,8 +365,9 @@ __global__ __launch_bounds__(512, 1) void k_bwd(BwdArgs a) {
     buf ^= 1;
   }
 
-  // This workgroup's slab of Z partial sums: zslots[blockIdx][j][channel].
-  float* z = a.zslots + (int64_t)blockIdx.x * S * d;
+  // This workgroup's slab of Z partial sums: zslots[blockIdx][j][channel],
+  // slabs zld floats apart.
+  float* z = a.zslots + (int64_t)blockIdx.x * a.zld;
 #pragma unroll
   for (int j = 0; j < S; ++j) {
     float4* zp = reinterpret_cast<float4*>(z + (int64_t)j * d + tid * 8);
@@ -344,9 +376,10 @@ __global__ __launch_bounds__(512, 1) void k_bwd(BwdArgs a) {
   }
 }
 
-template <int N, int S, int HH>
-hipError_t bwd_go(const BwdArgs& a, const BwdPlan& p, int64_t* slots_used, hipStream_t st) {
-  auto kern = k_bwd<N, S, HH>;
+// Launches one chunk (or, with dry set, only reports the grid it would use).
+template <int N, int S, int HH, int PO>
+hipError_t bwd_go(const BwdArgs& a, const BwdPlan& p, bool dry, int64_t* slots_used, hipStream_t st) {
+  auto kern = k_bwd<N, S, HH, PO>;
   static std::atomic<size_t> allowed{64 * 1024};
   if (p.lds > allowed.load(std::memory_order_relaxed)) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -361,31 +394,43 @@ hipError_t bwd_go(const BwdArgs& a, const BwdPlan& p, int64_t* slots_used, hipSt
   int64_t grid = (int64_t)num_cus() * per_cu;
   if (grid > a.T) grid = a.T;
   if (grid > a.slots) grid = a.slots;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3((unsigned)p.B), p.lds, st, a);
   *slots_used = grid;
+  if (dry) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3((unsigned)p.B), p.lds, st, a);
   return hipGetLastError();
 }
 
-template <int N, int S>
-hipError_t bwd_go_s(const BwdArgs& a, const BwdPlan& p, int64_t* slots_used, hipStream_t st) {
+template <int N, int S, int PO>
+hipError_t bwd_go_s(const BwdArgs& a, const BwdPlan& p, bool dry, int64_t* slots_used, hipStream_t st) {
   switch (p.hh) {
-    case 1: return bwd_go<N, S, 1>(a, p, slots_used, st);
-    case 2: return bwd_go<N, S, 2>(a, p, slots_used, st);
-    case 4: return bwd_go<N, S, 4>(a, p, slots_used, st);
-    case 8: return bwd_go<N, S, 8>(a, p, slots_used, st);
+    case 1: return bwd_go<N, S, 1, PO>(a, p, dry, slots_used, st);
+    case 2: return bwd_go<N, S, 2, PO>(a, p, dry, slots_used, st);
+    case 4: return bwd_go<N, S, 4, PO>(a, p, dry, slots_used, st);
+    case 8: return bwd_go<N, S, 8, PO>(a, p, dry, slots_used, st);
     default: return hipErrorNotSupported;
   }
 }
 
 }  // namespace
 
+// a.S destinations of one chunk: PO = 1 for S = 1..4, PO = 0 for S = 2..4
+// (a later chunk of a block of 5..8).
 template <int N>
-hipError_t bwd_launch_for(const BwdArgs& a, const BwdPlan& p, int64_t* slots_used, hipStream_t st) {
+hipError_t bwd_launch_for(const BwdArgs& a, const BwdPlan& p, int po, bool dry, int64_t* slots_used,
+                          hipStream_t st) {
+  if (po == 0) {
+    switch (a.S) {
+      case 2: return bwd_go_s<N, 2, 0>(a, p, dry, slots_used, st);
+      case 3: return bwd_go_s<N, 3, 0>(a, p, dry, slots_used, st);
+      case 4: return bwd_go_s<N, 4, 0>(a, p, dry, slots_used, st);
+      default: return hipErrorNotSupported;
+    }
+  }
   switch (a.S) {
-    case 1: return bwd_go_s<N, 1>(a, p, slots_used, st);
-    case 2: return bwd_go_s<N, 2>(a, p, slots_used, st);
-    case 3: return bwd_go_s<N, 3>(a, p, slots_used, st);
-    case 4: return bwd_go_s<N, 4>(a, p, slots_used, st);
+    case 1: return bwd_go_s<N, 1, 1>(a, p, dry, slots_used, st);
+    case 2: return bwd_go_s<N, 2, 1>(a, p, dry, slots_used, st);
+    case 3: return bwd_go_s<N, 3, 1>(a, p, dry, slots_used, st);
+    case 4: return bwd_go_s<N, 4, 1>(a, p, dry, slots_used, st);
     default: return hipErrorNotSupported;
   }
 }

@@ -119,10 +119,19 @@ struct BwdArgs {
   int accumulate;
   float* zslots;  // [slots, S, d] fp32
   int64_t slots;
+  // Set by the specialised kernel's launcher for each destination chunk:
+  // floats between Z slabs; rep gradients to d_reps (rep_mode 0), to the fp32
+  // buffer rep32 [N, T, d] (1), or added to rep32's before the store (2).
+  int64_t zld = 0;
+  float* rep32 = nullptr;
+  int rep_mode = 0;
 };
 
 // Maximum number of [S, d] partial-gradient slabs in the backward workspace.
 constexpr int64_t kMaxBwdSlots = 1024;
+// Destinations one specialised backward kernel holds; a larger block runs as
+// two chunks.
+constexpr int kBwdChunkMax = 4;
 
 // Full AttnRes backward: gradients of sum_j <dout_j, out_j> for the Full forward.
 struct FullBwdArgs {

@@ -264,7 +264,11 @@ int mhar_fwd_noalloc(const void* reps, int64_t N, const void* partials, int64_t 
 
 /*
  * Bytes of device workspace attnres_bwd needs (fp32 partial sums of the
- * pseudo-query gradient, one [S, d] slab per slot, min(T, 1024) slots).
+ * pseudo-query gradient, one [S, d] slab per slot, min(T, 1024) slots).  With
+ * S > 4 it also holds the rep gradients of the block's first destinations in
+ * fp32 ([N, T, d], 4 N T d bytes): such a block runs as two chunks of at most
+ * 4 destinations, and the second adds its rep gradients to the first's before
+ * the one rounding to the I/O dtype.
  */
 size_t attnres_bwd_workspace_size(int64_t N, int64_t S, int64_t T, int64_t d, int32_t H);
 

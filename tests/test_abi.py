@@ -75,6 +75,9 @@ def test_workspace_sizes():
     assert binding.attnres_bwd_workspace_size(N, S, 8192, d, H) == 1024 * S * d * 4
     assert binding.attnres_bwd_workspace_size(N, S, 5, d, H) == 8 * S * d * 4
     assert binding.attnres_bwd_workspace_size(N, S, 0, d, H) == 0
+    # more than 4 destinations: two chunks, the first chunk's rep gradients kept in fp32
+    assert binding.attnres_bwd_workspace_size(9, 6, 8192, d, H) == 1024 * 6 * d * 4 + 9 * 8192 * d * 4
+    assert binding.attnres_bwd_workspace_size(2, 5, 5, 1024, H) == 8 * 5 * 1024 * 4 + 2 * 5 * 1024 * 4
 
 
 def _rc_full(**kw):

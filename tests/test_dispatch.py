@@ -67,10 +67,13 @@ def test_phase1_general_kernel_cases():
 
 
 @pytest.mark.parametrize("N", range(1, 13))
-@pytest.mark.parametrize("S", range(1, 5))
+@pytest.mark.parametrize("S", range(1, 9))
 def test_bwd_every_block_depth(N, S):
+    """Every N up to 12 and S up to 8; more than 4 destinations run as two chunks,
+    the first the larger (S0 destinations)."""
     kind, f, B = parse(variant(binding.OP_BWD, N, S, 100, 4096))
     assert kind == "bwd_fast" and f["N"] == N and f["S"] == S and f["HH"] == 1 and B == 512
+    assert f["S0"] == (S if S <= 4 else (S + 1) // 2)
 
 
 def test_bwd_widths_heads_and_limits():
@@ -82,7 +85,11 @@ def test_bwd_widths_heads_and_limits():
                 assert kind == "bwd_fast" and f["HH"] == H and B == d // 8, (d, H)
             else:
                 assert name == "bwd_generic", (d, H)
-    assert variant(binding.OP_BWD, 8, 5, 100, 4096) == "bwd_generic"
+    assert variant(binding.OP_BWD, 8, 9, 100, 4096) == "bwd_generic"
+    for d in (1024, 2048, 4096):
+        for S in (5, 6, 8):
+            kind, f, B = parse(variant(binding.OP_BWD, 9, S, 100, d, 2 if d > 1024 else 1))
+            assert kind == "bwd_fast" and f["S0"] == (S + 1) // 2 and B == d // 8, (d, S)
     assert variant(binding.OP_BWD, 8, 4, 100, 8192) == "bwd_generic"
     assert variant(binding.OP_BWD, 8, 4, 100, 4096, dtype=F32) == "bwd_generic"
 

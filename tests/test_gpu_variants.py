@@ -105,6 +105,10 @@ BWD_CASES = (
     + [(8, 4, d, 1, 600) for d in (512, 1024, 1536, 2048)]
     + [(8, 4, 4096, H, 300) for H in (2, 4, 8)]
     + [(12, 4, 4096, 8, 200), (3, 2, 2048, 4, 300), (9, 3, 1024, 2, 400), (5, 1, 4096, 1, 700)]
+    # more than 4 destinations: two destination chunks
+    + [(N, S, 4096, 1, 7) for N in range(1, 13) for S in range(5, 9)]
+    + [(9, 6, d, 1, 300) for d in (512, 1024, 2048)] + [(9, 6, 4096, H, 200) for H in (2, 8)]
+    + [(4, 8, 1024, 2, 500), (12, 8, 2048, 4, 130), (9, 5, 4096, 1, 1100), (11, 7, 4096, 8, 90)]
 )
 
 
@@ -130,6 +134,33 @@ def test_bwd_variant(N, S, d, H, T):
     ref1 = orc.block_bwd(wl.reps, wl.partials, wl.w, g1, wl.eps, H, wl.dh)
     check(host(got1[0]), ref1[0], "bf16", "d_reps (shared gain)")
     check(host(got1[3]), ref1[3], "f32_from_bf16", "dgain (shared gain)")
+
+
+@pytest.mark.parametrize("N,S,d,H", [(9, 6, 2048, 1), (4, 8, 4096, 2), (8, 5, 1024, 1)])
+def test_bwd_chunks_accumulate(N, S, d, H):
+    """A block of more than 4 destinations runs as two chunks; with accumulate
+    the rep gradients of both chunks are added to the given d_reps before the
+    one rounding, and the other outputs are added to as usual."""
+    T = 260
+    name = ar.attnres_kernel_variant(ar.OP_BWD, N, S, T, d, H)
+    say(f"bwd chunks accumulate N={N} S={S} d={d} H={H} T={T}: {name}")
+    assert name.startswith("bwd_fast") and "S0=%d" % ((S + 1) // 2) in name, name
+    wl = synth.block_workload(T=T, d=d, N=N, S=S, H=H, rep_std_step=0.3, dtype="bf16", seed=90 + N + S,
+                              with_dh=True)
+    reps, w, g, dh = dev(wl.reps, True), dev(wl.w), dev(wl.gain), dev(wl.dh, True)
+    parts = dev(wl.partials, True)
+    rng = np.random.default_rng(N * 16 + S)
+    base = [rng.standard_normal(x.shape) for x in (wl.reps, wl.partials, wl.w, wl.gain)]
+    base[0] = host(dev(base[0], True))  # bf16-exact starting values
+    base[1] = host(dev(base[1], True))
+    outs = [dev(base[0], True), dev(base[1], True), dev(base[2]), dev(base[3])]
+    ar.attnres_bwd(reps, parts, w, dh, g, wl.eps, H, d_reps=outs[0], d_partials=outs[1], dw=outs[2],
+                   dgain=outs[3], accumulate=True)
+    ref = orc.block_bwd(wl.reps, wl.partials, wl.w, wl.gain, wl.eps, H, wl.dh)
+    check(host(outs[0]), base[0] + ref[0], "bf16", "d_reps accumulated")
+    check(host(outs[1]), base[1] + ref[1], "bf16", "d_partials accumulated")
+    check(host(outs[2]), base[2] + ref[2], "f32_from_bf16", "dw accumulated")
+    check(host(outs[3]), base[3] + ref[3], "f32_from_bf16", "dgain accumulated")
 
 
 @pytest.mark.parametrize("H", [1, 8])
