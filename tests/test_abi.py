@@ -325,6 +325,11 @@ def test_bwd_rejects_bad_arguments():
     assert _rc_bwd(N=60, S=6) == EUNSUP
     assert _rc_bwd(ws=None) == EWS
     assert _rc_bwd(ws_bytes=100) == EWS
+    # more than 4 destinations: the Z slabs alone are too short, the fp32 rep gradients need room too
+    slabs = 8 * 6 * 64 * 4
+    assert _rc_bwd(S=6, ws_bytes=slabs) == EWS
+    assert _rc_bwd(S=6, ws_bytes=slabs + 8 * 8 * 64 * 4 - 4) == EWS
+    assert binding.attnres_bwd_workspace_size(8, 6, 8, 64, 1) == slabs + 8 * 8 * 64 * 4
 
 
 @fake_ptrs

@@ -108,7 +108,8 @@ BWD_CASES = (
     # more than 4 destinations: two destination chunks
     + [(N, S, 4096, 1, 7) for N in range(1, 13) for S in range(5, 9)]
     + [(9, 6, d, 1, 300) for d in (512, 1024, 2048)] + [(9, 6, 4096, H, 200) for H in (2, 8)]
-    + [(4, 8, 1024, 2, 500), (12, 8, 2048, 4, 130), (9, 5, 4096, 1, 1100), (11, 7, 4096, 8, 90)]
+    + [(4, 8, 1024, 2, 500), (12, 8, 2048, 4, 130), (9, 5, 4096, 1, 1100), (11, 7, 4096, 8, 90),
+       (9, 6, 4096, 1, 1), (3, 5, 512, 1, 1)]
 )
 
 
