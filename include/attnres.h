@@ -290,7 +290,9 @@ size_t attnres_bwd_workspace_size(int64_t N, int64_t S, int64_t T, int64_t d, in
  *              by later blocks too, so their gradients accumulate)
  *  ws          device workspace of at least attnres_bwd_workspace_size() bytes
  * Requires 1 <= N, N + S - 1 <= 64, S * H * (N + 1) <= 1024 on the general
- * path.
+ * path.  The specialised kernel takes bf16 with N <= 12, S <= 8, d a multiple
+ * of 512 up to 4096 and H in {1, 2, 4, 8} dividing d / 512; with S > 4 it runs
+ * as two launches over the first ceil(S/2) and the remaining destinations.
  */
 int attnres_bwd(const void* reps, int64_t N, const void* partials, int64_t S, int64_t T, int64_t d,
                 const float* w, const float* gain, int64_t gain_ld, float eps, int32_t H,
